@@ -1,0 +1,98 @@
+"""Attention over the decoded cache, split partials and their merge.
+
+The method's attention is exact softmax attention over the dequantised
+cache, so the oracle writes it out by its plain definition in float64 in
+the original (un-rotated) domain:
+
+    s_t = scale * q . K_t,   lse = ln sum_t exp(s_t),   o = sum_t exp(s_t - lse) V_t
+
+Readings: R13 (kv head = q head // (H_q / H_kv)), R14 (natural-log LSE).
+A sequence with no cached tokens gives o = 0 and lse = -inf.
+
+Split-K (flash-decoding): the logical blocks of a sequence are cut into
+contiguous chunks of `chunk_blocks` blocks; each chunk yields its own
+normalised o_p and lse_p (empty chunks: o_p = 0, lse_p = -inf) and the merge
+is the log-sum-exp identity
+
+    lse = M + ln sum_p exp(lse_p - M),   o = sum_p exp(lse_p - lse) o_p.
+
+[D "Serving Route Design"]: the workspace of the split is bounded by the
+runtime shape (sequences x heads x splits x d), never by context length.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .pages import reconstruct_sequence
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """q[d], K[n, d], V[n, d] -> (o[d], lse) in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    n = K.shape[0]
+    if n == 0:
+        return np.zeros(q.shape[-1]), -math.inf
+    s = scale * (K @ q)
+    mx = np.max(s)
+    e = np.exp(s - mx)
+    tot = np.sum(e)
+    lse = mx + math.log(tot)
+    o = (e / tot) @ V
+    return o, lse
+
+
+def split_partials(q, K, V, scale, block_size: int, chunk_blocks: int, num_splits: int):
+    """Partials (o_p[P, d], lse_p[P]) of one (sequence, q head) for chunks of
+    chunk_blocks logical blocks."""
+    n = K.shape[0]
+    d = K.shape[1]
+    o = np.zeros((num_splits, d))
+    lse = np.full(num_splits, -math.inf)
+    span = chunk_blocks * block_size
+    for p in range(num_splits):
+        lo, hi = p * span, min((p + 1) * span, n)
+        if lo < hi:
+            o[p], lse[p] = attention(q, K[lo:hi], V[lo:hi], scale)
+    return o, lse
+
+
+def merge_partials(o_p: np.ndarray, lse_p: np.ndarray):
+    """LSE-weighted merge of partials o_p[P, d], lse_p[P]."""
+    o_p = np.asarray(o_p, dtype=np.float64)
+    lse_p = np.asarray(lse_p, dtype=np.float64)
+    if not np.any(np.isfinite(lse_p)):
+        return np.zeros(o_p.shape[-1]), -math.inf
+    M = np.max(lse_p)
+    w = np.exp(lse_p - M)
+    lse = M + math.log(np.sum(w))
+    o = np.sum(np.exp(lse_p - lse)[:, None] * o_p, axis=0)
+    return o, lse
+
+
+def decode_reference(q: np.ndarray, k_pages, v_pages, block_tables, context_lens, kfmt, vfmt,
+                     scale: float, block_size: int, pairs=None):
+    """fp64 decode of q[B, H_q, d] against packed pages.  Returns
+    (out[B, H_q, d], lse[B, H_q]); with `pairs` (list of (seq, q_head)) only
+    those entries are computed (others stay NaN)."""
+    B, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    out = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    todo = pairs if pairs is not None else [(s, h) for s in range(B) for h in range(Hq)]
+    cache = {}
+    for s, h in todo:
+        kvh = h // G
+        key = (s, kvh)
+        if key not in cache:
+            n = int(context_lens[s])
+            K = reconstruct_sequence(k_pages, block_tables[s], n, kvh, kfmt, block_size)
+            V = reconstruct_sequence(v_pages, block_tables[s], n, kvh, vfmt, block_size)
+            cache = {key: (K, V)}
+        K, V = cache[key]
+        out[s, h], lse[s, h] = attention(q[s, h], K, V, scale)
+    return out, lse

@@ -1,0 +1,100 @@
+"""Persistent uint8 pages: slot mapping, block tables, tile layout.
+
+[D "Serving Route Design"]: a token slot maps to a physical block and an
+offset, block = slot // block_size and offset = slot % block_size, then to
+the packed row bytes; packed rows are written into persistent pages and
+read back through block tables.  [D "Data Ownership"]: the page cache owns
+vLLM-style uint8 pages.  [D "Error Model"]: slots outside the allocated
+pages are IndexErrors.
+
+Layout (readings R10, R11): pages are [num_blocks][num_kv_heads][tile].  A
+tile holds block_size rows of packed indices (the index plane, row `offset`
+at byte offset*row_bytes) followed by the norm plane, fp16 little-endian,
+group-major: the norm of group g for row `offset` sits at
+block_size*row_bytes + (g*block_size + offset)*2.  The tile is padded to a
+multiple of 16 bytes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .encode import Format, encode_rows, pack_row, unpack_row, dequantize_rotated, row_bytes
+from .rotation import inverse_rotate
+
+
+def tile_layout(fmt: Format, block_size: int):
+    """(row_idx_bytes, norm_plane_offset, tile_bytes)."""
+    rb = row_bytes(fmt)
+    norm_off = block_size * rb
+    raw = norm_off + block_size * fmt.num_groups * 2
+    tile = (raw + 15) // 16 * 16
+    return rb, norm_off, tile
+
+
+def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt: Format,
+                block_size: int) -> None:
+    """Quantise rows x[T, H, d] and store them in pages[num_blocks, H, tile]
+    at the rows named by slot_mapping[T].  Bytes outside the written rows and
+    norm slots are left untouched."""
+    x = np.asarray(x)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    T, H, d = x.shape
+    nb = pages.shape[0]
+    rb, norm_off, tile = tile_layout(fmt, block_size)
+    if pages.dtype != np.uint8 or pages.shape[1:] != (H, tile):
+        raise ValueError("page pool shape does not match the format")
+    if slots.shape != (T,):
+        raise ValueError("slot_mapping length differs from the number of tokens")
+    bad = (slots < 0) | (slots >= nb * block_size)
+    if np.any(bad):
+        i = int(np.nonzero(bad)[0][0])
+        raise IndexError(f"slot {int(slots[i])} of token {i} outside [0, {nb * block_size})")
+    if len(np.unique(slots)) != T:
+        raise ValueError("duplicate slots in one write")
+    blk = slots // block_size
+    off = slots % block_size
+    idx_groups, norms = encode_rows(x, fmt)              # [T, H, m] per group, [T, H, G]
+    data = pack_row(idx_groups, fmt)                      # [T, H, rb]
+    for h in range(H):
+        for b in range(rb):
+            pages[blk, h, off * rb + b] = data[:, h, b]
+        for g in range(fmt.num_groups):
+            pos = norm_off + (g * block_size + off) * 2
+            pages[blk, h, pos] = (norms[:, h, g] & 0xFF).astype(np.uint8)
+            pages[blk, h, pos + 1] = (norms[:, h, g] >> 8).astype(np.uint8)
+
+
+def read_rows(pages: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, head: int, fmt: Format,
+              block_size: int):
+    """Unpack the rows at (blocks[i], offsets[i]) of one kv head ->
+    (index arrays per group, fp16 norm bits [n, G])."""
+    rb, norm_off, tile = tile_layout(fmt, block_size)
+    blocks = np.asarray(blocks, dtype=np.int64)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    t = pages[blocks, head]                                          # [n, tile]
+    cols = offsets[:, None] * rb + np.arange(rb)[None, :]
+    data = np.take_along_axis(t, cols, axis=1)
+    idx = unpack_row(data, fmt)
+    norms = np.empty((len(blocks), fmt.num_groups), dtype=np.uint16)
+    for g in range(fmt.num_groups):
+        pos = norm_off + (g * block_size + offsets) * 2
+        lo = t[np.arange(len(blocks)), pos].astype(np.uint16)
+        hi = t[np.arange(len(blocks)), pos + 1].astype(np.uint16)
+        norms[:, g] = lo | (hi << 8)
+    return idx, norms
+
+
+def reconstruct_sequence(pages: np.ndarray, block_table_row: np.ndarray, ctx: int, head: int,
+                         fmt: Format, block_size: int, rotated: bool = False) -> np.ndarray:
+    """Dense float64 K or V rows [ctx, d] of one sequence and kv head, walked
+    through its block table ([D "Diagnostic Route Design"]: dense
+    reconstruction is a diagnostic, allowed for validation only).  With
+    rotated=True the rows stay in the rotated domain."""
+    t = np.arange(ctx)
+    bt = np.asarray(block_table_row, dtype=np.int64)
+    blocks = bt[t // block_size]
+    if np.any(blocks < 0) or np.any(blocks >= pages.shape[0]):
+        raise IndexError("block table entry outside the page pool")
+    idx, norms = read_rows(pages, blocks, t % block_size, head, fmt, block_size)
+    y = dequantize_rotated(idx, norms, fmt)
+    return y if rotated else inverse_rotate(y, fmt.signs)

@@ -1,0 +1,105 @@
+"""Pins for the oracle's attention, split partials and merge."""
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+
+from oracle import attn as att
+from oracle import encode as enc
+from oracle import pages as pg
+from oracle.rotation import rotate
+from workloads import signs
+
+
+def _brute(q, K, V, scale, digits=50):
+    """Attention in 50-digit decimal arithmetic, straight from the definition."""
+    getcontext().prec = digits
+    qd = [Decimal(float(v)) for v in q]
+    sc = Decimal(float(scale))
+    s = [sc * sum(qd[j] * Decimal(float(K[t, j])) for j in range(len(q))) for t in range(K.shape[0])]
+    mx = max(s)
+    e = [(si - mx).exp() for si in s]
+    tot = sum(e)
+    lse = mx + tot.ln()
+    o = [sum(e[t] * Decimal(float(V[t, j])) for t in range(K.shape[0])) / tot for j in range(V.shape[1])]
+    return np.array([float(v) for v in o]), float(lse)
+
+
+@pytest.mark.parametrize("n,d", [(1, 8), (5, 8), (37, 16)])
+def test_attention_against_high_precision(n, d):
+    rng = np.random.default_rng(n)
+    q = rng.standard_normal(d)
+    K = rng.standard_normal((n, d)) * 3
+    V = rng.standard_normal((n, d))
+    o, lse = att.attention(q, K, V, 0.7)
+    ob, lb = _brute(q, K, V, 0.7)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    assert abs(lse - lb) < 1e-12
+
+
+def test_special_cases():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal(16)
+    K = rng.standard_normal((1, 16))
+    V = rng.standard_normal((1, 16))
+    o, lse = att.attention(q, K, V, 0.25)
+    np.testing.assert_array_equal(o, V[0])
+    assert lse == pytest.approx(0.25 * float(q @ K[0]), abs=1e-15)
+    # identical keys: uniform weights, lse = s + ln n
+    Kr = np.repeat(K, 9, axis=0)
+    Vr = rng.standard_normal((9, 16))
+    o, lse = att.attention(q, Kr, Vr, 0.25)
+    np.testing.assert_allclose(o, Vr.mean(axis=0), atol=1e-15)
+    assert lse == pytest.approx(0.25 * float(q @ K[0]) + math.log(9), abs=1e-14)
+    # empty context
+    o, lse = att.attention(q, np.zeros((0, 16)), np.zeros((0, 16)), 1.0)
+    assert np.all(o == 0) and lse == -math.inf
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 7, 64])
+def test_split_merge_identity(P):
+    rng = np.random.default_rng(P)
+    n, d, bs = 301, 32, 16
+    q = rng.standard_normal(d)
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    nb = -(-n // bs)
+    chunk = -(-nb // P)
+    o_p, l_p = att.split_partials(q, K, V, 0.3, bs, chunk, P)
+    if P == 64:
+        assert np.sum(np.isinf(l_p)) > 0          # empty chunks present
+    o, lse = att.merge_partials(o_p, l_p)
+    o_ref, l_ref = att.attention(q, K, V, 0.3)
+    np.testing.assert_allclose(o, o_ref, atol=1e-12)
+    assert abs(lse - l_ref) < 1e-12
+
+
+def test_merge_all_empty():
+    o, lse = att.merge_partials(np.zeros((3, 4)), np.full(3, -math.inf))
+    assert np.all(o == 0) and lse == -math.inf
+
+
+def test_rotated_domain_equals_original_domain():
+    """Scores and outputs computed against the rotated-domain cache (q rotated
+    once, output inverse-rotated once) equal the original-domain ones."""
+    d, bs, n = 128, 16, 70
+    s = signs(4, 1, d)
+    f = enc.Format.make(d, [4], s)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((n, 1, d))
+    _, _, tile = pg.tile_layout(f, bs)
+    pages = np.zeros((5, 1, tile), dtype=np.uint8)
+    bt = np.array([3, 1, 4, 0, 2])
+    slots = bt[np.arange(n) // bs] * bs + np.arange(n) % bs
+    pg.write_pages(x, slots, pages, f, bs)
+    K = pg.reconstruct_sequence(pages, bt, n, 0, f, bs)
+    Y = pg.reconstruct_sequence(pages, bt, n, 0, f, bs, rotated=True)
+    q = rng.standard_normal(d)
+    q_rot = rotate(q, s) / np.sqrt(d)
+    np.testing.assert_allclose(Y @ q_rot, K @ q, atol=1e-12)
+    o, lse = att.attention(q, K, K, 0.1)
+    o_r, lse_r = att.attention(q_rot, Y, Y, 0.1)
+    from oracle.rotation import inverse_rotate
+    np.testing.assert_allclose(inverse_rotate(o_r, s), o, atol=1e-12)
+    assert abs(lse - lse_r) < 1e-12

@@ -1,0 +1,109 @@
+"""Pins for the oracle's page writer and reader (slot -> block -> offset -> row)."""
+import numpy as np
+import pytest
+
+from oracle import encode as enc
+from oracle import pages as pg
+from workloads import signs, channel_subset
+
+
+def fmts():
+    s = signs(0, 1, 128)
+    k = enc.Format.make(128, [4], s)
+    v = enc.Format.make(128, [2], s)
+    hi = channel_subset(0, 3, 128, 64)
+    lo = np.array(sorted(set(range(128)) - set(hi.tolist())))
+    km = enc.Format.make(128, [4, 3], s, np.concatenate([hi, lo]))
+    k64 = enc.Format.make(64, [4], signs(0, 1, 64))
+    return k, v, km, k64
+
+
+def test_tile_layout_closed_forms():
+    k, v, km, k64 = fmts()
+    assert pg.tile_layout(k, 16) == (64, 1024, 1056)
+    assert pg.tile_layout(v, 16) == (32, 512, 544)
+    assert pg.tile_layout(km, 16) == (56, 896, 960)
+    assert pg.tile_layout(k64, 16) == (32, 512, 544)
+
+
+def test_write_places_rows_at_slot_block_offset():
+    """A hand-built slot list: each row lands at block = slot // 16,
+    offset = slot % 16 and nothing else in the pool changes."""
+    k, _, _, _ = fmts()
+    bs, H, nb = 16, 2, 5
+    rb, noff, tile = pg.tile_layout(k, bs)
+    pages = np.full((nb, H, tile), 0xA5, dtype=np.uint8)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((4, H, 128))
+    slots = np.array([0, 17, 79, 35])
+    pg.write_pages(x, slots, pages, k, bs)
+    idx, norms = enc.encode_rows(x, k)
+    data = enc.pack_row(idx, k)
+    touched = np.zeros_like(pages, dtype=bool)
+    for i, s in enumerate(slots):
+        b, o = divmod(int(s), bs)
+        for h in range(H):
+            np.testing.assert_array_equal(pages[b, h, o * rb:(o + 1) * rb], data[i, h])
+            touched[b, h, o * rb:(o + 1) * rb] = True
+            lo, hi = pages[b, h, noff + 2 * o], pages[b, h, noff + 2 * o + 1]
+            assert int(lo) | (int(hi) << 8) == int(norms[i, h, 0])
+            touched[b, h, noff + 2 * o:noff + 2 * o + 2] = True
+    assert np.all(pages[~touched] == 0xA5)
+
+
+def test_two_group_norm_plane_is_group_major():
+    _, _, km, _ = fmts()
+    bs = 16
+    rb, noff, tile = pg.tile_layout(km, bs)
+    pages = np.zeros((2, 1, tile), dtype=np.uint8)
+    x = np.random.default_rng(1).standard_normal((1, 1, 128))
+    pg.write_pages(x, np.array([16 + 5]), pages, km, bs)
+    _, norms = enc.encode_rows(x, km)
+    for g in range(2):
+        pos = noff + (g * bs + 5) * 2
+        assert int(pages[1, 0, pos]) | (int(pages[1, 0, pos + 1]) << 8) == int(norms[0, 0, g])
+
+
+def test_read_back_and_reconstruct():
+    k, v, km, _ = fmts()
+    bs, H = 16, 3
+    rng = np.random.default_rng(2)
+    n = 53
+    bt = np.array([4, 0, 6, 2], dtype=np.int32)        # 4 blocks cover 53 tokens
+    slots = bt[np.arange(n) // bs].astype(np.int64) * bs + np.arange(n) % bs
+    for f in (k, v, km):
+        rb, noff, tile = pg.tile_layout(f, bs)
+        pages = np.zeros((7, H, tile), dtype=np.uint8)
+        x = rng.standard_normal((n, H, 128))
+        pg.write_pages(x, slots, pages, f, bs)
+        idx, norms = enc.encode_rows(x, f)
+        for h in range(H):
+            ridx, rn = pg.read_rows(pages, bt[np.arange(n) // bs], np.arange(n) % bs, h, f, bs)
+            for g in range(f.num_groups):
+                np.testing.assert_array_equal(ridx[g], idx[g][:, h])
+            np.testing.assert_array_equal(rn, norms[:, h])
+            K = pg.reconstruct_sequence(pages, bt, n, h, f, bs)
+            ref = enc.dequantize_rotated([i[:, h] for i in idx], norms[:, h], f)
+            from oracle.rotation import inverse_rotate
+            np.testing.assert_allclose(K, inverse_rotate(ref, f.signs), atol=1e-15)
+            # reconstruction is close to the input (4-bit: ~10% relative)
+            rel = np.linalg.norm(K - x[:, h], axis=1) / np.linalg.norm(x[:, h], axis=1)
+            assert np.all(rel < {4: 0.2, 2: 0.55}[max(f.group_bits)])
+
+
+def test_write_errors():
+    k, _, _, _ = fmts()
+    bs = 16
+    _, _, tile = pg.tile_layout(k, bs)
+    pages = np.zeros((2, 1, tile), dtype=np.uint8)
+    x = np.zeros((2, 1, 128))
+    with pytest.raises(IndexError):
+        pg.write_pages(x, np.array([0, 32]), pages, k, bs)
+    with pytest.raises(IndexError):
+        pg.write_pages(x, np.array([-1, 3]), pages, k, bs)
+    with pytest.raises(ValueError):
+        pg.write_pages(x, np.array([3, 3]), pages, k, bs)
+    with pytest.raises(ValueError):
+        pg.write_pages(np.zeros((2, 1, 64)), np.array([0, 1]), pages, k, bs)
+    with pytest.raises(IndexError):
+        pg.reconstruct_sequence(pages, np.array([0, 5]), 20, 0, k, bs)
