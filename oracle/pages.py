@@ -10,9 +10,11 @@ pages are IndexErrors.
 Layout (readings R10, R11): pages are [num_blocks][num_kv_heads][tile].  A
 tile holds block_size rows of packed indices (the index plane, row `offset`
 at byte offset*row_bytes) followed by the norm plane, fp16 little-endian,
-group-major: the norm of group g for row `offset` sits at
-block_size*row_bytes + (g*block_size + offset)*2.  The tile is padded to a
-multiple of 16 bytes.
+group-major, with the 16 rows of a block in interleaved slots: the norm of
+group g for the row at in-block offset t sits at
+block_size*row_bytes + (g*block_size + norm_slot(t))*2, where
+norm_slot(t) = 4*(t % 4) + t // 4.  The tile is padded to a multiple of 16
+bytes.  Only block_size 16 is defined.
 """
 from __future__ import annotations
 
@@ -22,8 +24,15 @@ from .encode import Format, encode_rows, pack_row, unpack_row, dequantize_rotate
 from .rotation import inverse_rotate
 
 
+def norm_slot(t):
+    """Slot of in-block offset t (0..15) in a norm plane."""
+    return 4 * (np.asarray(t) % 4) + np.asarray(t) // 4
+
+
 def tile_layout(fmt: Format, block_size: int):
     """(row_idx_bytes, norm_plane_offset, tile_bytes)."""
+    if block_size != 16:
+        raise ValueError("block_size must be 16")
     rb = row_bytes(fmt)
     norm_off = block_size * rb
     raw = norm_off + block_size * fmt.num_groups * 2
@@ -59,7 +68,7 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
         for b in range(rb):
             pages[blk, h, off * rb + b] = data[:, h, b]
         for g in range(fmt.num_groups):
-            pos = norm_off + (g * block_size + off) * 2
+            pos = norm_off + (g * block_size + norm_slot(off)) * 2
             pages[blk, h, pos] = (norms[:, h, g] & 0xFF).astype(np.uint8)
             pages[blk, h, pos + 1] = (norms[:, h, g] >> 8).astype(np.uint8)
 
@@ -77,7 +86,7 @@ def read_rows(pages: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, head: 
     idx = unpack_row(data, fmt)
     norms = np.empty((len(blocks), fmt.num_groups), dtype=np.uint16)
     for g in range(fmt.num_groups):
-        pos = norm_off + (g * block_size + offsets) * 2
+        pos = norm_off + (g * block_size + norm_slot(offsets)) * 2
         lo = t[np.arange(len(blocks)), pos].astype(np.uint16)
         hi = t[np.arange(len(blocks)), pos + 1].astype(np.uint16)
         norms[:, g] = lo | (hi << 8)

@@ -45,10 +45,22 @@ def test_write_places_rows_at_slot_block_offset():
         for h in range(H):
             np.testing.assert_array_equal(pages[b, h, o * rb:(o + 1) * rb], data[i, h])
             touched[b, h, o * rb:(o + 1) * rb] = True
-            lo, hi = pages[b, h, noff + 2 * o], pages[b, h, noff + 2 * o + 1]
+            slot = 4 * (o % 4) + o // 4
+            lo, hi = pages[b, h, noff + 2 * slot], pages[b, h, noff + 2 * slot + 1]
             assert int(lo) | (int(hi) << 8) == int(norms[i, h, 0])
-            touched[b, h, noff + 2 * o:noff + 2 * o + 2] = True
+            touched[b, h, noff + 2 * slot:noff + 2 * slot + 2] = True
     assert np.all(pages[~touched] == 0xA5)
+
+
+def test_norm_slots_are_interleaved():
+    """Slot of offset t is 4*(t%4) + t//4: a permutation of 0..15 in which
+    offsets q, q+4, q+8, q+12 occupy four consecutive slots."""
+    t = np.arange(16)
+    sl = pg.norm_slot(t)
+    assert sorted(sl.tolist()) == list(range(16))
+    for q in range(4):
+        assert sl[[q, q + 4, q + 8, q + 12]].tolist() == [4 * q, 4 * q + 1, 4 * q + 2, 4 * q + 3]
+    assert sl.tolist()[:6] == [0, 4, 8, 12, 1, 5]
 
 
 def test_two_group_norm_plane_is_group_major():
@@ -60,7 +72,7 @@ def test_two_group_norm_plane_is_group_major():
     pg.write_pages(x, np.array([16 + 5]), pages, km, bs)
     _, norms = enc.encode_rows(x, km)
     for g in range(2):
-        pos = noff + (g * bs + 5) * 2
+        pos = noff + (g * bs + 4 * 1 + 1) * 2      # offset 5 -> slot 4*(5%4) + 5//4 = 5
         assert int(pages[1, 0, pos]) | (int(pages[1, 0, pos + 1]) << 8) == int(norms[0, 0, g])
 
 
