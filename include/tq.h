@@ -1,0 +1,244 @@
+/*
+ * tq.h -- C ABI of libtq: quantise-on-write into packed KV pages and paged
+ * decode attention that consumes the packed pages directly (MI355X, gfx950).
+ *
+ * The method: each cached K or V row is rotated (seeded +-1 signs, then a
+ * Walsh-Hadamard transform scaled by 1/sqrt(d)), split into one or two
+ * channel groups, each group stored as an fp16 vector norm plus per-channel
+ * indices into a Lloyd-Max codebook, packed LSB-first into uint8 pages.
+ *
+ * Sources, cited by page title and section:
+ *   [D] TurboQuant documentation, "Design" page: "System Invariants",
+ *       "Data Ownership", "Serving Route Design", "Format Strategy",
+ *       "Recipe Strategy", "Error Model".
+ *   [S] "TurboQuant Inference Server" README: "What it does",
+ *       "Architecture notes" (Lloyd-Max codebooks computed once on the CPU).
+ *   [T] "Tattletale" README, "Highlights" (random Hadamard rotation plus
+ *       codebooks).
+ *
+ * Ownership and threading ([D "Data Ownership"]: the cache owner owns the
+ * persistent bytes, the attention path only consumes them):
+ *   - The caller allocates every buffer (pages, q, out, lse, workspace,
+ *     slot_mapping, block tables, context lengths, error words).  The library
+ *     allocates nothing and keeps no state between calls.
+ *   - Pointers named "device" must be device memory; "host" pointers are
+ *     read during the call only.
+ *   - Every GPU call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Buffers must stay valid until that work completes.
+ *   - Page pools are never cleared by the library; bytes of rows that were
+ *     never written are unspecified.
+ *   - Calls are thread-safe; tq_last_error() is per thread.
+ *
+ * Errors ([D "Error Model"]; a Python binding maps them to exceptions):
+ *   TQ_ERR_VALUE        bad shapes, dtypes, bit widths, group sizes,
+ *                       malformed codebook / signs / channel list, NULL
+ *                       required pointer, workspace too small  (ValueError)
+ *   TQ_ERR_INDEX        slot or block-table entry outside the pool; for
+ *                       device-resident data this is reported through the
+ *                       optional device error word        (IndexError)
+ *   TQ_ERR_UNSUPPORTED_FORMAT  a valid format no kernel serves; the library
+ *                       never falls back to a dense path
+ *                       ([D "System Invariants", "Serving Route Design"])
+ *   TQ_ERR_NOT_FOUND    reserved for metadata loaders   (FileNotFoundError)
+ *   TQ_ERR_DEVICE       HIP launch or runtime failure
+ *
+ * Device error word: `int32_t dev_err[2]` in device memory, zeroed by the
+ * caller.  A kernel that meets an out-of-range slot or block-table entry
+ * sets dev_err[0] = TQ_ERR_INDEX (if it was 0) and dev_err[1] = the position
+ * of that entry (see each call); which entry is recorded when several are
+ * bad is unspecified.  The offending row is not written / the offending
+ * block is skipped; nothing is read or written out of bounds.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* tq_stream_t; /* same type as hipStream_t */
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_VALUE = 1,
+  TQ_ERR_INDEX = 2,
+  TQ_ERR_UNSUPPORTED_FORMAT = 3,
+  TQ_ERR_NOT_FOUND = 4,
+  TQ_ERR_DEVICE = 5
+} tq_status;
+
+typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+#define TQ_MAX_HEAD_DIM 128
+#define TQ_BLOCK_SIZE 16
+
+/*
+ * One tensor's storage format (K and V each get their own: [D "System
+ * Invariants"], "Key and value formats are independent").  Host struct,
+ * read during the call.
+ *
+ *   head_dim        64 or 128.
+ *   num_groups      1 or 2.  Two groups split the rotated channels into a
+ *                   high-precision and a low-precision half, chosen by
+ *                   metadata, never guessed at run time ([D "Recipe
+ *                   Strategy"]).  Each group has head_dim / num_groups
+ *                   channels.
+ *   group_bits      bits per index of each group: 2, 3 or 4.
+ *   group_channels  rotated-domain channel ids: group 0 ascending, then
+ *                   group 1 ascending (a permutation of 0..head_dim-1); the
+ *                   identity for one group.
+ *   codebook        per group, 2^bits fp16 bit patterns: finite, strictly
+ *                   ascending unit-variance levels (entries beyond 2^bits
+ *                   are ignored).  tq_lloyd_max_codebook() fills them.
+ *   signs           +1 / -1 per channel: the seeded signs of the rotation.
+ *
+ * Encoding of a row x (head_dim values), per group G of m channels:
+ *   w   = H (signs * x)           Sylvester Walsh-Hadamard, natural order,
+ *                                 fp64 butterflies h = 1, 2, ..., d/2
+ *   ss  = pairwise-tree sum of w_j^2 over G (adjacent pairs first), fp64
+ *   norm= fp16 round-to-nearest-even of sqrt(ss / head_dim)
+ *   T_i = fp64 (t_i * sqrt(ss / m)), t_i = midpoint of levels i, i+1
+ *   idx = number of thresholds T_i strictly below w_j
+ *   (ss == 0: norm +0 and every index 2^bits/2 - 1)
+ * Decoding: rotated value of channel j in G is norm * codebook[idx] / sqrt(m).
+ */
+typedef struct tq_format {
+  int32_t head_dim;
+  int32_t num_groups;
+  int32_t group_bits[2];
+  uint8_t group_channels[TQ_MAX_HEAD_DIM];
+  uint16_t codebook[2][16];
+  int8_t signs[TQ_MAX_HEAD_DIM];
+} tq_format;
+
+/*
+ * Page layout ([D "Serving Route Design"]: slot -> physical block -> token
+ * offset -> packed row bytes, with block = slot / 16 and offset = slot % 16):
+ *   pages  : [num_blocks][num_kv_heads][tile_bytes] uint8, device memory.
+ *   tile   : index plane, 16 rows of row_index_bytes (row `offset` at byte
+ *            offset * row_index_bytes; each group's indices packed LSB-first,
+ *            group 0 first), then the norm plane: fp16 little-endian,
+ *            group-major, the norm of group g of the row at in-block offset t
+ *            stored at  16*row_index_bytes + 2*(16*g + 4*(t % 4) + t / 4).
+ *            The tile is padded to a multiple of 16 bytes.
+ */
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* tq_last_error(void);
+
+/*
+ * Fill out_f16[0 .. 2^bits) with the fp16 Lloyd-Max levels of a unit
+ * Gaussian (ascending, exactly symmetric), computed on the host in extended
+ * precision and rounded to nearest even ([S "Architecture notes"]: Lloyd-Max
+ * codebooks are computed once on the CPU).  bits in 1..4.
+ * Errors: VALUE for bits out of range or a NULL pointer.
+ */
+tq_status tq_lloyd_max_codebook(int32_t bits, uint16_t* out_f16 /* host */);
+
+/* Check a format descriptor (VALUE on any malformed field). */
+tq_status tq_format_check(const tq_format* fmt /* host */);
+
+/*
+ * Byte math of a format ([D "Serving Route Design"]).  block_size must be 16.
+ *   row_index_bytes = sum over groups of m * bits / 8
+ *   tile_bytes      = roundup16(16 * row_index_bytes + 16 * num_groups * 2)
+ */
+tq_status tq_tile_bytes(const tq_format* fmt, int32_t block_size, int32_t* row_index_bytes /* host out */,
+                        int32_t* tile_bytes /* host out */);
+
+/*
+ * Quantise-on-write ([D "Serving Route Design"]: the serving route writes
+ * packed rows into persistent pages).  For token i and kv head h the row
+ * k[i][h][0..head_dim) (resp. v) is encoded with kfmt (resp. vfmt) and stored
+ * at block slot_mapping[i] / 16, offset slot_mapping[i] % 16 of head h.
+ *
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim] contiguous,
+ *                 in_dtype TQ_BF16 or TQ_F32.  Either may be NULL (then its
+ *                 pages and format are ignored), not both.
+ *   slot_mapping  device int64 [num_tokens]; slots must be distinct within a
+ *                 call (documented precondition, not checked).
+ *   k_pages/v_pages  device pools [num_blocks][num_kv_heads][tile_bytes].
+ *   dev_err       device int32[2] or NULL: a slot outside
+ *                 [0, num_blocks*16) records (TQ_ERR_INDEX, token index) and
+ *                 that token's rows are not written.
+ * Status: VALUE (shapes, dtype, formats, NULLs), UNSUPPORTED_FORMAT
+ * (block_size != 16), DEVICE (launch failure), else OK.
+ */
+tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype, int64_t num_tokens,
+                      int32_t num_kv_heads, const int64_t* slot_mapping, uint8_t* k_pages,
+                      uint8_t* v_pages, int64_t num_blocks, int32_t block_size, const tq_format* kfmt,
+                      const tq_format* vfmt, int32_t* dev_err, tq_stream_t stream);
+
+/*
+ * Workspace of tq_decode_paged: num_seqs * num_q_heads * num_splits *
+ * (head_dim + 1) * 4 bytes when num_splits > 1, else 0.  It depends on the
+ * runtime shape only, never on context length ([D "Serving Route Design"]:
+ * "keep workspace bounded by runtime shape").
+ */
+tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t num_splits, uint64_t* bytes /* host out */);
+
+/*
+ * Paged decode attention over packed pages ([D "Serving Route Design"]: block
+ * tables map logical to physical blocks, K rows are read inside the score
+ * computation and V rows are dequantised inside the accumulation; no dense
+ * K/V history is ever built).
+ *
+ *   q            device [num_seqs][num_q_heads][head_dim], q_dtype BF16/F32.
+ *   q head h attends with kv head h / (num_q_heads / num_kv_heads).
+ *   block_tables device int32 [num_seqs][max_blocks_per_seq]; entry b of
+ *                sequence s is the physical block of its tokens 16b..16b+15.
+ *                Entries at or beyond ceil(context_lens[s] / 16) are not read.
+ *   context_lens device int32 [num_seqs]: cached tokens per sequence (the
+ *                current token included: write it first).
+ *   scale        softmax scale applied to q.k.
+ *   num_splits   P >= 1.  The logical blocks of every sequence are cut into
+ *                chunks of C = ceil(max_blocks_per_seq / P) blocks; each chunk
+ *                yields a partial (o_p, lse_p) and the partials are merged by
+ *                log-sum-exp inside this call.  workspace must hold
+ *                tq_decode_workspace_bytes() bytes (device, may be NULL when
+ *                P == 1).
+ *   out          device [num_seqs][num_q_heads][head_dim], out_dtype BF16/F32.
+ *   lse          device float [num_seqs][num_q_heads] or NULL: natural-log
+ *                sum of exp(scale * q.k) over the context.
+ *   dev_err      device int32[2] or NULL: a block-table entry outside
+ *                [0, num_blocks) records (TQ_ERR_INDEX, s*max_blocks_per_seq+b)
+ *                and the block is skipped; a context length outside
+ *                [0, 16*max_blocks_per_seq] records (TQ_ERR_INDEX, -1 - s) and
+ *                is clamped.
+ * A sequence with context length 0 gets out = 0 and lse = -inf.
+ * Served formats (else UNSUPPORTED_FORMAT): head_dim 64 or 128; K one group
+ * of 4 or 2 bits, or two groups of 4 + 3 bits; V one group of 4 or 2 bits;
+ * num_q_heads / num_kv_heads in 1..8; block_size 16.
+ */
+tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
+                          int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const tq_format* kfmt, const tq_format* vfmt, float scale,
+                          int32_t num_splits, void* workspace, uint64_t workspace_bytes, void* out,
+                          tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream);
+
+/*
+ * Log-sum-exp merge of split partials (flash-decoding):
+ *   lse = M + ln sum_p exp(lse_p - M),  out = sum_p exp(lse_p - lse) * o_p
+ *   part_out  device float [num_seqs][num_heads][num_splits][head_dim]
+ *             (normalised partial outputs, original domain)
+ *   part_lse  device float [num_seqs][num_heads][num_splits]; -inf marks an
+ *             empty partial.  All partials empty: out = 0, lse = -inf.
+ *   out       device [num_seqs][num_heads][head_dim], BF16 or F32.
+ *   lse       device float [num_seqs][num_heads] or NULL.
+ */
+tq_status tq_split_merge(const float* part_out, const float* part_lse, int32_t num_seqs,
+                         int32_t num_heads, int32_t num_splits, int32_t head_dim, void* out,
+                         tq_dtype out_dtype, float* lse, tq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

