@@ -1,0 +1,290 @@
+"""Benchmark of one decode layer-step over a packed, paged KV cache.
+
+A step = quantise-on-write of the current token of every sequence
+(tq_write_kv) + paged decode attention over the whole context
+(tq_decode_paged, split-K with its merge), for one layer.  The timed loop
+cycles over several layers' caches whose pools together exceed the 256 MB
+Infinity Cache, so every step streams its pages from HBM, as a real
+multi-layer decode does.
+
+Default workload: the Llama-3-8B-shaped layer (batch 32, 32 q / 8 kv heads,
+d = 128, context lengths uniform in [1024, 8192], K4/V4).  The
+Llama-3.1-70B-shaped layer share (batch 8, 64 q / 8 kv heads, context
+32768, K4/V2) is measured in the same run and reported under "secondary".
+
+Prints one JSON line.  Inputs are seeded synthetic tensors of the
+workloads' shapes and distributions (data: "synthetic").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+SPLITS = {2: 16, 4: 16, 5: 64, 1: 1}
+LAYERS = {2: 3, 4: 2, 5: 3, 1: 2}
+NAMES = {"8b": 2, "70b": 4, "long": 5, "tiny": 1}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, kf, vf):
+    """Bytes the method must move in one layer-step (decode + write)."""
+    import numpy as np
+    krow = kf.tile_bytes()[0] + 2 * kf.num_groups
+    vrow = vf.tile_bytes()[0] + 2 * vf.num_groups
+    ctx = w.context_lens.astype(np.int64)
+    cache = int(ctx.sum()) * w.num_kv_heads * (krow + vrow)
+    esz = 2 if w.q_dtype == "bf16" else 4
+    q = w.num_seqs * w.num_q_heads * w.head_dim * esz
+    out = w.num_seqs * w.num_q_heads * w.head_dim * (2 if w.out_dtype == "bf16" else 4)
+    lse = w.num_seqs * w.num_q_heads * 4
+    bt = int(((ctx + 15) // 16).sum()) * 4 + w.num_seqs * 4
+    decode = cache + q + out + lse + bt
+    write = w.num_seqs * w.num_kv_heads * (2 * w.head_dim * esz + krow + vrow) + w.num_seqs * 8
+    return decode, write
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "tq_internal.h"):
+        h.update(open(os.path.join(ROOT, "quantized_paged_kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(tag):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_{tag}_counters.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_sha") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, index, layers=None, splits=None, device="cuda"):
+        import numpy as np
+        import torch
+        import quantized_paged_kv_amd as tq
+        import workloads as wl
+        self.tq, self.torch, self.np = tq, torch, np
+        self.w = w = wl.decode_workload(index)
+        self.index = index
+        self.P = splits or SPLITS[index]
+        self.L = layers or LAYERS[index]
+        kf = tq.Format(w.head_dim, w.kfmt.group_bits, w.kfmt.signs, w.kfmt.group_channels)
+        vf = tq.Format(w.head_dim, w.vfmt.group_bits, w.vfmt.signs, w.vfmt.group_channels)
+        self.kf, self.vf = kf, vf
+        dt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+        self.pools = [(tq.alloc_pages(w.num_blocks, w.num_kv_heads, kf), tq.alloc_pages(w.num_blocks, w.num_kv_heads, vf))
+                      for _ in range(self.L)]
+        err = tq.new_error_word()
+        last_k, last_v, last_slot = [], [], []
+        for s in range(w.num_seqs):
+            n = int(w.context_lens[s])
+            t = np.arange(n)
+            sl = torch.from_numpy(w.block_tables[s, t // 16].astype(np.int64) * 16 + t % 16).cuda()
+            xk = self._dev(wl.kv_values(w, "k", s), w.in_dtype)
+            xv = self._dev(wl.kv_values(w, "v", s), w.in_dtype)
+            for kp, vp in self.pools:
+                tq.write_kv(xk, xv, sl, kp, vp, kf, vf, dev_err=err)
+            last_k.append(xk[-1:])
+            last_v.append(xv[-1:])
+            last_slot.append(sl[-1:])
+            del xk, xv
+        tq.raise_device_error(err, "cache build")
+        log(f"cache built: {w.name}, {self.L} layer pools")
+        # the current token of every sequence (the last cached position)
+        self.new_k = torch.cat(last_k).contiguous()
+        self.new_v = torch.cat(last_v).contiguous()
+        self.new_slots = torch.cat(last_slot).contiguous()
+        self.q = self._dev(wl.q_values(w), w.q_dtype)
+        self.bt = torch.from_numpy(w.block_tables).cuda()
+        self.cl = torch.from_numpy(w.context_lens).cuda()
+        od = torch.bfloat16 if w.out_dtype == "bf16" else torch.float32
+        self.out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=od, device="cuda")
+        self.lse = torch.empty((w.num_seqs, w.num_q_heads), dtype=torch.float32, device="cuda")
+        nbytes = tq.workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, self.P)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        self.decode_bytes, self.write_bytes = algorithmic_bytes(w, kf, vf)
+        torch.cuda.synchronize()
+
+    def _dev(self, x, dtype):
+        import workloads as wl
+        np, torch = self.np, self.torch
+        if dtype == "bf16":
+            return torch.from_numpy(wl.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+    def write(self, layer):
+        kp, vp = self.pools[layer]
+        self.tq.write_kv(self.new_k, self.new_v, self.new_slots, kp, vp, self.kf, self.vf)
+
+    def decode(self, layer):
+        kp, vp = self.pools[layer]
+        w = self.w
+        self.tq.decode_paged(self.q, kp, vp, self.bt, self.cl, self.kf, self.vf, w.scale, num_splits=self.P,
+                             out=self.out, lse=self.lse, workspace=self.ws)
+
+    def step(self, i):
+        layer = i % self.L
+        self.write(layer)
+        self.decode(layer)
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # per-launch decode duration with HIP events on the launch stream
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            layer = (warmup + i) % self.L
+            self.write(layer)
+            ev[i][0].record()
+            self.decode(layer)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        dec_ms = sorted(a.elapsed_time(b) for a, b in ev)
+        return wall / steps * 1e3, dec_ms
+
+
+def cpu_baseline(index, budget_s=12.0):
+    """The oracle (as it stands) decoding whole sequences of the workload on
+    the host: dense reconstruction from oracle-written pages + fp64
+    attention for every q head.  Pages are prepared untimed."""
+    import numpy as np
+    import oracle
+    from oracle import attn as oatt
+    from oracle import pages as opg
+    import workloads as wl
+    w = wl.decode_workload(index)
+    kof = oracle.Format.make(w.head_dim, w.kfmt.group_bits, w.kfmt.signs, w.kfmt.group_channels)
+    vof = oracle.Format.make(w.head_dim, w.vfmt.group_bits, w.vfmt.signs, w.vfmt.group_channels)
+    q = wl.q_values(w)
+    G = w.num_q_heads // w.num_kv_heads
+    krow = opg.tile_layout(kof, 16)[0] + 2 * kof.num_groups
+    vrow = opg.tile_layout(vof, 16)[0] + 2 * vof.num_groups
+    total_bytes, total_t, done = 0, 0.0, []
+    for s in range(w.num_seqs):
+        n = int(w.context_lens[s])
+        bt = np.arange((n + 15) // 16)
+        sl = bt[np.arange(n) // 16] * 16 + np.arange(n) % 16
+        xk, xv = wl.kv_values(w, "k", s), wl.kv_values(w, "v", s)
+        pools = []
+        for h in range(w.num_kv_heads):
+            Kp = np.zeros((len(bt), 1, opg.tile_layout(kof, 16)[2]), np.uint8)
+            Vp = np.zeros((len(bt), 1, opg.tile_layout(vof, 16)[2]), np.uint8)
+            for a in range(0, n, 16384):
+                opg.write_pages(xk[a:a + 16384, h:h + 1], sl[a:a + 16384], Kp, kof, 16)
+                opg.write_pages(xv[a:a + 16384, h:h + 1], sl[a:a + 16384], Vp, vof, 16)
+            pools.append((Kp, Vp))
+        t0 = time.perf_counter()
+        for h in range(w.num_kv_heads):
+            Kp, Vp = pools[h]
+            K = opg.reconstruct_sequence(Kp, bt, n, 0, kof, 16)
+            V = opg.reconstruct_sequence(Vp, bt, n, 0, vof, 16)
+            for g in range(G):
+                oatt.attention(q[s, h * G + g].astype(np.float64), K, V, w.scale)
+        total_t += time.perf_counter() - t0
+        total_bytes += n * w.num_kv_heads * (krow + vrow)
+        done.append(s)
+        if total_t >= budget_s:
+            break
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} whole sequence(s) of the workload ({sum(int(w.context_lens[s]) for s in done)} "
+                      f"tokens x {w.num_kv_heads} kv heads x {w.num_q_heads // w.num_kv_heads} q heads each): "
+                      f"dense reconstruction + fp64 attention, {total_t:.1f} s on {cores} allowed cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="8b", choices=sorted(NAMES))
+    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode shards by kv head or "
+              f"sequence with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    index = NAMES[args.workload]
+    b = Bench(index, splits=args.splits)
+    ms_step, dec_ms = b.timed(args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step")
+    w = b.w
+    step_bytes = b.decode_bytes + b.write_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    achieved = b.decode_bytes / (dec_avg * 1e-3) / 1e9
+    tag = args.workload
+    traffic = stored_traffic(tag)
+    result = {
+        "metric": "tq_decode_paged HBM GB/s (% of peak) and us/layer-step at 8B/70B shapes",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16-mfma/fp32-acc over u8 pages", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "context_tokens": int(w.context_lens.sum()),
+                   "k_bits": w.kfmt.group_bits, "v_bits": w.vfmt.group_bits, "num_splits": b.P,
+                   "layers_cycled": b.L, "step": "tq_write_kv(current token) + tq_decode_paged",
+                   "parallelism": "single GPU"},
+        "us_per_layer_step": round(ms_step * 1e3, 2),
+        "decode_us": {"avg": round(dec_avg * 1e3, 2), "p10": round(dec_ms[len(dec_ms) // 10] * 1e3, 2),
+                      "p50": round(dec_ms[len(dec_ms) // 2] * 1e3, 2), "p90": round(dec_ms[9 * len(dec_ms) // 10] * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "tq_decode_paged (decode kernel + split merge)",
+                     "algorithmic_bytes_per_launch": b.decode_bytes},
+    }
+    del b
+    torch.cuda.empty_cache()
+    if not args.no_secondary and index == 2:
+        b4 = Bench(4)
+        ms4, d4 = b4.timed(max(10, args.steps // 2), args.warmup)
+        log(f"secondary timed: {ms4 * 1e3:.1f} us/step")
+        a4 = sum(d4) / len(d4)
+        result["secondary"] = {"workload": b4.w.name, "us_per_layer_step": round(ms4 * 1e3, 2),
+                               "decode_us_avg": round(a4 * 1e3, 2),
+                               "decode_GBs": round(b4.decode_bytes / (a4 * 1e-3) / 1e9, 1),
+                               "frac_of_peak": round(b4.decode_bytes / (a4 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                               "num_splits": b4.P, "traffic": stored_traffic("70b")}
+        del b4
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(index)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

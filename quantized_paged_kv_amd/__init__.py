@@ -48,6 +48,11 @@ class tq_format(ctypes.Structure):
 
 
 def _load():
+    # torch first: its bundled HIP runtime is registered under the soname that
+    # libtq.so asks for, so libtq binds to that same runtime instance (the one
+    # that owns torch's device memory and stream handles) instead of loading a
+    # second copy of the runtime.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_paged_kv_amd._build`")
     lib = ctypes.CDLL(LIB_PATH)

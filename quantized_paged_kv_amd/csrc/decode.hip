@@ -7,13 +7,20 @@
 // [D "System Invariants"]: production routes consume packed history (no dense
 // K/V tensor is ever formed); unsupported formats raise.
 //
-// Work decomposition.  One workgroup (8 waves) owns one item = (sequence,
-// kv head, chunk of C logical blocks); the 8 waves take the chunk's blocks
-// round-robin, each keeping its own online-softmax state, and merge through
-// LDS at the end.  Items are numbered sequence-major over the chunks that a
-// sequence actually has, so no workgroup is spent on empty chunks, and the
-// workgroup-to-item map places the kv heads of one chunk on one XCD (the
-// heads of a physical block are adjacent in the pool and share cache lines).
+// Work decomposition (balanced split-K).  The work is the list of
+// (sequence, kv head, logical block) triples, ordered sequence-major, then
+// kv head, then block; a "segment" is the run of one (sequence, kv head).
+// The grid is two persistent workgroups per CU and workgroup w owns the
+// contiguous range [w*R, (w+1)*R) of that list, so every workgroup gets the
+// same number of blocks whatever the context lengths.  A workgroup walks the
+// pieces of the segments its range covers; a segment that lies inside one
+// range is finished there and written out directly, a segment cut by range
+// boundaries leaves one partial (o, lse) per piece in the workspace and the
+// merge kernel combines them.  R is at least ceil(max_blocks / (P - 1)), so
+// no segment has more than P pieces (P = num_splits, the workspace bound).
+//
+// Inside a piece the 8 waves take the blocks round-robin, each with its own
+// online-softmax state; the states are merged through LDS at the end.
 //
 // Inner loop (per wave, per 16-token block), all in the rotated domain:
 //   q.K:  v_mfma_f32_16x16x32_f16, A = dequantised K rows (16 tokens x 32
@@ -26,11 +33,15 @@
 //         that hold that head's 16 scores; rescale only when the max grows.
 //   P.V:  v_mfma_f32_16x16x16_f16, A = dequantised V (dims x tokens), B =
 //         p * (V norm) in fp16, accumulators fp32.
+// Tile loads for block i+1 are issued before block i is computed (two
+// register buffers used alternately, loads never conditional).
 // Codebook lookups use byte-indexed LDS tables replicated across banks
 // (one v_perm builds the address from a packed byte and the lane's copy).
-// Epilogue: inverse rotation of the output once per head (Walsh-Hadamard
-// across the wave, signs, 1/sqrt(d)), LDS merge of the 8 wave states, then
-// either the final output or a split partial.
+// LDS per workgroup stays within 80 KB so that two workgroups fit a CU.
+// Epilogue: LDS tree merge of the 8 wave states, inverse rotation of the
+// output once per head (Walsh-Hadamard across the wave, signs, 1/sqrt(d)).
+#include <mutex>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -45,8 +56,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kLutBytes = 65536;    // 256 entries x 256 B (two halves)
-constexpr int kLut3Bytes = 8192;    // 64 entries x 32 copies x 4 B
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLut3Bytes = 4096;    // 64 entries x 16 copies x 4 B
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum KKind { K4 = 0, K2 = 1, KM43 = 2 };
@@ -64,9 +74,9 @@ struct DecodeParams {
   float* part_lse;   // [S][Hq][P]
   int32_t* dev_err;
   int64_t num_blocks;
-  int32_t S, Hq, Hkv, G, max_blocks, P, C;
+  int32_t S, Hq, Hkv, G, max_blocks, P;
+  int32_t n_wg;      // grid size (persistent workgroups)
   int32_t k_tile, v_tile, k_norm_off, v_norm_off;
-  int32_t n_items_bound;
   float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K))
   float v_mul;       // 1 / sqrt(m_V)
   uint32_t v_signs[4];
@@ -95,8 +105,6 @@ __device__ __forceinline__ uint2 lds_u64(const uint8_t* lds, uint32_t addr) {
   return *reinterpret_cast<const uint2*>(lds + addr);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   const uint32_t b = __float_as_uint(x);
   if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
@@ -107,8 +115,9 @@ __device__ __forceinline__ float row_ror8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ uint32_t half2_bits(_Float16 lo, _Float16 hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+__device__ __forceinline__ float half_at(uint2 w, int e) {
+  const uint32_t d = (e >> 1) ? w.y : w.x;
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> (16 * (e & 1))));
 }
 
 template <int D, int KK, int VK>
@@ -119,7 +128,9 @@ struct Cfg {
   static constexpr int VROW = VK == V4 ? D / 2 : D / 4;
   static constexpr int VLANE = VK == V4 ? D / 32 : D / 64;  // bytes per lane per token in V
   static constexpr bool MIXED = KK == KM43;
-  static constexpr int LDS_BYTES = kLutBytes + (MIXED ? kLut3Bytes : 0);
+  static constexpr int LDS_LUT = kLutBytes + (MIXED ? kLut3Bytes : 0);
+  static constexpr int NSLOT = MIXED ? 2 : 3;             // merge slots (wave states); LDS <= 80 KB
+  static constexpr int SLOT_FLOATS = 8 * D + 16;          // O[8][D], m[8], l[8]
 };
 
 // Per-block raw loads of one wave.
@@ -133,186 +144,206 @@ struct Tile {
 };
 
 template <int D, int KK, int VK>
-__device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, const uint8_t* kt, const uint8_t* vt, int tokK, int c,
-                                          int a, int i, int k_norm_off, int v_norm_off) {
+__device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, const uint8_t* kt, const uint8_t* vt, uint32_t k_off,
+                                          uint32_t klo_off, uint32_t kn_off, uint32_t v_off, uint32_t vn_off) {
   using C = Cfg<D, KK, VK>;
-  if constexpr (KK == K4) {
-    if constexpr (D == 128) {
-      const uint4 x = *reinterpret_cast<const uint4*>(kt + tokK * C::KROW + 16 * c);
-      t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
-    } else {
-      const uint2 x = *reinterpret_cast<const uint2*>(kt + tokK * C::KROW + 8 * c);
-      t.k[0] = x.x; t.k[1] = x.y;
-    }
-  } else if constexpr (KK == K2) {
-    if constexpr (D == 128) {
-      const uint2 x = *reinterpret_cast<const uint2*>(kt + tokK * C::KROW + 8 * c);
-      t.k[0] = x.x; t.k[1] = x.y;
-    } else {
-      t.k[0] = *reinterpret_cast<const uint32_t*>(kt + tokK * C::KROW + 4 * c);
-    }
+  if constexpr (KK == K4 && D == 128) {
+    const uint4 x = *reinterpret_cast<const uint4*>(kt + k_off);
+    t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
+  } else if constexpr ((KK == K4 && D == 64) || (KK != K4 && D == 128)) {
+    const uint2 x = *reinterpret_cast<const uint2*>(kt + k_off);
+    t.k[0] = x.x; t.k[1] = x.y;
   } else {
-    constexpr int HB = D / 4;             // high group bytes per row (4-bit, D/2 channels)
-    constexpr int LB = 3 * D / 64;        // low group bytes per lane (3-bit, D/8 channels)
-    if constexpr (D == 128) {
-      const uint2 x = *reinterpret_cast<const uint2*>(kt + tokK * C::KROW + 8 * c);
-      t.k[0] = x.x; t.k[1] = x.y;
-    } else {
-      t.k[0] = *reinterpret_cast<const uint32_t*>(kt + tokK * C::KROW + 4 * c);
-    }
-    const int lo_off = tokK * C::KROW + HB + LB * c;
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(kt + (lo_off & ~3));
-    t.k_lo[0] = w[0];
-    t.k_lo[1] = w[1];
+    t.k[0] = *reinterpret_cast<const uint32_t*>(kt + k_off);
   }
-  t.kn[0] = *reinterpret_cast<const uint2*>(kt + k_norm_off + 8 * a);
-  if constexpr (C::MIXED) t.kn[1] = *reinterpret_cast<const uint2*>(kt + k_norm_off + 32 + 8 * a);
+  if constexpr (C::MIXED) {
+    const uint2 w = *reinterpret_cast<const uint2*>(kt + klo_off);
+    t.k_lo[0] = w.x;
+    t.k_lo[1] = w.y;
+  }
+  t.kn[0] = *reinterpret_cast<const uint2*>(kt + kn_off);
+  if constexpr (C::MIXED) t.kn[1] = *reinterpret_cast<const uint2*>(kt + kn_off + 32u);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const uint8_t* row = vt + (a + 4 * r) * C::VROW;
-    if constexpr (C::VLANE == 4) t.v[r] = *reinterpret_cast<const uint32_t*>(row + 4 * i);
-    else if constexpr (C::VLANE == 2) t.v[r] = *reinterpret_cast<const uint16_t*>(row + 2 * i);
-    else t.v[r] = row[i];
+    const uint8_t* row = vt + v_off + (uint32_t)(4 * r * C::VROW);
+    if constexpr (C::VLANE == 4) t.v[r] = *reinterpret_cast<const uint32_t*>(row);
+    else if constexpr (C::VLANE == 2) t.v[r] = *reinterpret_cast<const uint16_t*>(row);
+    else t.v[r] = *row;
   }
-  t.vn = *reinterpret_cast<const uint2*>(vt + v_norm_off + 8 * a);
+  t.vn = *reinterpret_cast<const uint2*>(vt + vn_off);
+}
+
+__device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
+
+// A value known to be the same in every lane, moved to a scalar register so
+// that everything derived from it (addresses above all) stays scalar.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Wave-wide: total work W = H_kv * sum of block counts (all lanes get it).
+__device__ int total_work(const int32_t* context_lens, int S, int Hkv, int max_blocks, int lane) {
+  int tot = 0;
+  const int cap = max_blocks * 16;
+  for (int base = 0; base < S; base += 64) {
+    const int sq = base + lane;
+    int v = sq < S ? (clamp_ctx(context_lens[sq], cap) + 15) >> 4 : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    tot += uni(v);
+  }
+  return tot * Hkv;
+}
+
+// Wave-wide: the segment that contains work position pos (pos < W).
+__device__ void locate(const DecodeParams& p, int lane, int pos, int& s, int& kvh, int& blk, int& nb_s) {
+  const int cap = p.max_blocks * 16;
+  int before = 0;
+  s = -1;
+  kvh = blk = nb_s = 0;
+  for (int base = 0; base < p.S && s < 0; base += 64) {
+    const int sq = base + lane;
+    int cnt = 0;
+    if (sq < p.S) cnt = ((clamp_ctx(p.context_lens[sq], cap) + 15) >> 4) * p.Hkv;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - cnt;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(sq < p.S && pos >= before + excl && pos < before + incl);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      s = base + src;
+      const int r = pos - before - uni(__shfl(excl, src));
+      nb_s = uni(__shfl(cnt, src)) / p.Hkv;
+      kvh = r / nb_s;
+      blk = r % nb_s;
+    }
+    before += uni(__shfl(incl, 63));
+  }
+}
+
+// Wave-wide: the first segment start at or after work position x (W if none).
+__device__ int snap_to_segment(const DecodeParams& p, int lane, int x, int W) {
+  if (x >= W) return W;
+  int s, kvh, blk, nb;
+  locate(p, lane, x, s, kvh, blk, nb);
+  return blk == 0 ? x : x - blk + nb;
+}
+
+// Blocks per workgroup range: an even share of the work and, when segments
+// may be split (P > 1), at least ceil(max_blocks / (P - 1)) so that no
+// segment has more than P pieces.  With P == 1 the range boundaries are
+// moved to segment starts (see snap_to_segment) and no segment is split.
+__device__ __forceinline__ int range_len(int W, int n_wg, int max_blocks, int P) {
+  int R = (W + n_wg - 1) / n_wg;
+  if (R < 1) R = 1;
+  if (P == 1) return R;
+  const int need = (max_blocks + P - 2) / (P - 1);
+  return R > need ? R : need;
 }
 
 template <int D, int KK, int VK>
 __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
   using C = Cfg<D, KK, VK>;
-  constexpr int R = C::R;
+  constexpr int R4 = 4 * C::R;   // output dims per lane
   constexpr int NQK = C::NQK;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_BYTES];
-  __shared__ float qbuf[8][D];
-  __shared__ int qexp[8];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_LUT];
+  __shared__ __attribute__((aligned(16))) float mrg[C::NSLOT * C::SLOT_FLOATS];  // q buffer, then merge slots
+  __shared__ uint32_t s_par[64];
+  __shared__ int s_qexp[8];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uni(tid >> 6);
   const int lane = tid & 63;
 
-  // ---- which item: XCD-aware order, then sequence-major scan of chunk counts
-  const int nwg = gridDim.x;
-  const int per_xcd = (nwg + 7) >> 3;
-  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  int s = -1, part = 0, kvh = 0, ctx = 0;
-  {
-    int before = 0;
-    for (int base = 0; base < p.S && s < 0; base += 64) {
-      const int sq = base + lane;
-      int cnt = 0, c_l = 0;
-      if (sq < p.S) {
-        c_l = p.context_lens[sq];
-        const int cap = p.max_blocks * 16;
-        if (c_l < 0 || c_l > cap) {
-          if (blockIdx.x == 0 && wave == 0) record_error(p.dev_err, TQ_ERR_INDEX, -1 - sq);
-          c_l = c_l < 0 ? 0 : cap;
-        }
-        const int nb = (c_l + 15) >> 4;
-        int np = (nb + p.C - 1) / p.C;
-        if (np < 1) np = 1;
-        cnt = np * p.Hkv;
-      }
-      int incl = cnt;
+  // ---- small per-call tables to LDS (kernel arguments read at compile-time
+  // offsets only, then spread over lanes by lane selects; lane-indexed reads
+  // of the argument block would be slow per-lane vector loads)
+  if (wave == 0) {
+    uint32_t x = 0;
+    auto put = [&](uint32_t v, int i, uint32_t cur) -> uint32_t { return lane == i ? v : cur; };
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
+    for (int i = 0; i < 8; ++i) {
+      x = put((uint32_t)p.half_cb[0][2 * i] | ((uint32_t)p.half_cb[0][2 * i + 1] << 16), i, x);
+      x = put((uint32_t)p.half_cb[1][2 * i] | ((uint32_t)p.half_cb[1][2 * i + 1] << 16), 8 + i, x);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x = put((uint32_t)p.k3_cb[2 * i] | ((uint32_t)p.k3_cb[2 * i + 1] << 16), 16 + i, x);
+      x = put(p.k_signs[i], 20 + i, x);
+      x = put(p.v_signs[i], 24 + i, x);
+    }
+    if constexpr (C::MIXED) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        x = put((uint32_t)p.k_ch[4 * i] | ((uint32_t)p.k_ch[4 * i + 1] << 8) | ((uint32_t)p.k_ch[4 * i + 2] << 16) |
+                    ((uint32_t)p.k_ch[4 * i + 3] << 24),
+                32 + i, x);
+    }
+    s_par[lane] = x;
+  }
+
+  // ---- work range of this workgroup (every wave computes the same numbers)
+  const int W = total_work(p.context_lens, p.S, p.Hkv, p.max_blocks, lane);
+  const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
+  int r0 = blockIdx.x * R;
+  int r1 = (r0 + R < W) ? r0 + R : W;
+  if (p.P == 1) {   // whole segments only: there is no workspace for partials
+    r0 = snap_to_segment(p, lane, r0, W);
+    r1 = snap_to_segment(p, lane, r1, W);
+  }
+
+  // sequences with no cached token: out = 0, lse = -inf (first workgroup);
+  // context lengths outside [0, 16 * max_blocks] are reported and clamped
+  if (blockIdx.x == 0) {
+    const int cap = p.max_blocks * 16;
+    for (int s = wave; s < p.S; s += kWaves) {
+      const int c = p.context_lens[s];
+      if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
+      if (clamp_ctx(c, cap) == 0) {
+        for (int idx = lane; idx < p.Hq * D; idx += 64) {
+          const int64_t off = (int64_t)s * p.Hq * D + idx;
+          if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
+          else static_cast<uint16_t*>(p.out)[off] = 0;
+        }
+        if (p.lse)
+          for (int h = lane; h < p.Hq; h += 64) p.lse[(int64_t)s * p.Hq + h] = -INFINITY;
       }
-      const int excl = incl - cnt;
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(sq < p.S && item >= before + excl && item < before + incl);
-      if (hit) {
-        const int src = __builtin_ctzll(hit);
-        const int e0 = __shfl(excl, src);
-        s = base + src;
-        ctx = __shfl(c_l, src);
-        const int r = item - before - e0;
-        part = r / p.Hkv;
-        kvh = r % p.Hkv;
-      }
-      before += __shfl(incl, 63);
     }
   }
-  if (s < 0) return;  // uniform across the workgroup
+  if (r0 >= r1) return;  // uniform across the workgroup
+  __syncthreads();       // s_par ready
 
-  const int nb_seq = (ctx + 15) >> 4;
-  const int b_begin = part * p.C;
-  int b_end = b_begin + p.C;
-  if (b_end > nb_seq) b_end = nb_seq;
+  auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
   // ---- LDS tables: byte-indexed, two halves of 128 B per entry
-  for (int idx = tid; idx < kLutBytes / 4; idx += kThreads) {
-    const int e = idx >> 6, w = idx & 63, h = w >> 5;
-    const int kind = p.half_kind[h];
-    uint32_t val = 0;
-    if (kind == 4) {
-      val = (uint32_t)p.half_cb[h][e & 15] | ((uint32_t)p.half_cb[h][e >> 4] << 16);
-    } else if (kind == 2) {
-      val = (w & 1) ? ((uint32_t)p.half_cb[h][(e >> 4) & 3] | ((uint32_t)p.half_cb[h][e >> 6] << 16))
-                    : ((uint32_t)p.half_cb[h][e & 3] | ((uint32_t)p.half_cb[h][(e >> 2) & 3] << 16));
+  {
+    const int kind0 = p.half_kind[0], kind1 = p.half_kind[1];
+    for (int c = tid; c < kLutBytes / 16; c += kThreads) {
+      const int e = c >> 4, h = (c >> 3) & 1;
+      const int kind = h ? kind1 : kind0;
+      uint4 val = {0u, 0u, 0u, 0u};
+      if (kind == 4) {
+        const uint32_t v = cb_half(h, e & 15) | (cb_half(h, e >> 4) << 16);
+        val = uint4{v, v, v, v};
+      } else if (kind == 2) {
+        const uint32_t ev = cb_half(h, e & 3) | (cb_half(h, (e >> 2) & 3) << 16);
+        const uint32_t od = cb_half(h, (e >> 4) & 3) | (cb_half(h, e >> 6) << 16);
+        val = uint4{ev, od, ev, od};
+      }
+      reinterpret_cast<uint4*>(lds)[c] = val;
     }
-    reinterpret_cast<uint32_t*>(lds)[idx] = val;
   }
   if constexpr (C::MIXED) {
-    for (int idx = tid; idx < kLut3Bytes / 4; idx += kThreads) {
-      const int e = idx >> 5;
-      reinterpret_cast<uint32_t*>(lds + kLutBytes)[idx] = (uint32_t)p.k3_cb[e & 7] | ((uint32_t)p.k3_cb[e >> 3] << 16);
+    for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
+      const int e = c >> 2;
+      const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t hi = (s_par[16 + ((e >> 3) >> 1)] >> (16 * ((e >> 3) & 1))) & 0xFFFFu;
+      const uint32_t v = lo | (hi << 16);
+      reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
     }
   }
-
-  // ---- rotate the G q heads once: qbuf[g][ch] = (H (s_K * q))[ch], fp32
-  if (wave == 0) {
-    constexpr int PER = D / 8;              // channels per lane, 8 lanes per head
-    const int g = lane >> 3, l8 = lane & 7;
-    float x[PER];
-    const int hq = kvh * p.G + g;
-    const bool live = g < p.G;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int chn = l8 * PER + e;
-      float v = 0.f;
-      if (live) {
-        const int64_t off = ((int64_t)s * p.Hq + hq) * D + chn;
-        v = p.q_f32 ? static_cast<const float*>(p.q)[off] : bf16_to_f32(static_cast<const uint16_t*>(p.q)[off]);
-        if ((p.k_signs[chn >> 5] >> (chn & 31)) & 1u) v = -v;
-      }
-      x[e] = v;
-    }
-#pragma unroll
-    for (int h = 1; h < PER; h <<= 1) {
-#pragma unroll
-      for (int e = 0; e < PER; ++e)
-        if ((e & h) == 0) {
-          const float a0 = x[e], b0 = x[e + h];
-          x[e] = a0 + b0;
-          x[e + h] = a0 - b0;
-        }
-    }
-#pragma unroll
-    for (int k = 1; k < 8; k <<= 1) {
-      const bool up = (l8 & k) != 0;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const float o = __shfl_xor(x[e], k);
-        x[e] = up ? (o - x[e]) : (x[e] + o);
-      }
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      qbuf[g][l8 * PER + e] = x[e];
-      amax = fmaxf(amax, fabsf(x[e]));
-    }
-#pragma unroll
-    for (int k = 1; k < 8; k <<= 1) amax = fmaxf(amax, __shfl_xor(amax, k));
-    if (l8 == 0) {
-      int ex = 0;
-      if (amax > 0.f) {
-        frexpf(amax, &ex);
-      }
-      qexp[g] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
-    }
-  }
-  __syncthreads();
 
   // ---- per-lane roles
   const int j = lane & 15;          // MFMA column: q head j & 7, high (j < 8) or low part
@@ -320,85 +351,153 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
   const int gq = j & 7;
   const bool lo_part = j >= 8;
   const bool col_live = gq < p.G;
-  const int kq = qexp[gq];
-  const float q_pow = ldexpf(1.0f, kq);
-  const float w_col = ldexpf(p.score_mul, -kq);
-
-  // B operands of q.K: MFMA t covers listed channels of this lane's range
-  half8_t qb[NQK];
-#pragma unroll
-  for (int t = 0; t < NQK; ++t) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int pos;
-      if constexpr (C::MIXED) {
-        constexpr int m = D / 2;
-        constexpr int per_g = NQK / 2;
-        const int grp = t / per_g, u = t % per_g;
-        pos = grp * m + a * (m / 4) + 8 * u + e;
-      } else {
-        pos = a * (D / 4) + 8 * t + e;
-      }
-      const int chn = C::MIXED ? (int)p.k_ch[pos] : pos;
-      const float v = col_live ? qbuf[gq][chn] * q_pow : 0.f;
-      const _Float16 hi = (_Float16)v;
-      const _Float16 lo = (_Float16)(v - (float)hi);
-      qb[t][e] = lo_part ? lo : hi;
-    }
-  }
-  __syncthreads();  // qbuf is not read again; tables are complete
-
-  // ---- lane-dependent table offsets
   const uint32_t off4_k = (uint32_t)(lane & 31) * 4u;                      // K nibble table, half 0
   const uint32_t off2_k = (uint32_t)(lane & 15) * 8u;                      // K crumb table, half 0
   const uint32_t off_v4 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 31) * 4u;
   const uint32_t off_v2 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 15) * 8u;
-  const uint32_t off3 = (uint32_t)kLutBytes + (uint32_t)(lane & 31) * 4u;
-
-  // token of this lane's K row: sigma(j) = j/4 + 4*(j%4)
-  const int tokK = (j >> 2) + 4 * (j & 3);
-
-  const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
-  const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
+  const uint32_t off3 = (uint32_t)kLutBytes + (uint32_t)(lane & 15) * 4u;
+  const int tokK = (j >> 2) + 4 * (j & 3);   // token of this lane's K row: sigma(j)
+  // per-lane byte offsets inside a K / V tile
+  constexpr int KLANE = KK == K4 ? D / 8 : (KK == K2 ? D / 16 : D / 16);   // index bytes of the (high) group
+  const uint32_t k_off = (uint32_t)(tokK * C::KROW + KLANE * a);
+  const uint32_t klo_off = (uint32_t)((tokK * C::KROW + D / 4 + (3 * D / 64) * a) & ~3);
+  const uint32_t kn_off = (uint32_t)(p.k_norm_off + 8 * a);
+  const uint32_t v_off = (uint32_t)(a * C::VROW + C::VLANE * j);
+  const uint32_t vn_off = (uint32_t)(p.v_norm_off + 8 * a);
   const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
   const int64_t v_blk_stride = (int64_t)p.Hkv * p.v_tile;
-  const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
+  const int cap = p.max_blocks * 16;
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float4_t o_acc[R];
+  // ---- walk the pieces of this workgroup's range
+  int s, kvh, blk, nb_s;
+  locate(p, lane, r0, s, kvh, blk, nb_s);
+  int pos = r0;
+  while (pos < r1) {
+    const int seg_start = pos - blk;
+    const int b0 = blk;
+    const int b1 = (nb_s - blk < r1 - pos) ? nb_s : blk + (r1 - pos);
+    // one piece: the final output is written here (always so when P == 1)
+    const bool whole = p.P == 1 || (seg_start / R) == ((seg_start + nb_s - 1) / R);
+    const int piece = (int)blockIdx.x - seg_start / R;
+    const int ctx = clamp_ctx(p.context_lens[s], cap);
+
+    // -------- rotate the G q heads of (s, kvh) once: mrg[g*D + ch] = (H (s_K * q))[ch]
+    __syncthreads();  // the previous piece's merge slots are free
+    if (wave == 0) {
+      constexpr int PER = D / 8;              // channels per lane, 8 lanes per head
+      const int g = lane >> 3, l8 = lane & 7;
+      const bool live = g < p.G;
+      const int hq = kvh * p.G + (live ? g : 0);
+      const int64_t base = ((int64_t)s * p.Hq + hq) * D + l8 * PER;
+      float x[PER];
+      if (p.q_f32) {
+        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + base);
 #pragma unroll
-  for (int u = 0; u < R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nbw = (b_end - b_begin - wave + kWaves - 1) / kWaves;  // blocks of this wave
-  for (int chunk0 = 0; chunk0 < nbw; chunk0 += 64) {
-    const int cnt = (nbw - chunk0) < 64 ? (nbw - chunk0) : 64;
-    int bt_reg = 0;
-    if (lane < cnt) bt_reg = bt_row[b_begin + wave + kWaves * (chunk0 + lane)];
-
-    Tile<D, KK, VK> cur, nxt;
-    auto tile_ptrs = [&](int it, const uint8_t*& kt, const uint8_t*& vt) -> bool {
-      const int phys = __builtin_amdgcn_readlane(bt_reg, it);
-      const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
-      const int64_t ph = ok ? phys : 0;
-      kt = k_head + ph * k_blk_stride;
-      vt = v_head + ph * v_blk_stride;
-      return ok;
-    };
-    const uint8_t *kt0, *vt0;
-    bool ok_cur = tile_ptrs(0, kt0, vt0);
-    load_tile<D, KK, VK>(cur, kt0, vt0, tokK, a, a, j, p.k_norm_off, p.v_norm_off);
-
-    for (int it = 0; it < cnt; ++it) {
-      bool ok_nxt = false;
-      if (it + 1 < cnt) {
-        const uint8_t *kt1, *vt1;
-        ok_nxt = tile_ptrs(it + 1, kt1, vt1);
-        load_tile<D, KK, VK>(nxt, kt1, vt1, tokK, a, a, j, p.k_norm_off, p.v_norm_off);
+        for (int v4 = 0; v4 < PER / 4; ++v4) {
+          const float4 t = src[v4];
+          x[4 * v4] = t.x; x[4 * v4 + 1] = t.y; x[4 * v4 + 2] = t.z; x[4 * v4 + 3] = t.w;
+        }
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + base);
+#pragma unroll
+        for (int v8 = 0; v8 < PER / 8; ++v8) {
+          const uint4 t = src[v8];
+          const uint32_t w4[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            x[8 * v8 + 2 * k] = __uint_as_float(w4[k] << 16);
+            x[8 * v8 + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+          }
+        }
       }
-      const int b = b_begin + wave + kWaves * (chunk0 + it);
-      if (!ok_cur && lane == 0) record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b);
+      const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        if ((sw >> e) & 1u) x[e] = -x[e];
+        if (!live) x[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 1; h < PER; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          if ((e & h) == 0) {
+            const float a0 = x[e], b0v = x[e + h];
+            x[e] = a0 + b0v;
+            x[e + h] = a0 - b0v;
+          }
+      }
+#pragma unroll
+      for (int k = 1; k < 8; k <<= 1) {
+        const bool up = (l8 & k) != 0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const float o = __shfl_xor(x[e], k);
+          x[e] = up ? (o - x[e]) : (x[e] + o);
+        }
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        mrg[g * D + l8 * PER + e] = x[e];
+        amax = fmaxf(amax, fabsf(x[e]));
+      }
+#pragma unroll
+      for (int k = 1; k < 8; k <<= 1) amax = fmaxf(amax, __shfl_xor(amax, k));
+      if (l8 == 0) {
+        int ex = 0;
+        if (amax > 0.f) frexpf(amax, &ex);
+        s_qexp[g] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
+      }
+    }
+    __syncthreads();
 
-      // -------- q.K on the matrix cores
+    // q.K B operands, per lane (column j, channel chunk a): built once per
+    // piece and kept in LDS (the first 4 KB of the merge area), shared by
+    // all waves and re-read per block, which keeps 16 VGPRs free.
+    {
+      const int kq = s_qexp[gq];
+      const float q_pow = ldexpf(1.0f, kq);
+      half8_t qv[NQK];
+#pragma unroll
+      for (int t = 0; t < NQK; ++t) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          int pos_l;
+          if constexpr (C::MIXED) {
+            constexpr int m = D / 2;
+            constexpr int per_g = NQK / 2;
+            const int grp = t / per_g, u = t % per_g;
+            pos_l = grp * m + a * (m / 4) + 8 * u + e;
+          } else {
+            pos_l = a * (D / 4) + 8 * t + e;
+          }
+          const int chn = C::MIXED ? (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu) : pos_l;
+          const float v = mrg[gq * D + chn] * q_pow;
+          const _Float16 hi = (_Float16)v;
+          const _Float16 lo = (_Float16)(v - (float)hi);
+          qv[t][e] = lo_part ? lo : hi;
+        }
+      }
+      __syncthreads();  // all waves have read the rotated q
+      if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) reinterpret_cast<half8_t*>(mrg)[t * 64 + lane] = qv[t];
+      }
+    }
+    const float w_col = ldexpf(p.score_mul, -s_qexp[gq]);
+    const half8_t* qb = reinterpret_cast<const half8_t*>(mrg) + lane;   // qb[64 * t]: operand of MFMA t
+    __syncthreads();  // operands ready
+
+    // -------- stream this wave's blocks of the piece
+    const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
+    const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
+    const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
+    float m_run = -INFINITY, l_run = 0.f;
+    float4_t o_acc[C::R];
+#pragma unroll
+    for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Tile<D, KK, VK>& cur, int b, bool ok) {
       float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
       float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (KK == K4) {
@@ -407,8 +506,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
           u32x4_t av;
 #pragma unroll
           for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[t], off4_k, by));
-          const half8_t A = __builtin_bit_cast(half8_t, av);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[t], acc0, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
         }
       } else if constexpr (KK == K2) {
 #pragma unroll
@@ -416,89 +514,72 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
           const uint2 x0 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1)));
           const uint2 x1 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1) + 1));
           const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
-          const half8_t A = __builtin_bit_cast(half8_t, av);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[t], acc0, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
         }
       } else {
         constexpr int per_g = NQK / 2;
-        // high group: 4-bit nibbles
 #pragma unroll
         for (int u = 0; u < per_g; ++u) {
           u32x4_t av;
 #pragma unroll
           for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[u], off4_k, by));
-          const half8_t A = __builtin_bit_cast(half8_t, av);
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[u], acc0, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
         }
-        // low group: 3-bit indices, looked up in pairs (6-bit keys)
-        {
-          constexpr int LB = 3 * D / 64;
-          const int lo_off = tokK * C::KROW + D / 4 + LB * a;
-          const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((lo_off & 3) * 8);
+        constexpr int LB = 3 * D / 64;
+        const int lo_off = tokK * C::KROW + D / 4 + LB * a;
+        const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((lo_off & 3) * 8);
 #pragma unroll
-          for (int u = 0; u < per_g; ++u) {
-            u32x4_t av;
+        for (int u = 0; u < per_g; ++u) {
+          u32x4_t av;
 #pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-              const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
-              av[pr] = lds_u32(lds, (key << 7) | off3);
-            }
-            const half8_t A = __builtin_bit_cast(half8_t, av);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[per_g + u], acc1, 0, 0, 0);
+          for (int pr = 0; pr < 4; ++pr) {
+            const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
+            av[pr] = lds_u32(lds, (key << 6) | off3);
           }
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
         }
       }
 
-      // -------- scores of this lane's 4 tokens for q head gq (exp2 domain)
+      // stage boundary: keeps the scheduler from hoisting the next stage's
+      // table reads above these MFMAs (bounds the live registers)
+      __builtin_amdgcn_sched_barrier(0);
+      // scores of this lane's 4 tokens for q head gq (exp2 domain)
       const int tok0 = 16 * b;
       float sc[4];
-      {
-        const uint32_t kn0[2] = {cur.kn[0].x, cur.kn[0].y};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float full0 = acc0[e] + row_ror8(acc0[e]);
-          const _Float16 n0 = __builtin_bit_cast(_Float16, (uint16_t)(kn0[e >> 1] >> (16 * (e & 1))));
-          float v = full0 * ((float)n0 * w_col);
-          if constexpr (C::MIXED) {
-            const uint32_t kn1[2] = {cur.kn[1].x, cur.kn[1].y};
-            const float full1 = acc1[e] + row_ror8(acc1[e]);
-            const _Float16 n1 = __builtin_bit_cast(_Float16, (uint16_t)(kn1[e >> 1] >> (16 * (e & 1))));
-            v += full1 * ((float)n1 * w_col);
-          }
-          const bool valid = ok_cur && col_live && (tok0 + a + 4 * e) < ctx;
-          sc[e] = valid ? v : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        const float full0 = acc0[e] + row_ror8(acc0[e]);
+        float v = full0 * (half_at(cur.kn[0], e) * w_col);
+        if constexpr (C::MIXED) {
+          const float full1 = acc1[e] + row_ror8(acc1[e]);
+          v += full1 * (half_at(cur.kn[1], e) * w_col);
         }
+        const bool valid = ok && col_live && (tok0 + a + 4 * e) < ctx;
+        sc[e] = valid ? v : -INFINITY;
       }
       float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       const float m_new = fmaxf(m_run, bm);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // m_run = -inf -> 0
+        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         l_run *= alpha;
 #pragma unroll
-        for (int u = 0; u < R; ++u) o_acc[u] *= alpha;
+        for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
         m_run = m_new;
       }
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float pr[4];
+      half4_t pb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
-        l_run += pr[e];
-      }
-      half4_t pb;
-      {
-        const uint32_t vn[2] = {cur.vn.x, cur.vn.y};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const _Float16 nv = __builtin_bit_cast(_Float16, (uint16_t)(vn[e >> 1] >> (16 * (e & 1))));
-          const float pv = (sc[e] == -INFINITY) ? 0.f : pr[e] * ((float)nv * p.v_mul);
-          pb[e] = (_Float16)pv;
-        }
+        const float pr = __builtin_amdgcn_exp2f(sc[e] - m_use);
+        l_run += pr;
+        const float pv = (sc[e] == -INFINITY) ? 0.f : pr * (half_at(cur.vn, e) * p.v_mul);
+        pb[e] = (_Float16)pv;
       }
 
-      // -------- P.V on the matrix cores: A = V (dims x tokens) per MFMA u
+      __builtin_amdgcn_sched_barrier(0);
+      // P.V on the matrix cores: A = V (dims x tokens) per MFMA u
       if constexpr (VK == V4) {
         constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
 #pragma unroll
@@ -510,8 +591,8 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
           for (int hh = 0; hh < 2; ++hh) {
             const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
             const u32x2_t av = {__builtin_amdgcn_perm(lk[1], lk[0], sel), __builtin_amdgcn_perm(lk[3], lk[2], sel)};
-            const half4_t A = __builtin_bit_cast(half4_t, av);
-            o_acc[2 * k + hh] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, pb, o_acc[2 * k + hh], 0, 0, 0);
+            o_acc[2 * k + hh] =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[2 * k + hh], 0, 0, 0);
           }
         }
       } else {
@@ -529,106 +610,175 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
             const uint32_t w2 = (t >> 1) ? lk[2].y : lk[2].x;
             const uint32_t w3 = (t >> 1) ? lk[3].y : lk[3].x;
             const u32x2_t av = {__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
-            const half4_t A = __builtin_bit_cast(half4_t, av);
-            o_acc[4 * k + t] = __builtin_amdgcn_mfma_f32_16x16x16f16(A, pb, o_acc[4 * k + t], 0, 0, 0);
+            o_acc[4 * k + t] =
+                __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[4 * k + t], 0, 0, 0);
           }
         }
       }
-      cur = nxt;
-      ok_cur = ok_nxt;
-    }
-  }
+    };
 
-  // ---- wave epilogue: full row sum, inverse rotation of this lane's dims
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  float y[4 * R];
-#pragma unroll
-  for (int u = 0; u < R; ++u)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[R * e + u] = o_acc[u][e];
-#pragma unroll
-  for (int h = 1; h < 4 * R; h <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 4 * R; ++e)
-      if ((e & h) == 0) {
-        const float a0 = y[e], b0 = y[e + h];
-        y[e] = a0 + b0;
-        y[e + h] = a0 - b0;
+    const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;  // blocks of this wave
+    for (int chunk0 = 0; chunk0 < nbw; chunk0 += 64) {
+      const int cnt = (nbw - chunk0) < 64 ? (nbw - chunk0) : 64;
+      int bt_reg = 0;
+      if (lane < cnt) bt_reg = bt_row[b0 + wave + kWaves * (chunk0 + lane)];
+      const bool bad = lane < cnt && (bt_reg < 0 || (int64_t)bt_reg >= p.num_blocks);
+      const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
+      if (badm) {
+        if (lane == (int)__builtin_ctzll(badm))
+          record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + wave + kWaves * (chunk0 + lane));
+        if (bad) bt_reg = 0;
       }
-  }
-#pragma unroll
-  for (int k = 16; k < 64; k <<= 1) {
-    const bool up = (lane & k) != 0;
-#pragma unroll
-    for (int e = 0; e < 4 * R; ++e) {
-      const float o = __shfl_xor(y[e], k);
-      y[e] = up ? (o - y[e]) : (y[e] + o);
-    }
-  }
-
-  __syncthreads();  // every wave is done with the tables: reuse LDS for the merge
-  float* mo = reinterpret_cast<float*>(lds);               // [kWaves][8][D]
-  float* mm = mo + kWaves * 8 * D;                          // [kWaves][8]
-  float* ml = mm + kWaves * 8;                              // [kWaves][8]
-  if (!lo_part) {
-#pragma unroll
-    for (int e = 0; e < 4 * R; ++e) {
-      const int dim = 4 * R * a + e;
-      const float sg = ((p.v_signs[dim >> 5] >> (dim & 31)) & 1u) ? -1.f : 1.f;
-      mo[(wave * 8 + gq) * D + dim] = y[e] * sg;
-    }
-    if (a == 0) {
-      mm[wave * 8 + gq] = m_run;
-      ml[wave * 8 + gq] = l_run;
-    }
-  }
-  __syncthreads();
-
-  // ---- merge the 8 wave states and write the result
-  const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
-  for (int idx = tid; idx < p.G * D; idx += kThreads) {
-    const int g = idx / D, dim = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mm[w * 8 + g]);
-    float den = 0.f, num = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = mm[w * 8 + g];
-        const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        den += f * ml[w * 8 + g];
-        num += f * mo[(w * 8 + g) * D + dim];
+      auto ptrs = [&](int it, const uint8_t*& kt, const uint8_t*& vt) {
+        const int64_t ph = __builtin_amdgcn_readlane(bt_reg, it);
+        kt = k_head + ph * k_blk_stride;
+        vt = v_head + ph * v_blk_stride;
+      };
+      Tile<D, KK, VK> A, B;
+      const uint8_t *kt, *vt;
+      ptrs(0, kt, vt);
+      load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, kn_off, v_off, vn_off);
+      int it = 0;
+      for (;;) {
+        ptrs(it + 1 < cnt ? it + 1 : it, kt, vt);
+        load_tile<D, KK, VK>(B, kt, vt, k_off, klo_off, kn_off, v_off, vn_off);
+        compute(A, b0 + wave + kWaves * (chunk0 + it), !((badm >> it) & 1ull));
+        if (++it >= cnt) break;
+        ptrs(it + 1 < cnt ? it + 1 : it, kt, vt);
+        load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, kn_off, v_off, vn_off);
+        compute(B, b0 + wave + kWaves * (chunk0 + it), !((badm >> it) & 1ull));
+        if (++it >= cnt) break;
       }
     }
-    const bool empty = !(den > 0.f);
-    const float o = empty ? 0.f : num / den * inv_sqrt_d;
-    const float lse = empty ? -INFINITY : (M + log2f(den)) * kLn2;
-    const int hq = kvh * p.G + g;
-    if (p.P == 1) {
-      const int64_t off = ((int64_t)s * p.Hq + hq) * D + dim;
-      if (p.out_f32) static_cast<float*>(p.out)[off] = o;
-      else static_cast<uint16_t*>(p.out)[off] = f32_to_bf16_rne(o);
-      if (dim == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
-    } else {
-      const int64_t row = ((int64_t)s * p.Hq + hq) * p.P + part;
-      p.part_o[row * D + dim] = o;
-      if (dim == 0) p.part_lse[row] = lse;
+
+    // -------- merge the 8 wave states (LDS tree), rotated domain
+    __syncthreads();  // every wave is done with the q operands in the merge area
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    {
+      int active = kWaves;
+      while (active > 1) {
+        const int k = (active / 2 < C::NSLOT) ? active / 2 : C::NSLOT;
+        const int wr0 = active - k, rd0 = active - 2 * k;
+        if (wave >= wr0 && wave < active && !lo_part) {
+          float* slot = mrg + (wave - wr0) * C::SLOT_FLOATS;
+#pragma unroll
+          for (int u = 0; u < C::R; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) slot[gq * D + R4 * a + C::R * e + u] = o_acc[u][e];
+          if (a == 0) {
+            slot[8 * D + gq] = m_run;
+            slot[8 * D + 8 + gq] = l_run;
+          }
+        }
+        __syncthreads();
+        if (wave >= rd0 && wave < wr0) {
+          const float* slot = mrg + (wave - rd0) * C::SLOT_FLOATS;
+          const float m2 = slot[8 * D + gq], l2 = slot[8 * D + 8 + gq];
+          const float M = fmaxf(m_run, m2);
+          const float f1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+          const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+          for (int u = 0; u < C::R; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o_acc[u][e] = f1 * o_acc[u][e] + f2 * slot[gq * D + R4 * a + C::R * e + u];
+          l_run = f1 * l_run + f2 * l2;
+          m_run = M;
+        }
+        __syncthreads();
+        active -= k;
+      }
+    }
+
+    // -------- wave 0: normalise, inverse rotation, write
+    if (wave == 0) {
+      float y[R4];
+#pragma unroll
+      for (int u = 0; u < C::R; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[C::R * e + u] = o_acc[u][e];
+#pragma unroll
+      for (int h = 1; h < R4; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < R4; ++e)
+          if ((e & h) == 0) {
+            const float a0 = y[e], b0v = y[e + h];
+            y[e] = a0 + b0v;
+            y[e + h] = a0 - b0v;
+          }
+      }
+#pragma unroll
+      for (int k = 16; k < 64; k <<= 1) {
+        const bool up = (lane & k) != 0;
+#pragma unroll
+        for (int e = 0; e < R4; ++e) {
+          const float o = __shfl_xor(y[e], k);
+          y[e] = up ? (o - y[e]) : (y[e] + o);
+        }
+      }
+      const bool empty = !(l_run > 0.f);
+      const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
+      const float scale = empty ? 0.f : inv_sqrt_d / l_run;
+      const float lse = empty ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
+      if (!lo_part && col_live) {
+        const int hq = kvh * p.G + gq;
+        const uint32_t sw = s_par[24 + ((R4 * a) >> 5)] >> ((R4 * a) & 31);
+#pragma unroll
+        for (int e = 0; e < R4; ++e) y[e] = ((sw >> e) & 1u) ? -y[e] * scale : y[e] * scale;
+        if (whole) {
+          const int64_t off = ((int64_t)s * p.Hq + hq) * D + R4 * a;
+          if (p.out_f32) {
+            float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + off);
+#pragma unroll
+            for (int e = 0; e < R4 / 4; ++e) dst[e] = float4{y[4 * e], y[4 * e + 1], y[4 * e + 2], y[4 * e + 3]};
+          } else {
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + off);
+#pragma unroll
+            for (int e = 0; e < R4 / 8; ++e) {
+              uint32_t w4[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                w4[k] = (uint32_t)f32_to_bf16_rne(y[8 * e + 2 * k]) |
+                        ((uint32_t)f32_to_bf16_rne(y[8 * e + 2 * k + 1]) << 16);
+              dst[e] = uint4{w4[0], w4[1], w4[2], w4[3]};
+            }
+          }
+          if (a == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
+        } else {
+          const int64_t row = ((int64_t)s * p.Hq + hq) * p.P + piece;
+          float4* dst = reinterpret_cast<float4*>(p.part_o + row * D + R4 * a);
+#pragma unroll
+          for (int e = 0; e < R4 / 4; ++e) dst[e] = float4{y[4 * e], y[4 * e + 1], y[4 * e + 2], y[4 * e + 3]};
+          if (a == 0) p.part_lse[row] = lse;
+        }
+      }
+    }
+
+    // -------- next piece
+    pos += b1 - b0;
+    if (pos >= r1) break;
+    blk = 0;
+    if (++kvh == p.Hkv) {
+      kvh = 0;
+      do {
+        ++s;
+        nb_s = (clamp_ctx(p.context_lens[s], cap) + 15) >> 4;
+      } while (nb_s == 0);
     }
   }
 }
 
 // ----------------------------------------------------------------- merge
-// One wave per (sequence, head).  n_valid(s) partials are read (all P for
-// the generic entry point; the chunks the sequence has for the decode).
+// One wave per (sequence, q head).  Generic mode: all P partials, -inf lse
+// marks an empty partial.  Decode mode: only segments cut into several
+// pieces are merged (the others were written by the decode kernel).
 struct MergeParams {
   const float* part_o;
   const float* part_lse;
   void* out;
   float* lse;
-  const int32_t* context_lens;  // NULL: all P partials
-  int32_t S, H, P, D, C, max_blocks, out_f32;
+  const int32_t* context_lens;  // NULL: generic mode
+  int32_t S, H, P, D, Hkv, G, max_blocks, n_wg, out_f32;
 };
 
 __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
@@ -637,13 +787,24 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
   const int lane = threadIdx.x;
   int n = p.P;
   if (p.context_lens) {
-    int c = p.context_lens[s];
+    // recompute the decode kernel's workgroup ranges for this segment
+    const int W = total_work(p.context_lens, p.S, p.Hkv, p.max_blocks, lane);
+    const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
     const int cap = p.max_blocks * 16;
-    c = c < 0 ? 0 : (c > cap ? cap : c);
-    const int nb = (c + 15) >> 4;
-    n = (nb + p.C - 1) / p.C;
-    if (n < 1) n = 1;
-    if (n > p.P) n = p.P;
+    int before = 0;
+    for (int base = 0; base < s; base += 64) {
+      const int sq = base + lane;
+      int v = sq < s ? ((clamp_ctx(p.context_lens[sq], cap) + 15) >> 4) : 0;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      before += v;
+    }
+    const int nb = (clamp_ctx(p.context_lens[s], cap) + 15) >> 4;
+    if (nb == 0) return;  // written by the decode kernel
+    const int kvh = (sh % p.H) / p.G;
+    const int seg_start = before * p.Hkv + kvh * nb;
+    n = (seg_start + nb - 1) / R - seg_start / R + 1;
+    if (n <= 1) return;   // written directly by the decode kernel
   }
   const float* lse_p = p.part_lse + (int64_t)sh * p.P;
   const float* o_p = p.part_o + (int64_t)sh * p.P * p.D;
@@ -654,7 +815,27 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
   float acc[2] = {0.f, 0.f};
   float den = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+      float li[4], ov[4][2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        li[k] = lse_p[i + k];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int dim = lane + 64 * r;
+          ov[k][r] = dim < p.D ? o_p[(int64_t)(i + k) * p.D + dim] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float w = (li[k] == -INFINITY) ? 0.f : expf(li[k] - M);
+        den += w;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) acc[r] += w * ov[k][r];
+      }
+    }
+    for (; i < n; ++i) {
       const float li = lse_p[i];
       const float w = (li == -INFINITY) ? 0.f : expf(li - M);
       den += w;
@@ -679,8 +860,8 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
 }
 
 template <int D, int KK, int VK>
-void launch_decode(const DecodeParams& p, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<D, KK, VK>), dim3(grid), dim3(kThreads), 0, st, p);
+void launch_decode(const DecodeParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<D, KK, VK>), dim3((unsigned)p.n_wg), dim3(kThreads), 0, st, p);
 }
 
 int format_kind_k(const tq_format* f) {
@@ -696,6 +877,21 @@ int format_kind_v(const tq_format* f) {
   return -1;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace
 }  // namespace tq
 
@@ -709,7 +905,7 @@ extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse
   if (out_dtype != TQ_BF16 && out_dtype != TQ_F32) return set_error(TQ_ERR_VALUE, "out_dtype must be BF16 or F32");
   if (num_seqs == 0) return TQ_OK;
   if (!part_out || !part_lse || !out) return set_error(TQ_ERR_VALUE, "NULL merge buffer");
-  MergeParams mp = {part_out, part_lse, out, lse, nullptr, num_seqs, num_heads, num_splits, head_dim, 1, 1,
+  MergeParams mp = {part_out, part_lse, out, lse, nullptr, num_seqs, num_heads, num_splits, head_dim, 1, 1, 1, 1,
                     out_dtype == TQ_F32};
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
                      reinterpret_cast<hipStream_t>(stream), mp);
@@ -741,7 +937,6 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   if (kk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit groups)");
   if (vk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this V format (served: 4-bit, 2-bit)");
   const int D = kfmt->head_dim;
-  if (kk == KM43 && D != 128 && D != 64) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "mixed K needs head_dim 64 or 128");
   if (num_seqs == 0) return TQ_OK;
   if (!q || !k_pages || !v_pages || !block_tables || !context_lens || !out)
     return set_error(TQ_ERR_VALUE, "NULL required pointer");
@@ -749,8 +944,9 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   tq_decode_workspace_bytes(num_seqs, num_q_heads, D, num_splits, &need);
   if (workspace_bytes < need || (need && !workspace))
     return set_error(TQ_ERR_VALUE, "workspace too small: need " + std::to_string(need) + " bytes");
-  const int64_t items = (int64_t)num_seqs * num_splits * num_kv_heads;
-  if (items >= (1ll << 31) / 2) return set_error(TQ_ERR_VALUE, "too many decode items");
+  const int64_t work_bound = (int64_t)num_seqs * num_kv_heads * max_blocks_per_seq;
+  if (work_bound >= (1ll << 30) || max_blocks_per_seq > (1 << 20))
+    return set_error(TQ_ERR_VALUE, "too much work for one call (2^30 block-heads, 2^20 blocks per sequence)");
 
   DecodeParams p = {};
   p.q = q;
@@ -768,7 +964,8 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   p.G = G;
   p.max_blocks = max_blocks_per_seq;
   p.P = num_splits;
-  p.C = (max_blocks_per_seq + num_splits - 1) / num_splits;
+  const int64_t wg = 2ll * device_cus();
+  p.n_wg = (int)(work_bound < wg ? (work_bound > 0 ? work_bound : 1) : wg);
   p.k_tile = tile_bytes_of(kfmt);
   p.v_tile = tile_bytes_of(vfmt);
   p.k_norm_off = TQ_BLOCK_SIZE * row_index_bytes(kfmt);
@@ -786,7 +983,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   p.half_kind[0] = kbits0;
   for (int i = 0; i < 16; ++i) p.half_cb[0][i] = kfmt->codebook[0][i];
   const int vbits = vfmt->group_bits[0];
-  bool share = (kk == K4 || kk == KM43 || kk == K2) && vbits == kbits0;
+  bool share = vbits == kbits0;
   for (int i = 0; i < (1 << vbits) && share; ++i) share = vfmt->codebook[0][i] == kfmt->codebook[0][i];
   if (share) {
     p.v_half = 0;
@@ -804,10 +1001,9 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (int64_t)num_seqs * num_q_heads * num_splits * D;
   }
-  const unsigned grid = (unsigned)((items + 7) / 8 * 8);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-#define TQ_LAUNCH(DD, KKK, VVV)                                              \
-  if (D == DD && kk == KKK && vk == VVV) launch_decode<DD, KKK, VVV>(p, grid, hs);
+#define TQ_LAUNCH(DD, KKK, VVV) \
+  if (D == DD && kk == KKK && vk == VVV) launch_decode<DD, KKK, VVV>(p, hs);
   TQ_LAUNCH(128, K4, V4) TQ_LAUNCH(128, K4, V2) TQ_LAUNCH(128, K2, V4) TQ_LAUNCH(128, K2, V2)
   TQ_LAUNCH(128, KM43, V4) TQ_LAUNCH(128, KM43, V2)
   TQ_LAUNCH(64, K4, V4) TQ_LAUNCH(64, K4, V2) TQ_LAUNCH(64, K2, V4) TQ_LAUNCH(64, K2, V2)
@@ -815,8 +1011,8 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
 #undef TQ_LAUNCH
   st = launch_status("tq_decode_paged launch");
   if (st != TQ_OK || num_splits == 1) return st;
-  MergeParams mp = {p.part_o, p.part_lse, out, lse, context_lens, num_seqs, num_q_heads, num_splits, D, p.C,
-                    max_blocks_per_seq, p.out_f32};
+  MergeParams mp = {p.part_o, p.part_lse, out, lse, context_lens, num_seqs, num_q_heads, num_splits, D,
+                    num_kv_heads, G, max_blocks_per_seq, p.n_wg, p.out_f32};
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_q_heads)), dim3(64), 0, hs, mp);
   return launch_status("tq_decode_paged merge launch");
 }

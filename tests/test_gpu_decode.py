@@ -6,9 +6,10 @@ and bf16 q/out; LSE within 1e-4 absolute):
   * lse: max |lse - lse_ref| <= 1e-4;
   * fp32 out: per (sequence, head) normwise relative error <= 2e-3 and every
     element within 2e-3 of the vector's largest |value|;
-  * bf16 out: normwise relative error <= 2e-3 against the fp64 reference
-    rounded to bf16 (the rounding the caller asked for is not charged to the
-    kernel; bf16 alone can exceed 2e-3 normwise).
+  * bf16 out: the normwise relative error against fp64, minus what rounding
+    the exact result to bf16 costs by itself, is <= 2e-3 (bf16 rounding alone
+    is ~1.7e-3 RMS normwise, so it cannot be charged to the kernel).
+Full-size cases check both output dtypes.
 """
 import math
 
@@ -93,20 +94,22 @@ def run_decode(w, kp, vp, kf, vf, num_splits, out_dtype):
     return q, o.float().cpu().numpy(), l.cpu().numpy()
 
 
-def check(w, q, o, l, pairs, out_dtype):
-    ref = oracle_decode(w, q, pairs)
-    worst_o = worst_l = worst_e = 0.0
+def check(w, q, o, l, pairs, out_dtype, ref=None):
+    ref = ref if ref is not None else oracle_decode(w, q, pairs)
+    worst_o = worst_l = worst_e = worst_raw = 0.0
     for (s, h) in pairs:
         o_ref, l_ref = ref[(s, h)]
         if l_ref == -math.inf:
             assert l[s, h] == -math.inf and np.all(o[s, h] == 0), (s, h)
             continue
         eo = out_error(o[s, h][None], o_ref[None], out_dtype == "bf16")[0]
+        worst_raw = max(worst_raw, out_error(o[s, h][None], o_ref[None])[0])
         el = abs(float(l[s, h]) - l_ref)
         worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
         if out_dtype == "f32":
             worst_e = max(worst_e, float(np.max(elem_error(o[s, h][None], o_ref[None]))))
-    print(f"worst out {worst_o:.2e}  lse {worst_l:.2e}  elem {worst_e:.2e}", flush=True)
+    print(f"[{out_dtype}] worst out {worst_o:.2e} (raw normwise {worst_raw:.2e})  lse {worst_l:.2e}  "
+          f"elem {worst_e:.2e}", flush=True)
     assert worst_l <= LSE_TOL
     assert worst_o <= OUT_TOL
     assert worst_e <= OUT_TOL
@@ -244,13 +247,16 @@ BENCH_SPLITS = {2: 16, 4: 16, 5: 64}
                                                       (5, [0], [0, 9, 18, 27, 36, 45, 54, 63])])
 def test_full_size_workloads_sampled(index, seqs, heads_per_seq):
     """The decode workloads at full size, in the launch configuration the
-    benchmark times (same num_splits); outputs sampled per sequence."""
+    benchmark times (same num_splits); outputs sampled per sequence, checked
+    with the workload's output dtype and with fp32 output."""
     w = wl.decode_workload(index)
     P = BENCH_SPLITS.get(index, 1)
     print(f"case workload {index} {w.name} splits {P}", flush=True)
     kp, vp, kf, vf = build_gpu_cache(w)
-    q, o, l = run_decode(w, kp, vp, kf, vf, P, w.out_dtype)
     heads = heads_per_seq or list(range(w.num_q_heads))
     pairs = [(s, h) for s in seqs for h in heads]
-    check(w, q, o, l, pairs, w.out_dtype)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    ref = oracle_decode(w, wl.q_values(w), pairs)
+    for odt in sorted({w.out_dtype, "f32"}):
+        q, o, l = run_decode(w, kp, vp, kf, vf, P, odt)
+        check(w, q, o, l, pairs, odt, ref=ref)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
