@@ -47,15 +47,15 @@ class tq_format(ctypes.Structure):
     ]
 
 
-def _load():
+def _load(path: str = LIB_PATH):
     # torch first: its bundled HIP runtime is registered under the soname that
     # libtq.so asks for, so libtq binds to that same runtime instance (the one
     # that owns torch's device memory and stream handles) instead of loading a
     # second copy of the runtime.
     import torch  # noqa: F401
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_paged_kv_amd._build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m quantized_paged_kv_amd._build`")
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, u64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
     fmtp = ctypes.POINTER(tq_format)

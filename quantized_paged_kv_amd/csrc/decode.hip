@@ -77,8 +77,8 @@ struct DecodeParams {
   int32_t S, Hq, Hkv, G, max_blocks, P;
   int32_t n_wg;      // grid size (persistent workgroups)
   int32_t k_tile, v_tile, k_norm_off, v_norm_off;
-  float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K))
-  float v_mul;       // 1 / sqrt(m_V)
+  float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K)), > 0
+  float v_mul;       // 1 / sqrt(m_V), applied once in the epilogue
   uint32_t v_signs[4];
   uint32_t k_signs[4];
   uint16_t half_cb[2][16];   // codebook of the table in each LUT half
@@ -543,54 +543,63 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
       // stage boundary: keeps the scheduler from hoisting the next stage's
       // table reads above these MFMAs (bounds the live registers)
       __builtin_amdgcn_sched_barrier(0);
-      // scores of this lane's 4 tokens for q head gq (exp2 domain)
+      // raw scores of this lane's 4 tokens for q head gq: sr = (q . c) * n_K;
+      // the exp2-domain score is w_col * sr (w_col > 0), folded into one fma
       const int tok0 = 16 * b;
       float sc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float full0 = acc0[e] + row_ror8(acc0[e]);
-        float v = full0 * (half_at(cur.kn[0], e) * w_col);
+        float v = full0 * half_at(cur.kn[0], e);
         if constexpr (C::MIXED) {
           const float full1 = acc1[e] + row_ror8(acc1[e]);
-          v += full1 * (half_at(cur.kn[1], e) * w_col);
+          v += full1 * half_at(cur.kn[1], e);
         }
-        const bool valid = ok && col_live && (tok0 + a + 4 * e) < ctx;
-        sc[e] = valid ? v : -INFINITY;
+        sc[e] = v;
+      }
+      if (!(ok && tok0 + 16 <= ctx)) {   // partial or skipped block (wave-uniform branch)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx) ? sc[e] : -INFINITY;
       }
       float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       const float m_new = fmaxf(m_run, bm);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
+        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f((m_run - m_new) * w_col) : 1.f;
         l_run *= alpha;
 #pragma unroll
         for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
         m_run = m_new;
       }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      const float nm = (m_run == -INFINITY) ? 0.f : -m_run * w_col;
       half4_t pb;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(sc[e] - m_use);
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
         l_run += pr;
-        const float pv = (sc[e] == -INFINITY) ? 0.f : pr * (half_at(cur.vn, e) * p.v_mul);
-        pb[e] = (_Float16)pv;
+        pb[e] = (_Float16)(pr * half_at(cur.vn, e));
       }
 
       __builtin_amdgcn_sched_barrier(0);
       // P.V on the matrix cores: A = V (dims x tokens) per MFMA u
       if constexpr (VK == V4) {
+        // Lookup keys pair the nibbles of two tokens for one dim, so the
+        // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
+        // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
+        const uint32_t x1s = cur.v[1] << 4, x3s = cur.v[3] << 4;
+        const uint32_t E01 = (cur.v[0] & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
+        const uint32_t O01 = ((cur.v[0] >> 4) & 0x0F0F0F0Fu) | (cur.v[1] & 0xF0F0F0F0u);
+        const uint32_t E23 = (cur.v[2] & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
+        const uint32_t O23 = ((cur.v[2] >> 4) & 0x0F0F0F0Fu) | (cur.v[3] & 0xF0F0F0F0u);
         constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
-          uint32_t lk[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) lk[r] = lds_u32(lds, lut_addr(cur.v[r], off_v4, k));
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t sel = hh ? 0x07060302u : 0x05040100u;
-            const u32x2_t av = {__builtin_amdgcn_perm(lk[1], lk[0], sel), __builtin_amdgcn_perm(lk[3], lk[2], sel)};
+            const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
+                                lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
             o_acc[2 * k + hh] =
                 __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[2 * k + hh], 0, 0, 0);
           }
@@ -676,8 +685,8 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
           const float* slot = mrg + (wave - rd0) * C::SLOT_FLOATS;
           const float m2 = slot[8 * D + gq], l2 = slot[8 * D + 8 + gq];
           const float M = fmaxf(m_run, m2);
-          const float f1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-          const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+          const float f1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * w_col);
+          const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - M) * w_col);
 #pragma unroll
           for (int u = 0; u < C::R; ++u)
 #pragma unroll
@@ -718,8 +727,8 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
       }
       const bool empty = !(l_run > 0.f);
       const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
-      const float scale = empty ? 0.f : inv_sqrt_d / l_run;
-      const float lse = empty ? -INFINITY : (m_run + log2f(l_run)) * kLn2;
+      const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / l_run;
+      const float lse = empty ? -INFINITY : (m_run * w_col + log2f(l_run)) * kLn2;
       if (!lo_part && col_live) {
         const int hq = kvh * p.G + gq;
         const uint32_t sw = s_par[24 + ((R4 * a) >> 5)] >> ((R4 * a) & 31);
@@ -930,6 +939,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
     return set_error(TQ_ERR_VALUE, "shape arguments must be positive");
   if (num_q_heads % num_kv_heads != 0) return set_error(TQ_ERR_VALUE, "num_q_heads must be a multiple of num_kv_heads");
   if (num_splits <= 0) return set_error(TQ_ERR_VALUE, "num_splits must be >= 1");
+  if (!(scale > 0.f) || !(scale < INFINITY)) return set_error(TQ_ERR_VALUE, "scale must be positive and finite");
   if (block_size != TQ_BLOCK_SIZE) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "block_size must be 16");
   const int G = num_q_heads / num_kv_heads;
   if (G > 8) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "more than 8 q heads per kv head");

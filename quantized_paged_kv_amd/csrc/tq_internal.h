@@ -6,7 +6,7 @@
 
 #include <string>
 
-#include "../../include/tq.h"
+#include "tq.h"
 
 namespace tq {
 
