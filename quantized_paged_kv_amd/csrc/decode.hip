@@ -87,6 +87,7 @@ struct DecodeParams {
   uint8_t k_ch[128];
   int32_t v_half;            // LUT half that V reads
   int32_t q_f32, out_f32;
+  int32_t q_bytes;           // size of q in bytes (< 2^31)
 };
 
 __device__ __forceinline__ void record_error(int32_t* err, int32_t code, int32_t pos) {
@@ -129,8 +130,11 @@ struct Cfg {
   static constexpr int VLANE = VK == V4 ? D / 32 : D / 64;  // bytes per lane per token in V
   static constexpr bool MIXED = KK == KM43;
   static constexpr int LDS_LUT = kLutBytes + (MIXED ? kLut3Bytes : 0);
-  static constexpr int NSLOT = MIXED ? 2 : 3;             // merge slots (wave states); LDS <= 80 KB
-  static constexpr int SLOT_FLOATS = 8 * D + 16;          // O[8][D], m[8], l[8]
+  static constexpr int QS = D + D / 4 + 4;                // rotated-q row stride (floats), conflict-free rows
+  static constexpr int QV_FLOATS = NQK * 64 * 4;          // q.K B operands: NQK x 64 lanes x half8
+  static constexpr int Q_FLOATS = QV_FLOATS + 8 * QS;
+  static constexpr int DS = D + 4;                        // merge slot row stride (floats)
+  static_assert(kWaves * 8 * DS * 4 <= kLutBytes, "merge slots must fit the table area");
 };
 
 // Per-block raw loads of one wave.
@@ -143,34 +147,59 @@ struct Tile {
   uint2 vn;           // V norms
 };
 
+// Buffer descriptor flags word for raw (untyped) loads: 32-bit data format.
+constexpr int kBufFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufFlags);
+}
+
+// One wave's loads of a block: buffer loads against a per-block descriptor
+// (scalar base; lane offsets fixed for the whole kernel, constant parts in
+// the scalar offset), so that no vector address registers are live between
+// issue and use.  V rows narrower than 4 B per lane are still loaded as a
+// dword (the bytes past the lane's share stay inside the tile: the norm
+// area follows the last row) so the loaded value needs no zero extension.
 template <int D, int KK, int VK>
-__device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, const uint8_t* kt, const uint8_t* vt, uint32_t k_off,
-                                          uint32_t klo_off, uint32_t kn_off, uint32_t v_off, uint32_t vn_off) {
+__device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                          uint32_t k_off, uint32_t klo_off, uint32_t n_off, uint32_t v_off,
+                                          int k_norm_off, int v_norm_off) {
   using C = Cfg<D, KK, VK>;
   if constexpr (KK == K4 && D == 128) {
-    const uint4 x = *reinterpret_cast<const uint4*>(kt + k_off);
-    t.k[0] = x.x; t.k[1] = x.y; t.k[2] = x.z; t.k[3] = x.w;
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off, 0, 0);
+    t.k[0] = x[0]; t.k[1] = x[1]; t.k[2] = x[2]; t.k[3] = x[3];
   } else if constexpr ((KK == K4 && D == 64) || (KK != K4 && D == 128)) {
-    const uint2 x = *reinterpret_cast<const uint2*>(kt + k_off);
-    t.k[0] = x.x; t.k[1] = x.y;
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off, 0, 0);
+    t.k[0] = x[0]; t.k[1] = x[1];
   } else {
-    t.k[0] = *reinterpret_cast<const uint32_t*>(kt + k_off);
+    t.k[0] = __builtin_amdgcn_raw_buffer_load_b32(kr, k_off, 0, 0);
   }
   if constexpr (C::MIXED) {
-    const uint2 w = *reinterpret_cast<const uint2*>(kt + klo_off);
-    t.k_lo[0] = w.x;
-    t.k_lo[1] = w.y;
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, klo_off, 0, 0);
+    t.k_lo[0] = w[0];
+    t.k_lo[1] = w[1];
   }
-  t.kn[0] = *reinterpret_cast<const uint2*>(kt + kn_off);
-  if constexpr (C::MIXED) t.kn[1] = *reinterpret_cast<const uint2*>(kt + kn_off + 32u);
+  {
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, n_off, k_norm_off, 0);
+    t.kn[0] = uint2{w[0], w[1]};
+  }
+  if constexpr (C::MIXED) {
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, n_off, k_norm_off + 32, 0);
+    t.kn[1] = uint2{w[0], w[1]};
+  }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint8_t* row = vt + v_off + (uint32_t)(4 * r * C::VROW);
-    if constexpr (C::VLANE == 4) t.v[r] = *reinterpret_cast<const uint32_t*>(row);
-    else if constexpr (C::VLANE == 2) t.v[r] = *reinterpret_cast<const uint16_t*>(row);
-    else t.v[r] = *row;
+  for (int r = 0; r < 4; ++r) t.v[r] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off, 4 * r * C::VROW, 0);
+  {
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(vr, n_off, v_norm_off, 0);
+    t.vn = uint2{w[0], w[1]};
   }
-  t.vn = *reinterpret_cast<const uint2*>(vt + vn_off);
+}
+
+// Uniform read of a value the kernel never writes, through the scalar cache
+// (a constant-address-space load), so that waiting for it does not order it
+// with the vector loads in flight.
+__device__ __forceinline__ int scalar_ld(const int32_t* ptr, int idx) {
+  return ((const __attribute__((address_space(4))) int32_t*)ptr)[idx];
 }
 
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
@@ -249,8 +278,9 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
   constexpr int R4 = 4 * C::R;   // output dims per lane
   constexpr int NQK = C::NQK;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_LUT];
-  __shared__ __attribute__((aligned(16))) float mrg[C::NSLOT * C::SLOT_FLOATS];  // q buffer, then merge slots
-  __shared__ uint32_t s_par[64];
+  __shared__ __attribute__((aligned(16))) float qbuf[C::Q_FLOATS];  // q.K operands, rotated q
+  __shared__ float s_ml[kWaves * 16];   // per wave: running max and sum of each q head
+  __shared__ __attribute__((aligned(16))) uint32_t s_par[64];
   __shared__ int s_qexp[8];
 
   const int tid = threadIdx.x;
@@ -313,44 +343,63 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
     }
   }
   if (r0 >= r1) return;  // uniform across the workgroup
-  __syncthreads();       // s_par ready
 
   auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
-  // ---- LDS tables: byte-indexed, two halves of 128 B per entry
-  {
-    const int kind0 = p.half_kind[0], kind1 = p.half_kind[1];
-    for (int c = tid; c < kLutBytes / 16; c += kThreads) {
-      const int e = c >> 4, h = (c >> 3) & 1;
-      const int kind = h ? kind1 : kind0;
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (kind == 4) {
-        const uint32_t v = cb_half(h, e & 15) | (cb_half(h, e >> 4) << 16);
-        val = uint4{v, v, v, v};
-      } else if (kind == 2) {
-        const uint32_t ev = cb_half(h, e & 3) | (cb_half(h, (e >> 2) & 3) << 16);
-        const uint32_t od = cb_half(h, (e >> 4) & 3) | (cb_half(h, e >> 6) << 16);
-        val = uint4{ev, od, ev, od};
+  // LDS tables: byte-indexed, two halves of 128 B per entry.  The merge of
+  // the wave states reuses the start of this area, so the tables are built
+  // again for every piece (the 3-bit table lies past the merge slots).
+  auto build_tables = [&](bool with3) {
+    // thread -> 16 B chunk (16 e + lane & 15) of entry e = 16 e_hi + e_lo:
+    // lane & 15 walks the 256 B of an entry (8 chunks per half), so each
+    // store instruction writes 1 KB contiguous; e_lo is fixed per lane and
+    // e_hi = (wave >> 2) | 2 it, so the codebook word of e_hi is word it
+    // of the lane's half, its fp16 selected by wave >> 2.
+    // (the lane id goes through an empty asm so that none of this is hoisted
+    // out of the piece loop and kept live across it)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int h = (ln >> 3) & 1;
+    const int e_lo = (ln >> 4) | ((wave & 3) << 2);
+    const uint32_t wsh = (uint32_t)(wave >> 2) * 16u;
+    const int kind0 = uni(p.half_kind[0]), kind1 = uni(p.half_kind[1]);   // scalar reads
+    const int kind = h ? kind1 : kind0;
+    const uint4 w03 = *reinterpret_cast<const uint4*>(s_par + 8 * h);
+    const uint4 w47 = *reinterpret_cast<const uint4*>(s_par + 8 * h + 4);
+    const uint32_t cbw[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
+    const uint32_t lo_n = cb_half(h, e_lo);
+    const uint32_t ev = cb_half(h, e_lo & 3) | (cb_half(h, e_lo >> 2) << 16);
+    uint4* dst = reinterpret_cast<uint4*>(lds) + (ln & 15) + 16 * e_lo + 256 * (wave >> 2);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      // nibble table: (cb[e & 15], cb[e >> 4]);
+      // crumb table: (cb[e & 3], cb[(e >> 2) & 3]), (cb[(e >> 4) & 3], cb[e >> 6])
+      const uint32_t v4 = lo_n | (((cbw[it] >> wsh) & 0xFFFFu) << 16);
+      const uint32_t c2 = (cbw[it & 1] >> wsh) & 0xFFFFu;
+      const uint32_t c3 = (cbw[it >> 2] >> (16 * ((it >> 1) & 1))) & 0xFFFFu;
+      const uint32_t od = c2 | (c3 << 16);
+      const uint32_t x0 = kind == 4 ? v4 : (kind == 2 ? ev : 0u);
+      const uint32_t x1 = kind == 4 ? v4 : (kind == 2 ? od : 0u);
+      dst[512 * it] = uint4{x0, x1, x0, x1};
+    }
+    if constexpr (C::MIXED) {
+      if (with3) {
+        for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
+          const int e = c >> 2;
+          const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
+          const uint32_t hi = (s_par[16 + ((e >> 3) >> 1)] >> (16 * ((e >> 3) & 1))) & 0xFFFFu;
+          const uint32_t v = lo | (hi << 16);
+          reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
+        }
       }
-      reinterpret_cast<uint4*>(lds)[c] = val;
     }
-  }
-  if constexpr (C::MIXED) {
-    for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
-      const int e = c >> 2;
-      const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint32_t hi = (s_par[16 + ((e >> 3) >> 1)] >> (16 * ((e >> 3) & 1))) & 0xFFFFu;
-      const uint32_t v = lo | (hi << 16);
-      reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
-    }
-  }
+  };
 
   // ---- per-lane roles
   const int j = lane & 15;          // MFMA column: q head j & 7, high (j < 8) or low part
   const int a = lane >> 4;          // token group: tokens a, a+4, a+8, a+12 of a block
   const int gq = j & 7;
   const bool lo_part = j >= 8;
-  const bool col_live = gq < p.G;
   const uint32_t off4_k = (uint32_t)(lane & 31) * 4u;                      // K nibble table, half 0
   const uint32_t off2_k = (uint32_t)(lane & 15) * 8u;                      // K crumb table, half 0
   const uint32_t off_v4 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 31) * 4u;
@@ -361,17 +410,19 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
   constexpr int KLANE = KK == K4 ? D / 8 : (KK == K2 ? D / 16 : D / 16);   // index bytes of the (high) group
   const uint32_t k_off = (uint32_t)(tokK * C::KROW + KLANE * a);
   const uint32_t klo_off = (uint32_t)((tokK * C::KROW + D / 4 + (3 * D / 64) * a) & ~3);
-  const uint32_t kn_off = (uint32_t)(p.k_norm_off + 8 * a);
+  const uint32_t n_off = (uint32_t)(8 * a);   // this lane's 4 norms, after the tile's norm offset
   const uint32_t v_off = (uint32_t)(a * C::VROW + C::VLANE * j);
-  const uint32_t vn_off = (uint32_t)(p.v_norm_off + 8 * a);
   const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
   const int64_t v_blk_stride = (int64_t)p.Hkv * p.v_tile;
   const int cap = p.max_blocks * 16;
+  float* const qf_all = qbuf + C::QV_FLOATS;   // rotated q, row g at g * QS, 4 pad floats per 16 channels
+  float* const slots = reinterpret_cast<float*>(lds);   // merge: wave w, head g row at (8 w + g) * DS
 
   // ---- walk the pieces of this workgroup's range
   int s, kvh, blk, nb_s;
   locate(p, lane, r0, s, kvh, blk, nb_s);
   int pos = r0;
+  bool first = true;
   while (pos < r1) {
     const int seg_start = pos - blk;
     const int b0 = blk;
@@ -379,42 +430,84 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
     // one piece: the final output is written here (always so when P == 1)
     const bool whole = p.P == 1 || (seg_start / R) == ((seg_start + nb_s - 1) / R);
     const int piece = (int)blockIdx.x - seg_start / R;
-    const int ctx = clamp_ctx(p.context_lens[s], cap);
+    const int ctx = clamp_ctx(scalar_ld(p.context_lens, s), cap);
+    const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
+    const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
+    const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
 
-    // -------- rotate the G q heads of (s, kvh) once: mrg[g*D + ch] = (H (s_K * q))[ch]
-    __syncthreads();  // the previous piece's merge slots are free
+    // -------- issue the long-latency loads first: this wave's first 64
+    // block-table entries, and (wave 0) the G raw q rows
+    const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;  // blocks of this wave
+    int cnt = nbw < 64 ? nbw : 64;
+    int bt_reg = 0;
+    if (lane < cnt) bt_reg = bt_row[b0 + wave + kWaves * lane];
+    constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per head
+    const int g8 = lane >> 3, l8 = lane & 7;
+    const bool q_live = g8 < p.G;
+    // raw q words of this lane's PER channels (bf16: two per word, the upper
+    // half of qw unused); one load shape for both dtypes, bytes past the q
+    // tensor read as zero through the descriptor's range check
+    uint32_t qw[PER];
+    {   // issued by every wave (only wave 0 uses them) so that all paths
+        // carry the same loads and later waits count exactly
+      const int esz = p.q_f32 ? 4 : 2;
+      const int head0 = uni((int)(((int64_t)s * p.Hq + kvh * p.G) * D * esz));   // first q row of the group
+      const uint32_t lane_off = (uint32_t)(((q_live ? g8 : 0) * D + l8 * PER) * esz);
+      const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
+#pragma unroll
+      for (int i = 0; i < PER / 4; ++i) {
+        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
+        qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
+      }
+    }
+
+    __syncthreads();  // first piece: s_par ready; later pieces: merge slots free
+    build_tables(first);
+    first = false;
+
+    // -------- bad block-table entries of a chunk: reported, then skipped
+    auto check_chunk = [&](int chunk0) -> uint64_t {
+      const bool bad = lane < cnt && (bt_reg < 0 || (int64_t)bt_reg >= p.num_blocks);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(bad);
+      if (m) {
+        if (lane == (int)__builtin_ctzll(m))
+          record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + wave + kWaves * (chunk0 + lane));
+        if (bad) bt_reg = 0;
+      }
+      return m;
+    };
+    auto ptrs = [&](int it, __amdgpu_buffer_rsrc_t& kt, __amdgpu_buffer_rsrc_t& vt) {
+      const int64_t ph = __builtin_amdgcn_readlane(bt_reg, it);
+      kt = tile_rsrc(k_head + ph * k_blk_stride, p.k_tile);
+      vt = tile_rsrc(v_head + ph * v_blk_stride, p.v_tile);
+    };
+    uint64_t badm = check_chunk(0);
+    Tile<D, KK, VK> A, B;
+    __amdgpu_buffer_rsrc_t kt, vt;
+    // first tile in flight during the q rotation (issued even when this wave
+    // has no block: then it reads block 0 of the pool, unused)
+    ptrs(0, kt, vt);
+    load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
+
+    // -------- rotate the G q heads of (s, kvh) once: row g of the rotated q
+    // is H (s_K * q_g), unnormalised
     if (wave == 0) {
-      constexpr int PER = D / 8;              // channels per lane, 8 lanes per head
-      const int g = lane >> 3, l8 = lane & 7;
-      const bool live = g < p.G;
-      const int hq = kvh * p.G + (live ? g : 0);
-      const int64_t base = ((int64_t)s * p.Hq + hq) * D + l8 * PER;
       float x[PER];
       if (p.q_f32) {
-        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + base);
 #pragma unroll
-        for (int v4 = 0; v4 < PER / 4; ++v4) {
-          const float4 t = src[v4];
-          x[4 * v4] = t.x; x[4 * v4 + 1] = t.y; x[4 * v4 + 2] = t.z; x[4 * v4 + 3] = t.w;
-        }
+        for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
       } else {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + base);
 #pragma unroll
-        for (int v8 = 0; v8 < PER / 8; ++v8) {
-          const uint4 t = src[v8];
-          const uint32_t w4[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            x[8 * v8 + 2 * k] = __uint_as_float(w4[k] << 16);
-            x[8 * v8 + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
-          }
+        for (int k = 0; k < PER / 2; ++k) {
+          x[2 * k] = __uint_as_float(qw[k] << 16);
+          x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
         }
       }
       const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         if ((sw >> e) & 1u) x[e] = -x[e];
-        if (!live) x[e] = 0.f;
+        if (!q_live) x[e] = 0.f;
       }
 #pragma unroll
       for (int h = 1; h < PER; h <<= 1) {
@@ -436,62 +529,66 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
         }
       }
       float amax = 0.f;
+      float* qrow = qf_all + g8 * C::QS;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        mrg[g * D + l8 * PER + e] = x[e];
-        amax = fmaxf(amax, fabsf(x[e]));
+      for (int i = 0; i < PER / 4; ++i) {
+        const int c = l8 * PER + 4 * i;
+        *reinterpret_cast<float4*>(qrow + c + 4 * (c >> 4)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
       }
+#pragma unroll
+      for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
       for (int k = 1; k < 8; k <<= 1) amax = fmaxf(amax, __shfl_xor(amax, k));
       if (l8 == 0) {
         int ex = 0;
         if (amax > 0.f) frexpf(amax, &ex);
-        s_qexp[g] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
+        s_qexp[g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
       }
     }
-    __syncthreads();
+    __syncthreads();  // rotated q and tables ready
 
-    // q.K B operands, per lane (column j, channel chunk a): built once per
-    // piece and kept in LDS (the first 4 KB of the merge area), shared by
-    // all waves and re-read per block, which keeps 16 VGPRs free.
-    {
-      const int kq = s_qexp[gq];
-      const float q_pow = ldexpf(1.0f, kq);
-      half8_t qv[NQK];
-#pragma unroll
-      for (int t = 0; t < NQK; ++t) {
+    // q.K B operands (column j, channel chunk a), one MFMA per wave: the
+    // scaled rotated q split into an fp16 high part (columns 0-7) and the
+    // fp16 rounding of the remainder (columns 8-15); kept in LDS, re-read
+    // per block by every wave.
+    if (wave < NQK) {
+      const int t = wave;
+      const float q_pow = ldexpf(1.0f, s_qexp[gq]);
+      const float* qrow = qf_all + gq * C::QS;
+      float vq[8];
+      if constexpr (C::MIXED) {
+        constexpr int m = D / 2;
+        constexpr int per_g = NQK / 2;
+        const int grp = t / per_g, u = t % per_g;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          int pos_l;
-          if constexpr (C::MIXED) {
-            constexpr int m = D / 2;
-            constexpr int per_g = NQK / 2;
-            const int grp = t / per_g, u = t % per_g;
-            pos_l = grp * m + a * (m / 4) + 8 * u + e;
-          } else {
-            pos_l = a * (D / 4) + 8 * t + e;
-          }
-          const int chn = C::MIXED ? (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu) : pos_l;
-          const float v = mrg[gq * D + chn] * q_pow;
-          const _Float16 hi = (_Float16)v;
-          const _Float16 lo = (_Float16)(v - (float)hi);
-          qv[t][e] = lo_part ? lo : hi;
+          const int pos_l = grp * m + a * (m / 4) + 8 * u + e;
+          const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
+          vq[e] = qrow[chn + 4 * (chn >> 4)];
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = a * (D / 4) + 8 * t + 4 * h;
+          const float4 f = *reinterpret_cast<const float4*>(qrow + c + 4 * (c >> 4));
+          vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
         }
       }
-      __syncthreads();  // all waves have read the rotated q
-      if (wave == 0) {
+      half8_t qv;
 #pragma unroll
-        for (int t = 0; t < NQK; ++t) reinterpret_cast<half8_t*>(mrg)[t * 64 + lane] = qv[t];
+      for (int e = 0; e < 8; ++e) {
+        const float v = vq[e] * q_pow;
+        const _Float16 hi = (_Float16)v;
+        const _Float16 lo = (_Float16)(v - (float)hi);
+        qv[e] = lo_part ? lo : hi;
       }
+      reinterpret_cast<half8_t*>(qbuf)[t * 64 + lane] = qv;
     }
-    const float w_col = ldexpf(p.score_mul, -s_qexp[gq]);
-    const half8_t* qb = reinterpret_cast<const half8_t*>(mrg) + lane;   // qb[64 * t]: operand of MFMA t
     __syncthreads();  // operands ready
+    const float w_col = ldexpf(p.score_mul, -s_qexp[gq]);
+    const half8_t* qb = reinterpret_cast<const half8_t*>(qbuf) + lane;   // qb[64 * t]: operand of MFMA t
 
     // -------- stream this wave's blocks of the piece
-    const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
-    const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
-    const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
     float m_run = -INFINITY, l_run = 0.f;
     float4_t o_acc[C::R];
 #pragma unroll
@@ -626,140 +723,110 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
       }
     };
 
-    const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;  // blocks of this wave
-    for (int chunk0 = 0; chunk0 < nbw; chunk0 += 64) {
-      const int cnt = (nbw - chunk0) < 64 ? (nbw - chunk0) : 64;
-      int bt_reg = 0;
-      if (lane < cnt) bt_reg = bt_row[b0 + wave + kWaves * (chunk0 + lane)];
-      const bool bad = lane < cnt && (bt_reg < 0 || (int64_t)bt_reg >= p.num_blocks);
-      const uint64_t badm = __builtin_amdgcn_ballot_w64(bad);
-      if (badm) {
-        if (lane == (int)__builtin_ctzll(badm))
-          record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + wave + kWaves * (chunk0 + lane));
-        if (bad) bt_reg = 0;
-      }
-      auto ptrs = [&](int it, const uint8_t*& kt, const uint8_t*& vt) {
-        const int64_t ph = __builtin_amdgcn_readlane(bt_reg, it);
-        kt = k_head + ph * k_blk_stride;
-        vt = v_head + ph * v_blk_stride;
-      };
-      Tile<D, KK, VK> A, B;
-      const uint8_t *kt, *vt;
-      ptrs(0, kt, vt);
-      load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, kn_off, v_off, vn_off);
+    for (int chunk0 = 0; cnt > 0;) {
       int it = 0;
       for (;;) {
         ptrs(it + 1 < cnt ? it + 1 : it, kt, vt);
-        load_tile<D, KK, VK>(B, kt, vt, k_off, klo_off, kn_off, v_off, vn_off);
+        load_tile<D, KK, VK>(B, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
         compute(A, b0 + wave + kWaves * (chunk0 + it), !((badm >> it) & 1ull));
         if (++it >= cnt) break;
         ptrs(it + 1 < cnt ? it + 1 : it, kt, vt);
-        load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, kn_off, v_off, vn_off);
+        load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
         compute(B, b0 + wave + kWaves * (chunk0 + it), !((badm >> it) & 1ull));
         if (++it >= cnt) break;
       }
+      chunk0 += 64;
+      if (chunk0 >= nbw) break;
+      cnt = (nbw - chunk0) < 64 ? (nbw - chunk0) : 64;
+      bt_reg = 0;
+      if (lane < cnt) bt_reg = bt_row[b0 + wave + kWaves * (chunk0 + lane)];
+      badm = check_chunk(chunk0);
+      ptrs(0, kt, vt);
+      load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
     }
 
-    // -------- merge the 8 wave states (LDS tree), rotated domain
-    __syncthreads();  // every wave is done with the q operands in the merge area
+    // -------- merge the 8 wave states through LDS, rotated domain.  Wave w
+    // stores its unnormalised O rows (head g at slot row 8 w + g) and its
+    // running max / sum; wave g then combines head g over the waves.
+    __syncthreads();  // every wave is done with the tables and the q operands
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    {
-      int active = kWaves;
-      while (active > 1) {
-        const int k = (active / 2 < C::NSLOT) ? active / 2 : C::NSLOT;
-        const int wr0 = active - k, rd0 = active - 2 * k;
-        if (wave >= wr0 && wave < active && !lo_part) {
-          float* slot = mrg + (wave - wr0) * C::SLOT_FLOATS;
+    if (!lo_part) {
+      float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
 #pragma unroll
-          for (int u = 0; u < C::R; ++u)
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) slot[gq * D + R4 * a + C::R * e + u] = o_acc[u][e];
-          if (a == 0) {
-            slot[8 * D + gq] = m_run;
-            slot[8 * D + 8 + gq] = l_run;
-          }
-        }
-        __syncthreads();
-        if (wave >= rd0 && wave < wr0) {
-          const float* slot = mrg + (wave - rd0) * C::SLOT_FLOATS;
-          const float m2 = slot[8 * D + gq], l2 = slot[8 * D + 8 + gq];
-          const float M = fmaxf(m_run, m2);
-          const float f1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_run - M) * w_col);
-          const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m2 - M) * w_col);
-#pragma unroll
-          for (int u = 0; u < C::R; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o_acc[u][e] = f1 * o_acc[u][e] + f2 * slot[gq * D + R4 * a + C::R * e + u];
-          l_run = f1 * l_run + f2 * l2;
-          m_run = M;
-        }
-        __syncthreads();
-        active -= k;
+        for (int h = 0; h < C::R / 4; ++h)
+          *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
+              float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
+      if (a == 0) {
+        s_ml[16 * wave + gq] = m_run;
+        s_ml[16 * wave + 8 + gq] = l_run;
       }
     }
+    __syncthreads();
 
-    // -------- wave 0: normalise, inverse rotation, write
-    if (wave == 0) {
-      float y[R4];
+    // -------- wave g: combine, normalise, inverse rotation, write head g.
+    // Lane l holds dims l + 64 i; the rotation's top stage (D = 128) is in
+    // the lane, the others pair lanes.
+    if (wave < p.G) {
+      const int g = wave;
+      const float wc = ldexpf(p.score_mul, -s_qexp[g]);
+      float M = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < C::R; ++u)
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[16 * w + g]);
+      constexpr int NY = D / 64;
+      float y[NY];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[C::R * e + u] = o_acc[u][e];
+      for (int i = 0; i < NY; ++i) y[i] = 0.f;
+      float L = 0.f;
 #pragma unroll
-      for (int h = 1; h < R4; h <<= 1) {
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = s_ml[16 * w + g];
+        const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * wc);
+        L = __builtin_fmaf(f, s_ml[16 * w + 8 + g], L);
+        const float* srow = slots + (8 * w + g) * C::DS;
 #pragma unroll
-        for (int e = 0; e < R4; ++e)
-          if ((e & h) == 0) {
-            const float a0 = y[e], b0v = y[e + h];
-            y[e] = a0 + b0v;
-            y[e + h] = a0 - b0v;
-          }
+        for (int i = 0; i < NY; ++i) y[i] = __builtin_fmaf(f, srow[lane + 64 * i], y[i]);
+      }
+      if constexpr (NY == 2) {
+        const float t0 = y[0];
+        y[0] = t0 + y[1];
+        y[1] = t0 - y[1];
       }
 #pragma unroll
-      for (int k = 16; k < 64; k <<= 1) {
+      for (int k = 32; k > 0; k >>= 1) {
         const bool up = (lane & k) != 0;
 #pragma unroll
-        for (int e = 0; e < R4; ++e) {
-          const float o = __shfl_xor(y[e], k);
-          y[e] = up ? (o - y[e]) : (y[e] + o);
+        for (int i = 0; i < NY; ++i) {
+          const float o = __shfl_xor(y[i], k);
+          y[i] = up ? (o - y[i]) : (y[i] + o);
         }
       }
-      const bool empty = !(l_run > 0.f);
+      const bool empty = !(L > 0.f);
       const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
-      const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / l_run;
-      const float lse = empty ? -INFINITY : (m_run * w_col + log2f(l_run)) * kLn2;
-      if (!lo_part && col_live) {
-        const int hq = kvh * p.G + gq;
-        const uint32_t sw = s_par[24 + ((R4 * a) >> 5)] >> ((R4 * a) & 31);
+      const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
+      const float lse = empty ? -INFINITY : (M * wc + log2f(L)) * kLn2;
+      const int hq = kvh * p.G + g;
 #pragma unroll
-        for (int e = 0; e < R4; ++e) y[e] = ((sw >> e) & 1u) ? -y[e] * scale : y[e] * scale;
-        if (whole) {
-          const int64_t off = ((int64_t)s * p.Hq + hq) * D + R4 * a;
-          if (p.out_f32) {
-            float4* dst = reinterpret_cast<float4*>(static_cast<float*>(p.out) + off);
+      for (int i = 0; i < NY; ++i) {
+        const int d = lane + 64 * i;
+        const float sv = y[i] * scale;
+        y[i] = ((s_par[24 + (d >> 5)] >> (d & 31)) & 1u) ? -sv : sv;
+      }
+      if (whole) {
+        const int64_t off = ((int64_t)s * p.Hq + hq) * D + lane;
 #pragma unroll
-            for (int e = 0; e < R4 / 4; ++e) dst[e] = float4{y[4 * e], y[4 * e + 1], y[4 * e + 2], y[4 * e + 3]};
-          } else {
-            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + off);
-#pragma unroll
-            for (int e = 0; e < R4 / 8; ++e) {
-              uint32_t w4[4];
-#pragma unroll
-              for (int k = 0; k < 4; ++k)
-                w4[k] = (uint32_t)f32_to_bf16_rne(y[8 * e + 2 * k]) |
-                        ((uint32_t)f32_to_bf16_rne(y[8 * e + 2 * k + 1]) << 16);
-              dst[e] = uint4{w4[0], w4[1], w4[2], w4[3]};
-            }
-          }
-          if (a == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
-        } else {
-          const int64_t row = ((int64_t)s * p.Hq + hq) * p.P + piece;
-          float4* dst = reinterpret_cast<float4*>(p.part_o + row * D + R4 * a);
-#pragma unroll
-          for (int e = 0; e < R4 / 4; ++e) dst[e] = float4{y[4 * e], y[4 * e + 1], y[4 * e + 2], y[4 * e + 3]};
-          if (a == 0) p.part_lse[row] = lse;
+        for (int i = 0; i < NY; ++i) {
+          if (p.out_f32) static_cast<float*>(p.out)[off + 64 * i] = y[i];
+          else static_cast<uint16_t*>(p.out)[off + 64 * i] = f32_to_bf16_rne(y[i]);
         }
+        if (lane == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
+      } else {
+        const int64_t row = ((int64_t)s * p.Hq + hq) * p.P + piece;
+#pragma unroll
+        for (int i = 0; i < NY; ++i) p.part_o[row * D + lane + 64 * i] = y[i];
+        if (lane == 0) p.part_lse[row] = lse;
       }
     }
 
@@ -771,7 +838,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
       kvh = 0;
       do {
         ++s;
-        nb_s = (clamp_ctx(p.context_lens[s], cap) + 15) >> 4;
+        nb_s = (clamp_ctx(scalar_ld(p.context_lens, s), cap) + 15) >> 4;
       } while (nb_s == 0);
     }
   }
@@ -957,6 +1024,8 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   const int64_t work_bound = (int64_t)num_seqs * num_kv_heads * max_blocks_per_seq;
   if (work_bound >= (1ll << 30) || max_blocks_per_seq > (1 << 20))
     return set_error(TQ_ERR_VALUE, "too much work for one call (2^30 block-heads, 2^20 blocks per sequence)");
+  const int64_t q_bytes = (int64_t)num_seqs * num_q_heads * D * (q_dtype == TQ_F32 ? 4 : 2);
+  if (q_bytes >= (1ll << 31)) return set_error(TQ_ERR_VALUE, "q must be smaller than 2 GiB");
 
   DecodeParams p = {};
   p.q = q;
@@ -1007,6 +1076,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
     for (int i = 0; i < 8; ++i) p.k3_cb[i] = kfmt->codebook[1][i];
   p.q_f32 = q_dtype == TQ_F32;
   p.out_f32 = out_dtype == TQ_F32;
+  p.q_bytes = (int32_t)q_bytes;
   if (num_splits > 1) {
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (int64_t)num_seqs * num_q_heads * num_splits * D;
