@@ -195,13 +195,13 @@ def cpu_baseline(index, budget_s=12.0):
             Vp = np.zeros((len(bt), 1, opg.tile_layout(vof, 16)[2]), np.uint8)
             for a in range(0, n, 16384):
                 opg.write_pages(xk[a:a + 16384, h:h + 1], sl[a:a + 16384], Kp, kof, 16)
-                opg.write_pages(xv[a:a + 16384, h:h + 1], sl[a:a + 16384], Vp, vof, 16)
+                opg.write_pages(xv[a:a + 16384, h:h + 1], sl[a:a + 16384], Vp, vof, 16, "v")
             pools.append((Kp, Vp))
         t0 = time.perf_counter()
         for h in range(w.num_kv_heads):
             Kp, Vp = pools[h]
             K = opg.reconstruct_sequence(Kp, bt, n, 0, kof, 16)
-            V = opg.reconstruct_sequence(Vp, bt, n, 0, vof, 16)
+            V = opg.reconstruct_sequence(Vp, bt, n, 0, vof, 16, role="v")
             for g in range(G):
                 oatt.attention(q[s, h * G + g].astype(np.float64), K, V, w.scale)
         total_t += time.perf_counter() - t0

@@ -91,7 +91,7 @@ def decode_reference(q: np.ndarray, k_pages, v_pages, block_tables, context_lens
         if key not in cache:
             n = int(context_lens[s])
             K = reconstruct_sequence(k_pages, block_tables[s], n, kvh, kfmt, block_size)
-            V = reconstruct_sequence(v_pages, block_tables[s], n, kvh, vfmt, block_size)
+            V = reconstruct_sequence(v_pages, block_tables[s], n, kvh, vfmt, block_size, role="v")
             cache = {key: (K, V)}
         K, V = cache[key]
         out[s, h], lse[s, h] = attention(q[s, h], K, V, scale)

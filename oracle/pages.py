@@ -7,14 +7,20 @@ read back through block tables.  [D "Data Ownership"]: the page cache owns
 vLLM-style uint8 pages.  [D "Error Model"]: slots outside the allocated
 pages are IndexErrors.
 
-Layout (readings R10, R11): pages are [num_blocks][num_kv_heads][tile].  A
-tile holds block_size rows of packed indices (the index plane, row `offset`
-at byte offset*row_bytes) followed by the norm plane, fp16 little-endian,
-group-major, with the 16 rows of a block in interleaved slots: the norm of
-group g for the row at in-block offset t sits at
-block_size*row_bytes + (g*block_size + norm_slot(t))*2, where
+Layout (readings R10, R11, R24): pages are [num_blocks][num_kv_heads][tile].
+A tile holds the index plane of block_size packed rows followed by the norm
+plane, fp16 little-endian, group-major, with the 16 rows of a block in
+interleaved slots: the norm of group g for the row at in-block offset t sits
+at block_size*row_bytes + (g*block_size + norm_slot(t))*2, where
 norm_slot(t) = 4*(t % 4) + t // 4.  The tile is padded to a multiple of 16
 bytes.  Only block_size 16 is defined.
+
+Index plane: in K pages ("k" role) row t occupies bytes
+[t*row_bytes, (t+1)*row_bytes).  In V pages ("v" role), when row_bytes is a
+multiple of 16, the plane is lane-major: with c = row_bytes / 16, byte b of
+row t sits at ((16*(t % 4) + b // c)*4 + t // 4)*c + b % c, i.e. 64 runs of
+4*c bytes, run 16*q + j holding bytes [c*j, c*(j+1)) of rows q, q+4, q+8,
+q+12 in that order; other V formats use the K layout.
 """
 from __future__ import annotations
 
@@ -29,6 +35,24 @@ def norm_slot(t):
     return 4 * (np.asarray(t) % 4) + np.asarray(t) // 4
 
 
+def lane_chunk(fmt: Format, role: str) -> int:
+    """Bytes per lane run of the V index plane (0: rows are contiguous)."""
+    if role not in ("k", "v"):
+        raise ValueError("role must be 'k' or 'v'")
+    rb = row_bytes(fmt)
+    return rb // 16 if role == "v" and rb % 16 == 0 else 0
+
+
+def row_positions(rb: int, t, chunk: int) -> np.ndarray:
+    """Tile byte offsets of bytes 0..rb-1 of the rows at in-block offsets t:
+    array [len(t), rb]."""
+    t = np.asarray(t, dtype=np.int64).reshape(-1, 1)
+    b = np.arange(rb, dtype=np.int64)[None, :]
+    if chunk == 0:
+        return t * rb + b
+    return ((16 * (t % 4) + b // chunk) * 4 + t // 4) * chunk + b % chunk
+
+
 def tile_layout(fmt: Format, block_size: int):
     """(row_idx_bytes, norm_plane_offset, tile_bytes)."""
     if block_size != 16:
@@ -41,15 +65,17 @@ def tile_layout(fmt: Format, block_size: int):
 
 
 def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt: Format,
-                block_size: int) -> None:
+                block_size: int, role: str = "k") -> None:
     """Quantise rows x[T, H, d] and store them in pages[num_blocks, H, tile]
-    at the rows named by slot_mapping[T].  Bytes outside the written rows and
-    norm slots are left untouched."""
+    at the rows named by slot_mapping[T] (role "k" or "v" picks the index
+    plane layout).  Bytes outside the written rows and norm slots are left
+    untouched."""
     x = np.asarray(x)
     slots = np.asarray(slot_mapping, dtype=np.int64)
     T, H, d = x.shape
     nb = pages.shape[0]
     rb, norm_off, tile = tile_layout(fmt, block_size)
+    chunk = lane_chunk(fmt, role)
     if pages.dtype != np.uint8 or pages.shape[1:] != (H, tile):
         raise ValueError("page pool shape does not match the format")
     if slots.shape != (T,):
@@ -64,9 +90,10 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
     off = slots % block_size
     idx_groups, norms = encode_rows(x, fmt)              # [T, H, m] per group, [T, H, G]
     data = pack_row(idx_groups, fmt)                      # [T, H, rb]
+    pos_rows = row_positions(rb, off, chunk)              # [T, rb]
     for h in range(H):
         for b in range(rb):
-            pages[blk, h, off * rb + b] = data[:, h, b]
+            pages[blk, h, pos_rows[:, b]] = data[:, h, b]
         for g in range(fmt.num_groups):
             pos = norm_off + (g * block_size + norm_slot(off)) * 2
             pages[blk, h, pos] = (norms[:, h, g] & 0xFF).astype(np.uint8)
@@ -74,14 +101,14 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
 
 
 def read_rows(pages: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, head: int, fmt: Format,
-              block_size: int):
+              block_size: int, role: str = "k"):
     """Unpack the rows at (blocks[i], offsets[i]) of one kv head ->
     (index arrays per group, fp16 norm bits [n, G])."""
     rb, norm_off, tile = tile_layout(fmt, block_size)
     blocks = np.asarray(blocks, dtype=np.int64)
     offsets = np.asarray(offsets, dtype=np.int64)
     t = pages[blocks, head]                                          # [n, tile]
-    cols = offsets[:, None] * rb + np.arange(rb)[None, :]
+    cols = row_positions(rb, offsets, lane_chunk(fmt, role))
     data = np.take_along_axis(t, cols, axis=1)
     idx = unpack_row(data, fmt)
     norms = np.empty((len(blocks), fmt.num_groups), dtype=np.uint16)
@@ -94,7 +121,7 @@ def read_rows(pages: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, head: 
 
 
 def reconstruct_sequence(pages: np.ndarray, block_table_row: np.ndarray, ctx: int, head: int,
-                         fmt: Format, block_size: int, rotated: bool = False) -> np.ndarray:
+                         fmt: Format, block_size: int, rotated: bool = False, role: str = "k") -> np.ndarray:
     """Dense float64 K or V rows [ctx, d] of one sequence and kv head, walked
     through its block table ([D "Diagnostic Route Design"]: dense
     reconstruction is a diagnostic, allowed for validation only).  With
@@ -104,6 +131,6 @@ def reconstruct_sequence(pages: np.ndarray, block_table_row: np.ndarray, ctx: in
     blocks = bt[t // block_size]
     if np.any(blocks < 0) or np.any(blocks >= pages.shape[0]):
         raise IndexError("block table entry outside the page pool")
-    idx, norms = read_rows(pages, blocks, t % block_size, head, fmt, block_size)
+    idx, norms = read_rows(pages, blocks, t % block_size, head, fmt, block_size, role)
     y = dequantize_rotated(idx, norms, fmt)
     return y if rotated else inverse_rotate(y, fmt.signs)

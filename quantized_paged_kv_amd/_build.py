@@ -2,9 +2,10 @@
 
 Usage: python -m quantized_paged_kv_amd._build   (or build() from Python)
 
-Every HIP source is compiled with the packed-FP32 target feature off, and
-the quantise-on-write source additionally with -ffp-contract=off so that no
-multiply-add is fused on the bit-exact fp64 path.
+Every HIP source is compiled with the packed-FP32 target feature off, the
+quantise-on-write source additionally with -ffp-contract=off so that no
+multiply-add is fused on the bit-exact fp64 path, and the decode source
+without the atomic optimizer (its block counter is read one block late).
 """
 from __future__ import annotations
 
@@ -28,7 +29,10 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno
 SOURCES = {
     "tq_host.cpp": ["-x", "hip"],
     "write_kv.hip": ["-ffp-contract=off"],
-    "decode.hip": [],
+    # one lane takes the next block index with an LDS atomic whose result is
+    # read a block later; the atomic optimizer would turn it into a wave-wide
+    # reduction that waits for the result immediately
+    "decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }
 
 

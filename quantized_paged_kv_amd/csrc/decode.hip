@@ -53,10 +53,11 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 16;   // one workgroup per CU
 constexpr int kThreads = kWaves * 64;
 constexpr int kLutBytes = 65536;    // 256 entries x 256 B (two halves)
 constexpr int kLut3Bytes = 4096;    // 64 entries x 16 copies x 4 B
+constexpr int kBtCap = 2048;        // block-table entries of a piece staged in LDS
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum KKind { K4 = 0, K2 = 1, KM43 = 2 };
@@ -73,10 +74,12 @@ struct DecodeParams {
   float* part_o;     // [S][Hq][P][D]
   float* part_lse;   // [S][Hq][P]
   int32_t* dev_err;
-  int64_t num_blocks;
+  int64_t num_blocks;        // < 2^31
   int32_t S, Hq, Hkv, G, max_blocks, P;
+  int32_t HG, NG;    // kv heads per workgroup group (1, 2, 4 or 8) and groups (Hkv / HG)
   int32_t n_wg;      // grid size (persistent workgroups)
   int32_t k_tile, v_tile, k_norm_off, v_norm_off;
+  uint32_t k_span, v_span;   // bytes of each pool (< 4 GiB)
   float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K)), > 0
   float v_mul;       // 1 / sqrt(m_V), applied once in the epilogue
   uint32_t v_signs[4];
@@ -116,6 +119,45 @@ __device__ __forceinline__ float row_ror8(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
+// x * (fp16 half HI of w) in one v_fma_mix (the f16 operand is read as is:
+// f16 denormal norms count as zero, which only drops contributions below
+// 2^-14 relative to the row's scale)
+template <int HI>
+__device__ __forceinline__ float mul_h(float x, uint32_t w) {
+  float r;
+  if constexpr (HI) asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
+  else asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
+  return r;
+}
+// x * (fp16 half HI of w) + y
+template <int HI>
+__device__ __forceinline__ float fma_h(float x, uint32_t w, float y) {
+  float r;
+  if constexpr (HI) asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w), "v"(y));
+  else asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w), "v"(y));
+  return r;
+}
+// fp16 pair (x0 * half 0 of w, x1 * half 1 of w), each rounded once
+__device__ __forceinline__ uint32_t mul_h2(float x0, float x1, uint32_t w) {
+  uint32_t r = 0;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x0), "v"(w));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x1), "v"(w));
+  return r;
+}
+// max of two floats known not to be NaN (no canonicalisation)
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// max over the lanes l, l^16, l^32, l^48 (gfx950 row and half swaps)
+__device__ __forceinline__ float max_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return max_nn(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+
 __device__ __forceinline__ float half_at(uint2 w, int e) {
   const uint32_t d = (e >> 1) ? w.y : w.x;
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(d >> (16 * (e & 1))));
@@ -131,10 +173,11 @@ struct Cfg {
   static constexpr bool MIXED = KK == KM43;
   static constexpr int LDS_LUT = kLutBytes + (MIXED ? kLut3Bytes : 0);
   static constexpr int QS = D + D / 4 + 4;                // rotated-q row stride (floats), conflict-free rows
-  static constexpr int QV_FLOATS = NQK * 64 * 4;          // q.K B operands: NQK x 64 lanes x half8
-  static constexpr int Q_FLOATS = QV_FLOATS + 8 * QS;
-  static constexpr int DS = D + 4;                        // merge slot row stride (floats)
-  static_assert(kWaves * 8 * DS * 4 <= kLutBytes, "merge slots must fit the table area");
+  static constexpr int QV_FLOATS = NQK * 64 * 4;          // q.K B operands of one kv head: NQK x 64 lanes x half8
+  static constexpr int DS = D + 4;                        // wave-state row stride (floats)
+  static constexpr int QX_FLOATS = 8 * QV_FLOATS + 8 * 8 * QS;   // operands + rotated q of up to 8 kv heads
+  static constexpr int SX_FLOATS = kWaves * 8 * DS;              // wave states
+  static constexpr int X_FLOATS = QX_FLOATS > SX_FLOATS ? QX_FLOATS : SX_FLOATS;
 };
 
 // Per-block raw loads of one wave.
@@ -143,7 +186,7 @@ struct Tile {
   uint32_t k[4];      // packed K bits of this lane (up to 16 B)
   uint32_t k_lo[2];   // mixed: low-group bits (aligned 8 B window)
   uint2 kn[2];        // K norms of the lane's 4 tokens, per group
-  uint32_t v[4];      // packed V bits of the lane's 4 tokens
+  uint32_t v[4];      // packed V bits of the lane's 4 tokens (raw words of its run)
   uint2 vn;           // V norms
 };
 
@@ -154,43 +197,56 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kBufFlags);
 }
 
-// One wave's loads of a block: buffer loads against a per-block descriptor
-// (scalar base; lane offsets fixed for the whole kernel, constant parts in
-// the scalar offset), so that no vector address registers are live between
-// issue and use.  V rows narrower than 4 B per lane are still loaded as a
-// dword (the bytes past the lane's share stay inside the tile: the norm
-// area follows the last row) so the loaded value needs no zero extension.
+// One wave's loads of a block: buffer loads against the wave's pool
+// descriptors (scalar base and range) with the lane's fixed offset as the
+// vector offset and the block's byte offset plus compile-time constants as
+// the scalar offset, so no vector address registers are live between issue
+// and use (constants added to the vector offset would be hoisted out of the
+// block loop into registers of their own).  V rows narrower than 4 B per
+// lane are still loaded as a dword (the bytes past the lane's share stay
+// inside the tile: the norm area follows the last row) so the loaded value
+// needs no zero extension.
 template <int D, int KK, int VK>
 __device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                          uint32_t k_off, uint32_t klo_off, uint32_t n_off, uint32_t v_off,
-                                          int k_norm_off, int v_norm_off) {
+                                          uint32_t kb, uint32_t vb, uint32_t k_off, uint32_t klo_off,
+                                          uint32_t n_off, uint32_t v_off) {
   using C = Cfg<D, KK, VK>;
+  constexpr uint32_t KN = 16 * C::KROW, VN = 16 * C::VROW;   // norm areas follow the 16 rows
   if constexpr (KK == K4 && D == 128) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off, 0, 0);
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off, kb, 0);
     t.k[0] = x[0]; t.k[1] = x[1]; t.k[2] = x[2]; t.k[3] = x[3];
   } else if constexpr ((KK == K4 && D == 64) || (KK != K4 && D == 128)) {
-    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off, 0, 0);
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off, kb, 0);
     t.k[0] = x[0]; t.k[1] = x[1];
   } else {
-    t.k[0] = __builtin_amdgcn_raw_buffer_load_b32(kr, k_off, 0, 0);
+    t.k[0] = __builtin_amdgcn_raw_buffer_load_b32(kr, k_off, kb, 0);
   }
   if constexpr (C::MIXED) {
-    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, klo_off, 0, 0);
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, klo_off, kb, 0);
     t.k_lo[0] = w[0];
     t.k_lo[1] = w[1];
   }
   {
-    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, n_off, k_norm_off, 0);
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, n_off, kb + KN, 0);
     t.kn[0] = uint2{w[0], w[1]};
   }
   if constexpr (C::MIXED) {
-    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, n_off, k_norm_off + 32, 0);
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, n_off, kb + KN + 32u, 0);
     t.kn[1] = uint2{w[0], w[1]};
   }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) t.v[r] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off, 4 * r * C::VROW, 0);
+  // lane-major V plane: the lane's run holds its bytes of tokens a, a+4, a+8,
+  // a+12 back to back (raw words; compute() picks each token's bytes)
+  if constexpr (C::VLANE == 4) {
+    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, vb, 0);
+    t.v[0] = x[0]; t.v[1] = x[1]; t.v[2] = x[2]; t.v[3] = x[3];
+  } else if constexpr (C::VLANE == 2) {
+    const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vr, v_off, vb, 0);
+    t.v[0] = x[0]; t.v[1] = x[1];
+  } else {
+    t.v[0] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off, vb, 0);
+  }
   {
-    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(vr, n_off, v_norm_off, 0);
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(vr, n_off, vb + VN, 0);
     t.vn = uint2{w[0], w[1]};
   }
 }
@@ -208,8 +264,9 @@ __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c
 // that everything derived from it (addresses above all) stays scalar.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Wave-wide: total work W = H_kv * sum of block counts (all lanes get it).
-__device__ int total_work(const int32_t* context_lens, int S, int Hkv, int max_blocks, int lane) {
+// Wave-wide: total work W = NG * sum of block counts (all lanes get it); a
+// work unit is one block of one (sequence, kv-head group) segment.
+__device__ int total_work(const int32_t* context_lens, int S, int NG, int max_blocks, int lane) {
   int tot = 0;
   const int cap = max_blocks * 16;
   for (int base = 0; base < S; base += 64) {
@@ -219,19 +276,19 @@ __device__ int total_work(const int32_t* context_lens, int S, int Hkv, int max_b
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     tot += uni(v);
   }
-  return tot * Hkv;
+  return tot * NG;
 }
 
 // Wave-wide: the segment that contains work position pos (pos < W).
-__device__ void locate(const DecodeParams& p, int lane, int pos, int& s, int& kvh, int& blk, int& nb_s) {
+__device__ void locate(const DecodeParams& p, int lane, int pos, int& s, int& grp, int& blk, int& nb_s) {
   const int cap = p.max_blocks * 16;
   int before = 0;
   s = -1;
-  kvh = blk = nb_s = 0;
+  grp = blk = nb_s = 0;
   for (int base = 0; base < p.S && s < 0; base += 64) {
     const int sq = base + lane;
     int cnt = 0;
-    if (sq < p.S) cnt = ((clamp_ctx(p.context_lens[sq], cap) + 15) >> 4) * p.Hkv;
+    if (sq < p.S) cnt = ((clamp_ctx(p.context_lens[sq], cap) + 15) >> 4) * p.NG;
     int incl = cnt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -244,8 +301,8 @@ __device__ void locate(const DecodeParams& p, int lane, int pos, int& s, int& kv
       const int src = __builtin_ctzll(hit);
       s = base + src;
       const int r = pos - before - uni(__shfl(excl, src));
-      nb_s = uni(__shfl(cnt, src)) / p.Hkv;
-      kvh = r / nb_s;
+      nb_s = uni(__shfl(cnt, src)) / p.NG;
+      grp = r / nb_s;
       blk = r % nb_s;
     }
     before += uni(__shfl(incl, 63));
@@ -255,8 +312,8 @@ __device__ void locate(const DecodeParams& p, int lane, int pos, int& s, int& kv
 // Wave-wide: the first segment start at or after work position x (W if none).
 __device__ int snap_to_segment(const DecodeParams& p, int lane, int x, int W) {
   if (x >= W) return W;
-  int s, kvh, blk, nb;
-  locate(p, lane, x, s, kvh, blk, nb);
+  int s, grp, blk, nb;
+  locate(p, lane, x, s, grp, blk, nb);
   return blk == 0 ? x : x - blk + nb;
 }
 
@@ -272,16 +329,35 @@ __device__ __forceinline__ int range_len(int W, int n_wg, int max_blocks, int P)
   return R > need ? R : need;
 }
 
+// Workgroup LDS.  The tables come first so that every table address
+// (< 64 KB) fits the immediate offset of the LDS read.
 template <int D, int KK, int VK>
-__global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
+struct Smem {
+  using C = Cfg<D, KK, VK>;
+  uint8_t lut[C::LDS_LUT];
+  // per kv head of the group: q.K operands (NQK x 64 lanes x half8) and the
+  // rotated q rows; after the block loop the same bytes hold the wave states
+  float xbuf[C::X_FLOATS];
+  float s_ml[kWaves * 16];   // per wave: running max and sum of each q head
+  uint32_t s_par[64];
+  int s_qexp[64];            // [kv head of the group][q head]
+  int s_next[8];             // per kv head of the group: next free piece block
+  int s_bt[kBtCap];          // block-table entries of the piece's first kBtCap blocks
+};
+
+template <int D, int KK, int VK>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   using C = Cfg<D, KK, VK>;
   constexpr int R4 = 4 * C::R;   // output dims per lane
   constexpr int NQK = C::NQK;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS_LUT];
-  __shared__ __attribute__((aligned(16))) float qbuf[C::Q_FLOATS];  // q.K operands, rotated q
-  __shared__ float s_ml[kWaves * 16];   // per wave: running max and sum of each q head
-  __shared__ __attribute__((aligned(16))) uint32_t s_par[64];
-  __shared__ int s_qexp[8];
+  __shared__ __attribute__((aligned(16))) Smem<D, KK, VK> sm;
+  uint8_t* const lds = sm.lut;
+  float* const xbuf = sm.xbuf;
+  float* const s_ml = sm.s_ml;
+  uint32_t* const s_par = sm.s_par;
+  int* const s_qexp = sm.s_qexp;
+  int* const s_next = sm.s_next;
+  int* const s_bt = sm.s_bt;
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);
@@ -315,7 +391,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
   }
 
   // ---- work range of this workgroup (every wave computes the same numbers)
-  const int W = total_work(p.context_lens, p.S, p.Hkv, p.max_blocks, lane);
+  const int W = total_work(p.context_lens, p.S, p.NG, p.max_blocks, lane);
   const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
   int r0 = blockIdx.x * R;
   int r1 = (r0 + R < W) ? r0 + R : W;
@@ -346,54 +422,48 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
 
   auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
-  // LDS tables: byte-indexed, two halves of 128 B per entry.  The merge of
-  // the wave states reuses the start of this area, so the tables are built
-  // again for every piece (the 3-bit table lies past the merge slots).
-  auto build_tables = [&](bool with3) {
-    // thread -> 16 B chunk (16 e + lane & 15) of entry e = 16 e_hi + e_lo:
-    // lane & 15 walks the 256 B of an entry (8 chunks per half), so each
-    // store instruction writes 1 KB contiguous; e_lo is fixed per lane and
-    // e_hi = (wave >> 2) | 2 it, so the codebook word of e_hi is word it
-    // of the lane's half, its fp16 selected by wave >> 2.
-    // (the lane id goes through an empty asm so that none of this is hoisted
-    // out of the piece loop and kept live across it)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int h = (ln >> 3) & 1;
-    const int e_lo = (ln >> 4) | ((wave & 3) << 2);
-    const uint32_t wsh = (uint32_t)(wave >> 2) * 16u;
+  // LDS tables: byte-indexed, two halves of 128 B per entry, built once.
+  // Thread -> 16 B chunk (16 e + lane & 15) of entry e = 16 e_hi + e_lo:
+  // lane & 15 walks the 256 B of an entry (8 chunks per half), so each
+  // store instruction writes 1 KB contiguous; e_lo is fixed per lane,
+  // e_hi = (wave >> 2) + 4 it.
+  {
+    const int h = (lane >> 3) & 1;
+    const int e_lo = (lane >> 4) | ((wave & 3) << 2);
+    const int wh = wave >> 2;
+    const uint32_t sh = (uint32_t)(wh & 1) * 16u;
     const int kind0 = uni(p.half_kind[0]), kind1 = uni(p.half_kind[1]);   // scalar reads
     const int kind = h ? kind1 : kind0;
-    const uint4 w03 = *reinterpret_cast<const uint4*>(s_par + 8 * h);
-    const uint4 w47 = *reinterpret_cast<const uint4*>(s_par + 8 * h + 4);
-    const uint32_t cbw[8] = {w03.x, w03.y, w03.z, w03.w, w47.x, w47.y, w47.z, w47.w};
+    __syncthreads();   // s_par written by wave 0
+    const uint4 r03 = *reinterpret_cast<const uint4*>(s_par + 8 * h);
+    const uint4 r47 = *reinterpret_cast<const uint4*>(s_par + 8 * h + 4);
+    const uint32_t cw[8] = {r03.x, r03.y, r03.z, r03.w, r47.x, r47.y, r47.z, r47.w};
     const uint32_t lo_n = cb_half(h, e_lo);
     const uint32_t ev = cb_half(h, e_lo & 3) | (cb_half(h, e_lo >> 2) << 16);
-    uint4* dst = reinterpret_cast<uint4*>(lds) + (ln & 15) + 16 * e_lo + 256 * (wave >> 2);
+    const uint32_t c2 = (((wh >> 1) ? cw[1] : cw[0]) >> sh) & 0xFFFFu;   // cb[e_hi & 3] = cb[wh]
+    uint4* dst = reinterpret_cast<uint4*>(lds) + (lane & 15) + 16 * e_lo + 256 * wh;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < 4; ++it) {
       // nibble table: (cb[e & 15], cb[e >> 4]);
       // crumb table: (cb[e & 3], cb[(e >> 2) & 3]), (cb[(e >> 4) & 3], cb[e >> 6])
-      const uint32_t v4 = lo_n | (((cbw[it] >> wsh) & 0xFFFFu) << 16);
-      const uint32_t c2 = (cbw[it & 1] >> wsh) & 0xFFFFu;
-      const uint32_t c3 = (cbw[it >> 2] >> (16 * ((it >> 1) & 1))) & 0xFFFFu;
+      const uint32_t hiw = (wh >> 1) ? cw[2 * it + 1] : cw[2 * it];
+      const uint32_t v4 = lo_n | (((hiw >> sh) & 0xFFFFu) << 16);
+      const uint32_t c3 = (cw[it >> 1] >> (16 * (it & 1))) & 0xFFFFu;
       const uint32_t od = c2 | (c3 << 16);
       const uint32_t x0 = kind == 4 ? v4 : (kind == 2 ? ev : 0u);
       const uint32_t x1 = kind == 4 ? v4 : (kind == 2 ? od : 0u);
-      dst[512 * it] = uint4{x0, x1, x0, x1};
+      dst[1024 * it] = uint4{x0, x1, x0, x1};
     }
     if constexpr (C::MIXED) {
-      if (with3) {
-        for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
-          const int e = c >> 2;
-          const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
-          const uint32_t hi = (s_par[16 + ((e >> 3) >> 1)] >> (16 * ((e >> 3) & 1))) & 0xFFFFu;
-          const uint32_t v = lo | (hi << 16);
-          reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
-        }
+      for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
+        const int e = c >> 2;
+        const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t hi = (s_par[16 + ((e >> 3) >> 1)] >> (16 * ((e >> 3) & 1))) & 0xFFFFu;
+        const uint32_t v = lo | (hi << 16);
+        reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
       }
     }
-  };
+  }
 
   // ---- per-lane roles
   const int j = lane & 15;          // MFMA column: q head j & 7, high (j < 8) or low part
@@ -411,16 +481,22 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
   const uint32_t k_off = (uint32_t)(tokK * C::KROW + KLANE * a);
   const uint32_t klo_off = (uint32_t)((tokK * C::KROW + D / 4 + (3 * D / 64) * a) & ~3);
   const uint32_t n_off = (uint32_t)(8 * a);   // this lane's 4 norms, after the tile's norm offset
-  const uint32_t v_off = (uint32_t)(a * C::VROW + C::VLANE * j);
+  const uint32_t v_off = (uint32_t)(lane * 4 * C::VLANE);   // this lane's run of the V plane
   const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
   const int64_t v_blk_stride = (int64_t)p.Hkv * p.v_tile;
   const int cap = p.max_blocks * 16;
-  float* const qf_all = qbuf + C::QV_FLOATS;   // rotated q, row g at g * QS, 4 pad floats per 16 channels
-  float* const slots = reinterpret_cast<float*>(lds);   // merge: wave w, head g row at (8 w + g) * DS
+  // wave -> (kv head of the group, part): the NPW waves of a head share its blocks
+  const int HG = p.HG;
+  const int NPW = kWaves / HG;
+  const int hl = uni(wave % HG);
+  const int part = uni(wave / HG);
+  half8_t* const qv_all = reinterpret_cast<half8_t*>(xbuf);            // [hl][t][lane]
+  float* const qf_all = xbuf + 8 * C::QV_FLOATS;                       // [hl][g] rows of QS floats
+  float* const slots = xbuf;                                           // [wave][g] rows of DS floats
 
   // ---- walk the pieces of this workgroup's range
-  int s, kvh, blk, nb_s;
-  locate(p, lane, r0, s, kvh, blk, nb_s);
+  int s, grp, blk, nb_s;
+  locate(p, lane, r0, s, grp, blk, nb_s);
   int pos = r0;
   bool first = true;
   while (pos < r1) {
@@ -431,27 +507,47 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
     const bool whole = p.P == 1 || (seg_start / R) == ((seg_start + nb_s - 1) / R);
     const int piece = (int)blockIdx.x - seg_start / R;
     const int ctx = clamp_ctx(scalar_ld(p.context_lens, s), cap);
+    const int kvh = grp * HG + hl;   // this wave's kv head
     const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
     const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
     const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
 
-    // -------- issue the long-latency loads first: this wave's first 64
-    // block-table entries, and (wave 0) the G raw q rows
-    const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;  // blocks of this wave
-    int cnt = nbw < 64 ? nbw : 64;
-    int bt_reg = 0;
-    if (lane < cnt) bt_reg = bt_row[b0 + wave + kWaves * lane];
-    constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per head
+    if (!first) __syncthreads();   // the previous piece's states have been read
+    first = false;
+
+    // -------- blocks of the piece are handed out per kv head: part q of a
+    // head starts with piece blocks q, q + NPW and q + 2 NPW, then takes the
+    // next free index from the head's LDS counter, so parts that run ahead
+    // take more blocks and all finish together.  The HG heads of the group
+    // read the HG adjacent tiles of each physical block at about the same
+    // time.  The piece's block-table entries are staged in LDS (the first
+    // kBtCap of them; later ones are read from memory), so a block costs
+    // index (LDS atomic) -> entry (LDS read) -> tile loads; while a tile is
+    // computed the next two tiles are in flight.
+    const int n = b1 - b0;   // blocks of the piece, >= 1
+    if (tid < 8) s_next[tid] = 3 * NPW;
+    const __amdgpu_buffer_rsrc_t btr = tile_rsrc(reinterpret_cast<const uint8_t*>(bt_row), 4 * p.max_blocks);
+    auto bt_load = [&](int idx) -> int {   // entry of piece block idx (block b0 when idx >= n)
+      return (int)__builtin_amdgcn_raw_buffer_load_b32(btr, 0u, 4 * (b0 + (idx < n ? idx : 0)), 0);
+    };
+    constexpr int NBT = kBtCap / kThreads;
+    int btv[NBT];
+#pragma unroll
+    for (int i = 0; i < NBT; ++i) {
+      const int e = tid + kThreads * i;
+      btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
+    }
+    constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per q head
     const int g8 = lane >> 3, l8 = lane & 7;
     const bool q_live = g8 < p.G;
     // raw q words of this lane's PER channels (bf16: two per word, the upper
     // half of qw unused); one load shape for both dtypes, bytes past the q
     // tensor read as zero through the descriptor's range check
     uint32_t qw[PER];
-    {   // issued by every wave (only wave 0 uses them) so that all paths
+    {   // issued by every wave (parts > 0 discard them) so that all paths
         // carry the same loads and later waits count exactly
       const int esz = p.q_f32 ? 4 : 2;
-      const int head0 = uni((int)(((int64_t)s * p.Hq + kvh * p.G) * D * esz));   // first q row of the group
+      const int head0 = uni((int)(((int64_t)s * p.Hq + kvh * p.G) * D * esz));   // first q row of the head
       const uint32_t lane_off = (uint32_t)(((q_live ? g8 : 0) * D + l8 * PER) * esz);
       const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
 #pragma unroll
@@ -460,140 +556,159 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
         qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
       }
     }
+    int idx_c = part, idx_1 = part + NPW, idx_2 = part + 2 * NPW;
+    const int v0 = bt_load(idx_c);
+    const int v1 = bt_load(idx_1);
 
-    __syncthreads();  // first piece: s_par ready; later pieces: merge slots free
-    build_tables(first);
-    first = false;
-
-    // -------- bad block-table entries of a chunk: reported, then skipped
-    auto check_chunk = [&](int chunk0) -> uint64_t {
-      const bool bad = lane < cnt && (bt_reg < 0 || (int64_t)bt_reg >= p.num_blocks);
-      const uint64_t m = __builtin_amdgcn_ballot_w64(bad);
-      if (m) {
-        if (lane == (int)__builtin_ctzll(m))
-          record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + wave + kWaves * (chunk0 + lane));
-        if (bad) bt_reg = 0;
-      }
-      return m;
+    // -------- block-table entry -> scalar byte offsets of the block's tiles
+    // in the pools (whose bytes, less than 4 GiB each, one descriptor per
+    // wave covers); entries outside the pool are reported and their block
+    // skipped (read as block 0)
+    const __amdgpu_buffer_rsrc_t kt = tile_rsrc(k_head, (int)(p.k_span - (uint32_t)kvh * (uint32_t)p.k_tile));
+    const __amdgpu_buffer_rsrc_t vt = tile_rsrc(v_head, (int)(p.v_span - (uint32_t)kvh * (uint32_t)p.v_tile));
+    uint32_t kb, vb;
+    auto entry = [&](int v, int idx, bool& ok) {
+      const uint32_t raw = (uint32_t)__builtin_amdgcn_readfirstlane(v);
+      const bool live = idx < n;
+      const bool bad = live && raw >= (uint32_t)p.num_blocks;
+      if (bad && lane == 0) record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + idx);
+      const uint32_t ph = (uint32_t)uni(bad ? 0 : (int)raw);
+      ok = live && !bad;
+      kb = ph * (uint32_t)k_blk_stride;
+      vb = ph * (uint32_t)v_blk_stride;
     };
-    auto ptrs = [&](int it, __amdgpu_buffer_rsrc_t& kt, __amdgpu_buffer_rsrc_t& vt) {
-      const int64_t ph = __builtin_amdgcn_readlane(bt_reg, it);
-      kt = tile_rsrc(k_head + ph * k_blk_stride, p.k_tile);
-      vt = tile_rsrc(v_head + ph * v_blk_stride, p.v_tile);
+    auto bt_at = [&](int idx) -> int {   // entry value of piece block idx (any lane)
+      if (idx >= n) return 0;
+      if (idx < kBtCap) return s_bt[idx];
+      const int v = bt_load(idx);        // long piece: read from memory (latency exposed)
+      return __builtin_amdgcn_readfirstlane(v);
     };
-    uint64_t badm = check_chunk(0);
-    Tile<D, KK, VK> A, B;
-    __amdgpu_buffer_rsrc_t kt, vt;
-    // first tile in flight during the q rotation (issued even when this wave
-    // has no block: then it reads block 0 of the pool, unused)
-    ptrs(0, kt, vt);
-    load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
+    auto grab = [&]() -> int {   // next free piece block of this head (valid in lane 0)
+      int g = 0;
+      if (lane == 0) g = atomicAdd(&s_next[hl], 1);
+      return g;
+    };
+    Tile<D, KK, VK> A, B, C3;
+    bool ok_c, ok_1;
+    entry(v0, idx_c, ok_c);
+    load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+    entry(v1, idx_1, ok_1);
+    load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+#pragma unroll
+    for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
 
-    // -------- rotate the G q heads of (s, kvh) once: row g of the rotated q
-    // is H (s_K * q_g), unnormalised
-    if (wave == 0) {
-      float x[PER];
-      if (p.q_f32) {
+    // -------- part 0 of each head: rotate the head's G q rows once (row g of
+    // the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
+    // operands: the scaled rotated q split into an fp16 high part (columns
+    // 0-7) and the fp16 rounding of the remainder (columns 8-15).
+    if (part == 0) {
+      float* qf = qf_all + hl * (8 * C::QS);
+      {
+        float x[PER];
+        if (p.q_f32) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
-      } else {
+          for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
+        } else {
 #pragma unroll
-        for (int k = 0; k < PER / 2; ++k) {
-          x[2 * k] = __uint_as_float(qw[k] << 16);
-          x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
-        }
-      }
-      const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        if ((sw >> e) & 1u) x[e] = -x[e];
-        if (!q_live) x[e] = 0.f;
-      }
-#pragma unroll
-      for (int h = 1; h < PER; h <<= 1) {
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-          if ((e & h) == 0) {
-            const float a0 = x[e], b0v = x[e + h];
-            x[e] = a0 + b0v;
-            x[e + h] = a0 - b0v;
+          for (int k = 0; k < PER / 2; ++k) {
+            x[2 * k] = __uint_as_float(qw[k] << 16);
+            x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
           }
-      }
-#pragma unroll
-      for (int k = 1; k < 8; k <<= 1) {
-        const bool up = (l8 & k) != 0;
+        }
+        const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-          const float o = __shfl_xor(x[e], k);
-          x[e] = up ? (o - x[e]) : (x[e] + o);
+          if ((sw >> e) & 1u) x[e] = -x[e];
+          if (!q_live) x[e] = 0.f;
         }
-      }
-      float amax = 0.f;
-      float* qrow = qf_all + g8 * C::QS;
 #pragma unroll
-      for (int i = 0; i < PER / 4; ++i) {
-        const int c = l8 * PER + 4 * i;
-        *reinterpret_cast<float4*>(qrow + c + 4 * (c >> 4)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
-      }
+        for (int h = 1; h < PER; h <<= 1) {
 #pragma unroll
-      for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
+          for (int e = 0; e < PER; ++e)
+            if ((e & h) == 0) {
+              const float a0 = x[e], b0v = x[e + h];
+              x[e] = a0 + b0v;
+              x[e + h] = a0 - b0v;
+            }
+        }
 #pragma unroll
-      for (int k = 1; k < 8; k <<= 1) amax = fmaxf(amax, __shfl_xor(amax, k));
-      if (l8 == 0) {
+        for (int k = 1; k < 8; k <<= 1) {
+          const bool up = (l8 & k) != 0;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            const float o = __shfl_xor(x[e], k);
+            x[e] = up ? (o - x[e]) : (x[e] + o);
+          }
+        }
+        float amax = 0.f;
+        float* qrow = qf + g8 * C::QS;
+#pragma unroll
+        for (int i = 0; i < PER / 4; ++i) {
+          const int c = l8 * PER + 4 * i;
+          *reinterpret_cast<float4*>(qrow + c + 4 * (c >> 4)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+        for (int k = 1; k < 8; k <<= 1) amax = fmaxf(amax, __shfl_xor(amax, k));
         int ex = 0;
         if (amax > 0.f) frexpf(amax, &ex);
-        s_qexp[g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
+        if (l8 == 0) s_qexp[8 * hl + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
       }
-    }
-    __syncthreads();  // rotated q and tables ready
-
-    // q.K B operands (column j, channel chunk a), one MFMA per wave: the
-    // scaled rotated q split into an fp16 high part (columns 0-7) and the
-    // fp16 rounding of the remainder (columns 8-15); kept in LDS, re-read
-    // per block by every wave.
-    if (wave < NQK) {
-      const int t = wave;
-      const float q_pow = ldexpf(1.0f, s_qexp[gq]);
-      const float* qrow = qf_all + gq * C::QS;
-      float vq[8];
-      if constexpr (C::MIXED) {
-        constexpr int m = D / 2;
-        constexpr int per_g = NQK / 2;
-        const int grp = t / per_g, u = t % per_g;
+      // (same wave: its LDS writes above are visible to its reads below)
+      const float q_pow = ldexpf(1.0f, s_qexp[8 * hl + gq]);
+      const float* qrow = qf + gq * C::QS;
+#pragma unroll
+      for (int t = 0; t < NQK; ++t) {
+        float vq[8];
+        if constexpr (C::MIXED) {
+          constexpr int m = D / 2;
+          constexpr int per_g = NQK / 2;
+          const int grp_k = t / per_g, u = t % per_g;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int pos_l = grp_k * m + a * (m / 4) + 8 * u + e;
+            const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
+            vq[e] = qrow[chn + 4 * (chn >> 4)];
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = a * (D / 4) + 8 * t + 4 * h;
+            const float4 f = *reinterpret_cast<const float4*>(qrow + c + 4 * (c >> 4));
+            vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
+          }
+        }
+        half8_t qv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int pos_l = grp * m + a * (m / 4) + 8 * u + e;
-          const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
-          vq[e] = qrow[chn + 4 * (chn >> 4)];
+          const float v = vq[e] * q_pow;
+          const _Float16 hi = (_Float16)v;
+          const _Float16 lo = (_Float16)(v - (float)hi);
+          qv[e] = lo_part ? lo : hi;
         }
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int c = a * (D / 4) + 8 * t + 4 * h;
-          const float4 f = *reinterpret_cast<const float4*>(qrow + c + 4 * (c >> 4));
-          vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
-        }
+        qv_all[(hl * NQK + t) * 64 + lane] = qv;
       }
-      half8_t qv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = vq[e] * q_pow;
-        const _Float16 hi = (_Float16)v;
-        const _Float16 lo = (_Float16)(v - (float)hi);
-        qv[e] = lo_part ? lo : hi;
-      }
-      reinterpret_cast<half8_t*>(qbuf)[t * 64 + lane] = qv;
     }
-    __syncthreads();  // operands ready
-    const float w_col = ldexpf(p.score_mul, -s_qexp[gq]);
-    const half8_t* qb = reinterpret_cast<const half8_t*>(qbuf) + lane;   // qb[64 * t]: operand of MFMA t
+    __syncthreads();  // operands, counters and block-table entries ready
+    int ph2v = bt_at(idx_2);
+    int g3 = grab();
+    const float w_col = ldexpf(p.score_mul, -s_qexp[8 * hl + gq]);
+    const half8_t* qb = qv_all + hl * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
 
     // -------- stream this wave's blocks of the piece
     float m_run = -INFINITY, l_run = 0.f;
+    float nm = 0.f;   // -m_run * w_col (0 while m_run is -inf)
     float4_t o_acc[C::R];
 #pragma unroll
     for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+    // token r's V bytes of this lane, from byte 0 (r compile-time)
+    auto vword = [&](const Tile<D, KK, VK>& t, int r) -> uint32_t {
+      if constexpr (C::VLANE == 4) return t.v[r];
+      else if constexpr (C::VLANE == 2) return (r & 1) ? (t.v[r >> 1] >> 16) : t.v[r >> 1];
+      else return t.v[0] >> (8 * r);
+    };
     auto compute = [&](const Tile<D, KK, VK>& cur, int b, bool ok) {
       float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
       float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -647,10 +762,12 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float full0 = acc0[e] + row_ror8(acc0[e]);
-        float v = full0 * half_at(cur.kn[0], e);
+        const uint32_t kw = (e >> 1) ? cur.kn[0].y : cur.kn[0].x;
+        float v = (e & 1) ? mul_h<1>(full0, kw) : mul_h<0>(full0, kw);
         if constexpr (C::MIXED) {
           const float full1 = acc1[e] + row_ror8(acc1[e]);
-          v += full1 * half_at(cur.kn[1], e);
+          const uint32_t kw1 = (e >> 1) ? cur.kn[1].y : cur.kn[1].x;
+          v = (e & 1) ? fma_h<1>(full1, kw1, v) : fma_h<0>(full1, kw1, v);
         }
         sc[e] = v;
       }
@@ -658,10 +775,8 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx) ? sc[e] : -INFINITY;
       }
-      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m_run, bm);
+      const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
+      const float m_new = max_nn(m_run, bm);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
         asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
         const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f((m_run - m_new) * w_col) : 1.f;
@@ -669,15 +784,13 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
         m_run = m_new;
+        nm = (m_run == -INFINITY) ? 0.f : -m_run * w_col;
       }
-      const float nm = (m_run == -INFINITY) ? 0.f : -m_run * w_col;
-      half4_t pb;
+      float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
-        l_run += pr;
-        pb[e] = (_Float16)(pr * half_at(cur.vn, e));
-      }
+      for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_h2(pr[0], pr[1], cur.vn.x), mul_h2(pr[2], pr[3], cur.vn.y)});
 
       __builtin_amdgcn_sched_barrier(0);
       // P.V on the matrix cores: A = V (dims x tokens) per MFMA u
@@ -685,11 +798,12 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
         // Lookup keys pair the nibbles of two tokens for one dim, so the
         // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
         // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
-        const uint32_t x1s = cur.v[1] << 4, x3s = cur.v[3] << 4;
-        const uint32_t E01 = (cur.v[0] & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
-        const uint32_t O01 = ((cur.v[0] >> 4) & 0x0F0F0F0Fu) | (cur.v[1] & 0xF0F0F0F0u);
-        const uint32_t E23 = (cur.v[2] & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
-        const uint32_t O23 = ((cur.v[2] >> 4) & 0x0F0F0F0Fu) | (cur.v[3] & 0xF0F0F0F0u);
+        const uint32_t w0 = vword(cur, 0), w1 = vword(cur, 1), w2 = vword(cur, 2), w3 = vword(cur, 3);
+        const uint32_t x1s = w1 << 4, x3s = w3 << 4;
+        const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
+        const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+        const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
+        const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
         constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
 #pragma unroll
         for (int k = 0; k < NB; ++k) {
@@ -707,7 +821,11 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
         for (int k = 0; k < NBY; ++k) {
           uint2 lk[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) lk[r] = lds_u64(lds, lut_addr(cur.v[r], off_v2, k));
+          for (int r = 0; r < 4; ++r) {
+            // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
+            if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
+            else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
+          }
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
@@ -723,32 +841,32 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
       }
     };
 
-    for (int chunk0 = 0; cnt > 0;) {
-      int it = 0;
-      for (;;) {
-        ptrs(it + 1 < cnt ? it + 1 : it, kt, vt);
-        load_tile<D, KK, VK>(B, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
-        compute(A, b0 + wave + kWaves * (chunk0 + it), !((badm >> it) & 1ull));
-        if (++it >= cnt) break;
-        ptrs(it + 1 < cnt ? it + 1 : it, kt, vt);
-        load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
-        compute(B, b0 + wave + kWaves * (chunk0 + it), !((badm >> it) & 1ull));
-        if (++it >= cnt) break;
-      }
-      chunk0 += 64;
-      if (chunk0 >= nbw) break;
-      cnt = (nbw - chunk0) < 64 ? (nbw - chunk0) : 64;
-      bt_reg = 0;
-      if (lane < cnt) bt_reg = bt_row[b0 + wave + kWaves * (chunk0 + lane)];
-      badm = check_chunk(chunk0);
-      ptrs(0, kt, vt);
-      load_tile<D, KK, VK>(A, kt, vt, k_off, klo_off, n_off, v_off, p.k_norm_off, p.v_norm_off);
+    // one block (j): issue tile j+2, look up the entry of j+3 and take the
+    // index of j+4, compute tile j
+    auto step = [&](const Tile<D, KK, VK>& cur, Tile<D, KK, VK>& dst) -> bool {
+      if (idx_c >= n) return false;
+      bool ok2;
+      entry(ph2v, idx_2, ok2);
+      load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+      const int idx_3 = __builtin_amdgcn_readfirstlane(g3);
+      const int ph3v = bt_at(idx_3);
+      g3 = grab();
+      compute(cur, b0 + idx_c, ok_c);
+      idx_c = idx_1; ok_c = ok_1;
+      idx_1 = idx_2; ok_1 = ok2;
+      idx_2 = idx_3; ph2v = ph3v;
+      return true;
+    };
+    for (;;) {
+      if (!step(A, C3)) break;
+      if (!step(B, A)) break;
+      if (!step(C3, B)) break;
     }
 
-    // -------- merge the 8 wave states through LDS, rotated domain.  Wave w
-    // stores its unnormalised O rows (head g at slot row 8 w + g) and its
-    // running max / sum; wave g then combines head g over the waves.
-    __syncthreads();  // every wave is done with the tables and the q operands
+    // -------- wave states to LDS (rotated domain): wave w stores its
+    // unnormalised O rows (q head g at slot row 8 w + g) and its running
+    // max / sum per q head
+    __syncthreads();  // every wave is done with the q operands (the slots overlay them)
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     if (!lo_part) {
@@ -766,26 +884,25 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
     }
     __syncthreads();
 
-    // -------- wave g: combine, normalise, inverse rotation, write head g.
-    // Lane l holds dims l + 64 i; the rotation's top stage (D = 128) is in
-    // the lane, the others pair lanes.
-    if (wave < p.G) {
-      const int g = wave;
-      const float wc = ldexpf(p.score_mul, -s_qexp[g]);
+    // -------- combine the parts of each (kv head, q head) pair, normalise,
+    // inverse rotation, write.  Pairs are spread over the waves; lane l
+    // holds dims l + 64 i (the rotation's top stage, D = 128, is in the lane).
+    for (int pr = wave; pr < HG * p.G; pr += kWaves) {
+      const int h2 = pr / p.G, g = pr % p.G;
+      const float wc = ldexpf(p.score_mul, -s_qexp[8 * h2 + g]);
       float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[16 * w + g]);
+      for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * (h2 + HG * q) + g]);
       constexpr int NY = D / 64;
       float y[NY];
 #pragma unroll
       for (int i = 0; i < NY; ++i) y[i] = 0.f;
       float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_ml[16 * w + g];
+      for (int q = 0; q < NPW; ++q) {
+        const int wq = h2 + HG * q;
+        const float mw = s_ml[16 * wq + g];
         const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * wc);
-        L = __builtin_fmaf(f, s_ml[16 * w + 8 + g], L);
-        const float* srow = slots + (8 * w + g) * C::DS;
+        L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
+        const float* srow = slots + (8 * wq + g) * C::DS;
 #pragma unroll
         for (int i = 0; i < NY; ++i) y[i] = __builtin_fmaf(f, srow[lane + 64 * i], y[i]);
       }
@@ -807,7 +924,7 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
       const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
       const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
       const float lse = empty ? -INFINITY : (M * wc + log2f(L)) * kLn2;
-      const int hq = kvh * p.G + g;
+      const int hq = (grp * HG + h2) * p.G + g;
 #pragma unroll
       for (int i = 0; i < NY; ++i) {
         const int d = lane + 64 * i;
@@ -834,8 +951,8 @@ __global__ __launch_bounds__(kThreads, 4) void decode_kernel(DecodeParams p) {
     pos += b1 - b0;
     if (pos >= r1) break;
     blk = 0;
-    if (++kvh == p.Hkv) {
-      kvh = 0;
+    if (++grp == p.NG) {
+      grp = 0;
       do {
         ++s;
         nb_s = (clamp_ctx(scalar_ld(p.context_lens, s), cap) + 15) >> 4;
@@ -854,7 +971,7 @@ struct MergeParams {
   void* out;
   float* lse;
   const int32_t* context_lens;  // NULL: generic mode
-  int32_t S, H, P, D, Hkv, G, max_blocks, n_wg, out_f32;
+  int32_t S, H, P, D, NG, HG, G, max_blocks, n_wg, out_f32;
 };
 
 __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
@@ -864,7 +981,7 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
   int n = p.P;
   if (p.context_lens) {
     // recompute the decode kernel's workgroup ranges for this segment
-    const int W = total_work(p.context_lens, p.S, p.Hkv, p.max_blocks, lane);
+    const int W = total_work(p.context_lens, p.S, p.NG, p.max_blocks, lane);
     const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
     const int cap = p.max_blocks * 16;
     int before = 0;
@@ -877,8 +994,8 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
     }
     const int nb = (clamp_ctx(p.context_lens[s], cap) + 15) >> 4;
     if (nb == 0) return;  // written by the decode kernel
-    const int kvh = (sh % p.H) / p.G;
-    const int seg_start = before * p.Hkv + kvh * nb;
+    const int grp = (sh % p.H) / p.G / p.HG;
+    const int seg_start = before * p.NG + grp * nb;
     n = (seg_start + nb - 1) / R - seg_start / R + 1;
     if (n <= 1) return;   // written directly by the decode kernel
   }
@@ -981,7 +1098,7 @@ extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse
   if (out_dtype != TQ_BF16 && out_dtype != TQ_F32) return set_error(TQ_ERR_VALUE, "out_dtype must be BF16 or F32");
   if (num_seqs == 0) return TQ_OK;
   if (!part_out || !part_lse || !out) return set_error(TQ_ERR_VALUE, "NULL merge buffer");
-  MergeParams mp = {part_out, part_lse, out, lse, nullptr, num_seqs, num_heads, num_splits, head_dim, 1, 1, 1, 1,
+  MergeParams mp = {part_out, part_lse, out, lse, nullptr, num_seqs, num_heads, num_splits, head_dim, 1, 1, 1, 1, 1,
                     out_dtype == TQ_F32};
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
                      reinterpret_cast<hipStream_t>(stream), mp);
@@ -1025,6 +1142,10 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   if (work_bound >= (1ll << 30) || max_blocks_per_seq > (1 << 20))
     return set_error(TQ_ERR_VALUE, "too much work for one call (2^30 block-heads, 2^20 blocks per sequence)");
   const int64_t q_bytes = (int64_t)num_seqs * num_q_heads * D * (q_dtype == TQ_F32 ? 4 : 2);
+  const int64_t k_pool = num_blocks * num_kv_heads * (int64_t)tile_bytes_of(kfmt);
+  const int64_t v_pool = num_blocks * num_kv_heads * (int64_t)tile_bytes_of(vfmt);
+  if (num_blocks >= (1ll << 31) || k_pool > 0xFFFFFFFFll || v_pool > 0xFFFFFFFFll)
+    return set_error(TQ_ERR_VALUE, "each page pool must be smaller than 4 GiB");
   if (q_bytes >= (1ll << 31)) return set_error(TQ_ERR_VALUE, "q must be smaller than 2 GiB");
 
   DecodeParams p = {};
@@ -1043,10 +1164,24 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   p.G = G;
   p.max_blocks = max_blocks_per_seq;
   p.P = num_splits;
-  const int64_t wg = 2ll * device_cus();
-  p.n_wg = (int)(work_bound < wg ? (work_bound > 0 ? work_bound : 1) : wg);
+  // One 16-wave workgroup per CU.  A workgroup takes the HG kv heads of a
+  // group together (its waves read the HG adjacent tiles of each physical
+  // block); HG is the largest of 8, 4, 2, 1 dividing Hkv that still leaves
+  // at least one piece per CU when every context is full length.
+  const int cus = device_cus();
+  int HG = 1;
+  for (int hg : {8, 4, 2}) {
+    if (num_kv_heads % hg) continue;
+    if ((int64_t)num_seqs * (num_kv_heads / hg) * num_splits >= cus) { HG = hg; break; }
+  }
+  p.HG = HG;
+  p.NG = num_kv_heads / HG;
+  const int64_t units = (int64_t)num_seqs * p.NG * max_blocks_per_seq;
+  p.n_wg = (int)(units < cus ? (units > 0 ? units : 1) : cus);
   p.k_tile = tile_bytes_of(kfmt);
   p.v_tile = tile_bytes_of(vfmt);
+  p.k_span = (uint32_t)k_pool;
+  p.v_span = (uint32_t)v_pool;
   p.k_norm_off = TQ_BLOCK_SIZE * row_index_bytes(kfmt);
   p.v_norm_off = TQ_BLOCK_SIZE * row_index_bytes(vfmt);
   const double mK = (double)D / kfmt->num_groups, mV = (double)D / vfmt->num_groups;
@@ -1092,7 +1227,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   st = launch_status("tq_decode_paged launch");
   if (st != TQ_OK || num_splits == 1) return st;
   MergeParams mp = {p.part_o, p.part_lse, out, lse, context_lens, num_seqs, num_q_heads, num_splits, D,
-                    num_kv_heads, G, max_blocks_per_seq, p.n_wg, p.out_f32};
+                    p.NG, p.HG, G, max_blocks_per_seq, p.n_wg, p.out_f32};
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_q_heads)), dim3(64), 0, hs, mp);
   return launch_status("tq_decode_paged merge launch");
 }

@@ -28,6 +28,7 @@ struct DevFormat {
   int32_t row_bytes;       // index bytes per row
   int32_t tile_bytes;
   int32_t norm_off;        // byte offset of the norm plane in a tile
+  int32_t chunk;           // V pages: bytes per lane run of the index plane (0: row-major)
 };
 
 void make_dev_format(const tq_format* f, DevFormat* out);

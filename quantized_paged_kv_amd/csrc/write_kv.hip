@@ -200,8 +200,24 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
   const int64_t blk = slot >> 4;
   const int offs = (int)(slot & 15);
   uint8_t* tile = p.pages[tensor] + ((int64_t)blk * p.H + head) * f.tile_bytes;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(tile + offs * f.row_bytes);
-  for (int w = L; w < f.row_bytes / 4; w += LPR) dst[w] = lds_row[lr][w];
+  if (f.chunk == 0) {   // row-major index plane
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + offs * f.row_bytes);
+    for (int w = L; w < f.row_bytes / 4; w += LPR) dst[w] = lds_row[lr][w];
+  } else {              // lane-major: chunk j of the row goes to run 16*(offs%4)+j, place offs/4
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(lds_row[lr]);
+    const int c = f.chunk;
+    for (int jj = L; jj < 16; jj += LPR) {
+      uint8_t* cd = tile + ((16 * (offs & 3) + jj) * 4 + (offs >> 2)) * c;
+      const uint8_t* cs = src + jj * c;
+      if ((c & 3) == 0) {
+        for (int w = 0; w < c / 4; ++w) reinterpret_cast<uint32_t*>(cd)[w] = reinterpret_cast<const uint32_t*>(cs)[w];
+      } else if (c == 2) {
+        *reinterpret_cast<uint16_t*>(cd) = *reinterpret_cast<const uint16_t*>(cs);
+      } else {
+        for (int b = 0; b < c; ++b) cd[b] = cs[b];
+      }
+    }
+  }
   if (L == 0) {
     const int nslot = 4 * (offs & 3) + (offs >> 2);
     uint16_t* np = reinterpret_cast<uint16_t*>(tile + f.norm_off);
@@ -243,6 +259,8 @@ extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype
     p.src[n_tensors] = src[t];
     p.pages[n_tensors] = pages[t];
     make_dev_format(fmts[t], &p.fmt[n_tensors]);
+    // V pages: lane-major index plane when the row bytes split into 16 runs
+    if (t == 1 && p.fmt[n_tensors].row_bytes % 16 == 0) p.fmt[n_tensors].chunk = p.fmt[n_tensors].row_bytes / 16;
     ++n_tensors;
   }
   if (num_tokens == 0) return TQ_OK;

@@ -31,22 +31,23 @@ def to_device(x: np.ndarray, dtype: str, device="cuda"):
     return t.to(device)
 
 
-def oracle_pages(x: np.ndarray, slots: np.ndarray, num_blocks: int, fmt: oenc.Format, fill=0xA5):
+def oracle_pages(x: np.ndarray, slots: np.ndarray, num_blocks: int, fmt: oenc.Format, role: str, fill=0xA5):
     """Pool written by the oracle (sentinel-filled first)."""
     T, H, d = x.shape
     _, _, tile = opg.tile_layout(fmt, 16)
     pages = np.full((num_blocks, H, tile), fill, dtype=np.uint8)
-    opg.write_pages(x, slots, pages, fmt, 16)
+    opg.write_pages(x, slots, pages, fmt, 16, role)
     return pages
 
 
-def written_mask(slots: np.ndarray, num_blocks: int, H: int, fmt: oenc.Format) -> np.ndarray:
+def written_mask(slots: np.ndarray, num_blocks: int, H: int, fmt: oenc.Format, role: str) -> np.ndarray:
     """Boolean mask of the bytes a write of `slots` owns (rows + norm slots)."""
     rb, noff, tile = opg.tile_layout(fmt, 16)
+    chunk = opg.lane_chunk(fmt, role)
     mask = np.zeros((num_blocks, H, tile), dtype=bool)
     for s in slots:
         b, o = divmod(int(s), 16)
-        mask[b, :, o * rb:(o + 1) * rb] = True
+        mask[b, :, opg.row_positions(rb, [o], chunk)[0]] = True
         sl = 4 * (o % 4) + o // 4
         for g in range(fmt.num_groups):
             pos = noff + 2 * (16 * g + sl)

@@ -72,9 +72,9 @@ def oracle_decode(w, q, pairs):
             Vp = np.zeros((len(bt), 1, opg.tile_layout(vof, 16)[2]), np.uint8)
             for a in range(0, n, 16384):
                 opg.write_pages(xk[a:a + 16384, kvh:kvh + 1], sl[a:a + 16384], Kp, kof, 16)
-                opg.write_pages(xv[a:a + 16384, kvh:kvh + 1], sl[a:a + 16384], Vp, vof, 16)
+                opg.write_pages(xv[a:a + 16384, kvh:kvh + 1], sl[a:a + 16384], Vp, vof, 16, "v")
             K = opg.reconstruct_sequence(Kp, bt, n, 0, kof, 16)
-            V = opg.reconstruct_sequence(Vp, bt, n, 0, vof, 16)
+            V = opg.reconstruct_sequence(Vp, bt, n, 0, vof, 16, role="v")
             for h in heads:
                 if h // G == kvh:
                     out[(s, h)] = oatt.attention(q[s, h].astype(np.float64), K, V, w.scale)
@@ -152,7 +152,7 @@ def test_pages_written_on_gpu_match_oracle_for_decode_cache():
     for pool, of, which in ((kp, kof, "k"), (vp, vof, "v")):
         ref = np.full(tuple(pool.shape), 0xA5, np.uint8)
         for s, sl in enumerate(slots_of(w.block_tables, w.context_lens)):
-            opg.write_pages(wl.kv_values(w, which, s), sl, ref, of, 16)
+            opg.write_pages(wl.kv_values(w, which, s), sl, ref, of, 16, which)
         assert np.array_equal(pool.cpu().numpy(), ref)
 
 
@@ -182,9 +182,9 @@ def test_identical_keys_uniform_attention():
     Kp = np.zeros((nb, 1, opg.tile_layout(of, 16)[2]), np.uint8)
     Vp = Kp.copy()
     opg.write_pages(xk, slots, Kp, of, 16)
-    opg.write_pages(xv, slots, Vp, of, 16)
+    opg.write_pages(xv, slots, Vp, of, 16, "v")
     K = opg.reconstruct_sequence(Kp, np.arange(nb), n, 0, of, 16)
-    V = opg.reconstruct_sequence(Vp, np.arange(nb), n, 0, of, 16)
+    V = opg.reconstruct_sequence(Vp, np.arange(nb), n, 0, of, 16, role="v")
     for h in range(4):
         sc = 0.1 * float(q[0, h].astype(np.float64) @ K[0])
         assert abs(float(l[0, h]) - (sc + math.log(n))) < LSE_TOL

@@ -31,12 +31,12 @@ def _gpu_write(x_k, x_v, slots, num_blocks, kspec, vspec, dtype, fill=0xA5, chun
     return kp.cpu().numpy(), vp.cpu().numpy()
 
 
-def _oracle_pool(x, slots, num_blocks, spec, chunk=8192):
+def _oracle_pool(x, slots, num_blocks, spec, role, chunk=8192):
     f = oracle_format(spec)
     _, _, tile = opg.tile_layout(f, 16)
     pages = np.full((num_blocks, x.shape[1], tile), 0xA5, dtype=np.uint8)
     for a in range(0, len(slots), chunk):
-        opg.write_pages(x[a:a + chunk], slots[a:a + chunk], pages, f, 16)
+        opg.write_pages(x[a:a + chunk], slots[a:a + chunk], pages, f, 16, role)
     return pages
 
 
@@ -53,8 +53,8 @@ def test_tiny_fp32_d64():
     slots = w.block_tables[0, np.arange(256) // 16].astype(np.int64) * 16 + np.arange(256) % 16
     print("case tiny d64 fp32", flush=True)
     kp, vp = _gpu_write(xk, xv, slots, w.num_blocks, w.kfmt, w.vfmt, "f32")
-    _assert_pool_equal(kp, _oracle_pool(xk, slots, w.num_blocks, w.kfmt), "K")
-    _assert_pool_equal(vp, _oracle_pool(xv, slots, w.num_blocks, w.vfmt), "V")
+    _assert_pool_equal(kp, _oracle_pool(xk, slots, w.num_blocks, w.kfmt, "k"), "K")
+    _assert_pool_equal(vp, _oracle_pool(xv, slots, w.num_blocks, w.vfmt, "v"), "V")
 
 
 @pytest.mark.parametrize("kbits,vbits,d,dist,dtype", [
@@ -80,8 +80,8 @@ def test_formats_random_slots(kbits, vbits, d, dist, dtype):
         vspec = wl.FormatSpec(d, list(vbits), np.concatenate([hi, lo]), w.vfmt.signs)
     print(f"case formats K{kbits} V{vbits} d{d} {dist} {dtype}", flush=True)
     kp, vp = _gpu_write(xk, xv, w.slot_mapping, w.num_blocks, kspec, vspec, dtype)
-    _assert_pool_equal(kp, _oracle_pool(xk, w.slot_mapping, w.num_blocks, kspec), "K")
-    _assert_pool_equal(vp, _oracle_pool(xv, w.slot_mapping, w.num_blocks, vspec), "V")
+    _assert_pool_equal(kp, _oracle_pool(xk, w.slot_mapping, w.num_blocks, kspec, "k"), "K")
+    _assert_pool_equal(vp, _oracle_pool(xv, w.slot_mapping, w.num_blocks, vspec, "v"), "V")
 
 
 def test_exact_threshold_ties_and_zero_rows():
@@ -134,7 +134,7 @@ def test_out_of_range_slot_reports_index_error_and_skips_row():
     with pytest.raises(IndexError, match="position 7"):
         tq.write_kv(to_device(xk, "bf16"), None, torch.from_numpy(slots).cuda(), kp, None, kf, kf, check=True)
     good = np.delete(np.arange(40), 7)
-    ref = _oracle_pool(xk[good], slots[good], w.num_blocks, w.kfmt)
+    ref = _oracle_pool(xk[good], slots[good], w.num_blocks, w.kfmt, "k")
     _assert_pool_equal(kp.cpu().numpy(), ref, "K with one bad slot")
     slots[7] = -1
     kp2 = torch.full_like(kp, 0xA5)
@@ -149,5 +149,5 @@ def test_write_workload_full_size():
     xk, xv = wl.write_values(w, "k"), wl.write_values(w, "v")
     print("case write full size", flush=True)
     kp, vp = _gpu_write(xk, xv, w.slot_mapping, w.num_blocks, w.kfmt, w.vfmt, "bf16")
-    _assert_pool_equal(kp, _oracle_pool(xk, w.slot_mapping, w.num_blocks, w.kfmt), "K")
-    _assert_pool_equal(vp, _oracle_pool(xv, w.slot_mapping, w.num_blocks, w.vfmt), "V")
+    _assert_pool_equal(kp, _oracle_pool(xk, w.slot_mapping, w.num_blocks, w.kfmt, "k"), "K")
+    _assert_pool_equal(vp, _oracle_pool(xv, w.slot_mapping, w.num_blocks, w.vfmt, "v"), "V")

@@ -119,3 +119,57 @@ def test_write_errors():
         pg.write_pages(np.zeros((2, 1, 64)), np.array([0, 1]), pages, k, bs)
     with pytest.raises(IndexError):
         pg.reconstruct_sequence(pages, np.array([0, 5]), 20, 0, k, bs)
+
+
+def test_v_lane_major_closed_form():
+    """V pages with row bytes a multiple of 16 are lane-major: with
+    c = row_bytes / 16, byte b of row t is at ((16*(t%4) + b//c)*4 + t//4)*c + b%c.
+    Hand-computed spots for the 2-bit d=128 format (c = 2)."""
+    _, v, _, _ = fmts()
+    assert pg.lane_chunk(v, "v") == 2 and pg.lane_chunk(v, "k") == 0
+    rb = 32
+    pos = pg.row_positions(rb, [0, 5, 15], 2)
+    assert pos[0, 0] == 0 and pos[0, 1] == 1 and pos[0, 2] == 8     # row 0: run 0, then run 1
+    assert pos[1, 7] == 155                                         # run 19 at 152, row 1 of it, byte 1
+    assert pos[2, 31] == ((16 * 3 + 15) * 4 + 3) * 2 + 1            # last byte of the plane
+    assert pos[2, 31] == 16 * rb - 1
+
+
+@pytest.mark.parametrize("rb", [16, 32, 48, 64])
+def test_v_lane_major_is_a_permutation_with_runs(rb):
+    """Every byte of the index plane is used once, and run 16q+j holds bytes
+    [c*j, c*(j+1)) of rows q, q+4, q+8, q+12 in order."""
+    c = rb // 16
+    pos = pg.row_positions(rb, np.arange(16), c)
+    assert sorted(pos.ravel().tolist()) == list(range(16 * rb))
+    for q in range(4):
+        for j in range(16):
+            run = pos[[q, q + 4, q + 8, q + 12]][:, c * j:c * (j + 1)].ravel()
+            assert run.tolist() == list(range((16 * q + j) * 4 * c, (16 * q + j + 1) * 4 * c))
+
+
+def test_v_pages_roundtrip_and_other_formats_stay_row_major():
+    """Rows written with role v read back with role v; a V format whose row
+    bytes are not a multiple of 16 keeps the row-major plane."""
+    _, v, km, _ = fmts()
+    bs, H, nb = 16, 2, 3
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((20, H, 128))
+    slots = rng.permutation(nb * bs)[:20]
+    for f in (v, km):
+        _, _, tile = pg.tile_layout(f, bs)
+        pages = np.full((nb, H, tile), 0xA5, dtype=np.uint8)
+        pg.write_pages(x, slots, pages, f, bs, "v")
+        idx, norms = enc.encode_rows(x, f)
+        for h in range(H):
+            ridx, rn = pg.read_rows(pages, slots // bs, slots % bs, h, f, bs, "v")
+            for g in range(f.num_groups):
+                np.testing.assert_array_equal(ridx[g], idx[g][:, h])
+            np.testing.assert_array_equal(rn, norms[:, h])
+    assert pg.lane_chunk(km, "v") == 0   # 56-byte rows
+    # the row-major reader sees a lane-major plane as different bytes
+    _, _, tile = pg.tile_layout(v, bs)
+    pages = np.zeros((nb, H, tile), dtype=np.uint8)
+    pg.write_pages(x, slots, pages, v, bs, "v")
+    k_view, _ = pg.read_rows(pages, slots // bs, slots % bs, 0, v, bs, "k")
+    assert not np.array_equal(k_view[0], enc.encode_rows(x, v)[0][0][:, 0])
