@@ -118,7 +118,7 @@ class Bench:
         self.out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=od, device="cuda")
         self.lse = torch.empty((w.num_seqs, w.num_q_heads), dtype=torch.float32, device="cuda")
         nbytes = tq.workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, self.P)
-        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")   # split counters start at zero
         self.decode_bytes, self.write_bytes = algorithmic_bytes(w, kf, vf)
         torch.cuda.synchronize()
 
@@ -231,7 +231,18 @@ def main():
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device to device 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "launches": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode shards by kv head or "
               f"sequence with no exchange, see DESIGN.md", file=sys.stderr)
