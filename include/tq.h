@@ -119,12 +119,18 @@ typedef struct tq_format {
  * Page layout ([D "Serving Route Design"]: slot -> physical block -> token
  * offset -> packed row bytes, with block = slot / 16 and offset = slot % 16):
  *   pages  : [num_blocks][num_kv_heads][tile_bytes] uint8, device memory.
- *   tile   : index plane, 16 rows of row_index_bytes (row `offset` at byte
- *            offset * row_index_bytes; each group's indices packed LSB-first,
- *            group 0 first), then the norm plane: fp16 little-endian,
- *            group-major, the norm of group g of the row at in-block offset t
- *            stored at  16*row_index_bytes + 2*(16*g + 4*(t % 4) + t / 4).
+ *   tile   : index plane of 16 packed rows (each group's indices packed
+ *            LSB-first, group 0 first, row_index_bytes per row), then the
+ *            norm plane: fp16 little-endian, group-major, the norm of group g
+ *            of the row at in-block offset t stored at
+ *            16*row_index_bytes + 2*(16*g + 4*(t % 4) + t / 4).
  *            The tile is padded to a multiple of 16 bytes.
+ *   index plane, K pages: row t at bytes [t*rb, (t+1)*rb), rb = row_index_bytes.
+ *   index plane, V pages: when rb is a multiple of 16 (c = rb / 16), byte b
+ *            of row t is at ((16*(t % 4) + b / c)*4 + t / 4)*c + b % c: 64 runs
+ *            of 4c bytes, run 16q + j holding bytes [c*j, c*(j+1)) of rows q,
+ *            q+4, q+8, q+12 (one decode lane's share, one wide load); other V
+ *            formats use the K layout.
  */
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -177,7 +183,7 @@ tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype, int64_t n
  * Workspace of tq_decode_paged: num_seqs * num_q_heads * num_splits *
  * (head_dim + 1) * 4 bytes when num_splits > 1, else 0.  It depends on the
  * runtime shape only, never on context length ([D "Serving Route Design"]:
- * "keep workspace bounded by runtime shape").
+ * the workspace is bounded by the runtime shape).
  */
 tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                     int32_t num_splits, uint64_t* bytes /* host out */);
@@ -196,12 +202,16 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *   context_lens device int32 [num_seqs]: cached tokens per sequence (the
  *                current token included: write it first).
  *   scale        softmax scale applied to q.k.
- *   num_splits   P >= 1.  The logical blocks of every sequence are cut into
- *                chunks of C = ceil(max_blocks_per_seq / P) blocks; each chunk
- *                yields a partial (o_p, lse_p) and the partials are merged by
- *                log-sum-exp inside this call.  workspace must hold
- *                tq_decode_workspace_bytes() bytes (device, may be NULL when
- *                P == 1).
+ *   num_splits   P >= 1: the most pieces one (sequence, kv head) may be cut
+ *                into.  The work (sequence, kv-head group, logical block) is
+ *                split evenly over one persistent workgroup per CU; a range of
+ *                at least ceil(max_blocks_per_seq / (P - 1)) blocks each keeps
+ *                every segment within P pieces (P == 1: ranges end at segment
+ *                boundaries, nothing is split).  A cut segment leaves one
+ *                partial (o_p, lse_p) per piece in the workspace and the
+ *                partials are merged by log-sum-exp inside this call.
+ *                workspace must hold tq_decode_workspace_bytes() bytes
+ *                (device, may be NULL when P == 1).
  *   out          device [num_seqs][num_q_heads][head_dim], out_dtype BF16/F32.
  *   lse          device float [num_seqs][num_q_heads] or NULL: natural-log
  *                sum of exp(scale * q.k) over the context.
@@ -213,7 +223,10 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * A sequence with context length 0 gets out = 0 and lse = -inf.
  * Served formats (else UNSUPPORTED_FORMAT): head_dim 64 or 128; K one group
  * of 4 or 2 bits, or two groups of 4 + 3 bits; V one group of 4 or 2 bits;
- * num_q_heads / num_kv_heads in 1..8; block_size 16.
+ * num_q_heads / num_kv_heads in 1..8; block_size 16.  Each page pool must be
+ * smaller than 4 GiB and num_blocks below 2^31 (else VALUE).
+ * Results are reproducible up to the order of floating-point accumulation:
+ * blocks are shared dynamically among the waves serving a kv head.
  */
 tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
                           int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,

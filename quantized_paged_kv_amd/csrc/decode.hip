@@ -7,20 +7,25 @@
 // [D "System Invariants"]: production routes consume packed history (no dense
 // K/V tensor is ever formed); unsupported formats raise.
 //
-// Work decomposition (balanced split-K).  The work is the list of
-// (sequence, kv head, logical block) triples, ordered sequence-major, then
-// kv head, then block; a "segment" is the run of one (sequence, kv head).
-// The grid is two persistent workgroups per CU and workgroup w owns the
-// contiguous range [w*R, (w+1)*R) of that list, so every workgroup gets the
-// same number of blocks whatever the context lengths.  A workgroup walks the
-// pieces of the segments its range covers; a segment that lies inside one
-// range is finished there and written out directly, a segment cut by range
-// boundaries leaves one partial (o, lse) per piece in the workspace and the
-// merge kernel combines them.  R is at least ceil(max_blocks / (P - 1)), so
-// no segment has more than P pieces (P = num_splits, the workspace bound).
+// Work decomposition (balanced split-K).  Kv heads are taken in groups of
+// HG adjacent heads (HG in 8, 4, 2, 1, chosen on the host).  The work is the
+// list of (sequence, head group, logical block) units, sequence-major; a
+// "segment" is the run of one (sequence, head group).  The grid is one
+// persistent 16-wave workgroup per CU and workgroup w owns the contiguous
+// range [w*R, (w+1)*R) of that list, so every workgroup gets the same number
+// of blocks whatever the context lengths.  A workgroup walks the pieces of
+// the segments its range covers; a segment that lies inside one range is
+// finished there and written out directly, a segment cut by range
+// boundaries leaves one partial (o, lse) per piece and q head in the
+// workspace and the merge kernel combines them.  R is at least
+// ceil(max_blocks / (P - 1)), so no segment has more than P pieces
+// (P = num_splits, the workspace bound).
 //
-// Inside a piece the 8 waves take the blocks round-robin, each with its own
-// online-softmax state; the states are merged through LDS at the end.
+// Inside a piece, wave w serves kv head w % HG; the 16 / HG waves of a head
+// take its blocks from an LDS counter (balanced however the SIMDs schedule
+// them), each with its own online-softmax state, so the HG heads' tiles of
+// a physical block (adjacent in the pool) are read at about the same time.
+// The states are combined through LDS at the end of the piece.
 //
 // Inner loop (per wave, per 16-token block), all in the rotated domain:
 //   q.K:  v_mfma_f32_16x16x32_f16, A = dequantised K rows (16 tokens x 32
@@ -33,13 +38,13 @@
 //         that hold that head's 16 scores; rescale only when the max grows.
 //   P.V:  v_mfma_f32_16x16x16_f16, A = dequantised V (dims x tokens), B =
 //         p * (V norm) in fp16, accumulators fp32.
-// Tile loads for block i+1 are issued before block i is computed (two
-// register buffers used alternately, loads never conditional).
-// Codebook lookups use byte-indexed LDS tables replicated across banks
-// (one v_perm builds the address from a packed byte and the lane's copy).
-// LDS per workgroup stays within 80 KB so that two workgroups fit a CU.
-// Epilogue: LDS tree merge of the 8 wave states, inverse rotation of the
-// output once per head (Walsh-Hadamard across the wave, signs, 1/sqrt(d)).
+// While block i is computed, the tiles of blocks i+1 and i+2 are in flight
+// (three register buffers, loads never conditional).
+// Codebook lookups use byte-indexed LDS tables replicated 32 times across
+// the banks (one v_perm builds the address from a packed byte and the
+// lane's copy); the tables sit at LDS offset 0 so the address needs no add.
+// Epilogue: per (kv head, q head), combine the waves' states, inverse
+// rotation once (Walsh-Hadamard across the wave, signs, 1/sqrt(d)).
 #include <mutex>
 
 #include "tq_internal.h"
