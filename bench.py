@@ -118,7 +118,7 @@ class Bench:
         self.out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=od, device="cuda")
         self.lse = torch.empty((w.num_seqs, w.num_q_heads), dtype=torch.float32, device="cuda")
         nbytes = tq.workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, self.P)
-        self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")   # split counters start at zero
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
         self.decode_bytes, self.write_bytes = algorithmic_bytes(w, kf, vf)
         torch.cuda.synchronize()
 

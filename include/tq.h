@@ -211,7 +211,10 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *                partial (o_p, lse_p) per piece in the workspace and the
  *                partials are merged by log-sum-exp inside this call.
  *                workspace must hold tq_decode_workspace_bytes() bytes
- *                (device, may be NULL when P == 1).
+ *                (device, may be NULL when P == 1); its contents on entry
+ *                do not matter (every slot the merge reads is written first:
+ *                an uncut row's slot 0 holds a marker, the slots past a cut
+ *                segment's last piece hold -inf).
  *   out          device [num_seqs][num_q_heads][head_dim], out_dtype BF16/F32.
  *   lse          device float [num_seqs][num_q_heads] or NULL: natural-log
  *                sum of exp(scale * q.k) over the context.
@@ -242,7 +245,8 @@ tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
  *   part_out  device float [num_seqs][num_heads][num_splits][head_dim]
  *             (normalised partial outputs, original domain)
  *   part_lse  device float [num_seqs][num_heads][num_splits]; -inf marks an
- *             empty partial.  All partials empty: out = 0, lse = -inf.
+ *             empty partial, whose part_out row is not read.  All partials
+ *             empty: out = 0, lse = -inf.
  *   out       device [num_seqs][num_heads][head_dim], BF16 or F32.
  *   lse       device float [num_seqs][num_heads] or NULL.
  */

@@ -276,7 +276,7 @@ def decode_paged(q, k_pages, v_pages, block_tables, context_lens, kfmt: Format, 
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     need = workspace_bytes(B, Hq, d, num_splits)
     if need and workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)   # counters start at zero
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     own_err = dev_err is None and check
     if own_err:

@@ -63,6 +63,9 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kLutBytes = 65536;    // 256 entries x 256 B (two halves)
 constexpr int kLut3Bytes = 4096;    // 64 entries x 16 copies x 4 B
 constexpr int kBtCap = 2048;        // block-table entries of a piece staged in LDS
+// Slot 0 of a row's partial lse holds this quiet NaN when the decode kernel
+// has written the row's final output itself (nothing to merge).
+constexpr uint32_t kDoneBits = 0x7FC0D0E5u;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum KKind { K4 = 0, K2 = 1, KM43 = 2 };
@@ -420,6 +423,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
         if (p.lse)
           for (int h = lane; h < p.Hq; h += 64) p.lse[(int64_t)s * p.Hq + h] = -INFINITY;
+        if (p.P > 1)   // tell the merge that these rows are final
+          for (int h = lane; h < p.Hq; h += 64) p.part_lse[((int64_t)s * p.Hq + h) * p.P] = __uint_as_float(kDoneBits);
       }
     }
   }
@@ -511,6 +516,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     // one piece: the final output is written here (always so when P == 1)
     const bool whole = p.P == 1 || (seg_start / R) == ((seg_start + nb_s - 1) / R);
     const int piece = (int)blockIdx.x - seg_start / R;
+    const int n_pieces = (seg_start + nb_s - 1) / R - seg_start / R + 1;
     const int ctx = clamp_ctx(scalar_ld(p.context_lens, s), cap);
     const int kvh = grp * HG + hl;   // this wave's kv head
     const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
@@ -944,11 +950,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           else static_cast<uint16_t*>(p.out)[off + 64 * i] = f32_to_bf16_rne(y[i]);
         }
         if (lane == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
+        if (lane == 0 && p.P > 1) p.part_lse[((int64_t)s * p.Hq + hq) * p.P] = __uint_as_float(kDoneBits);
       } else {
-        const int64_t row = ((int64_t)s * p.Hq + hq) * p.P + piece;
+        const int64_t row0 = ((int64_t)s * p.Hq + hq) * p.P;
+        const int64_t row = row0 + piece;
 #pragma unroll
         for (int i = 0; i < NY; ++i) p.part_o[row * D + lane + 64 * i] = y[i];
         if (lane == 0) p.part_lse[row] = lse;
+        if (piece == n_pieces - 1)   // the last piece closes the slots no piece uses
+          for (int i = n_pieces + lane; i < p.P; i += 64) p.part_lse[row0 + i] = -INFINITY;
       }
     }
 
@@ -967,80 +977,59 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 }
 
 // ----------------------------------------------------------------- merge
-// One wave per (sequence, q head).  Generic mode: all P partials, -inf lse
-// marks an empty partial.  Decode mode: only segments cut into several
-// pieces are merged (the others were written by the decode kernel).
+// One wave per (sequence, q head): out = sum_i exp(lse_i - M) o_i /
+// sum_i exp(lse_i - M), lse = M + log(sum_i exp(lse_i - M)), M = max lse_i,
+// over the P partial slots; a -inf lse marks an empty or unused slot.  In
+// decode mode the decode kernel has marked the rows it wrote out directly
+// (kDoneBits in slot 0) and set the slots past a segment's last piece to
+// -inf, so no segment bookkeeping is redone here.  Lane l loads the lse of
+// slot l; the o rows of the live slots of each chunk of 16 are then loaded
+// together (two memory round trips for P <= 16).
 struct MergeParams {
   const float* part_o;
   const float* part_lse;
   void* out;
   float* lse;
-  const int32_t* context_lens;  // NULL: generic mode
-  int32_t S, H, P, D, NG, HG, G, max_blocks, n_wg, out_f32;
+  int32_t S, H, P, D, out_f32, decode;
 };
 
 __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
-  const int sh = blockIdx.x;
-  const int s = sh / p.H;
+  constexpr int CH = 16;
+  const int64_t sh = blockIdx.x;
   const int lane = threadIdx.x;
-  int n = p.P;
-  if (p.context_lens) {
-    // recompute the decode kernel's workgroup ranges for this segment
-    const int W = total_work(p.context_lens, p.S, p.NG, p.max_blocks, lane);
-    const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
-    const int cap = p.max_blocks * 16;
-    int before = 0;
-    for (int base = 0; base < s; base += 64) {
-      const int sq = base + lane;
-      int v = sq < s ? ((clamp_ctx(p.context_lens[sq], cap) + 15) >> 4) : 0;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-      before += v;
-    }
-    const int nb = (clamp_ctx(p.context_lens[s], cap) + 15) >> 4;
-    if (nb == 0) return;  // written by the decode kernel
-    const int grp = (sh % p.H) / p.G / p.HG;
-    const int seg_start = before * p.NG + grp * nb;
-    n = (seg_start + nb - 1) / R - seg_start / R + 1;
-    if (n <= 1) return;   // written directly by the decode kernel
-  }
-  const float* lse_p = p.part_lse + (int64_t)sh * p.P;
-  const float* o_p = p.part_o + (int64_t)sh * p.P * p.D;
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, lse_p[i]);
+  const int P = p.P, D = p.D;
+  const float* lse_p = p.part_lse + sh * P;
+  const float* o_p = p.part_o + sh * (int64_t)P * D;
+  const float lf = lane < P ? lse_p[lane] : -INFINITY;
+  if (p.decode && (uint32_t)__builtin_amdgcn_readfirstlane(__float_as_uint(lf)) == kDoneBits) return;
+  auto slot_lse = [&](int i) -> float {   // i uniform
+    return i < 64 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lf), i)) : lse_p[i];
+  };
+  float M = lf;
+  for (int i = 64 + lane; i < P; i += 64) M = fmaxf(M, lse_p[i]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
   float acc[2] = {0.f, 0.f};
   float den = 0.f;
   if (M != -INFINITY) {
-    int i = 0;
-    for (; i + 4 <= n; i += 4) {
-      float li[4], ov[4][2];
+    for (int base = 0; base < P; base += CH) {
+      float w[CH], ov[CH][2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        li[k] = lse_p[i + k];
+      for (int k = 0; k < CH; ++k) {   // all loads of the chunk before any use
+        const float li = base + k < P ? slot_lse(base + k) : -INFINITY;
+        w[k] = li;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int dim = lane + 64 * r;
-          ov[k][r] = dim < p.D ? o_p[(int64_t)(i + k) * p.D + dim] : 0.f;
+          ov[k][r] = (li != -INFINITY && dim < D) ? o_p[(int64_t)(base + k) * D + dim] : 0.f;
         }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float w = (li[k] == -INFINITY) ? 0.f : expf(li[k] - M);
-        den += w;
+      for (int k = 0; k < CH; ++k) {
+        const float wk = (w[k] == -INFINITY) ? 0.f : expf(w[k] - M);
+        den += wk;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) acc[r] += w * ov[k][r];
-      }
-    }
-    for (; i < n; ++i) {
-      const float li = lse_p[i];
-      const float w = (li == -INFINITY) ? 0.f : expf(li - M);
-      den += w;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int dim = lane + 64 * r;
-        if (dim < p.D) acc[r] += w * o_p[(int64_t)i * p.D + dim];
+        for (int r = 0; r < 2; ++r) acc[r] = __builtin_fmaf(wk, ov[k][r], acc[r]);
       }
     }
   }
@@ -1048,9 +1037,9 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int dim = lane + 64 * r;
-    if (dim >= p.D) continue;
+    if (dim >= D) continue;
     const float o = empty ? 0.f : acc[r] / den;
-    const int64_t off = (int64_t)sh * p.D + dim;
+    const int64_t off = sh * D + dim;
     if (p.out_f32) static_cast<float*>(p.out)[off] = o;
     else static_cast<uint16_t*>(p.out)[off] = f32_to_bf16_rne(o);
   }
@@ -1103,8 +1092,7 @@ extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse
   if (out_dtype != TQ_BF16 && out_dtype != TQ_F32) return set_error(TQ_ERR_VALUE, "out_dtype must be BF16 or F32");
   if (num_seqs == 0) return TQ_OK;
   if (!part_out || !part_lse || !out) return set_error(TQ_ERR_VALUE, "NULL merge buffer");
-  MergeParams mp = {part_out, part_lse, out, lse, nullptr, num_seqs, num_heads, num_splits, head_dim, 1, 1, 1, 1, 1,
-                    out_dtype == TQ_F32};
+  MergeParams mp = {part_out, part_lse, out, lse, num_seqs, num_heads, num_splits, head_dim, out_dtype == TQ_F32, 0};
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
                      reinterpret_cast<hipStream_t>(stream), mp);
   return launch_status("tq_split_merge launch");
@@ -1231,8 +1219,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
 #undef TQ_LAUNCH
   st = launch_status("tq_decode_paged launch");
   if (st != TQ_OK || num_splits == 1) return st;
-  MergeParams mp = {p.part_o, p.part_lse, out, lse, context_lens, num_seqs, num_q_heads, num_splits, D,
-                    p.NG, p.HG, G, max_blocks_per_seq, p.n_wg, p.out_f32};
+  MergeParams mp = {p.part_o, p.part_lse, out, lse, num_seqs, num_q_heads, num_splits, D, p.out_f32, 1};
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_q_heads)), dim3(64), 0, hs, mp);
   return launch_status("tq_decode_paged merge launch");
 }

@@ -239,6 +239,42 @@ def test_split_merge_against_oracle_partials():
     assert np.all(o.cpu().numpy() == 0) and l.item() == -math.inf
 
 
+def test_split_workspace_contents_do_not_matter():
+    """The workspace is read only where the same call wrote it: a NaN-filled
+    workspace, and one left over from a call with other context lengths,
+    give the same outputs as a zeroed one."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    P = 4
+    w = wl.small_decode_workload(21, 3, 8, 2, 128, [1000, 0, 300], [4], [4], num_splits=P,
+                                 max_blocks_per_seq=70)
+    kp, vp, kf, vf = build_gpu_cache(w)
+    q = to_device(wl.q_values(w), "bf16")
+    bt = torch.from_numpy(w.block_tables.astype(np.int32)).cuda()
+    nbytes = tq.workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim, P)
+
+    def run(cl, ws):
+        o, l = tq.decode_paged(q, kp, vp, bt, torch.tensor(cl, dtype=torch.int32).cuda(), kf, vf, w.scale,
+                               num_splits=P, workspace=ws, out_dtype=torch.float32, check=True)
+        torch.cuda.synchronize()
+        return o.cpu().numpy(), l.cpu().numpy()
+
+    cl = [int(c) for c in w.context_lens]
+    o0, l0 = run(cl, torch.zeros(nbytes, dtype=torch.uint8, device="cuda"))
+    o1, l1 = run(cl, torch.full((nbytes // 4,), math.nan, dtype=torch.float32, device="cuda"))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    run([500, 0, 100], ws)   # leaves partials of other segment cuts behind
+    o2, l2 = run(cl, ws)
+    for o, l in ((o1, l1), (o2, l2)):
+        assert np.all(np.isfinite(o))
+        # same cuts, same pieces: only the accumulation order inside a piece may differ
+        assert np.max(np.abs(l - l0)[np.isfinite(l0)]) <= 1e-5 and np.array_equal(np.isinf(l), np.isinf(l0))
+        assert np.max(np.abs(o - o0)) <= 1e-5
+    q_np = wl.q_values(w)
+    pairs = [(s, h) for s in range(w.num_seqs) for h in range(w.num_q_heads)]
+    check(w, q_np, o1, l1, pairs, "f32")
+
+
 # ------------------------------------------------------------------ full size
 BENCH_SPLITS = {2: 16, 4: 16, 5: 64}
 
