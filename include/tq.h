@@ -204,8 +204,10 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *   scale        softmax scale applied to q.k.
  *   num_splits   P >= 1: the most pieces one (sequence, kv head) may be cut
  *                into.  The work (sequence, kv-head group, logical block) is
- *                split evenly over one persistent workgroup per CU; a range of
- *                at least ceil(max_blocks_per_seq / (P - 1)) blocks each keeps
+ *                split evenly over one persistent workgroup per CU, each
+ *                segment charged a fixed number of extra blocks for the cost
+ *                of starting a piece; a range of at least
+ *                ceil(max_blocks_per_seq / (P - 1)) positions each keeps
  *                every segment within P pieces (P == 1: ranges end at segment
  *                boundaries, nothing is split).  A cut segment leaves one
  *                partial (o_p, lse_p) per piece in the workspace and the

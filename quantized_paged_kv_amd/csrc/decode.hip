@@ -86,6 +86,7 @@ struct DecodeParams {
   int32_t S, Hq, Hkv, G, max_blocks, P;
   int32_t HG, NG;    // kv heads per workgroup group (1, 2, 4 or 8) and groups (Hkv / HG)
   int32_t n_wg;      // grid size (persistent workgroups)
+  int32_t seg_cost;  // work positions charged for starting a piece (see seg_span)
   int32_t k_tile, v_tile, k_norm_off, v_norm_off;
   uint32_t k_span, v_span;   // bytes of each pool (< 4 GiB)
   float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K)), > 0
@@ -159,6 +160,46 @@ __device__ __forceinline__ float max_nn(float a, float b) {
   return r;
 }
 // max over the lanes l, l^16, l^32, l^48 (gfx950 row and half swaps)
+// Value of x in lane (lane ^ K), K a power of two below 64, without the
+// LDS crossbar: DPP quad permutes for K = 1, 2, the half-row mirror (lane
+// i <-> 7 - i) followed by the quad reversal (i <-> 3 - i) for K = 4, the
+// 8-lane row rotation for K = 8, and the gfx950 row-swap permutes for K =
+// 16, 32 (after swapping a value with itself, the partner's copy is the
+// first result in the upper row of each pair and the second in the lower).
+template <int K>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+  const int xi = __float_as_int(x);
+  if constexpr (K == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  } else if constexpr (K == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  } else if constexpr (K == 4) {
+    const int m = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xF, 0xF, false);           // row_half_mirror
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false));    // quad_perm 3,2,1,0
+  } else if constexpr (K == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x128, 0xF, 0xF, false));  // row_ror 8
+  } else if constexpr (K == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(K == 32, "lane_xor: K must be a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// One radix-2 stage of an unnormalised Walsh-Hadamard transform across
+// lanes: the lane with bit K clear keeps the sum, the other the difference.
+template <int K, int N>
+__device__ __forceinline__ void wht_lanes(float (&x)[N], int lane) {
+  const bool up = (lane & K) != 0;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float o = lane_xor<K>(x[e], lane);
+    x[e] = up ? (o - x[e]) : (x[e] + o);
+  }
+}
+
 __device__ __forceinline__ float max_rows(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float y = max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -272,62 +313,105 @@ __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c
 // that everything derived from it (addresses above all) stays scalar.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Wave-wide: total work W = NG * sum of block counts (all lanes get it); a
-// work unit is one block of one (sequence, kv-head group) segment.
-__device__ int total_work(const int32_t* context_lens, int S, int NG, int max_blocks, int lane) {
-  int tot = 0;
-  const int cap = max_blocks * 16;
-  for (int base = 0; base < S; base += 64) {
-    const int sq = base + lane;
-    int v = sq < S ? (clamp_ctx(context_lens[sq], cap) + 15) >> 4 : 0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    tot += uni(v);
-  }
-  return tot * NG;
+template <int K>
+__device__ __forceinline__ int lane_xor_i(int v, int lane) {
+  return __float_as_int(lane_xor<K>(__int_as_float(v), lane));
 }
 
-// Wave-wide: the segment that contains work position pos (pos < W).
-__device__ void locate(const DecodeParams& p, int lane, int pos, int& s, int& grp, int& blk, int& nb_s) {
-  const int cap = p.max_blocks * 16;
+// Wave-wide sum (every lane gets it).
+__device__ __forceinline__ int wave_sum(int v, int lane) {
+  v += lane_xor_i<32>(v, lane);
+  v += lane_xor_i<16>(v, lane);
+  v += lane_xor_i<8>(v, lane);
+  v += lane_xor_i<4>(v, lane);
+  v += lane_xor_i<2>(v, lane);
+  v += lane_xor_i<1>(v, lane);
+  return v;
+}
+
+// Wave-wide inclusive prefix sum over lanes: shifts within each 16-lane row
+// (DPP row_shr 1, 2, 4, 8 give lane i the value of lane i - k), then the
+// row totals are carried up with the row broadcasts (lane 15 of a row to the
+// next row, lane 31 to the upper half).
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+  const int r = lane & 15;
+  int t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  if (r >= 1) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  if (r >= 2) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  if (r >= 4) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  if (r >= 8) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xF, 0xF, false);   // row_bcast 15
+  if (lane & 16) x += t;
+  t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xF, 0xF, false);   // row_bcast 31
+  if (lane & 32) x += t;
+  return x;
+}
+
+// Context lengths, clamped to [0, 16 max_blocks]: cl0 holds sequence `lane`
+// (sequences 0-63, read once per kernel); later sequences are read on use.
+__device__ __forceinline__ int seq_len(const DecodeParams& p, int cl0, int s) {
+  if (s < 64) return __builtin_amdgcn_readlane(cl0, s);
+  return clamp_ctx(scalar_ld(p.context_lens, s), p.max_blocks * 16);
+}
+__device__ __forceinline__ int lane_len(const DecodeParams& p, int cl0, int base, int lane) {
+  const int sq = base + lane;
+  if (sq >= p.S) return 0;
+  return base == 0 ? cl0 : clamp_ctx(p.context_lens[sq], p.max_blocks * 16);
+}
+
+// Work positions: a (sequence, kv-head group) segment of nb > 0 blocks spans
+// seg_cost + nb positions, a fixed charge for starting a piece (its set-up
+// and epilogue) followed by one position per block, so that a workgroup
+// range that covers a segment start gets fewer blocks.  Sequences with no
+// block have no segment.
+__device__ __forceinline__ int seg_span(const DecodeParams& p, int nb) { return nb > 0 ? nb + p.seg_cost : 0; }
+
+// Wave-wide: total work W = NG * sum of segment spans (all lanes get it).
+__device__ int total_work(const DecodeParams& p, int cl0, int lane) {
+  int tot = 0;
+  for (int base = 0; base < p.S; base += 64)
+    tot += uni(wave_sum(seg_span(p, (lane_len(p, cl0, base, lane) + 15) >> 4), lane));
+  return tot * p.NG;
+}
+
+// Wave-wide: the segment that contains work position pos (pos < W): its
+// sequence, kv-head group, block count and the offset of pos in its span.
+__device__ void locate(const DecodeParams& p, int cl0, int lane, int pos, int& s, int& grp, int& off, int& nb_s) {
   int before = 0;
   s = -1;
-  grp = blk = nb_s = 0;
+  grp = off = nb_s = 0;
   for (int base = 0; base < p.S && s < 0; base += 64) {
-    const int sq = base + lane;
-    int cnt = 0;
-    if (sq < p.S) cnt = ((clamp_ctx(p.context_lens[sq], cap) + 15) >> 4) * p.NG;
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
+    const int cnt = seg_span(p, (lane_len(p, cl0, base, lane) + 15) >> 4) * p.NG;
+    const int incl = wave_incl_scan(cnt, lane);
     const int excl = incl - cnt;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(sq < p.S && pos >= before + excl && pos < before + incl);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(base + lane < p.S && pos >= before + excl && pos < before + incl);
     if (hit) {
-      const int src = __builtin_ctzll(hit);
+      const int src = uni(__builtin_ctzll(hit));
       s = base + src;
-      const int r = pos - before - uni(__shfl(excl, src));
-      nb_s = uni(__shfl(cnt, src)) / p.NG;
-      grp = r / nb_s;
-      blk = r % nb_s;
+      const int r = pos - before - __builtin_amdgcn_readlane(excl, src);
+      const int span = __builtin_amdgcn_readlane(cnt, src) / p.NG;
+      nb_s = span - p.seg_cost;
+      grp = r / span;
+      off = r % span;
     }
-    before += uni(__shfl(incl, 63));
+    before += __builtin_amdgcn_readlane(incl, 63);
   }
 }
 
 // Wave-wide: the first segment start at or after work position x (W if none).
-__device__ int snap_to_segment(const DecodeParams& p, int lane, int x, int W) {
+__device__ int snap_to_segment(const DecodeParams& p, int cl0, int lane, int x, int W) {
   if (x >= W) return W;
-  int s, grp, blk, nb;
-  locate(p, lane, x, s, grp, blk, nb);
-  return blk == 0 ? x : x - blk + nb;
+  int s, grp, off, nb;
+  locate(p, cl0, lane, x, s, grp, off, nb);
+  return off == 0 ? x : x - off + seg_span(p, nb);
 }
 
-// Blocks per workgroup range: an even share of the work and, when segments
-// may be split (P > 1), at least ceil(max_blocks / (P - 1)) so that no
-// segment has more than P pieces.  With P == 1 the range boundaries are
+// Positions per workgroup range: an even share of the work and, when
+// segments may be split (P > 1), at least ceil(max_blocks / (P - 1)) so that
+// the blocks of no segment meet more than P ranges.  With P == 1 the range boundaries are
 // moved to segment starts (see snap_to_segment) and no segment is split.
 __device__ __forceinline__ int range_len(int W, int n_wg, int max_blocks, int P) {
   int R = (W + n_wg - 1) / n_wg;
@@ -370,6 +454,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);
   const int lane = tid & 63;
+  // context length of sequence `lane` (its load overlaps the table set-up)
+  const int cl_raw = lane < p.S ? p.context_lens[lane] : 0;
+  const int cl0 = clamp_ctx(cl_raw, p.max_blocks * 16);
 
   // ---- small per-call tables to LDS (kernel arguments read at compile-time
   // offsets only, then spread over lanes by lane selects; lane-indexed reads
@@ -397,38 +484,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     s_par[lane] = x;
   }
-
-  // ---- work range of this workgroup (every wave computes the same numbers)
-  const int W = total_work(p.context_lens, p.S, p.NG, p.max_blocks, lane);
-  const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
-  int r0 = blockIdx.x * R;
-  int r1 = (r0 + R < W) ? r0 + R : W;
-  if (p.P == 1) {   // whole segments only: there is no workspace for partials
-    r0 = snap_to_segment(p, lane, r0, W);
-    r1 = snap_to_segment(p, lane, r1, W);
-  }
-
-  // sequences with no cached token: out = 0, lse = -inf (first workgroup);
-  // context lengths outside [0, 16 * max_blocks] are reported and clamped
-  if (blockIdx.x == 0) {
-    const int cap = p.max_blocks * 16;
-    for (int s = wave; s < p.S; s += kWaves) {
-      const int c = p.context_lens[s];
-      if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
-      if (clamp_ctx(c, cap) == 0) {
-        for (int idx = lane; idx < p.Hq * D; idx += 64) {
-          const int64_t off = (int64_t)s * p.Hq * D + idx;
-          if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
-          else static_cast<uint16_t*>(p.out)[off] = 0;
-        }
-        if (p.lse)
-          for (int h = lane; h < p.Hq; h += 64) p.lse[(int64_t)s * p.Hq + h] = -INFINITY;
-        if (p.P > 1)   // tell the merge that these rows are final
-          for (int h = lane; h < p.Hq; h += 64) p.part_lse[((int64_t)s * p.Hq + h) * p.P] = __uint_as_float(kDoneBits);
-      }
-    }
-  }
-  if (r0 >= r1) return;  // uniform across the workgroup
 
   auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
@@ -475,6 +530,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
   }
 
+  // ---- work range of this workgroup (every wave computes the same numbers)
+  const int W = total_work(p, cl0, lane);
+  const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
+  int r0 = blockIdx.x * R;
+  int r1 = (r0 + R < W) ? r0 + R : W;
+  if (p.P == 1) {   // whole segments only: there is no workspace for partials
+    r0 = snap_to_segment(p, cl0, lane, r0, W);
+    r1 = snap_to_segment(p, cl0, lane, r1, W);
+  }
+
+  // sequences with no cached token: out = 0, lse = -inf (first workgroup);
+  // context lengths outside [0, 16 * max_blocks] are reported and clamped
+  if (blockIdx.x == 0) {
+    const int cap = p.max_blocks * 16;
+    for (int s = wave; s < p.S; s += kWaves) {
+      const int c = s < 64 ? __builtin_amdgcn_readlane(cl_raw, s) : p.context_lens[s];
+      if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
+      if (clamp_ctx(c, cap) == 0) {
+        for (int idx = lane; idx < p.Hq * D; idx += 64) {
+          const int64_t off = (int64_t)s * p.Hq * D + idx;
+          if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
+          else static_cast<uint16_t*>(p.out)[off] = 0;
+        }
+        if (p.lse)
+          for (int h = lane; h < p.Hq; h += 64) p.lse[(int64_t)s * p.Hq + h] = -INFINITY;
+        if (p.P > 1)   // tell the merge that these rows are final
+          for (int h = lane; h < p.Hq; h += 64) p.part_lse[((int64_t)s * p.Hq + h) * p.P] = __uint_as_float(kDoneBits);
+      }
+    }
+  }
+  if (r0 >= r1) return;  // uniform across the workgroup
+
   // ---- per-lane roles
   const int j = lane & 15;          // MFMA column: q head j & 7, high (j < 8) or low part
   const int a = lane >> 4;          // token group: tokens a, a+4, a+8, a+12 of a block
@@ -505,472 +592,467 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   float* const slots = xbuf;                                           // [wave][g] rows of DS floats
 
   // ---- walk the pieces of this workgroup's range
-  int s, grp, blk, nb_s;
-  locate(p, lane, r0, s, grp, blk, nb_s);
+  int s, grp, off, nb_s;
+  locate(p, cl0, lane, r0, s, grp, off, nb_s);
   int pos = r0;
   bool first = true;
   while (pos < r1) {
-    const int seg_start = pos - blk;
-    const int b0 = blk;
-    const int b1 = (nb_s - blk < r1 - pos) ? nb_s : blk + (r1 - pos);
+    const int vb0 = pos - off + p.seg_cost;   // position of the segment's block 0
+    const int b0 = off > p.seg_cost ? off - p.seg_cost : 0;
+    const int b1 = (r1 - vb0 < nb_s) ? r1 - vb0 : nb_s;
+    if (b1 > b0) {   // the range holds blocks of this segment
     // one piece: the final output is written here (always so when P == 1)
-    const bool whole = p.P == 1 || (seg_start / R) == ((seg_start + nb_s - 1) / R);
-    const int piece = (int)blockIdx.x - seg_start / R;
-    const int n_pieces = (seg_start + nb_s - 1) / R - seg_start / R + 1;
-    const int ctx = clamp_ctx(scalar_ld(p.context_lens, s), cap);
-    const int kvh = grp * HG + hl;   // this wave's kv head
-    const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
-    const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
-    const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
+    const bool whole = p.P == 1 || (vb0 / R) == ((vb0 + nb_s - 1) / R);
+    const int piece = (int)blockIdx.x - vb0 / R;
+    const int n_pieces = (vb0 + nb_s - 1) / R - vb0 / R + 1;
+      const int ctx = seq_len(p, cl0, s);
+      const int kvh = grp * HG + hl;   // this wave's kv head
+      const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
+      const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
+      const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
 
-    if (!first) __syncthreads();   // the previous piece's states have been read
-    first = false;
+      if (!first) __syncthreads();   // the previous piece's states have been read
+      first = false;
 
-    // -------- blocks of the piece are handed out per kv head: part q of a
-    // head starts with piece blocks q, q + NPW and q + 2 NPW, then takes the
-    // next free index from the head's LDS counter, so parts that run ahead
-    // take more blocks and all finish together.  The HG heads of the group
-    // read the HG adjacent tiles of each physical block at about the same
-    // time.  The piece's block-table entries are staged in LDS (the first
-    // kBtCap of them; later ones are read from memory), so a block costs
-    // index (LDS atomic) -> entry (LDS read) -> tile loads; while a tile is
-    // computed the next two tiles are in flight.
-    const int n = b1 - b0;   // blocks of the piece, >= 1
-    if (tid < 8) s_next[tid] = 3 * NPW;
-    const __amdgpu_buffer_rsrc_t btr = tile_rsrc(reinterpret_cast<const uint8_t*>(bt_row), 4 * p.max_blocks);
-    auto bt_load = [&](int idx) -> int {   // entry of piece block idx (block b0 when idx >= n)
-      return (int)__builtin_amdgcn_raw_buffer_load_b32(btr, 0u, 4 * (b0 + (idx < n ? idx : 0)), 0);
-    };
-    constexpr int NBT = kBtCap / kThreads;
-    int btv[NBT];
-#pragma unroll
-    for (int i = 0; i < NBT; ++i) {
-      const int e = tid + kThreads * i;
-      btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
-    }
-    constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per q head
-    const int g8 = lane >> 3, l8 = lane & 7;
-    const bool q_live = g8 < p.G;
-    // raw q words of this lane's PER channels (bf16: two per word, the upper
-    // half of qw unused); one load shape for both dtypes, bytes past the q
-    // tensor read as zero through the descriptor's range check
-    uint32_t qw[PER];
-    {   // issued by every wave (parts > 0 discard them) so that all paths
-        // carry the same loads and later waits count exactly
-      const int esz = p.q_f32 ? 4 : 2;
-      const int head0 = uni((int)(((int64_t)s * p.Hq + kvh * p.G) * D * esz));   // first q row of the head
-      const uint32_t lane_off = (uint32_t)(((q_live ? g8 : 0) * D + l8 * PER) * esz);
-      const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
-#pragma unroll
-      for (int i = 0; i < PER / 4; ++i) {
-        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
-        qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
+      // -------- blocks of the piece are handed out per kv head: part q of a
+      // head starts with piece blocks q, q + NPW and q + 2 NPW, then takes the
+      // next free index from the head's LDS counter, so parts that run ahead
+      // take more blocks and all finish together.  The HG heads of the group
+      // read the HG adjacent tiles of each physical block at about the same
+      // time.  The piece's block-table entries are staged in LDS (the first
+      // kBtCap of them; later ones are read from memory), so a block costs
+      // index (LDS atomic) -> entry (LDS read) -> tile loads; while a tile is
+      // computed the next two tiles are in flight.
+      const int n = b1 - b0;   // blocks of the piece, >= 1
+      if (tid < 8) s_next[tid] = 3 * NPW;
+      const __amdgpu_buffer_rsrc_t btr = tile_rsrc(reinterpret_cast<const uint8_t*>(bt_row), 4 * p.max_blocks);
+      auto bt_load = [&](int idx) -> int {   // entry of piece block idx (block b0 when idx >= n)
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(btr, 0u, 4 * (b0 + (idx < n ? idx : 0)), 0);
+      };
+      constexpr int NBT = kBtCap / kThreads;
+      int btv[NBT];
+  #pragma unroll
+      for (int i = 0; i < NBT; ++i) {
+        const int e = tid + kThreads * i;
+        btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
       }
-    }
-    int idx_c = part, idx_1 = part + NPW, idx_2 = part + 2 * NPW;
-    const int v0 = bt_load(idx_c);
-    const int v1 = bt_load(idx_1);
-
-    // -------- block-table entry -> scalar byte offsets of the block's tiles
-    // in the pools (whose bytes, less than 4 GiB each, one descriptor per
-    // wave covers); entries outside the pool are reported and their block
-    // skipped (read as block 0)
-    const __amdgpu_buffer_rsrc_t kt = tile_rsrc(k_head, (int)(p.k_span - (uint32_t)kvh * (uint32_t)p.k_tile));
-    const __amdgpu_buffer_rsrc_t vt = tile_rsrc(v_head, (int)(p.v_span - (uint32_t)kvh * (uint32_t)p.v_tile));
-    uint32_t kb, vb;
-    auto entry = [&](int v, int idx, bool& ok) {
-      const uint32_t raw = (uint32_t)__builtin_amdgcn_readfirstlane(v);
-      const bool live = idx < n;
-      const bool bad = live && raw >= (uint32_t)p.num_blocks;
-      if (bad && lane == 0) record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + idx);
-      const uint32_t ph = (uint32_t)uni(bad ? 0 : (int)raw);
-      ok = live && !bad;
-      kb = ph * (uint32_t)k_blk_stride;
-      vb = ph * (uint32_t)v_blk_stride;
-    };
-    auto bt_at = [&](int idx) -> int {   // entry value of piece block idx (any lane)
-      if (idx >= n) return 0;
-      if (idx < kBtCap) return s_bt[idx];
-      const int v = bt_load(idx);        // long piece: read from memory (latency exposed)
-      return __builtin_amdgcn_readfirstlane(v);
-    };
-    auto grab = [&]() -> int {   // next free piece block of this head (valid in lane 0)
-      int g = 0;
-      if (lane == 0) g = atomicAdd(&s_next[hl], 1);
-      return g;
-    };
-    Tile<D, KK, VK> A, B, C3;
-    bool ok_c, ok_1;
-    entry(v0, idx_c, ok_c);
-    load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
-    entry(v1, idx_1, ok_1);
-    load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
-#pragma unroll
-    for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
-
-    // -------- part 0 of each head: rotate the head's G q rows once (row g of
-    // the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
-    // operands: the scaled rotated q split into an fp16 high part (columns
-    // 0-7) and the fp16 rounding of the remainder (columns 8-15).
-    if (part == 0) {
-      float* qf = qf_all + hl * (8 * C::QS);
-      {
-        float x[PER];
-        if (p.q_f32) {
-#pragma unroll
-          for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < PER / 2; ++k) {
-            x[2 * k] = __uint_as_float(qw[k] << 16);
-            x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
-          }
-        }
-        const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          if ((sw >> e) & 1u) x[e] = -x[e];
-          if (!q_live) x[e] = 0.f;
-        }
-#pragma unroll
-        for (int h = 1; h < PER; h <<= 1) {
-#pragma unroll
-          for (int e = 0; e < PER; ++e)
-            if ((e & h) == 0) {
-              const float a0 = x[e], b0v = x[e + h];
-              x[e] = a0 + b0v;
-              x[e + h] = a0 - b0v;
-            }
-        }
-#pragma unroll
-        for (int k = 1; k < 8; k <<= 1) {
-          const bool up = (l8 & k) != 0;
-#pragma unroll
-          for (int e = 0; e < PER; ++e) {
-            const float o = __shfl_xor(x[e], k);
-            x[e] = up ? (o - x[e]) : (x[e] + o);
-          }
-        }
-        float amax = 0.f;
-        float* qrow = qf + g8 * C::QS;
-#pragma unroll
+      constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per q head
+      const int g8 = lane >> 3, l8 = lane & 7;
+      const bool q_live = g8 < p.G;
+      // raw q words of this lane's PER channels (bf16: two per word, the upper
+      // half of qw unused); one load shape for both dtypes, bytes past the q
+      // tensor read as zero through the descriptor's range check
+      uint32_t qw[PER];
+      {   // issued by every wave (parts > 0 discard them) so that all paths
+          // carry the same loads and later waits count exactly
+        const int esz = p.q_f32 ? 4 : 2;
+        const int head0 = uni((int)(((int64_t)s * p.Hq + kvh * p.G) * D * esz));   // first q row of the head
+        const uint32_t lane_off = (uint32_t)(((q_live ? g8 : 0) * D + l8 * PER) * esz);
+        const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
+  #pragma unroll
         for (int i = 0; i < PER / 4; ++i) {
-          const int c = l8 * PER + 4 * i;
-          *reinterpret_cast<float4*>(qrow + c + 4 * (c >> 4)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+          const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
+          qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
         }
-#pragma unroll
-        for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-        for (int k = 1; k < 8; k <<= 1) amax = fmaxf(amax, __shfl_xor(amax, k));
-        int ex = 0;
-        if (amax > 0.f) frexpf(amax, &ex);
-        if (l8 == 0) s_qexp[8 * hl + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
       }
-      // (same wave: its LDS writes above are visible to its reads below)
-      const float q_pow = ldexpf(1.0f, s_qexp[8 * hl + gq]);
-      const float* qrow = qf + gq * C::QS;
-#pragma unroll
-      for (int t = 0; t < NQK; ++t) {
-        float vq[8];
-        if constexpr (C::MIXED) {
-          constexpr int m = D / 2;
-          constexpr int per_g = NQK / 2;
-          const int grp_k = t / per_g, u = t % per_g;
-#pragma unroll
+      int idx_c = part, idx_1 = part + NPW, idx_2 = part + 2 * NPW;
+      const int v0 = bt_load(idx_c);
+      const int v1 = bt_load(idx_1);
+
+      // -------- block-table entry -> scalar byte offsets of the block's tiles
+      // in the pools (whose bytes, less than 4 GiB each, one descriptor per
+      // wave covers); entries outside the pool are reported and their block
+      // skipped (read as block 0)
+      const __amdgpu_buffer_rsrc_t kt = tile_rsrc(k_head, (int)(p.k_span - (uint32_t)kvh * (uint32_t)p.k_tile));
+      const __amdgpu_buffer_rsrc_t vt = tile_rsrc(v_head, (int)(p.v_span - (uint32_t)kvh * (uint32_t)p.v_tile));
+      uint32_t kb, vb;
+      auto entry = [&](int v, int idx, bool& ok) {
+        const uint32_t raw = (uint32_t)__builtin_amdgcn_readfirstlane(v);
+        const bool live = idx < n;
+        const bool bad = live && raw >= (uint32_t)p.num_blocks;
+        if (bad && lane == 0) record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + idx);
+        const uint32_t ph = (uint32_t)uni(bad ? 0 : (int)raw);
+        ok = live && !bad;
+        kb = ph * (uint32_t)k_blk_stride;
+        vb = ph * (uint32_t)v_blk_stride;
+      };
+      auto bt_at = [&](int idx) -> int {   // entry value of piece block idx (any lane)
+        if (idx >= n) return 0;
+        if (idx < kBtCap) return s_bt[idx];
+        const int v = bt_load(idx);        // long piece: read from memory (latency exposed)
+        return __builtin_amdgcn_readfirstlane(v);
+      };
+      auto grab = [&]() -> int {   // next free piece block of this head (valid in lane 0)
+        int g = 0;
+        if (lane == 0) g = atomicAdd(&s_next[hl], 1);
+        return g;
+      };
+      Tile<D, KK, VK> A, B, C3;
+      bool ok_c, ok_1;
+      entry(v0, idx_c, ok_c);
+      load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+      entry(v1, idx_1, ok_1);
+      load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+  #pragma unroll
+      for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
+
+      // -------- part 0 of each head: rotate the head's G q rows once (row g of
+      // the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
+      // operands: the scaled rotated q split into an fp16 high part (columns
+      // 0-7) and the fp16 rounding of the remainder (columns 8-15).
+      if (part == 0) {
+        float* qf = qf_all + hl * (8 * C::QS);
+        {
+          float x[PER];
+          if (p.q_f32) {
+  #pragma unroll
+            for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
+          } else {
+  #pragma unroll
+            for (int k = 0; k < PER / 2; ++k) {
+              x[2 * k] = __uint_as_float(qw[k] << 16);
+              x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
+            }
+          }
+          const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
+  #pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            if ((sw >> e) & 1u) x[e] = -x[e];
+            if (!q_live) x[e] = 0.f;
+          }
+  #pragma unroll
+          for (int h = 1; h < PER; h <<= 1) {
+  #pragma unroll
+            for (int e = 0; e < PER; ++e)
+              if ((e & h) == 0) {
+                const float a0 = x[e], b0v = x[e + h];
+                x[e] = a0 + b0v;
+                x[e + h] = a0 - b0v;
+              }
+          }
+          wht_lanes<1>(x, lane);   // lane bits 0-2: the 8 lanes of a q row
+          wht_lanes<2>(x, lane);
+          wht_lanes<4>(x, lane);
+          float amax = 0.f;
+          float* qrow = qf + g8 * C::QS;
+  #pragma unroll
+          for (int i = 0; i < PER / 4; ++i) {
+            const int c = l8 * PER + 4 * i;
+            *reinterpret_cast<float4*>(qrow + c + 4 * (c >> 4)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+          }
+  #pragma unroll
+          for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
+          amax = fmaxf(amax, lane_xor<1>(amax, lane));
+          amax = fmaxf(amax, lane_xor<2>(amax, lane));
+          amax = fmaxf(amax, lane_xor<4>(amax, lane));
+          int ex = 0;
+          if (amax > 0.f) frexpf(amax, &ex);
+          if (l8 == 0) s_qexp[8 * hl + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
+        }
+        // (same wave: its LDS writes above are visible to its reads below)
+        const float q_pow = ldexpf(1.0f, s_qexp[8 * hl + gq]);
+        const float* qrow = qf + gq * C::QS;
+  #pragma unroll
+        for (int t = 0; t < NQK; ++t) {
+          float vq[8];
+          if constexpr (C::MIXED) {
+            constexpr int m = D / 2;
+            constexpr int per_g = NQK / 2;
+            const int grp_k = t / per_g, u = t % per_g;
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int pos_l = grp_k * m + a * (m / 4) + 8 * u + e;
+              const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
+              vq[e] = qrow[chn + 4 * (chn >> 4)];
+            }
+          } else {
+  #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int c = a * (D / 4) + 8 * t + 4 * h;
+              const float4 f = *reinterpret_cast<const float4*>(qrow + c + 4 * (c >> 4));
+              vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
+            }
+          }
+          half8_t qv;
+  #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int pos_l = grp_k * m + a * (m / 4) + 8 * u + e;
-            const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
-            vq[e] = qrow[chn + 4 * (chn >> 4)];
+            const float v = vq[e] * q_pow;
+            const _Float16 hi = (_Float16)v;
+            const _Float16 lo = (_Float16)(v - (float)hi);
+            qv[e] = lo_part ? lo : hi;
+          }
+          qv_all[(hl * NQK + t) * 64 + lane] = qv;
+        }
+      }
+      __syncthreads();  // operands, counters and block-table entries ready
+      int ph2v = bt_at(idx_2);
+      int g3 = grab();
+      const float w_col = ldexpf(p.score_mul, -s_qexp[8 * hl + gq]);
+      const half8_t* qb = qv_all + hl * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
+
+      // -------- stream this wave's blocks of the piece
+      float m_run = -INFINITY, l_run = 0.f;
+      float nm = 0.f;   // -m_run * w_col (0 while m_run is -inf)
+      float4_t o_acc[C::R];
+  #pragma unroll
+      for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+      // token r's V bytes of this lane, from byte 0 (r compile-time)
+      auto vword = [&](const Tile<D, KK, VK>& t, int r) -> uint32_t {
+        if constexpr (C::VLANE == 4) return t.v[r];
+        else if constexpr (C::VLANE == 2) return (r & 1) ? (t.v[r >> 1] >> 16) : t.v[r >> 1];
+        else return t.v[0] >> (8 * r);
+      };
+      auto compute = [&](const Tile<D, KK, VK>& cur, int b, bool ok) {
+        float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
+        float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KK == K4) {
+  #pragma unroll
+          for (int t = 0; t < NQK; ++t) {
+            u32x4_t av;
+  #pragma unroll
+            for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[t], off4_k, by));
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
+          }
+        } else if constexpr (KK == K2) {
+  #pragma unroll
+          for (int t = 0; t < NQK; ++t) {
+            const uint2 x0 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1)));
+            const uint2 x1 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1) + 1));
+            const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
           }
         } else {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int c = a * (D / 4) + 8 * t + 4 * h;
-            const float4 f = *reinterpret_cast<const float4*>(qrow + c + 4 * (c >> 4));
-            vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
+          constexpr int per_g = NQK / 2;
+  #pragma unroll
+          for (int u = 0; u < per_g; ++u) {
+            u32x4_t av;
+  #pragma unroll
+            for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[u], off4_k, by));
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
+          }
+          constexpr int LB = 3 * D / 64;
+          const int lo_off = tokK * C::KROW + D / 4 + LB * a;
+          const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((lo_off & 3) * 8);
+  #pragma unroll
+          for (int u = 0; u < per_g; ++u) {
+            u32x4_t av;
+  #pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
+              av[pr] = lds_u32(lds, (key << 6) | off3);
+            }
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
           }
         }
-        half8_t qv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = vq[e] * q_pow;
-          const _Float16 hi = (_Float16)v;
-          const _Float16 lo = (_Float16)(v - (float)hi);
-          qv[e] = lo_part ? lo : hi;
-        }
-        qv_all[(hl * NQK + t) * 64 + lane] = qv;
-      }
-    }
-    __syncthreads();  // operands, counters and block-table entries ready
-    int ph2v = bt_at(idx_2);
-    int g3 = grab();
-    const float w_col = ldexpf(p.score_mul, -s_qexp[8 * hl + gq]);
-    const half8_t* qb = qv_all + hl * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
 
-    // -------- stream this wave's blocks of the piece
-    float m_run = -INFINITY, l_run = 0.f;
-    float nm = 0.f;   // -m_run * w_col (0 while m_run is -inf)
-    float4_t o_acc[C::R];
-#pragma unroll
-    for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    // token r's V bytes of this lane, from byte 0 (r compile-time)
-    auto vword = [&](const Tile<D, KK, VK>& t, int r) -> uint32_t {
-      if constexpr (C::VLANE == 4) return t.v[r];
-      else if constexpr (C::VLANE == 2) return (r & 1) ? (t.v[r >> 1] >> 16) : t.v[r >> 1];
-      else return t.v[0] >> (8 * r);
-    };
-    auto compute = [&](const Tile<D, KK, VK>& cur, int b, bool ok) {
-      float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
-      float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KK == K4) {
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-          u32x4_t av;
-#pragma unroll
-          for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[t], off4_k, by));
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
-        }
-      } else if constexpr (KK == K2) {
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-          const uint2 x0 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1)));
-          const uint2 x1 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1) + 1));
-          const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
-        }
-      } else {
-        constexpr int per_g = NQK / 2;
-#pragma unroll
-        for (int u = 0; u < per_g; ++u) {
-          u32x4_t av;
-#pragma unroll
-          for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[u], off4_k, by));
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
-        }
-        constexpr int LB = 3 * D / 64;
-        const int lo_off = tokK * C::KROW + D / 4 + LB * a;
-        const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((lo_off & 3) * 8);
-#pragma unroll
-        for (int u = 0; u < per_g; ++u) {
-          u32x4_t av;
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
-            av[pr] = lds_u32(lds, (key << 6) | off3);
+        // stage boundary: keeps the scheduler from hoisting the next stage's
+        // table reads above these MFMAs (bounds the live registers)
+        __builtin_amdgcn_sched_barrier(0);
+        // raw scores of this lane's 4 tokens for q head gq: sr = (q . c) * n_K;
+        // the exp2-domain score is w_col * sr (w_col > 0), folded into one fma
+        const int tok0 = 16 * b;
+        float sc[4];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float full0 = acc0[e] + row_ror8(acc0[e]);
+          const uint32_t kw = (e >> 1) ? cur.kn[0].y : cur.kn[0].x;
+          float v = (e & 1) ? mul_h<1>(full0, kw) : mul_h<0>(full0, kw);
+          if constexpr (C::MIXED) {
+            const float full1 = acc1[e] + row_ror8(acc1[e]);
+            const uint32_t kw1 = (e >> 1) ? cur.kn[1].y : cur.kn[1].x;
+            v = (e & 1) ? fma_h<1>(full1, kw1, v) : fma_h<0>(full1, kw1, v);
           }
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
+          sc[e] = v;
         }
-      }
-
-      // stage boundary: keeps the scheduler from hoisting the next stage's
-      // table reads above these MFMAs (bounds the live registers)
-      __builtin_amdgcn_sched_barrier(0);
-      // raw scores of this lane's 4 tokens for q head gq: sr = (q . c) * n_K;
-      // the exp2-domain score is w_col * sr (w_col > 0), folded into one fma
-      const int tok0 = 16 * b;
-      float sc[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float full0 = acc0[e] + row_ror8(acc0[e]);
-        const uint32_t kw = (e >> 1) ? cur.kn[0].y : cur.kn[0].x;
-        float v = (e & 1) ? mul_h<1>(full0, kw) : mul_h<0>(full0, kw);
-        if constexpr (C::MIXED) {
-          const float full1 = acc1[e] + row_ror8(acc1[e]);
-          const uint32_t kw1 = (e >> 1) ? cur.kn[1].y : cur.kn[1].x;
-          v = (e & 1) ? fma_h<1>(full1, kw1, v) : fma_h<0>(full1, kw1, v);
+        if (!(ok && tok0 + 16 <= ctx)) {   // partial or skipped block (wave-uniform branch)
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx) ? sc[e] : -INFINITY;
         }
-        sc[e] = v;
-      }
-      if (!(ok && tok0 + 16 <= ctx)) {   // partial or skipped block (wave-uniform branch)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx) ? sc[e] : -INFINITY;
-      }
-      const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
-      const float m_new = max_nn(m_run, bm);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-        asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
-        const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f((m_run - m_new) * w_col) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
-        m_run = m_new;
-        nm = (m_run == -INFINITY) ? 0.f : -m_run * w_col;
-      }
-      float pr[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
-      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_h2(pr[0], pr[1], cur.vn.x), mul_h2(pr[2], pr[3], cur.vn.y)});
+        const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
+        const float m_new = max_nn(m_run, bm);
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+          asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
+          const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f((m_run - m_new) * w_col) : 1.f;
+          l_run *= alpha;
+  #pragma unroll
+          for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
+          m_run = m_new;
+          nm = (m_run == -INFINITY) ? 0.f : -m_run * w_col;
+        }
+        float pr[4];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
+        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_h2(pr[0], pr[1], cur.vn.x), mul_h2(pr[2], pr[3], cur.vn.y)});
 
-      __builtin_amdgcn_sched_barrier(0);
-      // P.V on the matrix cores: A = V (dims x tokens) per MFMA u
-      if constexpr (VK == V4) {
-        // Lookup keys pair the nibbles of two tokens for one dim, so the
-        // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
-        // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
-        const uint32_t w0 = vword(cur, 0), w1 = vword(cur, 1), w2 = vword(cur, 2), w3 = vword(cur, 3);
-        const uint32_t x1s = w1 << 4, x3s = w3 << 4;
-        const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
-        const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
-        const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
-        const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
-        constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
-#pragma unroll
-        for (int k = 0; k < NB; ++k) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
-                                lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
-            o_acc[2 * k + hh] =
-                __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[2 * k + hh], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // P.V on the matrix cores: A = V (dims x tokens) per MFMA u
+        if constexpr (VK == V4) {
+          // Lookup keys pair the nibbles of two tokens for one dim, so the
+          // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
+          // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
+          const uint32_t w0 = vword(cur, 0), w1 = vword(cur, 1), w2 = vword(cur, 2), w3 = vword(cur, 3);
+          const uint32_t x1s = w1 << 4, x3s = w3 << 4;
+          const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
+          const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+          const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
+          const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
+          constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
+  #pragma unroll
+          for (int k = 0; k < NB; ++k) {
+  #pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
+                                  lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
+              o_acc[2 * k + hh] =
+                  __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[2 * k + hh], 0, 0, 0);
+            }
+          }
+        } else {
+          constexpr int NBY = D / 64;  // bytes per token in this lane (4 dims each)
+  #pragma unroll
+          for (int k = 0; k < NBY; ++k) {
+            uint2 lk[4];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
+              if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
+              else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
+            }
+  #pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+              const uint32_t w0 = (t >> 1) ? lk[0].y : lk[0].x;
+              const uint32_t w1 = (t >> 1) ? lk[1].y : lk[1].x;
+              const uint32_t w2 = (t >> 1) ? lk[2].y : lk[2].x;
+              const uint32_t w3 = (t >> 1) ? lk[3].y : lk[3].x;
+              const u32x2_t av = {__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
+              o_acc[4 * k + t] =
+                  __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[4 * k + t], 0, 0, 0);
+            }
           }
         }
-      } else {
-        constexpr int NBY = D / 64;  // bytes per token in this lane (4 dims each)
-#pragma unroll
-        for (int k = 0; k < NBY; ++k) {
-          uint2 lk[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
-            if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
-            else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-            const uint32_t w0 = (t >> 1) ? lk[0].y : lk[0].x;
-            const uint32_t w1 = (t >> 1) ? lk[1].y : lk[1].x;
-            const uint32_t w2 = (t >> 1) ? lk[2].y : lk[2].x;
-            const uint32_t w3 = (t >> 1) ? lk[3].y : lk[3].x;
-            const u32x2_t av = {__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
-            o_acc[4 * k + t] =
-                __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[4 * k + t], 0, 0, 0);
-          }
+      };
+
+      // one block (j): issue tile j+2, look up the entry of j+3 and take the
+      // index of j+4, compute tile j
+      auto step = [&](const Tile<D, KK, VK>& cur, Tile<D, KK, VK>& dst) -> bool {
+        if (idx_c >= n) return false;
+        bool ok2;
+        entry(ph2v, idx_2, ok2);
+        load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+        const int idx_3 = __builtin_amdgcn_readfirstlane(g3);
+        const int ph3v = bt_at(idx_3);
+        g3 = grab();
+        compute(cur, b0 + idx_c, ok_c);
+        idx_c = idx_1; ok_c = ok_1;
+        idx_1 = idx_2; ok_1 = ok2;
+        idx_2 = idx_3; ph2v = ph3v;
+        return true;
+      };
+      for (;;) {
+        if (!step(A, C3)) break;
+        if (!step(B, A)) break;
+        if (!step(C3, B)) break;
+      }
+
+      // -------- wave states to LDS (rotated domain): wave w stores its
+      // unnormalised O rows (q head g at slot row 8 w + g) and its running
+      // max / sum per q head
+      __syncthreads();  // every wave is done with the q operands (the slots overlay them)
+      l_run += lane_xor<16>(l_run, lane);
+      l_run += lane_xor<32>(l_run, lane);
+      if (!lo_part) {
+        float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
+  #pragma unroll
+        for (int e = 0; e < 4; ++e)
+  #pragma unroll
+          for (int h = 0; h < C::R / 4; ++h)
+            *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
+                float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
+        if (a == 0) {
+          s_ml[16 * wave + gq] = m_run;
+          s_ml[16 * wave + 8 + gq] = l_run;
         }
       }
-    };
+      __syncthreads();
 
-    // one block (j): issue tile j+2, look up the entry of j+3 and take the
-    // index of j+4, compute tile j
-    auto step = [&](const Tile<D, KK, VK>& cur, Tile<D, KK, VK>& dst) -> bool {
-      if (idx_c >= n) return false;
-      bool ok2;
-      entry(ph2v, idx_2, ok2);
-      load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
-      const int idx_3 = __builtin_amdgcn_readfirstlane(g3);
-      const int ph3v = bt_at(idx_3);
-      g3 = grab();
-      compute(cur, b0 + idx_c, ok_c);
-      idx_c = idx_1; ok_c = ok_1;
-      idx_1 = idx_2; ok_1 = ok2;
-      idx_2 = idx_3; ph2v = ph3v;
-      return true;
-    };
-    for (;;) {
-      if (!step(A, C3)) break;
-      if (!step(B, A)) break;
-      if (!step(C3, B)) break;
-    }
-
-    // -------- wave states to LDS (rotated domain): wave w stores its
-    // unnormalised O rows (q head g at slot row 8 w + g) and its running
-    // max / sum per q head
-    __syncthreads();  // every wave is done with the q operands (the slots overlay them)
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (!lo_part) {
-      float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int h = 0; h < C::R / 4; ++h)
-          *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
-              float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
-      if (a == 0) {
-        s_ml[16 * wave + gq] = m_run;
-        s_ml[16 * wave + 8 + gq] = l_run;
-      }
-    }
-    __syncthreads();
-
-    // -------- combine the parts of each (kv head, q head) pair, normalise,
-    // inverse rotation, write.  Pairs are spread over the waves; lane l
-    // holds dims l + 64 i (the rotation's top stage, D = 128, is in the lane).
-    for (int pr = wave; pr < HG * p.G; pr += kWaves) {
-      const int h2 = pr / p.G, g = pr % p.G;
-      const float wc = ldexpf(p.score_mul, -s_qexp[8 * h2 + g]);
-      float M = -INFINITY;
-      for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * (h2 + HG * q) + g]);
-      constexpr int NY = D / 64;
-      float y[NY];
-#pragma unroll
-      for (int i = 0; i < NY; ++i) y[i] = 0.f;
-      float L = 0.f;
-      for (int q = 0; q < NPW; ++q) {
-        const int wq = h2 + HG * q;
-        const float mw = s_ml[16 * wq + g];
-        const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * wc);
-        L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
-        const float* srow = slots + (8 * wq + g) * C::DS;
-#pragma unroll
-        for (int i = 0; i < NY; ++i) y[i] = __builtin_fmaf(f, srow[lane + 64 * i], y[i]);
-      }
-      if constexpr (NY == 2) {
-        const float t0 = y[0];
-        y[0] = t0 + y[1];
-        y[1] = t0 - y[1];
-      }
-#pragma unroll
-      for (int k = 32; k > 0; k >>= 1) {
-        const bool up = (lane & k) != 0;
-#pragma unroll
+      // -------- combine the parts of each (kv head, q head) pair, normalise,
+      // inverse rotation, write.  Pairs are spread over the waves; lane l
+      // holds dims l + 64 i (the rotation's top stage, D = 128, is in the lane).
+      for (int pr = wave; pr < HG * p.G; pr += kWaves) {
+        const int h2 = pr / p.G, g = pr % p.G;
+        const float wc = ldexpf(p.score_mul, -s_qexp[8 * h2 + g]);
+        float M = -INFINITY;
+        for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * (h2 + HG * q) + g]);
+        constexpr int NY = D / 64;
+        float y[NY];
+  #pragma unroll
+        for (int i = 0; i < NY; ++i) y[i] = 0.f;
+        float L = 0.f;
+        for (int q = 0; q < NPW; ++q) {
+          const int wq = h2 + HG * q;
+          const float mw = s_ml[16 * wq + g];
+          const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * wc);
+          L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
+          const float* srow = slots + (8 * wq + g) * C::DS;
+  #pragma unroll
+          for (int i = 0; i < NY; ++i) y[i] = __builtin_fmaf(f, srow[lane + 64 * i], y[i]);
+        }
+        if constexpr (NY == 2) {
+          const float t0 = y[0];
+          y[0] = t0 + y[1];
+          y[1] = t0 - y[1];
+        }
+        wht_lanes<32>(y, lane);
+        wht_lanes<16>(y, lane);
+        wht_lanes<8>(y, lane);
+        wht_lanes<4>(y, lane);
+        wht_lanes<2>(y, lane);
+        wht_lanes<1>(y, lane);
+        const bool empty = !(L > 0.f);
+        const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
+        const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
+        const float lse = empty ? -INFINITY : (M * wc + log2f(L)) * kLn2;
+        const int hq = (grp * HG + h2) * p.G + g;
+  #pragma unroll
         for (int i = 0; i < NY; ++i) {
-          const float o = __shfl_xor(y[i], k);
-          y[i] = up ? (o - y[i]) : (y[i] + o);
+          const int d = lane + 64 * i;
+          const float sv = y[i] * scale;
+          y[i] = ((s_par[24 + (d >> 5)] >> (d & 31)) & 1u) ? -sv : sv;
+        }
+        if (whole) {
+          const int64_t off = ((int64_t)s * p.Hq + hq) * D + lane;
+  #pragma unroll
+          for (int i = 0; i < NY; ++i) {
+            if (p.out_f32) static_cast<float*>(p.out)[off + 64 * i] = y[i];
+            else static_cast<uint16_t*>(p.out)[off + 64 * i] = f32_to_bf16_rne(y[i]);
+          }
+          if (lane == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
+          if (lane == 0 && p.P > 1) p.part_lse[((int64_t)s * p.Hq + hq) * p.P] = __uint_as_float(kDoneBits);
+        } else {
+          const int64_t row0 = ((int64_t)s * p.Hq + hq) * p.P;
+          const int64_t row = row0 + piece;
+  #pragma unroll
+          for (int i = 0; i < NY; ++i) p.part_o[row * D + lane + 64 * i] = y[i];
+          if (lane == 0) p.part_lse[row] = lse;
+          if (piece == n_pieces - 1)   // the last piece closes the slots no piece uses
+            for (int i = n_pieces + lane; i < p.P; i += 64) p.part_lse[row0 + i] = -INFINITY;
         }
       }
-      const bool empty = !(L > 0.f);
-      const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
-      const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
-      const float lse = empty ? -INFINITY : (M * wc + log2f(L)) * kLn2;
-      const int hq = (grp * HG + h2) * p.G + g;
-#pragma unroll
-      for (int i = 0; i < NY; ++i) {
-        const int d = lane + 64 * i;
-        const float sv = y[i] * scale;
-        y[i] = ((s_par[24 + (d >> 5)] >> (d & 31)) & 1u) ? -sv : sv;
-      }
-      if (whole) {
-        const int64_t off = ((int64_t)s * p.Hq + hq) * D + lane;
-#pragma unroll
-        for (int i = 0; i < NY; ++i) {
-          if (p.out_f32) static_cast<float*>(p.out)[off + 64 * i] = y[i];
-          else static_cast<uint16_t*>(p.out)[off + 64 * i] = f32_to_bf16_rne(y[i]);
-        }
-        if (lane == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
-        if (lane == 0 && p.P > 1) p.part_lse[((int64_t)s * p.Hq + hq) * p.P] = __uint_as_float(kDoneBits);
-      } else {
-        const int64_t row0 = ((int64_t)s * p.Hq + hq) * p.P;
-        const int64_t row = row0 + piece;
-#pragma unroll
-        for (int i = 0; i < NY; ++i) p.part_o[row * D + lane + 64 * i] = y[i];
-        if (lane == 0) p.part_lse[row] = lse;
-        if (piece == n_pieces - 1)   // the last piece closes the slots no piece uses
-          for (int i = n_pieces + lane; i < p.P; i += 64) p.part_lse[row0 + i] = -INFINITY;
-      }
+
     }
 
-    // -------- next piece
-    pos += b1 - b0;
+    // -------- next segment
+    pos = vb0 + nb_s;
     if (pos >= r1) break;
-    blk = 0;
+    off = 0;
     if (++grp == p.NG) {
       grp = 0;
       do {
         ++s;
-        nb_s = (clamp_ctx(scalar_ld(p.context_lens, s), cap) + 15) >> 4;
+        nb_s = (seq_len(p, cl0, s) + 15) >> 4;
       } while (nb_s == 0);
     }
   }
@@ -1131,7 +1213,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   tq_decode_workspace_bytes(num_seqs, num_q_heads, D, num_splits, &need);
   if (workspace_bytes < need || (need && !workspace))
     return set_error(TQ_ERR_VALUE, "workspace too small: need " + std::to_string(need) + " bytes");
-  const int64_t work_bound = (int64_t)num_seqs * num_kv_heads * max_blocks_per_seq;
+  const int64_t work_bound = (int64_t)num_seqs * num_kv_heads * (max_blocks_per_seq + 128);
   if (work_bound >= (1ll << 30) || max_blocks_per_seq > (1 << 20))
     return set_error(TQ_ERR_VALUE, "too much work for one call (2^30 block-heads, 2^20 blocks per sequence)");
   const int64_t q_bytes = (int64_t)num_seqs * num_q_heads * D * (q_dtype == TQ_F32 ? 4 : 2);
@@ -1169,6 +1251,9 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   }
   p.HG = HG;
   p.NG = num_kv_heads / HG;
+  // starting a piece (set-up, rotation of q, epilogue) costs about as much
+  // time as streaming 128 tiles of one kv head, i.e. 128 / HG blocks
+  p.seg_cost = 128 / HG;
   const int64_t units = (int64_t)num_seqs * p.NG * max_blocks_per_seq;
   p.n_wg = (int)(units < cus ? (units > 0 ? units : 1) : cus);
   p.k_tile = tile_bytes_of(kfmt);
