@@ -421,6 +421,24 @@ __device__ __forceinline__ int range_len(int W, int n_wg, int max_blocks, int P)
   return R > need ? R : need;
 }
 
+// Waves -> (kv head of the group, part).  The 16 waves sit on the 4 SIMDs
+// as wave % 4, and on a SIMD older waves (lower index) issue first.  With 8
+// heads of 2 parts, head h % 4 + 4 b is served by the waves of ranks {0, 3}
+// (b = 0) or {1, 2} (b = 1) on SIMD h % 4, so that every head gets the same
+// share of issue slots; otherwise head h has parts h + HG q.
+__device__ __forceinline__ int head_of_wave(int wave, int HG) {
+  if (HG == 8) {
+    const int r = wave >> 2;
+    return (wave & 3) | (((r ^ (r >> 1)) & 1) << 2);
+  }
+  return wave % HG;
+}
+__device__ __forceinline__ int part_of_wave(int wave, int HG) { return HG == 8 ? wave >> 3 : wave / HG; }
+__device__ __forceinline__ int wave_of_part(int h, int q, int HG) {
+  if (HG == 8) return 4 * (q ? ((h & 4) ? 2 : 3) : ((h & 4) ? 1 : 0)) + (h & 3);
+  return h + HG * q;
+}
+
 // Workgroup LDS.  The tables come first so that every table address
 // (< 64 KB) fits the immediate offset of the LDS read.
 template <int D, int KK, int VK>
@@ -585,8 +603,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // wave -> (kv head of the group, part): the NPW waves of a head share its blocks
   const int HG = p.HG;
   const int NPW = kWaves / HG;
-  const int hl = uni(wave % HG);
-  const int part = uni(wave / HG);
+  const int hl = uni(head_of_wave(wave, HG));
+  const int part = uni(part_of_wave(wave, HG));
   half8_t* const qv_all = reinterpret_cast<half8_t*>(xbuf);            // [hl][t][lane]
   float* const qf_all = xbuf + 8 * C::QV_FLOATS;                       // [hl][g] rows of QS floats
   float* const slots = xbuf;                                           // [wave][g] rows of DS floats
@@ -985,14 +1003,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int h2 = pr / p.G, g = pr % p.G;
         const float wc = ldexpf(p.score_mul, -s_qexp[8 * h2 + g]);
         float M = -INFINITY;
-        for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * (h2 + HG * q) + g]);
+        for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * wave_of_part(h2, q, HG) + g]);
         constexpr int NY = D / 64;
         float y[NY];
   #pragma unroll
         for (int i = 0; i < NY; ++i) y[i] = 0.f;
         float L = 0.f;
         for (int q = 0; q < NPW; ++q) {
-          const int wq = h2 + HG * q;
+          const int wq = wave_of_part(h2, q, HG);
           const float mw = s_ml[16 * wq + g];
           const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * wc);
           L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
@@ -1041,7 +1059,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             for (int i = n_pieces + lane; i < p.P; i += 64) p.part_lse[row0 + i] = -INFINITY;
         }
       }
-
     }
 
     // -------- next segment
