@@ -87,6 +87,7 @@ struct DecodeParams {
   int32_t HG, NG;    // kv heads per workgroup group (1, 2, 4 or 8) and groups (Hkv / HG)
   int32_t n_wg;      // grid size (persistent workgroups)
   int32_t seg_cost;  // work positions charged for starting a piece (see seg_span)
+  float inv_G;       // 1 / G
   int32_t k_tile, v_tile, k_norm_off, v_norm_off;
   uint32_t k_span, v_span;   // bytes of each pool (< 4 GiB)
   float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K)), > 0
@@ -309,6 +310,15 @@ __device__ __forceinline__ int scalar_ld(const int32_t* ptr, int idx) {
 
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
+// The lane index, recomputed where it is called: values derived from it
+// are then not kept live across the block loop (which has no registers to
+// spare) but rebuilt where they are needed.
+__device__ __forceinline__ int fresh_lane() {
+  int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // A value known to be the same in every lane, moved to a scalar register so
 // that everything derived from it (addresses above all) stays scalar.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -472,8 +482,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);
   const int lane = tid & 63;
-  // context length of sequence `lane` (its load overlaps the table set-up)
-  const int cl_raw = lane < p.S ? p.context_lens[lane] : 0;
+  // Touch every 64-byte line of the argument block at once: the first read
+  // of a line misses the scalar cache, and the fields are read at many
+  // points of the set-up, which would otherwise wait for a miss each.
+  {
+    const __attribute__((address_space(4))) uint32_t* ka =
+        (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+    static_assert(sizeof(DecodeParams) <= 7 * 64, "argument block spans more lines than are touched");
+    const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96];
+    asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6));
+  }
+  // context length of sequence `lane` (its load overlaps the table set-up;
+  // lanes past the last sequence read 0 through the descriptor's range check)
+  const int cl_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      tile_rsrc(reinterpret_cast<const uint8_t*>(p.context_lens), 4 * p.S), (uint32_t)(4 * lane), 0, 0);
   const int cl0 = clamp_ctx(cl_raw, p.max_blocks * 16);
 
   // ---- small per-call tables to LDS (kernel arguments read at compile-time
@@ -649,13 +671,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       };
       constexpr int NBT = kBtCap / kThreads;
       int btv[NBT];
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < NBT; ++i) {
         const int e = tid + kThreads * i;
         btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
       }
       constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per q head
-      const int g8 = lane >> 3, l8 = lane & 7;
+      const int ln = fresh_lane();
+      const int g8 = ln >> 3, l8 = ln & 7;
       const bool q_live = g8 < p.G;
       // raw q words of this lane's PER channels (bf16: two per word, the upper
       // half of qw unused); one load shape for both dtypes, bytes past the q
@@ -667,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int head0 = uni((int)(((int64_t)s * p.Hq + kvh * p.G) * D * esz));   // first q row of the head
         const uint32_t lane_off = (uint32_t)(((q_live ? g8 : 0) * D + l8 * PER) * esz);
         const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < PER / 4; ++i) {
           const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
           qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
@@ -711,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
       entry(v1, idx_1, ok_1);
       load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
 
       // -------- part 0 of each head: rotate the head's G q rows once (row g of
@@ -723,24 +746,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         {
           float x[PER];
           if (p.q_f32) {
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
           } else {
-  #pragma unroll
+#pragma unroll
             for (int k = 0; k < PER / 2; ++k) {
               x[2 * k] = __uint_as_float(qw[k] << 16);
               x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
             }
           }
           const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < PER; ++e) {
             if ((sw >> e) & 1u) x[e] = -x[e];
             if (!q_live) x[e] = 0.f;
           }
-  #pragma unroll
+#pragma unroll
           for (int h = 1; h < PER; h <<= 1) {
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < PER; ++e)
               if ((e & h) == 0) {
                 const float a0 = x[e], b0v = x[e + h];
@@ -748,21 +771,53 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
                 x[e + h] = a0 - b0v;
               }
           }
-          wht_lanes<1>(x, lane);   // lane bits 0-2: the 8 lanes of a q row
-          wht_lanes<2>(x, lane);
-          wht_lanes<4>(x, lane);
-          float amax = 0.f;
+          // the 3 stages across the 8 lanes of the row go through LDS: the
+          // row is written in channel order, then lane l8 takes channels
+          // PER k + PH l8 + m (k < 8, m < PH) and runs those stages in its
+          // registers
+          constexpr int PH = PER / 8;
           float* qrow = qf + g8 * C::QS;
-  #pragma unroll
+          auto at = [](int c) { return c + 4 * (c >> 4); };   // padded position of channel c
+#pragma unroll
           for (int i = 0; i < PER / 4; ++i) {
             const int c = l8 * PER + 4 * i;
-            *reinterpret_cast<float4*>(qrow + c + 4 * (c >> 4)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+            *reinterpret_cast<float4*>(qrow + at(c)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
           }
-  #pragma unroll
-          for (int e = 0; e < PER; ++e) amax = fmaxf(amax, fabsf(x[e]));
-          amax = fmaxf(amax, lane_xor<1>(amax, lane));
-          amax = fmaxf(amax, lane_xor<2>(amax, lane));
-          amax = fmaxf(amax, lane_xor<4>(amax, lane));
+          // (same wave: its LDS writes are visible to its later reads)
+          float y[8 * PH];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int c = PER * k + PH * l8;
+            if constexpr (PH == 2) {
+              const float2 f = *reinterpret_cast<const float2*>(qrow + at(c));
+              y[2 * k] = f.x;
+              y[2 * k + 1] = f.y;
+            } else {
+              y[k] = qrow[at(c)];
+            }
+          }
+#pragma unroll
+          for (int h = PH; h < 8 * PH; h <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 8 * PH; ++e)
+              if ((e & h) == 0) {
+                const float a0 = y[e], b0v = y[e + h];
+                y[e] = a0 + b0v;
+                y[e + h] = a0 - b0v;
+              }
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int c = PER * k + PH * l8;
+            if constexpr (PH == 2) *reinterpret_cast<float2*>(qrow + at(c)) = float2{y[2 * k], y[2 * k + 1]};
+            else qrow[at(c)] = y[k];
+          }
+#pragma unroll
+          for (int e = 0; e < 8 * PH; ++e) amax = fmaxf(amax, fabsf(y[e]));
+          amax = fmaxf(amax, lane_xor<1>(amax, ln));
+          amax = fmaxf(amax, lane_xor<2>(amax, ln));
+          amax = fmaxf(amax, lane_xor<4>(amax, ln));
           int ex = 0;
           if (amax > 0.f) frexpf(amax, &ex);
           if (l8 == 0) s_qexp[8 * hl + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
@@ -770,21 +825,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         // (same wave: its LDS writes above are visible to its reads below)
         const float q_pow = ldexpf(1.0f, s_qexp[8 * hl + gq]);
         const float* qrow = qf + gq * C::QS;
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < NQK; ++t) {
           float vq[8];
           if constexpr (C::MIXED) {
             constexpr int m = D / 2;
             constexpr int per_g = NQK / 2;
             const int grp_k = t / per_g, u = t % per_g;
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int pos_l = grp_k * m + a * (m / 4) + 8 * u + e;
               const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
               vq[e] = qrow[chn + 4 * (chn >> 4)];
             }
           } else {
-  #pragma unroll
+#pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int c = a * (D / 4) + 8 * t + 4 * h;
               const float4 f = *reinterpret_cast<const float4*>(qrow + c + 4 * (c >> 4));
@@ -792,14 +847,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             }
           }
           half8_t qv;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float v = vq[e] * q_pow;
             const _Float16 hi = (_Float16)v;
             const _Float16 lo = (_Float16)(v - (float)hi);
             qv[e] = lo_part ? lo : hi;
           }
-          qv_all[(hl * NQK + t) * 64 + lane] = qv;
+          qv_all[(hl * NQK + t) * 64 + ln] = qv;
         }
       }
       __syncthreads();  // operands, counters and block-table entries ready
@@ -812,7 +867,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       float m_run = -INFINITY, l_run = 0.f;
       float nm = 0.f;   // -m_run * w_col (0 while m_run is -inf)
       float4_t o_acc[C::R];
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
 
       // token r's V bytes of this lane, from byte 0 (r compile-time)
@@ -825,15 +880,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
         float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
         if constexpr (KK == K4) {
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < NQK; ++t) {
             u32x4_t av;
-  #pragma unroll
+#pragma unroll
             for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[t], off4_k, by));
             acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
           }
         } else if constexpr (KK == K2) {
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < NQK; ++t) {
             const uint2 x0 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1)));
             const uint2 x1 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1) + 1));
@@ -842,20 +897,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
         } else {
           constexpr int per_g = NQK / 2;
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < per_g; ++u) {
             u32x4_t av;
-  #pragma unroll
+#pragma unroll
             for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[u], off4_k, by));
             acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
           }
           constexpr int LB = 3 * D / 64;
           const int lo_off = tokK * C::KROW + D / 4 + LB * a;
           const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((lo_off & 3) * 8);
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < per_g; ++u) {
             u32x4_t av;
-  #pragma unroll
+#pragma unroll
             for (int pr = 0; pr < 4; ++pr) {
               const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
               av[pr] = lds_u32(lds, (key << 6) | off3);
@@ -871,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         // the exp2-domain score is w_col * sr (w_col > 0), folded into one fma
         const int tok0 = 16 * b;
         float sc[4];
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float full0 = acc0[e] + row_ror8(acc0[e]);
           const uint32_t kw = (e >> 1) ? cur.kn[0].y : cur.kn[0].x;
@@ -884,7 +939,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           sc[e] = v;
         }
         if (!(ok && tok0 + 16 <= ctx)) {   // partial or skipped block (wave-uniform branch)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx) ? sc[e] : -INFINITY;
         }
         const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
@@ -893,13 +948,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
           const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f((m_run - m_new) * w_col) : 1.f;
           l_run *= alpha;
-  #pragma unroll
+#pragma unroll
           for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
           m_run = m_new;
           nm = (m_run == -INFINITY) ? 0.f : -m_run * w_col;
         }
         float pr[4];
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
         l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_h2(pr[0], pr[1], cur.vn.x), mul_h2(pr[2], pr[3], cur.vn.y)});
@@ -917,9 +972,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
           const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
           constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < NB; ++k) {
-  #pragma unroll
+#pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
                                   lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
@@ -929,16 +984,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
         } else {
           constexpr int NBY = D / 64;  // bytes per token in this lane (4 dims each)
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < NBY; ++k) {
             uint2 lk[4];
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 4; ++r) {
               // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
               if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
               else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
             }
-  #pragma unroll
+#pragma unroll
             for (int t = 0; t < 4; ++t) {
               const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
               const uint32_t w0 = (t >> 1) ? lk[0].y : lk[0].x;
@@ -979,13 +1034,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // unnormalised O rows (q head g at slot row 8 w + g) and its running
       // max / sum per q head
       __syncthreads();  // every wave is done with the q operands (the slots overlay them)
-      l_run += lane_xor<16>(l_run, lane);
-      l_run += lane_xor<32>(l_run, lane);
+      const int le = fresh_lane();
+      l_run += lane_xor<16>(l_run, le);
+      l_run += lane_xor<32>(l_run, le);
       if (!lo_part) {
         float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 4; ++e)
-  #pragma unroll
+#pragma unroll
           for (int h = 0; h < C::R / 4; ++h)
             *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
                 float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
@@ -997,66 +1053,108 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       __syncthreads();
 
       // -------- combine the parts of each (kv head, q head) pair, normalise,
-      // inverse rotation, write.  Pairs are spread over the waves; lane l
-      // holds dims l + 64 i (the rotation's top stage, D = 128, is in the lane).
-      for (int pr = wave; pr < HG * p.G; pr += kWaves) {
-        const int h2 = pr / p.G, g = pr % p.G;
+      // inverse rotation, write.  Wave w takes pairs 4 w .. 4 w + 3, 16 lanes
+      // each.  Lane m of a pair first holds dims m + 16 k (k < D / 16) and
+      // runs the transform stages over k in its registers, passes the row
+      // through LDS, then holds dims (D / 16) m + k, runs the stages over k
+      // again and the remaining ones across the lanes of the pair.
+      if (4 * wave < HG * p.G) {
+        constexpr int ND = D / 16;
+        const int m = le & 15;
+        const int npair = HG * p.G;
+        const int pr_raw = 4 * wave + (le >> 4);
+        const bool live = pr_raw < npair;
+        const int pr = live ? pr_raw : npair - 1;
+        const int h2 = (int)(((float)pr + 0.5f) * p.inv_G);   // pr / G (pr < 64, G <= 8)
+        const int g = pr - h2 * p.G;
         const float wc = ldexpf(p.score_mul, -s_qexp[8 * h2 + g]);
         float M = -INFINITY;
         for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * wave_of_part(h2, q, HG) + g]);
-        constexpr int NY = D / 64;
-        float y[NY];
-  #pragma unroll
-        for (int i = 0; i < NY; ++i) y[i] = 0.f;
+        float y[ND];
+#pragma unroll
+        for (int k = 0; k < ND; ++k) y[k] = 0.f;
         float L = 0.f;
         for (int q = 0; q < NPW; ++q) {
           const int wq = wave_of_part(h2, q, HG);
           const float mw = s_ml[16 * wq + g];
           const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * wc);
           L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
-          const float* srow = slots + (8 * wq + g) * C::DS;
-  #pragma unroll
-          for (int i = 0; i < NY; ++i) y[i] = __builtin_fmaf(f, srow[lane + 64 * i], y[i]);
+          const float* srow = slots + (8 * wq + g) * C::DS + m;
+#pragma unroll
+          for (int k = 0; k < ND; ++k) y[k] = __builtin_fmaf(f, srow[16 * k], y[k]);
         }
-        if constexpr (NY == 2) {
-          const float t0 = y[0];
-          y[0] = t0 + y[1];
-          y[1] = t0 - y[1];
+#pragma unroll
+        for (int h = 1; h < ND; h <<= 1) {
+#pragma unroll
+          for (int e = 0; e < ND; ++e)
+            if ((e & h) == 0) {
+              const float a0 = y[e], b0v = y[e + h];
+              y[e] = a0 + b0v;
+              y[e + h] = a0 - b0v;
+            }
         }
-        wht_lanes<32>(y, lane);
-        wht_lanes<16>(y, lane);
-        wht_lanes<8>(y, lane);
-        wht_lanes<4>(y, lane);
-        wht_lanes<2>(y, lane);
-        wht_lanes<1>(y, lane);
+        // the row of part 0 is read only by this pair's lanes, each lane
+        // rewrites the dims it read (same wave: later reads see the writes)
+        float* row = slots + (8 * wave_of_part(h2, 0, HG) + g) * C::DS;
+#pragma unroll
+        for (int k = 0; k < ND; ++k) row[m + 16 * k] = y[k];
+#pragma unroll
+        for (int k = 0; k < ND; k += 4) {
+          const float4 f = *reinterpret_cast<const float4*>(row + ND * m + k);
+          y[k] = f.x; y[k + 1] = f.y; y[k + 2] = f.z; y[k + 3] = f.w;
+        }
+#pragma unroll
+        for (int h = 1; h < ND; h <<= 1) {
+#pragma unroll
+          for (int e = 0; e < ND; ++e)
+            if ((e & h) == 0) {
+              const float a0 = y[e], b0v = y[e + h];
+              y[e] = a0 + b0v;
+              y[e + h] = a0 - b0v;
+            }
+        }
+        wht_lanes<1>(y, le);   // dim bit 3 (D = 128) or bits 2, 3 (D = 64)
+        if constexpr (ND == 4) wht_lanes<2>(y, le);
         const bool empty = !(L > 0.f);
         const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
         const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
         const float lse = empty ? -INFINITY : (M * wc + log2f(L)) * kLn2;
         const int hq = (grp * HG + h2) * p.G + g;
-  #pragma unroll
-        for (int i = 0; i < NY; ++i) {
-          const int d = lane + 64 * i;
-          const float sv = y[i] * scale;
-          y[i] = ((s_par[24 + (d >> 5)] >> (d & 31)) & 1u) ? -sv : sv;
+        const int d0 = ND * m;
+        const uint32_t sgn = s_par[24 + (d0 >> 5)] >> (d0 & 31);
+#pragma unroll
+        for (int k = 0; k < ND; ++k) {
+          const float sv = y[k] * scale;
+          y[k] = ((sgn >> k) & 1u) ? -sv : sv;
         }
-        if (whole) {
-          const int64_t off = ((int64_t)s * p.Hq + hq) * D + lane;
-  #pragma unroll
-          for (int i = 0; i < NY; ++i) {
-            if (p.out_f32) static_cast<float*>(p.out)[off + 64 * i] = y[i];
-            else static_cast<uint16_t*>(p.out)[off + 64 * i] = f32_to_bf16_rne(y[i]);
+        if (live) {
+          if (whole) {
+            const int64_t off = ((int64_t)s * p.Hq + hq) * D + d0;
+            if (p.out_f32) {
+#pragma unroll
+              for (int k = 0; k < ND; k += 4)
+                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off + k) = float4{y[k], y[k + 1], y[k + 2], y[k + 3]};
+            } else {
+              uint32_t w[ND / 2];
+#pragma unroll
+              for (int k = 0; k < ND / 2; ++k)
+                w[k] = (uint32_t)f32_to_bf16_rne(y[2 * k]) | ((uint32_t)f32_to_bf16_rne(y[2 * k + 1]) << 16);
+              uint16_t* o16 = static_cast<uint16_t*>(p.out) + off;
+              if constexpr (ND == 8) *reinterpret_cast<uint4*>(o16) = uint4{w[0], w[1], w[2], w[3]};
+              else *reinterpret_cast<uint2*>(o16) = uint2{w[0], w[1]};
+            }
+            if (m == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
+            if (m == 0 && p.P > 1) p.part_lse[((int64_t)s * p.Hq + hq) * p.P] = __uint_as_float(kDoneBits);
+          } else {
+            const int64_t row0 = ((int64_t)s * p.Hq + hq) * p.P;
+            const int64_t prow = row0 + piece;
+#pragma unroll
+            for (int k = 0; k < ND; k += 4)
+              *reinterpret_cast<float4*>(p.part_o + prow * D + d0 + k) = float4{y[k], y[k + 1], y[k + 2], y[k + 3]};
+            if (m == 0) p.part_lse[prow] = lse;
+            if (piece == n_pieces - 1)   // the last piece closes the slots no piece uses
+              for (int i = n_pieces + m; i < p.P; i += 16) p.part_lse[row0 + i] = -INFINITY;
           }
-          if (lane == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
-          if (lane == 0 && p.P > 1) p.part_lse[((int64_t)s * p.Hq + hq) * p.P] = __uint_as_float(kDoneBits);
-        } else {
-          const int64_t row0 = ((int64_t)s * p.Hq + hq) * p.P;
-          const int64_t row = row0 + piece;
-  #pragma unroll
-          for (int i = 0; i < NY; ++i) p.part_o[row * D + lane + 64 * i] = y[i];
-          if (lane == 0) p.part_lse[row] = lse;
-          if (piece == n_pieces - 1)   // the last piece closes the slots no piece uses
-            for (int i = n_pieces + lane; i < p.P; i += 64) p.part_lse[row0 + i] = -INFINITY;
         }
       }
     }
@@ -1271,6 +1369,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   // starting a piece (set-up, rotation of q, epilogue) costs about as much
   // time as streaming 128 tiles of one kv head, i.e. 128 / HG blocks
   p.seg_cost = 128 / HG;
+  p.inv_G = 1.0f / (float)G;
   const int64_t units = (int64_t)num_seqs * p.NG * max_blocks_per_seq;
   p.n_wg = (int)(units < cus ? (units > 0 ? units : 1) : cus);
   p.k_tile = tile_bytes_of(kfmt);
