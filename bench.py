@@ -154,11 +154,14 @@ class Bench:
             self.step(warmup + i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        # per-launch decode duration with HIP events on the launch stream
+        # per-launch decode duration with HIP events on the launch stream; a
+        # short GPU-side spin before each start event keeps the host's
+        # enqueue time of the call out of the measured interval
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for i in range(steps):
             layer = (warmup + i) % self.L
             self.write(layer)
+            torch.cuda._sleep(200000)
             ev[i][0].record()
             self.decode(layer)
             ev[i][1].record()
