@@ -361,9 +361,10 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 }
 
 // Context lengths, clamped to [0, 16 max_blocks]: cl0 holds sequence `lane`
-// (sequences 0-63, read once per kernel); later sequences are read on use.
-__device__ __forceinline__ int seq_len(const DecodeParams& p, int cl0, int s) {
-  if (s < 64) return __builtin_amdgcn_readlane(cl0, s);
+// (sequences 0-63, read once per kernel, kept in LDS as s_cl); later
+// sequences are read on use.
+__device__ __forceinline__ int seq_len(const DecodeParams& p, const int* s_cl, int s) {
+  if (s < 64) return __builtin_amdgcn_readfirstlane(s_cl[s]);
   return clamp_ctx(scalar_ld(p.context_lens, s), p.max_blocks * 16);
 }
 __device__ __forceinline__ int lane_len(const DecodeParams& p, int cl0, int base, int lane) {
@@ -463,6 +464,8 @@ struct Smem {
   int s_qexp[64];            // [kv head of the group][q head]
   int s_next[8];             // per kv head of the group: next free piece block
   int s_bt[kBtCap];          // block-table entries of the piece's first kBtCap blocks
+  int s_cl[64];              // clamped context lengths of sequences 0-63
+  int s_plan[8];             // work split: R, range start and end, first segment
 };
 
 template <int D, int KK, int VK>
@@ -478,30 +481,53 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   int* const s_qexp = sm.s_qexp;
   int* const s_next = sm.s_next;
   int* const s_bt = sm.s_bt;
+  int* const s_cl = sm.s_cl;
+  int* const s_plan = sm.s_plan;
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);
   const int lane = tid & 63;
-  // Touch every 64-byte line of the argument block at once: the first read
-  // of a line misses the scalar cache, and the fields are read at many
-  // points of the set-up, which would otherwise wait for a miss each.
-  {
-    const __attribute__((address_space(4))) uint32_t* ka =
-        (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
-    static_assert(sizeof(DecodeParams) <= 7 * 64, "argument block spans more lines than are touched");
-    const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96];
-    asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6));
-  }
-  // context length of sequence `lane` (its load overlaps the table set-up;
-  // lanes past the last sequence read 0 through the descriptor's range check)
-  const int cl_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(
-      tile_rsrc(reinterpret_cast<const uint8_t*>(p.context_lens), 4 * p.S), (uint32_t)(4 * lane), 0, 0);
-  const int cl0 = clamp_ctx(cl_raw, p.max_blocks * 16);
-
-  // ---- small per-call tables to LDS (kernel arguments read at compile-time
-  // offsets only, then spread over lanes by lane selects; lane-indexed reads
-  // of the argument block would be slow per-lane vector loads)
+  // ---- wave 0 plans: it alone reads the context lengths and splits the
+  // work, and publishes its results in LDS; wave 1 meanwhile spreads the
+  // small per-call tables (kernel arguments read at compile-time offsets
+  // only, then spread over lanes by lane selects; lane-indexed reads of the
+  // argument block would be slow per-lane vector loads)
   if (wave == 0) {
+    // Touch every 64-byte line of the argument block at once: the first read
+    // of a line misses the scalar cache, and the fields are read at many
+    // points of the set-up, which would otherwise wait for a miss each.
+    {
+      const __attribute__((address_space(4))) uint32_t* ka =
+          (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+      static_assert(sizeof(DecodeParams) <= 7 * 64, "argument block spans more lines than are touched");
+      const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96];
+      asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6));
+    }
+    // context length of sequence `lane` (lanes past the last sequence read 0
+    // through the descriptor's range check)
+    const int cl_raw = (int)__builtin_amdgcn_raw_buffer_load_b32(
+        tile_rsrc(reinterpret_cast<const uint8_t*>(p.context_lens), 4 * p.S), (uint32_t)(4 * lane), 0, 0);
+    const int cap = p.max_blocks * 16;
+    const int cl0 = clamp_ctx(cl_raw, cap);
+    s_cl[lane] = cl0;
+    // context lengths outside [0, 16 * max_blocks] are reported (first
+    // workgroup) and clamped
+    if (blockIdx.x == 0 && lane < p.S && (cl_raw < 0 || cl_raw > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - lane);
+    const int W = total_work(p, cl0, lane);
+    const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
+    int r0 = blockIdx.x * R;
+    int r1 = (r0 + R < W) ? r0 + R : W;
+    if (p.P == 1) {   // whole segments only: there is no workspace for partials
+      r0 = snap_to_segment(p, cl0, lane, r0, W);
+      r1 = snap_to_segment(p, cl0, lane, r1, W);
+    }
+    int s0 = 0, grp0 = 0, off0 = 0, nb0 = 0;
+    if (r0 < r1) locate(p, cl0, lane, r0, s0, grp0, off0, nb0);
+    if (lane == 0) {
+      s_plan[0] = R; s_plan[1] = r0; s_plan[2] = r1; s_plan[3] = s0;
+      s_plan[4] = grp0; s_plan[5] = off0; s_plan[6] = nb0;
+    }
+  } else if (wave == 1) {
     uint32_t x = 0;
     auto put = [&](uint32_t v, int i, uint32_t cur) -> uint32_t { return lane == i ? v : cur; };
 #pragma unroll
@@ -524,6 +550,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     s_par[lane] = x;
   }
+  __syncthreads();   // plan, lengths and s_par written
 
   auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
@@ -539,7 +566,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const uint32_t sh = (uint32_t)(wh & 1) * 16u;
     const int kind0 = uni(p.half_kind[0]), kind1 = uni(p.half_kind[1]);   // scalar reads
     const int kind = h ? kind1 : kind0;
-    __syncthreads();   // s_par written by wave 0
     const uint4 r03 = *reinterpret_cast<const uint4*>(s_par + 8 * h);
     const uint4 r47 = *reinterpret_cast<const uint4*>(s_par + 8 * h + 4);
     const uint32_t cw[8] = {r03.x, r03.y, r03.z, r03.w, r47.x, r47.y, r47.z, r47.w};
@@ -570,24 +596,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
   }
 
-  // ---- work range of this workgroup (every wave computes the same numbers)
-  const int W = total_work(p, cl0, lane);
-  const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
-  int r0 = blockIdx.x * R;
-  int r1 = (r0 + R < W) ? r0 + R : W;
-  if (p.P == 1) {   // whole segments only: there is no workspace for partials
-    r0 = snap_to_segment(p, cl0, lane, r0, W);
-    r1 = snap_to_segment(p, cl0, lane, r1, W);
-  }
+  // ---- the plan (uniform values)
+  const int R = uni(s_plan[0]);
+  const int r0 = uni(s_plan[1]), r1 = uni(s_plan[2]);
 
-  // sequences with no cached token: out = 0, lse = -inf (first workgroup);
-  // context lengths outside [0, 16 * max_blocks] are reported and clamped
+  // sequences with no cached token: out = 0, lse = -inf (first workgroup;
+  // lengths of sequences past the first 64 are reported here)
   if (blockIdx.x == 0) {
     const int cap = p.max_blocks * 16;
     for (int s = wave; s < p.S; s += kWaves) {
-      const int c = s < 64 ? __builtin_amdgcn_readlane(cl_raw, s) : p.context_lens[s];
-      if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
-      if (clamp_ctx(c, cap) == 0) {
+      int c;
+      if (s < 64) {
+        c = uni(s_cl[s]);
+      } else {
+        c = p.context_lens[s];
+        if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
+        c = clamp_ctx(c, cap);
+      }
+      if (c == 0) {
         for (int idx = lane; idx < p.Hq * D; idx += 64) {
           const int64_t off = (int64_t)s * p.Hq * D + idx;
           if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
@@ -632,8 +658,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   float* const slots = xbuf;                                           // [wave][g] rows of DS floats
 
   // ---- walk the pieces of this workgroup's range
-  int s, grp, off, nb_s;
-  locate(p, cl0, lane, r0, s, grp, off, nb_s);
+  int s = uni(s_plan[3]), grp = uni(s_plan[4]), off = uni(s_plan[5]), nb_s = uni(s_plan[6]);
   int pos = r0;
   bool first = true;
   while (pos < r1) {
@@ -645,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const bool whole = p.P == 1 || (vb0 / R) == ((vb0 + nb_s - 1) / R);
     const int piece = (int)blockIdx.x - vb0 / R;
     const int n_pieces = (vb0 + nb_s - 1) / R - vb0 / R + 1;
-      const int ctx = seq_len(p, cl0, s);
+      const int ctx = seq_len(p, s_cl, s);
       const int kvh = grp * HG + hl;   // this wave's kv head
       const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
       const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
@@ -1167,7 +1192,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       grp = 0;
       do {
         ++s;
-        nb_s = (seq_len(p, cl0, s) + 15) >> 4;
+        nb_s = (seq_len(p, s_cl, s) + 15) >> 4;
       } while (nb_s == 0);
     }
   }
@@ -1180,8 +1205,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 // decode mode the decode kernel has marked the rows it wrote out directly
 // (kDoneBits in slot 0) and set the slots past a segment's last piece to
 // -inf, so no segment bookkeeping is redone here.  Lane l loads the lse of
-// slot l; the o rows of the live slots of each chunk of 16 are then loaded
-// together (two memory round trips for P <= 16).
+// slot l; the o rows of the first 16 slots are loaded at the same time, those
+// of the live slots among later ones once their lse values are known.
 struct MergeParams {
   const float* part_o;
   const float* part_lse;
@@ -1190,14 +1215,28 @@ struct MergeParams {
   int32_t S, H, P, D, out_f32, decode;
 };
 
-__global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
+constexpr int kMergeRows = 1;   // rows (one per wave) per merge workgroup
+
+__global__ __launch_bounds__(64 * kMergeRows) void merge_kernel(MergeParams p) {
   constexpr int CH = 16;
-  const int64_t sh = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int64_t sh = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (sh >= (int64_t)p.S * p.H) return;   // (wave-uniform)
   const int P = p.P, D = p.D;
   const float* lse_p = p.part_lse + sh * P;
   const float* o_p = p.part_o + sh * (int64_t)P * D;
   const float lf = lane < P ? lse_p[lane] : -INFINITY;
+  // the o rows of the first CH slots are loaded with the lse values, before
+  // the slots are known to be live (dead slots hold stale values that get
+  // weight 0), so that rows with up to CH pieces take one memory round trip
+  float ov0[CH][2];
+#pragma unroll
+  for (int k = 0; k < CH; ++k)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int dim = lane + 64 * r;
+      ov0[k][r] = (k < P && dim < D) ? o_p[(int64_t)k * D + dim] : 0.f;
+    }
   if (p.decode && (uint32_t)__builtin_amdgcn_readfirstlane(__float_as_uint(lf)) == kDoneBits) return;
   auto slot_lse = [&](int i) -> float {   // i uniform
     return i < 64 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lf), i)) : lse_p[i];
@@ -1218,7 +1257,7 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int dim = lane + 64 * r;
-          ov[k][r] = (li != -INFINITY && dim < D) ? o_p[(int64_t)(base + k) * D + dim] : 0.f;
+          ov[k][r] = base == 0 ? ov0[k][r] : ((li != -INFINITY && dim < D) ? o_p[(int64_t)(base + k) * D + dim] : 0.f);
         }
       }
 #pragma unroll
@@ -1226,7 +1265,7 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeParams p) {
         const float wk = (w[k] == -INFINITY) ? 0.f : expf(w[k] - M);
         den += wk;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) acc[r] = __builtin_fmaf(wk, ov[k][r], acc[r]);
+        for (int r = 0; r < 2; ++r) acc[r] = wk > 0.f ? __builtin_fmaf(wk, ov[k][r], acc[r]) : acc[r];
       }
     }
   }
@@ -1290,7 +1329,8 @@ extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse
   if (num_seqs == 0) return TQ_OK;
   if (!part_out || !part_lse || !out) return set_error(TQ_ERR_VALUE, "NULL merge buffer");
   MergeParams mp = {part_out, part_lse, out, lse, num_seqs, num_heads, num_splits, head_dim, out_dtype == TQ_F32, 0};
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_heads)), dim3(64), 0,
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((num_seqs * num_heads + kMergeRows - 1) / kMergeRows)),
+                     dim3(64 * kMergeRows), 0,
                      reinterpret_cast<hipStream_t>(stream), mp);
   return launch_status("tq_split_merge launch");
 }
@@ -1421,6 +1461,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   st = launch_status("tq_decode_paged launch");
   if (st != TQ_OK || num_splits == 1) return st;
   MergeParams mp = {p.part_o, p.part_lse, out, lse, num_seqs, num_q_heads, num_splits, D, p.out_f32, 1};
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(num_seqs * num_q_heads)), dim3(64), 0, hs, mp);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((num_seqs * num_q_heads + kMergeRows - 1) / kMergeRows)),
+                     dim3(64 * kMergeRows), 0, hs, mp);
   return launch_status("tq_decode_paged merge launch");
 }
