@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 SPLITS = {2: 16, 4: 16, 5: 64, 1: 1}
-LAYERS = {2: 3, 4: 2, 5: 3, 1: 2}
+LAYERS = {2: 3, 4: 2, 5: 1, 1: 1}
+FLUSH_BYTES = 1 << 30
 NAMES = {"8b": 2, "70b": 4, "long": 5, "tiny": 1}
 
 
@@ -144,6 +145,27 @@ class Bench:
         self.write(layer)
         self.decode(layer)
 
+    def timed_cold(self, launches, warmup, flush):
+        """Decode call durations (ms, sorted) with cold caches: before each
+        timed call a flush reads `flush` (1 GiB, evicting L2 and the 256 MB
+        Infinity Cache with clean lines, so that the timed call does not pay
+        for writing back someone else's dirty data), then a GPU-side spin
+        keeps the host's enqueue time out of the interval the HIP events
+        bracket."""
+        torch = self.torch
+        for i in range(warmup):
+            self.decode(i % self.L)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for i in range(launches):
+            layer = i % self.L
+            flush_caches(flush)
+            torch.cuda._sleep(200000)
+            ev[i][0].record()
+            self.decode(layer)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
+
     def timed(self, steps, warmup):
         torch = self.torch
         for i in range(warmup):
@@ -168,6 +190,50 @@ class Bench:
         torch.cuda.synchronize()
         dec_ms = sorted(a.elapsed_time(b) for a, b in ev)
         return wall / steps * 1e3, dec_ms
+
+
+def flush_caches(flush):
+    """Read every byte of `flush` (int64 view; one small result)."""
+    flush.view(__import__("torch").int64).max()
+
+
+def write_cold(launches, warmup, flush):
+    """Quantise-on-write of the write workload (16 sequences x 2048 new
+    tokens, 8 kv heads, d = 128, K4/V4, Student-t(5) bf16 input) into a shared
+    pool, each timed launch after a cache flush."""
+    import numpy as np
+    import torch
+    import quantized_paged_kv_amd as tq
+    import workloads as wl
+    w = wl.write_workload(0)
+    kf = tq.Format(w.head_dim, w.kfmt.group_bits, w.kfmt.signs, w.kfmt.group_channels)
+    vf = tq.Format(w.head_dim, w.vfmt.group_bits, w.vfmt.signs, w.vfmt.group_channels)
+    kp, vp = tq.alloc_pages(w.num_blocks, w.num_kv_heads, kf), tq.alloc_pages(w.num_blocks, w.num_kv_heads, vf)
+    dev = lambda x: torch.from_numpy(wl.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+    xk, xv = dev(wl.write_values(w, "k")), dev(wl.write_values(w, "v"))
+    slots = torch.from_numpy(w.slot_mapping).cuda()
+    for _ in range(warmup):
+        tq.write_kv(xk, xv, slots, kp, vp, kf, vf)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for i in range(launches):
+        flush_caches(flush)
+        torch.cuda._sleep(200000)
+        ev[i][0].record()
+        tq.write_kv(xk, xv, slots, kp, vp, kf, vf)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    rows = w.num_tokens * w.num_kv_heads
+    krow = kf.tile_bytes()[0] + 2 * kf.num_groups
+    vrow = vf.tile_bytes()[0] + 2 * vf.num_groups
+    nbytes = rows * (2 * w.head_dim * 2 + krow + vrow) + w.num_tokens * 8
+    return w, ms, nbytes
+
+
+def stats_us(ms):
+    n = len(ms)
+    return {"avg": round(sum(ms) / n * 1e3, 2), "p10": round(ms[n // 10] * 1e3, 2),
+            "p50": round(ms[n // 2] * 1e3, 2), "p90": round(ms[9 * n // 10] * 1e3, 2)}
 
 
 def cpu_baseline(index, budget_s=12.0):
@@ -252,9 +318,11 @@ def main():
         sys.exit(2)
     import torch
     index = NAMES[args.workload]
+    flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     b = Bench(index, splits=args.splits)
-    ms_step, dec_ms = b.timed(args.steps, args.warmup)
+    ms_step, dec_warm = b.timed(args.steps, args.warmup)
     log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step")
+    dec_ms = b.timed_cold(args.steps, args.warmup, flush)
     w = b.w
     step_bytes = b.decode_bytes + b.write_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -273,27 +341,50 @@ def main():
                    "layers_cycled": b.L, "step": "tq_write_kv(current token) + tq_decode_paged",
                    "parallelism": "single GPU"},
         "us_per_layer_step": round(ms_step * 1e3, 2),
-        "decode_us": {"avg": round(dec_avg * 1e3, 2), "p10": round(dec_ms[len(dec_ms) // 10] * 1e3, 2),
-                      "p50": round(dec_ms[len(dec_ms) // 2] * 1e3, 2), "p90": round(dec_ms[9 * len(dec_ms) // 10] * 1e3, 2)},
+        "decode_us": stats_us(dec_ms),
+        "decode_us_layers_cycled": stats_us(dec_warm),
+        "decode_GBs_median": round(b.decode_bytes / (dec_ms[len(dec_ms) // 2] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "tq_decode_paged (decode kernel + split merge)",
-                     "algorithmic_bytes_per_launch": b.decode_bytes},
+                     "algorithmic_bytes_per_launch": b.decode_bytes,
+                     "timing": "cold caches (1 GiB read before each launch)"},
     }
     del b
     torch.cuda.empty_cache()
     if not args.no_secondary and index == 2:
         b4 = Bench(4)
-        ms4, d4 = b4.timed(max(10, args.steps // 2), args.warmup)
+        n4 = max(10, args.steps // 2)
+        ms4, d4w = b4.timed(n4, args.warmup)
         log(f"secondary timed: {ms4 * 1e3:.1f} us/step")
+        d4 = b4.timed_cold(n4, args.warmup, flush)
         a4 = sum(d4) / len(d4)
         result["secondary"] = {"workload": b4.w.name, "us_per_layer_step": round(ms4 * 1e3, 2),
+                               "decode_us": stats_us(d4), "decode_us_layers_cycled": stats_us(d4w),
                                "decode_us_avg": round(a4 * 1e3, 2),
                                "decode_GBs": round(b4.decode_bytes / (a4 * 1e-3) / 1e9, 1),
                                "frac_of_peak": round(b4.decode_bytes / (a4 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                "num_splits": b4.P, "traffic": stored_traffic("70b")}
         del b4
         torch.cuda.empty_cache()
+        # the other workloads: the write path and the tiny / long-context decodes
+        ww, wms, wbytes = write_cold(args.steps, args.warmup, flush)
+        wavg = sum(wms) / len(wms)
+        result["write"] = {"workload": ww.name, "us": stats_us(wms), "algorithmic_bytes": wbytes,
+                           "GBs": round(wbytes / (wavg * 1e-3) / 1e9, 1),
+                           "frac_of_peak": round(wbytes / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"write: {wavg * 1e3:.1f} us")
+        torch.cuda.empty_cache()
+        for idx, key in ((5, "long"), (1, "tiny")):
+            bx = Bench(idx)
+            dx = bx.timed_cold(max(10, args.steps // 2), args.warmup, flush)
+            ax = sum(dx) / len(dx)
+            result[key] = {"workload": bx.w.name, "decode_us": stats_us(dx), "num_splits": bx.P,
+                           "algorithmic_bytes": bx.decode_bytes,
+                           "GBs": round(bx.decode_bytes / (ax * 1e-3) / 1e9, 1)}
+            log(f"{key}: {ax * 1e3:.1f} us")
+            del bx
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(index)

@@ -126,7 +126,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 
 __device__ __forceinline__ float row_ror8(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
 // x * (fp16 half HI of w) in one v_fma_mix (the f16 operand is read as is:
@@ -160,35 +160,6 @@ __device__ __forceinline__ float max_nn(float a, float b) {
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
-// max over the lanes l, l^16, l^32, l^48 (gfx950 row and half swaps)
-// Value of x in lane (lane ^ K), K a power of two below 64, without the
-// LDS crossbar: DPP quad permutes for K = 1, 2, the half-row mirror (lane
-// i <-> 7 - i) followed by the quad reversal (i <-> 3 - i) for K = 4, the
-// 8-lane row rotation for K = 8, and the gfx950 row-swap permutes for K =
-// 16, 32 (after swapping a value with itself, the partner's copy is the
-// first result in the upper row of each pair and the second in the lower).
-template <int K>
-__device__ __forceinline__ float lane_xor(float x, int lane) {
-  const int xi = __float_as_int(x);
-  if constexpr (K == 1) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  } else if constexpr (K == 2) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  } else if constexpr (K == 4) {
-    const int m = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xF, 0xF, false);           // row_half_mirror
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false));    // quad_perm 3,2,1,0
-  } else if constexpr (K == 8) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x128, 0xF, 0xF, false));  // row_ror 8
-  } else if constexpr (K == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 16) ? r[0] : r[1]);
-  } else {
-    static_assert(K == 32, "lane_xor: K must be a power of two below 64");
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float((lane & 32) ? r[0] : r[1]);
-  }
-}
-
 // One radix-2 stage of an unnormalised Walsh-Hadamard transform across
 // lanes: the lane with bit K clear keeps the sum, the other the difference.
 template <int K, int N>
@@ -201,6 +172,7 @@ __device__ __forceinline__ void wht_lanes(float (&x)[N], int lane) {
   }
 }
 
+// max over the lanes l, l^16, l^32, l^48 (gfx950 row and half swaps)
 __device__ __forceinline__ float max_rows(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   const float y = max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -345,17 +317,17 @@ __device__ __forceinline__ int wave_sum(int v, int lane) {
 // next row, lane 31 to the upper half).
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   const int r = lane & 15;
-  int t = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  int t = __builtin_amdgcn_mov_dpp(x, 0x111, 0xF, 0xF, true);
   if (r >= 1) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  t = __builtin_amdgcn_mov_dpp(x, 0x112, 0xF, 0xF, true);
   if (r >= 2) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  t = __builtin_amdgcn_mov_dpp(x, 0x114, 0xF, 0xF, true);
   if (r >= 4) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  t = __builtin_amdgcn_mov_dpp(x, 0x118, 0xF, 0xF, true);
   if (r >= 8) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x142, 0xF, 0xF, false);   // row_bcast 15
+  t = __builtin_amdgcn_mov_dpp(x, 0x142, 0xF, 0xF, true);   // row_bcast 15
   if (lane & 16) x += t;
-  t = __builtin_amdgcn_update_dpp(0, x, 0x143, 0xF, 0xF, false);   // row_bcast 31
+  t = __builtin_amdgcn_mov_dpp(x, 0x143, 0xF, 0xF, true);   // row_bcast 31
   if (lane & 32) x += t;
   return x;
 }
@@ -1301,19 +1273,6 @@ int format_kind_v(const tq_format* f) {
 }
 
 // Compute units of the current device (cached per device).
-int device_cus() {
-  static std::mutex mu;
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  std::lock_guard<std::mutex> lk(mu);
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 }  // namespace
 }  // namespace tq

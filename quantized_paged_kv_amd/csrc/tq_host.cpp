@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "tq_internal.h"
@@ -89,6 +90,24 @@ void make_dev_format(const tq_format* f, DevFormat* o) {
     o->grp_byte_off[g] = off;
     off += o->m * f->group_bits[g] / 8;
     for (int i = 0; i < 16; ++i) o->cb[g][i] = f->codebook[g][i];
+    for (int i = 0; i + 1 < (1 << f->group_bits[g]); ++i)   // exact in fp64
+      o->thr[g][i] = (f16_bits_to_f64(f->codebook[g][i]) + f16_bits_to_f64(f->codebook[g][i + 1])) * 0.5;
+    const int nthr = (1 << f->group_bits[g]) - 1;
+    for (double off : {128.5, 128.25, 128.75, 128.375, 128.625, 128.125, 128.875}) {
+      bool ok = true;
+      double prev = -1.0;
+      for (int i = 0; i < nthr && ok; ++i) {
+        const double x = o->thr[g][i] * 32.0 + off;
+        const double b = floor(x), fr = x - b;
+        ok = x >= 1.0 && x < 255.0 && fr >= 0.02 && fr <= 0.98 && b > prev;
+        prev = b;
+      }
+      if (ok) {
+        o->lut_off[g] = (float)off;
+        o->fast[g] = 1;
+        break;
+      }
+    }
   }
   o->row_bytes = row_index_bytes(f);
   o->tile_bytes = tile_bytes_of(f);
@@ -147,6 +166,21 @@ static long double shoot(long double y1, int half, long double* levels) {
   }
   levels[half - 1] = y;
   return y - cell_mean(a, INFINITY);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 }  // namespace tq

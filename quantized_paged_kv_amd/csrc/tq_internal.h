@@ -29,9 +29,18 @@ struct DevFormat {
   int32_t tile_bytes;
   int32_t norm_off;        // byte offset of the norm plane in a tile
   int32_t chunk;           // V pages: bytes per lane run of the index plane (0: row-major)
+  double thr[2][15];       // decision thresholds: midpoints of adjacent fp16 levels (exact)
+  // Bucketed search for the level index (see the write kernel): bucket
+  // k = floor(32 z + lut_off) of the scaled value z holds at most one
+  // threshold, none within 2% of a bucket width of its edges, all inside
+  // buckets 1..254; fast[g] = 0 when no offset meets that (then every
+  // threshold is compared).
+  float lut_off[2];
+  int32_t fast[2];
 };
 
 void make_dev_format(const tq_format* f, DevFormat* out);
+int device_cus();
 
 // ------------------------------------------------------ host + device helpers
 
@@ -82,6 +91,45 @@ __host__ __device__ inline double f16_bits_to_f64(uint16_t h) {
     v = ldexp((double)(1024 + f), e - 25);
   }
   return (h & 0x8000u) ? -v : v;
+}
+
+// ------------------------------------------------------ device lane helpers
+
+// Value of x in lane (lane ^ K), K a power of two below 64, without the
+// LDS crossbar: DPP quad permutes for K = 1, 2, the half-row mirror (lane
+// i <-> 7 - i) followed by the quad reversal (i <-> 3 - i) for K = 4, the
+// 8-lane row rotation for K = 8, and the gfx950 row-swap permutes for K =
+// 16, 32 (after swapping a value with itself, the partner's copy is the
+// first result in the upper row of each pair and the second in the lower).
+template <int K>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+  const int xi = __float_as_int(x);
+  if constexpr (K == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+  } else if constexpr (K == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+  } else if constexpr (K == 4) {
+    const int m = __builtin_amdgcn_mov_dpp(xi, 0x141, 0xF, 0xF, true);           // row_half_mirror
+    return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true));    // quad_perm 3,2,1,0
+  } else if constexpr (K == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, true));  // row_ror 8
+  } else if constexpr (K == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(K == 32, "lane_xor: K must be a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// Double in lane (lane ^ K): the two 32-bit halves moved separately.
+template <int K>
+__device__ __forceinline__ double lane_xor_d(double x, int lane) {
+  const uint64_t u = __double_as_longlong(x);
+  const float lo = lane_xor<K>(__uint_as_float((uint32_t)u), lane);
+  const float hi = lane_xor<K>(__uint_as_float((uint32_t)(u >> 32)), lane);
+  return __longlong_as_double((long long)(((uint64_t)__float_as_uint(hi) << 32) | __float_as_uint(lo)));
 }
 
 }  // namespace tq

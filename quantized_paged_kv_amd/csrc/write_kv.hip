@@ -16,9 +16,13 @@
 //   fp16 rounded to nearest even directly from fp64.
 //
 // Thread layout: one row (token, kv head, tensor) per D/8 lanes, eight
-// channels per lane (lane L holds channels 8L..8L+7 after the load).  The
-// butterflies for h < 8 run inside a lane, the rest across lanes.
+// channels per lane (lane L holds channels 8L..8L+7 after the load); a
+// workgroup takes consecutive tokens of one kv head.  The butterflies for
+// h < 8 run inside a lane, the rest across lanes (DPP).
 #pragma clang fp contract(off)
+
+#include <algorithm>
+#include <type_traits>
 
 #include "tq_internal.h"
 
@@ -32,7 +36,8 @@ struct WriteParams {
   uint8_t* pages[2];
   DevFormat fmt[2];
   const int64_t* slots;
-  int64_t num_rows;     // T * H
+  int64_t num_tokens;   // T
+  int64_t num_units;    // ceil(T / rows per unit) * H
   int64_t num_slots;    // num_blocks * 16
   int32_t H;
   int32_t* dev_err;
@@ -48,19 +53,90 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
   constexpr int RPB = kThreads / LPR;     // rows per block
   __shared__ double lds_w[RPB][D];
   __shared__ uint32_t lds_row[RPB][D / 8 + 1];  // packed row (<= D/2 bytes)
+  __shared__ uint8_t lds_bkt[2][256];           // per bucket: thresholds below it | 0x80 if one inside
+  __shared__ double lds_thr[2][16];
+
+  __shared__ DevFormat sf;
 
   const int tensor = blockIdx.y;
-  const DevFormat& f = p.fmt[tensor];
+  // the tensor's format to LDS once: reads of the argument block indexed by
+  // the tensor would otherwise be vector loads inside the loop, which every
+  // wait on the prefetched rows would also wait for
+  {
+    static_assert(sizeof(DevFormat) % 4 == 0, "format copied in words");
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&p.fmt[tensor]);
+    for (int i = threadIdx.x; i < (int)(sizeof(DevFormat) / 4); i += kThreads)
+      reinterpret_cast<uint32_t*>(&sf)[i] = src[i];
+  }
+  __syncthreads();
+  const DevFormat& f = sf;
+  // bucket table of each group (bucket k spans z in [(k - off) / 32, (k + 1 - off) / 32))
+  for (int g = 0; g < f.ng; ++g) {
+    const int nthr = (1 << f.bits[g]) - 1;
+    if (threadIdx.x < 16) lds_thr[g][threadIdx.x] = threadIdx.x < nthr ? f.thr[g][threadIdx.x] : 0.0;
+    if (f.fast[g]) {
+      const int k = threadIdx.x;   // kThreads == 256 buckets
+      const double lo = ((double)k - (double)f.lut_off[g]) / 32.0, hi = lo + 1.0 / 32.0;
+      int below = 0, inside = 0;
+      for (int i = 0; i < nthr; ++i) {
+        below += f.thr[g][i] < lo ? 1 : 0;
+        inside |= (f.thr[g][i] >= lo && f.thr[g][i] < hi) ? 1 : 0;
+      }
+      lds_bkt[g][k] = (uint8_t)(below | (inside << 7));
+    }
+  }
+  __syncthreads();
   const int L = threadIdx.x % LPR;
   const int lr = threadIdx.x / LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + lr;
-  const bool in_range = row < p.num_rows;
-  const int64_t rr = in_range ? row : 0;
-  const int64_t token = rr / p.H;
-  const int head = (int)(rr % p.H);
-  const int64_t slot = p.slots[token];
+  // unit -> RPB consecutive tokens of one kv head: with the usual slot
+  // mappings those rows fill whole tiles, so their partial-line writes meet
+  // in one L2 and leave it as whole lines.  Workgroups loop over units so
+  // that the set-up above is paid once per workgroup.
+  // The loads of the next unit (its rows and slots) are issued before the
+  // current unit is computed.
+  struct Fetch {
+    uint4 a, b;      // the lane's 8 channels (bf16: a only)
+    int64_t slot;
+  };
+  // unit = blockIdx.x + i gridDim.x = tg H + head, stepped without dividing
+  const uint32_t H = (uint32_t)p.H;
+  const uint32_t step_tg = gridDim.x / H, step_h = gridDim.x % H;
+  auto fetch = [&](int64_t unit, int64_t tg, int head) -> Fetch {
+    Fetch x;
+    const int64_t tok = tg * RPB + lr;
+    const int64_t token = (unit < p.num_units && tok < p.num_tokens) ? tok : 0;
+    const int64_t rr = token * p.H + head;
+    if (F32) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(p.src[tensor]) + rr * D + 8 * L);
+      x.a = src[0];
+      x.b = src[1];
+    } else {
+      x.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.src[tensor]) + rr * D + 8 * L);
+      x.b = uint4{0u, 0u, 0u, 0u};
+    }
+    x.slot = p.slots[token];
+    return x;
+  };
+  int64_t tg = blockIdx.x / H;
+  int head = (int)(blockIdx.x % H);
+  Fetch nxt = fetch(blockIdx.x, tg, head);
+  for (int64_t unit = blockIdx.x; unit < p.num_units; unit += gridDim.x) {
+  const Fetch cur = nxt;
+  const int64_t cur_tg = tg;
+  const int cur_head = head;
+  tg += step_tg;
+  head += (int)step_h;
+  if (head >= (int)H) {
+    head -= (int)H;
+    ++tg;
+  }
+  nxt = fetch(unit + gridDim.x, tg, head);
+  const int64_t tok = cur_tg * RPB + lr;
+  const bool in_range = tok < p.num_tokens;
+  const int64_t token = in_range ? tok : 0;
+  const int64_t slot = cur.slot;
   const bool slot_ok = slot >= 0 && slot < p.num_slots;
-  if (in_range && !slot_ok && head == 0 && L == 0 && tensor == 0) {
+  if (in_range && !slot_ok && cur_head == 0 && L == 0 && tensor == 0) {
     record_error(p.dev_err, TQ_ERR_INDEX, (int32_t)token);
   }
   const bool valid = in_range && slot_ok;
@@ -68,12 +144,11 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
   // ---- load eight channels and apply the signs (exact)
   double v[8];
   if (F32) {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.src[tensor]) + rr * D + 8 * L);
-    const float4 a = src[0], b = src[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const uint4 a = cur.a, b = cur.b;
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
   } else {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.src[tensor]) + rr * D + 8 * L);
+    const uint4 raw = cur.a;
     const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -100,16 +175,21 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
       }
     }
   }
-  // ---- h = 8, 16, ... across lanes: partner lane L ^ (h / 8)
+  // ---- h = 8, 16, ... across lanes: partner lane L ^ (h / 8), moved by DPP
+  // within the row's 8 or 16 lanes (the lower lane keeps a + b, the upper
+  // a - b, a being the lower lane's value)
+  // (one fma with a factor of +-1 is the add or the subtraction itself:
+  // the product is exact and the sum is rounded once)
+  auto across = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    const double sgn = (L & k) ? -1.0 : 1.0;
 #pragma unroll
-  for (int k = 1; k < LPR; k *= 2) {
-    const bool upper = (L & k) != 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double o = __shfl_xor(v[e], k);
-      v[e] = upper ? (o - v[e]) : (v[e] + o);
-    }
-  }
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_fma(sgn, v[e], lane_xor_d<k>(v[e], L));
+  };
+  across(std::integral_constant<int, 1>{});
+  across(std::integral_constant<int, 2>{});
+  across(std::integral_constant<int, 4>{});
+  if constexpr (LPR == 16) across(std::integral_constant<int, 8>{});
 
   // ---- gather each group's channels in listed order: lane L takes listed
   // positions [E*L, E*L+E) of each group (E = 8 for one group, 4 for two).
@@ -144,10 +224,15 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
     ss[0] = s03;
     ss[1] = s47;
   }
-#pragma unroll
-  for (int k = 1; k < LPR; k *= 2) {
-    ss[0] = ss[0] + __shfl_xor(ss[0], k);
-    ss[1] = ss[1] + __shfl_xor(ss[1], k);
+  ss[0] = ss[0] + lane_xor_d<1>(ss[0], L);
+  ss[1] = ss[1] + lane_xor_d<1>(ss[1], L);
+  ss[0] = ss[0] + lane_xor_d<2>(ss[0], L);
+  ss[1] = ss[1] + lane_xor_d<2>(ss[1], L);
+  ss[0] = ss[0] + lane_xor_d<4>(ss[0], L);
+  ss[1] = ss[1] + lane_xor_d<4>(ss[1], L);
+  if constexpr (LPR == 16) {
+    ss[0] = ss[0] + lane_xor_d<8>(ss[0], L);
+    ss[1] = ss[1] + lane_xor_d<8>(ss[1], L);
   }
 
   // ---- norms, thresholds, indices and the packed bit fields
@@ -168,13 +253,44 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
       norm16[g] = f64_to_f16_rne(__builtin_sqrt(s / (double)D));
       const double r = __builtin_sqrt(s / (double)m);
       uint32_t idx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int i = 0; i < levels - 1; ++i) {
-        const double t = (f16_bits_to_f64(f.cb[g][i]) + f16_bits_to_f64(f.cb[g][i + 1])) * 0.5;
-        const double T = t * r;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) idx[e] += (T < wg[e]) ? 1u : 0u;
-      }
+      // idx = number of scaled thresholds T_i = thr_i * r below the value.
+      // Fast path: the bucket of z = w / r (float estimate) gives the count
+      // of thresholds in lower buckets, exact because no threshold lies
+      // within the estimate's error of a bucket edge; the one threshold a
+      // bucket may hold is compared exactly.  Otherwise every threshold is
+      // compared (the level count made a compile-time constant so that the
+      // comparisons unroll).
       const int base = (ng == 1) ? 0 : 4 * g;
+      // (the float estimate needs r inside the normal float range; |z| <= sqrt(m))
+      if (f.fast[g] && r > 1e-30 && r < 1e30) {
+        const float rinv = __builtin_amdgcn_rcpf((float)r);
+        const float off = f.lut_off[g];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (e < base || e >= base + E) continue;
+          const float z = (float)wg[e] * rinv;
+          int k = __float2int_rd(__builtin_fmaf(z, 32.0f, off));
+          k = k < 0 ? 0 : (k > 255 ? 255 : k);
+          const uint32_t ent = lds_bkt[g][k];
+          const uint32_t below = ent & 0x7Fu;
+          const double T = lds_thr[g][below] * r;
+          idx[e] = below + (((ent & 0x80u) && T < wg[e]) ? 1u : 0u);
+        }
+      } else {
+        auto count_below = [&](auto lv) {
+          constexpr int LV = decltype(lv)::value;
+          double T[LV - 1];
+#pragma unroll
+          for (int i = 0; i < LV - 1; ++i) T[i] = f.thr[g][i] * r;
+#pragma unroll
+          for (int i = 0; i < LV - 1; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) idx[e] += (T[i] < wg[e]) ? 1u : 0u;
+        };
+        if (levels == 16) count_below(std::integral_constant<int, 16>{});
+        else if (levels == 8) count_below(std::integral_constant<int, 8>{});
+        else count_below(std::integral_constant<int, 4>{});
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (e < E) fld |= idx[base + e] << (bits * e);
@@ -182,7 +298,35 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
     field[g] = fld;
   }
 
-  // ---- assemble the row in LDS, then store it with dword writes
+  const int64_t blk = slot >> 4;
+  const int offs = (int)(slot & 15);
+  uint8_t* tile = p.pages[tensor] + ((int64_t)blk * p.H + cur_head) * f.tile_bytes;
+  if (ng == 1) {
+    // one group: lane L's eight indices are the row's bytes [bits L, bits
+    // (L + 1)) -- a dword (4-bit), a half-word (2-bit) or three bytes -- and
+    // go straight to their place in the index plane (row-major, or run
+    // 16 (offs % 4) + byte / c, place offs / 4 of the lane-major plane)
+    const int bits = f.bits[0];
+    const uint32_t fld = field[0];
+    const int b0 = bits * L;   // first row byte of this lane
+    const int c = f.chunk;
+    auto at = [&](int byte) -> uint8_t* {
+      if (c == 0) return tile + offs * f.row_bytes + byte;
+      return tile + ((16 * (offs & 3) + byte / c) * 4 + (offs >> 2)) * c + byte % c;
+    };
+    if (!valid) {
+    } else if (bits == 4 && (c == 0 || c % 4 == 0)) {
+      *reinterpret_cast<uint32_t*>(at(b0)) = fld;
+    } else if (bits == 2 && (c == 0 || c % 2 == 0)) {
+      *reinterpret_cast<uint16_t*>(at(b0)) = (uint16_t)fld;
+    } else if (bits == 4 && c == 2) {
+      *reinterpret_cast<uint16_t*>(at(b0)) = (uint16_t)fld;
+      *reinterpret_cast<uint16_t*>(at(b0 + 2)) = (uint16_t)(fld >> 16);
+    } else {
+      for (int j = 0; j < bits; ++j) *at(b0 + j) = (uint8_t)(fld >> (8 * j));
+    }
+  } else {
+  // ---- two groups: assemble the row in LDS, then store it with dword writes
   constexpr int WORDS = D / 8 + 1;
   for (int w = L; w < WORDS; w += LPR) lds_row[lr][w] = 0u;
   __syncthreads();
@@ -196,11 +340,8 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
     if (sh + nbits > 32) atomicOr(&lds_row[lr][word + 1], val >> (32 - sh));
   }
   __syncthreads();
-  if (!valid) return;
-  const int64_t blk = slot >> 4;
-  const int offs = (int)(slot & 15);
-  uint8_t* tile = p.pages[tensor] + ((int64_t)blk * p.H + head) * f.tile_bytes;
-  if (f.chunk == 0) {   // row-major index plane
+  if (!valid) {
+  } else if (f.chunk == 0) {   // row-major index plane
     uint32_t* dst = reinterpret_cast<uint32_t*>(tile + offs * f.row_bytes);
     for (int w = L; w < f.row_bytes / 4; w += LPR) dst[w] = lds_row[lr][w];
   } else {              // lane-major: chunk j of the row goes to run 16*(offs%4)+j, place offs/4
@@ -218,10 +359,12 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
       }
     }
   }
-  if (L == 0) {
+  }
+  if (valid && L == 0) {
     const int nslot = 4 * (offs & 3) + (offs >> 2);
     uint16_t* np = reinterpret_cast<uint16_t*>(tile + f.norm_off);
     for (int g = 0; g < ng; ++g) np[16 * g + nslot] = norm16[g];
+  }
   }
 }
 
@@ -266,12 +409,14 @@ extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype
   if (num_tokens == 0) return TQ_OK;
   if (num_tokens * (int64_t)num_kv_heads >= (int64_t)1 << 40) return set_error(TQ_ERR_VALUE, "too many rows");
   p.slots = slot_mapping;
-  p.num_rows = num_tokens * num_kv_heads;
+  p.num_tokens = num_tokens;
   p.num_slots = num_blocks * TQ_BLOCK_SIZE;
   p.H = num_kv_heads;
   p.dev_err = dev_err;
   const int rpb = kThreads / (d / 8);
-  dim3 grid((unsigned)((p.num_rows + rpb - 1) / rpb), (unsigned)n_tensors);
+  p.num_units = (num_tokens + rpb - 1) / rpb * num_kv_heads;
+  const int64_t wgs = std::min<int64_t>(p.num_units, (int64_t)device_cus() * 8);
+  dim3 grid((unsigned)wgs, (unsigned)n_tensors);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool f32 = in_dtype == TQ_F32;
   if (d == 128) {

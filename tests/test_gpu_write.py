@@ -122,6 +122,36 @@ def test_exact_threshold_ties_and_zero_rows():
     _assert_pool_equal(kp.cpu().numpy(), ref, "ties")
 
 
+@pytest.mark.parametrize("cb_vals", [[-1.5, -0.5, 0.5, 1.5], [-0.01, 0.0, 0.01, 1.0]],
+                         ids=["bucketed-search", "thresholds-too-close-for-buckets"])
+def test_level_search_extreme_scales(cb_vals):
+    """The level index is found by a bucketed search when the codebook allows
+    it and the row scale is inside the float range, else by comparing every
+    threshold; both give the oracle's bytes, also for rows scaled by 1e36 and
+    1e-36 (outside the bucketed search's range) and near thresholds."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    d, H = 128, 2
+    s = wl.signs(7, 1, d)
+    cb = np.array(cb_vals, dtype=np.float16)
+    rng = np.random.default_rng(11)
+    base = rng.standard_normal((96, H, d)).astype(np.float32)
+    scales = np.array([1.0, 1e36, 1e-36, 3.0, 2.0 ** -60, 2.0 ** 60] * 16, dtype=np.float32)[:, None, None]
+    x = wl.bf16_round(base * scales)
+    T = x.shape[0]
+    nb = (T + 15) // 16 + 1
+    slots = np.arange(T, dtype=np.int64) + 16
+    of = oenc.Format(d, [2], np.arange(d), [cb], s)
+    of.validate()
+    _, _, tile = opg.tile_layout(of, 16)
+    ref = np.full((nb, H, tile), 0xA5, dtype=np.uint8)
+    opg.write_pages(x, slots, ref, of, 16)
+    pf = tq.Format(d, [2], s, None, [cb.view(np.uint16)])
+    kp = torch.full((nb, H, tile), 0xA5, dtype=torch.uint8, device="cuda")
+    tq.write_kv(to_device(x, "bf16"), None, torch.from_numpy(slots).cuda(), kp, None, pf, pf, check=True)
+    _assert_pool_equal(kp.cpu().numpy(), ref, "extreme scales")
+
+
 def test_out_of_range_slot_reports_index_error_and_skips_row():
     import torch
     import quantized_paged_kv_amd as tq
