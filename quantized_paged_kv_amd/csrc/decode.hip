@@ -524,14 +524,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
   __syncthreads();   // plan, lengths and s_par written
 
+  // ---- the plan (uniform values)
+  const int R = uni(s_plan[0]);
+  const int r0 = uni(s_plan[1]), r1 = uni(s_plan[2]);
+
+  // sequences with no cached token: out = 0, lse = -inf (first workgroup;
+  // lengths of sequences past the first 64 are reported here)
+  if (blockIdx.x == 0) {
+    const int cap = p.max_blocks * 16;
+    for (int s = wave; s < p.S; s += kWaves) {
+      int c;
+      if (s < 64) {
+        c = uni(s_cl[s]);
+      } else {
+        c = p.context_lens[s];
+        if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
+        c = clamp_ctx(c, cap);
+      }
+      if (c == 0) {
+        for (int idx = lane; idx < p.Hq * D; idx += 64) {
+          const int64_t off = (int64_t)s * p.Hq * D + idx;
+          if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
+          else static_cast<uint16_t*>(p.out)[off] = 0;
+        }
+        if (p.lse)
+          for (int h = lane; h < p.Hq; h += 64) p.lse[(int64_t)s * p.Hq + h] = -INFINITY;
+        if (p.P > 1)   // tell the merge that these rows are final
+          for (int h = lane; h < p.Hq; h += 64) p.part_lse[((int64_t)s * p.Hq + h) * p.P] = __uint_as_float(kDoneBits);
+      }
+    }
+  }
+  if (r0 >= r1) return;  // uniform across the workgroup
+
   auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
-  // LDS tables: byte-indexed, two halves of 128 B per entry, built once.
+  // LDS tables: byte-indexed, two halves of 128 B per entry, built once
+  // (while the first piece's block-table, q and tile loads are in flight).
   // Thread -> 16 B chunk (16 e + lane & 15) of entry e = 16 e_hi + e_lo:
   // lane & 15 walks the 256 B of an entry (8 chunks per half), so each
   // store instruction writes 1 KB contiguous; e_lo is fixed per lane,
   // e_hi = (wave >> 2) + 4 it.
-  {
+  auto build_tables = [&]() {
     const int h = (lane >> 3) & 1;
     const int e_lo = (lane >> 4) | ((wave & 3) << 2);
     const int wh = wave >> 2;
@@ -566,39 +599,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
       }
     }
-  }
-
-  // ---- the plan (uniform values)
-  const int R = uni(s_plan[0]);
-  const int r0 = uni(s_plan[1]), r1 = uni(s_plan[2]);
-
-  // sequences with no cached token: out = 0, lse = -inf (first workgroup;
-  // lengths of sequences past the first 64 are reported here)
-  if (blockIdx.x == 0) {
-    const int cap = p.max_blocks * 16;
-    for (int s = wave; s < p.S; s += kWaves) {
-      int c;
-      if (s < 64) {
-        c = uni(s_cl[s]);
-      } else {
-        c = p.context_lens[s];
-        if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
-        c = clamp_ctx(c, cap);
-      }
-      if (c == 0) {
-        for (int idx = lane; idx < p.Hq * D; idx += 64) {
-          const int64_t off = (int64_t)s * p.Hq * D + idx;
-          if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
-          else static_cast<uint16_t*>(p.out)[off] = 0;
-        }
-        if (p.lse)
-          for (int h = lane; h < p.Hq; h += 64) p.lse[(int64_t)s * p.Hq + h] = -INFINITY;
-        if (p.P > 1)   // tell the merge that these rows are final
-          for (int h = lane; h < p.Hq; h += 64) p.part_lse[((int64_t)s * p.Hq + h) * p.P] = __uint_as_float(kDoneBits);
-      }
-    }
-  }
-  if (r0 >= r1) return;  // uniform across the workgroup
+  };
 
   // ---- per-lane roles
   const int j = lane & 15;          // MFMA column: q head j & 7, high (j < 8) or low part
@@ -633,6 +634,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   int s = uni(s_plan[3]), grp = uni(s_plan[4]), off = uni(s_plan[5]), nb_s = uni(s_plan[6]);
   int pos = r0;
   bool first = true;
+  bool tables_built = false;
   while (pos < r1) {
     const int vb0 = pos - off + p.seg_cost;   // position of the segment's block 0
     const int b0 = off > p.seg_cost ? off - p.seg_cost : 0;
@@ -696,6 +698,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       int idx_c = part, idx_1 = part + NPW, idx_2 = part + 2 * NPW;
       const int v0 = bt_load(idx_c);
       const int v1 = bt_load(idx_1);
+      if (!tables_built) {   // while the loads above are in flight
+        build_tables();
+        tables_built = true;
+      }
 
       // -------- block-table entry -> scalar byte offsets of the block's tiles
       // in the pools (whose bytes, less than 4 GiB each, one descriptor per
@@ -780,7 +786,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             const int c = l8 * PER + 4 * i;
             *reinterpret_cast<float4*>(qrow + at(c)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
           }
-          // (same wave: its LDS writes are visible to its later reads)
+          // the lanes of a row exchange values through LDS: a wave-scope
+          // fence orders the writes above before the reads below
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
           float y[8 * PH];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
@@ -819,7 +827,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           if (amax > 0.f) frexpf(amax, &ex);
           if (l8 == 0) s_qexp[8 * hl + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
         }
-        // (same wave: its LDS writes above are visible to its reads below)
+        // (the fence orders this wave's exponent and row writes before its reads)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         const float q_pow = ldexpf(1.0f, s_qexp[8 * hl + gq]);
         const float* qrow = qf + gq * C::QS;
 #pragma unroll
@@ -1091,10 +1100,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             }
         }
         // the row of part 0 is read only by this pair's lanes, each lane
-        // rewrites the dims it read (same wave: later reads see the writes)
+        // rewrites the dims it read; the fence below orders those writes
+        // before the reads of the other lanes' dims
         float* row = slots + (8 * wave_of_part(h2, 0, HG) + g) * C::DS;
 #pragma unroll
         for (int k = 0; k < ND; ++k) row[m + 16 * k] = y[k];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // other lanes' values below
 #pragma unroll
         for (int k = 0; k < ND; k += 4) {
           const float4 f = *reinterpret_cast<const float4*>(row + ND * m + k);
