@@ -230,6 +230,54 @@ def write_cold(launches, warmup, flush):
     return w, ms, nbytes
 
 
+def window_cold(b, launches, warmup, flush, cap=132):
+    """Dense window next to the packed history (the 8B-shaped cache of `b`):
+    every sequence keeps cap = 4 boundary + 128 recent tokens in bf16, attended
+    by tq_decode_dense and merged with the history's float32 (o, lse).  Times,
+    with cold caches, the window call alone and the whole window-augmented
+    decode (tq_decode_paged with float32 output, then tq_decode_dense)."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    tq, w = b.tq, b.w
+    B, Hq, Hkv, d = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    kw = b._dev(wl.window_values(w.seed, B, cap, Hkv, d, "k"), "bf16")
+    vw = b._dev(wl.window_values(w.seed, B, cap, Hkv, d, "v"), "bf16")
+    lens = torch.full((B,), cap, dtype=torch.int32, device="cuda")
+    ho = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    hl = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    kp, vp = b.pools[0]
+
+    def history():
+        tq.decode_paged(b.q, kp, vp, b.bt, b.cl, b.kf, b.vf, w.scale, num_splits=b.P, out=ho, lse=hl,
+                        workspace=b.ws)
+
+    def window():
+        tq.decode_dense(b.q, kw, vw, lens, w.scale, hist_out=ho, hist_lse=hl, out=out, lse=lse)
+
+    res = {}
+    for key, fns in (("window_us", (window,)), ("decode_plus_window_us", (history, window))):
+        history()
+        for _ in range(warmup):
+            for f in fns:
+                f()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for i in range(launches):
+            flush_caches(flush)
+            torch.cuda._sleep(200000)
+            ev[i][0].record()
+            for f in fns:
+                f()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        res[key] = sorted(a.elapsed_time(c) for a, c in ev)
+    win_bytes = 2 * B * cap * Hkv * d * 2                       # window K and V rows (bf16)
+    io_bytes = B * Hq * d * 2 + B * Hq * (d + 1) * 4 + B * Hq * d * 2 + B * Hq * 4 + B * 4   # q, history, out, lse, lens
+    return res, win_bytes + io_bytes, cap
+
+
 def stats_us(ms):
     n = len(ms)
     return {"avg": round(sum(ms) / n * 1e3, 2), "p10": round(ms[n // 10] * 1e3, 2),
@@ -350,6 +398,19 @@ def main():
                      "algorithmic_bytes_per_launch": b.decode_bytes,
                      "timing": "cold caches (1 GiB read before each launch)"},
     }
+    if not args.no_secondary and index == 2:
+        wres, wbytes_win, cap = window_cold(b, max(10, args.steps // 2), args.warmup, flush)
+        wavg = sum(wres["window_us"]) / len(wres["window_us"])
+        result["window"] = {
+            "workload": f"{w.name} + dense window of {cap} bf16 tokens per sequence (4 boundary + 128 recent)",
+            "window_us": stats_us(wres["window_us"]),
+            "decode_plus_window_us": stats_us(wres["decode_plus_window_us"]),
+            "window_algorithmic_bytes": wbytes_win,
+            "roofline": {"bound": "hbm", "achieved": round(wbytes_win / (wavg * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(wbytes_win / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "kernel": "tq_decode_dense (window attention + merge with the history)"}}
+        log(f"window: {wavg * 1e3:.1f} us")
     del b
     torch.cuda.empty_cache()
     if not args.no_secondary and index == 2:

@@ -256,6 +256,49 @@ tq_status tq_split_merge(const float* part_out, const float* part_lse, int32_t n
                          int32_t num_heads, int32_t num_splits, int32_t head_dim, void* out,
                          tq_dtype out_dtype, float* lse, tq_stream_t stream);
 
+/*
+ * Exact attention over a dense window of cached tokens, optionally merged
+ * with the packed history's result ([D "Format Strategy"]: a recent dense
+ * window and boundary-token preservation are among the first serving
+ * policies; [D "Data Ownership"]: the compressed cache owns its recent
+ * windows next to the compressed blocks).  Reading: the window holds a
+ * sequence's boundary (first) tokens and its most recent tokens unquantised;
+ * they are attended exactly in the original domain and combined with the
+ * packed history by the split merge's log-sum-exp identity.  The tokens of
+ * a window may sit in any order (attention over a set of tokens does not
+ * depend on their order) and must not also be in the pages.
+ *
+ *   q          device [num_seqs][num_q_heads][head_dim], q_dtype BF16/F32
+ *              (the same q as tq_decode_paged).
+ *   k, v       device [num_seqs][capacity][num_kv_heads][head_dim], kv_dtype
+ *              BF16/F32, 16-byte aligned; token t of sequence s at row
+ *              (s * capacity + t); may be NULL when capacity == 0.
+ *   lens       device int32 [num_seqs]: tokens held for each sequence, at
+ *              rows 0 .. lens[s]-1; a length outside [0, capacity] records
+ *              (TQ_ERR_INDEX, -1 - s) in dev_err and is clamped.
+ *   scale      softmax scale applied to q.k (finite, > 0).
+ *   hist_out   device float [num_seqs][num_q_heads][head_dim] and
+ *   hist_lse   device float [num_seqs][num_q_heads], both or neither: the
+ *              history's normalised output and natural-log lse (for example
+ *              tq_decode_paged with out_dtype F32 and lse).  A -inf hist_lse
+ *              marks an empty history, whose hist_out row is not read.
+ *              NULL: the result is the window's attention alone.
+ *   out        device [num_seqs][num_q_heads][head_dim], out_dtype BF16/F32,
+ *              8-byte aligned; may be hist_out itself (F32), and lse may be
+ *              hist_lse: every row is read before it is written.
+ *   lse        device float [num_seqs][num_q_heads] or NULL.
+ * History and window both empty: out = 0, lse = -inf.
+ * Served shapes (else UNSUPPORTED_FORMAT): head_dim 64 or 128, num_q_heads /
+ * num_kv_heads in 1..16.  One workgroup per (sequence, kv head); the window
+ * is walked in chunks of 256 tokens, so capacity has no upper limit other
+ * than memory.
+ */
+tq_status tq_decode_dense(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, const void* k, const void* v,
+                          tq_dtype kv_dtype, int32_t capacity, const int32_t* lens, float scale,
+                          const float* hist_out, const float* hist_lse, void* out,
+                          tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

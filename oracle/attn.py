@@ -18,6 +18,12 @@ is the log-sum-exp identity
 
 [D "Serving Route Design"]: the workspace of the split is bounded by the
 runtime shape (sequences x heads x splits x d), never by context length.
+
+Dense window ([D "Format Strategy"]: a recent dense window and boundary-token
+preservation; [D "Data Ownership"]: the compressed cache owns its recent
+windows).  Reading: a sequence's cache is its packed history plus a small set
+of tokens kept unquantised (its first tokens and its most recent ones), and
+attention runs over the union, by the same plain definition.
 """
 from __future__ import annotations
 
@@ -92,6 +98,40 @@ def decode_reference(q: np.ndarray, k_pages, v_pages, block_tables, context_lens
             n = int(context_lens[s])
             K = reconstruct_sequence(k_pages, block_tables[s], n, kvh, kfmt, block_size)
             V = reconstruct_sequence(v_pages, block_tables[s], n, kvh, vfmt, block_size, role="v")
+            cache = {key: (K, V)}
+        K, V = cache[key]
+        out[s, h], lse[s, h] = attention(q[s, h], K, V, scale)
+    return out, lse
+
+
+def decode_window_reference(q: np.ndarray, k_win: np.ndarray, v_win: np.ndarray, win_lens, scale: float,
+                            k_pages=None, v_pages=None, block_tables=None, context_lens=None, kfmt=None,
+                            vfmt=None, block_size: int = 16, pairs=None):
+    """fp64 attention of q[B, H_q, d] over each sequence's dense window rows
+    k_win[s, :win_lens[s], kv_head] / v_win (exact values, any float dtype)
+    together with its decoded packed history (when pages are given), as one
+    set of tokens.  Returns (out[B, H_q, d], lse[B, H_q]); with `pairs` only
+    those (seq, q_head) entries are computed (others stay NaN)."""
+    B, Hq, d = q.shape
+    Hkv = k_win.shape[2]
+    G = Hq // Hkv
+    out = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    todo = pairs if pairs is not None else [(s, h) for s in range(B) for h in range(Hq)]
+    cache = {}
+    for s, h in todo:
+        kvh = h // G
+        key = (s, kvh)
+        if key not in cache:
+            n = int(win_lens[s])
+            K = np.asarray(k_win[s, :n, kvh], dtype=np.float64)
+            V = np.asarray(v_win[s, :n, kvh], dtype=np.float64)
+            if k_pages is not None:
+                c = int(context_lens[s])
+                Kh = reconstruct_sequence(k_pages, block_tables[s], c, kvh, kfmt, block_size)
+                Vh = reconstruct_sequence(v_pages, block_tables[s], c, kvh, vfmt, block_size, role="v")
+                K = np.concatenate([Kh, K]) if c else K
+                V = np.concatenate([Vh, V]) if c else V
             cache = {key: (K, V)}
         K, V = cache[key]
         out[s, h], lse[s, h] = attention(q[s, h], K, V, scale)

@@ -69,6 +69,7 @@ def _load(path: str = LIB_PATH):
         "tq_decode_paged": ([P, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, f32, i32, P, u64,
                              P, i32, P, P, P], i32),
         "tq_split_merge": ([P, P, i32, i32, i32, i32, P, i32, P, P], i32),
+        "tq_decode_dense": ([P, i32, i32, i32, i32, i32, P, P, i32, i32, P, f32, P, P, P, i32, P, P, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -307,6 +308,42 @@ def split_merge(part_out, part_lse, out=None, lse=None, out_dtype=None, stream=N
     return out, lse
 
 
+def decode_dense(q, k_win, v_win, lens, scale: float, hist_out=None, hist_lse=None, out=None, lse=None,
+                 out_dtype=None, dev_err=None, check: bool = False, stream=None):
+    """Exact attention of q [B, H_q, d] over a dense window k_win / v_win
+    [B, capacity, H_kv, d] (bf16 or float32) holding lens[s] tokens of
+    sequence s, merged by log-sum-exp with (hist_out [B, H_q, d] float32,
+    hist_lse [B, H_q]) when given.  out may be hist_out and lse hist_lse.
+    Returns (out, lse)."""
+    import torch
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be a contiguous [B, H_q, d] GPU tensor")
+    B, Hq, d = q.shape
+    _need(k_win.dim() == 4 and k_win.shape == v_win.shape and k_win.dtype == v_win.dtype
+          and k_win.is_contiguous() and v_win.is_contiguous() and k_win.shape[0] == B and k_win.shape[3] == d,
+          "window K/V must be contiguous [B, capacity, H_kv, d] of one dtype")
+    _need(lens.dtype == torch.int32 and lens.numel() == B, "lens must be int32 [B]")
+    _need((hist_out is None) == (hist_lse is None), "hist_out and hist_lse go together")
+    if hist_out is not None:
+        _need(hist_out.dtype == torch.float32 and hist_out.shape == (B, Hq, d) and hist_out.is_contiguous()
+              and hist_lse.dtype == torch.float32 and hist_lse.shape == (B, Hq) and hist_lse.is_contiguous(),
+              "history must be float32 out [B, H_q, d] and lse [B, H_q]")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out.shape == (B, Hq, d) and out.is_contiguous(), "out must be contiguous [B, H_q, d]")
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    own_err = dev_err is None and check
+    if own_err:
+        dev_err = new_error_word(q.device)
+    _check(_lib.tq_decode_dense(_ptr(q), _dtype_code(q), B, Hq, k_win.shape[2], d, _ptr(k_win), _ptr(v_win),
+                                _dtype_code(k_win), k_win.shape[1], _ptr(lens), float(scale), _ptr(hist_out),
+                                _ptr(hist_lse), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(dev_err),
+                                _stream(stream)))
+    if check:
+        raise_device_error(dev_err, "tq_decode_dense")
+    return out, lse
+
+
 __all__ = ["Format", "UnsupportedFormatError", "DeviceError", "lloyd_max_codebook", "alloc_pages",
-           "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged", "split_merge",
+           "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged", "split_merge", "decode_dense",
            "LIB_PATH", "BLOCK_SIZE"]

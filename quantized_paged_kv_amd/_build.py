@@ -33,6 +33,7 @@ SOURCES = {
     # read a block later; the atomic optimizer would turn it into a wave-wide
     # reduction that waits for the result immediately
     "decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+    "window.hip": [],
 }
 
 

@@ -160,3 +160,33 @@ def test_merge_status_codes_without_launch():
     assert L.tq_split_merge(1, 1, 2, 2, 2, 96, 1, tq.TQ_F32, None, None) == tq.TQ_ERR_VALUE
     assert L.tq_split_merge(None, 1, 2, 2, 2, 128, 1, tq.TQ_F32, None, None) == tq.TQ_ERR_VALUE
     assert L.tq_split_merge(1, 1, 0, 2, 2, 128, 1, tq.TQ_F32, None, None) == tq.TQ_OK
+
+
+def _call_dense(q=16, qd=None, B=2, Hq=8, Hkv=2, d=128, k=16, v=16, kvd=None, cap=4, lens=16, scale=0.1,
+                ho=None, hl=None, out=16, od=None):
+    """tq_decode_dense with fake (never dereferenced) pointers: every call here
+    must be refused by host validation or return before any launch."""
+    qd = tq.TQ_BF16 if qd is None else qd
+    kvd = tq.TQ_BF16 if kvd is None else kvd
+    od = tq.TQ_F32 if od is None else od
+    return tq._lib.tq_decode_dense(q, qd, B, Hq, Hkv, d, k, v, kvd, cap, lens, scale, ho, hl, out, od,
+                                   None, None, None)
+
+
+def test_dense_window_status_codes_without_launch():
+    assert _call_dense(Hq=7) == tq.TQ_ERR_VALUE                      # not a multiple of H_kv
+    assert _call_dense(Hq=34, Hkv=2) == tq.TQ_ERR_UNSUPPORTED_FORMAT  # 17 q heads per kv head
+    assert _call_dense(d=96) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert _call_dense(qd=3) == tq.TQ_ERR_VALUE
+    assert _call_dense(kvd=3) == tq.TQ_ERR_VALUE
+    assert _call_dense(scale=0.0) == tq.TQ_ERR_VALUE
+    assert _call_dense(scale=float("nan")) == tq.TQ_ERR_VALUE
+    assert _call_dense(cap=-1) == tq.TQ_ERR_VALUE
+    assert _call_dense(ho=16) == tq.TQ_ERR_VALUE                      # hist_out without hist_lse
+    assert _call_dense(q=None) == tq.TQ_ERR_VALUE
+    assert _call_dense(lens=None) == tq.TQ_ERR_VALUE
+    assert _call_dense(k=None) == tq.TQ_ERR_VALUE
+    assert _call_dense(k=24) == tq.TQ_ERR_VALUE                       # not 16-byte aligned
+    assert _call_dense(out=12) == tq.TQ_ERR_VALUE                     # not 8-byte aligned
+    assert "aligned" in tq._lib.tq_last_error().decode()
+    assert _call_dense(B=0) == tq.TQ_OK

@@ -103,3 +103,88 @@ def test_rotated_domain_equals_original_domain():
     from oracle.rotation import inverse_rotate
     np.testing.assert_allclose(inverse_rotate(o_r, s), o, atol=1e-12)
     assert abs(lse - lse_r) < 1e-12
+
+
+def _paged_history(rng, B, Hkv, d, ctx, f, bs=16):
+    """A small packed history: per-sequence consecutive physical blocks in a
+    shuffled pool, written by the oracle's own encoder."""
+    nb_s = [-(-int(c) // bs) for c in ctx]
+    nb = max(1, sum(nb_s))
+    perm = rng.permutation(nb)
+    mb = max(1, max(nb_s))
+    bt = np.zeros((B, mb), dtype=np.int64)
+    _, _, tile = pg.tile_layout(f, bs)
+    kp = np.zeros((nb, Hkv, tile), dtype=np.uint8)
+    vp = np.zeros((nb, Hkv, tile), dtype=np.uint8)
+    used = 0
+    for s in range(B):
+        bt[s, :nb_s[s]] = perm[used:used + nb_s[s]]
+        used += nb_s[s]
+        n = int(ctx[s])
+        if n:
+            sl = bt[s, np.arange(n) // bs] * bs + np.arange(n) % bs
+            pg.write_pages(rng.standard_normal((n, Hkv, d)), sl, kp, f, bs)
+            pg.write_pages(rng.standard_normal((n, Hkv, d)), sl, vp, f, bs, "v")
+    return kp, vp, bt
+
+
+def _window_case(seed=3, B=3, Hq=4, Hkv=2, d=64, ctx=(40, 0, 17), wl=(5, 9, 0), cap=9):
+    rng = np.random.default_rng(seed)
+    f = enc.Format.make(d, [4], signs(seed, 1, d))
+    kp, vp, bt = _paged_history(rng, B, Hkv, d, ctx, f)
+    kw = rng.standard_normal((B, cap, Hkv, d))
+    vw = rng.standard_normal((B, cap, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    return q, kw, vw, np.array(wl), kp, vp, bt, np.array(ctx), f
+
+
+def test_window_equals_merge_of_history_and_window():
+    """Attention over the union equals the log-sum-exp merge of the history's
+    and the window's own attention (the merge identity), for every mix of
+    empty and non-empty parts."""
+    q, kw, vw, wl, kp, vp, bt, ctx, f = _window_case()
+    sc = 0.4
+    o, lse = att.decode_window_reference(q, kw, vw, wl, sc, kp, vp, bt, ctx, f, f)
+    oh, lh = att.decode_reference(q, kp, vp, bt, ctx, f, f, sc, 16)
+    G = q.shape[1] // kw.shape[2]
+    for s in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            ow, lw = att.attention(q[s, h], kw[s, :wl[s], h // G], vw[s, :wl[s], h // G], sc)
+            om, lm = att.merge_partials(np.stack([oh[s, h], ow]), np.array([lh[s, h], lw]))
+            np.testing.assert_allclose(o[s, h], om, atol=1e-12)
+            assert lse[s, h] == lm or abs(lse[s, h] - lm) < 1e-12
+    # sequence 1: no history -> the window alone; sequence 2: no window -> the history alone
+    np.testing.assert_allclose(o[2], oh[2], atol=1e-13)
+    np.testing.assert_allclose(lse[2], lh[2], atol=1e-13)
+
+
+def test_window_holding_a_copy_of_the_history():
+    """A window that repeats every history token (their decoded values)
+    leaves the output unchanged and adds ln 2 to the lse."""
+    q, kw, vw, wl, kp, vp, bt, ctx, f = _window_case(seed=5, ctx=(33, 20, 1), wl=(0, 0, 0), cap=33)
+    B, Hkv, d = q.shape[0], kw.shape[2], q.shape[2]
+    for s in range(B):
+        n = int(ctx[s])
+        for kvh in range(Hkv):
+            kw[s, :n, kvh] = pg.reconstruct_sequence(kp, bt[s], n, kvh, f, 16)
+            vw[s, :n, kvh] = pg.reconstruct_sequence(vp, bt[s], n, kvh, f, 16, role="v")
+    o, lse = att.decode_window_reference(q, kw, vw, ctx, 0.3, kp, vp, bt, ctx, f, f)
+    oh, lh = att.decode_reference(q, kp, vp, bt, ctx, f, f, 0.3, 16)
+    np.testing.assert_allclose(o, oh, atol=1e-13)
+    np.testing.assert_allclose(lse, lh + math.log(2.0), atol=1e-13)
+
+
+def test_window_alone_and_all_empty():
+    """Without pages the result is plain attention over the window rows; a
+    sequence with neither history nor window gives o = 0, lse = -inf; a
+    one-token window returns that token's V row and lse = scale q.k."""
+    q, kw, vw, wl, *_ = _window_case(seed=7, wl=(1, 9, 0))
+    o, lse = att.decode_window_reference(q, kw, vw, wl, 0.5)
+    G = q.shape[1] // kw.shape[2]
+    for h in range(q.shape[1]):
+        np.testing.assert_array_equal(o[0, h], vw[0, 0, h // G])
+        assert lse[0, h] == pytest.approx(0.5 * float(q[0, h] @ kw[0, 0, h // G]), abs=1e-14)
+        ob, lb = _brute(q[1, h], kw[1, :9, h // G], vw[1, :9, h // G], 0.5)
+        np.testing.assert_allclose(o[1, h], ob, atol=1e-13)
+        assert abs(lse[1, h] - lb) < 1e-12
+    assert np.all(o[2] == 0) and np.all(lse[2] == -math.inf)

@@ -58,3 +58,21 @@ def test_norm_inclusive_ratios_are_lower():
         assert L["ratio_all_inclusive"] < L["ratio_rows_with_norms"] < L["ratio_bits_only"] + 1e-12
         # metadata lowers it only a little
         assert L["ratio_all_inclusive"] > 0.999 * L["dense_bytes"] / L["storage_bytes"] - 1e-9
+
+
+def test_dense_window_counts_in_storage():
+    """Tokens kept unquantised (boundary + recent window) cost their full
+    bf16 bytes in storage and count in the dense baseline: with a window of
+    W tokens next to T packed ones (K4/V4, 132 B per packed token-head), the
+    rows-with-norms ratio is 512 (T + W) / (132 T + 512 W)."""
+    T, H, W = 4096, 8, 132
+    L0 = ledger(_f([4]), _f([4]), T, H, 16, T // 16)
+    L = ledger(_f([4]), _f([4]), T, H, 16, T // 16, window_tokens=W)
+    assert L["window_bytes"] == 2 * W * H * 128 * 2
+    assert L["storage_bytes"] == L0["storage_bytes"] + L["window_bytes"]
+    assert L["dense_bytes"] == 2 * (T + W) * H * 128 * 2
+    assert L["ratio_rows_with_norms"] == pytest.approx(512 * (T + W) / (132 * T + 512 * W))
+    assert L["ratio_rows_with_norms"] < L0["ratio_rows_with_norms"]
+    # a ring buffer with spare room is charged for its capacity
+    Lc = ledger(_f([4]), _f([4]), T, H, 16, T // 16, window_tokens=W, window_capacity_tokens=256)
+    assert Lc["window_bytes"] == 2 * 256 * H * 128 * 2

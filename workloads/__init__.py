@@ -42,6 +42,8 @@ STREAM_Q = 13
 STREAM_CTX = 14
 STREAM_NEW_K = 21
 STREAM_NEW_V = 22
+STREAM_WIN_K = 31
+STREAM_WIN_V = 32
 
 
 class SplitMix64:
@@ -315,3 +317,12 @@ def write_values(w: WriteWorkload, which: str) -> np.ndarray:
     if w.in_dtype == "bf16":
         x = bf16_round(x)
     return x
+
+
+def window_values(seed: int, num_seqs: int, capacity: int, num_kv_heads: int, head_dim: int, which: str,
+                  dtype: str = "bf16", dist: str = "normal") -> np.ndarray:
+    """Dense-window K or V rows: float32 array [num_seqs, capacity, H_kv, d]
+    holding values exactly representable in `dtype` (N(0, 1) by default)."""
+    g = rng(seed, STREAM_WIN_K if which == "k" else STREAM_WIN_V)
+    x = _draw(dist, g, (num_seqs, capacity, num_kv_heads, head_dim))
+    return bf16_round(x) if dtype == "bf16" else x
