@@ -29,10 +29,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-SPLITS = {2: 16, 4: 16, 5: 64, 1: 1}
-LAYERS = {2: 3, 4: 2, 5: 1, 1: 1}
+SPLITS = {2: 16, 4: 16, 5: 64, 6: 64, 1: 1}
+LAYERS = {2: 3, 4: 2, 5: 1, 6: 1, 1: 1}
 FLUSH_BYTES = 1 << 30
-NAMES = {"8b": 2, "70b": 4, "long": 5, "tiny": 1}
+NAMES = {"8b": 2, "70b": 4, "long": 5, "long25": 6, "tiny": 1}
 
 
 def log(msg):
@@ -429,6 +429,7 @@ def main():
         del b4
         torch.cuda.empty_cache()
         # the other workloads: the write path and the tiny / long-context decodes
+        # (the long context also with the 2.5-bit K recipe)
         ww, wms, wbytes = write_cold(args.steps, args.warmup, flush)
         wavg = sum(wms) / len(wms)
         result["write"] = {"workload": ww.name, "us": stats_us(wms), "algorithmic_bytes": wbytes,
@@ -436,7 +437,7 @@ def main():
                            "frac_of_peak": round(wbytes / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"write: {wavg * 1e3:.1f} us")
         torch.cuda.empty_cache()
-        for idx, key in ((5, "long"), (1, "tiny")):
+        for idx, key in ((5, "long"), (6, "long25"), (1, "tiny")):
             bx = Bench(idx)
             dx = bx.timed_cold(max(10, args.steps // 2), args.warmup, flush)
             ax = sum(dx) / len(dx)

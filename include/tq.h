@@ -227,7 +227,9 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *                is clamped.
  * A sequence with context length 0 gets out = 0 and lse = -inf.
  * Served formats (else UNSUPPORTED_FORMAT): head_dim 64 or 128; K one group
- * of 4 or 2 bits, or two groups of 4 + 3 bits; V one group of 4 or 2 bits;
+ * of 4 or 2 bits, or two groups of 4 + 3 bits (3.5-bit recipe) or 3 + 2 bits
+ * (2.5-bit recipe; [S "What it does"], [D "Recipe Strategy"]); V one group
+ * of 4 or 2 bits;
  * num_q_heads / num_kv_heads in 1..8; block_size 16.  Each page pool must be
  * smaller than 4 GiB and num_blocks below 2^31 (else VALUE).
  * Results are reproducible up to the order of floating-point accumulation:

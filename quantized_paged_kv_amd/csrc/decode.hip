@@ -68,7 +68,7 @@ constexpr int kBtCap = 2048;        // block-table entries of a piece staged in 
 constexpr uint32_t kDoneBits = 0x7FC0D0E5u;
 constexpr float kLn2 = 0.6931471805599453f;
 
-enum KKind { K4 = 0, K2 = 1, KM43 = 2 };
+enum KKind { K4 = 0, K2 = 1, KM43 = 2, KM32 = 3 };
 enum VKind { V4 = 0, V2 = 1 };
 
 struct DecodeParams {
@@ -189,10 +189,13 @@ template <int D, int KK, int VK>
 struct Cfg {
   static constexpr int R = D / 16;                       // dims per lane-row in P.V
   static constexpr int NQK = D / 32;                     // q.K MFMAs per block
-  static constexpr int KROW = KK == K4 ? D / 2 : (KK == K2 ? D / 4 : (D / 2) * 4 / 8 + (D / 2) * 3 / 8);
+  static constexpr int KROW = KK == K4 ? D / 2
+                              : KK == K2 ? D / 4
+                              : KK == KM43 ? (D / 2) * 4 / 8 + (D / 2) * 3 / 8
+                                           : (D / 2) * 3 / 8 + (D / 2) * 2 / 8;
   static constexpr int VROW = VK == V4 ? D / 2 : D / 4;
   static constexpr int VLANE = VK == V4 ? D / 32 : D / 64;  // bytes per lane per token in V
-  static constexpr bool MIXED = KK == KM43;
+  static constexpr bool MIXED = KK == KM43 || KK == KM32;   // two groups: 3-bit pair table in use
   static constexpr int LDS_LUT = kLutBytes + (MIXED ? kLut3Bytes : 0);
   static constexpr int QS = D + D / 4 + 4;                // rotated-q row stride (floats), conflict-free rows
   static constexpr int QV_FLOATS = NQK * 64 * 4;          // q.K B operands of one kv head: NQK x 64 lanes x half8
@@ -234,7 +237,9 @@ __device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rs
                                           uint32_t n_off, uint32_t v_off) {
   using C = Cfg<D, KK, VK>;
   constexpr uint32_t KN = 16 * C::KROW, VN = 16 * C::VROW;   // norm areas follow the 16 rows
-  if constexpr (KK == K4 && D == 128) {
+  if constexpr (KK == KM32) {   // the 2-bit group's bytes of this lane (aligned dword holding them)
+    t.k[0] = __builtin_amdgcn_raw_buffer_load_b32(kr, k_off, kb, 0);
+  } else if constexpr (KK == K4 && D == 128) {
     const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off, kb, 0);
     t.k[0] = x[0]; t.k[1] = x[1]; t.k[2] = x[2]; t.k[3] = x[3];
   } else if constexpr ((KK == K4 && D == 64) || (KK != K4 && D == 128)) {
@@ -612,10 +617,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const uint32_t off_v2 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 15) * 8u;
   const uint32_t off3 = (uint32_t)kLutBytes + (uint32_t)(lane & 15) * 4u;
   const int tokK = (j >> 2) + 4 * (j & 3);   // token of this lane's K row: sigma(j)
-  // per-lane byte offsets inside a K / V tile
-  constexpr int KLANE = KK == K4 ? D / 8 : (KK == K2 ? D / 16 : D / 16);   // index bytes of the (high) group
-  const uint32_t k_off = (uint32_t)(tokK * C::KROW + KLANE * a);
-  const uint32_t klo_off = (uint32_t)((tokK * C::KROW + D / 4 + (3 * D / 64) * a) & ~3);
+  // per-lane byte offsets inside a K / V tile: k_off the lane's bytes of the
+  // one group (K4, K2) or of the 4-bit group (4+3), or the aligned dword that
+  // holds its bytes of the 2-bit group (3+2); klo_off the aligned 8-B window
+  // that holds its bytes of the 3-bit group (two-group formats)
+  constexpr int KLANE = KK == K4 ? D / 8 : D / 16;
+  constexpr int G3_AT = KK == KM32 ? 0 : D / 4;   // first byte of the 3-bit group in a row
+  const uint32_t k_off = KK == KM32 ? (uint32_t)((tokK * C::KROW + 3 * D / 16 + (D / 32) * a) & ~3)
+                                    : (uint32_t)(tokK * C::KROW + KLANE * a);
+  const uint32_t klo_off = (uint32_t)((tokK * C::KROW + G3_AT + (3 * D / 64) * a) & ~3);
   const uint32_t n_off = (uint32_t)(8 * a);   // this lane's 4 norms, after the tile's norm offset
   const uint32_t v_off = (uint32_t)(lane * 4 * C::VLANE);   // this lane's run of the V plane
   const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
@@ -901,7 +911,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
             acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
           }
-        } else {
+        } else if constexpr (KK == KM43) {   // 4-bit group 0 by the nibble table, 3-bit group 1 by the pair table
           constexpr int per_g = NQK / 2;
 #pragma unroll
           for (int u = 0; u < per_g; ++u) {
@@ -921,6 +931,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
               const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
               av[pr] = lds_u32(lds, (key << 6) | off3);
             }
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
+          }
+        } else {   // 3 + 2 bits: 3-bit group 0 by the pair table, 2-bit group 1 by the crumb table
+          constexpr int per_g = NQK / 2;
+          constexpr int LB = 3 * D / 64;
+          const int g0_off = tokK * C::KROW + LB * a;
+          const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((g0_off & 3) * 8);
+#pragma unroll
+          for (int u = 0; u < per_g; ++u) {
+            u32x4_t av;
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) {
+              const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
+              av[pr] = lds_u32(lds, (key << 6) | off3);
+            }
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
+          }
+          const int g1_off = tokK * C::KROW + 3 * D / 16 + (D / 32) * a;
+          const uint32_t kw = cur.k[0] >> ((g1_off & 3) * 8);
+#pragma unroll
+          for (int u = 0; u < per_g; ++u) {
+            const uint2 x0 = lds_u64(lds, lut_addr(kw, off2_k, 2 * u));
+            const uint2 x1 = lds_u64(lds, lut_addr(kw, off2_k, 2 * u + 1));
+            const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
             acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
           }
         }
@@ -1274,6 +1308,7 @@ int format_kind_k(const tq_format* f) {
   if (f->num_groups == 1 && f->group_bits[0] == 4) return K4;
   if (f->num_groups == 1 && f->group_bits[0] == 2) return K2;
   if (f->num_groups == 2 && f->group_bits[0] == 4 && f->group_bits[1] == 3) return KM43;
+  if (f->num_groups == 2 && f->group_bits[0] == 3 && f->group_bits[1] == 2) return KM32;
   return -1;
 }
 
@@ -1328,7 +1363,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   const int G = num_q_heads / num_kv_heads;
   if (G > 8) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "more than 8 q heads per kv head");
   const int kk = format_kind_k(kfmt), vk = format_kind_v(vfmt);
-  if (kk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit groups)");
+  if (kk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
   if (vk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this V format (served: 4-bit, 2-bit)");
   const int D = kfmt->head_dim;
   if (num_seqs == 0) return TQ_OK;
@@ -1396,13 +1431,15 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
     if (vfmt->signs[jx] < 0) p.v_signs[jx >> 5] |= 1u << (jx & 31);
     p.k_ch[jx] = kfmt->group_channels[jx];
   }
-  // LUT halves: K's table in half 0; V shares it when bits and codebook agree
-  const int kbits0 = kfmt->group_bits[0];
+  // LUT halves: K's 4-bit or 2-bit table in half 0 (the 2-bit group's for
+  // 3+2 bits); V shares it when bits and codebook agree
+  const int kgh = kk == KM32 ? 1 : 0;   // K group whose levels fill half 0
+  const int kbits0 = kfmt->group_bits[kgh];
   p.half_kind[0] = kbits0;
-  for (int i = 0; i < 16; ++i) p.half_cb[0][i] = kfmt->codebook[0][i];
+  for (int i = 0; i < 16; ++i) p.half_cb[0][i] = kfmt->codebook[kgh][i];
   const int vbits = vfmt->group_bits[0];
   bool share = vbits == kbits0;
-  for (int i = 0; i < (1 << vbits) && share; ++i) share = vfmt->codebook[0][i] == kfmt->codebook[0][i];
+  for (int i = 0; i < (1 << vbits) && share; ++i) share = vfmt->codebook[0][i] == kfmt->codebook[kgh][i];
   if (share) {
     p.v_half = 0;
     p.half_kind[1] = 0;
@@ -1411,8 +1448,8 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
     p.half_kind[1] = vbits;
     for (int i = 0; i < 16; ++i) p.half_cb[1][i] = vfmt->codebook[0][i];
   }
-  if (kk == KM43)
-    for (int i = 0; i < 8; ++i) p.k3_cb[i] = kfmt->codebook[1][i];
+  if (kk == KM43 || kk == KM32)   // the 3-bit group's levels: group 1 (4+3) or group 0 (3+2)
+    for (int i = 0; i < 8; ++i) p.k3_cb[i] = kfmt->codebook[kk == KM43 ? 1 : 0][i];
   p.q_f32 = q_dtype == TQ_F32;
   p.out_f32 = out_dtype == TQ_F32;
   p.q_bytes = (int32_t)q_bytes;
@@ -1424,9 +1461,9 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
 #define TQ_LAUNCH(DD, KKK, VVV) \
   if (D == DD && kk == KKK && vk == VVV) launch_decode<DD, KKK, VVV>(p, hs);
   TQ_LAUNCH(128, K4, V4) TQ_LAUNCH(128, K4, V2) TQ_LAUNCH(128, K2, V4) TQ_LAUNCH(128, K2, V2)
-  TQ_LAUNCH(128, KM43, V4) TQ_LAUNCH(128, KM43, V2)
+  TQ_LAUNCH(128, KM43, V4) TQ_LAUNCH(128, KM43, V2) TQ_LAUNCH(128, KM32, V4) TQ_LAUNCH(128, KM32, V2)
   TQ_LAUNCH(64, K4, V4) TQ_LAUNCH(64, K4, V2) TQ_LAUNCH(64, K2, V4) TQ_LAUNCH(64, K2, V2)
-  TQ_LAUNCH(64, KM43, V4) TQ_LAUNCH(64, KM43, V2)
+  TQ_LAUNCH(64, KM43, V4) TQ_LAUNCH(64, KM43, V2) TQ_LAUNCH(64, KM32, V4) TQ_LAUNCH(64, KM32, V2)
 #undef TQ_LAUNCH
   st = launch_status("tq_decode_paged launch");
   if (st != TQ_OK || num_splits == 1) return st;

@@ -127,6 +127,11 @@ SMALL = [
     (64, [4], [2], 6, 3, [5, 400], 2, "bf16", "bf16", "normal"),
     (64, [4, 3], [4], 2, 2, [129], 1, "f32", "f32", "t3"),
     (64, [2], [2], 8, 1, [1000, 16], 7, "bf16", "f32", "normal"),
+    # the 2.5-bit K recipe (3-bit high + 2-bit low channel groups)
+    (128, [3, 2], [2], 16, 2, [700, 64, 0], 5, "bf16", "bf16", "t3"),
+    (128, [3, 2], [4], 8, 2, [33, 300], 1, "f32", "f32", "normal"),
+    (64, [3, 2], [2], 6, 3, [5, 400, 129], 3, "bf16", "f32", "t5u"),
+    (64, [3, 2], [4], 1, 1, [256], 1, "f32", "f32", "normal"),
 ]
 
 
@@ -276,11 +281,12 @@ def test_split_workspace_contents_do_not_matter():
 
 
 # ------------------------------------------------------------------ full size
-BENCH_SPLITS = {2: 16, 4: 16, 5: 64}
+BENCH_SPLITS = {2: 16, 4: 16, 5: 64, 6: 64}
 
 
 @pytest.mark.parametrize("index,seqs,heads_per_seq", [(1, [0], None), (2, [0, 13, 31], None), (4, [3], None),
-                                                      (5, [0], [0, 9, 18, 27, 36, 45, 54, 63])])
+                                                      (5, [0], [0, 9, 18, 27, 36, 45, 54, 63]),
+                                                      (6, [0], [0, 9, 18, 27, 36, 45, 54, 63])])
 def test_full_size_workloads_sampled(index, seqs, heads_per_seq):
     """The decode workloads at full size, in the launch configuration the
     benchmark times (same num_splits); outputs sampled per sequence, checked

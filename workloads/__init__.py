@@ -188,7 +188,9 @@ def _paged_tables(seed: int, context_lens: np.ndarray, block_size: int,
 
 
 def decode_workload(index: int, seed: int = 0) -> DecodeWorkload:
-    """The decode workloads (index 1, 2, 4, 5; index 3 is the write workload)."""
+    """The decode workloads (index 1, 2, 4, 5; index 3 is the write workload;
+    index 6 is workload 5 with the 2.5-bit K recipe: 64 channels at 3 bits
+    and 64 at 2 bits)."""
     bs = 16
     if index == 1:
         ctx = np.array([256], dtype=np.int32)
@@ -218,6 +220,13 @@ def decode_workload(index: int, seed: int = 0) -> DecodeWorkload:
         nb, bt = _paged_tables(seed, ctx, bs, 131072 // bs)
         kf, vf = _formats(seed, 128, [4, 3], [2])
         return DecodeWorkload("long-context B1 Hq64 Hkv8 ctx131072 K(4+3)/V2 64 splits", seed, 1, 64, 8,
+                              128, bs, ctx, nb, bt, kf, vf, "t3", "bf16", "bf16", "bf16",
+                              1.0 / math.sqrt(128.0), 64)
+    if index == 6:
+        ctx = np.array([131072], dtype=np.int32)
+        nb, bt = _paged_tables(seed, ctx, bs, 131072 // bs)
+        kf, vf = _formats(seed, 128, [3, 2], [2])
+        return DecodeWorkload("long-context B1 Hq64 Hkv8 ctx131072 K(3+2)/V2 64 splits", seed, 1, 64, 8,
                               128, bs, ctx, nb, bt, kf, vf, "t3", "bf16", "bf16", "bf16",
                               1.0 / math.sqrt(128.0), 64)
     raise ValueError(f"no decode workload {index}")
