@@ -278,6 +278,38 @@ def window_cold(b, launches, warmup, flush, cap=132):
     return res, win_bytes + io_bytes, cap
 
 
+def multi_cold(b, launches, warmup, flush, nq=2):
+    """Multi-query decode on the 8B-shaped cache of `b`: nq queries per
+    sequence (the last nq cached tokens are theirs) in one call; times it with
+    cold caches.  Returns (sorted ms, algorithmic bytes)."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    tq, w = b.tq, b.w
+    B, Hq, d = w.num_seqs, w.num_q_heads, w.head_dim
+    q = b._dev(wl.bf16_round(wl.rng(w.seed, 41).standard_normal((B, nq, Hq, d), dtype=np.float32)), "bf16")
+    out = torch.empty((B, nq, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, nq, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(tq.workspace_bytes(B * nq, Hq, d, b.P), 1), dtype=torch.uint8, device="cuda")
+
+    def call(layer):
+        kp, vp = b.pools[layer]
+        tq.decode_paged(q, kp, vp, b.bt, b.cl, b.kf, b.vf, w.scale, num_splits=b.P, out=out, lse=lse, workspace=ws)
+
+    for i in range(warmup):
+        call(i % b.L)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for i in range(launches):
+        flush_caches(flush)
+        torch.cuda._sleep(200000)
+        ev[i][0].record()
+        call(i % b.L)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    extra = (nq - 1) * B * Hq * (2 * d * 2 + 4)   # the other queries' q, out and lse
+    return sorted(a.elapsed_time(c) for a, c in ev), b.decode_bytes + extra
+
+
 def stats_us(ms):
     n = len(ms)
     return {"avg": round(sum(ms) / n * 1e3, 2), "p10": round(ms[n // 10] * 1e3, 2),
@@ -411,6 +443,14 @@ def main():
                          "frac": round(wbytes_win / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "kernel": "tq_decode_dense (window attention + merge with the history)"}}
         log(f"window: {wavg * 1e3:.1f} us")
+        mq_ms, mq_bytes = multi_cold(b, max(10, args.steps // 2), args.warmup, flush)
+        mq_avg = sum(mq_ms) / len(mq_ms)
+        result["multi_query"] = {
+            "workload": f"{w.name}, 2 queries per sequence (causal over the cache, one call)",
+            "decode_us": stats_us(mq_ms), "algorithmic_bytes": mq_bytes,
+            "GBs": round(mq_bytes / (mq_avg * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(mq_bytes / (mq_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"multi-query: {mq_avg * 1e3:.1f} us")
     del b
     torch.cuda.empty_cache()
     if not args.no_secondary and index == 2:

@@ -244,6 +244,30 @@ tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
                           tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream);
 
 /*
+ * Multi-query paged decode: num_queries new tokens per sequence attend the
+ * packed pages causally in one call (chunked prefill / several draft tokens
+ * per step; the "next" workload after single-query decode).  Reading: the
+ * sequence's last num_queries cached tokens are the queries' own (write
+ * them first, as for tq_decode_paged), so query i (0-based) attends tokens
+ * [0, context_lens[s] - (num_queries - 1 - i)); a query left with no token
+ * gets out = 0 and lse = -inf.  The (query, q head) pairs of a kv head share
+ * the matrix-core columns, so every page is read once for all queries.
+ *   q, out       device [num_seqs][num_queries][num_q_heads][head_dim].
+ *   lse          device float [num_seqs][num_queries][num_q_heads] or NULL.
+ *   workspace    tq_decode_workspace_bytes(num_seqs * num_queries, ...).
+ * Every other argument, error and format is as for tq_decode_paged, which
+ * is this call with num_queries = 1.  Served: num_queries * (num_q_heads /
+ * num_kv_heads) <= 8 (else UNSUPPORTED_FORMAT).
+ */
+tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
+                                int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,
+                                const uint8_t* v_pages, int64_t num_blocks, int32_t block_size,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const tq_format* kfmt, const tq_format* vfmt,
+                                float scale, int32_t num_splits, void* workspace, uint64_t workspace_bytes,
+                                void* out, tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream);
+
+/*
  * Log-sum-exp merge of split partials (flash-decoding):
  *   lse = M + ln sum_p exp(lse_p - M),  out = sum_p exp(lse_p - lse) * o_p
  *   part_out  device float [num_seqs][num_heads][num_splits][head_dim]

@@ -136,3 +136,26 @@ def decode_window_reference(q: np.ndarray, k_win: np.ndarray, v_win: np.ndarray,
         K, V = cache[key]
         out[s, h], lse[s, h] = attention(q[s, h], K, V, scale)
     return out, lse
+
+
+def decode_multi_reference(q: np.ndarray, k_pages, v_pages, block_tables, context_lens, kfmt, vfmt,
+                           scale: float, block_size: int):
+    """fp64 multi-query decode of q[B, NQ, H_q, d]: the sequence's last NQ
+    cached tokens are the queries' own, so query i (0-based) attends the
+    first context_lens[s] - (NQ - 1 - i) tokens (none: o = 0, lse = -inf).
+    Returns (out[B, NQ, H_q, d], lse[B, NQ, H_q])."""
+    B, NQ, Hq, d = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, NQ, Hq, d))
+    lse = np.full((B, NQ, Hq), -math.inf)
+    for s in range(B):
+        n = int(context_lens[s])
+        for kvh in range(Hkv):
+            K = reconstruct_sequence(k_pages, block_tables[s], n, kvh, kfmt, block_size) if n else np.zeros((0, d))
+            V = reconstruct_sequence(v_pages, block_tables[s], n, kvh, vfmt, block_size, role="v") if n else np.zeros((0, d))
+            for i in range(NQ):
+                c = max(n - (NQ - 1 - i), 0)
+                for h in range(kvh * G, (kvh + 1) * G):
+                    out[s, i, h], lse[s, i, h] = attention(q[s, i, h], K[:c], V[:c], scale)
+    return out, lse

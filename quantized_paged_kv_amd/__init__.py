@@ -68,6 +68,8 @@ def _load(path: str = LIB_PATH):
         "tq_decode_workspace_bytes": ([i32, i32, i32, i32, P], i32),
         "tq_decode_paged": ([P, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, f32, i32, P, u64,
                              P, i32, P, P, P], i32),
+        "tq_decode_paged_multi": ([P, i32, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, f32, i32,
+                                   P, u64, P, i32, P, P, P], i32),
         "tq_split_merge": ([P, P, i32, i32, i32, i32, P, i32, P, P], i32),
         "tq_decode_dense": ([P, i32, i32, i32, i32, i32, P, P, i32, i32, P, f32, P, P, P, i32, P, P, P], i32),
     }
@@ -256,10 +258,14 @@ def decode_paged(q, k_pages, v_pages, block_tables, context_lens, kfmt: Format, 
                  num_splits: int = 1, out=None, lse=None, workspace=None, out_dtype=None, dev_err=None,
                  check: bool = False, stream=None):
     """Decode attention of q [B, H_q, d] against the packed pages.  Returns
-    (out [B, H_q, d], lse [B, H_q] float32)."""
+    (out [B, H_q, d], lse [B, H_q] float32).  With q [B, NQ, H_q, d] the NQ
+    queries of each sequence attend causally (query i sees its first
+    context_lens - (NQ - 1 - i) tokens): out [B, NQ, H_q, d], lse [B, NQ, H_q]."""
     import torch
-    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be a contiguous [B, H_q, d] GPU tensor")
-    B, Hq, d = q.shape
+    _need(q.is_cuda and q.is_contiguous() and q.dim() in (3, 4),
+          "q must be a contiguous [B, H_q, d] or [B, NQ, H_q, d] GPU tensor")
+    NQ = q.shape[1] if q.dim() == 4 else 1
+    B, Hq, d = q.shape[0], q.shape[-2], q.shape[-1]
     _need(k_pages.dim() == 3 and v_pages.dim() == 3 and k_pages.dtype == torch.uint8 and v_pages.dtype == torch.uint8,
           "page pools must be uint8 [NB, H_kv, tile]")
     Hkv = k_pages.shape[1]
@@ -270,23 +276,25 @@ def decode_paged(q, k_pages, v_pages, block_tables, context_lens, kfmt: Format, 
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B
           and block_tables.is_contiguous(), "block_tables must be contiguous int32 [B, max_blocks]")
     _need(context_lens.dtype == torch.int32 and context_lens.numel() == B, "context_lens must be int32 [B]")
+    rows = tuple(q.shape[:-1])
     if out is None:
-        out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out.shape == (B, Hq, d) and out.is_contiguous(), "out must be contiguous [B, H_q, d]")
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _need(out.shape == q.shape and out.is_contiguous(), "out must be contiguous and shaped like q")
     if lse is None:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    need = workspace_bytes(B, Hq, d, num_splits)
+        lse = torch.empty(rows, dtype=torch.float32, device=q.device)
+    _need(lse.shape == rows and lse.dtype == torch.float32, "lse must be float32 shaped like q without d")
+    need = workspace_bytes(B * NQ, Hq, d, num_splits)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     own_err = dev_err is None and check
     if own_err:
         dev_err = new_error_word(q.device)
-    _check(_lib.tq_decode_paged(_ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(k_pages), _ptr(v_pages), k_pages.shape[0],
-                                BLOCK_SIZE, _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-                                ctypes.byref(kfmt.c), ctypes.byref(vfmt.c), float(scale), int(num_splits),
-                                _ptr(workspace), ws_bytes, _ptr(out), _dtype_code(out), _ptr(lse), _ptr(dev_err),
-                                _stream(stream)))
+    _check(_lib.tq_decode_paged_multi(_ptr(q), _dtype_code(q), B, NQ, Hq, Hkv, _ptr(k_pages), _ptr(v_pages),
+                                      k_pages.shape[0], BLOCK_SIZE, _ptr(block_tables), block_tables.shape[1],
+                                      _ptr(context_lens), ctypes.byref(kfmt.c), ctypes.byref(vfmt.c), float(scale),
+                                      int(num_splits), _ptr(workspace), ws_bytes, _ptr(out), _dtype_code(out),
+                                      _ptr(lse), _ptr(dev_err), _stream(stream)))
     if check:
         raise_device_error(dev_err, "tq_decode_paged")
     return out, lse

@@ -88,6 +88,13 @@ struct DecodeParams {
   int32_t n_wg;      // grid size (persistent workgroups)
   int32_t seg_cost;  // work positions charged for starting a piece (see seg_span)
   float inv_G;       // 1 / G
+  // Several queries per sequence (multi-query decode): the NQ * Gr (query, q
+  // head) pairs of a kv head are its G = NQ * Gr matrix-core columns; query i
+  // of a sequence attends its first ctx - (NQ - 1 - i) cached tokens; q / out
+  // rows are [sequence][query][q head].  NQ = 1, Gr = G for one query.
+  int32_t NQ, Gr;
+  int32_t rows_ps;   // q / out rows per sequence: NQ * Hq
+  float inv_Gr;      // 1 / Gr
   int32_t k_tile, v_tile, k_norm_off, v_norm_off;
   uint32_t k_span, v_span;   // bytes of each pool (< 4 GiB)
   float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K)), > 0
@@ -547,15 +554,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         c = clamp_ctx(c, cap);
       }
       if (c == 0) {
-        for (int idx = lane; idx < p.Hq * D; idx += 64) {
-          const int64_t off = (int64_t)s * p.Hq * D + idx;
+        for (int idx = lane; idx < p.rows_ps * D; idx += 64) {
+          const int64_t off = (int64_t)s * p.rows_ps * D + idx;
           if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
           else static_cast<uint16_t*>(p.out)[off] = 0;
         }
         if (p.lse)
-          for (int h = lane; h < p.Hq; h += 64) p.lse[(int64_t)s * p.Hq + h] = -INFINITY;
+          for (int h = lane; h < p.rows_ps; h += 64) p.lse[(int64_t)s * p.rows_ps + h] = -INFINITY;
         if (p.P > 1)   // tell the merge that these rows are final
-          for (int h = lane; h < p.Hq; h += 64) p.part_lse[((int64_t)s * p.Hq + h) * p.P] = __uint_as_float(kDoneBits);
+          for (int h = lane; h < p.rows_ps; h += 64) p.part_lse[((int64_t)s * p.rows_ps + h) * p.P] = __uint_as_float(kDoneBits);
       }
     }
   }
@@ -655,6 +662,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int piece = (int)blockIdx.x - vb0 / R;
     const int n_pieces = (vb0 + nb_s - 1) / R - vb0 / R + 1;
       const int ctx = seq_len(p, s_cl, s);
+      // causal lengths: the sequence's last NQ cached tokens are the queries'
+      // own, query i sees ctx - (NQ - 1 - i) of them; ctx_all is what every
+      // query sees, ctx_col this lane's column's (columns past G: ctx)
+      const int ctx_all = ctx - (p.NQ - 1);
+      const int qi_col = (int)(((float)gq + 0.5f) * p.inv_Gr);
+      const int ctx_col = qi_col < p.NQ ? ctx - (p.NQ - 1 - qi_col) : ctx;
       const int kvh = grp * HG + hl;   // this wave's kv head
       const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
       const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
@@ -696,8 +709,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       {   // issued by every wave (parts > 0 discard them) so that all paths
           // carry the same loads and later waits count exactly
         const int esz = p.q_f32 ? 4 : 2;
-        const int head0 = uni((int)(((int64_t)s * p.Hq + kvh * p.G) * D * esz));   // first q row of the head
-        const uint32_t lane_off = (uint32_t)(((q_live ? g8 : 0) * D + l8 * PER) * esz);
+        const int head0 = uni((int)(((int64_t)s * p.rows_ps + kvh * p.Gr) * D * esz));   // query 0, first q head
+        int qrow = 0;   // this lane's (query, q head) column: rows past head0
+        if (q_live) {
+          const int qi = (int)(((float)g8 + 0.5f) * p.inv_Gr);
+          qrow = qi * p.Hq + (g8 - qi * p.Gr);
+        }
+        const uint32_t lane_off = (uint32_t)((qrow * D + l8 * PER) * esz);
         const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
 #pragma unroll
         for (int i = 0; i < PER / 4; ++i) {
@@ -978,9 +996,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
           sc[e] = v;
         }
-        if (!(ok && tok0 + 16 <= ctx)) {   // partial or skipped block (wave-uniform branch)
+        if (!(ok && tok0 + 16 <= ctx_all)) {   // partial or skipped block (wave-uniform branch)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx) ? sc[e] : -INFINITY;
+          for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx_col) ? sc[e] : -INFINITY;
         }
         const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
         const float m_new = max_nn(m_run, bm);
@@ -1161,7 +1179,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
         const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
         const float lse = empty ? -INFINITY : (M * wc + log2f(L)) * kLn2;
-        const int hq = (grp * HG + h2) * p.G + g;
+        const int qi = (int)(((float)g + 0.5f) * p.inv_Gr);   // column g = (query qi, q head g - qi Gr)
+        const int64_t rowq = ((int64_t)s * p.NQ + qi) * p.Hq + (grp * HG + h2) * p.Gr + (g - qi * p.Gr);
         const int d0 = ND * m;
         const uint32_t sgn = s_par[24 + (d0 >> 5)] >> (d0 & 31);
 #pragma unroll
@@ -1171,7 +1190,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
         if (live) {
           if (whole) {
-            const int64_t off = ((int64_t)s * p.Hq + hq) * D + d0;
+            const int64_t off = rowq * D + d0;
             if (p.out_f32) {
 #pragma unroll
               for (int k = 0; k < ND; k += 4)
@@ -1185,10 +1204,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
               if constexpr (ND == 8) *reinterpret_cast<uint4*>(o16) = uint4{w[0], w[1], w[2], w[3]};
               else *reinterpret_cast<uint2*>(o16) = uint2{w[0], w[1]};
             }
-            if (m == 0 && p.lse) p.lse[(int64_t)s * p.Hq + hq] = lse;
-            if (m == 0 && p.P > 1) p.part_lse[((int64_t)s * p.Hq + hq) * p.P] = __uint_as_float(kDoneBits);
+            if (m == 0 && p.lse) p.lse[rowq] = lse;
+            if (m == 0 && p.P > 1) p.part_lse[rowq * p.P] = __uint_as_float(kDoneBits);
           } else {
-            const int64_t row0 = ((int64_t)s * p.Hq + hq) * p.P;
+            const int64_t row0 = rowq * p.P;
             const int64_t prow = row0 + piece;
 #pragma unroll
             for (int k = 0; k < ND; k += 4)
@@ -1340,13 +1359,14 @@ extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse
   return launch_status("tq_split_merge launch");
 }
 
-extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
-                                     int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
-                                     int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
-                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                     const tq_format* kfmt, const tq_format* vfmt, float scale,
-                                     int32_t num_splits, void* workspace, uint64_t workspace_bytes, void* out,
-                                     tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream) {
+extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
+                                           int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,
+                                           const uint8_t* v_pages, int64_t num_blocks, int32_t block_size,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, const tq_format* kfmt, const tq_format* vfmt,
+                                           float scale, int32_t num_splits, void* workspace, uint64_t workspace_bytes,
+                                           void* out, tq_dtype out_dtype, float* lse, int32_t* dev_err,
+                                           tq_stream_t stream) {
   tq_status st = check_format(kfmt, "K");
   if (st != TQ_OK) return st;
   st = check_format(vfmt, "V");
@@ -1358,10 +1378,13 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
     return set_error(TQ_ERR_VALUE, "shape arguments must be positive");
   if (num_q_heads % num_kv_heads != 0) return set_error(TQ_ERR_VALUE, "num_q_heads must be a multiple of num_kv_heads");
   if (num_splits <= 0) return set_error(TQ_ERR_VALUE, "num_splits must be >= 1");
+  if (num_queries <= 0) return set_error(TQ_ERR_VALUE, "num_queries must be >= 1");
   if (!(scale > 0.f) || !(scale < INFINITY)) return set_error(TQ_ERR_VALUE, "scale must be positive and finite");
   if (block_size != TQ_BLOCK_SIZE) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "block_size must be 16");
-  const int G = num_q_heads / num_kv_heads;
-  if (G > 8) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "more than 8 q heads per kv head");
+  const int Gr = num_q_heads / num_kv_heads;
+  if ((int64_t)num_queries * Gr > 8)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "more than 8 (query, q head) pairs per kv head");
+  const int G = num_queries * Gr;   // matrix-core columns used per kv head
   const int kk = format_kind_k(kfmt), vk = format_kind_v(vfmt);
   if (kk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
   if (vk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this V format (served: 4-bit, 2-bit)");
@@ -1370,13 +1393,13 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   if (!q || !k_pages || !v_pages || !block_tables || !context_lens || !out)
     return set_error(TQ_ERR_VALUE, "NULL required pointer");
   uint64_t need = 0;
-  tq_decode_workspace_bytes(num_seqs, num_q_heads, D, num_splits, &need);
+  tq_decode_workspace_bytes(num_seqs * num_queries, num_q_heads, D, num_splits, &need);
   if (workspace_bytes < need || (need && !workspace))
     return set_error(TQ_ERR_VALUE, "workspace too small: need " + std::to_string(need) + " bytes");
   const int64_t work_bound = (int64_t)num_seqs * num_kv_heads * (max_blocks_per_seq + 128);
   if (work_bound >= (1ll << 30) || max_blocks_per_seq > (1 << 20))
     return set_error(TQ_ERR_VALUE, "too much work for one call (2^30 block-heads, 2^20 blocks per sequence)");
-  const int64_t q_bytes = (int64_t)num_seqs * num_q_heads * D * (q_dtype == TQ_F32 ? 4 : 2);
+  const int64_t q_bytes = (int64_t)num_seqs * num_queries * num_q_heads * D * (q_dtype == TQ_F32 ? 4 : 2);
   const int64_t k_pool = num_blocks * num_kv_heads * (int64_t)tile_bytes_of(kfmt);
   const int64_t v_pool = num_blocks * num_kv_heads * (int64_t)tile_bytes_of(vfmt);
   if (num_blocks >= (1ll << 31) || k_pool > 0xFFFFFFFFll || v_pool > 0xFFFFFFFFll)
@@ -1415,6 +1438,10 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   // time as streaming 128 tiles of one kv head, i.e. 128 / HG blocks
   p.seg_cost = 128 / HG;
   p.inv_G = 1.0f / (float)G;
+  p.NQ = num_queries;
+  p.Gr = Gr;
+  p.rows_ps = num_queries * num_q_heads;
+  p.inv_Gr = 1.0f / (float)Gr;
   const int64_t units = (int64_t)num_seqs * p.NG * max_blocks_per_seq;
   p.n_wg = (int)(units < cus ? (units > 0 ? units : 1) : cus);
   p.k_tile = tile_bytes_of(kfmt);
@@ -1455,7 +1482,7 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
   p.q_bytes = (int32_t)q_bytes;
   if (num_splits > 1) {
     p.part_o = static_cast<float*>(workspace);
-    p.part_lse = p.part_o + (int64_t)num_seqs * num_q_heads * num_splits * D;
+    p.part_lse = p.part_o + (int64_t)num_seqs * num_queries * num_q_heads * num_splits * D;
   }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 #define TQ_LAUNCH(DD, KKK, VVV) \
@@ -1467,8 +1494,21 @@ extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t nu
 #undef TQ_LAUNCH
   st = launch_status("tq_decode_paged launch");
   if (st != TQ_OK || num_splits == 1) return st;
-  MergeParams mp = {p.part_o, p.part_lse, out, lse, num_seqs, num_q_heads, num_splits, D, p.out_f32, 1};
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((num_seqs * num_q_heads + kMergeRows - 1) / kMergeRows)),
+  MergeParams mp = {p.part_o, p.part_lse, out, lse, num_seqs * num_queries, num_q_heads, num_splits, D,
+                    p.out_f32, 1};
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((num_seqs * num_queries * num_q_heads + kMergeRows - 1) / kMergeRows)),
                      dim3(64 * kMergeRows), 0, hs, mp);
   return launch_status("tq_decode_paged merge launch");
+}
+
+extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
+                                     int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                     const tq_format* kfmt, const tq_format* vfmt, float scale,
+                                     int32_t num_splits, void* workspace, uint64_t workspace_bytes, void* out,
+                                     tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream) {
+  return tq_decode_paged_multi(q, q_dtype, num_seqs, 1, num_q_heads, num_kv_heads, k_pages, v_pages, num_blocks,
+                               block_size, block_tables, max_blocks_per_seq, context_lens, kfmt, vfmt, scale,
+                               num_splits, workspace, workspace_bytes, out, out_dtype, lse, dev_err, stream);
 }

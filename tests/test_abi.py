@@ -190,3 +190,19 @@ def test_dense_window_status_codes_without_launch():
     assert _call_dense(out=12) == tq.TQ_ERR_VALUE                     # not 8-byte aligned
     assert "aligned" in tq._lib.tq_last_error().decode()
     assert _call_dense(B=0) == tq.TQ_OK
+
+
+def test_multi_query_status_codes_without_launch():
+    s = signs(0, 1, 128)
+    f = tq.Format(128, [4], s)
+    L = tq._lib
+
+    def call(NQ=2, Hq=8, Hkv=2, B=2):
+        return L.tq_decode_paged_multi(16, tq.TQ_BF16, B, NQ, Hq, Hkv, 16, 16, 10, 16, 16, 4, 16,
+                                       ctypes.byref(f.c), ctypes.byref(f.c), 0.1, 1, None, 0, 16, tq.TQ_BF16,
+                                       None, None, None)
+    assert call(NQ=0) == tq.TQ_ERR_VALUE
+    assert call(NQ=3) == tq.TQ_ERR_UNSUPPORTED_FORMAT          # 3 queries x 4 q heads > 8 columns
+    assert "pairs per kv head" in L.tq_last_error().decode()
+    assert call(NQ=9, Hq=2, Hkv=2) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert call(B=0) == tq.TQ_OK

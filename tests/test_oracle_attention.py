@@ -188,3 +188,31 @@ def test_window_alone_and_all_empty():
         np.testing.assert_allclose(o[1, h], ob, atol=1e-13)
         assert abs(lse[1, h] - lb) < 1e-12
     assert np.all(o[2] == 0) and np.all(lse[2] == -math.inf)
+
+
+def test_multi_query_is_single_query_at_each_causal_length():
+    """Query i of NQ sees the first ctx - (NQ - 1 - i) tokens: it equals the
+    single-query reference run with that context length; queries left with
+    no token give o = 0, lse = -inf."""
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, d, NQ = 3, 4, 2, 64, 3
+    ctx = np.array([40, 2, 17])
+    f = enc.Format.make(d, [4], signs(11, 1, d))
+    kp, vp, bt = _paged_history(rng, B, Hkv, d, ctx, f)
+    q = rng.standard_normal((B, NQ, Hq, d))
+    o, lse = att.decode_multi_reference(q, kp, vp, bt, ctx, f, f, 0.3, 16)
+    for i in range(NQ):
+        ci = np.maximum(ctx - (NQ - 1 - i), 0)
+        oi, li = att.decode_reference(q[:, i], kp, vp, bt, ci, f, f, 0.3, 16)
+        np.testing.assert_allclose(o[:, i], oi, atol=1e-13)
+        np.testing.assert_array_equal(np.isinf(lse[:, i]), np.isinf(li))
+        fin = np.isfinite(li)
+        np.testing.assert_allclose(lse[:, i][fin], li[fin], atol=1e-13)
+    # sequence 1 has 2 tokens: query 0 sees none, query 1 one, query 2 both
+    assert np.all(o[1, 0] == 0) and np.all(lse[1, 0] == -math.inf)
+    assert np.all(np.isfinite(lse[1, 1:]))
+    # one query is the plain decode
+    o1, l1 = att.decode_multi_reference(q[:, -1:], kp, vp, bt, ctx, f, f, 0.3, 16)
+    ob, lb = att.decode_reference(q[:, -1], kp, vp, bt, ctx, f, f, 0.3, 16)
+    np.testing.assert_allclose(o1[:, 0], ob, atol=1e-13)
+    np.testing.assert_allclose(l1[:, 0], lb, atol=1e-13)
