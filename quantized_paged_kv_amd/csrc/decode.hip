@@ -110,9 +110,6 @@ struct DecodeParams {
   int32_t q_bytes;           // size of q in bytes (< 2^31)
 };
 
-__device__ __forceinline__ void record_error(int32_t* err, int32_t code, int32_t pos) {
-  if (err && atomicCAS(err, 0, code) == 0) atomicExch(err + 1, pos);
-}
 
 __device__ __forceinline__ uint32_t lut_addr(uint32_t packed, uint32_t lane_off, int byte) {
   // [lane_off.byte0, packed.byte(byte), 0, 0] = byte * 256 + lane_off
@@ -126,11 +123,6 @@ __device__ __forceinline__ uint2 lds_u64(const uint8_t* lds, uint32_t addr) {
   return *reinterpret_cast<const uint2*>(lds + addr);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  const uint32_t b = __float_as_uint(x);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
 
 __device__ __forceinline__ float row_ror8(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));

@@ -93,6 +93,21 @@ __host__ __device__ inline double f16_bits_to_f64(uint16_t h) {
   return (h & 0x8000u) ? -v : v;
 }
 
+// ------------------------------------------------------ device helpers
+
+// Device error word: the first reporter sets (code, position); later ones
+// leave it as it is.
+__device__ __forceinline__ void record_error(int32_t* err, int32_t code, int32_t pos) {
+  if (err && atomicCAS(err, 0, code) == 0) atomicExch(err + 1, pos);
+}
+
+// float -> bfloat16 bit pattern, rounded to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
 // ------------------------------------------------------ device lane helpers
 
 // Value of x in lane (lane ^ K), K a power of two below 64, without the

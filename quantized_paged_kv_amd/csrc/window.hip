@@ -47,16 +47,6 @@ struct WindowParams {
   int32_t q_f32, out_f32;
 };
 
-__device__ __forceinline__ void win_record_error(int32_t* err, int32_t code, int32_t pos) {
-  if (err && atomicCAS(err, 0, code) == 0) atomicExch(err + 1, pos);
-}
-
-__device__ __forceinline__ uint16_t win_f32_to_bf16(float x) {   // round to nearest even, NaN kept quiet
-  const uint32_t b = __float_as_uint(x);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
-  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
-
 template <int D>
 struct WinCfg {
   static constexpr int ESZ = 4;
@@ -142,7 +132,7 @@ __global__ __launch_bounds__(kWinThreads) void window_f32_kernel(WindowParams p)
 
   // window length, clamped to [0, cap] (out-of-range lengths reported)
   if (n < 0 || n > p.cap) {
-    if (tid == 0 && kvh == 0) win_record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
+    if (tid == 0 && kvh == 0) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
     n = n < 0 ? 0 : p.cap;
   }
   // q rows of the G heads -> LDS (f32); the history lse values are kept
@@ -350,7 +340,7 @@ __global__ __launch_bounds__(kWinThreads) void window_f32_kernel(WindowParams p)
     if (p.out_f32) {
       *reinterpret_cast<float2*>(static_cast<float*>(p.out) + off) = float2{o0, o1};
     } else {
-      const uint32_t w = (uint32_t)win_f32_to_bf16(o0) | ((uint32_t)win_f32_to_bf16(o1) << 16);
+      const uint32_t w = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
       *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + off) = w;
     }
     if (d == 0 && p.lse) p.lse[(int64_t)s * p.Hq + h] = lse_out;
@@ -449,7 +439,7 @@ __global__ __launch_bounds__(kWinThreads) void window_bf16_kernel(WindowParams p
     }
   }
   if (n < 0 || n > p.cap) {
-    if (tid == 0 && kvh == 0) win_record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
+    if (tid == 0 && kvh == 0) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
     n = n < 0 ? 0 : p.cap;
   }
 #pragma unroll
@@ -590,10 +580,10 @@ __global__ __launch_bounds__(kWinThreads) void window_bf16_kernel(WindowParams p
       for (int r = 0; r < R; ++r) {
         const float e = __builtin_amdgcn_exp2f(x[r] - m_new);   // -inf -> 0
         sum += e;
-        const uint16_t hi = win_f32_to_bf16(e);
+        const uint16_t hi = f32_to_bf16_rne(e);
         const float rest = e - __uint_as_float((uint32_t)hi << 16);
         phi[g * C::TP + lane + 64 * r] = hi;
-        plo[g * C::TP + lane + 64 * r] = win_f32_to_bf16(rest);
+        plo[g * C::TP + lane + 64 * r] = f32_to_bf16_rne(rest);
       }
       sum += lane_xor<32>(sum, lane);
       sum += lane_xor<16>(sum, lane);
@@ -664,8 +654,8 @@ __global__ __launch_bounds__(kWinThreads) void window_bf16_kernel(WindowParams p
     if (p.out_f32) {
       *reinterpret_cast<float4*>(static_cast<float*>(p.out) + out_off) = float4{o[0], o[1], o[2], o[3]};
     } else {
-      const uint2 w = uint2{(uint32_t)win_f32_to_bf16(o[0]) | ((uint32_t)win_f32_to_bf16(o[1]) << 16),
-                            (uint32_t)win_f32_to_bf16(o[2]) | ((uint32_t)win_f32_to_bf16(o[3]) << 16)};
+      const uint2 w = uint2{(uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16),
+                            (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16)};
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + out_off) = w;
     }
     if (wave == 0 && grp == 0 && p.lse) p.lse[(int64_t)s * p.Hq + h0 + col] = lse_out;

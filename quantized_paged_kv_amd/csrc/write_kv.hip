@@ -43,10 +43,6 @@ struct WriteParams {
   int32_t* dev_err;
 };
 
-__device__ __forceinline__ void record_error(int32_t* err, int32_t code, int32_t pos) {
-  if (err && atomicCAS(err, 0, code) == 0) atomicExch(err + 1, pos);
-}
-
 template <int D, bool F32>
 __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
   constexpr int LPR = D / 8;              // lanes per row
