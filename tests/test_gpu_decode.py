@@ -302,3 +302,82 @@ def test_full_size_workloads_sampled(index, seqs, heads_per_seq):
         q, o, l = run_decode(w, kp, vp, kf, vf, P, odt)
         check(w, q, o, l, pairs, odt, ref=ref)
         assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+@pytest.mark.parametrize("S,P", [(64, 1), (65, 3), (130, 4)])
+def test_sequences_beyond_the_first_64(S, P):
+    """The work split holds the first 64 context lengths in registers and
+    reads later ones from memory: 64, 65 and 130 ragged sequences (some
+    empty), every output against the oracle."""
+    g = wl.rng(900 + S, 1)
+    ctx = g.integers(0, 200, size=S)
+    ctx[::9] = 0
+    w = wl.small_decode_workload(900 + S, S, 4, 2, 64, list(ctx), [4], [2], out_dtype="f32", num_splits=P,
+                                 max_blocks_per_seq=(int(ctx.max()) + 15) // 16 + 1)
+    print(f"case S={S} P={P}", flush=True)
+    kp, vp, kf, vf = build_gpu_cache(w)
+    q, o, l = run_decode(w, kp, vp, kf, vf, P, "f32")
+    pairs = [(s, h) for s in range(S) for h in range(4)]
+    check(w, q, o, l, pairs, "f32")
+
+
+def test_context_length_out_of_range_past_the_first_64():
+    """A context length past the capacity, for a sequence beyond the first
+    64, is reported as (INDEX, -1 - s) and clamped to the capacity."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    S = 70
+    ctx = np.full(S, 40)
+    w = wl.small_decode_workload(950, S, 4, 2, 64, list(ctx), [4], [4], out_dtype="f32", num_splits=2,
+                                 max_blocks_per_seq=3)
+    print("case bad context length at s=66", flush=True)
+    kp, vp, kf, vf = build_gpu_cache(w)
+    q = wl.q_values(w)
+    bt = torch.from_numpy(w.block_tables.astype(np.int32)).cuda()
+    cl_host = w.context_lens.astype(np.int32).copy()
+    cl_host[66] = 3 * 16 + 7   # capacity is 3 blocks = 48 tokens
+    cl = torch.from_numpy(cl_host).cuda()
+    err = tq.new_error_word()
+    o, l = tq.decode_paged(to_device(q, w.q_dtype), kp, vp, bt, cl, kf, vf, w.scale, num_splits=2,
+                           out_dtype=torch.float32, dev_err=err)
+    torch.cuda.synchronize()
+    code, pos = err.cpu().tolist()
+    assert code == tq.TQ_ERR_INDEX and pos == -1 - 66
+    # sequence 66 was written with 40 tokens; the clamped length (48) reads 8
+    # more slots of its third block, which hold the sentinel bytes of a
+    # never-written row: only the finiteness of the other sequences is checked
+    o, l = o.cpu().numpy(), l.cpu().numpy()
+    pairs = [(s, h) for s in range(S) if s != 66 for h in range(4)]
+    check(w, q, o, l, pairs, "f32")
+
+
+def test_blocks_at_the_top_of_a_4_gib_pool():
+    """Page pools just under 4 GiB (the largest the 32-bit tile offsets
+    serve): one sequence whose blocks are the last ones of the pool, written
+    and decoded, against the oracle."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    w = wl.small_decode_workload(960, 1, 8, 8, 128, [100], [4], [4], out_dtype="f32", num_splits=2)
+    kf, vf = product_format(w.kfmt), product_format(w.vfmt)
+    tile = kf.tile_bytes()[1]
+    nb = (2 ** 32 - 1) // (8 * tile)          # 8 kv heads per block
+    assert nb * 8 * tile < 2 ** 32 and (nb + 1) * 8 * tile >= 2 ** 32
+    print(f"case 4 GiB pool: {nb} blocks of {8 * tile} B", flush=True)
+    kp = torch.full((nb, 8, tile), 0xA5, dtype=torch.uint8, device="cuda")
+    vp = torch.full((nb, 8, tile), 0xA5, dtype=torch.uint8, device="cuda")
+    bt = np.array([[nb - 1, nb - 3, nb - 7, nb - 2, nb - 5, nb - 4, nb - 6]], dtype=np.int64)
+    n = int(w.context_lens[0])
+    slots = bt[0, np.arange(n) // 16] * 16 + np.arange(n) % 16
+    err = tq.new_error_word()
+    tq.write_kv(to_device(wl.kv_values(w, "k", 0), w.in_dtype), to_device(wl.kv_values(w, "v", 0), w.in_dtype),
+                torch.from_numpy(slots).cuda(), kp, vp, kf, vf, dev_err=err)
+    tq.raise_device_error(err, "write")
+    q = wl.q_values(w)
+    o, l = tq.decode_paged(to_device(q, w.q_dtype), kp, vp, torch.from_numpy(bt.astype(np.int32)).cuda(),
+                           torch.tensor([n], dtype=torch.int32, device="cuda"), kf, vf, w.scale, num_splits=2,
+                           out_dtype=torch.float32, check=True)
+    torch.cuda.synchronize()
+    pairs = [(0, h) for h in range(8)]
+    check(w, q, o.cpu().numpy(), l.cpu().numpy(), pairs, "f32")
+    del kp, vp
+    torch.cuda.empty_cache()
