@@ -1230,14 +1230,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 }
 
 // ----------------------------------------------------------------- merge
-// One wave per (sequence, q head): out = sum_i exp(lse_i - M) o_i /
+// One workgroup per (sequence, q head) row: out = sum_i exp(lse_i - M) o_i /
 // sum_i exp(lse_i - M), lse = M + log(sum_i exp(lse_i - M)), M = max lse_i,
 // over the P partial slots; a -inf lse marks an empty or unused slot.  In
 // decode mode the decode kernel has marked the rows it wrote out directly
 // (kDoneBits in slot 0) and set the slots past a segment's last piece to
-// -inf, so no segment bookkeeping is redone here.  Lane l loads the lse of
-// slot l; the o rows of the first 16 slots are loaded at the same time, those
-// of the live slots among later ones once their lse values are known.
+// -inf, so no segment bookkeeping is redone here.  Every wave reads the lse
+// of slots 0-63 (lane l: slot l) and, at the same time, the o rows of its
+// own 16 slots (wave w: slots 16 w ..), before the slots are known to be live
+// (dead slots hold stale values that get weight 0): with NW = ceil(P / 16)
+// waves (up to 4) a row with up to 64 pieces costs one memory round trip.
+// Slots past 16 NW are read once their lse values are known.  The waves'
+// weighted sums are added in LDS.
 struct MergeParams {
   const float* part_o;
   const float* part_lse;
@@ -1246,27 +1250,24 @@ struct MergeParams {
   int32_t S, H, P, D, out_f32, decode;
 };
 
-constexpr int kMergeRows = 1;   // rows (one per wave) per merge workgroup
-
-__global__ __launch_bounds__(64 * kMergeRows) void merge_kernel(MergeParams p) {
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void merge_kernel(MergeParams p) {
   constexpr int CH = 16;
-  const int64_t sh = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (sh >= (int64_t)p.S * p.H) return;   // (wave-uniform)
+  __shared__ float red[NW > 1 ? NW - 1 : 1][2 * 64 + 1];
+  const int64_t sh = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int P = p.P, D = p.D;
   const float* lse_p = p.part_lse + sh * P;
   const float* o_p = p.part_o + sh * (int64_t)P * D;
   const float lf = lane < P ? lse_p[lane] : -INFINITY;
-  // the o rows of the first CH slots are loaded with the lse values, before
-  // the slots are known to be live (dead slots hold stale values that get
-  // weight 0), so that rows with up to CH pieces take one memory round trip
   float ov0[CH][2];
 #pragma unroll
   for (int k = 0; k < CH; ++k)
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int dim = lane + 64 * r;
-      ov0[k][r] = (k < P && dim < D) ? o_p[(int64_t)k * D + dim] : 0.f;
+      const int slot = CH * w + k;
+      ov0[k][r] = (slot < P && dim < D) ? o_p[(int64_t)slot * D + dim] : 0.f;
     }
   if (p.decode && (uint32_t)__builtin_amdgcn_readfirstlane(__float_as_uint(lf)) == kDoneBits) return;
   auto slot_lse = [&](int i) -> float {   // i uniform
@@ -1279,25 +1280,41 @@ __global__ __launch_bounds__(64 * kMergeRows) void merge_kernel(MergeParams p) {
   float acc[2] = {0.f, 0.f};
   float den = 0.f;
   if (M != -INFINITY) {
-    for (int base = 0; base < P; base += CH) {
-      float w[CH], ov[CH][2];
+    for (int base = CH * w; base < P; base += CH * NW) {
+      float wt[CH], ov[CH][2];
 #pragma unroll
       for (int k = 0; k < CH; ++k) {   // all loads of the chunk before any use
         const float li = base + k < P ? slot_lse(base + k) : -INFINITY;
-        w[k] = li;
+        wt[k] = li;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int dim = lane + 64 * r;
-          ov[k][r] = base == 0 ? ov0[k][r] : ((li != -INFINITY && dim < D) ? o_p[(int64_t)(base + k) * D + dim] : 0.f);
+          ov[k][r] = base == CH * w ? ov0[k][r]
+                                    : ((li != -INFINITY && dim < D) ? o_p[(int64_t)(base + k) * D + dim] : 0.f);
         }
       }
 #pragma unroll
       for (int k = 0; k < CH; ++k) {
-        const float wk = (w[k] == -INFINITY) ? 0.f : expf(w[k] - M);
+        const float wk = (wt[k] == -INFINITY) ? 0.f : expf(wt[k] - M);
         den += wk;
 #pragma unroll
         for (int r = 0; r < 2; ++r) acc[r] = wk > 0.f ? __builtin_fmaf(wk, ov[k][r], acc[r]) : acc[r];
       }
+    }
+  }
+  if constexpr (NW > 1) {   // add the other waves' sums to wave 0's
+    if (w > 0) {
+      red[w - 1][lane] = acc[0];
+      red[w - 1][64 + lane] = acc[1];
+      if (lane == 0) red[w - 1][128] = den;
+    }
+    __syncthreads();
+    if (w > 0) return;
+#pragma unroll
+    for (int v = 0; v < NW - 1; ++v) {
+      acc[0] += red[v][lane];
+      acc[1] += red[v][64 + lane];
+      den += red[v][128];
     }
   }
   const bool empty = !(den > 0.f);
@@ -1311,6 +1328,15 @@ __global__ __launch_bounds__(64 * kMergeRows) void merge_kernel(MergeParams p) {
     else static_cast<uint16_t*>(p.out)[off] = f32_to_bf16_rne(o);
   }
   if (lane == 0 && p.lse) p.lse[sh] = empty ? -INFINITY : M + logf(den);
+}
+
+// One workgroup per row, ceil(P / 16) waves (at most 4).
+void launch_merge(const MergeParams& mp, int64_t rows, hipStream_t st) {
+  const dim3 grid((unsigned)rows);
+  if (mp.P > 48) hipLaunchKernelGGL(merge_kernel<4>, grid, dim3(256), 0, st, mp);
+  else if (mp.P > 32) hipLaunchKernelGGL(merge_kernel<3>, grid, dim3(192), 0, st, mp);
+  else if (mp.P > 16) hipLaunchKernelGGL(merge_kernel<2>, grid, dim3(128), 0, st, mp);
+  else hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(64), 0, st, mp);
 }
 
 template <int D, int KK, int VK>
@@ -1348,9 +1374,7 @@ extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse
   if (num_seqs == 0) return TQ_OK;
   if (!part_out || !part_lse || !out) return set_error(TQ_ERR_VALUE, "NULL merge buffer");
   MergeParams mp = {part_out, part_lse, out, lse, num_seqs, num_heads, num_splits, head_dim, out_dtype == TQ_F32, 0};
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((num_seqs * num_heads + kMergeRows - 1) / kMergeRows)),
-                     dim3(64 * kMergeRows), 0,
-                     reinterpret_cast<hipStream_t>(stream), mp);
+  launch_merge(mp, (int64_t)num_seqs * num_heads, reinterpret_cast<hipStream_t>(stream));
   return launch_status("tq_split_merge launch");
 }
 
@@ -1491,8 +1515,7 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   if (st != TQ_OK || num_splits == 1) return st;
   MergeParams mp = {p.part_o, p.part_lse, out, lse, num_seqs * num_queries, num_q_heads, num_splits, D,
                     p.out_f32, 1};
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((num_seqs * num_queries * num_q_heads + kMergeRows - 1) / kMergeRows)),
-                     dim3(64 * kMergeRows), 0, hs, mp);
+  launch_merge(mp, (int64_t)num_seqs * num_queries * num_q_heads, hs);
   return launch_status("tq_decode_paged merge launch");
 }
 

@@ -132,6 +132,10 @@ SMALL = [
     (128, [3, 2], [4], 8, 2, [33, 300], 1, "f32", "f32", "normal"),
     (64, [3, 2], [2], 6, 3, [5, 400, 129], 3, "bf16", "f32", "t5u"),
     (64, [3, 2], [4], 1, 1, [256], 1, "f32", "f32", "normal"),
+    # many splits: the merge spreads each row's partials over 2 and 4 waves,
+    # and past 64 slots
+    (128, [4], [4], 8, 2, [1, 17, 300, 5000], 24, "bf16", "f32", "normal"),
+    (64, [4], [2], 4, 1, [3000, 40, 1700], 80, "f32", "f32", "normal"),
 ]
 
 
@@ -214,19 +218,22 @@ def test_bad_block_table_entry_reports_and_skips():
                         w.scale, check=True)
 
 
-def test_split_merge_against_oracle_partials():
+@pytest.mark.parametrize("P,d", [(7, 128), (16, 64), (17, 128), (40, 64), (64, 128), (100, 128)])
+def test_split_merge_against_oracle_partials(P, d):
     """tq_split_merge on partials the oracle computed (ragged chunks, empty
-    chunks at -inf) equals the oracle's merge."""
+    chunks at -inf) equals the oracle's merge; split counts on both sides of
+    each 16-slot wave boundary and past 64 slots."""
     import torch
     import quantized_paged_kv_amd as tq
-    rng = np.random.default_rng(3)
-    S, H, P, d = 3, 5, 7, 128
+    print(f"case P={P} d={d}", flush=True)
+    rng = np.random.default_rng(3 + P)
+    S, H = 3, 5
     po = np.zeros((S, H, P, d))
     pl = np.full((S, H, P), -math.inf)
     ref_o = np.zeros((S, H, d))
     ref_l = np.zeros((S, H))
     for s in range(S):
-        n = [300, 17, 1000][s]
+        n = [300, 17, 1600][s]
         K = rng.standard_normal((n, d))
         V = rng.standard_normal((n, d))
         for h in range(H):
