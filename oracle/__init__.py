@@ -29,7 +29,10 @@ function below names the reading it takes.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_*.py`` against closed forms, published values,
-brute force or invariants.  No function is "parity unpinned".
+brute force or invariants.  No function is "parity unpinned".  The QJL
+stage (``qjl.py``) follows a reading of fields the pages only name; it is
+pinned to the published estimator's closed-form mean and variance and to
+its identity / permutation special cases, not to anything on the pages.
 """
 from .codebook import lloyd_max_gaussian, codebook_f16, thresholds_f64, f64_to_f16_bits
 from .rotation import fwht, sylvester_hadamard, rotate, inverse_rotate
@@ -37,6 +40,7 @@ from .encode import Format, tree_sum, encode_rows, quantize_rotated, pack_group,
 from .pages import tile_layout, write_pages, read_rows, reconstruct_sequence
 from .attn import attention, split_partials, merge_partials, decode_reference
 from .ledger import ledger
+from . import qjl
 
 __all__ = [
     "lloyd_max_gaussian", "codebook_f16", "thresholds_f64", "f64_to_f16_bits",
@@ -44,5 +48,5 @@ __all__ = [
     "Format", "tree_sum", "encode_rows", "quantize_rotated", "pack_group", "unpack_group", "row_bytes",
     "tile_layout", "write_pages", "read_rows", "reconstruct_sequence",
     "attention", "split_partials", "merge_partials", "decode_reference",
-    "ledger",
+    "ledger", "qjl",
 ]

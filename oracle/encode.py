@@ -5,7 +5,8 @@ indices and a vector norm ("[MSE indices] ... [vector norm]"); the
 high/low channel groups come from metadata, never from a runtime guess
 [D "System Invariants"].  [D "Format Strategy"]: K and V formats are
 independent.  The QJL sign and residual-norm fields of the recipe row are
-not part of this format (reading R17).
+an option of a K format (reading R29, oracle/qjl.py); the steps below are
+the MSE stage every format has.
 
 Per row x (length d) and per group G of m channels (listed ascending):
 
@@ -38,19 +39,25 @@ class Format:
     group_channels: np.ndarray          # int [d]: group 0 ascending, then group 1 ascending
     codebooks: List[np.ndarray]         # float16 [2^bits] per group, ascending
     signs: np.ndarray                   # int8 [d] of +-1
+    qjl_proj: Optional[np.ndarray] = None   # float32 [num_groups, m, m]: QJL projection per group (R29)
 
     @staticmethod
     def make(head_dim: int, group_bits: Sequence[int], signs: np.ndarray,
-             group_channels: Optional[np.ndarray] = None) -> "Format":
+             group_channels: Optional[np.ndarray] = None, qjl_proj: Optional[np.ndarray] = None) -> "Format":
         ng = len(group_bits)
         if group_channels is None:
             if ng != 1:
                 raise ValueError("two groups need a channel list")
             group_channels = np.arange(head_dim)
         f = Format(head_dim, list(group_bits), np.asarray(group_channels, dtype=np.int64),
-                   [codebook_f16(b) for b in group_bits], np.asarray(signs, dtype=np.int8))
+                   [codebook_f16(b) for b in group_bits], np.asarray(signs, dtype=np.int8),
+                   None if qjl_proj is None else np.asarray(qjl_proj, dtype=np.float32))
         f.validate()
         return f
+
+    @property
+    def qjl(self) -> bool:
+        return self.qjl_proj is not None
 
     @property
     def num_groups(self) -> int:
@@ -90,6 +97,11 @@ class Format:
             c = np.asarray(cb, dtype=np.float16).astype(np.float64)
             if c.shape != (1 << b,) or not np.all(np.isfinite(c)) or np.any(np.diff(c) <= 0):
                 raise ValueError("codebook must be 2^bits finite, strictly ascending levels")
+        if self.qjl_proj is not None:
+            S = np.asarray(self.qjl_proj)
+            m = self.group_size
+            if S.dtype != np.float32 or S.shape != (self.num_groups, m, m) or not np.all(np.isfinite(S)):
+                raise ValueError("QJL projection must be finite float32 [num_groups, m, m]")
 
 
 def tree_sum(v: np.ndarray) -> np.ndarray:
@@ -101,8 +113,15 @@ def tree_sum(v: np.ndarray) -> np.ndarray:
     return v[..., 0]
 
 
-def row_bytes(fmt: Format) -> int:
+def mse_row_bytes(fmt: Format) -> int:
+    """Bytes of a row's packed MSE indices (all groups)."""
     return sum(fmt.group_size * b for b in fmt.group_bits) // 8
+
+
+def row_bytes(fmt: Format) -> int:
+    """Index-plane bytes of a row: MSE indices, then (QJL formats) one sign
+    bit per channel of every group."""
+    return mse_row_bytes(fmt) + (fmt.head_dim // 8 if fmt.qjl else 0)
 
 
 def encode_rows(x: np.ndarray, fmt: Format):

@@ -21,13 +21,20 @@ multiple of 16, the plane is lane-major: with c = row_bytes / 16, byte b of
 row t sits at ((16*(t % 4) + b // c)*4 + t // 4)*c + b % c, i.e. 64 runs of
 4*c bytes, run 16*q + j holding bytes [c*j, c*(j+1)) of rows q, q+4, q+8,
 q+12 in that order; other V formats use the K layout.
+
+QJL K formats (reading R29): each row's index bytes are its MSE indices
+followed by its sign string (oracle/qjl.py), and the norm plane holds the
+vector norms as above followed by the residual norms in the same
+arrangement: residual norm of group g at block_size*row_bytes +
+((G + g)*block_size + norm_slot(t))*2.  QJL is a K stage only.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .encode import Format, encode_rows, pack_row, unpack_row, dequantize_rotated, row_bytes
-from .rotation import inverse_rotate
+from .encode import Format, quantize_rotated, pack_row, unpack_row, dequantize_rotated, row_bytes, mse_row_bytes
+from .rotation import rotate, inverse_rotate
+from . import qjl as _qjl
 
 
 def norm_slot(t):
@@ -59,7 +66,7 @@ def tile_layout(fmt: Format, block_size: int):
         raise ValueError("block_size must be 16")
     rb = row_bytes(fmt)
     norm_off = block_size * rb
-    raw = norm_off + block_size * fmt.num_groups * 2
+    raw = norm_off + block_size * fmt.num_groups * 2 * (2 if fmt.qjl else 1)
     tile = (raw + 15) // 16 * 16
     return rb, norm_off, tile
 
@@ -78,6 +85,8 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
     chunk = lane_chunk(fmt, role)
     if pages.dtype != np.uint8 or pages.shape[1:] != (H, tile):
         raise ValueError("page pool shape does not match the format")
+    if fmt.qjl and role != "k":
+        raise ValueError("the QJL stage is defined for K formats only")
     if slots.shape != (T,):
         raise ValueError("slot_mapping length differs from the number of tokens")
     bad = (slots < 0) | (slots >= nb * block_size)
@@ -88,13 +97,20 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
         raise ValueError("duplicate slots in one write")
     blk = slots // block_size
     off = slots % block_size
-    idx_groups, norms = encode_rows(x, fmt)              # [T, H, m] per group, [T, H, G]
-    data = pack_row(idx_groups, fmt)                      # [T, H, rb]
+    if x.shape[-1] != fmt.head_dim:
+        raise ValueError("row length differs from head_dim")
+    w = rotate(np.asarray(x, dtype=np.float64), fmt.signs)
+    idx_groups, norms = quantize_rotated(w, fmt)          # [T, H, m] per group, [T, H, G]
+    data = pack_row(idx_groups, fmt)                      # [T, H, mse bytes]
+    if fmt.qjl:
+        sbits, gam = _qjl.residual_fields(w, idx_groups, norms, fmt)
+        data = np.concatenate([data, _qjl.pack_signs(sbits)], axis=-1)
+        norms = np.concatenate([norms, gam], axis=-1)     # [T, H, 2G]: vector norms, residual norms
     pos_rows = row_positions(rb, off, chunk)              # [T, rb]
     for h in range(H):
         for b in range(rb):
             pages[blk, h, pos_rows[:, b]] = data[:, h, b]
-        for g in range(fmt.num_groups):
+        for g in range(norms.shape[-1]):
             pos = norm_off + (g * block_size + norm_slot(off)) * 2
             pages[blk, h, pos] = (norms[:, h, g] & 0xFF).astype(np.uint8)
             pages[blk, h, pos + 1] = (norms[:, h, g] >> 8).astype(np.uint8)
@@ -103,7 +119,8 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
 def read_rows(pages: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, head: int, fmt: Format,
               block_size: int, role: str = "k"):
     """Unpack the rows at (blocks[i], offsets[i]) of one kv head ->
-    (index arrays per group, fp16 norm bits [n, G])."""
+    (index arrays per group, fp16 norm bits [n, G]); QJL formats also give
+    (sign bits [n, G, m], residual-norm bits [n, G])."""
     rb, norm_off, tile = tile_layout(fmt, block_size)
     blocks = np.asarray(blocks, dtype=np.int64)
     offsets = np.asarray(offsets, dtype=np.int64)
@@ -111,13 +128,18 @@ def read_rows(pages: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, head: 
     cols = row_positions(rb, offsets, lane_chunk(fmt, role))
     data = np.take_along_axis(t, cols, axis=1)
     idx = unpack_row(data, fmt)
-    norms = np.empty((len(blocks), fmt.num_groups), dtype=np.uint16)
-    for g in range(fmt.num_groups):
+    G = fmt.num_groups
+    nn = 2 * G if fmt.qjl else G
+    norms = np.empty((len(blocks), nn), dtype=np.uint16)
+    for g in range(nn):
         pos = norm_off + (g * block_size + norm_slot(offsets)) * 2
         lo = t[np.arange(len(blocks)), pos].astype(np.uint16)
         hi = t[np.arange(len(blocks)), pos + 1].astype(np.uint16)
         norms[:, g] = lo | (hi << 8)
-    return idx, norms
+    if not fmt.qjl:
+        return idx, norms
+    sbits = _qjl.unpack_signs(data[:, mse_row_bytes(fmt):], G, fmt.group_size)
+    return idx, norms[:, :G], sbits, norms[:, G:]
 
 
 def reconstruct_sequence(pages: np.ndarray, block_table_row: np.ndarray, ctx: int, head: int,
@@ -131,6 +153,8 @@ def reconstruct_sequence(pages: np.ndarray, block_table_row: np.ndarray, ctx: in
     blocks = bt[t // block_size]
     if np.any(blocks < 0) or np.any(blocks >= pages.shape[0]):
         raise IndexError("block table entry outside the page pool")
-    idx, norms = read_rows(pages, blocks, t % block_size, head, fmt, block_size, role)
-    y = dequantize_rotated(idx, norms, fmt)
+    fields = read_rows(pages, blocks, t % block_size, head, fmt, block_size, role)
+    y = dequantize_rotated(fields[0], fields[1], fmt)
+    if fmt.qjl:   # the effective key: MSE reconstruction plus the sketch's term
+        y = y + _qjl.correction_rotated(fields[2], fields[3], fmt)
     return y if rotated else inverse_rotate(y, fmt.signs)
