@@ -95,6 +95,17 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
  *                   ascending unit-variance levels (entries beyond 2^bits
  *                   are ignored).  tq_lloyd_max_codebook() fills them.
  *   signs           +1 / -1 per channel: the seeded signs of the rotation.
+ *   qjl             0, or 1 for a K format whose groups also store the QJL
+ *                   residual stage ([D "Recipe Strategy"]: each group stores
+ *                   [MSE indices][QJL signs][vector norm][residual norm];
+ *                   the pages define only the field names, the stage below
+ *                   is the published quantised Johnson-Lindenstrauss
+ *                   transform).  V formats must have qjl = 0.
+ *   qjl_proj        qjl = 1: DEVICE pointer to the projections, fp32
+ *                   [num_groups][m][m] row-major (entry [g][i][j] multiplies
+ *                   residual channel j of group g into output i), i.i.d.
+ *                   N(0, 1) values drawn by the caller; read by tq_write_kv
+ *                   and tq_decode_paged during the call.  Unused when qjl = 0.
  *
  * Encoding of a row x (head_dim values), per group G of m channels:
  *   w   = H (signs * x)           Sylvester Walsh-Hadamard, natural order,
@@ -105,6 +116,19 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
  *   idx = number of thresholds T_i strictly below w_j
  *   (ss == 0: norm +0 and every index 2^bits/2 - 1)
  * Decoding: rotated value of channel j in G is norm * codebook[idx] / sqrt(m).
+ *
+ * QJL stage (qjl = 1), per group G after the above, fp64, no fused
+ * multiply-add:
+ *   a     = norm (the stored fp16 value) * sqrt(head_dim / m)
+ *   r_j   = w_j - a * codebook[idx_j]                 residual, j in G
+ *   rnorm = fp16 RNE of sqrt(pairwise-tree sum of r_j^2 / head_dim)
+ *   z_i   = sum_j proj[g][i][j] * r_j;  sign bit i = (z_i < 0)
+ * Decoding adds, per group, sqrt(pi/2) / m * rnorm * sum_i (P_g q~_G)_i
+ * (1 - 2 bit_i) to the rotated score q~ . k (q~ the rotated, normalised
+ * query restricted to G): an unbiased estimate of q~ . (y_G - y_hat_G).
+ * The sign bits are fixed by fp64 sums whose order the caller does not
+ * see; an implementation that orders them differently may differ only for
+ * a z_i within rounding of zero.
  */
 typedef struct tq_format {
   int32_t head_dim;
@@ -113,6 +137,8 @@ typedef struct tq_format {
   uint8_t group_channels[TQ_MAX_HEAD_DIM];
   uint16_t codebook[2][16];
   int8_t signs[TQ_MAX_HEAD_DIM];
+  int32_t qjl;
+  const float* qjl_proj;
 } tq_format;
 
 /*
@@ -125,6 +151,12 @@ typedef struct tq_format {
  *            of the row at in-block offset t stored at
  *            16*row_index_bytes + 2*(16*g + 4*(t % 4) + t / 4).
  *            The tile is padded to a multiple of 16 bytes.
+ *   QJL K formats: a row's index bytes are its MSE indices followed by its
+ *            sign bits (head_dim / 8 bytes: group 0's m bits, then group
+ *            1's, output i of a group at bit i, LSB-first); the norm plane
+ *            holds the vector norms as above, then the residual norms in the
+ *            same arrangement (residual norm of group g at norm plane slot
+ *            16*(num_groups + g) + 4*(t % 4) + t / 4).
  *   index plane, K pages: row t at bytes [t*rb, (t+1)*rb), rb = row_index_bytes.
  *   index plane, V pages: when rb is a multiple of 16 (c = rb / 16), byte b
  *            of row t is at ((16*(t % 4) + b / c)*4 + t / 4)*c + b % c: 64 runs
@@ -150,8 +182,9 @@ tq_status tq_format_check(const tq_format* fmt /* host */);
 
 /*
  * Byte math of a format ([D "Serving Route Design"]).  block_size must be 16.
- *   row_index_bytes = sum over groups of m * bits / 8
- *   tile_bytes      = roundup16(16 * row_index_bytes + 16 * num_groups * 2)
+ *   row_index_bytes = sum over groups of m * bits / 8 (+ head_dim / 8 with qjl)
+ *   tile_bytes      = roundup16(16 * row_index_bytes + 16 * num_groups * 2
+ *                               (* 2 with qjl: residual norms))
  */
 tq_status tq_tile_bytes(const tq_format* fmt, int32_t block_size, int32_t* row_index_bytes /* host out */,
                         int32_t* tile_bytes /* host out */);
@@ -171,8 +204,11 @@ tq_status tq_tile_bytes(const tq_format* fmt, int32_t block_size, int32_t* row_i
  *   dev_err       device int32[2] or NULL: a slot outside
  *                 [0, num_blocks*16) records (TQ_ERR_INDEX, token index) and
  *                 that token's rows are not written.
- * Status: VALUE (shapes, dtype, formats, NULLs), UNSUPPORTED_FORMAT
- * (block_size != 16), DEVICE (launch failure), else OK.
+ * A K format with the QJL stage adds a second kernel on the same stream
+ * that computes each written row's residual, signs and residual norm.
+ * Status: VALUE (shapes, dtype, formats, NULLs, qjl set on the V format or
+ * qjl_proj NULL), UNSUPPORTED_FORMAT (block_size != 16), DEVICE (launch
+ * failure), else OK.
  */
 tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype, int64_t num_tokens,
                       int32_t num_kv_heads, const int64_t* slot_mapping, uint8_t* k_pages,
@@ -234,6 +270,11 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * smaller than 4 GiB and num_blocks below 2^31 (else VALUE).
  * Results are reproducible up to the order of floating-point accumulation:
  * blocks are shared dynamically among the waves serving a kv head.
+ * K formats with the QJL stage (qjl = 1; any group layout above, K bits 2-4)
+ * run a separate kernel that adds the sign sketch's term to every score:
+ * one workgroup per (sequence, kv head, split p), split p taking logical
+ * blocks [p*c, (p+1)*c), c = ceil(ceil(context_lens[s] / 16) / P), every
+ * split writing its partial (lse -inf when empty) before the same merge.
  */
 tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
                           int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
@@ -257,7 +298,8 @@ tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
  *   workspace    tq_decode_workspace_bytes(num_seqs * num_queries, ...).
  * Every other argument, error and format is as for tq_decode_paged, which
  * is this call with num_queries = 1.  Served: num_queries * (num_q_heads /
- * num_kv_heads) <= 8 (else UNSUPPORTED_FORMAT).
+ * num_kv_heads) <= 8, and num_queries = 1 for a K format with the QJL stage
+ * (else UNSUPPORTED_FORMAT).
  */
 tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
                                 int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,

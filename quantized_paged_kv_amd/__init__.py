@@ -44,6 +44,8 @@ class tq_format(ctypes.Structure):
         ("group_channels", ctypes.c_uint8 * 128),
         ("codebook", (ctypes.c_uint16 * 16) * 2),
         ("signs", ctypes.c_int8 * 128),
+        ("qjl", ctypes.c_int32),
+        ("qjl_proj", ctypes.c_void_p),
     ]
 
 
@@ -109,7 +111,10 @@ class Format:
     """One tensor's storage format.  K and V carry separate formats."""
 
     def __init__(self, head_dim: int, group_bits: Sequence[int], signs, group_channels=None,
-                 codebooks: Optional[Sequence[np.ndarray]] = None):
+                 codebooks: Optional[Sequence[np.ndarray]] = None, qjl_proj=None):
+        """qjl_proj: for a K format with the QJL residual stage, a contiguous
+        float32 GPU tensor [num_groups, m, m] of N(0, 1) projections (kept
+        alive by this object; the library reads it during each call)."""
         self.head_dim = int(head_dim)
         self.group_bits = [int(b) for b in group_bits]
         self.signs = np.asarray(signs, dtype=np.int8).reshape(-1)
@@ -134,6 +139,15 @@ class Format:
         for j in range(self.head_dim):
             c.group_channels[j] = int(self.group_channels[j])
             c.signs[j] = int(self.signs[j])
+        self.qjl_proj = qjl_proj
+        if qjl_proj is not None:
+            import torch
+            m = self.head_dim // ng
+            if not (qjl_proj.is_cuda and qjl_proj.dtype == torch.float32 and qjl_proj.is_contiguous()
+                    and tuple(qjl_proj.shape) == (ng, m, m)):
+                raise ValueError("qjl_proj must be a contiguous float32 GPU tensor [num_groups, m, m]")
+            c.qjl = 1
+            c.qjl_proj = qjl_proj.data_ptr()
         self.c = c
         _check(_lib.tq_format_check(ctypes.byref(c)))
 
@@ -148,10 +162,17 @@ class Format:
 
     # metadata persistence ([D "Recipe Strategy"]: runtime loads metadata and
     # validates head dimension and group sizes)
+    @property
+    def qjl(self) -> bool:
+        return self.qjl_proj is not None
+
     def to_json(self) -> dict:
-        return {"head_dim": self.head_dim, "group_bits": self.group_bits,
-                "group_channels": self.group_channels.tolist(), "signs": self.signs.tolist(),
-                "codebooks_f16": [c.tolist() for c in self.codebooks]}
+        d = {"head_dim": self.head_dim, "group_bits": self.group_bits,
+             "group_channels": self.group_channels.tolist(), "signs": self.signs.tolist(),
+             "codebooks_f16": [c.tolist() for c in self.codebooks]}
+        if self.qjl_proj is not None:
+            d["qjl_proj"] = self.qjl_proj.cpu().numpy().tolist()
+        return d
 
     def save(self, path: str):
         with open(path, "w") as fh:
@@ -164,8 +185,12 @@ class Format:
         with open(path) as fh:
             d = json.load(fh)
         try:
+            proj = None
+            if "qjl_proj" in d:
+                import torch
+                proj = torch.tensor(np.array(d["qjl_proj"], dtype=np.float32), device="cuda")
             return Format(d["head_dim"], d["group_bits"], d["signs"], d["group_channels"],
-                          [np.array(c, dtype=np.uint16) for c in d["codebooks_f16"]])
+                          [np.array(c, dtype=np.uint16) for c in d["codebooks_f16"]], proj)
         except KeyError as e:
             raise ValueError(f"malformed format metadata: missing {e}") from None
 

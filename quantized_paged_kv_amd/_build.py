@@ -34,6 +34,7 @@ SOURCES = {
     # reduction that waits for the result immediately
     "decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
     "window.hip": [],
+    "qjl.hip": ["-ffp-contract=off"],
 }
 
 

@@ -1405,7 +1405,10 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
     return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "more than 8 (query, q head) pairs per kv head");
   const int G = num_queries * Gr;   // matrix-core columns used per kv head
   const int kk = format_kind_k(kfmt), vk = format_kind_v(vfmt);
-  if (kk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
+  if (vfmt->qjl) return set_error(TQ_ERR_VALUE, "the QJL stage is defined for K formats only");
+  if (kfmt->qjl && num_queries != 1)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take one query per sequence");
+  if (kk < 0 && !kfmt->qjl) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
   if (vk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this V format (served: 4-bit, 2-bit)");
   const int D = kfmt->head_dim;
   if (num_seqs == 0) return TQ_OK;
@@ -1424,6 +1427,45 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   if (num_blocks >= (1ll << 31) || k_pool > 0xFFFFFFFFll || v_pool > 0xFFFFFFFFll)
     return set_error(TQ_ERR_VALUE, "each page pool must be smaller than 4 GiB");
   if (q_bytes >= (1ll << 31)) return set_error(TQ_ERR_VALUE, "q must be smaller than 2 GiB");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+
+  if (kfmt->qjl) {   // sketch term on every score: the QJL decode kernel, then the generic merge
+    if ((reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15)
+      return set_error(TQ_ERR_VALUE, "page pools must be 16-byte aligned");
+    DevFormat kf, vf;
+    make_dev_format(kfmt, &kf);
+    make_dev_format(vfmt, &vf);
+    if (vf.row_bytes % 16 == 0) vf.chunk = vf.row_bytes / 16;   // lane-major V index plane
+    QjlDecodeArgs qa = {};
+    qa.q = q;
+    qa.q_f32 = q_dtype == TQ_F32;
+    qa.S = num_seqs;
+    qa.Hq = num_q_heads;
+    qa.Hkv = num_kv_heads;
+    qa.G = Gr;
+    qa.k_pages = k_pages;
+    qa.v_pages = v_pages;
+    qa.num_blocks = num_blocks;
+    qa.block_tables = block_tables;
+    qa.max_blocks = max_blocks_per_seq;
+    qa.context_lens = context_lens;
+    qa.proj = kfmt->qjl_proj;
+    qa.scale = scale;
+    qa.P = num_splits;
+    qa.out = out;
+    qa.out_f32 = out_dtype == TQ_F32;
+    qa.lse = lse;
+    qa.dev_err = dev_err;
+    if (num_splits > 1) {
+      qa.part_o = static_cast<float*>(workspace);
+      qa.part_lse = qa.part_o + (int64_t)num_seqs * num_q_heads * num_splits * D;
+    }
+    st = launch_qjl_decode(qa, kf, vf, hs);
+    if (st != TQ_OK || num_splits == 1) return st;
+    MergeParams mp = {qa.part_o, qa.part_lse, out, lse, num_seqs, num_q_heads, num_splits, D, qa.out_f32, 0};
+    launch_merge(mp, (int64_t)num_seqs * num_q_heads, hs);
+    return launch_status("tq_decode_paged merge launch");
+  }
 
   DecodeParams p = {};
   p.q = q;
@@ -1503,7 +1545,6 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (int64_t)num_seqs * num_queries * num_q_heads * num_splits * D;
   }
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 #define TQ_LAUNCH(DD, KKK, VVV) \
   if (D == DD && kk == KKK && vk == VVV) launch_decode<DD, KKK, VVV>(p, hs);
   TQ_LAUNCH(128, K4, V4) TQ_LAUNCH(128, K4, V2) TQ_LAUNCH(128, K2, V4) TQ_LAUNCH(128, K2, V2)

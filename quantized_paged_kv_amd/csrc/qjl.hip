@@ -1,0 +1,545 @@
+// QJL residual stage of K channel groups: the write-side kernel that adds
+// each row's sign sketch and residual norm, and the decode kernel that adds
+// the sketch's estimate to every score.
+//
+// [D "Recipe Strategy"]: each group of a recipe row stores [MSE indices]
+// [QJL signs][vector norm][residual norm].  The pages give the fields, not
+// the stage; the one implemented is the quantised Johnson-Lindenstrauss
+// transform as published with TurboQuant's inner-product quantiser: the
+// group's MSE residual r is projected by a caller-supplied m x m Gaussian
+// matrix S, the signs of S r are stored with |r|, and a query q adds
+// sqrt(pi/2) / m * |r| * <S q, signs> to its score (unbiased for <q, r>).
+//
+// Write side (fp64, no fused multiply-add outside the projection sums): the
+// rotation is recomputed with the same butterflies as the MSE stage, the
+// stored indices and norm are read back from the tile the MSE kernel wrote
+// just before on the same stream, and
+//   r_j = w_j - (norm * sqrt(d/m)) * c[idx_j],  rnorm = fp16(sqrt(tree(r^2) / d)),
+//   bit_i = (sum_j S[i][j] r_j < 0).
+//
+// Decode: one 8-wave workgroup per (sequence, kv head, split).  Every wave
+// takes every 8th block of the split, stages the K and V tiles in LDS and
+// runs the scores on the matrix cores as one contraction over 2d "channels":
+// [rotated q | projected q] (fp16 high + low parts, columns 0-7 / 8-15)
+// against [codebook values | +-rnorm] of the 16 tokens (both exact in fp16),
+// one fp32 accumulator per MSE group and one for the sketch; softmax in the
+// exp2 domain; P.V on the matrix cores with the V codebook values.  The
+// waves' states are combined in LDS, the result is rotated back and written
+// out, or as a partial for the split merge.
+#pragma clang fp contract(off)
+
+#include <math.h>
+
+#include <algorithm>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void wave_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+__device__ __forceinline__ int norm_slot(int t) { return 4 * (t & 3) + (t >> 2); }
+
+// ------------------------------------------------------------------ write
+
+constexpr int kWriteWaves = 4;
+constexpr int kProjMax = 128 * 129;   // padded projection floats (one group of 128, or two of 64)
+
+struct QjlWriteParams {
+  QjlWriteArgs a;
+  DevFormat f;
+};
+
+// fp64 sum over the lanes of aligned groups of `span` lanes (span a power of
+// two <= 64) by the pairwise tree: level o adds lane l ^ o, which is the
+// adjacent-pairs-first order of the group's elements.
+__device__ __forceinline__ double group_tree_sum(double v, int span, int lane) {
+  if (span > 1) v += lane_xor_d<1>(v, lane);
+  if (span > 2) v += lane_xor_d<2>(v, lane);
+  if (span > 4) v += lane_xor_d<4>(v, lane);
+  if (span > 8) v += lane_xor_d<8>(v, lane);
+  if (span > 16) v += lane_xor_d<16>(v, lane);
+  if (span > 32) v += lane_xor_d<32>(v, lane);
+  return v;
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(64 * kWriteWaves) void qjl_write_kernel(QjlWriteParams p) {
+  constexpr int KP = D / 64;   // positions (and projection outputs) per lane
+  __shared__ float sproj[kProjMax];
+  __shared__ double sw[kWriteWaves][D];
+  __shared__ double sr[kWriteWaves][D];
+  const DevFormat& f = p.f;
+  const int m = f.m, ng = f.ng;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // projection rows padded to m + 1 floats (lanes read different rows)
+  for (int e = tid; e < ng * m * m; e += 64 * kWriteWaves) {
+    const int row = e / m, j = e - row * m;
+    sproj[row * (m + 1) + j] = p.a.proj[e];
+  }
+  __syncthreads();
+  const int64_t rows = p.a.num_tokens * p.a.H;
+  double* w = sw[wave];
+  double* r = sr[wave];
+  for (int64_t row = (int64_t)blockIdx.x * kWriteWaves + wave; row < rows;
+       row += (int64_t)gridDim.x * kWriteWaves) {
+    const int64_t tok = row / p.a.H;
+    const int h = (int)(row - tok * p.a.H);
+    const int64_t slot = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)p.a.slots[tok]) |
+                         ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)p.a.slots[tok] >> 32)) << 32);
+    if (slot < 0 || slot >= p.a.num_slots) continue;   // reported by the MSE write (wave-uniform)
+    uint8_t* tile = p.a.pages + ((slot >> 4) * p.a.H + h) * (int64_t)f.tile_bytes;
+    const int offs = (int)(slot & 15);
+    const uint8_t* rowb = tile + offs * f.row_bytes;
+    // signs, then the butterflies h = 1, 2, ..., D/2 in fp64
+    for (int c = lane; c < D; c += 64) {
+      double x;
+      if constexpr (F32) x = (double)static_cast<const float*>(p.a.src)[row * D + c];
+      else x = (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(p.a.src)[row * D + c] << 16);
+      if ((f.sign_bits[c >> 5] >> (c & 31)) & 1u) x = -x;
+      w[c] = x;
+    }
+    for (int hs = 1; hs < D; hs <<= 1) {
+      wave_fence();
+      for (int pr = lane; pr < D / 2; pr += 64) {
+        const int i = (pr / hs) * 2 * hs + (pr % hs), j = i + hs;
+        const double a0 = w[i], b0 = w[j];
+        w[i] = a0 + b0;
+        w[j] = a0 - b0;
+      }
+    }
+    wave_fence();
+    // residual at group position P = lane + 64 k (group P / m, position P % m)
+    double rv[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int P = lane + 64 * k;
+      const int g = P / m, pos = P - g * m;
+      const int bits = f.bits[g];
+      const int bit0 = pos * bits;
+      const int byte = f.grp_byte_off[g] + (bit0 >> 3);
+      const uint32_t two = (uint32_t)rowb[byte] | ((uint32_t)rowb[byte + 1] << 8);
+      const int code = (int)((two >> (bit0 & 7)) & ((1u << bits) - 1u));
+      const uint16_t nb = *reinterpret_cast<const uint16_t*>(tile + f.norm_off + 2 * (16 * g + norm_slot(offs)));
+      const double a = f16_bits_to_f64(nb) * p.a.kappa;
+      const double t = a * f16_bits_to_f64(f.cb[g][code]);
+      rv[k] = w[f.ch[P]] - t;
+      r[P] = rv[k];
+    }
+    // residual norm per group: pairwise tree over the group's positions
+    double ss[2] = {0.0, 0.0};
+    if (m >= 64) {
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        const double v = group_tree_sum(rv[k] * rv[k], 64, lane);
+        const int g = (64 * k) / m;
+        ss[g] = (64 * k) % m == 0 ? v : ss[g] + v;   // m = 128: (0..63) + (64..127), the tree's last level
+      }
+    } else {   // m = 32 (D = 64, two groups): lanes 0-31 group 0, 32-63 group 1
+      const double v = group_tree_sum(rv[0] * rv[0], 32, lane);
+      ss[0] = __shfl(v, 0);
+      ss[1] = __shfl(v, 32);
+    }
+    wave_fence();
+    // projection z_i = sum_j S[i][j] r_j (fp64 fma in j order), signs by ballot
+    uint64_t neg[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int O = lane + 64 * k;
+      const int g = O / m, i = O - g * m;
+      const float* srow = sproj + (g * m + i) * (m + 1);
+      const double* rg = r + g * m;
+      double z = 0.0;
+      for (int j = 0; j < m; ++j) z = __builtin_fma((double)srow[j], rg[j], z);
+      neg[k] = __builtin_amdgcn_ballot_w64(z < 0.0);
+    }
+    uint8_t* sgn = tile + offs * f.row_bytes + f.sign_off;
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+      if (lane < 8) sgn[8 * k + lane] = (uint8_t)(neg[k] >> (8 * lane));
+    if (lane < ng) {
+      const double s = lane == 0 ? ss[0] : ss[1];
+      *reinterpret_cast<uint16_t*>(tile + f.rnorm_off + 2 * (16 * lane + norm_slot(offs))) =
+          f64_to_f16_rne(__builtin_sqrt(s / (double)D));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode
+
+constexpr int kDecWaves = 8;
+constexpr int kKTileMax = 1536;
+constexpr int kVTileMax = 1088;
+
+struct QjlDecParams {
+  QjlDecodeArgs a;
+  DevFormat kf, vf;
+  float f_mse, f_q;   // score factors (log2 units): scale log2e / sqrt(m d), scale log2e sqrt(pi/2) / (m sqrt d)
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams p) {
+  constexpr int NT = D / 32;        // MSE contractions of 32 channels (and as many sketch ones)
+  constexpr int ND = D / 16;        // P.V contractions of 16 dims
+  __shared__ float qg[8][D];        // rotated query (unnormalised), then in group position order
+  __shared__ float qt[8][D];        // scratch: rotation, then the projected query
+  __shared__ half8_t bop[2 * NT][64];
+  __shared__ float wmse[8], wq[8];
+  __shared__ uint16_t cbk[2][16], cbv[16];
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[kDecWaves][kKTileMax];
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[kDecWaves][kVTileMax];
+  __shared__ float st_o[kDecWaves][8][D];
+  __shared__ float st_ml[kDecWaves][2][8];
+
+  const QjlDecodeArgs& a = p.a;
+  const DevFormat& kf = p.kf;
+  const DevFormat& vf = p.vf;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = a.P;
+  const int sp = blockIdx.x % P;
+  const int rest = blockIdx.x / P;
+  const int kvh = rest % a.Hkv;
+  const int s = rest / a.Hkv;
+  const int G = a.G;
+  const int cap = a.max_blocks * 16;
+  const int ctx_raw = a.context_lens[s];
+  if (sp == 0 && kvh == 0 && tid == 0 && (ctx_raw < 0 || ctx_raw > cap)) record_error(a.dev_err, TQ_ERR_INDEX, -1 - s);
+  const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > cap ? cap : ctx_raw);
+  const int nb = (ctx + 15) >> 4;
+  const int cb = (nb + P - 1) / P;
+  const int b0 = sp * cb;
+  const int b1 = std::min(nb, b0 + cb);
+
+  // ---- query: load, K signs, Walsh-Hadamard (fp32), group order
+  for (int e = tid; e < 8 * D; e += 64 * kDecWaves) {
+    const int g = e / D, c = e - g * D;
+    float x = 0.f;
+    if (g < G) {
+      const int64_t off = ((int64_t)s * a.Hq + kvh * G + g) * D + c;
+      x = a.q_f32 ? static_cast<const float*>(a.q)[off]
+                  : __uint_as_float((uint32_t)static_cast<const uint16_t*>(a.q)[off] << 16);
+      if ((kf.sign_bits[c >> 5] >> (c & 31)) & 1u) x = -x;
+    }
+    qt[g][c] = x;
+  }
+  if (tid < 32) {
+    const int g = tid >> 4, i = tid & 15;
+    cbk[g][i] = kf.cb[g][i];
+  } else if (tid < 48) {
+    cbv[tid - 32] = vf.cb[0][tid - 32];
+  }
+  for (int hs = 1; hs < D; hs <<= 1) {
+    __syncthreads();
+    for (int e = tid; e < 8 * D / 2; e += 64 * kDecWaves) {
+      const int g = e / (D / 2), pr = e - g * (D / 2);
+      const int i = (pr / hs) * 2 * hs + (pr % hs), j = i + hs;
+      const float x0 = qt[g][i], x1 = qt[g][j];
+      qt[g][i] = x0 + x1;
+      qt[g][j] = x0 - x1;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < 8 * D; e += 64 * kDecWaves) {
+    const int g = e / D, c = e - g * D;
+    qg[g][c] = qt[g][kf.ch[c]];
+  }
+  __syncthreads();
+  // ---- projected query u[g][O] = sum_j S[grp][i][j] qg[g][grp m + j], O = grp m + i
+  {
+    const int m = kf.m;
+    for (int e = tid; e < 8 * D; e += 64 * kDecWaves) {
+      const int g = e / D, O = e - g * D;
+      const int grp = O / m, i = O - grp * m;
+      const float4* srow = reinterpret_cast<const float4*>(a.proj + ((int64_t)grp * m + i) * m);
+      const float* qv = qg[g] + grp * m;
+      float acc = 0.f;
+      for (int j4 = 0; j4 < m / 4; ++j4) {
+        const float4 sv = srow[j4];
+        acc = __builtin_fmaf(sv.x, qv[4 * j4], acc);
+        acc = __builtin_fmaf(sv.y, qv[4 * j4 + 1], acc);
+        acc = __builtin_fmaf(sv.z, qv[4 * j4 + 2], acc);
+        acc = __builtin_fmaf(sv.w, qv[4 * j4 + 3], acc);
+      }
+      qt[g][O] = acc;
+    }
+  }
+  __syncthreads();
+  // ---- per q head: power-of-two scales that put each half of the operand in
+  // fp16 range (largest magnitude in [2^14, 2^15)), and the score factors
+  {
+    const int g = wave;   // 8 waves, 8 heads
+    float am = 0.f, au = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      am = fmaxf(am, fabsf(qg[g][c]));
+      au = fmaxf(au, fabsf(qt[g][c]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      am = fmaxf(am, __shfl_xor(am, o));
+      au = fmaxf(au, __shfl_xor(au, o));
+    }
+    int em = 0, eu = 0;
+    if (am > 0.f) frexpf(am, &em);
+    if (au > 0.f) frexpf(au, &eu);
+    const float pm = ldexpf(1.f, 15 - em), pu = ldexpf(1.f, 15 - eu);
+    for (int c = lane; c < D; c += 64) {
+      qg[g][c] *= pm;
+      qt[g][c] *= pu;
+    }
+    if (lane == 0) {
+      wmse[g] = ldexpf(p.f_mse, em - 15);
+      wq[g] = ldexpf(p.f_q, eu - 15);
+    }
+  }
+  __syncthreads();
+  // ---- B operands: operand t, lane l: column l % 16 (head (l % 16) & 7, high
+  // part below 8, low part from 8), channels 32 t + 8 (l / 16) + e
+  for (int e = tid; e < 2 * NT * 64; e += 64 * kDecWaves) {
+    const int t = e >> 6, l = e & 63;
+    const int col = l & 15, g = col & 7;
+    const bool lo = col >= 8;
+    half8_t v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = 32 * t + 8 * (l >> 4) + k;
+      const float x = c < D ? qg[g][c] : qt[g][c - D];
+      const _Float16 hi = (_Float16)x;
+      const _Float16 rest16 = (_Float16)(x - (float)hi);
+      v[k] = g < G ? (lo ? rest16 : hi) : (_Float16)0.f;
+    }
+    bop[t][l] = v;
+  }
+  __syncthreads();
+
+  // ---- blocks of this split, every 8th to each wave
+  const int col = lane & 15, gcol = col & 7, ta = lane >> 4;
+  const float w_m = wmse[gcol], w_q = wq[gcol];
+  float m_run = -INFINITY, l_run = 0.f;
+  float4_t o_acc[ND];
+#pragma unroll
+  for (int u = 0; u < ND; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint8_t* kt = ktile[wave];
+  uint8_t* vt = vtile[wave];
+  const int krb = kf.row_bytes, m = kf.m;
+  for (int b = b0 + wave; b < b1; b += kDecWaves) {
+    const int raw = __builtin_amdgcn_readfirstlane(a.block_tables[(int64_t)s * a.max_blocks + b]);
+    const bool bad = raw < 0 || (int64_t)raw >= a.num_blocks;
+    if (bad) {
+      if (lane == 0) record_error(a.dev_err, TQ_ERR_INDEX, s * a.max_blocks + b);
+      continue;   // wave-uniform
+    }
+    const uint8_t* ksrc = a.k_pages + ((int64_t)raw * a.Hkv + kvh) * kf.tile_bytes;
+    const uint8_t* vsrc = a.v_pages + ((int64_t)raw * a.Hkv + kvh) * vf.tile_bytes;
+    wave_fence();   // the previous block's reads of the staging area are done
+    for (int off = 16 * lane; off < kf.tile_bytes; off += 1024)
+      *reinterpret_cast<uint4*>(kt + off) = *reinterpret_cast<const uint4*>(ksrc + off);
+    for (int off = 16 * lane; off < vf.tile_bytes; off += 1024)
+      *reinterpret_cast<uint4*>(vt + off) = *reinterpret_cast<const uint4*>(vsrc + off);
+    wave_fence();
+
+    // scores: A row = token `col` (lane % 16), channels 32 t + 8 ta + e
+    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, accq = acc0;
+    const uint8_t* krow = kt + col * krb;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int P0 = 32 * t + 8 * ta;
+      const int g = P0 / m, pos = P0 - g * m;
+      const int bits = kf.bits[g];
+      const uint8_t* src = krow + kf.grp_byte_off[g] + pos * bits / 8;   // 8 codes = `bits` whole bytes
+      uint32_t word = 0;
+      for (int y = 0; y < bits; ++y) word |= (uint32_t)src[y] << (8 * y);
+      u32x4_t av;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t c0 = (word >> (bits * 2 * e2)) & ((1u << bits) - 1u);
+        const uint32_t c1 = (word >> (bits * (2 * e2 + 1))) & ((1u << bits) - 1u);
+        av[e2] = (uint32_t)cbk[g][c0] | ((uint32_t)cbk[g][c1] << 16);
+      }
+      const half8_t ah = __builtin_bit_cast(half8_t, av);
+      if (g == 0) acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bop[t][lane], acc0, 0, 0, 0);
+      else acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bop[t][lane], acc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int O0 = 32 * t + 8 * ta;
+      const int g = O0 / m;
+      const uint32_t gam = *reinterpret_cast<const uint16_t*>(kt + kf.rnorm_off + 2 * (16 * g + norm_slot(col)));
+      const uint32_t sb = krow[kf.sign_off + (O0 >> 3)];
+      u32x4_t av;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        av[e2] = (gam | (((sb >> (2 * e2)) & 1u) << 15)) | ((gam | (((sb >> (2 * e2 + 1)) & 1u) << 15)) << 16);
+      accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bop[NT + t][lane], accq, 0, 0, 0);
+    }
+    // lane holds tokens 4 ta + i of column col; high + low columns summed
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = 4 * ta + i;
+      const float f0 = acc0[i] + lane_xor<8>(acc0[i], lane);
+      const float f1 = acc1[i] + lane_xor<8>(acc1[i], lane);
+      const float fq = accq[i] + lane_xor<8>(accq[i], lane);
+      const float n0 = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(kt + kf.norm_off + 2 * norm_slot(tk)));
+      float v = n0 * f0;
+      if (kf.ng > 1) {
+        const float n1 = (float)__builtin_bit_cast(
+            _Float16, *reinterpret_cast<const uint16_t*>(kt + kf.norm_off + 2 * (16 + norm_slot(tk))));
+        v = __builtin_fmaf(n1, f1, v);
+      }
+      v = __builtin_fmaf(fq, w_q, v * w_m);
+      sc[i] = (16 * b + tk < ctx) ? v : -INFINITY;
+    }
+    // online softmax per column (exp2 domain)
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, lane_xor<16>(bm, lane));
+    bm = fmaxf(bm, lane_xor<32>(bm, lane));
+    // (no lane leaves here: the matrix-core steps below run with every lane)
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int u = 0; u < ND; ++u) o_acc[u] *= alpha;
+    half4_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = 4 * ta + i;
+      const float pr = sc[i] == -INFINITY ? 0.f : exp2f(sc[i] - m_use);
+      l_run += pr;
+      const float vn = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(vt + vf.norm_off + 2 * norm_slot(tk)));
+      pb[i] = pr > 0.f ? (_Float16)(pr * vn) : (_Float16)0.f;
+    }
+    // P.V: A = V codes of dim 16 u + col for tokens 4 ta + i
+    const int vbits = vf.bits[0], vc = vf.chunk, vrb = vf.row_bytes;
+#pragma unroll
+    for (int u = 0; u < ND; ++u) {
+      const int j = 16 * u + col;
+      const int bit0 = j * vbits, bb = bit0 >> 3, sh = bit0 & 7;
+      half4_t avv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tk = 4 * ta + i;
+        const int pos = vc == 0 ? tk * vrb + bb : ((16 * (tk & 3) + bb / vc) * 4 + (tk >> 2)) * vc + bb % vc;
+        const uint32_t code = ((uint32_t)vt[pos] >> sh) & ((1u << vbits) - 1u);
+        avv[i] = __builtin_bit_cast(_Float16, cbv[code]);
+      }
+      o_acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(avv, pb, o_acc[u], 0, 0, 0);
+    }
+  }
+  // ---- wave states: column sums over the 4 token groups
+  l_run += lane_xor<16>(l_run, lane);
+  l_run += lane_xor<32>(l_run, lane);
+  if (col < 8) {
+#pragma unroll
+    for (int u = 0; u < ND; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_o[wave][col][16 * u + 4 * ta + i] = o_acc[u][i];
+    if (ta == 0) {
+      st_ml[wave][0][col] = m_run;
+      st_ml[wave][1][col] = l_run;
+    }
+  }
+  __syncthreads();
+  // ---- combine, V's 1/sqrt(d), inverse rotation H(.) / sqrt(d) with V signs
+  for (int e = tid; e < 8 * D; e += 64 * kDecWaves) {
+    const int g = e / D, j = e - g * D;
+    float M = -INFINITY;
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, st_ml[w][0][g]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float mw = st_ml[w][0][g];
+        if (mw == -INFINITY) continue;
+        const float f = exp2f(mw - M);
+        L = __builtin_fmaf(st_ml[w][1][g], f, L);
+        O = __builtin_fmaf(st_o[w][g][j], f, O);
+      }
+    }
+    qt[g][j] = L > 0.f ? O / L : 0.f;
+  }
+  for (int hs = 1; hs < D; hs <<= 1) {
+    __syncthreads();
+    for (int e = tid; e < 8 * D / 2; e += 64 * kDecWaves) {
+      const int g = e / (D / 2), pr = e - g * (D / 2);
+      const int i = (pr / hs) * 2 * hs + (pr % hs), j = i + hs;
+      const float x0 = qt[g][i], x1 = qt[g][j];
+      qt[g][i] = x0 + x1;
+      qt[g][j] = x0 - x1;
+    }
+  }
+  __syncthreads();
+  const float inv_d = 1.0f / (float)D;
+  for (int e = tid; e < G * D; e += 64 * kDecWaves) {
+    const int g = e / D, j = e - g * D;
+    float M = -INFINITY, L = 0.f;
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, st_ml[w][0][g]);
+    if (M != -INFINITY)
+      for (int w = 0; w < kDecWaves; ++w)
+        if (st_ml[w][0][g] != -INFINITY) L = __builtin_fmaf(st_ml[w][1][g], exp2f(st_ml[w][0][g] - M), L);
+    float o = qt[g][j] * inv_d;
+    if ((vf.sign_bits[j >> 5] >> (j & 31)) & 1u) o = -o;
+    const bool empty = !(L > 0.f);
+    if (empty) o = 0.f;
+    const int64_t row = (int64_t)s * a.Hq + kvh * G + g;
+    const float lse = empty ? -INFINITY : (M + log2f(L)) * 0.6931471805599453f;
+    if (P == 1) {
+      if (a.out_f32) static_cast<float*>(a.out)[row * D + j] = o;
+      else static_cast<uint16_t*>(a.out)[row * D + j] = f32_to_bf16_rne(o);
+      if (j == 0 && a.lse) a.lse[row] = lse;
+    } else {
+      a.part_o[(row * P + sp) * D + j] = o;
+      if (j == 0) a.part_lse[row * P + sp] = lse;
+    }
+  }
+}
+
+}  // namespace
+
+tq_status launch_qjl_write(const QjlWriteArgs& a, const DevFormat& kf, hipStream_t st) {
+  QjlWriteParams p;
+  p.a = a;
+  p.f = kf;
+  const int64_t rows = a.num_tokens * a.H;
+  if (rows == 0) return TQ_OK;
+  const int64_t wgs = std::min<int64_t>((rows + kWriteWaves - 1) / kWriteWaves, (int64_t)device_cus() * 4);
+  const dim3 grid((unsigned)wgs);
+  if (kf.d == 128) {
+    if (a.f32) hipLaunchKernelGGL((qjl_write_kernel<128, true>), grid, dim3(64 * kWriteWaves), 0, st, p);
+    else hipLaunchKernelGGL((qjl_write_kernel<128, false>), grid, dim3(64 * kWriteWaves), 0, st, p);
+  } else {
+    if (a.f32) hipLaunchKernelGGL((qjl_write_kernel<64, true>), grid, dim3(64 * kWriteWaves), 0, st, p);
+    else hipLaunchKernelGGL((qjl_write_kernel<64, false>), grid, dim3(64 * kWriteWaves), 0, st, p);
+  }
+  return launch_status("tq_write_kv QJL launch");
+}
+
+tq_status launch_qjl_decode(const QjlDecodeArgs& a, const DevFormat& kf, const DevFormat& vf, hipStream_t st) {
+  if (kf.tile_bytes > kKTileMax || vf.tile_bytes > kVTileMax)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "QJL decode: tile larger than the staging area");
+  if (a.G < 1 || a.G > 8) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "QJL decode: more than 8 q heads per kv head");
+  QjlDecParams p;
+  p.a = a;
+  p.kf = kf;
+  p.vf = vf;
+  const double log2e = 1.4426950408889634;
+  const double d = kf.d, m = kf.m;
+  p.f_mse = (float)((double)a.scale * log2e / sqrt(m * d));
+  p.f_q = (float)((double)a.scale * log2e * sqrt(M_PI / 2.0) / (m * sqrt(d)));
+  const int64_t n_wg = (int64_t)a.S * a.Hkv * a.P;
+  if (n_wg == 0) return TQ_OK;
+  if (n_wg >= ((int64_t)1 << 31)) return set_error(TQ_ERR_VALUE, "QJL decode: too many workgroups");
+  const dim3 grid((unsigned)n_wg);
+  if (kf.d == 128) hipLaunchKernelGGL((qjl_decode_kernel<128>), grid, dim3(64 * kDecWaves), 0, st, p);
+  else hipLaunchKernelGGL((qjl_decode_kernel<64>), grid, dim3(64 * kDecWaves), 0, st, p);
+  return launch_status("tq_decode_paged QJL launch");
+}
+
+}  // namespace tq

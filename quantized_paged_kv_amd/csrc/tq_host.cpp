@@ -60,18 +60,22 @@ tq_status check_format(const tq_format* f, const char* which) {
       prev = v;
     }
   }
+  if (f->qjl != 0 && f->qjl != 1) return set_error(TQ_ERR_VALUE, w + " qjl must be 0 or 1");
+  if (f->qjl && !f->qjl_proj) return set_error(TQ_ERR_VALUE, w + " qjl_proj is NULL");
   return TQ_OK;
 }
 
-int row_index_bytes(const tq_format* f) {
+int mse_row_bytes(const tq_format* f) {
   const int m = f->head_dim / f->num_groups;
   int bits = 0;
   for (int g = 0; g < f->num_groups; ++g) bits += m * f->group_bits[g];
   return bits / 8;
 }
 
+int row_index_bytes(const tq_format* f) { return mse_row_bytes(f) + (f->qjl ? f->head_dim / 8 : 0); }
+
 int tile_bytes_of(const tq_format* f) {
-  const int raw = TQ_BLOCK_SIZE * row_index_bytes(f) + TQ_BLOCK_SIZE * f->num_groups * 2;
+  const int raw = TQ_BLOCK_SIZE * row_index_bytes(f) + TQ_BLOCK_SIZE * f->num_groups * 2 * (f->qjl ? 2 : 1);
   return (raw + 15) / 16 * 16;
 }
 
@@ -112,6 +116,9 @@ void make_dev_format(const tq_format* f, DevFormat* o) {
   o->row_bytes = row_index_bytes(f);
   o->tile_bytes = tile_bytes_of(f);
   o->norm_off = TQ_BLOCK_SIZE * o->row_bytes;
+  o->qjl = f->qjl;
+  o->sign_off = mse_row_bytes(f);
+  o->rnorm_off = o->norm_off + TQ_BLOCK_SIZE * f->num_groups * 2;
 }
 
 // ------------------------------------------------------------ Lloyd-Max

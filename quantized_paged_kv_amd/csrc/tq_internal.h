@@ -14,6 +14,7 @@ namespace tq {
 tq_status set_error(tq_status st, const std::string& msg);
 tq_status check_format(const tq_format* f, const char* which);
 int row_index_bytes(const tq_format* f);
+int mse_row_bytes(const tq_format* f);
 int tile_bytes_of(const tq_format* f);
 tq_status launch_status(const char* what);
 
@@ -37,10 +38,49 @@ struct DevFormat {
   // threshold is compared).
   float lut_off[2];
   int32_t fast[2];
+  int32_t qjl;             // QJL stage: sign bits after the MSE bytes, residual norms after the norms
+  int32_t sign_off;        // byte offset of the sign bits in a row (= MSE bytes)
+  int32_t rnorm_off;       // byte offset of the residual-norm plane in a tile
 };
 
 void make_dev_format(const tq_format* f, DevFormat* out);
 int device_cus();
+
+// QJL stage (qjl.hip): launched by tq_write_kv after the MSE write of the
+// same rows, and by tq_decode_paged_multi for K formats with the stage.
+struct QjlWriteArgs {
+  const void* src;          // K rows [T][H][D]
+  bool f32;
+  uint8_t* pages;
+  const float* proj;        // [ng][m][m]
+  double kappa;             // sqrt(D / m), correctly rounded on the host
+  const int64_t* slots;
+  int64_t num_tokens, num_slots;
+  int32_t H;
+};
+tq_status launch_qjl_write(const QjlWriteArgs& a, const DevFormat& kf, hipStream_t st);
+
+struct QjlDecodeArgs {
+  const void* q;
+  bool q_f32;
+  int32_t S, Hq, Hkv, G;
+  const uint8_t* k_pages;
+  const uint8_t* v_pages;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  const float* proj;
+  float scale;
+  int32_t P;
+  float* part_o;            // P > 1: [S][Hq][P][D] then lse [S][Hq][P]
+  float* part_lse;
+  void* out;
+  bool out_f32;
+  float* lse;
+  int32_t* dev_err;
+};
+tq_status launch_qjl_decode(const QjlDecodeArgs& a, const DevFormat& kf, const DevFormat& vf, hipStream_t st);
 
 // ------------------------------------------------------ host + device helpers
 

@@ -391,6 +391,7 @@ extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype
     if (!src[t]) continue;
     tq_status st = check_format(fmts[t], names[t]);
     if (st != TQ_OK) return st;
+    if (t == 1 && fmts[t]->qjl) return set_error(TQ_ERR_VALUE, "the QJL stage is defined for K formats only");
     if (!pages[t]) return set_error(TQ_ERR_VALUE, std::string(names[t]) + " pages are NULL");
     if (d && fmts[t]->head_dim != d) return set_error(TQ_ERR_VALUE, "K and V head_dim differ");
     d = fmts[t]->head_dim;
@@ -422,5 +423,17 @@ extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype
     if (f32) hipLaunchKernelGGL((write_kv_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((write_kv_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
   }
-  return launch_status("tq_write_kv launch");
+  tq_status st = launch_status("tq_write_kv launch");
+  if (st != TQ_OK || !k || !kfmt->qjl) return st;
+  QjlWriteArgs qa;
+  qa.src = k;
+  qa.f32 = f32;
+  qa.pages = k_pages;
+  qa.proj = kfmt->qjl_proj;
+  qa.kappa = sqrt((double)kfmt->head_dim / (double)(kfmt->head_dim / kfmt->num_groups));
+  qa.slots = slot_mapping;
+  qa.num_tokens = num_tokens;
+  qa.num_slots = p.num_slots;
+  qa.H = num_kv_heads;
+  return launch_qjl_write(qa, p.fmt[0], s);
 }

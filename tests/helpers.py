@@ -11,12 +11,17 @@ from workloads import FormatSpec, bf16_bits_to_f32, to_bf16_bits
 
 
 def oracle_format(spec: FormatSpec) -> oenc.Format:
-    return oenc.Format.make(spec.head_dim, spec.group_bits, spec.signs, spec.group_channels)
+    return oenc.Format.make(spec.head_dim, spec.group_bits, spec.signs, spec.group_channels,
+                            qjl_proj=spec.qjl_proj)
 
 
 def product_format(spec: FormatSpec):
     import quantized_paged_kv_amd as tq
-    return tq.Format(spec.head_dim, spec.group_bits, spec.signs, spec.group_channels)
+    proj = None
+    if spec.qjl_proj is not None:
+        import torch
+        proj = torch.from_numpy(spec.qjl_proj.copy()).cuda()
+    return tq.Format(spec.head_dim, spec.group_bits, spec.signs, spec.group_channels, qjl_proj=proj)
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda"):
@@ -49,7 +54,7 @@ def written_mask(slots: np.ndarray, num_blocks: int, H: int, fmt: oenc.Format, r
         b, o = divmod(int(s), 16)
         mask[b, :, opg.row_positions(rb, [o], chunk)[0]] = True
         sl = 4 * (o % 4) + o // 4
-        for g in range(fmt.num_groups):
+        for g in range(fmt.num_groups * (2 if fmt.qjl else 1)):   # vector (and residual) norms
             pos = noff + 2 * (16 * g + sl)
             mask[b, :, pos:pos + 2] = True
     return mask

@@ -206,3 +206,51 @@ def test_multi_query_status_codes_without_launch():
     assert "pairs per kv head" in L.tq_last_error().decode()
     assert call(NQ=9, Hq=2, Hkv=2) == tq.TQ_ERR_UNSUPPORTED_FORMAT
     assert call(B=0) == tq.TQ_OK
+
+
+def _qjl_c(f, proj=0x1000):
+    """The format's C struct with the QJL stage switched on (a stand-in
+    device pointer: no call here dereferences it)."""
+    c = tq.tq_format()
+    ctypes.memmove(ctypes.byref(c), ctypes.byref(f.c), ctypes.sizeof(c))
+    c.qjl = 1
+    c.qjl_proj = proj
+    return c
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_qjl_tile_bytes_match_oracle(i):
+    d, bits, s, ch = _fmts()[i]
+    c = _qjl_c(tq.Format(d, bits, s, ch))
+    m = d // len(bits)
+    of = oracle.Format.make(d, bits, s, ch, qjl_proj=np.zeros((len(bits), m, m), np.float32))
+    rb, _, tile = opg.tile_layout(of, 16)
+    rib, tb = ctypes.c_int32(), ctypes.c_int32()
+    assert tq._lib.tq_tile_bytes(ctypes.byref(c), 16, ctypes.byref(rib), ctypes.byref(tb)) == tq.TQ_OK
+    assert (rib.value, tb.value) == (rb, tile)
+
+
+def test_qjl_status_codes_without_launch():
+    s = signs(0, 1, 128)
+    f4 = tq.Format(128, [4], s)
+    assert ctypes.sizeof(tq.tq_format) == 352            # the C struct: 336 bytes, then qjl, padding, the pointer
+    c = _qjl_c(f4, proj=None)
+    assert tq._lib.tq_format_check(ctypes.byref(c)) == tq.TQ_ERR_VALUE     # projection missing
+    c = _qjl_c(f4)
+    c.qjl = 2
+    assert tq._lib.tq_format_check(ctypes.byref(c)) == tq.TQ_ERR_VALUE
+    kq = _qjl_c(f4)
+    assert tq._lib.tq_format_check(ctypes.byref(kq)) == tq.TQ_OK
+
+    class _F:   # a Format-like holder for the call helpers
+        def __init__(self, cs):
+            self.c = cs
+    fq = _F(kq)
+    assert _call_decode(vf=fq) == tq.TQ_ERR_VALUE                     # QJL on V
+    assert _call_decode(kf=fq, B=0) == tq.TQ_OK
+    assert _call_decode(kf=fq, P=4) == tq.TQ_ERR_VALUE                # workspace missing
+    L = tq._lib
+    st = L.tq_decode_paged_multi(1, tq.TQ_BF16, 2, 2, 8, 2, 1, 1, 10, 16, 1, 4, 1, ctypes.byref(kq),
+                                 ctypes.byref(f4.c), 0.1, 1, None, 0, 1, tq.TQ_BF16, None, None, None)
+    assert st == tq.TQ_ERR_UNSUPPORTED_FORMAT                         # one query per sequence only
+    assert _call_write(vf=fq) == tq.TQ_ERR_VALUE                      # QJL on V

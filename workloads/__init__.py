@@ -36,6 +36,7 @@ STREAM_V_SIGNS = 2
 STREAM_CHANNELS = 3
 STREAM_BLOCKS = 4
 STREAM_OUTLIERS = 5
+STREAM_QJL = 6
 STREAM_K = 11
 STREAM_V = 12
 STREAM_Q = 13
@@ -120,6 +121,7 @@ class FormatSpec:
     group_bits: List[int]
     group_channels: Optional[np.ndarray] = None  # full ordered list, group 0 then group 1
     signs: Optional[np.ndarray] = None
+    qjl_proj: Optional[np.ndarray] = None        # float32 [groups, m, m]: QJL projections (K only)
 
     @property
     def num_groups(self) -> int:
@@ -161,7 +163,12 @@ class DecodeWorkload:
         return self.num_q_heads // self.num_kv_heads
 
 
-def _formats(seed: int, head_dim: int, kbits: List[int], vbits: List[int]):
+def qjl_projection(seed: int, num_groups: int, m: int) -> np.ndarray:
+    """QJL projections: float32 [num_groups, m, m] of N(0, 1) draws."""
+    return rng(seed, STREAM_QJL).standard_normal((num_groups, m, m), dtype=np.float32)
+
+
+def _formats(seed: int, head_dim: int, kbits: List[int], vbits: List[int], qjl: bool = False):
     # The same seeded sign vector serves K and V ("a seeded rotation").
     s = signs(seed, STREAM_K_SIGNS, head_dim)
     kch = None
@@ -169,7 +176,8 @@ def _formats(seed: int, head_dim: int, kbits: List[int], vbits: List[int]):
         hi = channel_subset(seed, STREAM_CHANNELS, head_dim, head_dim // 2)
         lo = np.array(sorted(set(range(head_dim)) - set(hi.tolist())), dtype=np.int64)
         kch = np.concatenate([hi, lo])
-    kf = FormatSpec(head_dim, list(kbits), kch, s.copy())
+    proj = qjl_projection(seed, len(kbits), head_dim // len(kbits)) if qjl else None
+    kf = FormatSpec(head_dim, list(kbits), kch, s.copy(), proj)
     vf = FormatSpec(head_dim, list(vbits), None, s.copy())
     return kf, vf
 
@@ -190,7 +198,8 @@ def _paged_tables(seed: int, context_lens: np.ndarray, block_size: int,
 def decode_workload(index: int, seed: int = 0) -> DecodeWorkload:
     """The decode workloads (index 1, 2, 4, 5; index 3 is the write workload;
     index 6 is workload 5 with the 2.5-bit K recipe: 64 channels at 3 bits
-    and 64 at 2 bits)."""
+    and 64 at 2 bits; index 7 is workload 6 with the QJL residual stage on
+    both K groups: 3.5 bits per K channel)."""
     bs = 16
     if index == 1:
         ctx = np.array([256], dtype=np.int32)
@@ -229,20 +238,28 @@ def decode_workload(index: int, seed: int = 0) -> DecodeWorkload:
         return DecodeWorkload("long-context B1 Hq64 Hkv8 ctx131072 K(3+2)/V2 64 splits", seed, 1, 64, 8,
                               128, bs, ctx, nb, bt, kf, vf, "t3", "bf16", "bf16", "bf16",
                               1.0 / math.sqrt(128.0), 64)
+    if index == 7:
+        ctx = np.array([131072], dtype=np.int32)
+        nb, bt = _paged_tables(seed, ctx, bs, 131072 // bs)
+        kf, vf = _formats(seed, 128, [3, 2], [2], qjl=True)
+        return DecodeWorkload("long-context B1 Hq64 Hkv8 ctx131072 K(3+2)+QJL/V2 64 splits", seed, 1, 64, 8,
+                              128, bs, ctx, nb, bt, kf, vf, "t3", "bf16", "bf16", "bf16",
+                              1.0 / math.sqrt(128.0), 64)
     raise ValueError(f"no decode workload {index}")
 
 
 def small_decode_workload(seed: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
                           head_dim: int, context_lens, kbits, vbits, *, kv_dist="normal",
                           in_dtype="bf16", out_dtype="bf16", num_splits=1,
-                          max_blocks_per_seq: Optional[int] = None, pool_factor=1.25) -> DecodeWorkload:
+                          max_blocks_per_seq: Optional[int] = None, pool_factor=1.25,
+                          qjl: bool = False) -> DecodeWorkload:
     """Small seeded case for parity tests (ragged lengths, partial last block)."""
     bs = 16
     ctx = np.asarray(context_lens, dtype=np.int32)
     mb = max_blocks_per_seq or max(1, int(math.ceil(int(ctx.max()) / bs)))
     nb, bt = _paged_tables(seed, ctx, bs, mb, pool_factor)
     nb = max(nb, 1)
-    kf, vf = _formats(seed, head_dim, list(kbits), list(vbits))
+    kf, vf = _formats(seed, head_dim, list(kbits), list(vbits), qjl)
     return DecodeWorkload(f"small seed{seed}", seed, num_seqs, num_q_heads, num_kv_heads, head_dim, bs,
                           ctx, nb, bt, kf, vf, kv_dist, in_dtype, in_dtype, out_dtype,
                           1.0 / math.sqrt(head_dim), num_splits)
@@ -301,7 +318,7 @@ class WriteWorkload:
 
 def write_workload(seed: int = 0, num_seqs: int = 16, new_tokens: int = 2048,
                    num_kv_heads: int = 8, head_dim: int = 128, kbits=(4,), vbits=(4,),
-                   kv_dist="t5u", in_dtype="bf16") -> WriteWorkload:
+                   kv_dist="t5u", in_dtype="bf16", qjl: bool = False) -> WriteWorkload:
     """Quantise-on-write: num_seqs sequences each appending new_tokens tokens
     through a seeded slot mapping into one shared pool (1.25x the need)."""
     bs = 16
@@ -313,7 +330,7 @@ def write_workload(seed: int = 0, num_seqs: int = 16, new_tokens: int = 2048,
         blk = perm[s * per_seq:(s + 1) * per_seq]
         i = np.arange(new_tokens)
         slots[s * new_tokens:(s + 1) * new_tokens] = blk[i // bs] * bs + i % bs
-    kf, vf = _formats(seed, head_dim, list(kbits), list(vbits))
+    kf, vf = _formats(seed, head_dim, list(kbits), list(vbits), qjl)
     return WriteWorkload(f"write {num_seqs}x{new_tokens} Hkv{num_kv_heads} d{head_dim}", seed,
                          num_seqs * new_tokens, num_kv_heads, head_dim, bs, num_blocks, slots,
                          kf, vf, kv_dist, in_dtype)
