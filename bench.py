@@ -29,10 +29,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-SPLITS = {2: 16, 4: 16, 5: 64, 6: 64, 1: 1}
-LAYERS = {2: 3, 4: 2, 5: 1, 6: 1, 1: 1}
+SPLITS = {2: 16, 4: 16, 5: 64, 6: 64, 7: 64, 1: 1}
+LAYERS = {2: 3, 4: 2, 5: 1, 6: 1, 7: 1, 1: 1}
 FLUSH_BYTES = 1 << 30
-NAMES = {"8b": 2, "70b": 4, "long": 5, "long25": 6, "tiny": 1}
+NAMES = {"8b": 2, "70b": 4, "long": 5, "long25": 6, "long_qjl": 7, "tiny": 1}
 
 
 def log(msg):
@@ -42,7 +42,7 @@ def log(msg):
 def algorithmic_bytes(w, kf, vf):
     """Bytes the method must move in one layer-step (decode + write)."""
     import numpy as np
-    krow = kf.tile_bytes()[0] + 2 * kf.num_groups
+    krow = kf.tile_bytes()[0] + 2 * kf.num_groups * (2 if kf.qjl else 1)   # index bytes + norms (+ residual norms)
     vrow = vf.tile_bytes()[0] + 2 * vf.num_groups
     ctx = w.context_lens.astype(np.int64)
     cache = int(ctx.sum()) * w.num_kv_heads * (krow + vrow)
@@ -86,7 +86,8 @@ class Bench:
         self.index = index
         self.P = splits or SPLITS[index]
         self.L = layers or LAYERS[index]
-        kf = tq.Format(w.head_dim, w.kfmt.group_bits, w.kfmt.signs, w.kfmt.group_channels)
+        proj = None if w.kfmt.qjl_proj is None else torch.from_numpy(w.kfmt.qjl_proj.copy()).cuda()
+        kf = tq.Format(w.head_dim, w.kfmt.group_bits, w.kfmt.signs, w.kfmt.group_channels, qjl_proj=proj)
         vf = tq.Format(w.head_dim, w.vfmt.group_bits, w.vfmt.signs, w.vfmt.group_channels)
         self.kf, self.vf = kf, vf
         dt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
@@ -224,7 +225,7 @@ def write_cold(launches, warmup, flush):
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     rows = w.num_tokens * w.num_kv_heads
-    krow = kf.tile_bytes()[0] + 2 * kf.num_groups
+    krow = kf.tile_bytes()[0] + 2 * kf.num_groups * (2 if kf.qjl else 1)   # index bytes + norms (+ residual norms)
     vrow = vf.tile_bytes()[0] + 2 * vf.num_groups
     nbytes = rows * (2 * w.head_dim * 2 + krow + vrow) + w.num_tokens * 8
     return w, ms, nbytes
@@ -469,7 +470,8 @@ def main():
         del b4
         torch.cuda.empty_cache()
         # the other workloads: the write path and the tiny / long-context decodes
-        # (the long context also with the 2.5-bit K recipe)
+        # (the long context also with the 2.5-bit K recipe, and with the 3+2-bit
+        # recipe plus the QJL residual stage)
         ww, wms, wbytes = write_cold(args.steps, args.warmup, flush)
         wavg = sum(wms) / len(wms)
         result["write"] = {"workload": ww.name, "us": stats_us(wms), "algorithmic_bytes": wbytes,
@@ -477,7 +479,7 @@ def main():
                            "frac_of_peak": round(wbytes / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         log(f"write: {wavg * 1e3:.1f} us")
         torch.cuda.empty_cache()
-        for idx, key in ((5, "long"), (6, "long25"), (1, "tiny")):
+        for idx, key in ((5, "long"), (6, "long25"), (7, "long_qjl"), (1, "tiny")):
             bx = Bench(idx)
             dx = bx.timed_cold(max(10, args.steps // 2), args.warmup, flush)
             ax = sum(dx) / len(dx)

@@ -25,11 +25,14 @@ def ledger(kfmt: Format, vfmt: Format, num_tokens: int, num_kv_heads: int, block
     for name, f in (("k", kfmt), ("v", vfmt)):
         rb, _, tile = tile_layout(f, block_size)
         out[f"{name}_row_index_bytes"] = rb
-        out[f"{name}_row_norm_bytes"] = 2 * f.num_groups
-        out[f"{name}_row_bytes"] = rb + 2 * f.num_groups
+        nn = 2 * f.num_groups * (2 if f.qjl else 1)   # vector norms (and residual norms)
+        out[f"{name}_row_norm_bytes"] = nn
+        out[f"{name}_row_bytes"] = rb + nn
         out[f"{name}_tile_bytes"] = tile
         out[f"{name}_pool_bytes"] = num_blocks * num_kv_heads * tile
-        out[f"{name}_bits_per_channel"] = sum(b * (f.head_dim // f.num_groups) for b in f.group_bits) / f.head_dim
+        out[f"{name}_bits_per_channel"] = (sum(b * (f.head_dim // f.num_groups) for b in f.group_bits) / f.head_dim
+                                           + (1 if f.qjl else 0))   # QJL: one sign bit per channel
+        out[f"{name}_projection_bytes"] = 4 * f.num_groups * f.group_size ** 2 if f.qjl else 0
         out[f"{name}_codebook_bytes"] = sum(2 * (1 << b) for b in f.group_bits)
         out[f"{name}_signs_bytes"] = f.head_dim
         out[f"{name}_channel_list_bytes"] = f.head_dim if f.num_groups > 1 else 0
@@ -41,6 +44,7 @@ def ledger(kfmt: Format, vfmt: Format, num_tokens: int, num_kv_heads: int, block
     storage = out["k_pool_bytes"] + out["v_pool_bytes"] + out["window_bytes"]
     meta = (out["k_codebook_bytes"] + out["v_codebook_bytes"] + out["k_signs_bytes"]
             + out["v_signs_bytes"] + out["k_channel_list_bytes"] + out["v_channel_list_bytes"]
+            + out["k_projection_bytes"] + out["v_projection_bytes"]
             + 4 * num_seqs * max_blocks_per_seq + workspace_bytes)
     out.update(dense_bytes=dense, packed_row_bytes=packed_rows, storage_bytes=storage,
                metadata_bytes=meta,

@@ -76,3 +76,19 @@ def test_dense_window_counts_in_storage():
     # a ring buffer with spare room is charged for its capacity
     Lc = ledger(_f([4]), _f([4]), T, H, 16, T // 16, window_tokens=W, window_capacity_tokens=256)
     assert Lc["window_bytes"] == 2 * 256 * H * 128 * 2
+
+
+def test_qjl_row_bytes_and_bits():
+    """The QJL reading of the 3.5-bit recipe: 3 + 2 MSE bits and one sign bit
+    per channel; per row 40 + 16 index bytes, 2 vector + 2 residual norms."""
+    import numpy as np
+    from oracle import encode as enc
+    from oracle.ledger import ledger
+    s = np.ones(128, np.int8)
+    ch = np.concatenate([np.arange(0, 128, 2), np.arange(1, 128, 2)])
+    k = enc.Format.make(128, [3, 2], s, ch, qjl_proj=np.zeros((2, 64, 64), np.float32))
+    v = enc.Format.make(128, [2], s)
+    L = ledger(k, v, num_tokens=16, num_kv_heads=1, block_size=16, num_blocks=1)
+    assert L["k_row_bytes"] == 56 + 8 and L["k_tile_bytes"] == 1024
+    assert L["k_bits_per_channel"] == 3.5
+    assert L["k_projection_bytes"] == 2 * 64 * 64 * 4
