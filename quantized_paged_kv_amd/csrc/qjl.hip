@@ -184,8 +184,10 @@ struct QjlDecParams {
   float f_mse, f_q;   // score factors (log2 units): scale log2e / sqrt(m d), scale log2e sqrt(pi/2) / (m sqrt d)
 };
 
-template <int D>
-__global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams p) {
+template <int D, int NG, int VB>
+__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(4))) void qjl_decode_kernel(QjlDecParams p) {
+  constexpr int M = D / NG;         // channels per K group
+  constexpr int VC = D / 16 * VB / 8;   // V bytes per token in one lane's run of the lane-major plane
   constexpr int NT = D / 32;        // MSE contractions of 32 channels (and as many sketch ones)
   constexpr int ND = D / 16;        // P.V contractions of 16 dims
   __shared__ float qg[8][D];        // rotated query (unnormalised), then in group position order
@@ -251,26 +253,35 @@ __global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams
     qg[g][c] = qt[g][kf.ch[c]];
   }
   __syncthreads();
-  // ---- projected query u[g][O] = sum_j S[grp][i][j] qg[g][grp m + j], O = grp m + i
+  // ---- projected query u[g][O] = sum_j S[grp][i][j] qg[g][grp M + j], O = grp M + i.
+  // The projection rows pass through LDS 32 at a time (coalesced loads, all
+  // in flight together; rows padded to M + 1 floats), in the area that holds
+  // the wave states after the block loop.
   {
-    const int m = kf.m;
-    for (int e = tid; e < 8 * D; e += 64 * kDecWaves) {
-      const int g = e / D, O = e - g * D;
-      const int grp = O / m, i = O - grp * m;
-      const float4* srow = reinterpret_cast<const float4*>(a.proj + ((int64_t)grp * m + i) * m);
-      const float* qv = qg[g] + grp * m;
-      float acc = 0.f;
-      for (int j4 = 0; j4 < m / 4; ++j4) {
-        const float4 sv = srow[j4];
-        acc = __builtin_fmaf(sv.x, qv[4 * j4], acc);
-        acc = __builtin_fmaf(sv.y, qv[4 * j4 + 1], acc);
-        acc = __builtin_fmaf(sv.z, qv[4 * j4 + 2], acc);
-        acc = __builtin_fmaf(sv.w, qv[4 * j4 + 3], acc);
+    constexpr int RS = 32;
+    float* srows = &st_o[0][0][0];
+    static_assert(RS * (M + 1) <= kDecWaves * 8 * D, "projection slice larger than its staging area");
+    for (int r0 = 0; r0 < D; r0 += RS) {
+      for (int e = tid; e < RS * M / 4; e += 64 * kDecWaves) {
+        const int r = (4 * e) / M, j = 4 * e - r * M;
+        const float4 v = reinterpret_cast<const float4*>(a.proj + (int64_t)(r0 + r) * M)[j / 4];
+        float* dst = srows + r * (M + 1) + j;
+        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
       }
-      qt[g][O] = acc;
+      __syncthreads();
+      if (tid < 8 * RS) {
+        const int g = tid / RS, r = tid - g * RS;
+        const int O = r0 + r, grp = O / M;
+        const float* srow = srows + r * (M + 1);
+        const float* qv = qg[g] + grp * M;
+        float acc = 0.f;
+#pragma unroll 16
+        for (int j = 0; j < M; ++j) acc = __builtin_fmaf(srow[j], qv[j], acc);
+        qt[g][O] = acc;
+      }
+      __syncthreads();
     }
   }
-  __syncthreads();
   // ---- per q head: power-of-two scales that put each half of the operand in
   // fp16 range (largest magnitude in [2^14, 2^15)), and the score factors
   {
@@ -327,26 +338,55 @@ __global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams
   for (int u = 0; u < ND; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
   uint8_t* kt = ktile[wave];
   uint8_t* vt = vtile[wave];
-  const int krb = kf.row_bytes, m = kf.m;
-  for (int b = b0 + wave; b < b1; b += kDecWaves) {
+  const int krb = kf.row_bytes;
+  constexpr int m = M;
+  // Each wave keeps its next block's tiles in flight in registers (16 B at
+  // 16 lane and 16 lane + 1024 of each) while it computes the current one
+  // from LDS.  An entry outside the pool is reported when it is read and the
+  // block is skipped (block 0 is loaded in its place, never used).
+  auto entry_of = [&](int b, bool& ok) -> int {
     const int raw = __builtin_amdgcn_readfirstlane(a.block_tables[(int64_t)s * a.max_blocks + b]);
-    const bool bad = raw < 0 || (int64_t)raw >= a.num_blocks;
-    if (bad) {
-      if (lane == 0) record_error(a.dev_err, TQ_ERR_INDEX, s * a.max_blocks + b);
-      continue;   // wave-uniform
-    }
-    const uint8_t* ksrc = a.k_pages + ((int64_t)raw * a.Hkv + kvh) * kf.tile_bytes;
-    const uint8_t* vsrc = a.v_pages + ((int64_t)raw * a.Hkv + kvh) * vf.tile_bytes;
+    ok = !(raw < 0 || (int64_t)raw >= a.num_blocks);
+    if (!ok && lane == 0) record_error(a.dev_err, TQ_ERR_INDEX, s * a.max_blocks + b);
+    return ok ? raw : 0;
+  };
+  const int o0 = 16 * lane, o1 = o0 + 1024;
+  const int kbytes = kf.tile_bytes, vbytes = vf.tile_bytes;
+  uint4 nk0 = {0u, 0u, 0u, 0u}, nk1 = nk0, nv0 = nk0, nv1 = nk0;
+  bool ok_next = false;
+  int b = b0 + wave;
+  if (b < b1) {
+    const int ph = entry_of(b, ok_next);
+    const uint8_t* ksrc = a.k_pages + ((int64_t)ph * a.Hkv + kvh) * kbytes;
+    const uint8_t* vsrc = a.v_pages + ((int64_t)ph * a.Hkv + kvh) * vbytes;
+    if (o0 < kbytes) nk0 = *reinterpret_cast<const uint4*>(ksrc + o0);
+    if (o1 < kbytes) nk1 = *reinterpret_cast<const uint4*>(ksrc + o1);
+    if (o0 < vbytes) nv0 = *reinterpret_cast<const uint4*>(vsrc + o0);
+    if (o1 < vbytes) nv1 = *reinterpret_cast<const uint4*>(vsrc + o1);
+  }
+  for (; b < b1; b += kDecWaves) {
+    const bool ok = ok_next;
     wave_fence();   // the previous block's reads of the staging area are done
-    for (int off = 16 * lane; off < kf.tile_bytes; off += 1024)
-      *reinterpret_cast<uint4*>(kt + off) = *reinterpret_cast<const uint4*>(ksrc + off);
-    for (int off = 16 * lane; off < vf.tile_bytes; off += 1024)
-      *reinterpret_cast<uint4*>(vt + off) = *reinterpret_cast<const uint4*>(vsrc + off);
+    if (o0 < kbytes) *reinterpret_cast<uint4*>(kt + o0) = nk0;
+    if (o1 < kbytes) *reinterpret_cast<uint4*>(kt + o1) = nk1;
+    if (o0 < vbytes) *reinterpret_cast<uint4*>(vt + o0) = nv0;
+    if (o1 < vbytes) *reinterpret_cast<uint4*>(vt + o1) = nv1;
     wave_fence();
+    if (b + kDecWaves < b1) {
+      const int ph = entry_of(b + kDecWaves, ok_next);
+      const uint8_t* ksrc = a.k_pages + ((int64_t)ph * a.Hkv + kvh) * kbytes;
+      const uint8_t* vsrc = a.v_pages + ((int64_t)ph * a.Hkv + kvh) * vbytes;
+      if (o0 < kbytes) nk0 = *reinterpret_cast<const uint4*>(ksrc + o0);
+      if (o1 < kbytes) nk1 = *reinterpret_cast<const uint4*>(ksrc + o1);
+      if (o0 < vbytes) nv0 = *reinterpret_cast<const uint4*>(vsrc + o0);
+      if (o1 < vbytes) nv1 = *reinterpret_cast<const uint4*>(vsrc + o1);
+    }
+    if (!ok) continue;   // wave-uniform
 
-    // scores: A row = token `col` (lane % 16), channels 32 t + 8 ta + e
+    // scores: A row r = token sigma(r) = r / 4 + 4 (r % 4), channels 32 t + 8 ta + e;
+    // result row 4 ta + i is then token ta + 4 i, the order P.V takes them in
     float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, accq = acc0;
-    const uint8_t* krow = kt + col * krb;
+    const uint8_t* krow = kt + ((col >> 2) + 4 * (col & 3)) * krb;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int P0 = 32 * t + 8 * ta;
@@ -370,7 +410,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams
     for (int t = 0; t < NT; ++t) {
       const int O0 = 32 * t + 8 * ta;
       const int g = O0 / m;
-      const uint32_t gam = *reinterpret_cast<const uint16_t*>(kt + kf.rnorm_off + 2 * (16 * g + norm_slot(col)));
+      // residual norm of token sigma(col): norm slot col
+      const uint32_t gam = *reinterpret_cast<const uint16_t*>(kt + kf.rnorm_off + 2 * (16 * g + col));
       const uint32_t sb = krow[kf.sign_off + (O0 >> 3)];
       u32x4_t av;
 #pragma unroll
@@ -378,23 +419,26 @@ __global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams
         av[e2] = (gam | (((sb >> (2 * e2)) & 1u) << 15)) | ((gam | (((sb >> (2 * e2 + 1)) & 1u) << 15)) << 16);
       accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bop[NT + t][lane], accq, 0, 0, 0);
     }
-    // lane holds tokens 4 ta + i of column col; high + low columns summed
+    __builtin_amdgcn_sched_barrier(0);   // phase boundary: bounds the registers live across phases
+    // lane holds tokens ta + 4 i (norm slots 4 ta + i) of column col; high +
+    // low columns summed
+    const uint2 nk0 = *reinterpret_cast<const uint2*>(kt + kf.norm_off + 8 * ta);
+    const uint2 nk1 = *reinterpret_cast<const uint2*>(kt + kf.norm_off + 32 * (NG - 1) + 8 * ta);
+    const uint2 nvv = *reinterpret_cast<const uint2*>(vt + vf.norm_off + 8 * ta);
+    auto half_at = [](uint2 w, int i) -> float {
+      const uint32_t x = (i >> 1) ? w.y : w.x;
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> (16 * (i & 1))));
+    };
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tk = 4 * ta + i;
       const float f0 = acc0[i] + lane_xor<8>(acc0[i], lane);
       const float f1 = acc1[i] + lane_xor<8>(acc1[i], lane);
       const float fq = accq[i] + lane_xor<8>(accq[i], lane);
-      const float n0 = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(kt + kf.norm_off + 2 * norm_slot(tk)));
-      float v = n0 * f0;
-      if (kf.ng > 1) {
-        const float n1 = (float)__builtin_bit_cast(
-            _Float16, *reinterpret_cast<const uint16_t*>(kt + kf.norm_off + 2 * (16 + norm_slot(tk))));
-        v = __builtin_fmaf(n1, f1, v);
-      }
+      float v = half_at(nk0, i) * f0;
+      if (NG > 1) v = __builtin_fmaf(half_at(nk1, i), f1, v);
       v = __builtin_fmaf(fq, w_q, v * w_m);
-      sc[i] = (16 * b + tk < ctx) ? v : -INFINITY;
+      sc[i] = (16 * b + ta + 4 * i < ctx) ? v : -INFINITY;
     }
     // online softmax per column (exp2 domain)
     float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
@@ -411,26 +455,32 @@ __global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams
     half4_t pb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tk = 4 * ta + i;
       const float pr = sc[i] == -INFINITY ? 0.f : exp2f(sc[i] - m_use);
       l_run += pr;
-      const float vn = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(vt + vf.norm_off + 2 * norm_slot(tk)));
-      pb[i] = pr > 0.f ? (_Float16)(pr * vn) : (_Float16)0.f;
+      pb[i] = pr > 0.f ? (_Float16)(pr * half_at(nvv, i)) : (_Float16)0.f;
     }
-    // P.V: A = V codes of dim 16 u + col for tokens 4 ta + i
-    const int vbits = vf.bits[0], vc = vf.chunk, vrb = vf.row_bytes;
+    __builtin_amdgcn_sched_barrier(0);
+    // P.V: MFMA u, A row r = dim ND r + u; lane (col, ta) takes run 16 ta + col
+    // of the lane-major V plane: VC bytes of each of tokens ta + 4 i, its ND
+    // dims' codes, back to back
+    const uint8_t* run = vt + (16 * ta + col) * 4 * VC;
+    uint32_t vw[4];
+    if constexpr (VC == 1) {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(run);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vw[i] = (x >> (8 * i)) & 0xFFu;
+    } else if constexpr (VC == 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(run);
+      vw[0] = x.x & 0xFFFFu; vw[1] = x.x >> 16; vw[2] = x.y & 0xFFFFu; vw[3] = x.y >> 16;
+    } else {
+      const uint4 x = *reinterpret_cast<const uint4*>(run);
+      vw[0] = x.x; vw[1] = x.y; vw[2] = x.z; vw[3] = x.w;
+    }
 #pragma unroll
     for (int u = 0; u < ND; ++u) {
-      const int j = 16 * u + col;
-      const int bit0 = j * vbits, bb = bit0 >> 3, sh = bit0 & 7;
       half4_t avv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tk = 4 * ta + i;
-        const int pos = vc == 0 ? tk * vrb + bb : ((16 * (tk & 3) + bb / vc) * 4 + (tk >> 2)) * vc + bb % vc;
-        const uint32_t code = ((uint32_t)vt[pos] >> sh) & ((1u << vbits) - 1u);
-        avv[i] = __builtin_bit_cast(_Float16, cbv[code]);
-      }
+      for (int i = 0; i < 4; ++i) avv[i] = __builtin_bit_cast(_Float16, cbv[(vw[i] >> (VB * u)) & ((1u << VB) - 1u)]);
       o_acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(avv, pb, o_acc[u], 0, 0, 0);
     }
   }
@@ -441,7 +491,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void qjl_decode_kernel(QjlDecParams
 #pragma unroll
     for (int u = 0; u < ND; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st_o[wave][col][16 * u + 4 * ta + i] = o_acc[u][i];
+      for (int i = 0; i < 4; ++i) st_o[wave][col][ND * (4 * ta + i) + u] = o_acc[u][i];
     if (ta == 0) {
       st_ml[wave][0][col] = m_run;
       st_ml[wave][1][col] = l_run;
@@ -537,9 +587,18 @@ tq_status launch_qjl_decode(const QjlDecodeArgs& a, const DevFormat& kf, const D
   if (n_wg == 0) return TQ_OK;
   if (n_wg >= ((int64_t)1 << 31)) return set_error(TQ_ERR_VALUE, "QJL decode: too many workgroups");
   const dim3 grid((unsigned)n_wg);
-  if (kf.d == 128) hipLaunchKernelGGL((qjl_decode_kernel<128>), grid, dim3(64 * kDecWaves), 0, st, p);
-  else hipLaunchKernelGGL((qjl_decode_kernel<64>), grid, dim3(64 * kDecWaves), 0, st, p);
-  return launch_status("tq_decode_paged QJL launch");
+  const dim3 block(64 * kDecWaves);
+  if (vf.ng != 1 || (vf.bits[0] != 2 && vf.bits[0] != 4) || vf.chunk * 16 != vf.row_bytes)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "QJL decode: V must be one group of 2 or 4 bits");
+#define TQ_QJL(DD, NGG, VBB)                                                     \
+  if (kf.d == DD && kf.ng == NGG && vf.bits[0] == VBB) {                        \
+    hipLaunchKernelGGL((qjl_decode_kernel<DD, NGG, VBB>), grid, block, 0, st, p); \
+    return launch_status("tq_decode_paged QJL launch");                          \
+  }
+  TQ_QJL(128, 1, 4) TQ_QJL(128, 1, 2) TQ_QJL(128, 2, 4) TQ_QJL(128, 2, 2)
+  TQ_QJL(64, 1, 4) TQ_QJL(64, 1, 2) TQ_QJL(64, 2, 4) TQ_QJL(64, 2, 2)
+#undef TQ_QJL
+  return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "QJL decode: no kernel for this format");
 }
 
 }  // namespace tq
