@@ -413,10 +413,12 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       // residual norm of token sigma(col): norm slot col
       const uint32_t gam = *reinterpret_cast<const uint16_t*>(kt + kf.rnorm_off + 2 * (16 * g + col));
       const uint32_t sb = krow[kf.sign_off + (O0 >> 3)];
+      // +-gam in both halves: sign bit 2 e2 of sb to bit 15, bit 2 e2 + 1 to
+      // bit 31 (sb | sb << 15 puts them 15 - 2 e2 places below)
+      const uint32_t g2 = gam | (gam << 16), spread = sb | (sb << 15);
       u32x4_t av;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        av[e2] = (gam | (((sb >> (2 * e2)) & 1u) << 15)) | ((gam | (((sb >> (2 * e2 + 1)) & 1u) << 15)) << 16);
+      for (int e2 = 0; e2 < 4; ++e2) av[e2] = ((spread << (15 - 2 * e2)) & 0x80008000u) | g2;
       accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bop[NT + t][lane], accq, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);   // phase boundary: bounds the registers live across phases

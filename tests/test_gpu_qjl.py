@@ -186,3 +186,50 @@ def test_qjl_decode_full_size_long_context():
             o_ref[0, h], l_ref[0, h] = oatt.attention(q[0, h].astype(np.float64), K, V, w.scale)
             cells.append((0, h))
     check(o, l, o_ref, l_ref, cells, w.out_dtype)
+
+
+def test_qjl_bad_block_entry_and_context_length():
+    """A block-table entry outside the pool is reported as (INDEX, s * max_blocks
+    + b) and its block skipped: the output equals the oracle's attention over
+    the other blocks.  A context length past the capacity is reported as
+    (INDEX, -1 - s)."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    w = wl.small_decode_workload(71, 2, 8, 2, 128, [64, 100], [3, 2], [2], out_dtype="f32", num_splits=3,
+                                 qjl=True)
+    print("case QJL bad entry", flush=True)
+    kp, vp = build_cache(w)
+    kf, vf = w._gpu_formats
+    q = wl.q_values(w)
+    bt = w.block_tables.copy()
+    bt[1, 2] = w.num_blocks + 5
+    err = tq.new_error_word()
+    o, l = tq.decode_paged(to_device(q, w.q_dtype), kp, vp, torch.from_numpy(bt).cuda(),
+                           torch.from_numpy(w.context_lens).cuda(), kf, vf, w.scale, num_splits=3,
+                           out_dtype=torch.float32, dev_err=err)
+    torch.cuda.synchronize()
+    e = err.cpu().numpy()
+    assert e[0] == tq.TQ_ERR_INDEX and e[1] == 1 * bt.shape[1] + 2
+    kof, vof = oracle_format(w.kfmt), oracle_format(w.vfmt)
+    n = int(w.context_lens[1])
+    xk, xv = wl.kv_values(w, "k", 1), wl.kv_values(w, "v", 1)
+    keep = np.array([t for t in range(n) if t // 16 != 2])
+    nbk = (n + 15) // 16
+    sl = np.arange(nbk)[np.arange(n) // 16] * 16 + np.arange(n) % 16
+    o_ref = np.zeros((2, 8, 128))
+    l_ref = np.full((2, 8), -math.inf)
+    for kvh in range(2):
+        Kp = np.zeros((nbk, 1, opg.tile_layout(kof, 16)[2]), np.uint8)
+        Vp = np.zeros((nbk, 1, opg.tile_layout(vof, 16)[2]), np.uint8)
+        opg.write_pages(xk[:, kvh:kvh + 1], sl, Kp, kof, 16)
+        opg.write_pages(xv[:, kvh:kvh + 1], sl, Vp, vof, 16, "v")
+        K = opg.reconstruct_sequence(Kp, np.arange(nbk), n, 0, kof, 16)[keep]
+        V = opg.reconstruct_sequence(Vp, np.arange(nbk), n, 0, vof, 16, role="v")[keep]
+        for h in range(kvh * 4, kvh * 4 + 4):
+            o_ref[1, h], l_ref[1, h] = oatt.attention(q[1, h].astype(np.float64), K, V, w.scale)
+    check(o.cpu().numpy(), l.cpu().numpy(), o_ref, l_ref, [(1, h) for h in range(8)], "f32")
+    cl = w.context_lens.copy()
+    cl[0] = 16 * bt.shape[1] + 1
+    with pytest.raises(IndexError, match="position -1"):
+        tq.decode_paged(to_device(q, w.q_dtype), kp, vp, torch.from_numpy(w.block_tables).cuda(),
+                        torch.from_numpy(cl).cuda(), kf, vf, w.scale, check=True)
