@@ -1358,8 +1358,6 @@ int format_kind_v(const tq_format* f) {
   return -1;
 }
 
-// Compute units of the current device (cached per device).
-
 }  // namespace
 }  // namespace tq
 
