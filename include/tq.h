@@ -104,8 +104,9 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
  *   qjl_proj        qjl = 1: DEVICE pointer to the projections, fp32
  *                   [num_groups][m][m] row-major (entry [g][i][j] multiplies
  *                   residual channel j of group g into output i), i.i.d.
- *                   N(0, 1) values drawn by the caller; read by tq_write_kv
- *                   and tq_decode_paged during the call.  Unused when qjl = 0.
+ *                   N(0, 1) values drawn by the caller, 16-byte aligned;
+ *                   read by tq_write_kv and tq_decode_paged during the call.
+ *                   Unused when qjl = 0.
  *
  * Encoding of a row x (head_dim values), per group G of m channels:
  *   w   = H (signs * x)           Sylvester Walsh-Hadamard, natural order,
@@ -275,6 +276,7 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * one workgroup per (sequence, kv head, split p), split p taking logical
  * blocks [p*c, (p+1)*c), c = ceil(ceil(context_lens[s] / 16) / P), every
  * split writing its partial (lse -inf when empty) before the same merge.
+ * It needs 16-byte aligned page pools and qjl_proj (else VALUE).
  */
 tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
                           int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,

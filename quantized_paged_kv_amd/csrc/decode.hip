@@ -1428,8 +1428,9 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
   if (kfmt->qjl) {   // sketch term on every score: the QJL decode kernel, then the generic merge
-    if ((reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15)
-      return set_error(TQ_ERR_VALUE, "page pools must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages) |
+         reinterpret_cast<uintptr_t>(kfmt->qjl_proj)) & 15)
+      return set_error(TQ_ERR_VALUE, "page pools and qjl_proj must be 16-byte aligned");
     DevFormat kf, vf;
     make_dev_format(kfmt, &kf);
     make_dev_format(vfmt, &vf);

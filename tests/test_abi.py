@@ -254,3 +254,15 @@ def test_qjl_status_codes_without_launch():
                                  ctypes.byref(f4.c), 0.1, 1, None, 0, 1, tq.TQ_BF16, None, None, None)
     assert st == tq.TQ_ERR_UNSUPPORTED_FORMAT                         # one query per sequence only
     assert _call_write(vf=fq) == tq.TQ_ERR_VALUE                      # QJL on V
+
+
+def test_qjl_alignment_checked_before_launch():
+    s = signs(0, 1, 128)
+    f4 = tq.Format(128, [4], s)
+    kq = _qjl_c(f4, proj=0x1004)   # not 16-byte aligned
+
+    class _F:
+        def __init__(self, cs):
+            self.c = cs
+    assert _call_decode(kf=_F(kq), kp=0x1000, vp=0x2000) == tq.TQ_ERR_VALUE
+    assert "aligned" in tq._lib.tq_last_error().decode()
