@@ -219,6 +219,31 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   const int b0 = sp * cb;
   const int b1 = std::min(nb, b0 + cb);
 
+  // Each wave keeps its next block's tiles in flight in registers (16 B at
+  // 16 lane and 16 lane + 1024 of each) while it computes the current one
+  // from LDS.  An entry outside the pool is reported when it is read and the
+  // block is skipped (block 0 is loaded in its place, never used).
+  auto entry_of = [&](int b, bool& ok) -> int {
+    const int raw = __builtin_amdgcn_readfirstlane(a.block_tables[(int64_t)s * a.max_blocks + b]);
+    ok = !(raw < 0 || (int64_t)raw >= a.num_blocks);
+    if (!ok && lane == 0) record_error(a.dev_err, TQ_ERR_INDEX, s * a.max_blocks + b);
+    return ok ? raw : 0;
+  };
+  const int o0 = 16 * lane, o1 = o0 + 1024;
+  const int kbytes = kf.tile_bytes, vbytes = vf.tile_bytes;
+  uint4 nk0 = {0u, 0u, 0u, 0u}, nk1 = nk0, nv0 = nk0, nv1 = nk0;
+  bool ok_next = false;
+  int b = b0 + wave;
+  if (b < b1) {
+    const int ph = entry_of(b, ok_next);
+    const uint8_t* ksrc = a.k_pages + ((int64_t)ph * a.Hkv + kvh) * kbytes;
+    const uint8_t* vsrc = a.v_pages + ((int64_t)ph * a.Hkv + kvh) * vbytes;
+    if (o0 < kbytes) nk0 = *reinterpret_cast<const uint4*>(ksrc + o0);
+    if (o1 < kbytes) nk1 = *reinterpret_cast<const uint4*>(ksrc + o1);
+    if (o0 < vbytes) nv0 = *reinterpret_cast<const uint4*>(vsrc + o0);
+    if (o1 < vbytes) nv1 = *reinterpret_cast<const uint4*>(vsrc + o1);
+  }
+  // (the first block's tiles are requested here, before the query set-up)
   // ---- query: load, K signs, Walsh-Hadamard (fp32), group order
   for (int e = tid; e < 8 * D; e += 64 * kDecWaves) {
     const int g = e / D, c = e - g * D;
@@ -261,14 +286,28 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     constexpr int RS = 32;
     float* srows = &st_o[0][0][0];
     static_assert(RS * (M + 1) <= kDecWaves * 8 * D, "projection slice larger than its staging area");
+    constexpr int PER = (RS * M / 4 + 64 * kDecWaves - 1) / (64 * kDecWaves);   // float4 per thread per slice
+    float4 sv[PER];
+    auto fetch_slice = [&](int r0) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int e = tid + 64 * kDecWaves * k;
+        if (e < RS * M / 4) sv[k] = reinterpret_cast<const float4*>(a.proj + (int64_t)r0 * M)[e];
+      }
+    };
+    fetch_slice(0);
     for (int r0 = 0; r0 < D; r0 += RS) {
-      for (int e = tid; e < RS * M / 4; e += 64 * kDecWaves) {
-        const int r = (4 * e) / M, j = 4 * e - r * M;
-        const float4 v = reinterpret_cast<const float4*>(a.proj + (int64_t)(r0 + r) * M)[j / 4];
-        float* dst = srows + r * (M + 1) + j;
-        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int e = tid + 64 * kDecWaves * k;
+        if (e < RS * M / 4) {
+          const int r = (4 * e) / M, j = 4 * e - r * M;
+          float* dst = srows + r * (M + 1) + j;
+          dst[0] = sv[k].x; dst[1] = sv[k].y; dst[2] = sv[k].z; dst[3] = sv[k].w;
+        }
       }
       __syncthreads();
+      if (r0 + RS < D) fetch_slice(r0 + RS);   // in flight while this slice is used
       if (tid < 8 * RS) {
         const int g = tid / RS, r = tid - g * RS;
         const int O = r0 + r, grp = O / M;
@@ -340,30 +379,6 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   uint8_t* vt = vtile[wave];
   const int krb = kf.row_bytes;
   constexpr int m = M;
-  // Each wave keeps its next block's tiles in flight in registers (16 B at
-  // 16 lane and 16 lane + 1024 of each) while it computes the current one
-  // from LDS.  An entry outside the pool is reported when it is read and the
-  // block is skipped (block 0 is loaded in its place, never used).
-  auto entry_of = [&](int b, bool& ok) -> int {
-    const int raw = __builtin_amdgcn_readfirstlane(a.block_tables[(int64_t)s * a.max_blocks + b]);
-    ok = !(raw < 0 || (int64_t)raw >= a.num_blocks);
-    if (!ok && lane == 0) record_error(a.dev_err, TQ_ERR_INDEX, s * a.max_blocks + b);
-    return ok ? raw : 0;
-  };
-  const int o0 = 16 * lane, o1 = o0 + 1024;
-  const int kbytes = kf.tile_bytes, vbytes = vf.tile_bytes;
-  uint4 nk0 = {0u, 0u, 0u, 0u}, nk1 = nk0, nv0 = nk0, nv1 = nk0;
-  bool ok_next = false;
-  int b = b0 + wave;
-  if (b < b1) {
-    const int ph = entry_of(b, ok_next);
-    const uint8_t* ksrc = a.k_pages + ((int64_t)ph * a.Hkv + kvh) * kbytes;
-    const uint8_t* vsrc = a.v_pages + ((int64_t)ph * a.Hkv + kvh) * vbytes;
-    if (o0 < kbytes) nk0 = *reinterpret_cast<const uint4*>(ksrc + o0);
-    if (o1 < kbytes) nk1 = *reinterpret_cast<const uint4*>(ksrc + o1);
-    if (o0 < vbytes) nv0 = *reinterpret_cast<const uint4*>(vsrc + o0);
-    if (o1 < vbytes) nv1 = *reinterpret_cast<const uint4*>(vsrc + o1);
-  }
   for (; b < b1; b += kDecWaves) {
     const bool ok = ok_next;
     wave_fence();   // the previous block's reads of the staging area are done
