@@ -365,8 +365,15 @@ def cpu_baseline(index, budget_s=12.0):
     except Exception:
         threads = 1
     cores = len(os.sched_getaffinity(0))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
-            "kind": "oracle",
+            "kind": "oracle", "allowed_cores": cores, "blas_threads": threads, "cpu_model": cpu_model,
+            "numpy": np.__version__,
             "sample": f"{len(done)} whole sequence(s) of the workload ({sum(int(w.context_lens[s]) for s in done)} "
                       f"tokens x {w.num_kv_heads} kv heads x {w.num_q_heads // w.num_kv_heads} q heads each): "
                       f"dense reconstruction + fp64 attention, {total_t:.1f} s on {cores} allowed cores"}
