@@ -402,7 +402,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode shards by kv head or "
-              f"sequence with no exchange, see DESIGN.md", file=sys.stderr)
+              f"sequence with no exchange", file=sys.stderr)
         sys.exit(2)
     import torch
     index = NAMES[args.workload]

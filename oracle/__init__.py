@@ -24,8 +24,8 @@ Sources, cited by page title and section:
 * [T]  "Tattletale" README, "Highlights": random Hadamard rotations with
        codebooks (EXL3) as prior art for rotate-then-codebook.
 
-Readings of points the pages leave open are listed in the design doc; each
-function below names the reading it takes.
+Where the pages leave a point open, the function that depends on it
+states the reading it takes.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_*.py`` against closed forms, published values,

@@ -6,7 +6,8 @@ the original (un-rotated) domain:
 
     s_t = scale * q . K_t,   lse = ln sum_t exp(s_t),   o = sum_t exp(s_t - lse) V_t
 
-Readings: R13 (kv head = q head // (H_q / H_kv)), R14 (natural-log LSE).
+Readings of open points: kv head = q head // (H_q / H_kv); the LSE is a
+natural log.
 A sequence with no cached tokens gives o = 0 and lse = -inf.
 
 Split-K (flash-decoding): the logical blocks of a sequence are cut into

@@ -3,7 +3,8 @@
 [S "Architecture notes", Codebook caching]: the codebooks are Lloyd-Max
 quantisers computed once on the CPU.  The workloads fix them as 2^b-level
 Lloyd-Max quantisers of a Gaussian; the unit-variance codebook is used and
-the row's norm carries the scale (reading R1/R6 in the design doc).
+the row's norm carries the scale (a reading: the pages name Lloyd-Max
+codebooks, not their scale).
 
 Lloyd-Max optimality (Lloyd 1957 / Max 1960) is the pair of conditions
 
@@ -96,7 +97,8 @@ def codebook_f16(bits: int) -> np.ndarray:
 
     The fp64 Lloyd-Max levels are symmetrised and rounded to fp16; these fp16
     values are the codebook both the encoder and the decoder use, so the
-    codebook contributes no rounding of its own (reading R7)."""
+    codebook contributes no rounding of its own (a reading: the pages do not
+    say at which precision the levels are stored)."""
     c = lloyd_max_gaussian(1 << bits)
     c = 0.5 * (c - c[::-1])          # exact symmetry c_i = -c_{L-1-i}
     return c.astype(np.float16)

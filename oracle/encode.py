@@ -5,7 +5,7 @@ indices and a vector norm ("[MSE indices] ... [vector norm]"); the
 high/low channel groups come from metadata, never from a runtime guess
 [D "System Invariants"].  [D "Format Strategy"]: K and V formats are
 independent.  The QJL sign and residual-norm fields of the recipe row are
-an option of a K format (reading R29, oracle/qjl.py); the steps below are
+an option of a K format (oracle/qjl.py); the steps below are
 the MSE stage every format has.
 
 Per row x (length d) and per group G of m channels (listed ascending):
@@ -17,7 +17,8 @@ Per row x (length d) and per group G of m channels (listed ascending):
      idx_j = #{ i : T_i < w_j }                      (nearest level of w_j / r_G)
   5. pack idx LSB-first, groups concatenated.
 
-A group with ss_G == 0 stores norm +0 and every index L/2 - 1 (reading R8).
+A group with ss_G == 0 stores norm +0 and every index L/2 - 1 (a reading:
+the pages do not cover an all-zero group).
 Reconstruction of channel j in G: y_j = n_G * c[idx_j] / sqrt(m).
 """
 from __future__ import annotations
@@ -39,7 +40,7 @@ class Format:
     group_channels: np.ndarray          # int [d]: group 0 ascending, then group 1 ascending
     codebooks: List[np.ndarray]         # float16 [2^bits] per group, ascending
     signs: np.ndarray                   # int8 [d] of +-1
-    qjl_proj: Optional[np.ndarray] = None   # float32 [num_groups, m, m]: QJL projection per group (R29)
+    qjl_proj: Optional[np.ndarray] = None   # float32 [num_groups, m, m]: QJL projection per group
 
     @staticmethod
     def make(head_dim: int, group_bits: Sequence[int], signs: np.ndarray,
@@ -174,7 +175,8 @@ def unpack_group(data: np.ndarray, bits: int, m: int) -> np.ndarray:
 
 
 def pack_row(idx_groups, fmt: Format) -> np.ndarray:
-    """Row bytes: groups' bit strings concatenated, group 0 first (R9)."""
+    """Row bytes: groups' bit strings concatenated, group 0 first (a reading:
+    the pages give the field order of a group, not the bit order)."""
     return np.concatenate([pack_group(i, b) for i, b in zip(idx_groups, fmt.group_bits)], axis=-1)
 
 

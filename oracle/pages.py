@@ -7,7 +7,8 @@ read back through block tables.  [D "Data Ownership"]: the page cache owns
 vLLM-style uint8 pages.  [D "Error Model"]: slots outside the allocated
 pages are IndexErrors.
 
-Layout (readings R10, R11, R24): pages are [num_blocks][num_kv_heads][tile].
+Layout (the pages fix slot -> block -> offset -> row only; the arrangement
+inside a tile is this implementation's reading): pages are [num_blocks][num_kv_heads][tile].
 A tile holds the index plane of block_size packed rows followed by the norm
 plane, fp16 little-endian, group-major, with the 16 rows of a block in
 interleaved slots: the norm of group g for the row at in-block offset t sits
@@ -22,7 +23,7 @@ row t sits at ((16*(t % 4) + b // c)*4 + t // 4)*c + b % c, i.e. 64 runs of
 4*c bytes, run 16*q + j holding bytes [c*j, c*(j+1)) of rows q, q+4, q+8,
 q+12 in that order; other V formats use the K layout.
 
-QJL K formats (reading R29): each row's index bytes are its MSE indices
+QJL K formats (oracle/qjl.py): each row's index bytes are its MSE indices
 followed by its sign string (oracle/qjl.py), and the norm plane holds the
 vector norms as above followed by the residual norms in the same
 arrangement: residual norm of group g at block_size*row_bytes +

@@ -1,8 +1,8 @@
-"""QJL residual stage of a channel group (reading R29).  Test infrastructure.
+"""QJL residual stage of a channel group (a reading).  Test infrastructure.
 
 [D "Recipe Strategy"]: each group of a recipe row stores
 [MSE indices][QJL signs][vector norm][residual norm].  The pages name the
-fields and nothing more.  Reading R29 takes the quantised
+fields and nothing more.  The reading taken here is the quantised
 Johnson-Lindenstrauss transform as published with TurboQuant's
 inner-product quantiser: after the MSE stage, the group's residual is
 projected by an m x m matrix of i.i.d. standard normal entries (passed in,

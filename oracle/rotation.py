@@ -4,7 +4,7 @@
 workloads fix the rotation as seeded +-1 signs followed by a Walsh-Hadamard
 transform scaled by 1/sqrt(d).
 
-Reading R1: signs first, then the Sylvester (natural-order) Hadamard matrix
+Reading of an open point: signs first, then the Sylvester (natural-order) Hadamard matrix
 H_d with H[i][j] = (-1)^popcount(i & j), then 1/sqrt(d):
 
     R = H_d diag(s) / sqrt(d),      R^-1 = R^T = diag(s) H_d / sqrt(d).

@@ -1,4 +1,4 @@
-"""Pins of the oracle's QJL residual stage (oracle/qjl.py, reading R29).
+"""Pins of the oracle's QJL residual stage (oracle/qjl.py).
 
 The pages only name the fields ([D "Recipe Strategy"]: [MSE indices][QJL
 signs][vector norm][residual norm]); these tests pin the reading to what
