@@ -167,6 +167,37 @@ class Bench:
         torch.cuda.synchronize()
         return sorted(a.elapsed_time(b) for a, b in ev)
 
+    def capture(self):
+        """One graph per layer pool holding that layer's step (the write of
+        the current tokens, the decode and its merge): replaying it issues
+        the same kernels with the same arguments, without the host's
+        per-call enqueue work."""
+        torch = self.torch
+        for i in range(2 * self.L):   # eager warm-up (library state, allocator)
+            self.step(i)
+        torch.cuda.synchronize()
+        self.graphs = []
+        for layer in range(self.L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(layer)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def timed_graph(self, steps, warmup):
+        """Wall time per layer step (ms) replaying the captured steps."""
+        torch = self.torch
+        if not getattr(self, "graphs", None):
+            self.capture()
+        for i in range(warmup):
+            self.graphs[i % self.L].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.graphs[(warmup + i) % self.L].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
     def timed(self, steps, warmup):
         torch = self.torch
         for i in range(warmup):
@@ -409,7 +440,8 @@ def main():
     flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     b = Bench(index, splits=args.splits)
     ms_step, dec_warm = b.timed(args.steps, args.warmup)
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step")
+    ms_graph = b.timed_graph(args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {ms_graph * 1e3:.1f} us/step replayed as a graph")
     dec_ms = b.timed_cold(args.steps, args.warmup, flush)
     w = b.w
     step_bytes = b.decode_bytes + b.write_bytes
@@ -429,6 +461,9 @@ def main():
                    "layers_cycled": b.L, "step": "tq_write_kv(current token) + tq_decode_paged",
                    "parallelism": "single GPU"},
         "us_per_layer_step": round(ms_step * 1e3, 2),
+        "us_per_layer_step_graph": round(ms_graph * 1e3, 2),
+        "step_launch": "calls issued one by one (value, us_per_layer_step); us_per_layer_step_graph replays the "
+                       "same step captured as a HIP graph, slower here than the three eager launches",
         "decode_us": stats_us(dec_ms),
         "decode_us_layers_cycled": stats_us(dec_warm),
         "decode_GBs_median": round(b.decode_bytes / (dec_ms[len(dec_ms) // 2] * 1e-3) / 1e9, 1),
@@ -465,10 +500,12 @@ def main():
         b4 = Bench(4)
         n4 = max(10, args.steps // 2)
         ms4, d4w = b4.timed(n4, args.warmup)
-        log(f"secondary timed: {ms4 * 1e3:.1f} us/step")
+        ms4g = b4.timed_graph(n4, args.warmup)
+        log(f"secondary timed: {ms4 * 1e3:.1f} us/step, {ms4g * 1e3:.1f} as a graph")
         d4 = b4.timed_cold(n4, args.warmup, flush)
         a4 = sum(d4) / len(d4)
         result["secondary"] = {"workload": b4.w.name, "us_per_layer_step": round(ms4 * 1e3, 2),
+                               "us_per_layer_step_graph": round(ms4g * 1e3, 2),
                                "decode_us": stats_us(d4), "decode_us_layers_cycled": stats_us(d4w),
                                "decode_us_avg": round(a4 * 1e3, 2),
                                "decode_GBs": round(b4.decode_bytes / (a4 * 1e-3) / 1e9, 1),
