@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   __shared__ float qt[8][D];        // scratch: rotation, then the projected query
   __shared__ half8_t bop[2 * NT][64];
   __shared__ float wmse[8], wq[8];
-  __shared__ uint16_t cbk[2][16], cbv[16];
+  __shared__ uint16_t cbv[16];
+  __shared__ uint32_t cbpair[NG][256];   // per K group: two codes (c0 | c1 << bits) -> (cb[c0], cb[c1])
   __shared__ __attribute__((aligned(16))) uint8_t ktile[kDecWaves][kKTileMax];
   __shared__ __attribute__((aligned(16))) uint8_t vtile[kDecWaves][kVTileMax];
   __shared__ float st_o[kDecWaves][8][D];
@@ -256,11 +257,11 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     }
     qt[g][c] = x;
   }
-  if (tid < 32) {
-    const int g = tid >> 4, i = tid & 15;
-    cbk[g][i] = kf.cb[g][i];
-  } else if (tid < 48) {
-    cbv[tid - 32] = vf.cb[0][tid - 32];
+  if (tid < 16) cbv[tid] = vf.cb[0][tid];
+  for (int e = tid; e < NG * 256; e += 64 * kDecWaves) {
+    const int g = e >> 8, key = e & 255, bits = kf.bits[g];
+    const int c0 = key & ((1 << bits) - 1), c1 = (key >> bits) & ((1 << bits) - 1);
+    cbpair[g][key] = (uint32_t)kf.cb[g][c0] | ((uint32_t)kf.cb[g][c1] << 16);
   }
   for (int hs = 1; hs < D; hs <<= 1) {
     __syncthreads();
@@ -412,11 +413,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       for (int y = 0; y < bits; ++y) word |= (uint32_t)src[y] << (8 * y);
       u32x4_t av;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t c0 = (word >> (bits * 2 * e2)) & ((1u << bits) - 1u);
-        const uint32_t c1 = (word >> (bits * (2 * e2 + 1))) & ((1u << bits) - 1u);
-        av[e2] = (uint32_t)cbk[g][c0] | ((uint32_t)cbk[g][c1] << 16);
-      }
+      for (int e2 = 0; e2 < 4; ++e2) av[e2] = cbpair[g][(word >> (2 * bits * e2)) & ((1u << (2 * bits)) - 1u)];
       const half8_t ah = __builtin_bit_cast(half8_t, av);
       if (g == 0) acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bop[t][lane], acc0, 0, 0, 0);
       else acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bop[t][lane], acc1, 0, 0, 0);
