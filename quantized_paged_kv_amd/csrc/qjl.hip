@@ -195,6 +195,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   __shared__ half8_t bop[2 * NT][64];
   __shared__ float wmse[8], wq[8];
   __shared__ uint16_t cbv[16];
+  __shared__ uint32_t vpair[16];         // 2-bit V: two codes (c0 | c1 << 2) -> (cb[c0], cb[c1])
   __shared__ uint32_t cbpair[NG][256];   // per K group: two codes (c0 | c1 << bits) -> (cb[c0], cb[c1])
   __shared__ __attribute__((aligned(16))) uint8_t ktile[kDecWaves][kKTileMax];
   __shared__ __attribute__((aligned(16))) uint8_t vtile[kDecWaves][kVTileMax];
@@ -257,7 +258,10 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     }
     qt[g][c] = x;
   }
-  if (tid < 16) cbv[tid] = vf.cb[0][tid];
+  if (tid < 16) {
+    cbv[tid] = vf.cb[0][tid];
+    vpair[tid] = (uint32_t)vf.cb[0][tid & 3] | ((uint32_t)vf.cb[0][(tid >> 2) & 3] << 16);
+  }
   for (int e = tid; e < NG * 256; e += 64 * kDecWaves) {
     const int g = e >> 8, key = e & 255, bits = kf.bits[g];
     const int c0 = key & ((1 << bits) - 1), c1 = (key >> bits) & ((1 << bits) - 1);
@@ -490,12 +494,30 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       const uint4 x = *reinterpret_cast<const uint4*>(run);
       vw[0] = x.x; vw[1] = x.y; vw[2] = x.z; vw[3] = x.w;
     }
+    if constexpr (VB == 2) {
+      // two tokens' codes of a dim side by side: each token word's 2-bit
+      // codes spread to 4-bit slots, the second token's shifted by 2, so one
+      // 4-bit field is the pair-table key of (token i, token i + 1)
+      auto spread = [](uint32_t x) -> uint32_t {
+        x = (x | (x << 8)) & 0x00FF00FFu;
+        x = (x | (x << 4)) & 0x0F0F0F0Fu;
+        return (x | (x << 2)) & 0x33333333u;
+      };
+      const uint32_t w01 = spread(vw[0]) | (spread(vw[1]) << 2);
+      const uint32_t w23 = spread(vw[2]) | (spread(vw[3]) << 2);
 #pragma unroll
-    for (int u = 0; u < ND; ++u) {
-      half4_t avv;
+      for (int u = 0; u < ND; ++u) {
+        const u32x2_t pv = {vpair[(w01 >> (4 * u)) & 15u], vpair[(w23 >> (4 * u)) & 15u]};
+        o_acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, pv), pb, o_acc[u], 0, 0, 0);
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) avv[i] = __builtin_bit_cast(_Float16, cbv[(vw[i] >> (VB * u)) & ((1u << VB) - 1u)]);
-      o_acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(avv, pb, o_acc[u], 0, 0, 0);
+      for (int u = 0; u < ND; ++u) {
+        half4_t avv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) avv[i] = __builtin_bit_cast(_Float16, cbv[(vw[i] >> (VB * u)) & ((1u << VB) - 1u)]);
+        o_acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(avv, pb, o_acc[u], 0, 0, 0);
+      }
     }
   }
   // ---- wave states: column sums over the 4 token groups
