@@ -313,15 +313,18 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       }
       __syncthreads();
       if (r0 + RS < D) fetch_slice(r0 + RS);   // in flight while this slice is used
-      if (tid < 8 * RS) {
-        const int g = tid / RS, r = tid - g * RS;
+      {   // 8 heads x 32 rows x 2 halves of the sum = 512 threads; halves added across lanes l, l ^ 1
+        static_assert(8 * RS * 2 == 64 * kDecWaves, "one thread per (head, row, half)");
+        const int half = tid & 1, rest = tid >> 1;
+        const int g = rest / RS, r = rest - g * RS;
         const int O = r0 + r, grp = O / M;
-        const float* srow = srows + r * (M + 1);
-        const float* qv = qg[g] + grp * M;
+        const float* srow = srows + r * (M + 1) + half * (M / 2);
+        const float* qv = qg[g] + grp * M + half * (M / 2);
         float acc = 0.f;
 #pragma unroll 16
-        for (int j = 0; j < M; ++j) acc = __builtin_fmaf(srow[j], qv[j], acc);
-        qt[g][O] = acc;
+        for (int j = 0; j < M / 2; ++j) acc = __builtin_fmaf(srow[j], qv[j], acc);
+        acc += __shfl_xor(acc, 1);
+        if (half == 0) qt[g][O] = acc;
       }
       __syncthreads();
     }
@@ -414,7 +417,9 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       const int bits = kf.bits[g];
       const uint8_t* src = krow + kf.grp_byte_off[g] + pos * bits / 8;   // 8 codes = `bits` whole bytes
       uint32_t word = 0;
-      for (int y = 0; y < bits; ++y) word |= (uint32_t)src[y] << (8 * y);
+      if (bits == 4) word = *reinterpret_cast<const uint32_t*>(src);         // 4-byte aligned
+      else if (bits == 2) word = *reinterpret_cast<const uint16_t*>(src);    // 2-byte aligned
+      else for (int y = 0; y < bits; ++y) word |= (uint32_t)src[y] << (8 * y);
       u32x4_t av;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) av[e2] = cbpair[g][(word >> (2 * bits * e2)) & ((1u << (2 * bits)) - 1u)];
