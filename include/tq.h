@@ -207,9 +207,9 @@ tq_status tq_tile_bytes(const tq_format* fmt, int32_t block_size, int32_t* row_i
  *                 that token's rows are not written.
  * A K format with the QJL stage adds a second kernel on the same stream
  * that computes each written row's residual, signs and residual norm.
- * Status: VALUE (shapes, dtype, formats, NULLs, qjl set on the V format or
- * qjl_proj NULL), UNSUPPORTED_FORMAT (block_size != 16), DEVICE (launch
- * failure), else OK.
+ * Status: VALUE (shapes, dtype, formats, NULLs, qjl set on the V format,
+ * qjl_proj NULL or not 16-byte aligned), UNSUPPORTED_FORMAT (block_size !=
+ * 16), DEVICE (launch failure), else OK.
  */
 tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype, int64_t num_tokens,
                       int32_t num_kv_heads, const int64_t* slot_mapping, uint8_t* k_pages,

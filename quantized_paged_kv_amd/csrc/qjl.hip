@@ -79,10 +79,28 @@ __global__ __launch_bounds__(64 * kWriteWaves) void qjl_write_kernel(QjlWritePar
   const DevFormat& f = p.f;
   const int m = f.m, ng = f.ng;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // projection rows padded to m + 1 floats (lanes read different rows)
-  for (int e = tid; e < ng * m * m; e += 64 * kWriteWaves) {
-    const int row = e / m, j = e - row * m;
-    sproj[row * (m + 1) + j] = p.a.proj[e];
+  // projection rows padded to m + 1 floats (lanes read different rows);
+  // every 16-byte load of a thread is issued before any is stored, so the
+  // staging costs one memory round trip (ng m m = D m <= 16384 floats:
+  // at most 16 loads per thread)
+  {
+    constexpr int NV = D * D / 4 / (64 * kWriteWaves);   // float4 per thread when m = D (the most)
+    float4 v[NV];
+    const int n4 = ng * m * m / 4;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int e = tid + 64 * kWriteWaves * k;
+      if (e < n4) v[k] = reinterpret_cast<const float4*>(p.a.proj)[e];
+    }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int e = tid + 64 * kWriteWaves * k;
+      if (e < n4) {
+        const int row = (4 * e) / m, j = 4 * e - row * m;
+        float* dst = sproj + row * (m + 1) + j;
+        dst[0] = v[k].x; dst[1] = v[k].y; dst[2] = v[k].z; dst[3] = v[k].w;
+      }
+    }
   }
   __syncthreads();
   const int64_t rows = p.a.num_tokens * p.a.H;

@@ -392,6 +392,8 @@ extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype
     tq_status st = check_format(fmts[t], names[t]);
     if (st != TQ_OK) return st;
     if (t == 1 && fmts[t]->qjl) return set_error(TQ_ERR_VALUE, "the QJL stage is defined for K formats only");
+    if (t == 0 && fmts[t]->qjl && (reinterpret_cast<uintptr_t>(fmts[t]->qjl_proj) & 15))
+      return set_error(TQ_ERR_VALUE, "qjl_proj must be 16-byte aligned");
     if (!pages[t]) return set_error(TQ_ERR_VALUE, std::string(names[t]) + " pages are NULL");
     if (d && fmts[t]->head_dim != d) return set_error(TQ_ERR_VALUE, "K and V head_dim differ");
     d = fmts[t]->head_dim;

@@ -266,3 +266,14 @@ def test_qjl_alignment_checked_before_launch():
             self.c = cs
     assert _call_decode(kf=_F(kq), kp=0x1000, vp=0x2000) == tq.TQ_ERR_VALUE
     assert "aligned" in tq._lib.tq_last_error().decode()
+
+
+def test_qjl_write_alignment_checked_before_launch():
+    s = signs(0, 1, 128)
+    f4 = tq.Format(128, [4], s)
+
+    class _F:
+        def __init__(self, cs):
+            self.c = cs
+    assert _call_write(kf=_F(_qjl_c(f4, proj=0x1008))) == tq.TQ_ERR_VALUE
+    assert "aligned" in tq._lib.tq_last_error().decode()
