@@ -2,7 +2,7 @@
 of the quantise-on-write / paged-decode / split-merge path runs in the HIP
 kernels of libtq.so; torch supplies device memory and the current stream.
 
-The library must have been built (``python -m quantized_paged_kv_amd._build``
+The library must have been built (``python quantized_paged_kv_amd/_build.py``
 or ``__graft_entry__.build()``); importing this package without it raises,
 there is no fallback of any kind.
 
@@ -56,7 +56,7 @@ def _load(path: str = LIB_PATH):
     # second copy of the runtime.
     import torch  # noqa: F401
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m quantized_paged_kv_amd._build`")
+        raise ImportError(f"{path} is not built; run `python quantized_paged_kv_amd/_build.py`")
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, u64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float

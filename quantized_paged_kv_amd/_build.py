@@ -1,6 +1,7 @@
 """Build libtq.so in-tree with hipcc for gfx950.
 
-Usage: python -m quantized_paged_kv_amd._build   (or build() from Python)
+Usage: python quantized_paged_kv_amd/_build.py [-v]   (or __graft_entry__.build());
+the script is run by path, since importing the package needs the library.
 
 Every HIP source is compiled with the packed-FP32 target feature off, the
 quantise-on-write source additionally with -ffp-contract=off so that no
