@@ -342,6 +342,59 @@ def multi_cold(b, launches, warmup, flush, nq=2):
     return sorted(a.elapsed_time(c) for a, c in ev), b.decode_bytes + extra
 
 
+def phase_trace(index, launches, flush):
+    """Per-phase times of the decode kernel from the phase-timestamp build
+    (libtq_trace.so, TQ_PHASE_TRACE): each persistent workgroup records the
+    100 MHz real-time counter at its phase boundaries; cold calls (flush
+    before each).  Returns medians / maxima over workgroups in us."""
+    import numpy as np
+    import torch
+    b = Bench(index)
+    tq = b.tq
+    n_wg = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.zeros(16 * n_wg, dtype=torch.int64, device="cuda")
+    if not tq.set_phase_trace(buf):
+        raise SystemExit("the loaded library has no phase trace: run with the libtq_trace.so build")
+    runs = []
+    for i in range(launches):
+        buf.zero_()
+        flush_caches(flush)
+        torch.cuda._sleep(200000)
+        b.decode(i % b.L)
+        torch.cuda.synchronize()
+        runs.append(buf.view(n_wg, 16).cpu().numpy().astype(np.int64))
+    tq.set_phase_trace(None)
+    us = 0.01   # 100 MHz counter ticks
+    out = {}
+    keys = {"plan": (0, 1), "first_piece_prologue": (2, 3), "first_piece_loop": (3, 4),
+            "first_piece_epilogue": (4, 5), "second_piece_prologue": (6, 7), "second_piece_loop": (7, 8),
+            "second_piece_epilogue": (8, 9)}
+    for name, (a, c) in keys.items():
+        vals = []
+        for r in runs:
+            ok = (r[:, a] > 0) & (r[:, c] > 0)
+            vals.extend(((r[ok, c] - r[ok, a]) * us).tolist())
+        if vals:
+            v = np.array(vals)
+            out[name] = {"median": round(float(np.median(v)), 2), "max": round(float(v.max()), 2),
+                         "workgroups": int(len(v) / len(runs))}
+    ent, span, tail, pieces = [], [], [], []
+    for r in runs:
+        live = r[:, 0] > 0
+        t0 = r[live, 0].min()
+        ent.append(float(np.median(r[live, 0] - t0)) * us)
+        span.append(float(r[live, 14].max() - t0) * us)
+        tail.append(float(r[live, 14].max() - np.median(r[live, 14])) * us)
+        pieces.append(float(r[live, 15].mean()))
+    out["entry_after_first_workgroup"] = round(float(np.median(ent)), 2)
+    out["kernel_span"] = round(float(np.median(span)), 2)
+    out["exit_tail_after_median"] = round(float(np.median(tail)), 2)
+    out["pieces_per_workgroup"] = round(float(np.mean(pieces)), 3)
+    out["workload"] = b.w.name
+    out["launches"] = launches
+    return out
+
+
 def stats_us(ms):
     n = len(ms)
     return {"avg": round(sum(ms) / n * 1e3, 2), "p10": round(ms[n // 10] * 1e3, 2),
@@ -419,6 +472,8 @@ def main():
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="only report per-phase decode times from the phase-timestamp build (libtq_trace.so)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device to device 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -430,6 +485,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "launches": 5}), flush=True)
+        return
+    if args.phase_trace:
+        os.environ["TQ_LIB_PATH"] = os.path.join(ROOT, "quantized_paged_kv_amd", "libtq_trace.so")
+        import torch
+        flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        print(json.dumps({"phase_trace_us": phase_trace(NAMES[args.workload], args.steps, flush)}), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode shards by kv head or "

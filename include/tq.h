@@ -77,8 +77,8 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 #define TQ_BLOCK_SIZE 16
 
 /*
- * One tensor's storage format (K and V each get their own: [D "System
- * Invariants"], "Key and value formats are independent").  Host struct,
+ * One tensor's storage format.  K and V each get their own, chosen
+ * independently of each other ([D "System Invariants"]).  Host struct,
  * read during the call.
  *
  *   head_dim        64 or 128.
@@ -123,13 +123,14 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
  *   a     = norm (the stored fp16 value) * sqrt(head_dim / m)
  *   r_j   = w_j - a * codebook[idx_j]                 residual, j in G
  *   rnorm = fp16 RNE of sqrt(pairwise-tree sum of r_j^2 / head_dim)
- *   z_i   = sum_j proj[g][i][j] * r_j;  sign bit i = (z_i < 0)
+ *   z_i   = sum_j proj[g][i][j] * r_j, evaluated from +0 over j ascending,
+ *           each product and then each partial sum rounded to fp64 (never
+ *           fused); sign bit i = (z_i < 0)
  * Decoding adds, per group, sqrt(pi/2) / m * rnorm * sum_i (P_g q~_G)_i
  * (1 - 2 bit_i) to the rotated score q~ . k (q~ the rotated, normalised
  * query restricted to G): an unbiased estimate of q~ . (y_G - y_hat_G).
- * The sign bits are fixed by fp64 sums whose order the caller does not
- * see; an implementation that orders them differently may differ only for
- * a z_i within rounding of zero.
+ * The fixed order makes every sign bit well defined, also for a z_i whose
+ * exact value lies within rounding of zero.
  */
 typedef struct tq_format {
   int32_t head_dim;
@@ -368,6 +369,21 @@ tq_status tq_decode_dense(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
                           tq_dtype kv_dtype, int32_t capacity, const int32_t* lens, float scale,
                           const float* hist_out, const float* hist_lse, void* out,
                           tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream);
+
+/*
+ * Phase timestamps of the paged decode kernel, for performance analysis
+ * only.  In a library built with TQ_PHASE_TRACE defined, every later
+ * tq_decode_paged / tq_decode_paged_multi call (non-QJL formats) has thread
+ * 0 of each persistent workgroup w write 16 uint64 values to
+ * buf[16 w .. 16 w + 15]: the 100 MHz real-time counter at kernel entry
+ * (0), when the work split is known (1), per piece i < 3 at its start
+ * (2 + 4i), at the start (3 + 4i) and end (4 + 4i) of its block loop and at
+ * the end of its epilogue (5 + 4i), at exit (14), and the number of pieces
+ * (15).  buf: device, at least 16 * (number of CUs) values, or NULL to stop.
+ * Status: OK, or UNSUPPORTED_FORMAT in a library built without the option
+ * (the normal build; the pointer is then ignored).
+ */
+tq_status tq_debug_phase_trace(uint64_t* buf /* device, nullable */);
 
 #ifdef __cplusplus
 }

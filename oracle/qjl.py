@@ -18,7 +18,12 @@ idx_j), all in float64:
   r_j   = w_j - a_G * c[idx_j]               residual in w units (j in G)
   ssr   = tree_sum(r_j^2)                    same pinned tree as the norm
   gamma = fp16_rne(sqrt(ssr / d))            = |e|, e = r / sqrt(d) (y units)
-  z_i   = sum_j S_G[i, j] r_j                (S_G float32 entries, exact in fp64)
+  z_i   = sum_j S_G[i, j] r_j                (S_G float32 entries, exact in fp64),
+          evaluated in one fixed order: z = +0, then for j = 0, 1, ..., m-1
+          (ascending position in the group) z = z + S_G[i, j] * r_j with the
+          product rounded to fp64 and then the sum rounded (no fused
+          multiply-add).  The order fixes the sign of a sum whose exact value
+          lies within rounding of zero.
   bit_i = 1 if z_i < 0 else 0                (bit 1 stands for sign -1)
 
 Decoding (rotated, normalised domain, q~ = H (s * q) / sqrt(d)):
@@ -40,25 +45,46 @@ from .codebook import f64_to_f16_bits
 from .encode import Format, tree_sum
 
 
+def project(r: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """z[..., i] = sum_j S[i, j] r[..., j] in the order the stage defines:
+    start from +0 and add the terms for j = 0, 1, ... in turn, each product
+    rounded to fp64, then each sum rounded (numpy's elementwise multiply and
+    add, never fused)."""
+    r = np.asarray(r, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)          # float32 entries: exact
+    z = np.zeros(r.shape[:-1] + (S.shape[0],))
+    for j in range(S.shape[1]):
+        z = z + r[..., j:j + 1] * S[:, j]
+    return z
+
+
+def residuals(w: np.ndarray, idx_groups, norm_bits: np.ndarray, fmt: Format):
+    """Per group, the MSE residual r_j = w_j - a_G c[idx_j] of rotated rows
+    w[..., d] in w units, [..., m] in the group's listed channel order."""
+    w = np.asarray(w, dtype=np.float64)
+    d, m = fmt.head_dim, fmt.group_size
+    kappa = math.sqrt(d / m)
+    norms = np.asarray(norm_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    out = []
+    for g, ch in enumerate(fmt.groups()):
+        c = fmt.codebooks[g].astype(np.float64)
+        a = norms[..., g] * kappa
+        out.append(w[..., ch] - a[..., None] * c[idx_groups[g]])
+    return out
+
+
 def residual_fields(w: np.ndarray, idx_groups, norm_bits: np.ndarray, fmt: Format):
     """QJL fields of rotated rows w[..., d] whose MSE stage gave idx_groups
     (list of [..., m]) and norm_bits [..., G] -> (sign bits uint8
     [..., G, m], residual-norm fp16 bits uint16 [..., G])."""
     if not fmt.qjl:
         raise ValueError("format has no QJL stage")
-    w = np.asarray(w, dtype=np.float64)
-    d, m = fmt.head_dim, fmt.group_size
-    kappa = math.sqrt(d / m)
-    norms = np.asarray(norm_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+    d = fmt.head_dim
     bits, gam = [], []
-    for g, ch in enumerate(fmt.groups()):
-        c = fmt.codebooks[g].astype(np.float64)
-        a = norms[..., g] * kappa
-        r = w[..., ch] - a[..., None] * c[idx_groups[g]]
+    for g, r in enumerate(residuals(w, idx_groups, norm_bits, fmt)):
         ssr = tree_sum(r * r)
         gam.append(f64_to_f16_bits(np.sqrt(ssr / d)).astype(np.uint16))
-        S = fmt.qjl_proj[g].astype(np.float64)
-        z = r @ S.T                                        # z_i = sum_j S[i, j] r_j
+        z = project(r, fmt.qjl_proj[g])
         bits.append((z < 0).astype(np.uint8))
     return np.stack(bits, axis=-2), np.stack(gam, axis=-1)
 

@@ -21,7 +21,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_LIB_PATH selects another build of the library (for example the
+# phase-timestamp variant libtq_trace.so); the default is the in-tree libtq.so
+LIB_PATH = os.environ.get("TQ_LIB_PATH") or os.path.join(_HERE, "libtq.so")
 
 TQ_OK, TQ_ERR_VALUE, TQ_ERR_INDEX, TQ_ERR_UNSUPPORTED_FORMAT, TQ_ERR_NOT_FOUND, TQ_ERR_DEVICE = range(6)
 TQ_F32, TQ_BF16 = 0, 1
@@ -74,6 +76,7 @@ def _load(path: str = LIB_PATH):
                                    P, u64, P, i32, P, P, P], i32),
         "tq_split_merge": ([P, P, i32, i32, i32, i32, P, i32, P, P], i32),
         "tq_decode_dense": ([P, i32, i32, i32, i32, i32, P, P, i32, i32, P, f32, P, P, P, i32, P, P, P], i32),
+        "tq_debug_phase_trace": ([P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -377,6 +380,18 @@ def decode_dense(q, k_win, v_win, lens, scale: float, hist_out=None, hist_lse=No
     return out, lse
 
 
+def set_phase_trace(buf) -> bool:
+    """Phase-timestamp buffer (device uint64 tensor, 16 values per CU) for the
+    decode kernel; None stops recording.  Returns False when the loaded
+    library was built without TQ_PHASE_TRACE."""
+    st = _lib.tq_debug_phase_trace(_ptr(buf))
+    if st == TQ_ERR_UNSUPPORTED_FORMAT:
+        return False
+    _check(st)
+    return True
+
+
 __all__ = ["Format", "UnsupportedFormatError", "DeviceError", "lloyd_max_codebook", "alloc_pages",
-           "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged", "split_merge", "decode_dense",
+           "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged",
+           "split_merge", "decode_dense", "set_phase_trace",
            "LIB_PATH", "BLOCK_SIZE"]

@@ -1,6 +1,6 @@
 """Build libtq.so in-tree with hipcc for gfx950.
 
-Usage: python quantized_paged_kv_amd/_build.py [-v]   (or __graft_entry__.build());
+Usage: python quantized_paged_kv_amd/_build.py [-v] [--trace]   (or __graft_entry__.build());
 the script is run by path, since importing the package needs the library.
 
 Every HIP source is compiled with the packed-FP32 target feature off, the
@@ -46,16 +46,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+TRACE_LIB = os.path.join(HERE, "libtq_trace.so")
+
+
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compile every source and link libtq.so; trace=True builds the
+    phase-timestamp variant (TQ_PHASE_TRACE, see tq_debug_phase_trace) as
+    libtq_trace.so instead, for performance analysis only."""
+    bdir = BUILD + ("_trace" if trace else "")
+    lib = TRACE_LIB if trace else LIB
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
     procs = []
     objs = []
     t0 = time.time()
     for src, extra in SOURCES.items():
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         objs.append(obj)
-        cmd = [cc, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *COMMON, *extra, *(["-DTQ_PHASE_TRACE"] if trace else []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -71,16 +79,16 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if failed:
         msg = "\n".join(f"--- {s}\n{t}" for s, t in failed)
         raise RuntimeError(f"HIP build failed:\n{msg}")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)
-    return LIB
+        print(f"built {lib} in {time.time() - t0:.1f}s", flush=True)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
+    build(verbose="-v" in sys.argv, trace="--trace" in sys.argv)

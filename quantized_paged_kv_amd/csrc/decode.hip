@@ -108,7 +108,31 @@ struct DecodeParams {
   int32_t v_half;            // LUT half that V reads
   int32_t q_f32, out_f32;
   int32_t q_bytes;           // size of q in bytes (< 2^31)
+#ifdef TQ_PHASE_TRACE
+  uint64_t* trace;           // per workgroup kTraceSlots timestamps (or null)
+#endif
 };
+
+// Phase timestamps (built with TQ_PHASE_TRACE only): thread 0 of each
+// workgroup records the 100 MHz real-time counter at kernel entry, when the
+// plan is known, and per piece (up to 3) at its start, at the start and the
+// end of its block loop and at the end of its epilogue; slot 14 at exit,
+// slot 15 the number of pieces.
+constexpr int kTraceSlots = 16;
+#ifdef TQ_PHASE_TRACE
+#define TQ_MARK(slot)                                                                       \
+  do {                                                                                     \
+    if (p.trace && threadIdx.x == 0 && (slot) < kTraceSlots)                               \
+      p.trace[(int64_t)blockIdx.x * kTraceSlots + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define TQ_MARK_VALUE(slot, v)                                                       \
+  do {                                                                               \
+    if (p.trace && threadIdx.x == 0) p.trace[(int64_t)blockIdx.x * kTraceSlots + (slot)] = (v); \
+  } while (0)
+#else
+#define TQ_MARK(slot) do {} while (0)
+#define TQ_MARK_VALUE(slot, v) do {} while (0)
+#endif
 
 
 __device__ __forceinline__ uint32_t lut_addr(uint32_t packed, uint32_t lane_off, int byte) {
@@ -128,9 +152,16 @@ __device__ __forceinline__ float row_ror8(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
-// x * (fp16 half HI of w) in one v_fma_mix (the f16 operand is read as is:
-// f16 denormal norms count as zero, which only drops contributions below
-// 2^-14 relative to the row's scale)
+// Norm products.  K and V norms are applied as the f16 operand of a
+// v_fma_mix (single rounding; under this library's build, fp16/fp64
+// denormals on, the mix instructions take f16 subnormal operands and give
+// subnormal fp16 results as they are: measured on gfx950, and pinned by
+// the tiny-norm parity tests).  The fp16 P.V operand p * n_V carries a
+// power-of-two factor 2^E per wave (E tracks the largest V norm seen, so
+// that p * n_V * 2^E stays inside fp16's normal range whatever the scale of
+// the rows; see the block loop).
+
+// x * (fp16 half HI of w) in one v_fma_mix, rounded once
 template <int HI>
 __device__ __forceinline__ float mul_h(float x, uint32_t w) {
   float r;
@@ -152,6 +183,16 @@ __device__ __forceinline__ uint32_t mul_h2(float x0, float x1, uint32_t w) {
   asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x0), "v"(w));
   asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x1), "v"(w));
   return r;
+}
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2_t as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2_t, x); }
+// fp16 bit pattern of 2^(15 - e), minus one, for e in [-1, 39]: V norms above
+// it would make p * n_V * 2^e overflow fp16's range (e = -1: every finite
+// fp16 is below the bound)
+__device__ __forceinline__ uint32_t v_bound_m1(int e) {
+  const int k = 15 - e;
+  const uint32_t h = k >= 16 ? 0x7C00u : (k >= -14 ? (uint32_t)(k + 15) << 10 : 1u << (k + 24));
+  return h - 1u;
 }
 // max of two floats known not to be NaN (no canonicalisation)
 __device__ __forceinline__ float max_nn(float a, float b) {
@@ -466,6 +507,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);
   const int lane = tid & 63;
+  TQ_MARK(0);
   // ---- wave 0 plans: it alone reads the context lengths and splits the
   // work, and publishes its results in LDS; wave 1 meanwhile spreads the
   // small per-call tables (kernel arguments read at compile-time offsets
@@ -478,7 +520,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     {
       const __attribute__((address_space(4))) uint32_t* ka =
           (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+#ifdef TQ_PHASE_TRACE
+      static_assert(sizeof(DecodeParams) <= 8 * 64, "argument block spans more lines than are touched");
+      const uint32_t k7 = ka[112];
+      asm volatile("" ::"s"(k7));
+#else
       static_assert(sizeof(DecodeParams) <= 7 * 64, "argument block spans more lines than are touched");
+#endif
       const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96];
       asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6));
     }
@@ -530,6 +578,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     s_par[lane] = x;
   }
   __syncthreads();   // plan, lengths and s_par written
+  TQ_MARK(1);
 
   // ---- the plan (uniform values)
   const int R = uni(s_plan[0]);
@@ -561,7 +610,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
     }
   }
-  if (r0 >= r1) return;  // uniform across the workgroup
+  if (r0 >= r1) {  // uniform across the workgroup
+    TQ_MARK(14);
+    TQ_MARK_VALUE(15, 0);
+    return;
+  }
 
   auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
@@ -647,6 +700,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   int pos = r0;
   bool first = true;
   bool tables_built = false;
+  int n_done = 0;   // pieces this workgroup has run (phase trace)
   while (pos < r1) {
     const int vb0 = pos - off + p.seg_cost;   // position of the segment's block 0
     const int b0 = off > p.seg_cost ? off - p.seg_cost : 0;
@@ -670,6 +724,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 
       if (!first) __syncthreads();   // the previous piece's states have been read
       first = false;
+      TQ_MARK(2 + 4 * n_done);
 
       // -------- blocks of the piece are handed out per kv head: part q of a
       // head starts with piece blocks q, q + NPW and q + 2 NPW, then takes the
@@ -887,14 +942,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
       }
       __syncthreads();  // operands, counters and block-table entries ready
+      TQ_MARK(3 + 4 * n_done);
       int ph2v = bt_at(idx_2);
       int g3 = grab();
       const float w_col = ldexpf(p.score_mul, -s_qexp[8 * hl + gq]);
       const half8_t* qb = qv_all + hl * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
 
       // -------- stream this wave's blocks of the piece
+      // online softmax state per column: running max m_run (raw score
+      // units), sum l_run and accumulator o_acc of the weights
+      // 2^(w_col (s - m_run) + e_run); e_run (the same in every lane) is the
+      // power of two that keeps p * n_V * 2^e_run in fp16's normal range:
+      // 15 - ex, 2^(ex-1) <= the largest V norm so far < 2^ex (39 before any)
       float m_run = -INFINITY, l_run = 0.f;
-      float nm = 0.f;   // -m_run * w_col (0 while m_run is -inf)
+      int e_run = 39;
+      uint32_t v_hi = v_bound_m1(39);
+      float nm = 39.f;   // exp2 offset: e_run - w_col m_run (e_run while m_run is -inf)
       float4_t o_acc[C::R];
 #pragma unroll
       for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -975,9 +1038,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         // stage boundary: keeps the scheduler from hoisting the next stage's
         // table reads above these MFMAs (bounds the live registers)
         __builtin_amdgcn_sched_barrier(0);
+        const int tok0 = 16 * b;
+        const bool part = !(ok && tok0 + 16 <= ctx_all);   // partial or skipped block (wave-uniform)
+        // tokens a + 4e of this lane that count (all, unless part)
+        auto live = [&](int e) { return ok && (tok0 + a + 4 * e) < ctx_col; };
         // raw scores of this lane's 4 tokens for q head gq: sr = (q . c) * n_K;
         // the exp2-domain score is w_col * sr (w_col > 0), folded into one fma
-        const int tok0 = 16 * b;
         float sc[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -991,74 +1057,111 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
           sc[e] = v;
         }
-        if (!(ok && tok0 + 16 <= ctx_all)) {   // partial or skipped block (wave-uniform branch)
+        if (part) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sc[e] = (ok && (tok0 + a + 4 * e) < ctx_col) ? sc[e] : -INFINITY;
+          for (int e = 0; e < 4; ++e) sc[e] = live(e) ? sc[e] : -INFINITY;
         }
         const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
         const float m_new = max_nn(m_run, bm);
-        if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+        // a V norm of this lane's tokens too large for the current e_run?
+        // (masked tokens' norm bytes may hold anything: left out)
+        u16x2_t mxv = __builtin_elementwise_max(as_u16x2(cur.vn.x), as_u16x2(cur.vn.y));
+        if (part) {
+          uint32_t vx = cur.vn.x, vy = cur.vn.y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!live(e)) {
+              if (e >> 1) vy &= ~(0xFFFFu << (16 * (e & 1)));
+              else vx &= ~(0xFFFFu << (16 * (e & 1)));
+            }
+          mxv = __builtin_elementwise_max(as_u16x2(vx), as_u16x2(vy));
+        }
+        const bool over = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(mxv, u16x2_t{(uint16_t)v_hi, (uint16_t)v_hi})) != 0u;
+        if (__builtin_amdgcn_ballot_w64((m_new > m_run) | over)) {
           asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
-          const float alpha = (m_new > m_run) ? __builtin_amdgcn_exp2f((m_run - m_new) * w_col) : 1.f;
+          int e_new = e_run;
+          if (__builtin_amdgcn_ballot_w64(over)) {
+            // 15 - ex for the largest V norm of the tile (all 16 tokens),
+            // capped at the largest finite fp16
+            const uint32_t mh = mxv[0] > mxv[1] ? mxv[0] : mxv[1];
+            const float nmax = fminf(max_rows(f16_exact<0>(mh)), 65504.f);
+            const int ex = uni((int)((__float_as_uint(nmax) >> 23) & 0xFF) - 126);
+            e_new = 15 - ex < e_run ? 15 - ex : e_run;
+            v_hi = v_bound_m1(e_new);
+          }
+          const float sh = (float)(e_new - e_run);   // <= 0
+          const float alpha = __builtin_amdgcn_exp2f((m_new > m_run) ? __builtin_fmaf(m_run - m_new, w_col, sh) : sh);
           l_run *= alpha;
 #pragma unroll
           for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
           m_run = m_new;
-          nm = (m_run == -INFINITY) ? 0.f : -m_run * w_col;
+          e_run = e_new;
+          nm = (m_run == -INFINITY) ? (float)e_run : __builtin_fmaf(-m_run, w_col, (float)e_run);
         }
         float pr[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
         l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_h2(pr[0], pr[1], cur.vn.x), mul_h2(pr[2], pr[3], cur.vn.y)});
 
-        __builtin_amdgcn_sched_barrier(0);
-        // P.V on the matrix cores: A = V (dims x tokens) per MFMA u
-        if constexpr (VK == V4) {
-          // Lookup keys pair the nibbles of two tokens for one dim, so the
-          // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
-          // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
-          const uint32_t w0 = vword(cur, 0), w1 = vword(cur, 1), w2 = vword(cur, 2), w3 = vword(cur, 3);
-          const uint32_t x1s = w1 << 4, x3s = w3 << 4;
-          const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
-          const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
-          const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
-          const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
-          constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
+        // P.V on the matrix cores: A = V (dims x tokens) per MFMA i, through
+        // `into(i, A)`
+        auto pv = [&](auto&& into) {
+          if constexpr (VK == V4) {
+            // Lookup keys pair the nibbles of two tokens for one dim, so the
+            // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
+            // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
+            const uint32_t w0 = vword(cur, 0), w1 = vword(cur, 1), w2 = vword(cur, 2), w3 = vword(cur, 3);
+            const uint32_t x1s = w1 << 4, x3s = w3 << 4;
+            const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
+            const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+            const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
+            const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
+            constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
 #pragma unroll
-          for (int k = 0; k < NB; ++k) {
+            for (int k = 0; k < NB; ++k) {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
-                                  lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
-              o_acc[2 * k + hh] =
-                  __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[2 * k + hh], 0, 0, 0);
+              for (int hh = 0; hh < 2; ++hh) {
+                const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
+                                    lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
+                into(2 * k + hh, __builtin_bit_cast(half4_t, av));
+              }
+            }
+          } else {
+            constexpr int NBY = D / 64;  // bytes per token in this lane (4 dims each)
+#pragma unroll
+            for (int k = 0; k < NBY; ++k) {
+              uint2 lk[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
+                if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
+                else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
+              }
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t w0 = (t >> 1) ? lk[0].y : lk[0].x;
+                const uint32_t w1 = (t >> 1) ? lk[1].y : lk[1].x;
+                const uint32_t w2 = (t >> 1) ? lk[2].y : lk[2].x;
+                const uint32_t w3 = (t >> 1) ? lk[3].y : lk[3].x;
+                const u32x2_t av = {__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
+                into(4 * k + t, __builtin_bit_cast(half4_t, av));
+              }
             }
           }
-        } else {
-          constexpr int NBY = D / 64;  // bytes per token in this lane (4 dims each)
+        };
+        // B operand: p * n_V in fp16 (p carrying 2^e_run), each rounded once
+        u32x2_t pw = {mul_h2(pr[0], pr[1], cur.vn.x), mul_h2(pr[2], pr[3], cur.vn.y)};
+        if (part) {
+          // a masked token's weight is 0, but its norm bytes may hold any
+          // bits (a NaN times 0 is NaN): its operand is set to +0
 #pragma unroll
-          for (int k = 0; k < NBY; ++k) {
-            uint2 lk[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
-              if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
-              else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-              const uint32_t w0 = (t >> 1) ? lk[0].y : lk[0].x;
-              const uint32_t w1 = (t >> 1) ? lk[1].y : lk[1].x;
-              const uint32_t w2 = (t >> 1) ? lk[2].y : lk[2].x;
-              const uint32_t w3 = (t >> 1) ? lk[3].y : lk[3].x;
-              const u32x2_t av = {__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
-              o_acc[4 * k + t] =
-                  __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, av), pb, o_acc[4 * k + t], 0, 0, 0);
-            }
-          }
+          for (int e = 0; e < 4; ++e)
+            if (!live(e)) pw[e >> 1] &= ~(0xFFFFu << (16 * (e & 1)));
         }
+        const half4_t pb = __builtin_bit_cast(half4_t, pw);
+        __builtin_amdgcn_sched_barrier(0);
+        pv([&](int i, half4_t av) { o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, o_acc[i], 0, 0, 0); });
       };
 
       // one block (j): issue tile j+2, look up the entry of j+3 and take the
@@ -1087,6 +1190,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // unnormalised O rows (q head g at slot row 8 w + g) and its running
       // max / sum per q head
       __syncthreads();  // every wave is done with the q operands (the slots overlay them)
+      TQ_MARK(4 + 4 * n_done);
       const int le = fresh_lane();
       l_run += lane_xor<16>(l_run, le);
       l_run += lane_xor<32>(l_run, le);
@@ -1098,8 +1202,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           for (int h = 0; h < C::R / 4; ++h)
             *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
                 float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
-        if (a == 0) {
-          s_ml[16 * wave + gq] = m_run;
+        if (a == 0) {   // the exp2-domain offset of the weights (-inf: no token), and their sum
+          s_ml[16 * wave + gq] = m_run == -INFINITY ? -INFINITY : -nm;
           s_ml[16 * wave + 8 + gq] = l_run;
         }
       }
@@ -1120,8 +1224,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int pr = live ? pr_raw : npair - 1;
         const int h2 = (int)(((float)pr + 0.5f) * p.inv_G);   // pr / G (pr < 64, G <= 8)
         const int g = pr - h2 * p.G;
-        const float wc = ldexpf(p.score_mul, -s_qexp[8 * h2 + g]);
-        float M = -INFINITY;
+        float M = -INFINITY;   // wave states: weights 2^(w s - X_w), sums l_w
         for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * wave_of_part(h2, q, HG) + g]);
         float y[ND];
 #pragma unroll
@@ -1130,7 +1233,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         for (int q = 0; q < NPW; ++q) {
           const int wq = wave_of_part(h2, q, HG);
           const float mw = s_ml[16 * wq + g];
-          const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * wc);
+          const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
           L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
           const float* srow = slots + (8 * wq + g) * C::DS + m;
 #pragma unroll
@@ -1173,7 +1276,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const bool empty = !(L > 0.f);
         const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
         const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
-        const float lse = empty ? -INFINITY : (M * wc + log2f(L)) * kLn2;
+        const float lse = empty ? -INFINITY : (M + log2f(L)) * kLn2;
         const int qi = (int)(((float)g + 0.5f) * p.inv_Gr);   // column g = (query qi, q head g - qi Gr)
         const int64_t rowq = ((int64_t)s * p.NQ + qi) * p.Hq + (grp * HG + h2) * p.Gr + (g - qi * p.Gr);
         const int d0 = ND * m;
@@ -1213,6 +1316,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
         }
       }
+      TQ_MARK(5 + 4 * n_done);
+      ++n_done;
     }
 
     // -------- next segment
@@ -1227,6 +1332,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       } while (nb_s == 0);
     }
   }
+  TQ_MARK(14);
+  TQ_MARK_VALUE(15, (uint64_t)n_done);
+  (void)n_done;
 }
 
 // ----------------------------------------------------------------- merge
@@ -1362,6 +1470,20 @@ int format_kind_v(const tq_format* f) {
 }  // namespace tq
 
 using namespace tq;
+
+#ifdef TQ_PHASE_TRACE
+static uint64_t* g_phase_trace = nullptr;
+#endif
+
+extern "C" tq_status tq_debug_phase_trace(uint64_t* buf) {
+#ifdef TQ_PHASE_TRACE
+  __atomic_store_n(&g_phase_trace, buf, __ATOMIC_RELEASE);
+  return TQ_OK;
+#else
+  (void)buf;
+  return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "library built without TQ_PHASE_TRACE");
+#endif
+}
 
 extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse, int32_t num_seqs,
                                     int32_t num_heads, int32_t num_splits, int32_t head_dim, void* out,
@@ -1540,6 +1662,9 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   p.q_f32 = q_dtype == TQ_F32;
   p.out_f32 = out_dtype == TQ_F32;
   p.q_bytes = (int32_t)q_bytes;
+#ifdef TQ_PHASE_TRACE
+  p.trace = __atomic_load_n(&g_phase_trace, __ATOMIC_ACQUIRE);
+#endif
   if (num_splits > 1) {
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (int64_t)num_seqs * num_queries * num_q_heads * num_splits * D;

@@ -10,12 +10,13 @@
 // matrix S, the signs of S r are stored with |r|, and a query q adds
 // sqrt(pi/2) / m * |r| * <S q, signs> to its score (unbiased for <q, r>).
 //
-// Write side (fp64, no fused multiply-add outside the projection sums): the
+// Write side (fp64, no fused multiply-add anywhere): the
 // rotation is recomputed with the same butterflies as the MSE stage, the
 // stored indices and norm are read back from the tile the MSE kernel wrote
 // just before on the same stream, and
 //   r_j = w_j - (norm * sqrt(d/m)) * c[idx_j],  rnorm = fp16(sqrt(tree(r^2) / d)),
-//   bit_i = (sum_j S[i][j] r_j < 0).
+//   bit_i = (sum_j S[i][j] r_j < 0), the sum taken from +0 over j ascending,
+//           each product and each partial sum rounded to fp64 in turn.
 //
 // Decode: one 8-wave workgroup per (sequence, kv head, split).  Every wave
 // takes every 8th block of the split, stages the K and V tiles in LDS and
@@ -166,7 +167,10 @@ __global__ __launch_bounds__(64 * kWriteWaves) void qjl_write_kernel(QjlWritePar
       ss[1] = __shfl(v, 32);
     }
     wave_fence();
-    // projection z_i = sum_j S[i][j] r_j (fp64 fma in j order), signs by ballot
+    // projection z_i = sum_j S[i][j] r_j: from +0, j ascending, the product
+    // and then the sum rounded to fp64 at every step (the file is compiled
+    // without contraction, so the two operations stay separate); signs by
+    // ballot
     uint64_t neg[KP];
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
@@ -175,7 +179,7 @@ __global__ __launch_bounds__(64 * kWriteWaves) void qjl_write_kernel(QjlWritePar
       const float* srow = sproj + (g * m + i) * (m + 1);
       const double* rg = r + g * m;
       double z = 0.0;
-      for (int j = 0; j < m; ++j) z = __builtin_fma((double)srow[j], rg[j], z);
+      for (int j = 0; j < m; ++j) z = z + (double)srow[j] * rg[j];
       neg[k] = __builtin_amdgcn_ballot_w64(z < 0.0);
     }
     uint8_t* sgn = tile + offs * f.row_bytes + f.sign_off;
@@ -397,7 +401,12 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   // ---- blocks of this split, every 8th to each wave
   const int col = lane & 15, gcol = col & 7, ta = lane >> 4;
   const float w_m = wmse[gcol], w_q = wq[gcol];
+  // online softmax state per column (exp2 domain): weights 2^(s - m_run +
+  // e_run); e_run (the same in every lane) keeps p * n_V * 2^e_run inside
+  // fp16's normal range: 15 - ex for the largest V norm so far, 2^(ex-1) <=
+  // n < 2^ex (39 before any), so tiny rows keep their precision
   float m_run = -INFINITY, l_run = 0.f;
+  int e_run = 39;
   float4_t o_acc[ND];
 #pragma unroll
   for (int u = 0; u < ND; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -466,9 +475,9 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     const uint2 nk0 = *reinterpret_cast<const uint2*>(kt + kf.norm_off + 8 * ta);
     const uint2 nk1 = *reinterpret_cast<const uint2*>(kt + kf.norm_off + 32 * (NG - 1) + 8 * ta);
     const uint2 nvv = *reinterpret_cast<const uint2*>(vt + vf.norm_off + 8 * ta);
-    auto half_at = [](uint2 w, int i) -> float {
+    auto half_at = [](uint2 w, int i) -> float {   // exact, subnormals included
       const uint32_t x = (i >> 1) ? w.y : w.x;
-      return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> (16 * (i & 1))));
+      return (i & 1) ? f16_exact<1>(x) : f16_exact<0>(x);
     };
     float sc[4];
 #pragma unroll
@@ -487,19 +496,35 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     bm = fmaxf(bm, lane_xor<32>(bm, lane));
     // (no lane leaves here: the matrix-core steps below run with every lane)
     const float m_new = fmaxf(m_run, bm);
-    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new);
+    // V norms of the tokens that count (the other rows' bytes may hold
+    // anything); the largest of the tile (all lanes) may lower e_run
+    float nv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nv[i] = sc[i] == -INFINITY ? 0.f : half_at(nvv, i);
+    float vmax = fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3]));
+    vmax = fmaxf(vmax, lane_xor<16>(vmax, lane));
+    vmax = fminf(fmaxf(vmax, lane_xor<32>(vmax, lane)), 65504.f);
+    int e_new = e_run;
+    if (vmax > 0.f) {
+      const int ex = (int)((__float_as_uint(vmax) >> 23) & 0xFF) - 126;   // vmax in [2^(ex-1), 2^ex)
+      e_new = 15 - ex < e_run ? 15 - ex : e_run;
+    }
+    const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new + (float)(e_new - e_run));
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     m_run = m_new;
+    e_run = e_new;
     l_run *= alpha;
 #pragma unroll
     for (int u = 0; u < ND; ++u) o_acc[u] *= alpha;
-    half4_t pb;
+    float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pr = sc[i] == -INFINITY ? 0.f : exp2f(sc[i] - m_use);
-      l_run += pr;
-      pb[i] = pr > 0.f ? (_Float16)(pr * half_at(nvv, i)) : (_Float16)0.f;
+      pr[i] = sc[i] == -INFINITY ? 0.f : exp2f(sc[i] - m_use + (float)e_run);
+      l_run += pr[i];
     }
+    // p * n_V, each rounded once to fp16
+    const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_f2(pr[0], nv[0], pr[1], nv[1]),
+                                                             mul_f2(pr[2], nv[2], pr[3], nv[3])});
     __builtin_amdgcn_sched_barrier(0);
     // P.V: MFMA u, A row r = dim ND r + u; lane (col, ta) takes run 16 ta + col
     // of the lane-major V plane: VC bytes of each of tokens ta + 4 i, its ND
@@ -552,7 +577,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int i = 0; i < 4; ++i) st_o[wave][col][ND * (4 * ta + i) + u] = o_acc[u][i];
     if (ta == 0) {
-      st_ml[wave][0][col] = m_run;
+      st_ml[wave][0][col] = m_run == -INFINITY ? -INFINITY : m_run - (float)e_run;   // the weights' offset
       st_ml[wave][1][col] = l_run;
     }
   }

@@ -148,6 +148,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
+// fp16 half HI of w as fp32, exactly (subnormals by their definition, so the
+// result does not depend on the denormal mode)
+template <int HI>
+__device__ __forceinline__ float f16_exact(uint32_t w) {
+  const uint32_t h = HI ? (w >> 16) : (w & 0xFFFFu);
+  const float mag = (h & 0x7C00u) ? (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0x7FFFu))
+                                  : (float)(int)(h & 0x3FFu) * 0x1p-24f;
+  return (h & 0x8000u) ? -mag : mag;
+}
+
+// fp16 pair (x0 * n0, x1 * n1) from fp32 operands, each product rounded once
+// to fp16
+__device__ __forceinline__ uint32_t mul_f2(float x0, float n0, float x1, float n1) {
+  uint32_t r = 0;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(r) : "v"(x0), "v"(n0));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,0,0]" : "+v"(r) : "v"(x1), "v"(n1));
+  return r;
+}
+
 // ------------------------------------------------------ device lane helpers
 
 // Value of x in lane (lane ^ K), K a power of two below 64, without the

@@ -69,19 +69,44 @@ def slots_of(block_tables: np.ndarray, context_lens: np.ndarray):
     return out
 
 
+def bf16_neighbours(o: np.ndarray):
+    """For bf16 values o (held in float32), the next bf16 values below and
+    above, as float64 (infinite past the largest finite value)."""
+    bits = to_bf16_bits(np.asarray(o, dtype=np.float32)).astype(np.int64)
+    mag, neg = bits & 0x7FFF, (bits & 0x8000) != 0
+    up = np.where(neg, mag - 1, mag + 1)          # towards +inf in magnitude terms
+    dn = np.where(neg, mag + 1, mag - 1)
+    def val(m, sign_neg):
+        m = np.clip(m, 0, 0x7F80)
+        b = (m | np.where(sign_neg, 0x8000, 0)).astype(np.uint16)
+        return bf16_bits_to_f32(b).astype(np.float64)
+    zero = mag == 0
+    hi = np.where(zero, val(np.ones_like(mag), False), np.where(neg, val(up, True), val(up, False)))
+    lo = np.where(zero, -val(np.ones_like(mag), False), np.where(neg, val(dn, True), val(dn, False)))
+    return lo, hi
+
+
 def out_error(o_gpu: np.ndarray, o_ref: np.ndarray, bf16: bool = False):
     """Per (seq, head) vector: normwise relative error against the fp64
-    reference.  With bf16=True the error that rounding the exact result to
-    bf16 costs by itself is subtracted, so the figure is what the kernel adds
-    beyond the caller's requested output rounding."""
+    reference, ||o - ref|| / ||ref||.
+
+    With bf16=True the output is a bf16 vector and the error is taken modulo
+    its rounding: per element, the distance from ref to the interval of reals
+    that round to o (half-way to each bf16 neighbour), i.e. the smallest
+    perturbation of the exact result whose bf16 rounding is the output;
+    ||that|| / ||ref||.  (bf16 rounding of the exact result alone moves it by
+    up to 2^-8 relative per element, ~1e-3 to 2.5e-3 normwise, which is not
+    the kernel's error.)"""
     ref = o_ref.astype(np.float64)
     den = np.linalg.norm(ref, axis=-1)
     den = np.where(den == 0, 1.0, den)
-    err = np.linalg.norm(o_gpu.astype(np.float64) - ref, axis=-1) / den
-    if bf16:
-        rounded = bf16_bits_to_f32(to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
-        err = err - np.linalg.norm(rounded - ref, axis=-1) / den
-    return err
+    o = o_gpu.astype(np.float64)
+    if not bf16:
+        return np.linalg.norm(o - ref, axis=-1) / den
+    lo_n, hi_n = bf16_neighbours(o_gpu)
+    lo, hi = (o + lo_n) / 2, (o + hi_n) / 2
+    e = np.maximum(0.0, np.maximum(lo - ref, ref - hi))
+    return np.linalg.norm(e, axis=-1) / den
 
 
 def elem_error(o_gpu: np.ndarray, o_ref: np.ndarray):

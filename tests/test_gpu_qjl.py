@@ -2,9 +2,9 @@
 
 Write: whole pools bit-exact against the oracle (MSE indices, sign bits,
 vector and residual norms; bytes a write must not touch unchanged).  The
-sign bits come from fp64 projection sums, which the two sides order
-differently; a mismatch would need a sum within ~1e-15 of its terms' size
-of zero (probability far below the number of bits compared).
+sign bits come from fp64 projection sums taken in one defined order (j
+ascending, each product and partial sum rounded, no fused multiply-add),
+which both sides follow; rows whose sums cancel exactly check that order.
 
 Decode: out and lse against the oracle's fp64 attention over the effective
 keys (MSE reconstruction plus the sketch's term, reconstructed from the
@@ -62,6 +62,30 @@ def test_qjl_write_bit_exact(kbits, d, dtype, dist):
     keep[7] = False
     ref = oracle_pages(xk[keep], slots[keep], w.num_blocks, oracle_format(w.kfmt), "k")
     _assert_pool_equal(kp.cpu().numpy(), ref, "K (QJL)")
+
+
+@pytest.mark.parametrize("bits,d,dtype", [((4,), 128, "bf16"), ((2,), 128, "f32"), ((3, 2), 128, "bf16"),
+                                          ((4, 3), 128, "f32"), ((4,), 64, "f32"), ((3, 2), 64, "bf16")])
+def test_qjl_write_cancelling_projection_sums(bits, d, dtype):
+    """Rows and projections whose projection sums cancel exactly
+    (tests/qjl_cases.py): the defined order (j ascending, product and sum
+    each rounded, no fused multiply-add) gives bit 0 where exact arithmetic
+    or a fused multiply-add would give 1.  The pool written on the GPU equals
+    the oracle's byte for byte."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    from tests import qjl_cases as qc
+    print(f"case cancelling sums K{list(bits)}+QJL d{d} {dtype}", flush=True)
+    x, S, f, cases = qc.build(d, bits)
+    T = x.shape[0]
+    nb = (T + 15) // 16 + 1
+    slots = np.arange(T, dtype=np.int64) + 16   # blocks 1.. (block 0 untouched)
+    kf = tq.Format(d, list(bits), f.signs, f.group_channels, qjl_proj=torch.from_numpy(S.copy()).cuda())
+    kp = torch.full((nb, 1, kf.tile_bytes()[1]), 0xA5, dtype=torch.uint8, device="cuda")
+    tq.write_kv(to_device(x, dtype), None, torch.from_numpy(slots).cuda(), kp, None, kf, None, check=True)
+    torch.cuda.synchronize()
+    ref = oracle_pages(x, slots, nb, f, "k")
+    _assert_pool_equal(kp.cpu().numpy(), ref, "K (QJL, cancelling sums)")
 
 
 def test_qjl_rejected_on_v_and_multi_query():

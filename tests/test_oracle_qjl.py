@@ -146,3 +146,63 @@ def test_qjl_pages_round_trip_and_v_rejected():
         pg.write_pages(x, slots, np.zeros((4, 2, tile), np.uint8), f, 16, "v")
     with pytest.raises(ValueError):
         enc.Format.make(d, [3, 2], f.signs, f.group_channels, qjl_proj=S[:, :32])
+
+
+# ---------------------------------------------------------------- projection order
+def test_projection_equals_plain_python_loop():
+    """The vectorised projection equals the defined order written as a plain
+    Python loop over IEEE doubles (brute force, element by element)."""
+    from tests import qjl_cases as qc
+    rng = np.random.default_rng(11)
+    r = rng.standard_normal((6, 32)) * np.exp(rng.uniform(-20, 20, (6, 32)))
+    S = rng.standard_normal((32, 32)).astype(np.float32)
+    z = qjl.project(r, S)
+    for t in range(6):
+        for i in range(32):
+            assert z[t, i] == qc.python_chain(S[i], r[t])
+
+
+def test_projection_order_decides_a_cancelling_sum():
+    """Hand-worked: r = (0.1, -1e-30, -0.1), S row (1, 1, 1).  In the defined
+    order 0.1 + (-1e-30) rounds to 0.1 and 0.1 - 0.1 = +0, so the bit is 0,
+    although the exact sum is -1e-30 (an order adding the first and last
+    terms first would give bit 1).  r = (x, -x), S row (sigma, sigma) with
+    sigma * x inexact: unfused products cancel to +0."""
+    from fractions import Fraction
+    r = np.array([[0.1, -1e-30, -0.1]])
+    S = np.ones((1, 3), np.float32)
+    z = qjl.project(r, S)
+    assert z[0, 0] == 0.0 and not np.signbit(z[0, 0])
+    assert sum(Fraction(v) for v in r[0]) < 0
+    x = 0.1
+    sig = np.float32(1 / 3)
+    assert Fraction(float(sig) * x) != Fraction(float(sig)) * Fraction(x)   # inexact product
+    z2 = qjl.project(np.array([[x, -x]]), np.array([[sig, sig]], np.float32))
+    assert z2[0, 0] == 0.0
+
+
+@pytest.mark.parametrize("bits,d", [((4,), 128), ((2,), 128), ((3, 2), 128), ((4, 3), 128), ((4,), 64),
+                                    ((3, 2), 64)])
+def test_sign_bits_of_cancelling_sums_follow_the_defined_order(bits, d):
+    """Rows and projections built so that some projection sums cancel
+    exactly (tests/qjl_cases.py): the stage's order gives +0 (bit 0) for
+    every such sum, while exact arithmetic ("order" rows) or a fused
+    multiply-add ("fusion" rows) would give a negative z (bit 1).  The
+    oracle's bits for those rows are 0, its z equals the plain Python loop,
+    and each built case is really sensitive to the order."""
+    from tests import qjl_cases as qc
+    x, S, f, cases = qc.build(d, bits)
+    assert any(c[0] == "order" for c in cases) and any(c[0] == "fusion" for c in cases)
+    w = rotate(x[:, 0].astype(np.float64), f.signs)
+    idx, nb = enc.quantize_rotated(w, f)
+    res = qjl.residuals(w, idx, nb, f)
+    sb, _ = qjl.residual_fields(w, idx, nb, f)
+    for kind, g, i, tok, (a, c) in cases:
+        r = res[g][tok]
+        assert r[a] == -r[c] != 0
+        assert qc.python_chain(S[g, i], r) == 0.0
+        assert sb[tok, g, i] == 0, (kind, g, i, tok)
+        if kind == "order":
+            assert qc.exact_sum(S[g, i], r) < 0
+        else:
+            assert qc.fused_chain(S[g, i], r) < 0

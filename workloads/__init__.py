@@ -272,6 +272,13 @@ def _draw(dist: str, g: np.random.Generator, shape, outliers=None) -> np.ndarray
         x = g.standard_t(3, size=shape).astype(np.float32)
     elif dist == "t5u":
         x = (g.standard_t(5, size=shape) * math.sqrt(3.0 / 5.0)).astype(np.float32)
+    elif dist == "tiny":
+        # rows of tiny norm: N(0, 1) directions, each row scaled so its L2
+        # norm is log-uniform in [1e-7, 5e-5] (fp16 norms subnormal or near)
+        x = g.standard_normal(shape, dtype=np.float32)
+        lo, hi = math.log(1e-7), math.log(5e-5)
+        target = np.exp(g.uniform(lo, hi, size=shape[:-1] + (1,)))
+        x = (x / np.linalg.norm(x, axis=-1, keepdims=True) * target).astype(np.float32)
     else:
         raise ValueError(dist)
     return x
