@@ -313,6 +313,29 @@ tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seq
                                 void* out, tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream);
 
 /*
+ * tq_decode_paged without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  It allocates nothing: the split
+ * partials go to a device array of TQ_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (its address
+ * is looked up on the first call on each device).  The call runs on the
+ * current device; `stream` must belong to it.  Every argument, format and
+ * error is as for tq_decode_paged, plus VALUE when the split workspace
+ * (tq_decode_workspace_bytes) would exceed TQ_NOALLOC_SCRATCH_BYTES.  All
+ * calls on one GPU share the one array, which keeps the last call's
+ * contents: calls that overlap on one GPU (concurrent streams, threads)
+ * race and give undefined results; calls on one stream are ordered.
+ */
+#define TQ_NOALLOC_SCRATCH_BYTES (16ull << 20)
+tq_status tq_decode_paged_noalloc(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
+                                  int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  const tq_format* kfmt, const tq_format* vfmt, float scale,
+                                  int32_t num_splits, void* out, tq_dtype out_dtype, float* lse,
+                                  int32_t* dev_err, tq_stream_t stream);
+
+/*
  * Log-sum-exp merge of split partials (flash-decoding):
  *   lse = M + ln sum_p exp(lse_p - M),  out = sum_p exp(lse_p - lse) * o_p
  *   part_out  device float [num_seqs][num_heads][num_splits][head_dim]

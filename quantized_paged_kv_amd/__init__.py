@@ -77,6 +77,8 @@ def _load(path: str = LIB_PATH):
         "tq_split_merge": ([P, P, i32, i32, i32, i32, P, i32, P, P], i32),
         "tq_decode_dense": ([P, i32, i32, i32, i32, i32, P, P, i32, i32, P, f32, P, P, P, i32, P, P, P], i32),
         "tq_debug_phase_trace": ([P], i32),
+        "tq_decode_paged_noalloc": ([P, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, f32, i32, P, i32,
+                                     P, P, P], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -328,6 +330,34 @@ def decode_paged(q, k_pages, v_pages, block_tables, context_lens, kfmt: Format, 
     return out, lse
 
 
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_paged_noalloc(q, k_pages, v_pages, block_tables, context_lens, kfmt: Format, vfmt: Format,
+                         scale: float, out, lse=None, num_splits: int = 1, dev_err=None, stream=None):
+    """tq_decode_paged_noalloc: decode of q [B, H_q, d] into the caller's out
+    [B, H_q, d] (and lse [B, H_q] float32 if given) with the split partials
+    in the library's per-GPU array; this wrapper allocates nothing either.
+    Calls that overlap on one GPU race (they share that array)."""
+    import torch
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be a contiguous [B, H_q, d] GPU tensor")
+    B, Hq, d = q.shape
+    _need(k_pages.dim() == 3 and v_pages.dim() == 3 and k_pages.dtype == torch.uint8 and v_pages.dtype == torch.uint8,
+          "page pools must be uint8 [NB, H_kv, tile]")
+    _need(v_pages.shape[:2] == k_pages.shape[:2], "K and V pools differ in blocks or heads")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B
+          and block_tables.is_contiguous(), "block_tables must be contiguous int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == B, "context_lens must be int32 [B]")
+    _need(out is not None and out.shape == q.shape and out.is_contiguous(), "out must be contiguous and shaped like q")
+    _need(lse is None or (lse.shape == (B, Hq) and lse.dtype == torch.float32), "lse must be float32 [B, H_q]")
+    _check(_lib.tq_decode_paged_noalloc(_ptr(q), _dtype_code(q), B, Hq, k_pages.shape[1], _ptr(k_pages),
+                                        _ptr(v_pages), k_pages.shape[0], BLOCK_SIZE, _ptr(block_tables),
+                                        block_tables.shape[1], _ptr(context_lens), ctypes.byref(kfmt.c),
+                                        ctypes.byref(vfmt.c), float(scale), int(num_splits), _ptr(out),
+                                        _dtype_code(out), _ptr(lse), _ptr(dev_err), _stream(stream)))
+    return out, lse
+
+
 def split_merge(part_out, part_lse, out=None, lse=None, out_dtype=None, stream=None):
     """Log-sum-exp merge of partials part_out [S, H, P, d], part_lse [S, H, P]."""
     import torch
@@ -392,6 +422,6 @@ def set_phase_trace(buf) -> bool:
 
 
 __all__ = ["Format", "UnsupportedFormatError", "DeviceError", "lloyd_max_codebook", "alloc_pages",
-           "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged",
+           "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged", "decode_paged_noalloc",
            "split_merge", "decode_dense", "set_phase_trace",
            "LIB_PATH", "BLOCK_SIZE"]

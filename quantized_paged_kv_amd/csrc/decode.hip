@@ -1684,6 +1684,65 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   return launch_status("tq_decode_paged merge launch");
 }
 
+// ------------------------------------------------------------ no allocation
+// Split workspace of tq_decode_paged_noalloc: one array per GPU, part of the
+// library's code object, held until the process ends.  Host code must not
+// pass the array's name to a kernel (in host code it names a host-side
+// stand-in); its device address is looked up once per device below.
+static __device__ __align__(256) uint8_t scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device, with that device current).
+tq_status scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return set_error(TQ_ERR_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(ge));
+  if (dev < 0 || dev >= kMaxDevices) return set_error(TQ_ERR_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return set_error(TQ_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TQ_OK;
+}
+}  // namespace
+
+extern "C" tq_status tq_decode_paged_noalloc(const void* q, tq_dtype q_dtype, int32_t num_seqs,
+                                             int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,
+                                             const uint8_t* v_pages, int64_t num_blocks, int32_t block_size,
+                                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t* context_lens, const tq_format* kfmt,
+                                             const tq_format* vfmt, float scale, int32_t num_splits, void* out,
+                                             tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream) {
+  if (!kfmt) return set_error(TQ_ERR_VALUE, "NULL format");
+  uint64_t need = 0;
+  tq_status st = tq_decode_workspace_bytes(num_seqs, num_q_heads, kfmt->head_dim, num_splits, &need);
+  if (st != TQ_OK) return st;
+  if (need > TQ_NOALLOC_SCRATCH_BYTES)
+    return set_error(TQ_ERR_VALUE, "split workspace of " + std::to_string(need) + " bytes exceeds the " +
+                                       std::to_string((unsigned long long)TQ_NOALLOC_SCRATCH_BYTES) +
+                                       " bytes the allocation-free call holds per GPU (use fewer splits, or "
+                                       "tq_decode_paged with a workspace)");
+  void* ws = nullptr;
+  if (need) {
+    st = scratch_address(&ws);
+    if (st != TQ_OK) return st;
+  }
+  return tq_decode_paged_multi(q, q_dtype, num_seqs, 1, num_q_heads, num_kv_heads, k_pages, v_pages, num_blocks,
+                               block_size, block_tables, max_blocks_per_seq, context_lens, kfmt, vfmt, scale,
+                               num_splits, ws, need ? TQ_NOALLOC_SCRATCH_BYTES : 0, out, out_dtype, lse, dev_err,
+                               stream);
+}
+
 extern "C" tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
                                      int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
                                      int64_t num_blocks, int32_t block_size, const int32_t* block_tables,

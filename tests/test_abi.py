@@ -154,6 +154,23 @@ def test_decode_status_codes_without_launch():
     assert _call_decode(B=0) == tq.TQ_OK
 
 
+def test_noalloc_decode_status_codes_without_launch():
+    """The allocation-free decode rejects a split workspace past its array
+    (VALUE, with the sizes in the message) and a NULL format before any
+    device call; with no sequences it returns OK."""
+    L = tq._lib
+    s = signs(0, 1, 128)
+    kf = tq.Format(128, [4], s)
+    args = lambda B, P, f: (1, tq.TQ_BF16, B, 64, 8, 1, 1, 10, 16, 1, 4, 1, f, ctypes.byref(kf.c), 0.1, P, 1,
+                            tq.TQ_BF16, None, None, None)
+    assert L.tq_decode_paged_noalloc(*args(600, 128, ctypes.byref(kf.c))) == tq.TQ_ERR_VALUE
+    msg = L.tq_last_error().decode()
+    assert "exceeds" in msg and str(16 << 20) in msg
+    assert L.tq_decode_paged_noalloc(*args(4, 4, None)) == tq.TQ_ERR_VALUE
+    assert L.tq_decode_paged_noalloc(*args(0, 1, ctypes.byref(kf.c))) == tq.TQ_OK
+    assert tq.NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
 def test_merge_status_codes_without_launch():
     L = tq._lib
     assert L.tq_split_merge(1, 1, 2, 2, 0, 128, 1, tq.TQ_F32, None, None) == tq.TQ_ERR_VALUE
