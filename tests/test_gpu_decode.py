@@ -188,10 +188,15 @@ def test_bad_block_table_entry_reports_and_skips():
     with pytest.raises(IndexError, match=f"position {1 * bt.shape[1] + 2}"):
         tq.decode_paged(q, kp, vp, torch.from_numpy(bt).cuda(), torch.from_numpy(w.context_lens).cuda(), kf, vf,
                         w.scale, check=True)
+    # a context length past the capacity; every entry of that row is in the
+    # pool, so the length is the only error (with two, which one the error
+    # word records is unspecified)
     cl = w.context_lens.copy()
     cl[0] = 16 * bt.shape[1] + 1
+    bt_full = w.block_tables.copy()
+    bt_full[0][bt_full[0] < 0] = 0
     with pytest.raises(IndexError, match="position -1"):
-        tq.decode_paged(q, kp, vp, torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(cl).cuda(), kf, vf,
+        tq.decode_paged(q, kp, vp, torch.from_numpy(bt_full).cuda(), torch.from_numpy(cl).cuda(), kf, vf,
                         w.scale, check=True)
 
 
