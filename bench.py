@@ -401,10 +401,16 @@ def stats_us(ms):
             "p50": round(ms[n // 2] * 1e3, 2), "p90": round(ms[9 * n // 10] * 1e3, 2)}
 
 
-def cpu_baseline(index, budget_s=12.0):
+def cpu_baseline(index, budget_s=12.0, gpu_out=None, gpu_lse=None):
     """The oracle (as it stands) decoding whole sequences of the workload on
     the host: dense reconstruction from oracle-written pages + fp64
-    attention for every q head.  Pages are prepared untimed."""
+    attention for every q head.  Pages are prepared untimed.
+
+    With gpu_out / gpu_lse (the outputs of the timed tq_decode_paged calls
+    of this run), every (sequence, q head) the oracle decodes is also
+    compared with them: lse within 1e-4, out within 2e-3 normwise, bf16 out
+    taken modulo its rounding (the distance from the fp64 reference to the
+    interval of reals that round to each output value)."""
     import numpy as np
     import oracle
     from oracle import attn as oatt
@@ -417,7 +423,10 @@ def cpu_baseline(index, budget_s=12.0):
     G = w.num_q_heads // w.num_kv_heads
     krow = opg.tile_layout(kof, 16)[0] + 2 * kof.num_groups
     vrow = opg.tile_layout(vof, 16)[0] + 2 * vof.num_groups
+    from tests.helpers import out_error
     total_bytes, total_t, done = 0, 0.0, []
+    worst_out = worst_raw = worst_lse = 0.0
+    checked = 0
     for s in range(w.num_seqs):
         n = int(w.context_lens[s])
         bt = np.arange((n + 15) // 16)
@@ -432,13 +441,21 @@ def cpu_baseline(index, budget_s=12.0):
                 opg.write_pages(xv[a:a + 16384, h:h + 1], sl[a:a + 16384], Vp, vof, 16, "v")
             pools.append((Kp, Vp))
         t0 = time.perf_counter()
+        refs = []
         for h in range(w.num_kv_heads):
             Kp, Vp = pools[h]
             K = opg.reconstruct_sequence(Kp, bt, n, 0, kof, 16)
             V = opg.reconstruct_sequence(Vp, bt, n, 0, vof, 16, role="v")
             for g in range(G):
-                oatt.attention(q[s, h * G + g].astype(np.float64), K, V, w.scale)
+                refs.append((h * G + g, oatt.attention(q[s, h * G + g].astype(np.float64), K, V, w.scale)))
         total_t += time.perf_counter() - t0
+        if gpu_out is not None:
+            for hq, (o_ref, l_ref) in refs:
+                e = float(out_error(gpu_out[s, hq][None], o_ref[None], w.out_dtype == "bf16")[0])
+                worst_out = max(worst_out, e)
+                worst_raw = max(worst_raw, float(out_error(gpu_out[s, hq][None], o_ref[None])[0]))
+                worst_lse = max(worst_lse, abs(float(gpu_lse[s, hq]) - l_ref))
+                checked += 1
         total_bytes += n * w.num_kv_heads * (krow + vrow)
         done.append(s)
         if total_t >= budget_s:
@@ -455,12 +472,23 @@ def cpu_baseline(index, budget_s=12.0):
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
-            "kind": "oracle", "allowed_cores": cores, "blas_threads": threads, "cpu_model": cpu_model,
+    res = {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads),
+            "kind": "oracle", "route": "oracle-dense-fp64 (diagnostic)",
+            "allowed_cores": cores, "blas_threads": threads, "cpu_model": cpu_model,
             "numpy": np.__version__,
             "sample": f"{len(done)} whole sequence(s) of the workload ({sum(int(w.context_lens[s]) for s in done)} "
                       f"tokens x {w.num_kv_heads} kv heads x {w.num_q_heads // w.num_kv_heads} q heads each): "
                       f"dense reconstruction + fp64 attention, {total_t:.1f} s on {cores} allowed cores"}
+    if gpu_out is not None:
+        res["parity_same_run"] = {
+            "route_checked": "tq_decode_paged (serving)", "reference": "oracle-dense-fp64 (diagnostic)",
+            "rows_checked": checked, "worst_out_err": round(worst_out, 7), "worst_out_err_raw": round(worst_raw, 7),
+            "worst_lse_err": round(float(worst_lse), 8),
+            "reading": "per (sequence, q head): lse abs <= 1e-4; out normwise <= 2e-3 against the fp64 reference, "
+                       "bf16 out modulo its rounding (distance to the interval of reals rounding to each output "
+                       "element); raw = bf16 out against fp64 without that allowance",
+            "pass": bool(worst_lse <= 1e-4 and worst_out <= 2e-3)}
+    return res
 
 
 def main():
@@ -504,6 +532,9 @@ def main():
     ms_graph = b.timed_graph(args.steps, args.warmup)
     log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, {ms_graph * 1e3:.1f} us/step replayed as a graph")
     dec_ms = b.timed_cold(args.steps, args.warmup, flush)
+    torch.cuda.synchronize()
+    timed_out = b.out.float().cpu().numpy()   # outputs of the last timed call (the same for every layer)
+    timed_lse = b.lse.cpu().numpy()
     w = b.w
     step_bytes = b.decode_bytes + b.write_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -531,6 +562,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "tq_decode_paged (decode kernel + split merge)",
+                     "route": "tq_decode_paged (serving)",
                      "algorithmic_bytes_per_launch": b.decode_bytes,
                      "timing": "cold caches (1 GiB read before each launch)"},
     }
@@ -596,7 +628,7 @@ def main():
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(index)
+        result["cpu_baseline"] = cpu_baseline(index, gpu_out=timed_out, gpu_lse=timed_lse)
     print(json.dumps(result), flush=True)
 
 

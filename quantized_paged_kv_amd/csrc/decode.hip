@@ -161,39 +161,6 @@ __device__ __forceinline__ float row_ror8(float x) {
 // that p * n_V * 2^E stays inside fp16's normal range whatever the scale of
 // the rows; see the block loop).
 
-// x * (fp16 half HI of w) in one v_fma_mix, rounded once
-template <int HI>
-__device__ __forceinline__ float mul_h(float x, uint32_t w) {
-  float r;
-  if constexpr (HI) asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
-  else asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w));
-  return r;
-}
-// x * (fp16 half HI of w) + y
-template <int HI>
-__device__ __forceinline__ float fma_h(float x, uint32_t w, float y) {
-  float r;
-  if constexpr (HI) asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w), "v"(y));
-  else asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(x), "v"(w), "v"(y));
-  return r;
-}
-// fp16 pair (x0 * half 0 of w, x1 * half 1 of w), each rounded once
-__device__ __forceinline__ uint32_t mul_h2(float x0, float x1, uint32_t w) {
-  uint32_t r = 0;
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x0), "v"(w));
-  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(x1), "v"(w));
-  return r;
-}
-typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ u16x2_t as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2_t, x); }
-// fp16 bit pattern of 2^(15 - e), minus one, for e in [-1, 39]: V norms above
-// it would make p * n_V * 2^e overflow fp16's range (e = -1: every finite
-// fp16 is below the bound)
-__device__ __forceinline__ uint32_t v_bound_m1(int e) {
-  const int k = 15 - e;
-  const uint32_t h = k >= 16 ? 0x7C00u : (k >= -14 ? (uint32_t)(k + 15) << 10 : 1u << (k + 24));
-  return h - 1u;
-}
 // max of two floats known not to be NaN (no canonicalisation)
 __device__ __forceinline__ float max_nn(float a, float b) {
   float r;

@@ -407,6 +407,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
   // n < 2^ex (39 before any), so tiny rows keep their precision
   float m_run = -INFINITY, l_run = 0.f;
   int e_run = 39;
+  uint32_t v_hi = v_bound_m1(39);
   float4_t o_acc[ND];
 #pragma unroll
   for (int u = 0; u < ND; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -475,39 +476,50 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     const uint2 nk0 = *reinterpret_cast<const uint2*>(kt + kf.norm_off + 8 * ta);
     const uint2 nk1 = *reinterpret_cast<const uint2*>(kt + kf.norm_off + 32 * (NG - 1) + 8 * ta);
     const uint2 nvv = *reinterpret_cast<const uint2*>(vt + vf.norm_off + 8 * ta);
-    auto half_at = [](uint2 w, int i) -> float {   // exact, subnormals included
-      const uint32_t x = (i >> 1) ? w.y : w.x;
-      return (i & 1) ? f16_exact<1>(x) : f16_exact<0>(x);
-    };
+    // norm products through v_fma_mix (f16 subnormal norms taken as they
+    // are, single rounding)
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float f0 = acc0[i] + lane_xor<8>(acc0[i], lane);
       const float f1 = acc1[i] + lane_xor<8>(acc1[i], lane);
       const float fq = accq[i] + lane_xor<8>(accq[i], lane);
-      float v = half_at(nk0, i) * f0;
-      if (NG > 1) v = __builtin_fmaf(half_at(nk1, i), f1, v);
+      const uint32_t k0 = (i >> 1) ? nk0.y : nk0.x;
+      float v = (i & 1) ? mul_h<1>(f0, k0) : mul_h<0>(f0, k0);
+      if (NG > 1) {
+        const uint32_t k1 = (i >> 1) ? nk1.y : nk1.x;
+        v = (i & 1) ? fma_h<1>(f1, k1, v) : fma_h<0>(f1, k1, v);
+      }
       v = __builtin_fmaf(fq, w_q, v * w_m);
       sc[i] = (16 * b + ta + 4 * i < ctx) ? v : -INFINITY;
     }
+    // V norms of the tokens that count; the other rows' bytes may hold
+    // anything (set to +0: weight and operand 0)
+    uint32_t vx = nvv.x, vy = nvv.y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (sc[i] == -INFINITY) {
+        if (i >> 1) vy &= ~(0xFFFFu << (16 * (i & 1)));
+        else vx &= ~(0xFFFFu << (16 * (i & 1)));
+      }
     // online softmax per column (exp2 domain)
     float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     bm = fmaxf(bm, lane_xor<16>(bm, lane));
     bm = fmaxf(bm, lane_xor<32>(bm, lane));
     // (no lane leaves here: the matrix-core steps below run with every lane)
     const float m_new = fmaxf(m_run, bm);
-    // V norms of the tokens that count (the other rows' bytes may hold
-    // anything); the largest of the tile (all lanes) may lower e_run
-    float nv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) nv[i] = sc[i] == -INFINITY ? 0.f : half_at(nvv, i);
-    float vmax = fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3]));
-    vmax = fmaxf(vmax, lane_xor<16>(vmax, lane));
-    vmax = fminf(fmaxf(vmax, lane_xor<32>(vmax, lane)), 65504.f);
+    // a V norm too large for e_run lowers it to 15 - ex of the tile's largest
+    const u16x2_t mxv = __builtin_elementwise_max(as_u16x2(vx), as_u16x2(vy));
+    const bool over = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(mxv, u16x2_t{(uint16_t)v_hi, (uint16_t)v_hi})) != 0u;
     int e_new = e_run;
-    if (vmax > 0.f) {
-      const int ex = (int)((__float_as_uint(vmax) >> 23) & 0xFF) - 126;   // vmax in [2^(ex-1), 2^ex)
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      const uint32_t mh = mxv[0] > mxv[1] ? mxv[0] : mxv[1];
+      float vmax = f16_exact<0>(mh);
+      vmax = fmaxf(vmax, lane_xor<16>(vmax, lane));
+      vmax = fminf(fmaxf(vmax, lane_xor<32>(vmax, lane)), 65504.f);
+      const int ex = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(vmax) >> 23) & 0xFF) - 126);
       e_new = 15 - ex < e_run ? 15 - ex : e_run;
+      v_hi = v_bound_m1(e_new);
     }
     const float alpha = m_run == -INFINITY ? 0.f : exp2f(m_run - m_new + (float)(e_new - e_run));
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -523,8 +535,7 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
       l_run += pr[i];
     }
     // p * n_V, each rounded once to fp16
-    const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_f2(pr[0], nv[0], pr[1], nv[1]),
-                                                             mul_f2(pr[2], nv[2], pr[3], nv[3])});
+    const half4_t pb = __builtin_bit_cast(half4_t, u32x2_t{mul_h2(pr[0], pr[1], vx), mul_h2(pr[2], pr[3], vy)});
     __builtin_amdgcn_sched_barrier(0);
     // P.V: MFMA u, A row r = dim ND r + u; lane (col, ta) takes run 16 ta + col
     // of the lane-major V plane: VC bytes of each of tokens ta + 4 i, its ND
