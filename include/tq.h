@@ -75,6 +75,8 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
 #define TQ_MAX_HEAD_DIM 128
 #define TQ_BLOCK_SIZE 16
+/* (query, q head) pairs a paged decode call serves per kv head */
+#define TQ_MAX_COLUMNS 128
 
 /*
  * One tensor's storage format.  K and V each get their own, chosen
@@ -268,8 +270,9 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * of 4 or 2 bits, or two groups of 4 + 3 bits (3.5-bit recipe) or 3 + 2 bits
  * (2.5-bit recipe; [S "What it does"], [D "Recipe Strategy"]); V one group
  * of 4 or 2 bits;
- * num_q_heads / num_kv_heads in 1..8; block_size 16.  Each page pool must be
- * smaller than 4 GiB and num_blocks below 2^31 (else VALUE).
+ * num_q_heads / num_kv_heads in 1..TQ_MAX_COLUMNS (1..8 with the QJL
+ * stage); block_size 16.  Each page pool must be smaller than 4 GiB and
+ * num_blocks below 2^31 (else VALUE).
  * Results are reproducible up to the order of floating-point accumulation:
  * blocks are shared dynamically among the waves serving a kv head.
  * K formats with the QJL stage (qjl = 1; any group layout above, K bits 2-4)
@@ -295,14 +298,16 @@ tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
  * them first, as for tq_decode_paged), so query i (0-based) attends tokens
  * [0, context_lens[s] - (num_queries - 1 - i)); a query left with no token
  * gets out = 0 and lse = -inf.  The (query, q head) pairs of a kv head share
- * the matrix-core columns, so every page is read once for all queries.
+ * the matrix-core columns of the kv head's workgroup, 8 per group of
+ * waves, so every page is read from memory once for all queries (the waves
+ * of the column groups read each tile at about the same time).
  *   q, out       device [num_seqs][num_queries][num_q_heads][head_dim].
  *   lse          device float [num_seqs][num_queries][num_q_heads] or NULL.
  *   workspace    tq_decode_workspace_bytes(num_seqs * num_queries, ...).
  * Every other argument, error and format is as for tq_decode_paged, which
  * is this call with num_queries = 1.  Served: num_queries * (num_q_heads /
- * num_kv_heads) <= 8, and num_queries = 1 for a K format with the QJL stage
- * (else UNSUPPORTED_FORMAT).
+ * num_kv_heads) <= TQ_MAX_COLUMNS, and num_queries = 1 for a K format with
+ * the QJL stage (else UNSUPPORTED_FORMAT).
  */
 tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
                                 int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,

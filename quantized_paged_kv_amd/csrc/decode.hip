@@ -85,12 +85,20 @@ struct DecodeParams {
   int64_t num_blocks;        // < 2^31
   int32_t S, Hq, Hkv, G, max_blocks, P;
   int32_t HG, NG;    // kv heads per workgroup group (1, 2, 4 or 8) and groups (Hkv / HG)
+  // The G columns of a kv head are taken 8 at a time: column group cg holds
+  // columns 8 cg .. 8 cg + 7 (CG groups, a power of two, 8 CG >= G).  A
+  // (kv head, column group) pair is a virtual head; the HG kv heads of a
+  // workgroup give VH = HG * CG <= 16 of them, each served by 16 / VH waves
+  // that read the head's tiles (once from memory: the waves of the kv head
+  // read each tile at about the same time).
+  int32_t CG, VH;
   int32_t n_wg;      // grid size (persistent workgroups)
   int32_t seg_cost;  // work positions charged for starting a piece (see seg_span)
   float inv_G;       // 1 / G
   // Several queries per sequence (multi-query decode): the NQ * Gr (query, q
-  // head) pairs of a kv head are its G = NQ * Gr matrix-core columns; query i
-  // of a sequence attends its first ctx - (NQ - 1 - i) cached tokens; q / out
+  // head) pairs of a kv head are its G = NQ * Gr <= 128 matrix-core columns
+  // (column c: query c / Gr, q head c % Gr of the kv head); query i of a
+  // sequence attends its first ctx - (NQ - 1 - i) cached tokens; q / out
   // rows are [sequence][query][q head].  NQ = 1, Gr = G for one query.
   int32_t NQ, Gr;
   int32_t rows_ps;   // q / out rows per sequence: NQ * Hq
@@ -204,10 +212,9 @@ struct Cfg {
   static constexpr int VLANE = VK == V4 ? D / 32 : D / 64;  // bytes per lane per token in V
   static constexpr bool MIXED = KK == KM43 || KK == KM32;   // two groups: 3-bit pair table in use
   static constexpr int LDS_LUT = kLutBytes + (MIXED ? kLut3Bytes : 0);
-  static constexpr int QS = D + D / 4 + 4;                // rotated-q row stride (floats), conflict-free rows
-  static constexpr int QV_FLOATS = NQK * 64 * 4;          // q.K B operands of one kv head: NQK x 64 lanes x half8
+  static constexpr int QV_FLOATS = NQK * 64 * 4;          // q.K B operands of one virtual head: NQK x 64 lanes x half8
   static constexpr int DS = D + 4;                        // wave-state row stride (floats)
-  static constexpr int QX_FLOATS = 8 * QV_FLOATS + 8 * 8 * QS;   // operands + rotated q of up to 8 kv heads
+  static constexpr int QX_FLOATS = kWaves * QV_FLOATS;           // operands of up to 16 virtual heads
   static constexpr int SX_FLOATS = kWaves * 8 * DS;              // wave states
   static constexpr int X_FLOATS = QX_FLOATS > SX_FLOATS ? QX_FLOATS : SX_FLOATS;
 };
@@ -419,22 +426,22 @@ __device__ __forceinline__ int range_len(int W, int n_wg, int max_blocks, int P)
   return R > need ? R : need;
 }
 
-// Waves -> (kv head of the group, part).  The 16 waves sit on the 4 SIMDs
-// as wave % 4, and on a SIMD older waves (lower index) issue first.  With 8
-// heads of 2 parts, head h % 4 + 4 b is served by the waves of ranks {0, 3}
-// (b = 0) or {1, 2} (b = 1) on SIMD h % 4, so that every head gets the same
-// share of issue slots; otherwise head h has parts h + HG q.
-__device__ __forceinline__ int head_of_wave(int wave, int HG) {
-  if (HG == 8) {
+// Waves -> (virtual head of the group, part).  The 16 waves sit on the 4
+// SIMDs as wave % 4, and on a SIMD older waves (lower index) issue first.
+// With 8 heads of 2 parts, head h % 4 + 4 b is served by the waves of ranks
+// {0, 3} (b = 0) or {1, 2} (b = 1) on SIMD h % 4, so that every head gets
+// the same share of issue slots; otherwise head h has parts h + VH q.
+__device__ __forceinline__ int head_of_wave(int wave, int VH) {
+  if (VH == 8) {
     const int r = wave >> 2;
     return (wave & 3) | (((r ^ (r >> 1)) & 1) << 2);
   }
-  return wave % HG;
+  return wave % VH;
 }
-__device__ __forceinline__ int part_of_wave(int wave, int HG) { return HG == 8 ? wave >> 3 : wave / HG; }
-__device__ __forceinline__ int wave_of_part(int h, int q, int HG) {
-  if (HG == 8) return 4 * (q ? ((h & 4) ? 2 : 3) : ((h & 4) ? 1 : 0)) + (h & 3);
-  return h + HG * q;
+__device__ __forceinline__ int part_of_wave(int wave, int VH) { return VH == 8 ? wave >> 3 : wave / VH; }
+__device__ __forceinline__ int wave_of_part(int h, int q, int VH) {
+  if (VH == 8) return 4 * (q ? ((h & 4) ? 2 : 3) : ((h & 4) ? 1 : 0)) + (h & 3);
+  return h + VH * q;
 }
 
 // Workgroup LDS.  The tables come first so that every table address
@@ -443,13 +450,13 @@ template <int D, int KK, int VK>
 struct Smem {
   using C = Cfg<D, KK, VK>;
   uint8_t lut[C::LDS_LUT];
-  // per kv head of the group: q.K operands (NQK x 64 lanes x half8) and the
-  // rotated q rows; after the block loop the same bytes hold the wave states
+  // per virtual head: q.K operands (NQK x 64 lanes x half8); after the
+  // block loop the same bytes hold the wave states
   float xbuf[C::X_FLOATS];
-  float s_ml[kWaves * 16];   // per wave: running max and sum of each q head
+  float s_ml[kWaves * 16];   // per wave: running max and sum of each column
   uint32_t s_par[64];
-  int s_qexp[64];            // [kv head of the group][q head]
-  int s_next[8];             // per kv head of the group: next free piece block
+  int s_qexp[8 * kWaves];    // [virtual head][column]
+  int s_next[kWaves];        // per virtual head: next free piece block
   int s_bt[kBtCap];          // block-table entries of the piece's first kBtCap blocks
   int s_cl[64];              // clamped context lengths of sequences 0-63
   int s_plan[8];             // work split: R, range start and end, first segment
@@ -487,15 +494,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     {
       const __attribute__((address_space(4))) uint32_t* ka =
           (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
-#ifdef TQ_PHASE_TRACE
-      static_assert(sizeof(DecodeParams) <= 8 * 64, "argument block spans more lines than are touched");
-      const uint32_t k7 = ka[112];
-      asm volatile("" ::"s"(k7));
-#else
-      static_assert(sizeof(DecodeParams) <= 7 * 64, "argument block spans more lines than are touched");
-#endif
-      const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96];
-      asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6));
+      static_assert(sizeof(DecodeParams) > 7 * 64 && sizeof(DecodeParams) <= 8 * 64,
+                    "the argument block spans another number of lines than are touched");
+      const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96],
+                     k7 = ka[112];
+      asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6), "s"(k7));
     }
     // context length of sequence `lane` (lanes past the last sequence read 0
     // through the descriptor's range check)
@@ -653,13 +656,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
   const int64_t v_blk_stride = (int64_t)p.Hkv * p.v_tile;
   const int cap = p.max_blocks * 16;
-  // wave -> (kv head of the group, part): the NPW waves of a head share its blocks
-  const int HG = p.HG;
-  const int NPW = kWaves / HG;
-  const int hl = uni(head_of_wave(wave, HG));
-  const int part = uni(part_of_wave(wave, HG));
-  half8_t* const qv_all = reinterpret_cast<half8_t*>(xbuf);            // [hl][t][lane]
-  float* const qf_all = xbuf + 8 * C::QV_FLOATS;                       // [hl][g] rows of QS floats
+  // wave -> (virtual head of the group, part): the NPW waves of a virtual
+  // head share its blocks; virtual head vh is column group cg of kv head hl
+  const int HG = p.HG, CG = p.CG, VH = p.VH;
+  const int NPW = kWaves / VH;
+  const int vh = uni(head_of_wave(wave, VH));
+  const int part = uni(part_of_wave(wave, VH));
+  const int hl = uni(vh / CG);
+  const int cg = uni(vh - hl * CG);
+  half8_t* const qv_all = reinterpret_cast<half8_t*>(xbuf);            // [vh][t][lane]
   float* const slots = xbuf;                                           // [wave][g] rows of DS floats
 
   // ---- walk the pieces of this workgroup's range
@@ -682,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // own, query i sees ctx - (NQ - 1 - i) of them; ctx_all is what every
       // query sees, ctx_col this lane's column's (columns past G: ctx)
       const int ctx_all = ctx - (p.NQ - 1);
-      const int qi_col = (int)(((float)gq + 0.5f) * p.inv_Gr);
+      const int qi_col = (int)(((float)(8 * cg + gq) + 0.5f) * p.inv_Gr);
       const int ctx_col = qi_col < p.NQ ? ctx - (p.NQ - 1 - qi_col) : ctx;
       const int kvh = grp * HG + hl;   // this wave's kv head
       const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // index (LDS atomic) -> entry (LDS read) -> tile loads; while a tile is
       // computed the next two tiles are in flight.
       const int n = b1 - b0;   // blocks of the piece, >= 1
-      if (tid < 8) s_next[tid] = 3 * NPW;
+      if (tid < kWaves) s_next[tid] = 3 * NPW;
       const __amdgpu_buffer_rsrc_t btr = tile_rsrc(reinterpret_cast<const uint8_t*>(bt_row), 4 * p.max_blocks);
       auto bt_load = [&](int idx) -> int {   // entry of piece block idx (block b0 when idx >= n)
         return (int)__builtin_amdgcn_raw_buffer_load_b32(btr, 0u, 4 * (b0 + (idx < n ? idx : 0)), 0);
@@ -715,27 +720,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int e = tid + kThreads * i;
         btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
       }
-      constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per q head
-      const int ln = fresh_lane();
-      const int g8 = ln >> 3, l8 = ln & 7;
-      const bool q_live = g8 < p.G;
-      // raw q words of this lane's PER channels (bf16: two per word, the upper
-      // half of qw unused); one load shape for both dtypes, bytes past the q
+      // q of the virtual head's 8 columns: lane (a, j) loads channels
+      // CPL a .. CPL a + CPL - 1 of column 8 cg + (j & 7)'s q row (lanes j and
+      // j + 8 load the same); one load shape for both dtypes (bf16: two
+      // channels per word, the upper half of qw unused), bytes past the q
       // tensor read as zero through the descriptor's range check
-      uint32_t qw[PER];
+      constexpr int CPL = D / 4;
+      const int ln = fresh_lane();
+      const int colq = 8 * cg + (ln & 7);
+      const bool q_live = colq < p.G;
+      uint32_t qw[CPL];
       {   // issued by every wave (parts > 0 discard them) so that all paths
           // carry the same loads and later waits count exactly
         const int esz = p.q_f32 ? 4 : 2;
         const int head0 = uni((int)(((int64_t)s * p.rows_ps + kvh * p.Gr) * D * esz));   // query 0, first q head
         int qrow = 0;   // this lane's (query, q head) column: rows past head0
         if (q_live) {
-          const int qi = (int)(((float)g8 + 0.5f) * p.inv_Gr);
-          qrow = qi * p.Hq + (g8 - qi * p.Gr);
+          const int qi = (int)(((float)colq + 0.5f) * p.inv_Gr);
+          qrow = qi * p.Hq + (colq - qi * p.Gr);
         }
-        const uint32_t lane_off = (uint32_t)((qrow * D + l8 * PER) * esz);
+        const uint32_t lane_off = (uint32_t)((qrow * D + CPL * (ln >> 4)) * esz);
         const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
 #pragma unroll
-        for (int i = 0; i < PER / 4; ++i) {
+        for (int i = 0; i < CPL / 4; ++i) {
           const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
           qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
         }
@@ -773,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       };
       auto grab = [&]() -> int {   // next free piece block of this head (valid in lane 0)
         int g = 0;
-        if (lane == 0) g = atomicAdd(&s_next[hl], 1);
+        if (lane == 0) g = atomicAdd(&s_next[vh], 1);
         return g;
       };
       Tile<D, KK, VK> A, B, C3;
@@ -785,135 +792,114 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
 
-      // -------- part 0 of each head: rotate the head's G q rows once (row g of
-      // the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
-      // operands: the scaled rotated q split into an fp16 high part (columns
-      // 0-7) and the fp16 rounding of the remainder (columns 8-15).
+      // -------- part 0 of each virtual head: rotate its 8 q rows once (row g
+      // of the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
+      // operands: the scaled rotated q split into an fp16 high part (lanes
+      // j < 8) and the fp16 rounding of the remainder (lanes j >= 8).  Lane
+      // (a, j) holds channels CPL a + r (r < CPL) of its column: the
+      // transform stages over r run in its registers, the two over a across
+      // lanes (lane bits 4 and 5).
       if (part == 0) {
-        float* qf = qf_all + hl * (8 * C::QS);
-        {
-          float x[PER];
-          if (p.q_f32) {
+        const int la = ln >> 4;
+        float x[CPL];
+        if (p.q_f32) {
 #pragma unroll
-            for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
-          } else {
+          for (int e = 0; e < CPL; ++e) x[e] = __uint_as_float(qw[e]);
+        } else {
 #pragma unroll
-            for (int k = 0; k < PER / 2; ++k) {
-              x[2 * k] = __uint_as_float(qw[k] << 16);
-              x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
+          for (int k = 0; k < CPL / 2; ++k) {
+            x[2 * k] = __uint_as_float(qw[k] << 16);
+            x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
+          }
+        }
+        const uint32_t sw = s_par[20 + ((CPL * la) >> 5)] >> ((CPL * la) & 31);
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          if ((sw >> e) & 1u) x[e] = -x[e];
+          if (!q_live) x[e] = 0.f;
+        }
+#pragma unroll
+        for (int h = 1; h < CPL; h <<= 1) {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e)
+            if ((e & h) == 0) {
+              const float a0 = x[e], b0v = x[e + h];
+              x[e] = a0 + b0v;
+              x[e + h] = a0 - b0v;
             }
-          }
-          const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
+        }
 #pragma unroll
-          for (int e = 0; e < PER; ++e) {
-            if ((sw >> e) & 1u) x[e] = -x[e];
-            if (!q_live) x[e] = 0.f;
-          }
+        for (int e = 0; e < CPL; ++e) {   // channel bit log2(CPL): lanes l, l ^ 16
+          const float o = lane_xor<16>(x[e], ln);
+          x[e] = (ln & 16) ? o - x[e] : x[e] + o;
+        }
 #pragma unroll
-          for (int h = 1; h < PER; h <<= 1) {
+        for (int e = 0; e < CPL; ++e) {   // the next channel bit: lanes l, l ^ 32
+          const float o = lane_xor<32>(x[e], ln);
+          x[e] = (ln & 32) ? o - x[e] : x[e] + o;
+        }
+        float amax = 0.f;
 #pragma unroll
-            for (int e = 0; e < PER; ++e)
-              if ((e & h) == 0) {
-                const float a0 = x[e], b0v = x[e + h];
-                x[e] = a0 + b0v;
-                x[e + h] = a0 - b0v;
-              }
-          }
-          // the 3 stages across the 8 lanes of the row go through LDS: the
-          // row is written in channel order, then lane l8 takes channels
-          // PER k + PH l8 + m (k < 8, m < PH) and runs those stages in its
-          // registers
-          constexpr int PH = PER / 8;
-          float* qrow = qf + g8 * C::QS;
-          auto at = [](int c) { return c + 4 * (c >> 4); };   // padded position of channel c
+        for (int e = 0; e < CPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = fmaxf(amax, lane_xor<16>(amax, ln));
+        amax = fmaxf(amax, lane_xor<32>(amax, ln));
+        int ex = 0;
+        if (amax > 0.f) frexpf(amax, &ex);
+        if (ln < 8) s_qexp[8 * vh + ln] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
+        const float q_pow = ldexpf(1.0f, 15 - ex);
+        half8_t* const qdst = qv_all + vh * NQK * 64 + ln;
+        if constexpr (C::MIXED) {
+          // operand element (t, e) of lane (a, j) is channel k_ch[pos] of the
+          // column, pos = (t / per_g) m + a (m / 4) + 8 (t % per_g) + e: the
+          // rows go through the virtual head's own operand area (8 rows of D
+          // floats, 4 B x 8 D = its size), read back by channel, then the
+          // operands overwrite it
+          float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
+          float* const srow = stage + (ln & 7) * D;
+          if (!(ln & 8)) {
 #pragma unroll
-          for (int i = 0; i < PER / 4; ++i) {
-            const int c = l8 * PER + 4 * i;
-            *reinterpret_cast<float4*>(qrow + at(c)) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+            for (int i = 0; i < CPL / 4; ++i)
+              *reinterpret_cast<float4*>(srow + CPL * la + 4 * i) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
           }
-          // the lanes of a row exchange values through LDS: a wave-scope
+          // the lanes of a column exchange values through LDS: a wave-scope
           // fence orders the writes above before the reads below
           __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          float y[8 * PH];
+          constexpr int m = D / 2;
+          constexpr int per_g = NQK / 2;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int c = PER * k + PH * l8;
-            if constexpr (PH == 2) {
-              const float2 f = *reinterpret_cast<const float2*>(qrow + at(c));
-              y[2 * k] = f.x;
-              y[2 * k + 1] = f.y;
-            } else {
-              y[k] = qrow[at(c)];
-            }
-          }
-#pragma unroll
-          for (int h = PH; h < 8 * PH; h <<= 1) {
-#pragma unroll
-            for (int e = 0; e < 8 * PH; ++e)
-              if ((e & h) == 0) {
-                const float a0 = y[e], b0v = y[e + h];
-                y[e] = a0 + b0v;
-                y[e + h] = a0 - b0v;
-              }
-          }
-          float amax = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int c = PER * k + PH * l8;
-            if constexpr (PH == 2) *reinterpret_cast<float2*>(qrow + at(c)) = float2{y[2 * k], y[2 * k + 1]};
-            else qrow[at(c)] = y[k];
-          }
-#pragma unroll
-          for (int e = 0; e < 8 * PH; ++e) amax = fmaxf(amax, fabsf(y[e]));
-          amax = fmaxf(amax, lane_xor<1>(amax, ln));
-          amax = fmaxf(amax, lane_xor<2>(amax, ln));
-          amax = fmaxf(amax, lane_xor<4>(amax, ln));
-          int ex = 0;
-          if (amax > 0.f) frexpf(amax, &ex);
-          if (l8 == 0) s_qexp[8 * hl + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
-        }
-        // (the fence orders this wave's exponent and row writes before its reads)
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        const float q_pow = ldexpf(1.0f, s_qexp[8 * hl + gq]);
-        const float* qrow = qf + gq * C::QS;
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-          float vq[8];
-          if constexpr (C::MIXED) {
-            constexpr int m = D / 2;
-            constexpr int per_g = NQK / 2;
+          for (int t = 0; t < NQK; ++t) {
             const int grp_k = t / per_g, u = t % per_g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int pos_l = grp_k * m + a * (m / 4) + 8 * u + e;
+              const int pos_l = grp_k * m + la * (m / 4) + 8 * u + e;
               const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
-              vq[e] = qrow[chn + 4 * (chn >> 4)];
-            }
-          } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int c = a * (D / 4) + 8 * t + 4 * h;
-              const float4 f = *reinterpret_cast<const float4*>(qrow + c + 4 * (c >> 4));
-              vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
+              x[8 * t + e] = srow[chn];
             }
           }
+          // every read above is done before the operand writes below reuse
+          // the bytes
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+        const bool lo_q = (ln & 8) != 0;
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) {
           half8_t qv;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float v = vq[e] * q_pow;
+            const float v = x[8 * t + e] * q_pow;
             const _Float16 hi = (_Float16)v;
             const _Float16 lo = (_Float16)(v - (float)hi);
-            qv[e] = lo_part ? lo : hi;
+            qv[e] = lo_q ? lo : hi;
           }
-          qv_all[(hl * NQK + t) * 64 + ln] = qv;
+          qdst[64 * t] = qv;
         }
       }
       __syncthreads();  // operands, counters and block-table entries ready
       TQ_MARK(3 + 4 * n_done);
       int ph2v = bt_at(idx_2);
       int g3 = grab();
-      const float w_col = ldexpf(p.score_mul, -s_qexp[8 * hl + gq]);
-      const half8_t* qb = qv_all + hl * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
+      const float w_col = ldexpf(p.score_mul, -s_qexp[8 * vh + gq]);
+      const half8_t* qb = qv_all + vh * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
 
       // -------- stream this wave's blocks of the piece
       // online softmax state per column: running max m_run (raw score
@@ -1176,29 +1162,34 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
       __syncthreads();
 
-      // -------- combine the parts of each (kv head, q head) pair, normalise,
-      // inverse rotation, write.  Wave w takes pairs 4 w .. 4 w + 3, 16 lanes
-      // each.  Lane m of a pair first holds dims m + 16 k (k < D / 16) and
-      // runs the transform stages over k in its registers, passes the row
-      // through LDS, then holds dims (D / 16) m + k, runs the stages over k
-      // again and the remaining ones across the lanes of the pair.
-      if (4 * wave < HG * p.G) {
+      // -------- combine the parts of each (virtual head, column) pair,
+      // normalise, inverse rotation, write.  The pairs (CV columns per
+      // virtual head) are taken 64 at a time; wave w takes pairs 4 w .. 4 w +
+      // 3 of each round, 16 lanes each.  Lane m of a pair first holds dims m
+      // + 16 k (k < D / 16) and runs the transform stages over k in its
+      // registers, passes the row through LDS, then holds dims (D / 16) m + k,
+      // runs the stages over k again and the remaining ones across the lanes
+      // of the pair.
+      const int CV = CG == 1 ? p.G : 8;
+      const int npair = VH * CV;
+      for (int pbase = 4 * wave; pbase < npair; pbase += 4 * kWaves) {
         constexpr int ND = D / 16;
         const int m = le & 15;
-        const int npair = HG * p.G;
-        const int pr_raw = 4 * wave + (le >> 4);
-        const bool live = pr_raw < npair;
-        const int pr = live ? pr_raw : npair - 1;
-        const int h2 = (int)(((float)pr + 0.5f) * p.inv_G);   // pr / G (pr < 64, G <= 8)
-        const int g = pr - h2 * p.G;
+        const int pr_raw = pbase + (le >> 4);
+        const int pr = pr_raw < npair ? pr_raw : npair - 1;
+        const int h2 = CG == 1 ? (int)(((float)pr + 0.5f) * p.inv_G) : pr >> 3;   // virtual head: pr / CV (pr < 128)
+        const int g = pr - h2 * CV;
+        const int hk = h2 / CG;                   // its kv head of the group
+        const int col = 8 * (h2 - hk * CG) + g;   // its column of the kv head
+        const bool live = pr_raw < npair && col < p.G;
         float M = -INFINITY;   // wave states: weights 2^(w s - X_w), sums l_w
-        for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * wave_of_part(h2, q, HG) + g]);
+        for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * wave_of_part(h2, q, VH) + g]);
         float y[ND];
 #pragma unroll
         for (int k = 0; k < ND; ++k) y[k] = 0.f;
         float L = 0.f;
         for (int q = 0; q < NPW; ++q) {
-          const int wq = wave_of_part(h2, q, HG);
+          const int wq = wave_of_part(h2, q, VH);
           const float mw = s_ml[16 * wq + g];
           const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
           L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
@@ -1219,7 +1210,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         // the row of part 0 is read only by this pair's lanes, each lane
         // rewrites the dims it read; the fence below orders those writes
         // before the reads of the other lanes' dims
-        float* row = slots + (8 * wave_of_part(h2, 0, HG) + g) * C::DS;
+        float* row = slots + (8 * wave_of_part(h2, 0, VH) + g) * C::DS;
 #pragma unroll
         for (int k = 0; k < ND; ++k) row[m + 16 * k] = y[k];
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // other lanes' values below
@@ -1244,8 +1235,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
         const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
         const float lse = empty ? -INFINITY : (M + log2f(L)) * kLn2;
-        const int qi = (int)(((float)g + 0.5f) * p.inv_Gr);   // column g = (query qi, q head g - qi Gr)
-        const int64_t rowq = ((int64_t)s * p.NQ + qi) * p.Hq + (grp * HG + h2) * p.Gr + (g - qi * p.Gr);
+        const int qi = (int)(((float)col + 0.5f) * p.inv_Gr);   // column col = (query qi, q head col - qi Gr)
+        const int64_t rowq = ((int64_t)s * p.NQ + qi) * p.Hq + (grp * HG + hk) * p.Gr + (col - qi * p.Gr);
         const int d0 = ND * m;
         const uint32_t sgn = s_par[24 + (d0 >> 5)] >> (d0 & 31);
 #pragma unroll
@@ -1488,13 +1479,16 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   if (!(scale > 0.f) || !(scale < INFINITY)) return set_error(TQ_ERR_VALUE, "scale must be positive and finite");
   if (block_size != TQ_BLOCK_SIZE) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "block_size must be 16");
   const int Gr = num_q_heads / num_kv_heads;
-  if ((int64_t)num_queries * Gr > 8)
-    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "more than 8 (query, q head) pairs per kv head");
+  if ((int64_t)num_queries * Gr > TQ_MAX_COLUMNS)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "more than " + std::to_string(TQ_MAX_COLUMNS) +
+                                                    " (query, q head) pairs per kv head");
   const int G = num_queries * Gr;   // matrix-core columns used per kv head
   const int kk = format_kind_k(kfmt), vk = format_kind_v(vfmt);
   if (vfmt->qjl) return set_error(TQ_ERR_VALUE, "the QJL stage is defined for K formats only");
   if (kfmt->qjl && num_queries != 1)
     return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take one query per sequence");
+  if (kfmt->qjl && Gr > 8)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take at most 8 q heads per kv head");
   if (kk < 0 && !kfmt->qjl) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
   if (vk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this V format (served: 4-bit, 2-bit)");
   const int D = kfmt->head_dim;
@@ -1571,21 +1565,28 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   p.G = G;
   p.max_blocks = max_blocks_per_seq;
   p.P = num_splits;
-  // One 16-wave workgroup per CU.  A workgroup takes the HG kv heads of a
-  // group together (its waves read the HG adjacent tiles of each physical
-  // block); HG is the largest of 8, 4, 2, 1 dividing Hkv that still leaves
-  // at least one piece per CU when every context is full length.
+  // One 16-wave workgroup per CU.  The G columns of a kv head are taken in
+  // CG groups of 8 (CG the power of two with 8 CG >= G).  A workgroup takes
+  // the HG kv heads of a group together (its waves read the HG adjacent
+  // tiles of each physical block); HG is the largest of 8, 4, 2, 1 dividing
+  // Hkv with HG * CG <= 16 that still leaves at least one piece per CU when
+  // every context is full length.
+  int CG = 1;
+  while (8 * CG < G) CG *= 2;
   const int cus = device_cus();
   int HG = 1;
   for (int hg : {8, 4, 2}) {
-    if (num_kv_heads % hg) continue;
+    if (num_kv_heads % hg || hg * CG > 16) continue;
     if ((int64_t)num_seqs * (num_kv_heads / hg) * num_splits >= cus) { HG = hg; break; }
   }
   p.HG = HG;
   p.NG = num_kv_heads / HG;
+  p.CG = CG;
+  p.VH = HG * CG;
   // starting a piece (set-up, rotation of q, epilogue) costs about as much
-  // time as streaming 128 tiles of one kv head, i.e. 128 / HG blocks
-  p.seg_cost = 128 / HG;
+  // time as streaming 128 tiles of one kv head for one column group, i.e.
+  // 128 / (HG CG) blocks
+  p.seg_cost = 128 / (HG * CG);
   p.inv_G = 1.0f / (float)G;
   p.NQ = num_queries;
   p.Gr = Gr;

@@ -142,7 +142,7 @@ def test_decode_status_codes_without_launch():
     s = signs(0, 1, 128)
     assert _call_decode(Hq=7) == tq.TQ_ERR_VALUE
     assert _call_decode(bs=8) == tq.TQ_ERR_UNSUPPORTED_FORMAT
-    assert _call_decode(Hq=18, Hkv=1) == tq.TQ_ERR_UNSUPPORTED_FORMAT     # GQA group above 8
+    assert _call_decode(Hq=130, Hkv=1) == tq.TQ_ERR_UNSUPPORTED_FORMAT    # GQA group above 128
     assert _call_decode(kf=tq.Format(128, [3], s)) == tq.TQ_ERR_UNSUPPORTED_FORMAT
     assert _call_decode(vf=tq.Format(128, [3], s)) == tq.TQ_ERR_UNSUPPORTED_FORMAT
     assert "no decode kernel" in tq._lib.tq_last_error().decode()
@@ -219,10 +219,20 @@ def test_multi_query_status_codes_without_launch():
                                        ctypes.byref(f.c), ctypes.byref(f.c), 0.1, 1, None, 0, 16, tq.TQ_BF16,
                                        None, None, None)
     assert call(NQ=0) == tq.TQ_ERR_VALUE
-    assert call(NQ=3) == tq.TQ_ERR_UNSUPPORTED_FORMAT          # 3 queries x 4 q heads > 8 columns
+    assert call(NQ=33, B=0) == tq.TQ_ERR_UNSUPPORTED_FORMAT    # 33 queries x 4 q heads > 128 columns
     assert "pairs per kv head" in L.tq_last_error().decode()
-    assert call(NQ=9, Hq=2, Hkv=2) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert call(NQ=129, Hq=2, Hkv=2, B=0) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert call(NQ=32, B=0) == tq.TQ_OK                         # exactly 128 columns
+    assert call(NQ=1, Hq=256, Hkv=2, B=0) == tq.TQ_OK           # 128 q heads per kv head
     assert call(B=0) == tq.TQ_OK
+    qc = _qjl_c(f)
+    def call_qjl(NQ, Hq):
+        return L.tq_decode_paged_multi(16, tq.TQ_BF16, 0, NQ, Hq, 2, 16, 16, 10, 16, 16, 4, 16,
+                                       ctypes.byref(qc), ctypes.byref(f.c), 0.1, 1, None, 0, 16, tq.TQ_BF16,
+                                       None, None, None)
+    assert call_qjl(2, 8) == tq.TQ_ERR_UNSUPPORTED_FORMAT       # the QJL stage: one query
+    assert call_qjl(1, 32) == tq.TQ_ERR_UNSUPPORTED_FORMAT      # and at most 8 q heads per kv head
+    assert call_qjl(1, 16) == tq.TQ_OK
 
 
 def _qjl_c(f, proj=0x1000):
