@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_F16_TFLOPS = 2500.0   # dense fp16 matrix-core peak
 SPLITS = {2: 16, 4: 16, 5: 64, 6: 64, 7: 64, 1: 1}
 LAYERS = {2: 3, 4: 2, 5: 1, 6: 1, 7: 1, 1: 1}
 FLUSH_BYTES = 1 << 30
@@ -311,9 +312,10 @@ def window_cold(b, launches, warmup, flush, cap=132):
 
 
 def multi_cold(b, launches, warmup, flush, nq=2):
-    """Multi-query decode on the 8B-shaped cache of `b`: nq queries per
-    sequence (the last nq cached tokens are theirs) in one call; times it with
-    cold caches.  Returns (sorted ms, algorithmic bytes)."""
+    """Multi-query decode on the cache of `b`: nq queries per sequence (the
+    last nq cached tokens are theirs) in one call; times it with cold caches.
+    Returns (sorted ms, algorithmic bytes, algorithmic flops): the flops are
+    4 d per (query, q head, visible token), q.K and P.V at 2 d each."""
     import numpy as np
     import torch
     import workloads as wl
@@ -339,7 +341,10 @@ def multi_cold(b, launches, warmup, flush, nq=2):
         ev[i][1].record()
     torch.cuda.synchronize()
     extra = (nq - 1) * B * Hq * (2 * d * 2 + 4)   # the other queries' q, out and lse
-    return sorted(a.elapsed_time(c) for a, c in ev), b.decode_bytes + extra
+    ctx = w.context_lens.astype(np.int64)
+    visible = sum(int(np.maximum(ctx - (nq - 1 - i), 0).sum()) for i in range(nq))
+    flops = 4 * d * Hq * visible
+    return sorted(a.elapsed_time(c) for a, c in ev), b.decode_bytes + extra, flops
 
 
 def phase_trace(index, launches, flush):
@@ -579,7 +584,7 @@ def main():
                          "frac": round(wbytes_win / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "kernel": "tq_decode_dense (window attention + merge with the history)"}}
         log(f"window: {wavg * 1e3:.1f} us")
-        mq_ms, mq_bytes = multi_cold(b, max(10, args.steps // 2), args.warmup, flush)
+        mq_ms, mq_bytes, _ = multi_cold(b, max(10, args.steps // 2), args.warmup, flush)
         mq_avg = sum(mq_ms) / len(mq_ms)
         result["multi_query"] = {
             "workload": f"{w.name}, 2 queries per sequence (causal over the cache, one call)",
@@ -604,6 +609,21 @@ def main():
                                "decode_GBs": round(b4.decode_bytes / (a4 * 1e-3) / 1e9, 1),
                                "frac_of_peak": round(b4.decode_bytes / (a4 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                                "num_splits": b4.P, "traffic": stored_traffic("70b")}
+        # chunked prefill over the same cache: 16 queries per sequence, 128
+        # (query, q head) columns per kv head, one call
+        nq = 16
+        mq_ms, mq_bytes, mq_flops = multi_cold(b4, n4, args.warmup, flush, nq=nq)
+        mq_avg = sum(mq_ms) / len(mq_ms)
+        mq_tf = mq_flops / (mq_avg * 1e-3) / 1e12
+        result["multi_query_70b"] = {
+            "workload": f"{b4.w.name}, {nq} queries per sequence (causal over the cache, one call)",
+            "decode_us": stats_us(mq_ms), "num_splits": b4.P, "algorithmic_bytes": mq_bytes,
+            "algorithmic_flops": mq_flops,
+            "GBs": round(mq_bytes / (mq_avg * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(mq_bytes / (mq_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "TFLOPs": round(mq_tf, 1),
+            "frac_of_fp16_mfma_peak": round(mq_tf / PEAK_F16_TFLOPS, 4)}
+        log(f"multi-query 70b x{nq}: {mq_avg * 1e3:.1f} us, {mq_tf:.0f} TFLOP/s")
         del b4
         torch.cuda.empty_cache()
         # the other workloads: the write path and the tiny / long-context decodes

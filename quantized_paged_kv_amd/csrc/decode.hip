@@ -720,16 +720,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const int e = tid + kThreads * i;
         btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
       }
-      // q of the virtual head's 8 columns: lane (a, j) loads channels
-      // CPL a .. CPL a + CPL - 1 of column 8 cg + (j & 7)'s q row (lanes j and
-      // j + 8 load the same); one load shape for both dtypes (bf16: two
-      // channels per word, the upper half of qw unused), bytes past the q
-      // tensor read as zero through the descriptor's range check
-      constexpr int CPL = D / 4;
+      constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per column
       const int ln = fresh_lane();
-      const int colq = 8 * cg + (ln & 7);
+      const int g8 = ln >> 3, l8 = ln & 7;
+      const int colq = 8 * cg + g8;           // this lane's column in the rotation
       const bool q_live = colq < p.G;
-      uint32_t qw[CPL];
+      // raw q words of this lane's PER channels (bf16: two per word, the upper
+      // half of qw unused); one load shape for both dtypes, bytes past the q
+      // tensor read as zero through the descriptor's range check
+      uint32_t qw[PER];
       {   // issued by every wave (parts > 0 discard them) so that all paths
           // carry the same loads and later waits count exactly
         const int esz = p.q_f32 ? 4 : 2;
@@ -739,10 +738,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           const int qi = (int)(((float)colq + 0.5f) * p.inv_Gr);
           qrow = qi * p.Hq + (colq - qi * p.Gr);
         }
-        const uint32_t lane_off = (uint32_t)((qrow * D + CPL * (ln >> 4)) * esz);
+        const uint32_t lane_off = (uint32_t)((qrow * D + l8 * PER) * esz);
         const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
 #pragma unroll
-        for (int i = 0; i < CPL / 4; ++i) {
+        for (int i = 0; i < PER / 4; ++i) {
           const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
           qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
         }
@@ -795,103 +794,131 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // -------- part 0 of each virtual head: rotate its 8 q rows once (row g
       // of the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
       // operands: the scaled rotated q split into an fp16 high part (lanes
-      // j < 8) and the fp16 rounding of the remainder (lanes j >= 8).  Lane
-      // (a, j) holds channels CPL a + r (r < CPL) of its column: the
-      // transform stages over r run in its registers, the two over a across
-      // lanes (lane bits 4 and 5).
+      // j < 8) and the fp16 rounding of the remainder (lanes j >= 8).  The
+      // rows are staged in the virtual head's own operand area (8 rows of D
+      // floats: its size), which the operands overwrite once every lane has
+      // read its values.
       if (part == 0) {
-        const int la = ln >> 4;
-        float x[CPL];
-        if (p.q_f32) {
+        float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
+        {
+          float x[PER];
+          if (p.q_f32) {
 #pragma unroll
-          for (int e = 0; e < CPL; ++e) x[e] = __uint_as_float(qw[e]);
-        } else {
+            for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
+          } else {
 #pragma unroll
-          for (int k = 0; k < CPL / 2; ++k) {
-            x[2 * k] = __uint_as_float(qw[k] << 16);
-            x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
-          }
-        }
-        const uint32_t sw = s_par[20 + ((CPL * la) >> 5)] >> ((CPL * la) & 31);
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          if ((sw >> e) & 1u) x[e] = -x[e];
-          if (!q_live) x[e] = 0.f;
-        }
-#pragma unroll
-        for (int h = 1; h < CPL; h <<= 1) {
-#pragma unroll
-          for (int e = 0; e < CPL; ++e)
-            if ((e & h) == 0) {
-              const float a0 = x[e], b0v = x[e + h];
-              x[e] = a0 + b0v;
-              x[e + h] = a0 - b0v;
+            for (int k = 0; k < PER / 2; ++k) {
+              x[2 * k] = __uint_as_float(qw[k] << 16);
+              x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
             }
-        }
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {   // channel bit log2(CPL): lanes l, l ^ 16
-          const float o = lane_xor<16>(x[e], ln);
-          x[e] = (ln & 16) ? o - x[e] : x[e] + o;
-        }
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) {   // the next channel bit: lanes l, l ^ 32
-          const float o = lane_xor<32>(x[e], ln);
-          x[e] = (ln & 32) ? o - x[e] : x[e] + o;
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        amax = fmaxf(amax, lane_xor<16>(amax, ln));
-        amax = fmaxf(amax, lane_xor<32>(amax, ln));
-        int ex = 0;
-        if (amax > 0.f) frexpf(amax, &ex);
-        if (ln < 8) s_qexp[8 * vh + ln] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
-        const float q_pow = ldexpf(1.0f, 15 - ex);
-        half8_t* const qdst = qv_all + vh * NQK * 64 + ln;
-        if constexpr (C::MIXED) {
-          // operand element (t, e) of lane (a, j) is channel k_ch[pos] of the
-          // column, pos = (t / per_g) m + a (m / 4) + 8 (t % per_g) + e: the
-          // rows go through the virtual head's own operand area (8 rows of D
-          // floats, 4 B x 8 D = its size), read back by channel, then the
-          // operands overwrite it
-          float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
-          float* const srow = stage + (ln & 7) * D;
-          if (!(ln & 8)) {
-#pragma unroll
-            for (int i = 0; i < CPL / 4; ++i)
-              *reinterpret_cast<float4*>(srow + CPL * la + 4 * i) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
           }
-          // the lanes of a column exchange values through LDS: a wave-scope
+          const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            if ((sw >> e) & 1u) x[e] = -x[e];
+            if (!q_live) x[e] = 0.f;
+          }
+#pragma unroll
+          for (int h = 1; h < PER; h <<= 1) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+              if ((e & h) == 0) {
+                const float a0 = x[e], b0v = x[e + h];
+                x[e] = a0 + b0v;
+                x[e + h] = a0 - b0v;
+              }
+          }
+          // the 3 stages across the 8 lanes of the row go through LDS: the
+          // row is written in channel order, then lane l8 takes channels
+          // PER k + PH l8 + m (k < 8, m < PH) and runs those stages in its
+          // registers
+          constexpr int PH = PER / 8;
+          float* qrow = stage + g8 * D;
+#pragma unroll
+          for (int i = 0; i < PER / 4; ++i)
+            *reinterpret_cast<float4*>(qrow + l8 * PER + 4 * i) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+          // the lanes of a row exchange values through LDS: a wave-scope
           // fence orders the writes above before the reads below
           __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          constexpr int m = D / 2;
-          constexpr int per_g = NQK / 2;
+          float y[8 * PH];
 #pragma unroll
-          for (int t = 0; t < NQK; ++t) {
+          for (int k = 0; k < 8; ++k) {
+            const int c = PER * k + PH * l8;
+            if constexpr (PH == 2) {
+              const float2 f = *reinterpret_cast<const float2*>(qrow + c);
+              y[2 * k] = f.x;
+              y[2 * k + 1] = f.y;
+            } else {
+              y[k] = qrow[c];
+            }
+          }
+#pragma unroll
+          for (int h = PH; h < 8 * PH; h <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 8 * PH; ++e)
+              if ((e & h) == 0) {
+                const float a0 = y[e], b0v = y[e + h];
+                y[e] = a0 + b0v;
+                y[e + h] = a0 - b0v;
+              }
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int c = PER * k + PH * l8;
+            if constexpr (PH == 2) *reinterpret_cast<float2*>(qrow + c) = float2{y[2 * k], y[2 * k + 1]};
+            else qrow[c] = y[k];
+          }
+#pragma unroll
+          for (int e = 0; e < 8 * PH; ++e) amax = fmaxf(amax, fabsf(y[e]));
+          amax = fmaxf(amax, lane_xor<1>(amax, ln));
+          amax = fmaxf(amax, lane_xor<2>(amax, ln));
+          amax = fmaxf(amax, lane_xor<4>(amax, ln));
+          int ex = 0;
+          if (amax > 0.f) frexpf(amax, &ex);
+          if (l8 == 0) s_qexp[8 * vh + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
+        }
+        // (the fence orders this wave's exponent and row writes before its reads)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const float q_pow = ldexpf(1.0f, s_qexp[8 * vh + gq]);
+        const float* qrow = stage + gq * D;
+        float vq[NQK][8];
+#pragma unroll
+        for (int t = 0; t < NQK; ++t) {
+          if constexpr (C::MIXED) {
+            // operand element (t, e) of lane (a, j): channel k_ch[pos] of the
+            // column, pos = (t / per_g) m + a (m / 4) + 8 (t % per_g) + e
+            constexpr int m = D / 2;
+            constexpr int per_g = NQK / 2;
             const int grp_k = t / per_g, u = t % per_g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int pos_l = grp_k * m + la * (m / 4) + 8 * u + e;
+              const int pos_l = grp_k * m + a * (m / 4) + 8 * u + e;
               const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
-              x[8 * t + e] = srow[chn];
+              vq[t][e] = qrow[chn];
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float4 f = *reinterpret_cast<const float4*>(qrow + a * (D / 4) + 8 * t + 4 * h);
+              vq[t][4 * h] = f.x; vq[t][4 * h + 1] = f.y; vq[t][4 * h + 2] = f.z; vq[t][4 * h + 3] = f.w;
             }
           }
-          // every read above is done before the operand writes below reuse
-          // the bytes
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
-        const bool lo_q = (ln & 8) != 0;
+        // every row read above is done before the operand writes below reuse
+        // the bytes
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
         for (int t = 0; t < NQK; ++t) {
           half8_t qv;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float v = x[8 * t + e] * q_pow;
+            const float v = vq[t][e] * q_pow;
             const _Float16 hi = (_Float16)v;
             const _Float16 lo = (_Float16)(v - (float)hi);
-            qv[e] = lo_q ? lo : hi;
+            qv[e] = lo_part ? lo : hi;
           }
-          qdst[64 * t] = qv;
+          qv_all[(vh * NQK + t) * 64 + ln] = qv;
         }
       }
       __syncthreads();  // operands, counters and block-table entries ready
