@@ -501,7 +501,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="8b", choices=sorted(NAMES))
+    ap.add_argument("--workload", default="8b", choices=sorted(NAMES) + ["write"],
+                    help="decode workload of the step; 'write' times only the quantise-on-write workload")
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -530,8 +531,16 @@ def main():
               f"sequence with no exchange", file=sys.stderr)
         sys.exit(2)
     import torch
-    index = NAMES[args.workload]
     flush = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    if args.workload == "write":
+        ww, wms, wbytes = write_cold(args.steps, args.warmup, flush)
+        wavg = sum(wms) / len(wms)
+        print(json.dumps({"write": {"workload": ww.name, "us": stats_us(wms), "algorithmic_bytes": wbytes,
+                                    "GBs": round(wbytes / (wavg * 1e-3) / 1e9, 1),
+                                    "frac_of_peak": round(wbytes / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}),
+              flush=True)
+        return
+    index = NAMES[args.workload]
     b = Bench(index, splits=args.splits)
     ms_step, dec_warm = b.timed(args.steps, args.warmup)
     ms_graph = b.timed_graph(args.steps, args.warmup)

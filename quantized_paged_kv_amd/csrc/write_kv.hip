@@ -44,7 +44,7 @@ struct WriteParams {
 };
 
 template <int D, bool F32>
-__global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
+__global__ __launch_bounds__(kThreads, 4) void write_kv_kernel(WriteParams p) {
   constexpr int LPR = D / 8;              // lanes per row
   constexpr int RPB = kThreads / LPR;     // rows per block
   __shared__ double lds_w[RPB][D];
@@ -171,38 +171,58 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
       }
     }
   }
-  // ---- h = 8, 16, ... across lanes: partner lane L ^ (h / 8), moved by DPP
-  // within the row's 8 or 16 lanes (the lower lane keeps a + b, the upper
-  // a - b, a being the lower lane's value)
-  // (one fma with a factor of +-1 is the add or the subtraction itself:
-  // the product is exact and the sum is rounded once)
-  auto across = [&](auto kc) {
-    constexpr int k = decltype(kc)::value;
-    const double sgn = (L & k) ? -1.0 : 1.0;
+  // ---- h = 8: partner lane L ^ 1, moved by DPP (the lower lane keeps a + b,
+  // the upper a - b, a being the lower lane's value; one fma with a factor
+  // of +-1 is the add or the subtraction itself: the product is exact and
+  // the sum is rounded once)
+  {
+    const double sgn = (L & 1) ? -1.0 : 1.0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __builtin_fma(sgn, v[e], lane_xor_d<k>(v[e], L));
-  };
-  across(std::integral_constant<int, 1>{});
-  across(std::integral_constant<int, 2>{});
-  across(std::integral_constant<int, 4>{});
-  if constexpr (LPR == 16) across(std::integral_constant<int, 8>{});
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_fma(sgn, v[e], lane_xor_d<1>(v[e], L));
+  }
+  // ---- h = 16 .. D/2 inside the lane: the row goes through LDS once, lane
+  // L then holding channels L + LPR e (channel bits 4 and up are bits of e),
+  // and back (the row's lanes are in one wave: a wave-scope fence orders
+  // the exchange)
+  double* const wrow = lds_w[lr];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the previous row's reads are done
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) *reinterpret_cast<double2*>(wrow + 8 * L + e) = double2{v[e], v[e + 1]};
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = wrow[L + LPR * e];
+#pragma unroll
+  for (int h = 16 / LPR; h < 8; h *= 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if ((e & h) == 0) {
+        const double a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) wrow[L + LPR * e] = v[e];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
-  // ---- gather each group's channels in listed order: lane L takes listed
+  // ---- each group's channels in listed order: lane L takes listed
   // positions [E*L, E*L+E) of each group (E = 8 for one group, 4 for two).
   const int ng = f.ng;
   double wg[8];
   if (ng == 1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wg[e] = v[e];
+    for (int e = 0; e < 8; e += 2) {
+      const double2 t = *reinterpret_cast<const double2*>(wrow + 8 * L + e);
+      wg[e] = t.x;
+      wg[e + 1] = t.y;
+    }
   } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lds_w[lr][8 * L + e] = v[e];
-    __syncthreads();
     const int m = D / 2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int g = e >> 2;
-      wg[e] = lds_w[lr][f.ch[g * m + 4 * L + (e & 3)]];
+      wg[e] = wrow[f.ch[g * m + 4 * L + (e & 3)]];
     }
   }
 
@@ -221,34 +241,39 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
     ss[1] = s47;
   }
   ss[0] = ss[0] + lane_xor_d<1>(ss[0], L);
-  ss[1] = ss[1] + lane_xor_d<1>(ss[1], L);
   ss[0] = ss[0] + lane_xor_d<2>(ss[0], L);
-  ss[1] = ss[1] + lane_xor_d<2>(ss[1], L);
   ss[0] = ss[0] + lane_xor_d<4>(ss[0], L);
-  ss[1] = ss[1] + lane_xor_d<4>(ss[1], L);
-  if constexpr (LPR == 16) {
-    ss[0] = ss[0] + lane_xor_d<8>(ss[0], L);
-    ss[1] = ss[1] + lane_xor_d<8>(ss[1], L);
+  if constexpr (LPR == 16) ss[0] = ss[0] + lane_xor_d<8>(ss[0], L);
+  if (ng == 2) {   // (uniform: the tensor's format)
+    ss[1] = ss[1] + lane_xor_d<1>(ss[1], L);
+    ss[1] = ss[1] + lane_xor_d<2>(ss[1], L);
+    ss[1] = ss[1] + lane_xor_d<4>(ss[1], L);
+    if constexpr (LPR == 16) ss[1] = ss[1] + lane_xor_d<8>(ss[1], L);
   }
 
-  // ---- norms, thresholds, indices and the packed bit fields
+  // ---- norms, thresholds, indices and the packed bit fields: group g
+  // holds values wg[BASE .. BASE + E) (compile-time, so that every index
+  // into the lane's arrays is static)
   uint32_t field[2] = {0u, 0u};
   uint16_t norm16[2] = {0, 0};
-  const int E = (ng == 1) ? 8 : 4;
-  for (int g = 0; g < ng; ++g) {
+  auto quant = [&](auto gk, auto ek) {
+    constexpr int g = decltype(gk)::value;
+    constexpr int E = decltype(ek)::value;
+    constexpr int BASE = g * E;
     const int bits = f.bits[g];
     const int levels = 1 << bits;
-    const int m = D / ng;
+    const int m = D / (8 / E);   // channels of the group: D (one group) or D / 2
     const double s = ss[g];
     uint32_t fld = 0;
     if (s == 0.0) {
       const uint32_t z = (uint32_t)(levels / 2 - 1);
+#pragma unroll
       for (int e = 0; e < E; ++e) fld |= z << (bits * e);
       norm16[g] = 0;
     } else {
       norm16[g] = f64_to_f16_rne(__builtin_sqrt(s / (double)D));
       const double r = __builtin_sqrt(s / (double)m);
-      uint32_t idx[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      uint32_t idx[E];
       // idx = number of scaled thresholds T_i = thr_i * r below the value.
       // Fast path: the bucket of z = w / r (float estimate) gives the count
       // of thresholds in lower buckets, exact because no threshold lies
@@ -256,23 +281,23 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
       // bucket may hold is compared exactly.  Otherwise every threshold is
       // compared (the level count made a compile-time constant so that the
       // comparisons unroll).
-      const int base = (ng == 1) ? 0 : 4 * g;
       // (the float estimate needs r inside the normal float range; |z| <= sqrt(m))
       if (f.fast[g] && r > 1e-30 && r < 1e30) {
         const float rinv = __builtin_amdgcn_rcpf((float)r);
         const float off = f.lut_off[g];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (e < base || e >= base + E) continue;
-          const float z = (float)wg[e] * rinv;
+        for (int e = 0; e < E; ++e) {
+          const float z = (float)wg[BASE + e] * rinv;
           int k = __float2int_rd(__builtin_fmaf(z, 32.0f, off));
           k = k < 0 ? 0 : (k > 255 ? 255 : k);
           const uint32_t ent = lds_bkt[g][k];
           const uint32_t below = ent & 0x7Fu;
           const double T = lds_thr[g][below] * r;
-          idx[e] = below + (((ent & 0x80u) && T < wg[e]) ? 1u : 0u);
+          idx[e] = below + ((ent >> 7) & (T < wg[BASE + e] ? 1u : 0u));
         }
       } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) idx[e] = 0;
         auto count_below = [&](auto lv) {
           constexpr int LV = decltype(lv)::value;
           double T[LV - 1];
@@ -281,18 +306,24 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
 #pragma unroll
           for (int i = 0; i < LV - 1; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) idx[e] += (T[i] < wg[e]) ? 1u : 0u;
+            for (int e = 0; e < E; ++e) idx[e] += (T[i] < wg[BASE + e]) ? 1u : 0u;
         };
         if (levels == 16) count_below(std::integral_constant<int, 16>{});
         else if (levels == 8) count_below(std::integral_constant<int, 8>{});
         else count_below(std::integral_constant<int, 4>{});
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < E) fld |= idx[base + e] << (bits * e);
+      for (int e = 0; e < E; ++e) fld |= idx[e] << (bits * e);
     }
     field[g] = fld;
+  };
+  if (ng == 1) {
+    quant(std::integral_constant<int, 0>{}, std::integral_constant<int, 8>{});
+  } else {
+    quant(std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+    quant(std::integral_constant<int, 1>{}, std::integral_constant<int, 4>{});
   }
+  const int E = (ng == 1) ? 8 : 4;
 
   const int64_t blk = slot >> 4;
   const int offs = (int)(slot & 15);
@@ -364,6 +395,20 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(WriteParams p) {
   }
 }
 
+// Workgroups of write_kv_kernel<D, F32> one CU holds at once (looked up
+// once per instantiation).
+template <int D, bool F32>
+int resident_per_cu() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, write_kv_kernel<D, F32>, kThreads, 0) != hipSuccess ||
+        b < 1)
+      b = 1;
+    return b;
+  }();
+  return n;
+}
+
 }  // namespace
 }  // namespace tq
 
@@ -414,16 +459,25 @@ extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype
   p.dev_err = dev_err;
   const int rpb = kThreads / (d / 8);
   p.num_units = (num_tokens + rpb - 1) / rpb * num_kv_heads;
-  const int64_t wgs = std::min<int64_t>(p.num_units, (int64_t)device_cus() * 8);
-  dim3 grid((unsigned)wgs, (unsigned)n_tensors);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool f32 = in_dtype == TQ_F32;
+  // persistent workgroups: as many as can be resident at once, every one
+  // looping over units (a grid larger than that would run in rounds)
+  auto launch = [&](auto dk, auto fk) {
+    constexpr int DD = decltype(dk)::value;
+    constexpr bool FF = decltype(fk)::value;
+    const int64_t wgs = std::min<int64_t>(p.num_units, (int64_t)device_cus() * resident_per_cu<DD, FF>());
+    hipLaunchKernelGGL((write_kv_kernel<DD, FF>), dim3((unsigned)wgs, (unsigned)n_tensors), dim3(kThreads), 0, s,
+                       p);
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
   if (d == 128) {
-    if (f32) hipLaunchKernelGGL((write_kv_kernel<128, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((write_kv_kernel<128, false>), grid, dim3(kThreads), 0, s, p);
+    if (f32) launch(I128{}, std::true_type{});
+    else launch(I128{}, std::false_type{});
   } else {
-    if (f32) hipLaunchKernelGGL((write_kv_kernel<64, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((write_kv_kernel<64, false>), grid, dim3(kThreads), 0, s, p);
+    if (f32) launch(I64{}, std::true_type{});
+    else launch(I64{}, std::false_type{});
   }
   tq_status st = launch_status("tq_write_kv launch");
   if (st != TQ_OK || !k || !kfmt->qjl) return st;
