@@ -21,7 +21,12 @@ Index plane: in K pages ("k" role) row t occupies bytes
 multiple of 16, the plane is lane-major: with c = row_bytes / 16, byte b of
 row t sits at ((16*(t % 4) + b // c)*4 + t // 4)*c + b % c, i.e. 64 runs of
 4*c bytes, run 16*q + j holding bytes [c*j, c*(j+1)) of rows q, q+4, q+8,
-q+12 in that order; other V formats use the K layout.
+q+12 in that order.  Two-group V formats (the recipe row applied to V)
+store each group's bytes in a sub-plane of its own, group g's at 16 times
+the group's byte offset in a row: a row's m * b_g bits of group g fall into
+m / 8 octets of b_g bytes (8 indices each), and octet o of row t sits in
+run (m / 8) * (t % 4) + o of 4 * b_g bytes, at place t // 4.  Other V
+formats use the K layout.
 
 QJL K formats (oracle/qjl.py): each row's index bytes are its MSE indices
 followed by its sign string (oracle/qjl.py), and the norm plane holds the
@@ -49,6 +54,30 @@ def lane_chunk(fmt: Format, role: str) -> int:
         raise ValueError("role must be 'k' or 'v'")
     rb = row_bytes(fmt)
     return rb // 16 if role == "v" and rb % 16 == 0 else 0
+
+
+def octet_run_positions(fmt: Format, t) -> np.ndarray:
+    """Tile byte offsets of the index bytes of rows at in-block offsets t in
+    a two-group V page (octet runs per group, see the module docstring):
+    array [len(t), row_bytes]."""
+    t = np.asarray(t, dtype=np.int64).reshape(-1, 1)
+    m = fmt.group_size
+    cols, base = [], 0
+    for b in fmt.group_bits:
+        nbytes = m * b // 8
+        j = np.arange(nbytes, dtype=np.int64)[None, :]
+        o, q = j // b, j % b
+        cols.append(16 * base + ((m // 8) * (t % 4) + o) * 4 * b + (t // 4) * b + q)
+        base += nbytes
+    return np.concatenate(cols, axis=1)
+
+
+def index_positions(fmt: Format, role: str, t) -> np.ndarray:
+    """Tile byte offsets of index bytes 0..row_bytes-1 of the rows at in-block
+    offsets t for the page role ("k" or "v"): array [len(t), row_bytes]."""
+    if role == "v" and fmt.num_groups == 2 and not fmt.qjl:
+        return octet_run_positions(fmt, t)
+    return row_positions(row_bytes(fmt), t, lane_chunk(fmt, role))
 
 
 def row_positions(rb: int, t, chunk: int) -> np.ndarray:
@@ -83,7 +112,8 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
     T, H, d = x.shape
     nb = pages.shape[0]
     rb, norm_off, tile = tile_layout(fmt, block_size)
-    chunk = lane_chunk(fmt, role)
+    if role not in ("k", "v"):
+        raise ValueError("role must be 'k' or 'v'")
     if pages.dtype != np.uint8 or pages.shape[1:] != (H, tile):
         raise ValueError("page pool shape does not match the format")
     if fmt.qjl and role != "k":
@@ -107,7 +137,7 @@ def write_pages(x: np.ndarray, slot_mapping: np.ndarray, pages: np.ndarray, fmt:
         sbits, gam = _qjl.residual_fields(w, idx_groups, norms, fmt)
         data = np.concatenate([data, _qjl.pack_signs(sbits)], axis=-1)
         norms = np.concatenate([norms, gam], axis=-1)     # [T, H, 2G]: vector norms, residual norms
-    pos_rows = row_positions(rb, off, chunk)              # [T, rb]
+    pos_rows = index_positions(fmt, role, off)            # [T, rb]
     for h in range(H):
         for b in range(rb):
             pages[blk, h, pos_rows[:, b]] = data[:, h, b]
@@ -126,7 +156,7 @@ def read_rows(pages: np.ndarray, blocks: np.ndarray, offsets: np.ndarray, head: 
     blocks = np.asarray(blocks, dtype=np.int64)
     offsets = np.asarray(offsets, dtype=np.int64)
     t = pages[blocks, head]                                          # [n, tile]
-    cols = row_positions(rb, offsets, lane_chunk(fmt, role))
+    cols = index_positions(fmt, role, offsets)
     data = np.take_along_axis(t, cols, axis=1)
     idx = unpack_row(data, fmt)
     G = fmt.num_groups

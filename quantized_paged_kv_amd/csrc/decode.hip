@@ -57,6 +57,7 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 
 constexpr int kWaves = 16;   // one workgroup per CU
 constexpr int kThreads = kWaves * 64;
@@ -69,7 +70,7 @@ constexpr uint32_t kDoneBits = 0x7FC0D0E5u;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum KKind { K4 = 0, K2 = 1, KM43 = 2, KM32 = 3 };
-enum VKind { V4 = 0, V2 = 1 };
+enum VKind { V4 = 0, V2 = 1, VM43 = 2, VM32 = 3 };
 
 struct DecodeParams {
   const void* q;
@@ -113,7 +114,8 @@ struct DecodeParams {
   int32_t half_kind[2];      // 0 none, 4 = nibble table, 2 = crumb table
   uint16_t k3_cb[8];         // 3-bit codebook of the mixed K low group
   uint8_t k_ch[128];
-  int32_t v_half;            // LUT half that V reads
+  uint8_t v_ch[128];         // V's listed channel order (two-group V formats)
+  int32_t v_half;            // LUT half that V reads (its 4-bit or 2-bit group)
   int32_t q_f32, out_f32;
   int32_t q_bytes;           // size of q in bytes (< 2^31)
 #ifdef TQ_PHASE_TRACE
@@ -208,10 +210,21 @@ struct Cfg {
                               : KK == K2 ? D / 4
                               : KK == KM43 ? (D / 2) * 4 / 8 + (D / 2) * 3 / 8
                                            : (D / 2) * 3 / 8 + (D / 2) * 2 / 8;
-  static constexpr int VROW = VK == V4 ? D / 2 : D / 4;
-  static constexpr int VLANE = VK == V4 ? D / 32 : D / 64;  // bytes per lane per token in V
-  static constexpr bool MIXED = KK == KM43 || KK == KM32;   // two groups: 3-bit pair table in use
-  static constexpr int LDS_LUT = kLutBytes + (MIXED ? kLut3Bytes : 0);
+  static constexpr int VROW = VK == V4 ? D / 2 : VK == V2 ? D / 4 : VK == VM43 ? (D / 2) * 7 / 8 : (D / 2) * 5 / 8;
+  static constexpr int VLANE = VK == V4 ? D / 32 : D / 64;  // one-group V: bytes per lane per token
+  static constexpr bool MIXED = KK == KM43 || KK == KM32;   // two K groups
+  // Two V groups: group g's octets (8 indices, b_g bytes) in runs of 4
+  // tokens; lane (a, r) reads run (OCT a + r % OCT) of each group and holds
+  // positions 8 (r % OCT) + (r / OCT) PPL + i (i < PPL) of its 4 tokens
+  static constexpr bool MIXED_V = VK == VM43 || VK == VM32;
+  static constexpr int VB0 = VK == VM43 ? 4 : 3, VB1 = VK == VM43 ? 3 : 2;   // bits of V groups 0, 1
+  static constexpr int OCT = D / 16;                       // octets per V group (m / 8)
+  static constexpr int PPL = D / 32;                       // positions per lane per V group (m / 16)
+  static constexpr int VW0 = MIXED_V ? VB0 : 4;            // words of the lane's group-0 run (one group: v[4])
+  static constexpr int VW = MIXED_V ? VB0 + VB1 : 4;       // V index words per lane per tile
+  static constexpr int NVG = MIXED_V ? 2 : 1;              // V norm groups
+  static constexpr bool PAIR3 = MIXED || MIXED_V;          // 3-bit pair table in use
+  static constexpr int LDS_LUT = kLutBytes + (PAIR3 ? kLut3Bytes : 0);
   static constexpr int QV_FLOATS = NQK * 64 * 4;          // q.K B operands of one virtual head: NQK x 64 lanes x half8
   static constexpr int DS = D + 4;                        // wave-state row stride (floats)
   static constexpr int QX_FLOATS = kWaves * QV_FLOATS;           // operands of up to 16 virtual heads
@@ -225,8 +238,8 @@ struct Tile {
   uint32_t k[4];      // packed K bits of this lane (up to 16 B)
   uint32_t k_lo[2];   // mixed: low-group bits (aligned 8 B window)
   uint2 kn[2];        // K norms of the lane's 4 tokens, per group
-  uint32_t v[4];      // packed V bits of the lane's 4 tokens (raw words of its run)
-  uint2 vn;           // V norms
+  uint32_t v[Cfg<D, KK, VK>::VW];   // packed V bits of the lane's 4 tokens (raw words of its run(s))
+  uint2 vn[Cfg<D, KK, VK>::NVG];    // V norms of the lane's 4 tokens, per group
 };
 
 // Buffer descriptor flags word for raw (untyped) loads: 32-bit data format.
@@ -251,7 +264,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
 template <int D, int KK, int VK>
 __device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                           uint32_t kb, uint32_t vb, uint32_t k_off, uint32_t klo_off,
-                                          uint32_t n_off, uint32_t v_off) {
+                                          uint32_t n_off, uint32_t v_off, uint32_t v_off1) {
   using C = Cfg<D, KK, VK>;
   constexpr uint32_t KN = 16 * C::KROW, VN = 16 * C::VROW;   // norm areas follow the 16 rows
   if constexpr (KK == KM32) {   // the 2-bit group's bytes of this lane (aligned dword holding them)
@@ -279,8 +292,24 @@ __device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rs
     t.kn[1] = uint2{w[0], w[1]};
   }
   // lane-major V plane: the lane's run holds its bytes of tokens a, a+4, a+8,
-  // a+12 back to back (raw words; compute() picks each token's bytes)
-  if constexpr (C::VLANE == 4) {
+  // a+12 back to back (raw words; compute() picks each token's bytes); two
+  // groups: the lane's run of each group's sub-plane (4 b_g bytes)
+  if constexpr (C::MIXED_V) {
+    auto run = [&](uint32_t* dst, int words, uint32_t off) {
+      if (words == 4) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vr, off, vb, kTileAux);
+        dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2]; dst[3] = x[3];
+      } else if (words == 3) {
+        const u32x3_t x = __builtin_amdgcn_raw_buffer_load_b96(vr, off, vb, kTileAux);
+        dst[0] = x[0]; dst[1] = x[1]; dst[2] = x[2];
+      } else {
+        const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vr, off, vb, kTileAux);
+        dst[0] = x[0]; dst[1] = x[1];
+      }
+    };
+    run(t.v, C::VB0, v_off);
+    run(t.v + C::VB0, C::VB1, v_off1);
+  } else if constexpr (C::VLANE == 4) {
     const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, vb, kTileAux);
     t.v[0] = x[0]; t.v[1] = x[1]; t.v[2] = x[2]; t.v[3] = x[3];
   } else if constexpr (C::VLANE == 2) {
@@ -291,7 +320,11 @@ __device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rs
   }
   {
     const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(vr, n_off, vb + VN, kTileAux);
-    t.vn = uint2{w[0], w[1]};
+    t.vn[0] = uint2{w[0], w[1]};
+  }
+  if constexpr (C::MIXED_V) {
+    const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(vr, n_off, vb + VN + 32u, kTileAux);
+    t.vn[1] = uint2{w[0], w[1]};
   }
 }
 
@@ -455,6 +488,7 @@ struct Smem {
   float xbuf[C::X_FLOATS];
   float s_ml[kWaves * 16];   // per wave: running max and sum of each column
   uint32_t s_par[64];
+  uint32_t s_vch[32];        // V's listed channel order, 4 per word (two-group V)
   int s_qexp[8 * kWaves];    // [virtual head][column]
   int s_next[kWaves];        // per virtual head: next free piece block
   int s_bt[kBtCap];          // block-table entries of the piece's first kBtCap blocks
@@ -472,6 +506,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   float* const xbuf = sm.xbuf;
   float* const s_ml = sm.s_ml;
   uint32_t* const s_par = sm.s_par;
+  uint32_t* const s_vch = sm.s_vch;
   int* const s_qexp = sm.s_qexp;
   int* const s_next = sm.s_next;
   int* const s_bt = sm.s_bt;
@@ -494,11 +529,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     {
       const __attribute__((address_space(4))) uint32_t* ka =
           (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
-      static_assert(sizeof(DecodeParams) > 7 * 64 && sizeof(DecodeParams) <= 8 * 64,
+      static_assert(sizeof(DecodeParams) > 9 * 64 && sizeof(DecodeParams) <= 10 * 64,
                     "the argument block spans another number of lines than are touched");
       const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96],
-                     k7 = ka[112];
-      asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6), "s"(k7));
+                     k7 = ka[112], k8 = ka[128], k9 = ka[144];
+      asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6), "s"(k7), "s"(k8), "s"(k9));
     }
     // context length of sequence `lane` (lanes past the last sequence read 0
     // through the descriptor's range check)
@@ -546,6 +581,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
                 32 + i, x);
     }
     s_par[lane] = x;
+    if constexpr (C::MIXED_V) {
+      uint32_t y = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        y = put((uint32_t)p.v_ch[4 * i] | ((uint32_t)p.v_ch[4 * i + 1] << 8) | ((uint32_t)p.v_ch[4 * i + 2] << 16) |
+                    ((uint32_t)p.v_ch[4 * i + 3] << 24),
+                i, y);
+      if (lane < 32) s_vch[lane] = y;
+    }
   }
   __syncthreads();   // plan, lengths and s_par written
   TQ_MARK(1);
@@ -620,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       const uint32_t x1 = kind == 4 ? v4 : (kind == 2 ? od : 0u);
       dst[1024 * it] = uint4{x0, x1, x0, x1};
     }
-    if constexpr (C::MIXED) {
+    if constexpr (C::PAIR3) {
       for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
         const int e = c >> 2;
         const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
@@ -652,7 +696,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
                                     : (uint32_t)(tokK * C::KROW + KLANE * a);
   const uint32_t klo_off = (uint32_t)((tokK * C::KROW + G3_AT + (3 * D / 64) * a) & ~3);
   const uint32_t n_off = (uint32_t)(8 * a);   // this lane's 4 norms, after the tile's norm offset
-  const uint32_t v_off = (uint32_t)(lane * 4 * C::VLANE);   // this lane's run of the V plane
+  // this lane's run of the V plane (two groups: its run of each sub-plane,
+  // group 1's sub-plane after group 0's 16 (D / 2) VB0 / 8 bytes)
+  const int vrun = C::OCT * (lane >> 4) + (lane & 15) % C::OCT;
+  const uint32_t v_off = C::MIXED_V ? (uint32_t)(vrun * 4 * C::VB0) : (uint32_t)(lane * 4 * C::VLANE);
+  const uint32_t v_off1 = (uint32_t)(16 * ((D / 2) * C::VB0 / 8) + vrun * 4 * C::VB1);
   const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
   const int64_t v_blk_stride = (int64_t)p.Hkv * p.v_tile;
   const int cap = p.max_blocks * 16;
@@ -785,9 +833,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       Tile<D, KK, VK> A, B, C3;
       bool ok_c, ok_1;
       entry(v0, idx_c, ok_c);
-      load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+      load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1);
       entry(v1, idx_1, ok_1);
-      load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+      load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1);
 #pragma unroll
       for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
 
@@ -1045,16 +1093,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         const float m_new = max_nn(m_run, bm);
         // a V norm of this lane's tokens too large for the current e_run?
         // (masked tokens' norm bytes may hold anything: left out)
-        u16x2_t mxv = __builtin_elementwise_max(as_u16x2(cur.vn.x), as_u16x2(cur.vn.y));
+        u16x2_t mxv = __builtin_elementwise_max(as_u16x2(cur.vn[0].x), as_u16x2(cur.vn[0].y));
+        if constexpr (C::MIXED_V)
+          mxv = __builtin_elementwise_max(mxv, __builtin_elementwise_max(as_u16x2(cur.vn[1].x), as_u16x2(cur.vn[1].y)));
         if (part) {
-          uint32_t vx = cur.vn.x, vy = cur.vn.y;
+          mxv = u16x2_t{0, 0};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!live(e)) {
-              if (e >> 1) vy &= ~(0xFFFFu << (16 * (e & 1)));
-              else vx &= ~(0xFFFFu << (16 * (e & 1)));
-            }
-          mxv = __builtin_elementwise_max(as_u16x2(vx), as_u16x2(vy));
+          for (int g = 0; g < C::NVG; ++g) {
+            uint32_t vx = cur.vn[g].x, vy = cur.vn[g].y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!live(e)) {
+                if (e >> 1) vy &= ~(0xFFFFu << (16 * (e & 1)));
+                else vx &= ~(0xFFFFu << (16 * (e & 1)));
+              }
+            mxv = __builtin_elementwise_max(mxv, __builtin_elementwise_max(as_u16x2(vx), as_u16x2(vy)));
+          }
         }
         const bool over = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(mxv, u16x2_t{(uint16_t)v_hi, (uint16_t)v_hi})) != 0u;
         if (__builtin_amdgcn_ballot_w64((m_new > m_run) | over)) {
@@ -1084,9 +1138,69 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
         // P.V on the matrix cores: A = V (dims x tokens) per MFMA i, through
-        // `into(i, A)`
+        // `into(i, A)` (i compile-time)
         auto pv = [&](auto&& into) {
-          if constexpr (VK == V4) {
+          if constexpr (C::MIXED_V) {
+            // two groups: MFMAs 0 .. PPL-1 take group 0, PPL .. 2 PPL-1 group
+            // 1; MFMA (g, i) row r is position 8 (r % OCT) + (r / OCT) PPL + i
+            // of group g, so this lane's codes of token e sit at index
+            // (lane & 15) / OCT * PPL + i of the token's octet in its run
+            const int sub = (fresh_lane() & 15) / C::OCT;
+            auto group = [&](auto bk, const uint32_t* w, auto base) {
+              constexpr int b = decltype(bk)::value;
+              constexpr int I0 = decltype(base)::value;
+              if constexpr (b == 4) {
+                // octet of token e = word e (8 nibbles); nibbles sub PPL + i,
+                // paired across tokens as in the one-group 4-bit path
+                const uint32_t sh = (uint32_t)(4 * C::PPL * sub);
+                const uint32_t w0 = w[0] >> sh, w1 = w[1] >> sh, w2 = w[2] >> sh, w3 = w[3] >> sh;
+                const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
+                const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+                const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | ((w3 << 4) & 0xF0F0F0F0u);
+                const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
+#pragma unroll
+                for (int i = 0; i < C::PPL; ++i) {
+                  const u32x2_t av = {lds_u32(lds, lut_addr((i & 1) ? O01 : E01, off_v4, i >> 1)),
+                                      lds_u32(lds, lut_addr((i & 1) ? O23 : E23, off_v4, i >> 1))};
+                  into(I0 + i, __builtin_bit_cast(half4_t, av));
+                }
+              } else if constexpr (b == 3) {
+                // octet of token e = bits 24 e .. 24 e + 23 of the 3 words;
+                // keys of the pair table: code(t0) | code(t1) << 3
+                const uint32_t sh = (uint32_t)(3 * C::PPL * sub);
+                const uint32_t x0 = w[0] >> sh;
+                const uint32_t x1 = __builtin_amdgcn_alignbit(w[1], w[0], 24) >> sh;
+                const uint32_t x2 = __builtin_amdgcn_alignbit(w[2], w[1], 16) >> sh;
+                const uint32_t x3 = (w[2] >> 8) >> sh;
+#pragma unroll
+                for (int i = 0; i < C::PPL; ++i) {
+                  const uint32_t k01 = ((x0 >> (3 * i)) & 7u) | (((x1 >> (3 * i)) & 7u) << 3);
+                  const uint32_t k23 = ((x2 >> (3 * i)) & 7u) | (((x3 >> (3 * i)) & 7u) << 3);
+                  const u32x2_t av = {lds_u32(lds, (k01 << 6) | off3), lds_u32(lds, (k23 << 6) | off3)};
+                  into(I0 + i, __builtin_bit_cast(half4_t, av));
+                }
+              } else {
+                // octet of token e = half-word e of the 2 words (8 crumbs);
+                // crumbs sub PPL + i of the 4 tokens transposed so that byte i
+                // holds position i of tokens 0-3: the crumb table returns the
+                // operand's 4 values in token order
+                const uint32_t sh = (uint32_t)(2 * C::PPL * sub);
+                const uint32_t y = ((w[0] >> sh) & 0xFFu) | (((w[0] >> 16 >> sh) & 0xFFu) << 8) |
+                                   (((w[1] >> sh) & 0xFFu) << 16) | (((w[1] >> 16 >> sh) & 0xFFu) << 24);
+                uint32_t t = (y ^ (y >> 6)) & 0x00CC00CCu;
+                uint32_t x = y ^ t ^ (t << 6);
+                t = (x ^ (x >> 12)) & 0x0000F0F0u;
+                x = x ^ t ^ (t << 12);
+#pragma unroll
+                for (int i = 0; i < C::PPL; ++i) {
+                  const uint2 l4 = lds_u64(lds, lut_addr(x, off_v2, i));
+                  into(I0 + i, __builtin_bit_cast(half4_t, u32x2_t{l4.x, l4.y}));
+                }
+              }
+            };
+            group(std::integral_constant<int, C::VB0>{}, cur.v, std::integral_constant<int, 0>{});
+            group(std::integral_constant<int, C::VB1>{}, cur.v + C::VB0, std::integral_constant<int, C::PPL>{});
+          } else if constexpr (VK == V4) {
             // Lookup keys pair the nibbles of two tokens for one dim, so the
             // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
             // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
@@ -1131,17 +1245,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
         };
         // B operand: p * n_V in fp16 (p carrying 2^e_run), each rounded once
-        u32x2_t pw = {mul_h2(pr[0], pr[1], cur.vn.x), mul_h2(pr[2], pr[3], cur.vn.y)};
-        if (part) {
-          // a masked token's weight is 0, but its norm bytes may hold any
-          // bits (a NaN times 0 is NaN): its operand is set to +0
+        // (two V groups: one operand per group's norms)
+        half4_t pb[C::NVG];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (!live(e)) pw[e >> 1] &= ~(0xFFFFu << (16 * (e & 1)));
+        for (int g = 0; g < C::NVG; ++g) {
+          u32x2_t pw = {mul_h2(pr[0], pr[1], cur.vn[g].x), mul_h2(pr[2], pr[3], cur.vn[g].y)};
+          if (part) {
+            // a masked token's weight is 0, but its norm bytes may hold any
+            // bits (a NaN times 0 is NaN): its operand is set to +0
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!live(e)) pw[e >> 1] &= ~(0xFFFFu << (16 * (e & 1)));
+          }
+          pb[g] = __builtin_bit_cast(half4_t, pw);
         }
-        const half4_t pb = __builtin_bit_cast(half4_t, pw);
         __builtin_amdgcn_sched_barrier(0);
-        pv([&](int i, half4_t av) { o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, o_acc[i], 0, 0, 0); });
+        pv([&](int i, half4_t av) {
+          o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb[C::MIXED_V && i >= C::PPL ? 1 : 0], o_acc[i], 0, 0, 0);
+        });
       };
 
       // one block (j): issue tile j+2, look up the entry of j+3 and take the
@@ -1150,7 +1271,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if (idx_c >= n) return false;
         bool ok2;
         entry(ph2v, idx_2, ok2);
-        load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off);
+        load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1);
         const int idx_3 = __builtin_amdgcn_readfirstlane(g3);
         const int ph3v = bt_at(idx_3);
         g3 = grab();
@@ -1175,13 +1296,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       l_run += lane_xor<16>(l_run, le);
       l_run += lane_xor<32>(l_run, le);
       if (!lo_part) {
-        float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
+        if constexpr (C::MIXED_V) {
+          // accumulator (i, e) is position 8 (rho % OCT) + (rho / OCT) PPL +
+          // i % PPL of V group i / PPL, rho = 4 a + e: stored at its channel
+          float* srow = slots + (8 * wave + gq) * C::DS;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < 4; ++e) {
+            const int rho = 4 * a + e;
 #pragma unroll
-          for (int h = 0; h < C::R / 4; ++h)
-            *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
-                float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
+            for (int i = 0; i < C::R; ++i) {
+              const int pos = (i / C::PPL) * (D / 2) + 8 * (rho % C::OCT) + (rho / C::OCT) * C::PPL + i % C::PPL;
+              const int ch = (int)((s_vch[pos >> 2] >> (8 * (pos & 3))) & 0xFFu);
+              srow[ch] = o_acc[i][e];
+            }
+          }
+        } else {
+          float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int h = 0; h < C::R / 4; ++h)
+              *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
+                  float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
+        }
         if (a == 0) {   // the exp2-domain offset of the weights (-inf: no token), and their sum
           s_ml[16 * wave + gq] = m_run == -INFINITY ? -INFINITY : -nm;
           s_ml[16 * wave + 8 + gq] = l_run;
@@ -1448,6 +1585,8 @@ int format_kind_k(const tq_format* f) {
 int format_kind_v(const tq_format* f) {
   if (f->num_groups == 1 && f->group_bits[0] == 4) return V4;
   if (f->num_groups == 1 && f->group_bits[0] == 2) return V2;
+  if (f->num_groups == 2 && f->group_bits[0] == 4 && f->group_bits[1] == 3) return VM43;
+  if (f->num_groups == 2 && f->group_bits[0] == 3 && f->group_bits[1] == 2) return VM32;
   return -1;
 }
 
@@ -1517,7 +1656,11 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   if (kfmt->qjl && Gr > 8)
     return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take at most 8 q heads per kv head");
   if (kk < 0 && !kfmt->qjl) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
-  if (vk < 0) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this V format (served: 4-bit, 2-bit)");
+  if (vk < 0)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT,
+                     "no decode kernel for this V format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
+  if (kfmt->qjl && (vk == VM43 || vk == VM32))
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take one-group V formats");
   const int D = kfmt->head_dim;
   if (num_seqs == 0) return TQ_OK;
   if (!q || !k_pages || !v_pages || !block_tables || !context_lens || !out)
@@ -1636,24 +1779,37 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
     p.k_ch[jx] = kfmt->group_channels[jx];
   }
   // LUT halves: K's 4-bit or 2-bit table in half 0 (the 2-bit group's for
-  // 3+2 bits); V shares it when bits and codebook agree
+  // 3+2 bits); V's 4-bit or 2-bit group shares it when bits and codebook
+  // agree, else takes half 1.  The 3-bit groups (K's and V's) share the pair
+  // table, so their levels must agree.
   const int kgh = kk == KM32 ? 1 : 0;   // K group whose levels fill half 0
   const int kbits0 = kfmt->group_bits[kgh];
   p.half_kind[0] = kbits0;
   for (int i = 0; i < 16; ++i) p.half_cb[0][i] = kfmt->codebook[kgh][i];
-  const int vbits = vfmt->group_bits[0];
+  const int vgh = vk == VM32 ? 1 : 0;   // V group read through a LUT half
+  const int vbits = vfmt->group_bits[vgh];
   bool share = vbits == kbits0;
-  for (int i = 0; i < (1 << vbits) && share; ++i) share = vfmt->codebook[0][i] == kfmt->codebook[kgh][i];
+  for (int i = 0; i < (1 << vbits) && share; ++i) share = vfmt->codebook[vgh][i] == kfmt->codebook[kgh][i];
   if (share) {
     p.v_half = 0;
     p.half_kind[1] = 0;
   } else {
     p.v_half = 1;
     p.half_kind[1] = vbits;
-    for (int i = 0; i < 16; ++i) p.half_cb[1][i] = vfmt->codebook[0][i];
+    for (int i = 0; i < 16; ++i) p.half_cb[1][i] = vfmt->codebook[vgh][i];
   }
-  if (kk == KM43 || kk == KM32)   // the 3-bit group's levels: group 1 (4+3) or group 0 (3+2)
+  const bool kmix = kk == KM43 || kk == KM32, vmix = vk == VM43 || vk == VM32;
+  if (kmix)   // the 3-bit group's levels: group 1 (4+3) or group 0 (3+2)
     for (int i = 0; i < 8; ++i) p.k3_cb[i] = kfmt->codebook[kk == KM43 ? 1 : 0][i];
+  if (vmix) {
+    const uint16_t* v3 = vfmt->codebook[vk == VM43 ? 1 : 0];
+    for (int i = 0; i < 8; ++i) {
+      if (kmix && p.k3_cb[i] != v3[i])
+        return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K and V 3-bit groups with different codebooks");
+      p.k3_cb[i] = v3[i];
+    }
+    for (int jx = 0; jx < D; ++jx) p.v_ch[jx] = vfmt->group_channels[jx];
+  }
   p.q_f32 = q_dtype == TQ_F32;
   p.out_f32 = out_dtype == TQ_F32;
   p.q_bytes = (int32_t)q_bytes;
@@ -1666,10 +1822,10 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   }
 #define TQ_LAUNCH(DD, KKK, VVV) \
   if (D == DD && kk == KKK && vk == VVV) launch_decode<DD, KKK, VVV>(p, hs);
-  TQ_LAUNCH(128, K4, V4) TQ_LAUNCH(128, K4, V2) TQ_LAUNCH(128, K2, V4) TQ_LAUNCH(128, K2, V2)
-  TQ_LAUNCH(128, KM43, V4) TQ_LAUNCH(128, KM43, V2) TQ_LAUNCH(128, KM32, V4) TQ_LAUNCH(128, KM32, V2)
-  TQ_LAUNCH(64, K4, V4) TQ_LAUNCH(64, K4, V2) TQ_LAUNCH(64, K2, V4) TQ_LAUNCH(64, K2, V2)
-  TQ_LAUNCH(64, KM43, V4) TQ_LAUNCH(64, KM43, V2) TQ_LAUNCH(64, KM32, V4) TQ_LAUNCH(64, KM32, V2)
+#define TQ_LAUNCH_V(DD, KKK) TQ_LAUNCH(DD, KKK, V4) TQ_LAUNCH(DD, KKK, V2) TQ_LAUNCH(DD, KKK, VM43) TQ_LAUNCH(DD, KKK, VM32)
+  TQ_LAUNCH_V(128, K4) TQ_LAUNCH_V(128, K2) TQ_LAUNCH_V(128, KM43) TQ_LAUNCH_V(128, KM32)
+  TQ_LAUNCH_V(64, K4) TQ_LAUNCH_V(64, K2) TQ_LAUNCH_V(64, KM43) TQ_LAUNCH_V(64, KM32)
+#undef TQ_LAUNCH_V
 #undef TQ_LAUNCH
   st = launch_status("tq_decode_paged launch");
   if (st != TQ_OK || num_splits == 1) return st;

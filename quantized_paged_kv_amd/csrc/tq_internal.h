@@ -41,6 +41,7 @@ struct DevFormat {
   int32_t qjl;             // QJL stage: sign bits after the MSE bytes, residual norms after the norms
   int32_t sign_off;        // byte offset of the sign bits in a row (= MSE bytes)
   int32_t rnorm_off;       // byte offset of the residual-norm plane in a tile
+  int32_t octet;           // V pages of two-group formats: index plane in octet runs per group
 };
 
 void make_dev_format(const tq_format* f, DevFormat* out);

@@ -368,6 +368,27 @@ __global__ __launch_bounds__(kThreads, 4) void write_kv_kernel(WriteParams p) {
   }
   __syncthreads();
   if (!valid) {
+  } else if (f.octet) {
+    // two-group V pages: octet o of group g (b bytes: 8 indices) goes to
+    // run (m / 8) (offs % 4) + o of the group's sub-plane, place offs / 4;
+    // lane L takes octet L % (m / 8) of group L / (m / 8)
+    constexpr int OCT = D / 16;   // octets per group (m / 8, m = D / 2)
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(lds_row[lr]);
+    for (int u = L; u < 2 * OCT; u += LPR) {
+      const int g = u / OCT, o = u % OCT;
+      const int b = f.bits[g];
+      const int gbo = f.grp_byte_off[g];
+      uint8_t* cd = tile + 16 * gbo + (OCT * (offs & 3) + o) * 4 * b + (offs >> 2) * b;
+      const uint8_t* cs = src + gbo + o * b;
+      if (b == 4) {
+        *reinterpret_cast<uint32_t*>(cd) = (uint32_t)cs[0] | ((uint32_t)cs[1] << 8) | ((uint32_t)cs[2] << 16) |
+                                           ((uint32_t)cs[3] << 24);
+      } else if (b == 2) {
+        *reinterpret_cast<uint16_t*>(cd) = (uint16_t)(cs[0] | (cs[1] << 8));
+      } else {
+        for (int k = 0; k < b; ++k) cd[k] = cs[k];
+      }
+    }
   } else if (f.chunk == 0) {   // row-major index plane
     uint32_t* dst = reinterpret_cast<uint32_t*>(tile + offs * f.row_bytes);
     for (int w = L; w < f.row_bytes / 4; w += LPR) dst[w] = lds_row[lr][w];
@@ -446,8 +467,10 @@ extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype
     p.src[n_tensors] = src[t];
     p.pages[n_tensors] = pages[t];
     make_dev_format(fmts[t], &p.fmt[n_tensors]);
-    // V pages: lane-major index plane when the row bytes split into 16 runs
-    if (t == 1 && p.fmt[n_tensors].row_bytes % 16 == 0) p.fmt[n_tensors].chunk = p.fmt[n_tensors].row_bytes / 16;
+    // V pages: octet runs per group for two-group formats, else a lane-major
+    // index plane when the row bytes split into 16 runs
+    if (t == 1 && p.fmt[n_tensors].ng == 2) p.fmt[n_tensors].octet = 1;
+    else if (t == 1 && p.fmt[n_tensors].row_bytes % 16 == 0) p.fmt[n_tensors].chunk = p.fmt[n_tensors].row_bytes / 16;
     ++n_tensors;
   }
   if (num_tokens == 0) return TQ_OK;

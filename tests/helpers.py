@@ -48,11 +48,10 @@ def oracle_pages(x: np.ndarray, slots: np.ndarray, num_blocks: int, fmt: oenc.Fo
 def written_mask(slots: np.ndarray, num_blocks: int, H: int, fmt: oenc.Format, role: str) -> np.ndarray:
     """Boolean mask of the bytes a write of `slots` owns (rows + norm slots)."""
     rb, noff, tile = opg.tile_layout(fmt, 16)
-    chunk = opg.lane_chunk(fmt, role)
     mask = np.zeros((num_blocks, H, tile), dtype=bool)
     for s in slots:
         b, o = divmod(int(s), 16)
-        mask[b, :, opg.row_positions(rb, [o], chunk)[0]] = True
+        mask[b, :, opg.index_positions(fmt, role, [o])[0]] = True
         sl = 4 * (o % 4) + o // 4
         for g in range(fmt.num_groups * (2 if fmt.qjl else 1)):   # vector (and residual) norms
             pos = noff + 2 * (16 * g + sl)

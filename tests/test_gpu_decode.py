@@ -109,6 +109,14 @@ SMALL = [
     (128, [3, 2], [4], 8, 2, [33, 300], 1, "f32", "f32", "normal"),
     (64, [3, 2], [2], 6, 3, [5, 400, 129], 3, "bf16", "f32", "t5u"),
     (64, [3, 2], [4], 1, 1, [256], 1, "f32", "f32", "normal"),
+    # two-group (recipe) V formats, with every K kind
+    (128, [4], [4, 3], 8, 2, [1, 17, 300, 1000], 3, "bf16", "f32", "normal"),
+    (128, [4, 3], [4, 3], 16, 2, [700, 64], 5, "bf16", "bf16", "t3"),
+    (128, [3, 2], [3, 2], 16, 2, [700, 64, 0], 4, "bf16", "f32", "t3"),
+    (128, [2], [3, 2], 4, 4, [95, 257], 1, "f32", "f32", "normal"),
+    (128, [4, 3], [3, 2], 8, 2, [33, 300], 2, "bf16", "f32", "t5u"),
+    (64, [4], [3, 2], 6, 3, [5, 400, 129], 3, "bf16", "f32", "normal"),
+    (64, [3, 2], [4, 3], 2, 2, [129, 1000], 2, "f32", "f32", "t3"),
     # many splits: the merge spreads each row's partials over 2 and 4 waves,
     # and past 64 slots
     (128, [4], [4], 8, 2, [1, 17, 300, 5000], 24, "bf16", "f32", "normal"),
@@ -299,6 +307,8 @@ TINY = [
     (128, [4, 3], [2], 16, 2, [500, 17], 4, "bf16"),
     (128, [3, 2], [4], 8, 2, [129], 1, "f32"),
     (64, [2], [2], 4, 1, [1000], 2, "f32"),
+    (128, [4, 3], [4, 3], 8, 2, [300, 40], 2, "bf16"),
+    (128, [4], [3, 2], 8, 2, [129, 500], 1, "f32"),
 ]
 
 
@@ -348,7 +358,8 @@ def test_tiny_and_normal_rows_in_one_call():
     check(w_t, q, o, l, [(s, h) for s in range(2) for h in range(hq)], "f32", ref=ref)
 
 
-@pytest.mark.parametrize("kb,vb", [([4], [4]), ([4], [2]), ([4, 3], [2]), ([3, 2], [4])])
+@pytest.mark.parametrize("kb,vb", [([4], [4]), ([4], [2]), ([4, 3], [2]), ([3, 2], [4]), ([4, 3], [4, 3]),
+                                   ([3, 2], [3, 2])])
 def test_unwritten_rows_holding_nan_bytes(kb, vb):
     """Pools whose unwritten bytes are all 0xFF (NaN as fp16): the rows past
     each context length in a sequence's last block, and a block-table entry

@@ -65,6 +65,8 @@ def test_tiny_fp32_d64():
     ([3, 2], [4, 2], 128, "normal", "bf16"),
     ([4, 2], [2, 4], 64, "t3", "f32"),
     ([2], [4], 64, "normal", "bf16"),
+    ([4], [4, 3], 128, "normal", "bf16"),
+    ([3, 2], [3, 2], 64, "t3", "f32"),
 ])
 def test_formats_random_slots(kbits, vbits, d, dist, dtype):
     seed = 7 + d + sum(kbits) * 3 + sum(vbits)

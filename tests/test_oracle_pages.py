@@ -148,6 +148,43 @@ def test_v_lane_major_is_a_permutation_with_runs(rb):
             assert run.tolist() == list(range((16 * q + j) * 4 * c, (16 * q + j + 1) * 4 * c))
 
 
+def test_v_two_group_octet_runs_closed_form():
+    """Two-group V pages: group g's bytes in a sub-plane at 16 x its byte
+    offset in a row; octet o (b_g bytes, 8 indices) of row t in run
+    (m/8)(t%4) + o of 4 b_g bytes, at place t//4.  Hand-computed spots for
+    the 4+3-bit d=128 format (m = 64: group 0 bytes 0-31, group 1 bytes
+    32-55)."""
+    _, _, km, _ = fmts()
+    pos = pg.index_positions(km, "v", [0, 5, 15])
+    assert pos[0, 0] == 0 and pos[0, 3] == 3 and pos[0, 4] == 16      # row 0: octet 0 in run 0, octet 1 in run 1
+    assert pos[1, 9] == (8 * 1 + 2) * 16 + 1 * 4 + 1 == 165            # row 5, group 0 octet 2 byte 1
+    assert pos[0, 32] == 16 * 32                                       # group 1 sub-plane starts at 512
+    assert pos[1, 32 + 7] == 512 + (8 * 1 + 2) * 12 + 1 * 3 + 1        # row 5, group 1 octet 2 byte 1
+    assert pos[2, 55] == 895 == 16 * 56 - 1                            # last byte of the plane
+    # K pages of the same format keep whole rows
+    assert pg.index_positions(km, "k", [5])[0].tolist() == list(range(5 * 56, 6 * 56))
+
+
+@pytest.mark.parametrize("bits,d", [([4, 3], 128), ([3, 2], 128), ([4, 3], 64), ([3, 2], 64), ([4, 2], 128)])
+def test_v_two_group_octet_runs_permutation(bits, d):
+    """Every byte of the index plane is used once, and each run holds one
+    octet of rows q, q+4, q+8, q+12 in that order."""
+    f = enc.Format.make(d, bits, np.ones(d, dtype=np.int8), np.arange(d))
+    m = d // 2
+    pos = pg.index_positions(f, "v", np.arange(16))
+    rb = enc.row_bytes(f)
+    assert sorted(pos.ravel().tolist()) == list(range(16 * rb))
+    base = 0
+    for b in bits:
+        for q in range(4):
+            for o in range(m // 8):
+                cols = [base + o * b + k for k in range(b)]
+                run = pos[[q, q + 4, q + 8, q + 12]][:, cols].ravel()
+                start = 16 * base + ((m // 8) * q + o) * 4 * b
+                assert run.tolist() == list(range(start, start + 4 * b))
+        base += m * b // 8
+
+
 def test_v_pages_roundtrip_and_other_formats_stay_row_major():
     """Rows written with role v read back with role v; a V format whose row
     bytes are not a multiple of 16 keeps the row-major plane."""
@@ -166,7 +203,7 @@ def test_v_pages_roundtrip_and_other_formats_stay_row_major():
             for g in range(f.num_groups):
                 np.testing.assert_array_equal(ridx[g], idx[g][:, h])
             np.testing.assert_array_equal(rn, norms[:, h])
-    assert pg.lane_chunk(km, "v") == 0   # 56-byte rows
+    assert pg.lane_chunk(km, "v") == 0   # 56-byte rows: two groups, octet runs
     # the row-major reader sees a lane-major plane as different bytes
     _, _, tile = pg.tile_layout(v, bs)
     pages = np.zeros((nb, H, tile), dtype=np.uint8)

@@ -37,6 +37,7 @@ STREAM_CHANNELS = 3
 STREAM_BLOCKS = 4
 STREAM_OUTLIERS = 5
 STREAM_QJL = 6
+STREAM_V_CHANNELS = 7
 STREAM_K = 11
 STREAM_V = 12
 STREAM_Q = 13
@@ -176,9 +177,14 @@ def _formats(seed: int, head_dim: int, kbits: List[int], vbits: List[int], qjl: 
         hi = channel_subset(seed, STREAM_CHANNELS, head_dim, head_dim // 2)
         lo = np.array(sorted(set(range(head_dim)) - set(hi.tolist())), dtype=np.int64)
         kch = np.concatenate([hi, lo])
+    vch = None
+    if len(vbits) == 2:   # V's own channel groups, drawn independently of K's
+        hi = channel_subset(seed, STREAM_V_CHANNELS, head_dim, head_dim // 2)
+        lo = np.array(sorted(set(range(head_dim)) - set(hi.tolist())), dtype=np.int64)
+        vch = np.concatenate([hi, lo])
     proj = qjl_projection(seed, len(kbits), head_dim // len(kbits)) if qjl else None
     kf = FormatSpec(head_dim, list(kbits), kch, s.copy(), proj)
-    vf = FormatSpec(head_dim, list(vbits), None, s.copy())
+    vf = FormatSpec(head_dim, list(vbits), vch, s.copy())
     return kf, vf
 
 
