@@ -777,8 +777,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // half of qw unused); one load shape for both dtypes, bytes past the q
       // tensor read as zero through the descriptor's range check
       uint32_t qw[PER];
-      {   // issued by every wave (parts > 0 discard them) so that all paths
-          // carry the same loads and later waits count exactly
+      {   // issued by every wave so that all paths carry the same loads and
+          // later waits count exactly; parts > 0 discard them and read
+          // through an empty range (no memory access): on a long context
+          // hundreds of workgroups read the same few q rows at once
         const int esz = p.q_f32 ? 4 : 2;
         const int head0 = uni((int)(((int64_t)s * p.rows_ps + kvh * p.Gr) * D * esz));   // query 0, first q head
         int qrow = 0;   // this lane's (query, q head) column: rows past head0
@@ -787,7 +789,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           qrow = qi * p.Hq + (colq - qi * p.Gr);
         }
         const uint32_t lane_off = (uint32_t)((qrow * D + l8 * PER) * esz);
-        const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), p.q_bytes);
+        const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), part == 0 ? p.q_bytes : 0);
 #pragma unroll
         for (int i = 0; i < PER / 4; ++i) {
           const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
@@ -928,11 +930,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
         // (the fence orders this wave's exponent and row writes before its reads)
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        const float q_pow = ldexpf(1.0f, s_qexp[8 * vh + gq]);
-        const float* qrow = stage + gq * D;
-        float vq[NQK][8];
+        // (lane roles recomputed from the fresh lane index: values kept
+        // across the block loop may sit in scratch, whose reloads here would
+        // wait for the tile loads in flight)
+        const int la = ln >> 4, lq = ln & 7;
+        const bool lo_q = (ln & 8) != 0;
+        const float q_pow = ldexpf(1.0f, s_qexp[8 * vh + lq]);
+        const float* qrow = stage + lq * D;
+        // operand t of this lane: the 8 values it multiplies, scaled by
+        // 2^(15-ex) and split into the fp16 high part (lanes j < 8) or the
+        // fp16 rounding of the remainder (lanes j >= 8); all operands are
+        // built in registers before any is written over the rows
+        half8_t qvr[NQK];
 #pragma unroll
         for (int t = 0; t < NQK; ++t) {
+          float vq[8];
           if constexpr (C::MIXED) {
             // operand element (t, e) of lane (a, j): channel k_ch[pos] of the
             // column, pos = (t / per_g) m + a (m / 4) + 8 (t % per_g) + e
@@ -941,33 +953,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             const int grp_k = t / per_g, u = t % per_g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int pos_l = grp_k * m + a * (m / 4) + 8 * u + e;
+              const int pos_l = grp_k * m + la * (m / 4) + 8 * u + e;
               const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
-              vq[t][e] = qrow[chn];
+              vq[e] = qrow[chn];
             }
           } else {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              const float4 f = *reinterpret_cast<const float4*>(qrow + a * (D / 4) + 8 * t + 4 * h);
-              vq[t][4 * h] = f.x; vq[t][4 * h + 1] = f.y; vq[t][4 * h + 2] = f.z; vq[t][4 * h + 3] = f.w;
+              const float4 f = *reinterpret_cast<const float4*>(qrow + la * (D / 4) + 8 * t + 4 * h);
+              vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
             }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = vq[e] * q_pow;
+            const _Float16 hi = (_Float16)v;
+            const _Float16 lo = (_Float16)(v - (float)hi);
+            qvr[t][e] = lo_q ? lo : hi;
           }
         }
         // every row read above is done before the operand writes below reuse
         // the bytes
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-          half8_t qv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = vq[t][e] * q_pow;
-            const _Float16 hi = (_Float16)v;
-            const _Float16 lo = (_Float16)(v - (float)hi);
-            qv[e] = lo_part ? lo : hi;
-          }
-          qv_all[(vh * NQK + t) * 64 + ln] = qv;
-        }
+        for (int t = 0; t < NQK; ++t) qv_all[(vh * NQK + t) * 64 + ln] = qvr[t];
       }
       __syncthreads();  // operands, counters and block-table entries ready
       TQ_MARK(3 + 4 * n_done);
