@@ -70,6 +70,9 @@ constexpr uint32_t kDoneBits = 0x7FC0D0E5u;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum KKind { K4 = 0, K2 = 1, KM43 = 2, KM32 = 3 };
+// K kinds with the QJL stage: the MSE kind plus this flag (sign bits after
+// each row's MSE bytes, residual norms after the vector norms)
+constexpr int KQ = 4;
 enum VKind { V4 = 0, V2 = 1, VM43 = 2, VM32 = 3 };
 
 struct DecodeParams {
@@ -107,6 +110,7 @@ struct DecodeParams {
   int32_t k_tile, v_tile, k_norm_off, v_norm_off;
   uint32_t k_span, v_span;   // bytes of each pool (< 4 GiB)
   float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K)), > 0
+  const float* proj; // QJL: the projections S_g, fp32 [groups][m][m] (K kinds with KQ)
   float v_mul;       // 1 / sqrt(m_V), applied once in the epilogue
   uint32_t v_signs[4];
   uint32_t k_signs[4];
@@ -206,13 +210,18 @@ template <int D, int KK, int VK>
 struct Cfg {
   static constexpr int R = D / 16;                       // dims per lane-row in P.V
   static constexpr int NQK = D / 32;                     // q.K MFMAs per block
-  static constexpr int KROW = KK == K4 ? D / 2
-                              : KK == K2 ? D / 4
-                              : KK == KM43 ? (D / 2) * 4 / 8 + (D / 2) * 3 / 8
+  static constexpr int KB = KK & 3;                      // MSE kind of K
+  static constexpr bool QJ = (KK & KQ) != 0;             // QJL stage on K
+  static constexpr int KMSE = KB == K4 ? D / 2
+                              : KB == K2 ? D / 4
+                              : KB == KM43 ? (D / 2) * 4 / 8 + (D / 2) * 3 / 8
                                            : (D / 2) * 3 / 8 + (D / 2) * 2 / 8;
+  static constexpr int KROW = KMSE + (QJ ? D / 8 : 0);   // K row stride: MSE bytes (+ sign bits)
+  static constexpr int NGK = (KB == KM43 || KB == KM32) ? 2 : 1;   // K groups
+  static constexpr int KRN = 16 * KROW + 32 * NGK;       // residual norms in a K tile (QJL)
   static constexpr int VROW = VK == V4 ? D / 2 : VK == V2 ? D / 4 : VK == VM43 ? (D / 2) * 7 / 8 : (D / 2) * 5 / 8;
   static constexpr int VLANE = VK == V4 ? D / 32 : D / 64;  // one-group V: bytes per lane per token
-  static constexpr bool MIXED = KK == KM43 || KK == KM32;   // two K groups
+  static constexpr bool MIXED = NGK == 2;                 // two K groups
   // Two V groups: group g's octets (8 indices, b_g bytes) in runs of 4
   // tokens; lane (a, r) reads run (OCT a + r % OCT) of each group and holds
   // positions 8 (r % OCT) + (r / OCT) PPL + i (i < PPL) of its 4 tokens
@@ -239,6 +248,8 @@ struct Tile {
   uint32_t k_lo[2];   // mixed: low-group bits (aligned 8 B window)
   uint2 kn[2];        // K norms of the lane's 4 tokens, per group
   uint32_t v[Cfg<D, KK, VK>::VW];   // packed V bits of the lane's 4 tokens (raw words of its run(s))
+  uint32_t sg;        // QJL: the dword holding the sign bytes of this lane's MFMAs (its K row)
+  uint32_t gm;        // QJL: the dword holding the residual norm of its K row's token and group
   uint2 vn[Cfg<D, KK, VK>::NVG];    // V norms of the lane's 4 tokens, per group
 };
 
@@ -264,15 +275,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
 template <int D, int KK, int VK>
 __device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                           uint32_t kb, uint32_t vb, uint32_t k_off, uint32_t klo_off,
-                                          uint32_t n_off, uint32_t v_off, uint32_t v_off1) {
+                                          uint32_t n_off, uint32_t v_off, uint32_t v_off1, uint32_t sg_off,
+                                          uint32_t gm_off) {
   using C = Cfg<D, KK, VK>;
   constexpr uint32_t KN = 16 * C::KROW, VN = 16 * C::VROW;   // norm areas follow the 16 rows
-  if constexpr (KK == KM32) {   // the 2-bit group's bytes of this lane (aligned dword holding them)
+  if constexpr (C::KB == KM32) {   // the 2-bit group's bytes of this lane (aligned dword holding them)
     t.k[0] = __builtin_amdgcn_raw_buffer_load_b32(kr, k_off, kb, kTileAux);
-  } else if constexpr (KK == K4 && D == 128) {
+  } else if constexpr (C::KB == K4 && D == 128) {
     const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(kr, k_off, kb, kTileAux);
     t.k[0] = x[0]; t.k[1] = x[1]; t.k[2] = x[2]; t.k[3] = x[3];
-  } else if constexpr ((KK == K4 && D == 64) || (KK != K4 && D == 128)) {
+  } else if constexpr ((C::KB == K4 && D == 64) || (C::KB != K4 && D == 128)) {
     const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(kr, k_off, kb, kTileAux);
     t.k[0] = x[0]; t.k[1] = x[1];
   } else {
@@ -290,6 +302,10 @@ __device__ __forceinline__ void load_tile(Tile<D, KK, VK>& t, __amdgpu_buffer_rs
   if constexpr (C::MIXED) {
     const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(kr, n_off, kb + KN + 32u, kTileAux);
     t.kn[1] = uint2{w[0], w[1]};
+  }
+  if constexpr (C::QJ) {
+    t.sg = __builtin_amdgcn_raw_buffer_load_b32(kr, sg_off, kb, kTileAux);
+    t.gm = __builtin_amdgcn_raw_buffer_load_b32(kr, gm_off, kb, kTileAux);
   }
   // lane-major V plane: the lane's run holds its bytes of tokens a, a+4, a+8,
   // a+12 back to back (raw words; compute() picks each token's bytes); two
@@ -490,6 +506,7 @@ struct Smem {
   uint32_t s_par[64];
   uint32_t s_vch[32];        // V's listed channel order, 4 per word (two-group V)
   int s_qexp[8 * kWaves];    // [virtual head][column]
+  float s_rq[64];            // QJL: [virtual head][column] weight of the sketch sum against the q.K sum
   int s_next[kWaves];        // per virtual head: next free piece block
   int s_bt[kBtCap];          // block-table entries of the piece's first kBtCap blocks
   int s_cl[64];              // clamped context lengths of sequences 0-63
@@ -508,6 +525,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   uint32_t* const s_par = sm.s_par;
   uint32_t* const s_vch = sm.s_vch;
   int* const s_qexp = sm.s_qexp;
+  float* const s_rq = sm.s_rq;
   int* const s_next = sm.s_next;
   int* const s_bt = sm.s_bt;
   int* const s_cl = sm.s_cl;
@@ -690,12 +708,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // one group (K4, K2) or of the 4-bit group (4+3), or the aligned dword that
   // holds its bytes of the 2-bit group (3+2); klo_off the aligned 8-B window
   // that holds its bytes of the 3-bit group (two-group formats)
-  constexpr int KLANE = KK == K4 ? D / 8 : D / 16;
-  constexpr int G3_AT = KK == KM32 ? 0 : D / 4;   // first byte of the 3-bit group in a row
-  const uint32_t k_off = KK == KM32 ? (uint32_t)((tokK * C::KROW + 3 * D / 16 + (D / 32) * a) & ~3)
+  constexpr int KLANE = C::KB == K4 ? D / 8 : D / 16;
+  constexpr int G3_AT = C::KB == KM32 ? 0 : D / 4;   // first byte of the 3-bit group in a row
+  const uint32_t k_off = C::KB == KM32 ? (uint32_t)((tokK * C::KROW + 3 * D / 16 + (D / 32) * a) & ~3)
                                     : (uint32_t)(tokK * C::KROW + KLANE * a);
   const uint32_t klo_off = (uint32_t)((tokK * C::KROW + G3_AT + (3 * D / 64) * a) & ~3);
   const uint32_t n_off = (uint32_t)(8 * a);   // this lane's 4 norms, after the tile's norm offset
+  // QJL: the aligned dword holding the sign bytes NQK a .. NQK a + NQK - 1 of
+  // its K row (sketch output 32 a + 8 t + e of MFMA t is bit e of byte 4 a +
+  // t; d = 64: 16 a + 8 t + e, byte 2 a + t), and the one holding the
+  // residual norm of the row's token (norm slot j) for the group of those
+  // outputs, (a NGK) / 4
+  const uint32_t sg_off = (uint32_t)(tokK * C::KROW + C::KMSE + ((NQK * a) & ~3));
+  const uint32_t gm_off = (uint32_t)(C::KRN + 2 * (16 * ((a * C::NGK) >> 2) + (j & ~1)));
   // this lane's run of the V plane (two groups: its run of each sub-plane,
   // group 1's sub-plane after group 0's 16 (D / 2) VB0 / 8 bytes)
   const int vrun = C::OCT * (lane >> 4) + (lane & 15) % C::OCT;
@@ -796,6 +821,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
         }
       }
+      // QJL: wave w computes output tile ot_w = w % (D / 16) of the projected
+      // rows (16 outputs) for virtual heads w / (D / 16), + 16 / (D / 16), ...;
+      // its S values (the same for all of them) are requested here, before
+      // the tiles, so that waiting for them does not wait for the tiles
+      constexpr int QOT = D / 16, QM = D / C::NGK, QKC = QM / 32;
+      const int ot_w = wave % QOT;
+      float4 spf[C::QJ ? 2 * QKC : 1];
+      if constexpr (C::QJ) {
+        const int lp = fresh_lane();
+        const float* srow = p.proj + ((int64_t)(16 * ot_w + (lp & 15)) * QM + 8 * (lp >> 4));
+#pragma unroll
+        for (int kc = 0; kc < QKC; ++kc) {
+          spf[2 * kc] = *reinterpret_cast<const float4*>(srow + 32 * kc);
+          spf[2 * kc + 1] = *reinterpret_cast<const float4*>(srow + 32 * kc + 4);
+        }
+      }
       int idx_c = part, idx_1 = part + NPW, idx_2 = part + 2 * NPW;
       const int v0 = bt_load(idx_c);
       const int v1 = bt_load(idx_1);
@@ -834,10 +875,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       };
       Tile<D, KK, VK> A, B, C3;
       bool ok_c, ok_1;
-      entry(v0, idx_c, ok_c);
-      load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1);
-      entry(v1, idx_1, ok_1);
-      load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1);
+      // the first two tiles go out now, so that their latency overlaps the
+      // q rotation; with the QJL stage they go out after the projection,
+      // whose loads would otherwise wait for them (loads complete in order)
+      auto first_tiles = [&]() {
+        entry(v0, idx_c, ok_c);
+        load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
+        entry(v1, idx_1, ok_1);
+        load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
+      };
+      if constexpr (!C::QJ) first_tiles();
 #pragma unroll
       for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
 
@@ -928,8 +975,62 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           if (amax > 0.f) frexpf(amax, &ex);
           if (l8 == 0) s_qexp[8 * vh + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
         }
-        // (the fence orders this wave's exponent and row writes before its reads)
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+      if constexpr (C::QJ) {
+        // QJL: the projected rows u_g = S_g q_g of every virtual head (q_g:
+        // the rotated row scaled by 2^(15-ex), group g's channels in listed
+        // order) on the matrix cores, in 16-output tiles spread over all the
+        // workgroup's waves: A = S (fp16 high and low parts of the fp32 values,
+        // one MFMA each), B = the rows (high part in columns 0-7, low part in
+        // 8-15), so each output sums all four cross products in fp32.  The u
+        // rows go to the area of virtual head 8 + vh (at most 8 of them).
+        __syncthreads();   // the rotated rows of every virtual head are staged
+        const int lp = fresh_lane();
+        const int pa = lp >> 4, pc = lp & 15;
+        const int grp = (16 * ot_w) / QM;
+        half8_t ah[QKC], al[QKC];   // A: S_grp[i][32 kc + 8 pa .. + 7], i = output 16 ot_w + pc of the group
+#pragma unroll
+        for (int kc = 0; kc < QKC; ++kc) {
+          const float sv[8] = {spf[2 * kc].x, spf[2 * kc].y, spf[2 * kc].z, spf[2 * kc].w,
+                               spf[2 * kc + 1].x, spf[2 * kc + 1].y, spf[2 * kc + 1].z, spf[2 * kc + 1].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ah[kc][e] = (_Float16)sv[e];
+            al[kc][e] = (_Float16)(sv[e] - (float)ah[kc][e]);
+          }
+        }
+        for (int vq = wave / QOT; vq < VH; vq += kWaves / QOT) {
+          const float* rows = reinterpret_cast<const float*>(qv_all + vq * NQK * 64);
+          float* const urows = reinterpret_cast<float*>(qv_all + (8 + vq) * NQK * 64);
+          const float rpow = ldexpf(1.0f, s_qexp[8 * vq + (pc & 7)]);   // the column's row scale
+          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < QKC; ++kc) {
+            // B: values j = 32 kc + 8 pa + e of row pc & 7 (group order)
+            half8_t bq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int pos = grp * QM + 32 * kc + 8 * pa + e;
+              int chn = pos;
+              if constexpr (C::MIXED) chn = (int)((s_par[32 + (pos >> 2)] >> (8 * (pos & 3))) & 0xFFu);
+              const float v = rows[(pc & 7) * D + chn] * rpow;
+              const _Float16 hi = (_Float16)v;
+              bq[e] = (pc & 8) ? (_Float16)(v - (float)hi) : hi;
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[kc], bq, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[kc], bq, acc, 0, 0, 0);
+          }
+          // output 16 ot_w + 4 pa + e of row pc (columns pc and pc + 8 summed)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float u = acc[e] + row_ror8(acc[e]);
+            if (pc < 8) urows[pc * D + 16 * ot_w + 4 * pa + e] = u;
+          }
+        }
+        __syncthreads();   // every u row is written
+      }
+      if (part == 0) {
+        float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
         // (lane roles recomputed from the fresh lane index: values kept
         // across the block loop may sit in scratch, whose reloads here would
         // wait for the tile loads in flight)
@@ -977,13 +1078,53 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
         for (int t = 0; t < NQK; ++t) qv_all[(vh * NQK + t) * 64 + ln] = qvr[t];
+        if constexpr (C::QJ) {
+          // sketch operands: lane (a, j) multiplies outputs (D / 4) a + 8 t + e
+          // of its column's u row (sign byte NQK a + t of a K row), scaled
+          // by 2^(15-eu) (largest |u| of the row in [2^14, 2^15)) and split
+          // into high and low fp16 parts like q
+          const float* urow = reinterpret_cast<const float*>(qv_all + (8 + vh) * NQK * 64) + lq * D;
+          float uv[NQK][8];
+          float amax = 0.f;
+#pragma unroll
+          for (int t = 0; t < NQK; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float4 f = *reinterpret_cast<const float4*>(urow + la * (D / 4) + 8 * t + 4 * h);
+              uv[t][4 * h] = f.x; uv[t][4 * h + 1] = f.y; uv[t][4 * h + 2] = f.z; uv[t][4 * h + 3] = f.w;
+              amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+            }
+          amax = fmaxf(amax, lane_xor<16>(amax, ln));
+          amax = fmaxf(amax, lane_xor<32>(amax, ln));
+          int eu = 0;
+          if (amax > 0.f) frexpf(amax, &eu);
+          const float u_pow = ldexpf(1.0f, 15 - eu);
+          // the sketch's weight relative to the q.K sum: sqrt(pi / 2) / m
+          // against 1 / sqrt(m) (both over sqrt(d)), and the two scalings
+          if (ln < 8) s_rq[8 * vh + ln] = ldexpf(sqrtf(1.5707963267948966f / (float)(D / C::NGK)), eu - 15);
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the u rows are read
+#pragma unroll
+          for (int t = 0; t < NQK; ++t) {
+            half8_t sv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = uv[t][e] * u_pow;
+              const _Float16 hi = (_Float16)v;
+              sv[e] = lo_q ? (_Float16)(v - (float)hi) : hi;
+            }
+            qv_all[((8 + vh) * NQK + t) * 64 + ln] = sv;
+          }
+        }
       }
+      if constexpr (C::QJ) first_tiles();
       __syncthreads();  // operands, counters and block-table entries ready
       TQ_MARK(3 + 4 * n_done);
       int ph2v = bt_at(idx_2);
       int g3 = grab();
       const float w_col = ldexpf(p.score_mul, -s_qexp[8 * vh + gq]);
       const half8_t* qb = qv_all + vh * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
+      const half8_t* qs = qv_all + (8 + vh) * NQK * 64 + lane;   // QJL: sketch operand t at qs[64 * t]
+      const float r_col = C::QJ ? s_rq[8 * vh + gq] : 0.f;
 
       // -------- stream this wave's blocks of the piece
       // online softmax state per column: running max m_run (raw score
@@ -1008,7 +1149,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       auto compute = [&](const Tile<D, KK, VK>& cur, int b, bool ok) {
         float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
         float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (KK == K4) {
+        if constexpr (C::KB == K4) {
 #pragma unroll
           for (int t = 0; t < NQK; ++t) {
             u32x4_t av;
@@ -1016,7 +1157,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[t], off4_k, by));
             acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
           }
-        } else if constexpr (KK == K2) {
+        } else if constexpr (C::KB == K2) {
 #pragma unroll
           for (int t = 0; t < NQK; ++t) {
             const uint2 x0 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1)));
@@ -1024,7 +1165,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
             acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
           }
-        } else if constexpr (KK == KM43) {   // 4-bit group 0 by the nibble table, 3-bit group 1 by the pair table
+        } else if constexpr (C::KB == KM43) {   // 4-bit group 0 by the nibble table, 3-bit group 1 by the pair table
           constexpr int per_g = NQK / 2;
 #pragma unroll
           for (int u = 0; u < per_g; ++u) {
@@ -1093,6 +1234,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             v = (e & 1) ? fma_h<1>(full1, kw1, v) : fma_h<0>(full1, kw1, v);
           }
           sc[e] = v;
+        }
+        if constexpr (C::QJ) {
+          // QJL: the sketch sum of this lane's K row against the projected
+          // query (after the q.K sums are consumed, so that its accumulator
+          // reuses their registers), one MFMA per 32 outputs with A =
+          // +-(residual norm) in fp16 (exact): sign bit e2 of a byte to bit
+          // 15, bit e2 + 1 to bit 31 of the operand dword
+          float4_t accq = {0.f, 0.f, 0.f, 0.f};
+          const int lq = fresh_lane();
+          const uint32_t sb_all = cur.sg >> (8 * ((NQK * (lq >> 4)) & 3));
+          const uint32_t gam = (cur.gm >> (16 * (lq & 1))) & 0xFFFFu;
+          const uint32_t g2 = gam | (gam << 16);
+#pragma unroll
+          for (int t = 0; t < NQK; ++t) {
+            const uint32_t sb = (sb_all >> (8 * t)) & 0xFFu;
+            const uint32_t spread = sb | (sb << 15);
+            u32x4_t av;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) av[e2] = ((spread << (15 - 2 * e2)) & 0x80008000u) | g2;
+            accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qs[64 * t], accq, 0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[e] = __builtin_fmaf(accq[e] + row_ror8(accq[e]), r_col, sc[e]);
         }
         if (part) {
 #pragma unroll
@@ -1280,7 +1444,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if (idx_c >= n) return false;
         bool ok2;
         entry(ph2v, idx_2, ok2);
-        load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1);
+        load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
         const int idx_3 = __builtin_amdgcn_readfirstlane(g3);
         const int ph3v = bt_at(idx_3);
         g3 = grab();
@@ -1660,10 +1824,16 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   const int G = num_queries * Gr;   // matrix-core columns used per kv head
   const int kk = format_kind_k(kfmt), vk = format_kind_v(vfmt);
   if (vfmt->qjl) return set_error(TQ_ERR_VALUE, "the QJL stage is defined for K formats only");
-  if (kfmt->qjl && num_queries != 1)
-    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take one query per sequence");
-  if (kfmt->qjl && Gr > 8)
-    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take at most 8 q heads per kv head");
+  // QJL formats whose MSE groups and V format the main kernel reads take it
+  // (the sketch term on the matrix cores, up to 64 columns per kv head);
+  // other QJL layouts take the separate QJL kernel (one query, <= 8 q heads)
+  const bool qjl_fast = kfmt->qjl && kk >= 0 && (vk == V4 || vk == V2);
+  if (qjl_fast && G > 64)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "K formats with the QJL stage take at most 64 (query, q head) pairs per kv head");
+  if (kfmt->qjl && !qjl_fast && num_queries != 1)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "this QJL K format takes one query per sequence");
+  if (kfmt->qjl && !qjl_fast && Gr > 8)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "this QJL K format takes at most 8 q heads per kv head");
   if (kk < 0 && !kfmt->qjl) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "no decode kernel for this K format (served: 4-bit, 2-bit, 4+3-bit and 3+2-bit groups)");
   if (vk < 0)
     return set_error(TQ_ERR_UNSUPPORTED_FORMAT,
@@ -1689,7 +1859,9 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   if (q_bytes >= (1ll << 31)) return set_error(TQ_ERR_VALUE, "q must be smaller than 2 GiB");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
-  if (kfmt->qjl) {   // sketch term on every score: the QJL decode kernel, then the generic merge
+  if (kfmt->qjl && (reinterpret_cast<uintptr_t>(kfmt->qjl_proj) & 15))
+    return set_error(TQ_ERR_VALUE, "qjl_proj must be 16-byte aligned");
+  if (kfmt->qjl && !qjl_fast) {   // sketch term on every score: the QJL decode kernel, then the generic merge
     if ((reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages) |
          reinterpret_cast<uintptr_t>(kfmt->qjl_proj)) & 15)
       return set_error(TQ_ERR_VALUE, "page pools and qjl_proj must be 16-byte aligned");
@@ -1754,8 +1926,9 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   while (8 * CG < G) CG *= 2;
   const int cus = device_cus();
   int HG = 1;
+  const int vh_cap = qjl_fast ? 8 : 16;   // QJL: the sketch operands take the other 8 operand areas
   for (int hg : {8, 4, 2}) {
-    if (num_kv_heads % hg || hg * CG > 16) continue;
+    if (num_kv_heads % hg || hg * CG > vh_cap) continue;
     if ((int64_t)num_seqs * (num_kv_heads / hg) * num_splits >= cus) { HG = hg; break; }
   }
   p.HG = HG;
@@ -1819,6 +1992,7 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
     }
     for (int jx = 0; jx < D; ++jx) p.v_ch[jx] = vfmt->group_channels[jx];
   }
+  p.proj = kfmt->qjl_proj;
   p.q_f32 = q_dtype == TQ_F32;
   p.out_f32 = out_dtype == TQ_F32;
   p.q_bytes = (int32_t)q_bytes;
@@ -1829,11 +2003,16 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
     p.part_o = static_cast<float*>(workspace);
     p.part_lse = p.part_o + (int64_t)num_seqs * num_queries * num_q_heads * num_splits * D;
   }
+  const int kk_launch = kk | (qjl_fast ? KQ : 0);   // K kind with the QJL flag
 #define TQ_LAUNCH(DD, KKK, VVV) \
-  if (D == DD && kk == KKK && vk == VVV) launch_decode<DD, KKK, VVV>(p, hs);
+  if (D == DD && kk_launch == (KKK) && vk == VVV) launch_decode<DD, (KKK), VVV>(p, hs);
 #define TQ_LAUNCH_V(DD, KKK) TQ_LAUNCH(DD, KKK, V4) TQ_LAUNCH(DD, KKK, V2) TQ_LAUNCH(DD, KKK, VM43) TQ_LAUNCH(DD, KKK, VM32)
+#define TQ_LAUNCH_Q(DD, KKK) TQ_LAUNCH(DD, KKK | KQ, V4) TQ_LAUNCH(DD, KKK | KQ, V2)
   TQ_LAUNCH_V(128, K4) TQ_LAUNCH_V(128, K2) TQ_LAUNCH_V(128, KM43) TQ_LAUNCH_V(128, KM32)
   TQ_LAUNCH_V(64, K4) TQ_LAUNCH_V(64, K2) TQ_LAUNCH_V(64, KM43) TQ_LAUNCH_V(64, KM32)
+  TQ_LAUNCH_Q(128, K4) TQ_LAUNCH_Q(128, K2) TQ_LAUNCH_Q(128, KM43) TQ_LAUNCH_Q(128, KM32)
+  TQ_LAUNCH_Q(64, K4) TQ_LAUNCH_Q(64, K2) TQ_LAUNCH_Q(64, KM43) TQ_LAUNCH_Q(64, KM32)
+#undef TQ_LAUNCH_Q
 #undef TQ_LAUNCH_V
 #undef TQ_LAUNCH
   st = launch_status("tq_decode_paged launch");

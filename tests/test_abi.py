@@ -230,9 +230,19 @@ def test_multi_query_status_codes_without_launch():
         return L.tq_decode_paged_multi(16, tq.TQ_BF16, 0, NQ, Hq, 2, 16, 16, 10, 16, 16, 4, 16,
                                        ctypes.byref(qc), ctypes.byref(f.c), 0.1, 1, None, 0, 16, tq.TQ_BF16,
                                        None, None, None)
-    assert call_qjl(2, 8) == tq.TQ_ERR_UNSUPPORTED_FORMAT       # the QJL stage: one query
-    assert call_qjl(1, 32) == tq.TQ_ERR_UNSUPPORTED_FORMAT      # and at most 8 q heads per kv head
-    assert call_qjl(1, 16) == tq.TQ_OK
+    assert call_qjl(2, 8) == tq.TQ_OK                           # 4-bit K + QJL: the main kernel, several queries
+    assert call_qjl(1, 128) == tq.TQ_OK                         # 64 q heads per kv head
+    assert call_qjl(33, 4) == tq.TQ_ERR_UNSUPPORTED_FORMAT      # 66 columns: past the 64 of the QJL path
+    assert "64" in L.tq_last_error().decode()
+    f3 = tq.Format(128, [3], s)                                 # a layout only the separate QJL kernel reads
+    q3 = _qjl_c(f3)
+    def call_q3(NQ, Hq):
+        return L.tq_decode_paged_multi(16, tq.TQ_BF16, 0, NQ, Hq, 2, 16, 16, 10, 16, 16, 4, 16,
+                                       ctypes.byref(q3), ctypes.byref(f.c), 0.1, 1, None, 0, 16, tq.TQ_BF16,
+                                       None, None, None)
+    assert call_q3(2, 8) == tq.TQ_ERR_UNSUPPORTED_FORMAT        # one query there
+    assert call_q3(1, 32) == tq.TQ_ERR_UNSUPPORTED_FORMAT       # and at most 8 q heads per kv head
+    assert call_q3(1, 16) == tq.TQ_OK
 
 
 def _qjl_c(f, proj=0x1000):
@@ -277,9 +287,9 @@ def test_qjl_status_codes_without_launch():
     assert _call_decode(kf=fq, B=0) == tq.TQ_OK
     assert _call_decode(kf=fq, P=4) == tq.TQ_ERR_VALUE                # workspace missing
     L = tq._lib
-    st = L.tq_decode_paged_multi(1, tq.TQ_BF16, 2, 2, 8, 2, 1, 1, 10, 16, 1, 4, 1, ctypes.byref(kq),
+    st = L.tq_decode_paged_multi(1, tq.TQ_BF16, 2, 17, 8, 2, 1, 1, 10, 16, 1, 4, 1, ctypes.byref(kq),
                                  ctypes.byref(f4.c), 0.1, 1, None, 0, 1, tq.TQ_BF16, None, None, None)
-    assert st == tq.TQ_ERR_UNSUPPORTED_FORMAT                         # one query per sequence only
+    assert st == tq.TQ_ERR_UNSUPPORTED_FORMAT                         # 68 columns: past the QJL path's 64
     assert _call_write(vf=fq) == tq.TQ_ERR_VALUE                      # QJL on V
 
 

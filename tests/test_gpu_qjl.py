@@ -88,7 +88,7 @@ def test_qjl_write_cancelling_projection_sums(bits, d, dtype):
     _assert_pool_equal(kp.cpu().numpy(), ref, "K (QJL, cancelling sums)")
 
 
-def test_qjl_rejected_on_v_and_multi_query():
+def test_qjl_rejected_on_v_and_past_64_columns():
     import torch
     import quantized_paged_kv_amd as tq
     w = wl.small_decode_workload(41, 1, 4, 2, 128, [40], [3, 2], [4], qjl=True)
@@ -101,7 +101,7 @@ def test_qjl_rejected_on_v_and_multi_query():
     kp, vp = build_cache(w)
     bt = torch.from_numpy(w.block_tables).cuda()
     cl = torch.from_numpy(w.context_lens).cuda()
-    q2 = torch.zeros((1, 2, 4, 128), dtype=torch.bfloat16, device="cuda")
+    q2 = torch.zeros((1, 33, 4, 128), dtype=torch.bfloat16, device="cuda")   # 66 columns per kv head
     with pytest.raises(tq.UnsupportedFormatError):
         tq.decode_paged(q2, kp, vp, bt, cl, kf, vf, w.scale)
 
@@ -158,6 +158,11 @@ CASES = [
     (128, [4, 3], [2], 8, 8, [700], 20, "bf16", "f32", "normal"),
     (64, [2], [2], 8, 1, [1000, 16], 7, "bf16", "f32", "normal"),
     (64, [3, 2], [4], 6, 3, [5, 400, 129], 2, "f32", "f32", "t3"),
+    (64, [4], [2], 4, 1, [77, 300], 2, "bf16", "f32", "normal"),
+    (64, [4, 3], [4], 2, 2, [129], 1, "f32", "f32", "t3"),
+    # a K layout the main kernel does not read (one 3-bit group): the
+    # separate QJL kernel
+    (128, [3], [4], 8, 2, [200, 33], 2, "bf16", "f32", "normal"),
 ]
 
 
@@ -262,3 +267,43 @@ def test_qjl_bad_block_entry_and_context_length():
     with pytest.raises(IndexError, match="position -1"):
         tq.decode_paged(to_device(q, w.q_dtype), kp, vp, torch.from_numpy(bt_full).cuda(),
                         torch.from_numpy(cl).cuda(), kf, vf, w.scale, check=True)
+
+
+MULTI = [
+    # d, kbits, vbits, Hq, Hkv, ctx, queries, splits, out dtype
+    (128, [3, 2], [2], 16, 2, [1, 40, 300, 700], 2, 3, "f32"),
+    (128, [4], [4], 8, 2, [20, 500], 8, 1, "bf16"),
+    (128, [4, 3], [2], 8, 1, [64, 1000], 8, 4, "f32"),      # 64 columns
+    (64, [2], [4], 4, 2, [17, 257], 5, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", MULTI, ids=[f"d{c[0]}K{c[1]}V{c[2]}G{c[3]//c[4]}NQ{c[6]}P{c[7]}" for c in MULTI])
+def test_qjl_multi_query(case):
+    """QJL K formats with several queries per sequence (up to 64 (query, q
+    head) columns per kv head) against the oracle's multi-query reference,
+    whose keys include the sketch term."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    d, kb, vb, hq, hkv, ctx, NQ, P, odt = case
+    print(f"case {case}", flush=True)
+    w = wl.small_decode_workload(650 + d + NQ + P, len(ctx), hq, hkv, d, ctx, kb, vb, out_dtype=odt, num_splits=P,
+                                 max_blocks_per_seq=(max(ctx) + 15) // 16 + 1, qjl=True)
+    kp, vp = build_cache(w)
+    kf, vf = w._gpu_formats
+    g = wl.rng(w.seed, 41)
+    q = wl.bf16_round(g.standard_normal((w.num_seqs, NQ, hq, d), dtype=np.float32))
+    od = torch.float32 if odt == "f32" else torch.bfloat16
+    o, l = tq.decode_paged(to_device(q, "bf16"), kp, vp, torch.from_numpy(w.block_tables).cuda(),
+                           torch.from_numpy(w.context_lens).cuda(), kf, vf, w.scale, num_splits=P, out_dtype=od,
+                           check=True)
+    torch.cuda.synchronize()
+    o, l = o.float().cpu().numpy(), l.cpu().numpy()
+    kof, vof = oracle_format(w.kfmt), oracle_format(w.vfmt)
+    sl = slots_of(w.block_tables, w.context_lens)
+    allsl = np.concatenate(sl)
+    okp = oracle_pages(np.concatenate([wl.kv_values(w, "k", s) for s in range(w.num_seqs)]), allsl, w.num_blocks, kof, "k")
+    ovp = oracle_pages(np.concatenate([wl.kv_values(w, "v", s) for s in range(w.num_seqs)]), allsl, w.num_blocks, vof, "v")
+    o_ref, l_ref = oatt.decode_multi_reference(q.astype(np.float64), okp, ovp, w.block_tables, w.context_lens,
+                                               kof, vof, w.scale, 16)
+    check(o, l, o_ref, l_ref, [(s, i, h) for s in range(w.num_seqs) for i in range(NQ) for h in range(hq)], odt)
