@@ -165,8 +165,13 @@ typedef struct tq_format {
  *   index plane, V pages: when rb is a multiple of 16 (c = rb / 16), byte b
  *            of row t is at ((16*(t % 4) + b / c)*4 + t / 4)*c + b % c: 64 runs
  *            of 4c bytes, run 16q + j holding bytes [c*j, c*(j+1)) of rows q,
- *            q+4, q+8, q+12 (one decode lane's share, one wide load); other V
- *            formats use the K layout.
+ *            q+4, q+8, q+12 (one decode lane's share, one wide load).
+ *            Two-group V formats: group g's bytes form a sub-plane at byte
+ *            16 * (group g's byte offset in a row); a row's group bytes split
+ *            into octets of b_g bytes (8 indices each), and octet o of row t
+ *            sits in run (m/8)*(t % 4) + o of 4*b_g bytes, at place t / 4
+ *            (byte q of it at run start + (t / 4)*b_g + q).  Other V formats
+ *            use the K layout.
  */
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -268,19 +273,24 @@ tq_status tq_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * A sequence with context length 0 gets out = 0 and lse = -inf.
  * Served formats (else UNSUPPORTED_FORMAT): head_dim 64 or 128; K one group
  * of 4 or 2 bits, or two groups of 4 + 3 bits (3.5-bit recipe) or 3 + 2 bits
- * (2.5-bit recipe; [S "What it does"], [D "Recipe Strategy"]); V one group
- * of 4 or 2 bits;
- * num_q_heads / num_kv_heads in 1..TQ_MAX_COLUMNS (1..8 with the QJL
- * stage); block_size 16.  Each page pool must be smaller than 4 GiB and
+ * (2.5-bit recipe; [S "What it does"], [D "Recipe Strategy"]); V the same
+ * four (the formats independent, [D "System Invariants"]);
+ * num_q_heads / num_kv_heads in 1..TQ_MAX_COLUMNS (1..64 with the QJL
+ * stage; see below); block_size 16.  Each page pool must be smaller than 4 GiB and
  * num_blocks below 2^31 (else VALUE).
  * Results are reproducible up to the order of floating-point accumulation:
  * blocks are shared dynamically among the waves serving a kv head.
- * K formats with the QJL stage (qjl = 1; any group layout above, K bits 2-4)
- * run a separate kernel that adds the sign sketch's term to every score:
- * one workgroup per (sequence, kv head, split p), split p taking logical
- * blocks [p*c, (p+1)*c), c = ceil(ceil(context_lens[s] / 16) / P), every
- * split writing its partial (lse -inf when empty) before the same merge.
- * It needs 16-byte aligned page pools and qjl_proj (else VALUE).
+ * K formats with the QJL stage (qjl = 1) add the sign sketch's term to
+ * every score.  With K groups of 4, 2, 4+3 or 3+2 bits and a one-group V
+ * format the same kernel serves them (the projected query on the matrix
+ * cores, up to 64 (query, q head) pairs per kv head); other QJL layouts (K
+ * bits 2-4 in any grouping) run a separate kernel with one workgroup per
+ * (sequence, kv head, split p), split p taking logical blocks [p*c,
+ * (p+1)*c), c = ceil(ceil(context_lens[s] / 16) / P), every split writing
+ * its partial (lse -inf when empty) before the same merge; that kernel takes
+ * one query and at most 8 q heads per kv head, and 16-byte aligned page
+ * pools.  qjl_proj must be 16-byte aligned (else VALUE).  Two-group V with
+ * a QJL K format is UNSUPPORTED_FORMAT.
  */
 tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
                           int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
@@ -306,8 +316,9 @@ tq_status tq_decode_paged(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
  *   workspace    tq_decode_workspace_bytes(num_seqs * num_queries, ...).
  * Every other argument, error and format is as for tq_decode_paged, which
  * is this call with num_queries = 1.  Served: num_queries * (num_q_heads /
- * num_kv_heads) <= TQ_MAX_COLUMNS, and num_queries = 1 for a K format with
- * the QJL stage (else UNSUPPORTED_FORMAT).
+ * num_kv_heads) <= TQ_MAX_COLUMNS (64 for a K format with the QJL stage;
+ * one query and 8 q heads for the QJL layouts of the separate kernel, see
+ * tq_decode_paged), else UNSUPPORTED_FORMAT.
  */
 tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
                                 int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,
@@ -401,7 +412,8 @@ tq_status tq_decode_dense(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
 /*
  * Phase timestamps of the paged decode kernel, for performance analysis
  * only.  In a library built with TQ_PHASE_TRACE defined, every later
- * tq_decode_paged / tq_decode_paged_multi call (non-QJL formats) has thread
+ * tq_decode_paged / tq_decode_paged_multi call served by the main decode
+ * kernel (every format but the QJL layouts of the separate kernel) has thread
  * 0 of each persistent workgroup w write 16 uint64 values to
  * buf[16 w .. 16 w + 15]: the 100 MHz real-time counter at kernel entry
  * (0), when the work split is known (1), per piece i < 3 at its start

@@ -1004,15 +1004,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           float* const urows = reinterpret_cast<float*>(qv_all + (8 + vq) * NQK * 64);
           const float rpow = ldexpf(1.0f, s_qexp[8 * vq + (pc & 7)]);   // the column's row scale
           float4_t acc = {0.f, 0.f, 0.f, 0.f};
+          // listed channels of positions grp M + 32 kc + 8 pa .. + 7 (two-group
+          // K: 8 bytes of the channel list, read at once for every kc)
+          uint2 chw[QKC];
+          if constexpr (C::MIXED) {
+#pragma unroll
+            for (int kc = 0; kc < QKC; ++kc)
+              chw[kc] = *reinterpret_cast<const uint2*>(s_par + 32 + ((grp * QM + 32 * kc + 8 * pa) >> 2));
+          }
 #pragma unroll
           for (int kc = 0; kc < QKC; ++kc) {
             // B: values j = 32 kc + 8 pa + e of row pc & 7 (group order)
             half8_t bq;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int pos = grp * QM + 32 * kc + 8 * pa + e;
-              int chn = pos;
-              if constexpr (C::MIXED) chn = (int)((s_par[32 + (pos >> 2)] >> (8 * (pos & 3))) & 0xFFu);
+              int chn = grp * QM + 32 * kc + 8 * pa + e;
+              if constexpr (C::MIXED) chn = (int)((((e >> 2) ? chw[kc].y : chw[kc].x) >> (8 * (e & 3))) & 0xFFu);
               const float v = rows[(pc & 7) * D + chn] * rpow;
               const _Float16 hi = (_Float16)v;
               bq[e] = (pc & 8) ? (_Float16)(v - (float)hi) : hi;
@@ -1043,19 +1050,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         // fp16 rounding of the remainder (lanes j >= 8); all operands are
         // built in registers before any is written over the rows
         half8_t qvr[NQK];
+        // two-group K: operand element (t, e) of lane (a, j) is channel
+        // k_ch[pos] of the column, pos = (t / per_g) m + a (m / 4) + 8 (t %
+        // per_g) + e; the 8 list bytes of each t are read at once, before
+        // any row value
+        uint2 chl[NQK];
+        if constexpr (C::MIXED) {
+          constexpr int m = D / 2;
+          constexpr int per_g = NQK / 2;
+#pragma unroll
+          for (int t = 0; t < NQK; ++t)
+            chl[t] = *reinterpret_cast<const uint2*>(s_par + 32 + (((t / per_g) * m + la * (m / 4) + 8 * (t % per_g)) >> 2));
+        }
 #pragma unroll
         for (int t = 0; t < NQK; ++t) {
           float vq[8];
           if constexpr (C::MIXED) {
-            // operand element (t, e) of lane (a, j): channel k_ch[pos] of the
-            // column, pos = (t / per_g) m + a (m / 4) + 8 (t % per_g) + e
-            constexpr int m = D / 2;
-            constexpr int per_g = NQK / 2;
-            const int grp_k = t / per_g, u = t % per_g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int pos_l = grp_k * m + la * (m / 4) + 8 * u + e;
-              const int chn = (int)((s_par[32 + (pos_l >> 2)] >> (8 * (pos_l & 3))) & 0xFFu);
+              const int chn = (int)((((e >> 2) ? chl[t].y : chl[t].x) >> (8 * (e & 3))) & 0xFFu);
               vq[e] = qrow[chn];
             }
           } else {
