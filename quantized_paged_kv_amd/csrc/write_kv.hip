@@ -44,13 +44,18 @@ struct WriteParams {
 };
 
 template <int D, bool F32>
-__global__ __launch_bounds__(kThreads, 4) void write_kv_kernel(WriteParams p) {
+__global__ __launch_bounds__(kThreads, 5) void write_kv_kernel(WriteParams p) {
   constexpr int LPR = D / 8;              // lanes per row
   constexpr int RPB = kThreads / LPR;     // rows per block
   __shared__ double lds_w[RPB][D];
   __shared__ uint32_t lds_row[RPB][D / 8 + 1];  // packed row (<= D/2 bytes)
-  __shared__ uint8_t lds_bkt[2][256];           // per bucket: thresholds below it | 0x80 if one inside
-  __shared__ double lds_thr[2][16];
+  // per bucket: the threshold inside it (+inf if none) and the count of
+  // thresholds below it, one 16-byte entry (one LDS read per value)
+  struct alignas(16) Bucket {
+    double thr;
+    uint32_t below, pad;
+  };
+  __shared__ Bucket lds_bk[2][256];
 
   __shared__ DevFormat sf;
 
@@ -69,7 +74,6 @@ __global__ __launch_bounds__(kThreads, 4) void write_kv_kernel(WriteParams p) {
   // bucket table of each group (bucket k spans z in [(k - off) / 32, (k + 1 - off) / 32))
   for (int g = 0; g < f.ng; ++g) {
     const int nthr = (1 << f.bits[g]) - 1;
-    if (threadIdx.x < 16) lds_thr[g][threadIdx.x] = threadIdx.x < nthr ? f.thr[g][threadIdx.x] : 0.0;
     if (f.fast[g]) {
       const int k = threadIdx.x;   // kThreads == 256 buckets
       const double lo = ((double)k - (double)f.lut_off[g]) / 32.0, hi = lo + 1.0 / 32.0;
@@ -78,7 +82,8 @@ __global__ __launch_bounds__(kThreads, 4) void write_kv_kernel(WriteParams p) {
         below += f.thr[g][i] < lo ? 1 : 0;
         inside |= (f.thr[g][i] >= lo && f.thr[g][i] < hi) ? 1 : 0;
       }
-      lds_bkt[g][k] = (uint8_t)(below | (inside << 7));
+      lds_bk[g][k].thr = inside ? f.thr[g][below] : __builtin_inf();
+      lds_bk[g][k].below = (uint32_t)below;
     }
   }
   __syncthreads();
@@ -137,26 +142,27 @@ __global__ __launch_bounds__(kThreads, 4) void write_kv_kernel(WriteParams p) {
   }
   const bool valid = in_range && slot_ok;
 
-  // ---- load eight channels and apply the signs (exact)
+  // ---- load eight channels and apply the signs (exact: the sign bits are
+  // flipped in the input words before the conversion to fp64)
   double v[8];
+  const uint32_t sb = (f.sign_bits[(8 * L) >> 5] >> ((8 * L) & 31)) & 0xFFu;
   if (F32) {
     const uint4 a = cur.a, b = cur.b;
-    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+    const uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (double)__uint_as_float(w8[e] ^ (((sb >> e) & 1u) << 31));
   } else {
+    // sign bits 2 i and 2 i + 1 to bits 15 and 31 of word i (sb | sb << 15
+    // puts them 15 - 2 i places below)
+    const uint32_t spread = sb | (sb << 15);
     const uint4 raw = cur.a;
     const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = (double)__uint_as_float(w4[i] << 16);
-      v[2 * i + 1] = (double)__uint_as_float(w4[i] & 0xFFFF0000u);
+      const uint32_t w = w4[i] ^ ((spread << (15 - 2 * i)) & 0x80008000u);
+      v[2 * i] = (double)__uint_as_float(w << 16);
+      v[2 * i + 1] = (double)__uint_as_float(w & 0xFFFF0000u);
     }
-  }
-  {
-    const uint32_t sb = (f.sign_bits[(8 * L) >> 5] >> ((8 * L) & 31)) & 0xFFu;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (sb & (1u << e)) v[e] = -v[e];
   }
 
   // ---- Walsh-Hadamard transform, butterflies h = 1, 2, 4 inside the lane
@@ -285,16 +291,20 @@ __global__ __launch_bounds__(kThreads, 4) void write_kv_kernel(WriteParams p) {
       if (f.fast[g] && r > 1e-30 && r < 1e30) {
         const float rinv = __builtin_amdgcn_rcpf((float)r);
         const float off = f.lut_off[g];
+        // all buckets first, then all their entries (one LDS round trip)
+        int kb[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float z = (float)wg[BASE + e] * rinv;
-          int k = __float2int_rd(__builtin_fmaf(z, 32.0f, off));
-          k = k < 0 ? 0 : (k > 255 ? 255 : k);
-          const uint32_t ent = lds_bkt[g][k];
-          const uint32_t below = ent & 0x7Fu;
-          const double T = lds_thr[g][below] * r;
-          idx[e] = below + ((ent >> 7) & (T < wg[BASE + e] ? 1u : 0u));
+          const int k = __float2int_rd(__builtin_fmaf(z, 32.0f, off));
+          kb[e] = k < 0 ? 0 : (k > 255 ? 255 : k);
         }
+        Bucket ent[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) ent[e] = lds_bk[g][kb[e]];
+        // the threshold inside the bucket, scaled (+inf when none: never below)
+#pragma unroll
+        for (int e = 0; e < E; ++e) idx[e] = ent[e].below + (ent[e].thr * r < wg[BASE + e] ? 1u : 0u);
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) idx[e] = 0;
