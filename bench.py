@@ -268,7 +268,8 @@ def window_cold(b, launches, warmup, flush, cap=132):
     every sequence keeps cap = 4 boundary + 128 recent tokens in bf16, attended
     by tq_decode_dense and merged with the history's float32 (o, lse).  Times,
     with cold caches, the window call alone and the whole window-augmented
-    decode (tq_decode_paged with float32 output, then tq_decode_dense)."""
+    decode (tq_decode_paged with float32 output, then tq_decode_dense), and
+    the same result from one tq_decode_paged_window call."""
     import numpy as np
     import torch
     import workloads as wl
@@ -290,8 +291,15 @@ def window_cold(b, launches, warmup, flush, cap=132):
     def window():
         tq.decode_dense(b.q, kw, vw, lens, w.scale, hist_out=ho, hist_lse=hl, out=out, lse=lse)
 
+    ws_f = torch.empty(max(tq.workspace_bytes(B, Hq, d, b.P + 1), 1), dtype=torch.uint8, device="cuda")
+
+    def fused():
+        tq.decode_paged_window(b.q, kp, vp, b.bt, b.cl, b.kf, b.vf, kw, vw, lens, w.scale, num_splits=b.P,
+                               out=out, lse=lse, workspace=ws_f)
+
     res = {}
-    for key, fns in (("window_us", (window,)), ("decode_plus_window_us", (history, window))):
+    for key, fns in (("window_us", (window,)), ("decode_plus_window_us", (history, window)),
+                     ("decode_with_window_one_call_us", (fused,))):
         history()
         for _ in range(warmup):
             for f in fns:
@@ -587,12 +595,14 @@ def main():
             "workload": f"{w.name} + dense window of {cap} bf16 tokens per sequence (4 boundary + 128 recent)",
             "window_us": stats_us(wres["window_us"]),
             "decode_plus_window_us": stats_us(wres["decode_plus_window_us"]),
+            "decode_with_window_one_call_us": stats_us(wres["decode_with_window_one_call_us"]),
             "window_algorithmic_bytes": wbytes_win,
             "roofline": {"bound": "hbm", "achieved": round(wbytes_win / (wavg * 1e-3) / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(wbytes_win / (wavg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "kernel": "tq_decode_dense (window attention + merge with the history)"}}
-        log(f"window: {wavg * 1e3:.1f} us")
+        fz = wres["decode_with_window_one_call_us"]
+        log(f"window: {wavg * 1e3:.1f} us; decode + window in one call: {fz[len(fz) // 2] * 1e3:.1f} us")
         mq_ms, mq_bytes, _ = multi_cold(b, max(10, args.steps // 2), args.warmup, flush)
         mq_avg = sum(mq_ms) / len(mq_ms)
         result["multi_query"] = {

@@ -410,6 +410,40 @@ tq_status tq_decode_dense(const void* q, tq_dtype q_dtype, int32_t num_seqs, int
                           tq_dtype out_dtype, float* lse, int32_t* dev_err, tq_stream_t stream);
 
 /*
+ * The packed history and a dense bf16 window attended in ONE call: the
+ * result of tq_decode_paged over the pages followed by tq_decode_dense over
+ * the window with that history (same readings: [D "Format Strategy"] and
+ * [D "Data Ownership"], window tokens are not also in the pages).  The
+ * persistent workgroups of the paged decode take the (sequence, kv head)
+ * window items after their pages; each item's normalised output and lse go
+ * to one more partial slot of its rows, and the split merge combines every
+ * row's slots by the log-sum-exp identity.
+ *   q ... vfmt   as for tq_decode_paged (one query per sequence).
+ *   win_k, win_v device [num_seqs][win_capacity][num_kv_heads][head_dim],
+ *                win_dtype BF16 (else UNSUPPORTED_FORMAT: tq_decode_dense
+ *                takes f32 windows), 16-byte aligned; may be NULL when
+ *                win_capacity == 0.
+ *   win_lens     device int32 [num_seqs]: window tokens of sequence s at rows
+ *                0 .. win_lens[s]-1; outside [0, win_capacity] records
+ *                (TQ_ERR_INDEX, -1 - s) in dev_err and is clamped.
+ *   workspace    tq_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ *                num_splits + 1) bytes (needed even for num_splits == 1).
+ *   out, lse     as for tq_decode_paged; history and window both empty:
+ *                out = 0, lse = -inf.
+ * Served: num_q_heads / num_kv_heads <= 16 and the formats of the main
+ * decode kernel (not the QJL layouts of the separate kernel), else
+ * UNSUPPORTED_FORMAT.
+ */
+tq_status tq_decode_paged_window(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
+                                 int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, const tq_format* kfmt,
+                                 const tq_format* vfmt, const void* win_k, const void* win_v, tq_dtype win_dtype,
+                                 int32_t win_capacity, const int32_t* win_lens, float scale, int32_t num_splits,
+                                 void* workspace, uint64_t workspace_bytes, void* out, tq_dtype out_dtype,
+                                 float* lse, int32_t* dev_err, tq_stream_t stream);
+
+/*
  * Phase timestamps of the paged decode kernel, for performance analysis
  * only.  In a library built with TQ_PHASE_TRACE defined, every later
  * tq_decode_paged / tq_decode_paged_multi call served by the main decode

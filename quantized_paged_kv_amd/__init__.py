@@ -76,6 +76,8 @@ def _load(path: str = LIB_PATH):
                                    P, u64, P, i32, P, P, P], i32),
         "tq_split_merge": ([P, P, i32, i32, i32, i32, P, i32, P, P], i32),
         "tq_decode_dense": ([P, i32, i32, i32, i32, i32, P, P, i32, i32, P, f32, P, P, P, i32, P, P, P], i32),
+        "tq_decode_paged_window": ([P, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, P, P, i32, i32,
+                                    P, f32, i32, P, u64, P, i32, P, P, P], i32),
         "tq_debug_phase_trace": ([P], i32),
         "tq_decode_paged_noalloc": ([P, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, f32, i32, P, i32,
                                      P, P, P], i32),
@@ -410,6 +412,55 @@ def decode_dense(q, k_win, v_win, lens, scale: float, hist_out=None, hist_lse=No
     return out, lse
 
 
+def decode_paged_window(q, k_pages, v_pages, block_tables, context_lens, kfmt: Format, vfmt: Format, k_win, v_win,
+                        win_lens, scale: float, num_splits: int = 1, out=None, lse=None, workspace=None,
+                        out_dtype=None, dev_err=None, check: bool = False, stream=None):
+    """Decode attention of q [B, H_q, d] over the packed pages AND a dense
+    bf16 window k_win / v_win [B, capacity, H_kv, d] holding win_lens[s]
+    tokens of sequence s, in one call (the window's tokens are not also in
+    the pages).  Returns (out [B, H_q, d], lse [B, H_q] float32)."""
+    import torch
+    _need(q.is_cuda and q.is_contiguous() and q.dim() == 3, "q must be a contiguous [B, H_q, d] GPU tensor")
+    B, Hq, d = q.shape
+    _need(k_pages.dim() == 3 and v_pages.dim() == 3 and k_pages.dtype == torch.uint8 and v_pages.dtype == torch.uint8,
+          "page pools must be uint8 [NB, H_kv, tile]")
+    Hkv = k_pages.shape[1]
+    _need(v_pages.shape[:2] == k_pages.shape[:2], "K and V pools differ in blocks or heads")
+    _need(k_pages.shape[2] == kfmt.tile_bytes()[1] and v_pages.shape[2] == vfmt.tile_bytes()[1],
+          "page pool tile size does not match the format")
+    _need(kfmt.head_dim == d and vfmt.head_dim == d, "q head_dim differs from the formats")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B
+          and block_tables.is_contiguous(), "block_tables must be contiguous int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.numel() == B, "context_lens must be int32 [B]")
+    _need(k_win.dim() == 4 and k_win.shape == v_win.shape and k_win.dtype == v_win.dtype
+          and k_win.is_contiguous() and v_win.is_contiguous() and k_win.shape[0] == B
+          and k_win.shape[2] == Hkv and k_win.shape[3] == d,
+          "window K/V must be contiguous [B, capacity, H_kv, d] of one dtype")
+    _need(win_lens.dtype == torch.int32 and win_lens.numel() == B, "win_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _need(out.shape == q.shape and out.is_contiguous(), "out must be contiguous and shaped like q")
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(lse.shape == (B, Hq) and lse.dtype == torch.float32, "lse must be float32 [B, H_q]")
+    need = workspace_bytes(B, Hq, d, num_splits + 1)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    own_err = dev_err is None and check
+    if own_err:
+        dev_err = new_error_word(q.device)
+    _check(_lib.tq_decode_paged_window(_ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(k_pages), _ptr(v_pages),
+                                       k_pages.shape[0], BLOCK_SIZE, _ptr(block_tables), block_tables.shape[1],
+                                       _ptr(context_lens), ctypes.byref(kfmt.c), ctypes.byref(vfmt.c),
+                                       _ptr(k_win), _ptr(v_win), _dtype_code(k_win), k_win.shape[1],
+                                       _ptr(win_lens), float(scale), int(num_splits), _ptr(workspace), ws_bytes,
+                                       _ptr(out), _dtype_code(out), _ptr(lse), _ptr(dev_err), _stream(stream)))
+    if check:
+        raise_device_error(dev_err, "tq_decode_paged_window")
+    return out, lse
+
+
 def set_phase_trace(buf) -> bool:
     """Phase-timestamp buffer (device uint64 tensor, 16 values per CU) for the
     decode kernel; None stops recording.  Returns False when the loaded
@@ -423,5 +474,5 @@ def set_phase_trace(buf) -> bool:
 
 __all__ = ["Format", "UnsupportedFormatError", "DeviceError", "lloyd_max_codebook", "alloc_pages",
            "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged", "decode_paged_noalloc",
-           "split_merge", "decode_dense", "set_phase_trace",
+           "split_merge", "decode_dense", "decode_paged_window", "set_phase_trace",
            "LIB_PATH", "BLOCK_SIZE"]

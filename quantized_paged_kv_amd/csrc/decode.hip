@@ -48,6 +48,7 @@
 #include <mutex>
 
 #include "tq_internal.h"
+#include "window_item.h"
 
 namespace tq {
 namespace {
@@ -111,6 +112,15 @@ struct DecodeParams {
   uint32_t k_span, v_span;   // bytes of each pool (< 4 GiB)
   float score_mul;   // scale * log2(e) / (sqrt(D) * sqrt(m_K)), > 0
   const float* proj; // QJL: the projections S_g, fp32 [groups][m][m] (K kinds with KQ)
+  // Dense window attended with the history (one query per sequence): bf16
+  // rows [S][win_cap][Hkv][D], win_lens[s] valid; every row then goes
+  // through the split merge, whose rows hold PS = P + 1 slots, the window's
+  // result in slot P.  Without a window PS = P.
+  const void* win_k;
+  const void* win_v;
+  const int32_t* win_lens;
+  int32_t win_on, win_cap, PS;
+  float win_scale_log2;   // softmax scale times log2(e)
   float v_mul;       // 1 / sqrt(m_V), applied once in the epilogue
   uint32_t v_signs[4];
   uint32_t k_signs[4];
@@ -629,7 +639,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if (lane == 0 && (c < 0 || c > cap)) record_error(p.dev_err, TQ_ERR_INDEX, -1 - s);
         c = clamp_ctx(c, cap);
       }
-      if (c == 0) {
+      if (c == 0 && p.win_on) {   // the window alone: empty history slots for the merge
+        for (int h = lane; h < p.rows_ps * p.P; h += 64)
+          p.part_lse[((int64_t)s * p.rows_ps + h / p.P) * p.PS + h % p.P] = -INFINITY;
+      } else if (c == 0) {
         for (int idx = lane; idx < p.rows_ps * D; idx += 64) {
           const int64_t off = (int64_t)s * p.rows_ps * D + idx;
           if (p.out_f32) static_cast<float*>(p.out)[off] = 0.f;
@@ -638,11 +651,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if (p.lse)
           for (int h = lane; h < p.rows_ps; h += 64) p.lse[(int64_t)s * p.rows_ps + h] = -INFINITY;
         if (p.P > 1)   // tell the merge that these rows are final
-          for (int h = lane; h < p.rows_ps; h += 64) p.part_lse[((int64_t)s * p.rows_ps + h) * p.P] = __uint_as_float(kDoneBits);
+          for (int h = lane; h < p.rows_ps; h += 64) p.part_lse[((int64_t)s * p.rows_ps + h) * p.PS] = __uint_as_float(kDoneBits);
       }
     }
   }
+  // dense window: (sequence, kv head) items blockIdx.x, + n_wg, ... after
+  // the workgroup's pieces, in the LDS of the tables and operands (free by
+  // then), each result to slot P of its rows
+  auto window_items = [&]() {
+    if (!p.win_on) return;
+    using W = WinItemCfg<D, 16, kThreads, 128>;
+    static_assert(W::BYTES <= (int)(sizeof(sm.lut) + sizeof(sm.xbuf)), "window item larger than its LDS");
+    WindowParams wp = {};
+    wp.q = p.q; wp.k = p.win_k; wp.v = p.win_v; wp.lens = p.win_lens;
+    wp.dev_err = p.dev_err;
+    wp.S = p.S; wp.Hq = p.Hq; wp.Hkv = p.Hkv; wp.G = p.Gr; wp.cap = p.win_cap;
+    wp.scale_log2 = p.win_scale_log2;
+    wp.q_f32 = p.q_f32;
+    WinSink sink;
+    sink.part_o = p.part_o;
+    sink.part_lse = p.part_lse;
+    sink.PS = p.PS;
+    sink.slot = p.P;
+    for (int it = blockIdx.x; it < p.S * p.Hkv; it += p.n_wg) {
+      __syncthreads();   // the workgroup is done with the LDS (pieces or the previous item)
+      window_item_bf16<D, 16, kThreads, 128>(wp, sink, it / p.Hkv, it % p.Hkv, sm.lut, tid);
+    }
+  };
   if (r0 >= r1) {  // uniform across the workgroup
+    window_items();
     TQ_MARK(14);
     TQ_MARK_VALUE(15, 0);
     return;
@@ -752,9 +789,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int b1 = (r1 - vb0 < nb_s) ? r1 - vb0 : nb_s;
     if (b1 > b0) {   // the range holds blocks of this segment
     // one piece: the final output is written here (always so when P == 1)
-    const bool whole = p.P == 1 || (vb0 / R) == ((vb0 + nb_s - 1) / R);
-    const int piece = (int)blockIdx.x - vb0 / R;
-    const int n_pieces = (vb0 + nb_s - 1) / R - vb0 / R + 1;
+    // with a window every row is merged: a whole segment writes slot 0
+    const bool whole = !p.win_on && (p.P == 1 || (vb0 / R) == ((vb0 + nb_s - 1) / R));
+    const int piece = p.P == 1 ? 0 : (int)blockIdx.x - vb0 / R;
+    const int n_pieces = p.P == 1 ? 1 : (vb0 + nb_s - 1) / R - vb0 / R + 1;
       const int ctx = seq_len(p, s_cl, s);
       // causal lengths: the sequence's last NQ cached tokens are the queries'
       // own, query i sees ctx - (NQ - 1 - i) of them; ctx_all is what every
@@ -1611,9 +1649,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
               else *reinterpret_cast<uint2*>(o16) = uint2{w[0], w[1]};
             }
             if (m == 0 && p.lse) p.lse[rowq] = lse;
-            if (m == 0 && p.P > 1) p.part_lse[rowq * p.P] = __uint_as_float(kDoneBits);
+            if (m == 0 && p.P > 1) p.part_lse[rowq * p.PS] = __uint_as_float(kDoneBits);
           } else {
-            const int64_t row0 = rowq * p.P;
+            const int64_t row0 = rowq * p.PS;
             const int64_t prow = row0 + piece;
 #pragma unroll
             for (int k = 0; k < ND; k += 4)
@@ -1640,6 +1678,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       } while (nb_s == 0);
     }
   }
+  window_items();
   TQ_MARK(14);
   TQ_MARK_VALUE(15, (uint64_t)n_done);
   (void)n_done;
@@ -1808,14 +1847,23 @@ extern "C" tq_status tq_split_merge(const float* part_out, const float* part_lse
   return launch_status("tq_split_merge launch");
 }
 
-extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
-                                           int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,
-                                           const uint8_t* v_pages, int64_t num_blocks, int32_t block_size,
-                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                           const int32_t* context_lens, const tq_format* kfmt, const tq_format* vfmt,
-                                           float scale, int32_t num_splits, void* workspace, uint64_t workspace_bytes,
-                                           void* out, tq_dtype out_dtype, float* lse, int32_t* dev_err,
-                                           tq_stream_t stream) {
+namespace {
+// A dense window attended with the history (tq_decode_paged_window).
+struct WinArgs {
+  const void* k;
+  const void* v;
+  int32_t capacity;
+  const int32_t* lens;
+};
+
+tq_status decode_impl(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
+                      int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,
+                      const uint8_t* v_pages, int64_t num_blocks, int32_t block_size,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, const tq_format* kfmt, const tq_format* vfmt,
+                      float scale, int32_t num_splits, void* workspace, uint64_t workspace_bytes,
+                      void* out, tq_dtype out_dtype, float* lse, int32_t* dev_err,
+                      tq_stream_t stream, const WinArgs* win) {
   tq_status st = check_format(kfmt, "K");
   if (st != TQ_OK) return st;
   st = check_format(vfmt, "V");
@@ -1857,8 +1905,21 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
   if (num_seqs == 0) return TQ_OK;
   if (!q || !k_pages || !v_pages || !block_tables || !context_lens || !out)
     return set_error(TQ_ERR_VALUE, "NULL required pointer");
+  if (win) {   // the window's result takes one more partial slot per row
+    if (num_queries != 1) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "a dense window takes one query per sequence");
+    if (Gr > 16) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "a dense window takes at most 16 q heads per kv head");
+    if (kfmt->qjl && !qjl_fast) return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "this QJL K format takes no dense window");
+    if (win->capacity < 0) return set_error(TQ_ERR_VALUE, "window capacity must be >= 0");
+    if (num_seqs > 0 && !win->lens) return set_error(TQ_ERR_VALUE, "NULL window lengths");
+    if (win->capacity > 0 && (!win->k || !win->v)) return set_error(TQ_ERR_VALUE, "NULL window K or V");
+    if ((reinterpret_cast<uintptr_t>(win->k) | reinterpret_cast<uintptr_t>(win->v)) & 15u)
+      return set_error(TQ_ERR_VALUE, "window K and V must be 16-byte aligned");
+    if ((int64_t)num_seqs * win->capacity * num_kv_heads * D * 2 >= (1ll << 40))
+      return set_error(TQ_ERR_VALUE, "window too large");
+  }
+  const int slots = num_splits + (win ? 1 : 0);   // partial slots per row
   uint64_t need = 0;
-  tq_decode_workspace_bytes(num_seqs * num_queries, num_q_heads, D, num_splits, &need);
+  tq_decode_workspace_bytes(num_seqs * num_queries, num_q_heads, D, win ? slots : num_splits, &need);
   if (workspace_bytes < need || (need && !workspace))
     return set_error(TQ_ERR_VALUE, "workspace too small: need " + std::to_string(need) + " bytes");
   const int64_t work_bound = (int64_t)num_seqs * num_kv_heads * (max_blocks_per_seq + 128);
@@ -2012,9 +2073,18 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
 #ifdef TQ_PHASE_TRACE
   p.trace = __atomic_load_n(&g_phase_trace, __ATOMIC_ACQUIRE);
 #endif
-  if (num_splits > 1) {
+  p.PS = slots;
+  if (win) {
+    p.win_on = 1;
+    p.win_k = win->k;
+    p.win_v = win->v;
+    p.win_lens = win->lens;
+    p.win_cap = win->capacity;
+    p.win_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  }
+  if (slots > 1) {
     p.part_o = static_cast<float*>(workspace);
-    p.part_lse = p.part_o + (int64_t)num_seqs * num_queries * num_q_heads * num_splits * D;
+    p.part_lse = p.part_o + (int64_t)num_seqs * num_queries * num_q_heads * slots * D;
   }
   const int kk_launch = kk | (qjl_fast ? KQ : 0);   // K kind with the QJL flag
 #define TQ_LAUNCH(DD, KKK, VVV) \
@@ -2029,11 +2099,42 @@ extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int3
 #undef TQ_LAUNCH_V
 #undef TQ_LAUNCH
   st = launch_status("tq_decode_paged launch");
-  if (st != TQ_OK || num_splits == 1) return st;
-  MergeParams mp = {p.part_o, p.part_lse, out, lse, num_seqs * num_queries, num_q_heads, num_splits, D,
+  if (st != TQ_OK || slots == 1) return st;
+  MergeParams mp = {p.part_o, p.part_lse, out, lse, num_seqs * num_queries, num_q_heads, slots, D,
                     p.out_f32, 1};
   launch_merge(mp, (int64_t)num_seqs * num_queries * num_q_heads, hs);
   return launch_status("tq_decode_paged merge launch");
+}
+}  // namespace
+
+extern "C" tq_status tq_decode_paged_multi(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_queries,
+                                           int32_t num_q_heads, int32_t num_kv_heads, const uint8_t* k_pages,
+                                           const uint8_t* v_pages, int64_t num_blocks, int32_t block_size,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, const tq_format* kfmt, const tq_format* vfmt,
+                                           float scale, int32_t num_splits, void* workspace, uint64_t workspace_bytes,
+                                           void* out, tq_dtype out_dtype, float* lse, int32_t* dev_err,
+                                           tq_stream_t stream) {
+  return decode_impl(q, q_dtype, num_seqs, num_queries, num_q_heads, num_kv_heads, k_pages, v_pages, num_blocks,
+                     block_size, block_tables, max_blocks_per_seq, context_lens, kfmt, vfmt, scale, num_splits,
+                     workspace, workspace_bytes, out, out_dtype, lse, dev_err, stream, nullptr);
+}
+
+extern "C" tq_status tq_decode_paged_window(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                                            int32_t num_kv_heads, const uint8_t* k_pages, const uint8_t* v_pages,
+                                            int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                            const tq_format* kfmt, const tq_format* vfmt, const void* win_k,
+                                            const void* win_v, tq_dtype win_dtype, int32_t win_capacity,
+                                            const int32_t* win_lens, float scale, int32_t num_splits,
+                                            void* workspace, uint64_t workspace_bytes, void* out, tq_dtype out_dtype,
+                                            float* lse, int32_t* dev_err, tq_stream_t stream) {
+  if (win_dtype != TQ_BF16)
+    return set_error(TQ_ERR_UNSUPPORTED_FORMAT, "the fused window takes bf16 rows (use tq_decode_dense for f32)");
+  const WinArgs win = {win_k, win_v, win_capacity, win_lens};
+  return decode_impl(q, q_dtype, num_seqs, 1, num_q_heads, num_kv_heads, k_pages, v_pages, num_blocks, block_size,
+                     block_tables, max_blocks_per_seq, context_lens, kfmt, vfmt, scale, num_splits, workspace,
+                     workspace_bytes, out, out_dtype, lse, dev_err, stream, &win);
 }
 
 // ------------------------------------------------------------ no allocation

@@ -314,3 +314,34 @@ def test_qjl_write_alignment_checked_before_launch():
             self.c = cs
     assert _call_write(kf=_F(_qjl_c(f4, proj=0x1008))) == tq.TQ_ERR_VALUE
     assert "aligned" in tq._lib.tq_last_error().decode()
+
+
+def test_fused_window_status_codes_without_launch():
+    """tq_decode_paged_window with stand-in pointers: every call here is
+    refused by host validation or returns before any launch."""
+    s = signs(0, 1, 128)
+    f = tq.Format(128, [4], s)
+    L = tq._lib
+
+    def call(B=2, Hq=8, Hkv=2, kf=None, k=16, v=16, wd=None, cap=4, lens=16, ws=None, wsb=0):
+        kc = f.c if kf is None else kf
+        wd = tq.TQ_BF16 if wd is None else wd
+        return L.tq_decode_paged_window(16, tq.TQ_BF16, B, Hq, Hkv, 16, 16, 10, 16, 16, 4, 16, ctypes.byref(kc),
+                                        ctypes.byref(f.c), k, v, wd, cap, lens, 0.1, 1, ws, wsb, 16, tq.TQ_BF16,
+                                        None, None, None)
+    assert call(wd=tq.TQ_F32) == tq.TQ_ERR_UNSUPPORTED_FORMAT       # f32 windows: tq_decode_dense
+    assert call(Hq=34, Hkv=2) == tq.TQ_ERR_UNSUPPORTED_FORMAT       # 17 q heads per kv head
+    assert "16 q heads" in L.tq_last_error().decode()
+    assert call(cap=-1) == tq.TQ_ERR_VALUE
+    assert call(lens=None) == tq.TQ_ERR_VALUE
+    assert call(k=None) == tq.TQ_ERR_VALUE
+    assert call(k=24) == tq.TQ_ERR_VALUE                             # not 16-byte aligned
+    assert "aligned" in L.tq_last_error().decode()
+    assert call() == tq.TQ_ERR_VALUE                                 # one split still needs the window's slot
+    assert "workspace" in L.tq_last_error().decode()
+    need = tq.workspace_bytes(2, 8, 128, 2)
+    assert need > 0
+    assert call(ws=16, wsb=need - 1) == tq.TQ_ERR_VALUE
+    q3 = _qjl_c(tq.Format(128, [3], s))                              # the separate QJL kernel's layout
+    assert call(kf=q3) == tq.TQ_ERR_UNSUPPORTED_FORMAT
+    assert call(B=0) == tq.TQ_OK
