@@ -121,6 +121,7 @@ struct DecodeParams {
   const int32_t* win_lens;
   int32_t win_on, win_cap, PS;
   float win_scale_log2;   // softmax scale times log2(e)
+  int32_t win_items;   // S * Hkv (sequence, kv head) window items, or 0
   float v_mul;       // 1 / sqrt(m_V), applied once in the epilogue
   uint32_t v_signs[4];
   uint32_t k_signs[4];
@@ -520,7 +521,7 @@ struct Smem {
   int s_next[kWaves];        // per virtual head: next free piece block
   int s_bt[kBtCap];          // block-table entries of the piece's first kBtCap blocks
   int s_cl[64];              // clamped context lengths of sequences 0-63
-  int s_plan[8];             // work split: R, range start and end, first segment
+  int s_plan[10];            // work split: R, range start and end, first segment, window items
 };
 
 template <int D, int KK, int VK>
@@ -557,11 +558,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     {
       const __attribute__((address_space(4))) uint32_t* ka =
           (const __attribute__((address_space(4))) uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
-      static_assert(sizeof(DecodeParams) > 9 * 64 && sizeof(DecodeParams) <= 10 * 64,
-                    "the argument block spans another number of lines than are touched");
-      const uint32_t k0 = ka[0], k1 = ka[16], k2 = ka[32], k3 = ka[48], k4 = ka[64], k5 = ka[80], k6 = ka[96],
-                     k7 = ka[112], k8 = ka[128], k9 = ka[144];
-      asm volatile("" ::"s"(k0), "s"(k1), "s"(k2), "s"(k3), "s"(k4), "s"(k5), "s"(k6), "s"(k7), "s"(k8), "s"(k9));
+      constexpr int kLines = (int)((sizeof(DecodeParams) + 63) / 64);
+      uint32_t kw[kLines];
+#pragma unroll
+      for (int i = 0; i < kLines; ++i) kw[i] = ka[16 * i];   // all issued before the first use waits
+#pragma unroll
+      for (int i = 0; i < kLines; ++i) asm volatile("" ::"s"(kw[i]));
     }
     // context length of sequence `lane` (lanes past the last sequence read 0
     // through the descriptor's range check)
@@ -577,6 +579,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     const int R = range_len(W, p.n_wg, p.max_blocks, p.P);
     int r0 = blockIdx.x * R;
     int r1 = (r0 + R < W) ? r0 + R : W;
+    // window items: an even share for every workgroup, run after its pieces
+    // (a workgroup given only window items streams them latency-bound, far
+    // slower than the pieces' rate, so they are not traded against pieces)
+    const int i0 = (int)((int64_t)blockIdx.x * p.win_items / p.n_wg);
+    const int i1 = (int)((int64_t)(blockIdx.x + 1) * p.win_items / p.n_wg);
     if (p.P == 1) {   // whole segments only: there is no workspace for partials
       r0 = snap_to_segment(p, cl0, lane, r0, W);
       r1 = snap_to_segment(p, cl0, lane, r1, W);
@@ -586,6 +593,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     if (lane == 0) {
       s_plan[0] = R; s_plan[1] = r0; s_plan[2] = r1; s_plan[3] = s0;
       s_plan[4] = grp0; s_plan[5] = off0; s_plan[6] = nb0;
+      s_plan[7] = i0; s_plan[8] = i1;
     }
   } else if (wave == 1) {
     uint32_t x = 0;
@@ -655,11 +663,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
     }
   }
-  // dense window: (sequence, kv head) items blockIdx.x, + n_wg, ... after
-  // the workgroup's pieces, in the LDS of the tables and operands (free by
-  // then), each result to slot P of its rows
+  // dense window: the workgroup's (sequence, kv head) items after its
+  // pieces, in the LDS of the tables and operands (free by then), each
+  // result to slot P of its rows
   auto window_items = [&]() {
-    if (!p.win_on) return;
+    const int i0 = uni(s_plan[7]), i1 = uni(s_plan[8]);
+    if (i0 >= i1) return;
     using W = WinItemCfg<D, 16, kThreads, 128>;
     static_assert(W::BYTES <= (int)(sizeof(sm.lut) + sizeof(sm.xbuf)), "window item larger than its LDS");
     WindowParams wp = {};
@@ -673,10 +682,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     sink.part_lse = p.part_lse;
     sink.PS = p.PS;
     sink.slot = p.P;
-    for (int it = blockIdx.x; it < p.S * p.Hkv; it += p.n_wg) {
-      __syncthreads();   // the workgroup is done with the LDS (pieces or the previous item)
-      window_item_bf16<D, 16, kThreads, 128>(wp, sink, it / p.Hkv, it % p.Hkv, sm.lut, tid);
-    }
+    __syncthreads();   // the workgroup is done with the LDS of its pieces
+    window_items_bf16<D, 16, kThreads, 128, 2>(wp, sink, i0, i1, sm.lut, tid);
   };
   if (r0 >= r1) {  // uniform across the workgroup
     window_items();
@@ -2018,6 +2025,7 @@ tq_status decode_impl(const void* q, tq_dtype q_dtype, int32_t num_seqs, int32_t
   p.Gr = Gr;
   p.rows_ps = num_queries * num_q_heads;
   p.inv_Gr = 1.0f / (float)Gr;
+  p.win_items = win ? num_seqs * num_kv_heads : 0;
   const int64_t units = (int64_t)num_seqs * p.NG * max_blocks_per_seq;
   p.n_wg = (int)(units < cus ? (units > 0 ? units : 1) : cus);
   p.k_tile = tile_bytes_of(kfmt);

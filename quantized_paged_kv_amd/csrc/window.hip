@@ -344,8 +344,8 @@ __global__ __launch_bounds__(kWinThreads) void window_bf16_kernel(WindowParams p
   constexpr int T = (D == 128 && GMAX == 16) ? 128 : 256;
   using C = WinItemCfg<D, GMAX, kWinThreads, T>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::BYTES];
-  window_item_bf16<D, GMAX, kWinThreads, T>(p, WinSink{}, (int)(blockIdx.x / p.Hkv), (int)(blockIdx.x % p.Hkv),
-                                            lds, (int)threadIdx.x);
+  window_items_bf16<D, GMAX, kWinThreads, T, 1>(p, WinSink{}, (int)blockIdx.x, (int)blockIdx.x + 1, lds,
+                                             (int)threadIdx.x);
 }
 
 template <int D>
