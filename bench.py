@@ -59,7 +59,7 @@ def algorithmic_bytes(w, kf, vf):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("decode.hip", "tq_internal.h"):
+    for f in ("decode.hip", "tq_internal.h", "window_item.h"):
         h.update(open(os.path.join(ROOT, "quantized_paged_kv_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

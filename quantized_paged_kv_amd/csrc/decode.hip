@@ -1698,12 +1698,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 // decode mode the decode kernel has marked the rows it wrote out directly
 // (kDoneBits in slot 0) and set the slots past a segment's last piece to
 // -inf, so no segment bookkeeping is redone here.  Every wave reads the lse
-// of slots 0-63 (lane l: slot l) and, at the same time, the o rows of its
-// own 16 slots (wave w: slots 16 w ..), before the slots are known to be live
-// (dead slots hold stale values that get weight 0): with NW = ceil(P / 16)
-// waves (up to 4) a row with up to 64 pieces costs one memory round trip.
-// Slots past 16 NW are read once their lse values are known.  The waves'
-// weighted sums are added in LDS.
+// of slots 0-63 (lane l: slot l).  With one wave (P <= 16) it then reads the
+// o rows of the live slots only.  With NW = ceil(P / 16) > 1 waves (up to 4)
+// each wave reads the o rows of its own 16 slots (wave w: slots 16 w ..)
+// together with the lse, before the slots are known to be live (dead slots
+// hold stale values that get weight 0), so a row with up to 64 pieces costs
+// one memory round trip; slots past 16 NW are read once their lse values
+// are known.  The waves' weighted sums are added in LDS.
 struct MergeParams {
   const float* part_o;
   const float* part_lse;
@@ -1714,6 +1715,11 @@ struct MergeParams {
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void merge_kernel(MergeParams p) {
+  // one wave (P <= 16): the o rows are read once the lse values are in, and
+  // only for live slots (a cut segment's pieces; the rest hold -inf), which
+  // halves the bytes read at the 8B shape for one more short round trip;
+  // more waves: every wave's first 16 o rows are requested with the lse
+  constexpr bool LIVE = NW == 1;
   constexpr int CH = 16;
   __shared__ float red[NW > 1 ? NW - 1 : 1][2 * 64 + 1];
   const int64_t sh = blockIdx.x;
@@ -1723,15 +1729,27 @@ __global__ __launch_bounds__(64 * NW) void merge_kernel(MergeParams p) {
   const float* o_p = p.part_o + sh * (int64_t)P * D;
   const float lf = lane < P ? lse_p[lane] : -INFINITY;
   float ov0[CH][2];
+  if constexpr (!LIVE) {
 #pragma unroll
-  for (int k = 0; k < CH; ++k)
+    for (int k = 0; k < CH; ++k)
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int dim = lane + 64 * r;
-      const int slot = CH * w + k;
-      ov0[k][r] = (slot < P && dim < D) ? o_p[(int64_t)slot * D + dim] : 0.f;
-    }
+      for (int r = 0; r < 2; ++r) {
+        const int dim = lane + 64 * r;
+        const int slot = CH * w + k;
+        ov0[k][r] = (slot < P && dim < D) ? o_p[(int64_t)slot * D + dim] : 0.f;
+      }
+  }
   if (p.decode && (uint32_t)__builtin_amdgcn_readfirstlane(__float_as_uint(lf)) == kDoneBits) return;
+  if constexpr (LIVE) {
+    const uint64_t live = __builtin_amdgcn_ballot_w64(lane < P && lf != -INFINITY);
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int dim = lane + 64 * r;
+        ov0[k][r] = (((live >> k) & 1) && dim < D) ? o_p[(int64_t)k * D + dim] : 0.f;
+      }
+  }
   auto slot_lse = [&](int i) -> float {   // i uniform
     return i < 64 ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lf), i)) : lse_p[i];
   };
