@@ -582,8 +582,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     // window items: an even share for every workgroup, run after its pieces
     // (a workgroup given only window items streams them latency-bound, far
     // slower than the pieces' rate, so they are not traded against pieces)
-    const int i0 = (int)((int64_t)blockIdx.x * p.win_items / p.n_wg);
-    const int i1 = (int)((int64_t)(blockIdx.x + 1) * p.win_items / p.n_wg);
+    // (32-bit: win_items * n_wg < 2^32 by the host's work bound; no
+    // division at all without a window)
+    const int i0 = p.win_items ? (int)(blockIdx.x * (uint32_t)p.win_items / (uint32_t)p.n_wg) : 0;
+    const int i1 = p.win_items ? (int)((blockIdx.x + 1) * (uint32_t)p.win_items / (uint32_t)p.n_wg) : 0;
     if (p.P == 1) {   // whole segments only: there is no workspace for partials
       r0 = snap_to_segment(p, cl0, lane, r0, W);
       r1 = snap_to_segment(p, cl0, lane, r1, W);
@@ -683,1006 +685,1001 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     sink.PS = p.PS;
     sink.slot = p.P;
     __syncthreads();   // the workgroup is done with the LDS of its pieces
-    window_items_bf16<D, 16, kThreads, 128, 2>(wp, sink, i0, i1, sm.lut, tid);
+    window_items_bf16<D, 16, kThreads, 128, 1>(wp, sink, i0, i1, sm.lut, tid);
   };
-  if (r0 >= r1) {  // uniform across the workgroup
-    window_items();
-    TQ_MARK(14);
-    TQ_MARK_VALUE(15, 0);
-    return;
-  }
-
-  auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
-
-  // LDS tables: byte-indexed, two halves of 128 B per entry, built once
-  // (while the first piece's block-table, q and tile loads are in flight).
-  // Thread -> 16 B chunk (16 e + lane & 15) of entry e = 16 e_hi + e_lo:
-  // lane & 15 walks the 256 B of an entry (8 chunks per half), so each
-  // store instruction writes 1 KB contiguous; e_lo is fixed per lane,
-  // e_hi = (wave >> 2) + 4 it.
-  auto build_tables = [&]() {
-    const int h = (lane >> 3) & 1;
-    const int e_lo = (lane >> 4) | ((wave & 3) << 2);
-    const int wh = wave >> 2;
-    const uint32_t sh = (uint32_t)(wh & 1) * 16u;
-    const int kind0 = uni(p.half_kind[0]), kind1 = uni(p.half_kind[1]);   // scalar reads
-    const int kind = h ? kind1 : kind0;
-    const uint4 r03 = *reinterpret_cast<const uint4*>(s_par + 8 * h);
-    const uint4 r47 = *reinterpret_cast<const uint4*>(s_par + 8 * h + 4);
-    const uint32_t cw[8] = {r03.x, r03.y, r03.z, r03.w, r47.x, r47.y, r47.z, r47.w};
-    const uint32_t lo_n = cb_half(h, e_lo);
-    const uint32_t ev = cb_half(h, e_lo & 3) | (cb_half(h, e_lo >> 2) << 16);
-    const uint32_t c2 = (((wh >> 1) ? cw[1] : cw[0]) >> sh) & 0xFFFFu;   // cb[e_hi & 3] = cb[wh]
-    uint4* dst = reinterpret_cast<uint4*>(lds) + (lane & 15) + 16 * e_lo + 256 * wh;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      // nibble table: (cb[e & 15], cb[e >> 4]);
-      // crumb table: (cb[e & 3], cb[(e >> 2) & 3]), (cb[(e >> 4) & 3], cb[e >> 6])
-      const uint32_t hiw = (wh >> 1) ? cw[2 * it + 1] : cw[2 * it];
-      const uint32_t v4 = lo_n | (((hiw >> sh) & 0xFFFFu) << 16);
-      const uint32_t c3 = (cw[it >> 1] >> (16 * (it & 1))) & 0xFFFFu;
-      const uint32_t od = c2 | (c3 << 16);
-      const uint32_t x0 = kind == 4 ? v4 : (kind == 2 ? ev : 0u);
-      const uint32_t x1 = kind == 4 ? v4 : (kind == 2 ? od : 0u);
-      dst[1024 * it] = uint4{x0, x1, x0, x1};
-    }
-    if constexpr (C::PAIR3) {
-      for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
-        const int e = c >> 2;
-        const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t hi = (s_par[16 + ((e >> 3) >> 1)] >> (16 * ((e >> 3) & 1))) & 0xFFFFu;
-        const uint32_t v = lo | (hi << 16);
-        reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
-      }
-    }
-  };
-
-  // ---- per-lane roles
-  const int j = lane & 15;          // MFMA column: q head j & 7, high (j < 8) or low part
-  const int a = lane >> 4;          // token group: tokens a, a+4, a+8, a+12 of a block
-  const int gq = j & 7;
-  const bool lo_part = j >= 8;
-  const uint32_t off4_k = (uint32_t)(lane & 31) * 4u;                      // K nibble table, half 0
-  const uint32_t off2_k = (uint32_t)(lane & 15) * 8u;                      // K crumb table, half 0
-  const uint32_t off_v4 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 31) * 4u;
-  const uint32_t off_v2 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 15) * 8u;
-  const uint32_t off3 = (uint32_t)kLutBytes + (uint32_t)(lane & 15) * 4u;
-  const int tokK = (j >> 2) + 4 * (j & 3);   // token of this lane's K row: sigma(j)
-  // per-lane byte offsets inside a K / V tile: k_off the lane's bytes of the
-  // one group (K4, K2) or of the 4-bit group (4+3), or the aligned dword that
-  // holds its bytes of the 2-bit group (3+2); klo_off the aligned 8-B window
-  // that holds its bytes of the 3-bit group (two-group formats)
-  constexpr int KLANE = C::KB == K4 ? D / 8 : D / 16;
-  constexpr int G3_AT = C::KB == KM32 ? 0 : D / 4;   // first byte of the 3-bit group in a row
-  const uint32_t k_off = C::KB == KM32 ? (uint32_t)((tokK * C::KROW + 3 * D / 16 + (D / 32) * a) & ~3)
-                                    : (uint32_t)(tokK * C::KROW + KLANE * a);
-  const uint32_t klo_off = (uint32_t)((tokK * C::KROW + G3_AT + (3 * D / 64) * a) & ~3);
-  const uint32_t n_off = (uint32_t)(8 * a);   // this lane's 4 norms, after the tile's norm offset
-  // QJL: the aligned dword holding the sign bytes NQK a .. NQK a + NQK - 1 of
-  // its K row (sketch output 32 a + 8 t + e of MFMA t is bit e of byte 4 a +
-  // t; d = 64: 16 a + 8 t + e, byte 2 a + t), and the one holding the
-  // residual norm of the row's token (norm slot j) for the group of those
-  // outputs, (a NGK) / 4
-  const uint32_t sg_off = (uint32_t)(tokK * C::KROW + C::KMSE + ((NQK * a) & ~3));
-  const uint32_t gm_off = (uint32_t)(C::KRN + 2 * (16 * ((a * C::NGK) >> 2) + (j & ~1)));
-  // this lane's run of the V plane (two groups: its run of each sub-plane,
-  // group 1's sub-plane after group 0's 16 (D / 2) VB0 / 8 bytes)
-  const int vrun = C::OCT * (lane >> 4) + (lane & 15) % C::OCT;
-  const uint32_t v_off = C::MIXED_V ? (uint32_t)(vrun * 4 * C::VB0) : (uint32_t)(lane * 4 * C::VLANE);
-  const uint32_t v_off1 = (uint32_t)(16 * ((D / 2) * C::VB0 / 8) + vrun * 4 * C::VB1);
-  const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
-  const int64_t v_blk_stride = (int64_t)p.Hkv * p.v_tile;
-  const int cap = p.max_blocks * 16;
-  // wave -> (virtual head of the group, part): the NPW waves of a virtual
-  // head share its blocks; virtual head vh is column group cg of kv head hl
-  const int HG = p.HG, CG = p.CG, VH = p.VH;
-  const int NPW = kWaves / VH;
-  const int vh = uni(head_of_wave(wave, VH));
-  const int part = uni(part_of_wave(wave, VH));
-  const int hl = uni(vh / CG);
-  const int cg = uni(vh - hl * CG);
-  half8_t* const qv_all = reinterpret_cast<half8_t*>(xbuf);            // [vh][t][lane]
-  float* const slots = xbuf;                                           // [wave][g] rows of DS floats
-
-  // ---- walk the pieces of this workgroup's range
-  int s = uni(s_plan[3]), grp = uni(s_plan[4]), off = uni(s_plan[5]), nb_s = uni(s_plan[6]);
-  int pos = r0;
-  bool first = true;
-  bool tables_built = false;
   int n_done = 0;   // pieces this workgroup has run (phase trace)
-  while (pos < r1) {
-    const int vb0 = pos - off + p.seg_cost;   // position of the segment's block 0
-    const int b0 = off > p.seg_cost ? off - p.seg_cost : 0;
-    const int b1 = (r1 - vb0 < nb_s) ? r1 - vb0 : nb_s;
-    if (b1 > b0) {   // the range holds blocks of this segment
-    // one piece: the final output is written here (always so when P == 1)
-    // with a window every row is merged: a whole segment writes slot 0
-    const bool whole = !p.win_on && (p.P == 1 || (vb0 / R) == ((vb0 + nb_s - 1) / R));
-    const int piece = p.P == 1 ? 0 : (int)blockIdx.x - vb0 / R;
-    const int n_pieces = p.P == 1 ? 1 : (vb0 + nb_s - 1) / R - vb0 / R + 1;
-      const int ctx = seq_len(p, s_cl, s);
-      // causal lengths: the sequence's last NQ cached tokens are the queries'
-      // own, query i sees ctx - (NQ - 1 - i) of them; ctx_all is what every
-      // query sees, ctx_col this lane's column's (columns past G: ctx)
-      const int ctx_all = ctx - (p.NQ - 1);
-      const int qi_col = (int)(((float)(8 * cg + gq) + 0.5f) * p.inv_Gr);
-      const int ctx_col = qi_col < p.NQ ? ctx - (p.NQ - 1 - qi_col) : ctx;
-      const int kvh = grp * HG + hl;   // this wave's kv head
-      const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
-      const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
-      const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
+  if (r0 < r1) {  // uniform across the workgroup; else the window items only
+    auto cb_half = [&](int h, int i) -> uint32_t { return (s_par[8 * h + (i >> 1)] >> (16 * (i & 1))) & 0xFFFFu; };
 
-      if (!first) __syncthreads();   // the previous piece's states have been read
-      first = false;
-      TQ_MARK(2 + 4 * n_done);
-
-      // -------- blocks of the piece are handed out per kv head: part q of a
-      // head starts with piece blocks q, q + NPW and q + 2 NPW, then takes the
-      // next free index from the head's LDS counter, so parts that run ahead
-      // take more blocks and all finish together.  The HG heads of the group
-      // read the HG adjacent tiles of each physical block at about the same
-      // time.  The piece's block-table entries are staged in LDS (the first
-      // kBtCap of them; later ones are read from memory), so a block costs
-      // index (LDS atomic) -> entry (LDS read) -> tile loads; while a tile is
-      // computed the next two tiles are in flight.
-      const int n = b1 - b0;   // blocks of the piece, >= 1
-      if (tid < kWaves) s_next[tid] = 3 * NPW;
-      const __amdgpu_buffer_rsrc_t btr = tile_rsrc(reinterpret_cast<const uint8_t*>(bt_row), 4 * p.max_blocks);
-      auto bt_load = [&](int idx) -> int {   // entry of piece block idx (block b0 when idx >= n)
-        return (int)__builtin_amdgcn_raw_buffer_load_b32(btr, 0u, 4 * (b0 + (idx < n ? idx : 0)), 0);
-      };
-      constexpr int NBT = kBtCap / kThreads;
-      int btv[NBT];
-#pragma unroll
-      for (int i = 0; i < NBT; ++i) {
-        const int e = tid + kThreads * i;
-        btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
+    // LDS tables: byte-indexed, two halves of 128 B per entry, built once
+    // (while the first piece's block-table, q and tile loads are in flight).
+    // Thread -> 16 B chunk (16 e + lane & 15) of entry e = 16 e_hi + e_lo:
+    // lane & 15 walks the 256 B of an entry (8 chunks per half), so each
+    // store instruction writes 1 KB contiguous; e_lo is fixed per lane,
+    // e_hi = (wave >> 2) + 4 it.
+    auto build_tables = [&]() {
+      const int h = (lane >> 3) & 1;
+      const int e_lo = (lane >> 4) | ((wave & 3) << 2);
+      const int wh = wave >> 2;
+      const uint32_t sh = (uint32_t)(wh & 1) * 16u;
+      const int kind0 = uni(p.half_kind[0]), kind1 = uni(p.half_kind[1]);   // scalar reads
+      const int kind = h ? kind1 : kind0;
+      const uint4 r03 = *reinterpret_cast<const uint4*>(s_par + 8 * h);
+      const uint4 r47 = *reinterpret_cast<const uint4*>(s_par + 8 * h + 4);
+      const uint32_t cw[8] = {r03.x, r03.y, r03.z, r03.w, r47.x, r47.y, r47.z, r47.w};
+      const uint32_t lo_n = cb_half(h, e_lo);
+      const uint32_t ev = cb_half(h, e_lo & 3) | (cb_half(h, e_lo >> 2) << 16);
+      const uint32_t c2 = (((wh >> 1) ? cw[1] : cw[0]) >> sh) & 0xFFFFu;   // cb[e_hi & 3] = cb[wh]
+      uint4* dst = reinterpret_cast<uint4*>(lds) + (lane & 15) + 16 * e_lo + 256 * wh;
+  #pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        // nibble table: (cb[e & 15], cb[e >> 4]);
+        // crumb table: (cb[e & 3], cb[(e >> 2) & 3]), (cb[(e >> 4) & 3], cb[e >> 6])
+        const uint32_t hiw = (wh >> 1) ? cw[2 * it + 1] : cw[2 * it];
+        const uint32_t v4 = lo_n | (((hiw >> sh) & 0xFFFFu) << 16);
+        const uint32_t c3 = (cw[it >> 1] >> (16 * (it & 1))) & 0xFFFFu;
+        const uint32_t od = c2 | (c3 << 16);
+        const uint32_t x0 = kind == 4 ? v4 : (kind == 2 ? ev : 0u);
+        const uint32_t x1 = kind == 4 ? v4 : (kind == 2 ? od : 0u);
+        dst[1024 * it] = uint4{x0, x1, x0, x1};
       }
-      constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per column
-      const int ln = fresh_lane();
-      const int g8 = ln >> 3, l8 = ln & 7;
-      const int colq = 8 * cg + g8;           // this lane's column in the rotation
-      const bool q_live = colq < p.G;
-      // raw q words of this lane's PER channels (bf16: two per word, the upper
-      // half of qw unused); one load shape for both dtypes, bytes past the q
-      // tensor read as zero through the descriptor's range check
-      uint32_t qw[PER];
-      {   // issued by every wave so that all paths carry the same loads and
-          // later waits count exactly; parts > 0 discard them and read
-          // through an empty range (no memory access): on a long context
-          // hundreds of workgroups read the same few q rows at once
-        const int esz = p.q_f32 ? 4 : 2;
-        const int head0 = uni((int)(((int64_t)s * p.rows_ps + kvh * p.Gr) * D * esz));   // query 0, first q head
-        int qrow = 0;   // this lane's (query, q head) column: rows past head0
-        if (q_live) {
-          const int qi = (int)(((float)colq + 0.5f) * p.inv_Gr);
-          qrow = qi * p.Hq + (colq - qi * p.Gr);
-        }
-        const uint32_t lane_off = (uint32_t)((qrow * D + l8 * PER) * esz);
-        const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), part == 0 ? p.q_bytes : 0);
-#pragma unroll
-        for (int i = 0; i < PER / 4; ++i) {
-          const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
-          qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
+      if constexpr (C::PAIR3) {
+        for (int c = tid; c < kLut3Bytes / 16; c += kThreads) {
+          const int e = c >> 2;
+          const uint32_t lo = (s_par[16 + ((e & 7) >> 1)] >> (16 * (e & 1))) & 0xFFFFu;
+          const uint32_t hi = (s_par[16 + ((e >> 3) >> 1)] >> (16 * ((e >> 3) & 1))) & 0xFFFFu;
+          const uint32_t v = lo | (hi << 16);
+          reinterpret_cast<uint4*>(lds + kLutBytes)[c] = uint4{v, v, v, v};
         }
       }
-      // QJL: wave w computes output tile ot_w = w % (D / 16) of the projected
-      // rows (16 outputs) for virtual heads w / (D / 16), + 16 / (D / 16), ...;
-      // its S values (the same for all of them) are requested here, before
-      // the tiles, so that waiting for them does not wait for the tiles
-      constexpr int QOT = D / 16, QM = D / C::NGK, QKC = QM / 32;
-      const int ot_w = wave % QOT;
-      float4 spf[C::QJ ? 2 * QKC : 1];
-      if constexpr (C::QJ) {
-        const int lp = fresh_lane();
-        const float* srow = p.proj + ((int64_t)(16 * ot_w + (lp & 15)) * QM + 8 * (lp >> 4));
-#pragma unroll
-        for (int kc = 0; kc < QKC; ++kc) {
-          spf[2 * kc] = *reinterpret_cast<const float4*>(srow + 32 * kc);
-          spf[2 * kc + 1] = *reinterpret_cast<const float4*>(srow + 32 * kc + 4);
+    };
+
+    // ---- per-lane roles
+    const int j = lane & 15;          // MFMA column: q head j & 7, high (j < 8) or low part
+    const int a = lane >> 4;          // token group: tokens a, a+4, a+8, a+12 of a block
+    const int gq = j & 7;
+    const bool lo_part = j >= 8;
+    const uint32_t off4_k = (uint32_t)(lane & 31) * 4u;                      // K nibble table, half 0
+    const uint32_t off2_k = (uint32_t)(lane & 15) * 8u;                      // K crumb table, half 0
+    const uint32_t off_v4 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 31) * 4u;
+    const uint32_t off_v2 = (uint32_t)p.v_half * 128u + (uint32_t)(lane & 15) * 8u;
+    const uint32_t off3 = (uint32_t)kLutBytes + (uint32_t)(lane & 15) * 4u;
+    const int tokK = (j >> 2) + 4 * (j & 3);   // token of this lane's K row: sigma(j)
+    // per-lane byte offsets inside a K / V tile: k_off the lane's bytes of the
+    // one group (K4, K2) or of the 4-bit group (4+3), or the aligned dword that
+    // holds its bytes of the 2-bit group (3+2); klo_off the aligned 8-B window
+    // that holds its bytes of the 3-bit group (two-group formats)
+    constexpr int KLANE = C::KB == K4 ? D / 8 : D / 16;
+    constexpr int G3_AT = C::KB == KM32 ? 0 : D / 4;   // first byte of the 3-bit group in a row
+    const uint32_t k_off = C::KB == KM32 ? (uint32_t)((tokK * C::KROW + 3 * D / 16 + (D / 32) * a) & ~3)
+                                      : (uint32_t)(tokK * C::KROW + KLANE * a);
+    const uint32_t klo_off = (uint32_t)((tokK * C::KROW + G3_AT + (3 * D / 64) * a) & ~3);
+    const uint32_t n_off = (uint32_t)(8 * a);   // this lane's 4 norms, after the tile's norm offset
+    // QJL: the aligned dword holding the sign bytes NQK a .. NQK a + NQK - 1 of
+    // its K row (sketch output 32 a + 8 t + e of MFMA t is bit e of byte 4 a +
+    // t; d = 64: 16 a + 8 t + e, byte 2 a + t), and the one holding the
+    // residual norm of the row's token (norm slot j) for the group of those
+    // outputs, (a NGK) / 4
+    const uint32_t sg_off = (uint32_t)(tokK * C::KROW + C::KMSE + ((NQK * a) & ~3));
+    const uint32_t gm_off = (uint32_t)(C::KRN + 2 * (16 * ((a * C::NGK) >> 2) + (j & ~1)));
+    // this lane's run of the V plane (two groups: its run of each sub-plane,
+    // group 1's sub-plane after group 0's 16 (D / 2) VB0 / 8 bytes)
+    const int vrun = C::OCT * (lane >> 4) + (lane & 15) % C::OCT;
+    const uint32_t v_off = C::MIXED_V ? (uint32_t)(vrun * 4 * C::VB0) : (uint32_t)(lane * 4 * C::VLANE);
+    const uint32_t v_off1 = (uint32_t)(16 * ((D / 2) * C::VB0 / 8) + vrun * 4 * C::VB1);
+    const int64_t k_blk_stride = (int64_t)p.Hkv * p.k_tile;
+    const int64_t v_blk_stride = (int64_t)p.Hkv * p.v_tile;
+    const int cap = p.max_blocks * 16;
+    // wave -> (virtual head of the group, part): the NPW waves of a virtual
+    // head share its blocks; virtual head vh is column group cg of kv head hl
+    const int HG = p.HG, CG = p.CG, VH = p.VH;
+    const int NPW = kWaves / VH;
+    const int vh = uni(head_of_wave(wave, VH));
+    const int part = uni(part_of_wave(wave, VH));
+    const int hl = uni(vh / CG);
+    const int cg = uni(vh - hl * CG);
+    half8_t* const qv_all = reinterpret_cast<half8_t*>(xbuf);            // [vh][t][lane]
+    float* const slots = xbuf;                                           // [wave][g] rows of DS floats
+
+    // ---- walk the pieces of this workgroup's range
+    int s = uni(s_plan[3]), grp = uni(s_plan[4]), off = uni(s_plan[5]), nb_s = uni(s_plan[6]);
+    int pos = r0;
+    bool first = true;
+    bool tables_built = false;
+    while (pos < r1) {
+      const int vb0 = pos - off + p.seg_cost;   // position of the segment's block 0
+      const int b0 = off > p.seg_cost ? off - p.seg_cost : 0;
+      const int b1 = (r1 - vb0 < nb_s) ? r1 - vb0 : nb_s;
+      if (b1 > b0) {   // the range holds blocks of this segment
+      // one piece: the final output is written here (always so when P == 1)
+      // with a window every row is merged: a whole segment writes slot 0
+      const bool whole = !p.win_on && (p.P == 1 || (vb0 / R) == ((vb0 + nb_s - 1) / R));
+      const int piece = p.P == 1 ? 0 : (int)blockIdx.x - vb0 / R;
+      const int n_pieces = p.P == 1 ? 1 : (vb0 + nb_s - 1) / R - vb0 / R + 1;
+        const int ctx = seq_len(p, s_cl, s);
+        // causal lengths: the sequence's last NQ cached tokens are the queries'
+        // own, query i sees ctx - (NQ - 1 - i) of them; ctx_all is what every
+        // query sees, ctx_col this lane's column's (columns past G: ctx)
+        const int ctx_all = ctx - (p.NQ - 1);
+        const int qi_col = (int)(((float)(8 * cg + gq) + 0.5f) * p.inv_Gr);
+        const int ctx_col = qi_col < p.NQ ? ctx - (p.NQ - 1 - qi_col) : ctx;
+        const int kvh = grp * HG + hl;   // this wave's kv head
+        const uint8_t* k_head = p.k_pages + (int64_t)kvh * p.k_tile;
+        const uint8_t* v_head = p.v_pages + (int64_t)kvh * p.v_tile;
+        const int32_t* bt_row = p.block_tables + (int64_t)s * p.max_blocks;
+
+        if (!first) __syncthreads();   // the previous piece's states have been read
+        first = false;
+        TQ_MARK(2 + 4 * n_done);
+
+        // -------- blocks of the piece are handed out per kv head: part q of a
+        // head starts with piece blocks q, q + NPW and q + 2 NPW, then takes the
+        // next free index from the head's LDS counter, so parts that run ahead
+        // take more blocks and all finish together.  The HG heads of the group
+        // read the HG adjacent tiles of each physical block at about the same
+        // time.  The piece's block-table entries are staged in LDS (the first
+        // kBtCap of them; later ones are read from memory), so a block costs
+        // index (LDS atomic) -> entry (LDS read) -> tile loads; while a tile is
+        // computed the next two tiles are in flight.
+        const int n = b1 - b0;   // blocks of the piece, >= 1
+        if (tid < kWaves) s_next[tid] = 3 * NPW;
+        const __amdgpu_buffer_rsrc_t btr = tile_rsrc(reinterpret_cast<const uint8_t*>(bt_row), 4 * p.max_blocks);
+        auto bt_load = [&](int idx) -> int {   // entry of piece block idx (block b0 when idx >= n)
+          return (int)__builtin_amdgcn_raw_buffer_load_b32(btr, 0u, 4 * (b0 + (idx < n ? idx : 0)), 0);
+        };
+        constexpr int NBT = kBtCap / kThreads;
+        int btv[NBT];
+  #pragma unroll
+        for (int i = 0; i < NBT; ++i) {
+          const int e = tid + kThreads * i;
+          btv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(btr, (uint32_t)(4 * (e < n ? e : 0)), 4 * b0, 0);
         }
-      }
-      int idx_c = part, idx_1 = part + NPW, idx_2 = part + 2 * NPW;
-      const int v0 = bt_load(idx_c);
-      const int v1 = bt_load(idx_1);
-      if (!tables_built) {   // while the loads above are in flight
-        build_tables();
-        tables_built = true;
-      }
+        constexpr int PER = D / 8;              // q channels per lane in the rotation, 8 lanes per column
+        const int ln = fresh_lane();
+        const int g8 = ln >> 3, l8 = ln & 7;
+        const int colq = 8 * cg + g8;           // this lane's column in the rotation
+        const bool q_live = colq < p.G;
+        // raw q words of this lane's PER channels (bf16: two per word, the upper
+        // half of qw unused); one load shape for both dtypes, bytes past the q
+        // tensor read as zero through the descriptor's range check
+        uint32_t qw[PER];
+        {   // issued by every wave so that all paths carry the same loads and
+            // later waits count exactly; parts > 0 discard them and read
+            // through an empty range (no memory access): on a long context
+            // hundreds of workgroups read the same few q rows at once
+          const int esz = p.q_f32 ? 4 : 2;
+          const int head0 = uni((int)(((int64_t)s * p.rows_ps + kvh * p.Gr) * D * esz));   // query 0, first q head
+          int qrow = 0;   // this lane's (query, q head) column: rows past head0
+          if (q_live) {
+            const int qi = (int)(((float)colq + 0.5f) * p.inv_Gr);
+            qrow = qi * p.Hq + (colq - qi * p.Gr);
+          }
+          const uint32_t lane_off = (uint32_t)((qrow * D + l8 * PER) * esz);
+          const __amdgpu_buffer_rsrc_t qr = tile_rsrc(static_cast<const uint8_t*>(p.q), part == 0 ? p.q_bytes : 0);
+  #pragma unroll
+          for (int i = 0; i < PER / 4; ++i) {
+            const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(qr, lane_off + 16 * i, head0, 0);
+            qw[4 * i] = t[0]; qw[4 * i + 1] = t[1]; qw[4 * i + 2] = t[2]; qw[4 * i + 3] = t[3];
+          }
+        }
+        // QJL: wave w computes output tile ot_w = w % (D / 16) of the projected
+        // rows (16 outputs) for virtual heads w / (D / 16), + 16 / (D / 16), ...;
+        // its S values (the same for all of them) are requested here, before
+        // the tiles, so that waiting for them does not wait for the tiles
+        constexpr int QOT = D / 16, QM = D / C::NGK, QKC = QM / 32;
+        const int ot_w = wave % QOT;
+        float4 spf[C::QJ ? 2 * QKC : 1];
+        if constexpr (C::QJ) {
+          const int lp = fresh_lane();
+          const float* srow = p.proj + ((int64_t)(16 * ot_w + (lp & 15)) * QM + 8 * (lp >> 4));
+  #pragma unroll
+          for (int kc = 0; kc < QKC; ++kc) {
+            spf[2 * kc] = *reinterpret_cast<const float4*>(srow + 32 * kc);
+            spf[2 * kc + 1] = *reinterpret_cast<const float4*>(srow + 32 * kc + 4);
+          }
+        }
+        int idx_c = part, idx_1 = part + NPW, idx_2 = part + 2 * NPW;
+        const int v0 = bt_load(idx_c);
+        const int v1 = bt_load(idx_1);
+        if (!tables_built) {   // while the loads above are in flight
+          build_tables();
+          tables_built = true;
+        }
 
-      // -------- block-table entry -> scalar byte offsets of the block's tiles
-      // in the pools (whose bytes, less than 4 GiB each, one descriptor per
-      // wave covers); entries outside the pool are reported and their block
-      // skipped (read as block 0)
-      const __amdgpu_buffer_rsrc_t kt = tile_rsrc(k_head, (int)(p.k_span - (uint32_t)kvh * (uint32_t)p.k_tile));
-      const __amdgpu_buffer_rsrc_t vt = tile_rsrc(v_head, (int)(p.v_span - (uint32_t)kvh * (uint32_t)p.v_tile));
-      uint32_t kb, vb;
-      auto entry = [&](int v, int idx, bool& ok) {
-        const uint32_t raw = (uint32_t)__builtin_amdgcn_readfirstlane(v);
-        const bool live = idx < n;
-        const bool bad = live && raw >= (uint32_t)p.num_blocks;
-        if (bad && lane == 0) record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + idx);
-        const uint32_t ph = (uint32_t)uni(bad ? 0 : (int)raw);
-        ok = live && !bad;
-        kb = ph * (uint32_t)k_blk_stride;
-        vb = ph * (uint32_t)v_blk_stride;
-      };
-      auto bt_at = [&](int idx) -> int {   // entry value of piece block idx (any lane)
-        if (idx >= n) return 0;
-        if (idx < kBtCap) return s_bt[idx];
-        const int v = bt_load(idx);        // long piece: read from memory (latency exposed)
-        return __builtin_amdgcn_readfirstlane(v);
-      };
-      auto grab = [&]() -> int {   // next free piece block of this head (valid in lane 0)
-        int g = 0;
-        if (lane == 0) g = atomicAdd(&s_next[vh], 1);
-        return g;
-      };
-      Tile<D, KK, VK> A, B, C3;
-      bool ok_c, ok_1;
-      // the first two tiles go out now, so that their latency overlaps the
-      // q rotation; with the QJL stage they go out after the projection,
-      // whose loads would otherwise wait for them (loads complete in order)
-      auto first_tiles = [&]() {
-        entry(v0, idx_c, ok_c);
-        load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
-        entry(v1, idx_1, ok_1);
-        load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
-      };
-      if constexpr (!C::QJ) first_tiles();
-#pragma unroll
-      for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
+        // -------- block-table entry -> scalar byte offsets of the block's tiles
+        // in the pools (whose bytes, less than 4 GiB each, one descriptor per
+        // wave covers); entries outside the pool are reported and their block
+        // skipped (read as block 0)
+        const __amdgpu_buffer_rsrc_t kt = tile_rsrc(k_head, (int)(p.k_span - (uint32_t)kvh * (uint32_t)p.k_tile));
+        const __amdgpu_buffer_rsrc_t vt = tile_rsrc(v_head, (int)(p.v_span - (uint32_t)kvh * (uint32_t)p.v_tile));
+        uint32_t kb, vb;
+        auto entry = [&](int v, int idx, bool& ok) {
+          const uint32_t raw = (uint32_t)__builtin_amdgcn_readfirstlane(v);
+          const bool live = idx < n;
+          const bool bad = live && raw >= (uint32_t)p.num_blocks;
+          if (bad && lane == 0) record_error(p.dev_err, TQ_ERR_INDEX, s * p.max_blocks + b0 + idx);
+          const uint32_t ph = (uint32_t)uni(bad ? 0 : (int)raw);
+          ok = live && !bad;
+          kb = ph * (uint32_t)k_blk_stride;
+          vb = ph * (uint32_t)v_blk_stride;
+        };
+        auto bt_at = [&](int idx) -> int {   // entry value of piece block idx (any lane)
+          if (idx >= n) return 0;
+          if (idx < kBtCap) return s_bt[idx];
+          const int v = bt_load(idx);        // long piece: read from memory (latency exposed)
+          return __builtin_amdgcn_readfirstlane(v);
+        };
+        auto grab = [&]() -> int {   // next free piece block of this head (valid in lane 0)
+          int g = 0;
+          if (lane == 0) g = atomicAdd(&s_next[vh], 1);
+          return g;
+        };
+        Tile<D, KK, VK> A, B, C3;
+        bool ok_c, ok_1;
+        // the first two tiles go out now, so that their latency overlaps the
+        // q rotation; with the QJL stage they go out after the projection,
+        // whose loads would otherwise wait for them (loads complete in order)
+        auto first_tiles = [&]() {
+          entry(v0, idx_c, ok_c);
+          load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
+          entry(v1, idx_1, ok_1);
+          load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
+        };
+        if constexpr (!C::QJ) first_tiles();
+  #pragma unroll
+        for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
 
-      // -------- part 0 of each virtual head: rotate its 8 q rows once (row g
-      // of the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
-      // operands: the scaled rotated q split into an fp16 high part (lanes
-      // j < 8) and the fp16 rounding of the remainder (lanes j >= 8).  The
-      // rows are staged in the virtual head's own operand area (8 rows of D
-      // floats: its size), which the operands overwrite once every lane has
-      // read its values.
-      if (part == 0) {
-        float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
-        {
-          float x[PER];
-          if (p.q_f32) {
-#pragma unroll
-            for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
-          } else {
-#pragma unroll
-            for (int k = 0; k < PER / 2; ++k) {
-              x[2 * k] = __uint_as_float(qw[k] << 16);
-              x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
-            }
-          }
-          const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
-#pragma unroll
-          for (int e = 0; e < PER; ++e) {
-            if ((sw >> e) & 1u) x[e] = -x[e];
-            if (!q_live) x[e] = 0.f;
-          }
-#pragma unroll
-          for (int h = 1; h < PER; h <<= 1) {
-#pragma unroll
-            for (int e = 0; e < PER; ++e)
-              if ((e & h) == 0) {
-                const float a0 = x[e], b0v = x[e + h];
-                x[e] = a0 + b0v;
-                x[e + h] = a0 - b0v;
-              }
-          }
-          // the 3 stages across the 8 lanes of the row go through LDS: the
-          // row is written in channel order, then lane l8 takes channels
-          // PER k + PH l8 + m (k < 8, m < PH) and runs those stages in its
-          // registers
-          constexpr int PH = PER / 8;
-          float* qrow = stage + g8 * D;
-#pragma unroll
-          for (int i = 0; i < PER / 4; ++i)
-            *reinterpret_cast<float4*>(qrow + l8 * PER + 4 * i) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
-          // the lanes of a row exchange values through LDS: a wave-scope
-          // fence orders the writes above before the reads below
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          float y[8 * PH];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int c = PER * k + PH * l8;
-            if constexpr (PH == 2) {
-              const float2 f = *reinterpret_cast<const float2*>(qrow + c);
-              y[2 * k] = f.x;
-              y[2 * k + 1] = f.y;
+        // -------- part 0 of each virtual head: rotate its 8 q rows once (row g
+        // of the rotated q is H (s_K * q_g), unnormalised) and build its q.K B
+        // operands: the scaled rotated q split into an fp16 high part (lanes
+        // j < 8) and the fp16 rounding of the remainder (lanes j >= 8).  The
+        // rows are staged in the virtual head's own operand area (8 rows of D
+        // floats: its size), which the operands overwrite once every lane has
+        // read its values.
+        if (part == 0) {
+          float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
+          {
+            float x[PER];
+            if (p.q_f32) {
+  #pragma unroll
+              for (int e = 0; e < PER; ++e) x[e] = __uint_as_float(qw[e]);
             } else {
-              y[k] = qrow[c];
+  #pragma unroll
+              for (int k = 0; k < PER / 2; ++k) {
+                x[2 * k] = __uint_as_float(qw[k] << 16);
+                x[2 * k + 1] = __uint_as_float(qw[k] & 0xFFFF0000u);
+              }
+            }
+            const uint32_t sw = s_par[20 + ((l8 * PER) >> 5)] >> ((l8 * PER) & 31);
+  #pragma unroll
+            for (int e = 0; e < PER; ++e) {
+              if ((sw >> e) & 1u) x[e] = -x[e];
+              if (!q_live) x[e] = 0.f;
+            }
+  #pragma unroll
+            for (int h = 1; h < PER; h <<= 1) {
+  #pragma unroll
+              for (int e = 0; e < PER; ++e)
+                if ((e & h) == 0) {
+                  const float a0 = x[e], b0v = x[e + h];
+                  x[e] = a0 + b0v;
+                  x[e + h] = a0 - b0v;
+                }
+            }
+            // the 3 stages across the 8 lanes of the row go through LDS: the
+            // row is written in channel order, then lane l8 takes channels
+            // PER k + PH l8 + m (k < 8, m < PH) and runs those stages in its
+            // registers
+            constexpr int PH = PER / 8;
+            float* qrow = stage + g8 * D;
+  #pragma unroll
+            for (int i = 0; i < PER / 4; ++i)
+              *reinterpret_cast<float4*>(qrow + l8 * PER + 4 * i) = float4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+            // the lanes of a row exchange values through LDS: a wave-scope
+            // fence orders the writes above before the reads below
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            float y[8 * PH];
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int c = PER * k + PH * l8;
+              if constexpr (PH == 2) {
+                const float2 f = *reinterpret_cast<const float2*>(qrow + c);
+                y[2 * k] = f.x;
+                y[2 * k + 1] = f.y;
+              } else {
+                y[k] = qrow[c];
+              }
+            }
+  #pragma unroll
+            for (int h = PH; h < 8 * PH; h <<= 1) {
+  #pragma unroll
+              for (int e = 0; e < 8 * PH; ++e)
+                if ((e & h) == 0) {
+                  const float a0 = y[e], b0v = y[e + h];
+                  y[e] = a0 + b0v;
+                  y[e + h] = a0 - b0v;
+                }
+            }
+            float amax = 0.f;
+  #pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int c = PER * k + PH * l8;
+              if constexpr (PH == 2) *reinterpret_cast<float2*>(qrow + c) = float2{y[2 * k], y[2 * k + 1]};
+              else qrow[c] = y[k];
+            }
+  #pragma unroll
+            for (int e = 0; e < 8 * PH; ++e) amax = fmaxf(amax, fabsf(y[e]));
+            amax = fmaxf(amax, lane_xor<1>(amax, ln));
+            amax = fmaxf(amax, lane_xor<2>(amax, ln));
+            amax = fmaxf(amax, lane_xor<4>(amax, ln));
+            int ex = 0;
+            if (amax > 0.f) frexpf(amax, &ex);
+            if (l8 == 0) s_qexp[8 * vh + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
+          }
+        }
+        if constexpr (C::QJ) {
+          // QJL: the projected rows u_g = S_g q_g of every virtual head (q_g:
+          // the rotated row scaled by 2^(15-ex), group g's channels in listed
+          // order) on the matrix cores, in 16-output tiles spread over all the
+          // workgroup's waves: A = S (fp16 high and low parts of the fp32 values,
+          // one MFMA each), B = the rows (high part in columns 0-7, low part in
+          // 8-15), so each output sums all four cross products in fp32.  The u
+          // rows go to the area of virtual head 8 + vh (at most 8 of them).
+          __syncthreads();   // the rotated rows of every virtual head are staged
+          const int lp = fresh_lane();
+          const int pa = lp >> 4, pc = lp & 15;
+          const int grp = (16 * ot_w) / QM;
+          half8_t ah[QKC], al[QKC];   // A: S_grp[i][32 kc + 8 pa .. + 7], i = output 16 ot_w + pc of the group
+  #pragma unroll
+          for (int kc = 0; kc < QKC; ++kc) {
+            const float sv[8] = {spf[2 * kc].x, spf[2 * kc].y, spf[2 * kc].z, spf[2 * kc].w,
+                                 spf[2 * kc + 1].x, spf[2 * kc + 1].y, spf[2 * kc + 1].z, spf[2 * kc + 1].w};
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              ah[kc][e] = (_Float16)sv[e];
+              al[kc][e] = (_Float16)(sv[e] - (float)ah[kc][e]);
             }
           }
-#pragma unroll
-          for (int h = PH; h < 8 * PH; h <<= 1) {
-#pragma unroll
-            for (int e = 0; e < 8 * PH; ++e)
+          for (int vq = wave / QOT; vq < VH; vq += kWaves / QOT) {
+            const float* rows = reinterpret_cast<const float*>(qv_all + vq * NQK * 64);
+            float* const urows = reinterpret_cast<float*>(qv_all + (8 + vq) * NQK * 64);
+            const float rpow = ldexpf(1.0f, s_qexp[8 * vq + (pc & 7)]);   // the column's row scale
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+            // listed channels of positions grp M + 32 kc + 8 pa .. + 7 (two-group
+            // K: 8 bytes of the channel list, read at once for every kc)
+            uint2 chw[QKC];
+            if constexpr (C::MIXED) {
+  #pragma unroll
+              for (int kc = 0; kc < QKC; ++kc)
+                chw[kc] = *reinterpret_cast<const uint2*>(s_par + 32 + ((grp * QM + 32 * kc + 8 * pa) >> 2));
+            }
+  #pragma unroll
+            for (int kc = 0; kc < QKC; ++kc) {
+              // B: values j = 32 kc + 8 pa + e of row pc & 7 (group order)
+              half8_t bq;
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                int chn = grp * QM + 32 * kc + 8 * pa + e;
+                if constexpr (C::MIXED) chn = (int)((((e >> 2) ? chw[kc].y : chw[kc].x) >> (8 * (e & 3))) & 0xFFu);
+                const float v = rows[(pc & 7) * D + chn] * rpow;
+                const _Float16 hi = (_Float16)v;
+                bq[e] = (pc & 8) ? (_Float16)(v - (float)hi) : hi;
+              }
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[kc], bq, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[kc], bq, acc, 0, 0, 0);
+            }
+            // output 16 ot_w + 4 pa + e of row pc (columns pc and pc + 8 summed)
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float u = acc[e] + row_ror8(acc[e]);
+              if (pc < 8) urows[pc * D + 16 * ot_w + 4 * pa + e] = u;
+            }
+          }
+          __syncthreads();   // every u row is written
+        }
+        if (part == 0) {
+          float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
+          // (lane roles recomputed from the fresh lane index: values kept
+          // across the block loop may sit in scratch, whose reloads here would
+          // wait for the tile loads in flight)
+          const int la = ln >> 4, lq = ln & 7;
+          const bool lo_q = (ln & 8) != 0;
+          const float q_pow = ldexpf(1.0f, s_qexp[8 * vh + lq]);
+          const float* qrow = stage + lq * D;
+          // operand t of this lane: the 8 values it multiplies, scaled by
+          // 2^(15-ex) and split into the fp16 high part (lanes j < 8) or the
+          // fp16 rounding of the remainder (lanes j >= 8); all operands are
+          // built in registers before any is written over the rows
+          half8_t qvr[NQK];
+          // two-group K: operand element (t, e) of lane (a, j) is channel
+          // k_ch[pos] of the column, pos = (t / per_g) m + a (m / 4) + 8 (t %
+          // per_g) + e; the 8 list bytes of each t are read at once, before
+          // any row value
+          uint2 chl[NQK];
+          if constexpr (C::MIXED) {
+            constexpr int m = D / 2;
+            constexpr int per_g = NQK / 2;
+  #pragma unroll
+            for (int t = 0; t < NQK; ++t)
+              chl[t] = *reinterpret_cast<const uint2*>(s_par + 32 + (((t / per_g) * m + la * (m / 4) + 8 * (t % per_g)) >> 2));
+          }
+  #pragma unroll
+          for (int t = 0; t < NQK; ++t) {
+            float vq[8];
+            if constexpr (C::MIXED) {
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int chn = (int)((((e >> 2) ? chl[t].y : chl[t].x) >> (8 * (e & 3))) & 0xFFu);
+                vq[e] = qrow[chn];
+              }
+            } else {
+  #pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const float4 f = *reinterpret_cast<const float4*>(qrow + la * (D / 4) + 8 * t + 4 * h);
+                vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
+              }
+            }
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = vq[e] * q_pow;
+              const _Float16 hi = (_Float16)v;
+              const _Float16 lo = (_Float16)(v - (float)hi);
+              qvr[t][e] = lo_q ? lo : hi;
+            }
+          }
+          // every row read above is done before the operand writes below reuse
+          // the bytes
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  #pragma unroll
+          for (int t = 0; t < NQK; ++t) qv_all[(vh * NQK + t) * 64 + ln] = qvr[t];
+          if constexpr (C::QJ) {
+            // sketch operands: lane (a, j) multiplies outputs (D / 4) a + 8 t + e
+            // of its column's u row (sign byte NQK a + t of a K row), scaled
+            // by 2^(15-eu) (largest |u| of the row in [2^14, 2^15)) and split
+            // into high and low fp16 parts like q
+            const float* urow = reinterpret_cast<const float*>(qv_all + (8 + vh) * NQK * 64) + lq * D;
+            float uv[NQK][8];
+            float amax = 0.f;
+  #pragma unroll
+            for (int t = 0; t < NQK; ++t)
+  #pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const float4 f = *reinterpret_cast<const float4*>(urow + la * (D / 4) + 8 * t + 4 * h);
+                uv[t][4 * h] = f.x; uv[t][4 * h + 1] = f.y; uv[t][4 * h + 2] = f.z; uv[t][4 * h + 3] = f.w;
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+              }
+            amax = fmaxf(amax, lane_xor<16>(amax, ln));
+            amax = fmaxf(amax, lane_xor<32>(amax, ln));
+            int eu = 0;
+            if (amax > 0.f) frexpf(amax, &eu);
+            const float u_pow = ldexpf(1.0f, 15 - eu);
+            // the sketch's weight relative to the q.K sum: sqrt(pi / 2) / m
+            // against 1 / sqrt(m) (both over sqrt(d)), and the two scalings
+            if (ln < 8) s_rq[8 * vh + ln] = ldexpf(sqrtf(1.5707963267948966f / (float)(D / C::NGK)), eu - 15);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the u rows are read
+  #pragma unroll
+            for (int t = 0; t < NQK; ++t) {
+              half8_t sv;
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float v = uv[t][e] * u_pow;
+                const _Float16 hi = (_Float16)v;
+                sv[e] = lo_q ? (_Float16)(v - (float)hi) : hi;
+              }
+              qv_all[((8 + vh) * NQK + t) * 64 + ln] = sv;
+            }
+          }
+        }
+        if constexpr (C::QJ) first_tiles();
+        __syncthreads();  // operands, counters and block-table entries ready
+        TQ_MARK(3 + 4 * n_done);
+        int ph2v = bt_at(idx_2);
+        int g3 = grab();
+        const float w_col = ldexpf(p.score_mul, -s_qexp[8 * vh + gq]);
+        const half8_t* qb = qv_all + vh * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
+        const half8_t* qs = qv_all + (8 + vh) * NQK * 64 + lane;   // QJL: sketch operand t at qs[64 * t]
+        const float r_col = C::QJ ? s_rq[8 * vh + gq] : 0.f;
+
+        // -------- stream this wave's blocks of the piece
+        // online softmax state per column: running max m_run (raw score
+        // units), sum l_run and accumulator o_acc of the weights
+        // 2^(w_col (s - m_run) + e_run); e_run (the same in every lane) is the
+        // power of two that keeps p * n_V * 2^e_run in fp16's normal range:
+        // 15 - ex, 2^(ex-1) <= the largest V norm so far < 2^ex (39 before any)
+        float m_run = -INFINITY, l_run = 0.f;
+        int e_run = 39;
+        uint32_t v_hi = v_bound_m1(39);
+        float nm = 39.f;   // exp2 offset: e_run - w_col m_run (e_run while m_run is -inf)
+        float4_t o_acc[C::R];
+  #pragma unroll
+        for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+        // token r's V bytes of this lane, from byte 0 (r compile-time)
+        auto vword = [&](const Tile<D, KK, VK>& t, int r) -> uint32_t {
+          if constexpr (C::VLANE == 4) return t.v[r];
+          else if constexpr (C::VLANE == 2) return (r & 1) ? (t.v[r >> 1] >> 16) : t.v[r >> 1];
+          else return t.v[0] >> (8 * r);
+        };
+        auto compute = [&](const Tile<D, KK, VK>& cur, int b, bool ok) {
+          float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
+          float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (C::KB == K4) {
+  #pragma unroll
+            for (int t = 0; t < NQK; ++t) {
+              u32x4_t av;
+  #pragma unroll
+              for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[t], off4_k, by));
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
+            }
+          } else if constexpr (C::KB == K2) {
+  #pragma unroll
+            for (int t = 0; t < NQK; ++t) {
+              const uint2 x0 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1)));
+              const uint2 x1 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1) + 1));
+              const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
+            }
+          } else if constexpr (C::KB == KM43) {   // 4-bit group 0 by the nibble table, 3-bit group 1 by the pair table
+            constexpr int per_g = NQK / 2;
+  #pragma unroll
+            for (int u = 0; u < per_g; ++u) {
+              u32x4_t av;
+  #pragma unroll
+              for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[u], off4_k, by));
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
+            }
+            constexpr int LB = 3 * D / 64;
+            const int lo_off = tokK * C::KROW + D / 4 + LB * a;
+            const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((lo_off & 3) * 8);
+  #pragma unroll
+            for (int u = 0; u < per_g; ++u) {
+              u32x4_t av;
+  #pragma unroll
+              for (int pr = 0; pr < 4; ++pr) {
+                const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
+                av[pr] = lds_u32(lds, (key << 6) | off3);
+              }
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
+            }
+          } else {   // 3 + 2 bits: 3-bit group 0 by the pair table, 2-bit group 1 by the crumb table
+            constexpr int per_g = NQK / 2;
+            constexpr int LB = 3 * D / 64;
+            const int g0_off = tokK * C::KROW + LB * a;
+            const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((g0_off & 3) * 8);
+  #pragma unroll
+            for (int u = 0; u < per_g; ++u) {
+              u32x4_t av;
+  #pragma unroll
+              for (int pr = 0; pr < 4; ++pr) {
+                const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
+                av[pr] = lds_u32(lds, (key << 6) | off3);
+              }
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
+            }
+            const int g1_off = tokK * C::KROW + 3 * D / 16 + (D / 32) * a;
+            const uint32_t kw = cur.k[0] >> ((g1_off & 3) * 8);
+  #pragma unroll
+            for (int u = 0; u < per_g; ++u) {
+              const uint2 x0 = lds_u64(lds, lut_addr(kw, off2_k, 2 * u));
+              const uint2 x1 = lds_u64(lds, lut_addr(kw, off2_k, 2 * u + 1));
+              const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
+            }
+          }
+
+          // stage boundary: keeps the scheduler from hoisting the next stage's
+          // table reads above these MFMAs (bounds the live registers)
+          __builtin_amdgcn_sched_barrier(0);
+          const int tok0 = 16 * b;
+          const bool part = !(ok && tok0 + 16 <= ctx_all);   // partial or skipped block (wave-uniform)
+          // tokens a + 4e of this lane that count (all, unless part)
+          auto live = [&](int e) { return ok && (tok0 + a + 4 * e) < ctx_col; };
+          // raw scores of this lane's 4 tokens for q head gq: sr = (q . c) * n_K;
+          // the exp2-domain score is w_col * sr (w_col > 0), folded into one fma
+          float sc[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float full0 = acc0[e] + row_ror8(acc0[e]);
+            const uint32_t kw = (e >> 1) ? cur.kn[0].y : cur.kn[0].x;
+            float v = (e & 1) ? mul_h<1>(full0, kw) : mul_h<0>(full0, kw);
+            if constexpr (C::MIXED) {
+              const float full1 = acc1[e] + row_ror8(acc1[e]);
+              const uint32_t kw1 = (e >> 1) ? cur.kn[1].y : cur.kn[1].x;
+              v = (e & 1) ? fma_h<1>(full1, kw1, v) : fma_h<0>(full1, kw1, v);
+            }
+            sc[e] = v;
+          }
+          if constexpr (C::QJ) {
+            // QJL: the sketch sum of this lane's K row against the projected
+            // query (after the q.K sums are consumed, so that its accumulator
+            // reuses their registers), one MFMA per 32 outputs with A =
+            // +-(residual norm) in fp16 (exact): sign bit e2 of a byte to bit
+            // 15, bit e2 + 1 to bit 31 of the operand dword
+            float4_t accq = {0.f, 0.f, 0.f, 0.f};
+            const int lq = fresh_lane();
+            const uint32_t sb_all = cur.sg >> (8 * ((NQK * (lq >> 4)) & 3));
+            const uint32_t gam = (cur.gm >> (16 * (lq & 1))) & 0xFFFFu;
+            const uint32_t g2 = gam | (gam << 16);
+  #pragma unroll
+            for (int t = 0; t < NQK; ++t) {
+              const uint32_t sb = (sb_all >> (8 * t)) & 0xFFu;
+              const uint32_t spread = sb | (sb << 15);
+              u32x4_t av;
+  #pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) av[e2] = ((spread << (15 - 2 * e2)) & 0x80008000u) | g2;
+              accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qs[64 * t], accq, 0, 0, 0);
+            }
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) sc[e] = __builtin_fmaf(accq[e] + row_ror8(accq[e]), r_col, sc[e]);
+          }
+          if (part) {
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) sc[e] = live(e) ? sc[e] : -INFINITY;
+          }
+          const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
+          const float m_new = max_nn(m_run, bm);
+          // a V norm of this lane's tokens too large for the current e_run?
+          // (masked tokens' norm bytes may hold anything: left out)
+          u16x2_t mxv = __builtin_elementwise_max(as_u16x2(cur.vn[0].x), as_u16x2(cur.vn[0].y));
+          if constexpr (C::MIXED_V)
+            mxv = __builtin_elementwise_max(mxv, __builtin_elementwise_max(as_u16x2(cur.vn[1].x), as_u16x2(cur.vn[1].y)));
+          if (part) {
+            mxv = u16x2_t{0, 0};
+  #pragma unroll
+            for (int g = 0; g < C::NVG; ++g) {
+              uint32_t vx = cur.vn[g].x, vy = cur.vn[g].y;
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (!live(e)) {
+                  if (e >> 1) vy &= ~(0xFFFFu << (16 * (e & 1)));
+                  else vx &= ~(0xFFFFu << (16 * (e & 1)));
+                }
+              mxv = __builtin_elementwise_max(mxv, __builtin_elementwise_max(as_u16x2(vx), as_u16x2(vy)));
+            }
+          }
+          const bool over = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(mxv, u16x2_t{(uint16_t)v_hi, (uint16_t)v_hi})) != 0u;
+          if (__builtin_amdgcn_ballot_w64((m_new > m_run) | over)) {
+            asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
+            int e_new = e_run;
+            if (__builtin_amdgcn_ballot_w64(over)) {
+              // 15 - ex for the largest V norm of the tile (all 16 tokens),
+              // capped at the largest finite fp16
+              const uint32_t mh = mxv[0] > mxv[1] ? mxv[0] : mxv[1];
+              const float nmax = fminf(max_rows(f16_exact<0>(mh)), 65504.f);
+              const int ex = uni((int)((__float_as_uint(nmax) >> 23) & 0xFF) - 126);
+              e_new = 15 - ex < e_run ? 15 - ex : e_run;
+              v_hi = v_bound_m1(e_new);
+            }
+            const float sh = (float)(e_new - e_run);   // <= 0
+            const float alpha = __builtin_amdgcn_exp2f((m_new > m_run) ? __builtin_fmaf(m_run - m_new, w_col, sh) : sh);
+            l_run *= alpha;
+  #pragma unroll
+            for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
+            m_run = m_new;
+            e_run = e_new;
+            nm = (m_run == -INFINITY) ? (float)e_run : __builtin_fmaf(-m_run, w_col, (float)e_run);
+          }
+          float pr[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
+          l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+          // P.V on the matrix cores: A = V (dims x tokens) per MFMA i, through
+          // `into(i, A)` (i compile-time)
+          auto pv = [&](auto&& into) {
+            if constexpr (C::MIXED_V) {
+              // two groups: MFMAs 0 .. PPL-1 take group 0, PPL .. 2 PPL-1 group
+              // 1; MFMA (g, i) row r is position 8 (r % OCT) + (r / OCT) PPL + i
+              // of group g, so this lane's codes of token e sit at index
+              // (lane & 15) / OCT * PPL + i of the token's octet in its run
+              const int sub = (fresh_lane() & 15) / C::OCT;
+              auto group = [&](auto bk, const uint32_t* w, auto base) {
+                constexpr int b = decltype(bk)::value;
+                constexpr int I0 = decltype(base)::value;
+                if constexpr (b == 4) {
+                  // octet of token e = word e (8 nibbles); nibbles sub PPL + i,
+                  // paired across tokens as in the one-group 4-bit path
+                  const uint32_t sh = (uint32_t)(4 * C::PPL * sub);
+                  const uint32_t w0 = w[0] >> sh, w1 = w[1] >> sh, w2 = w[2] >> sh, w3 = w[3] >> sh;
+                  const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
+                  const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+                  const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | ((w3 << 4) & 0xF0F0F0F0u);
+                  const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
+  #pragma unroll
+                  for (int i = 0; i < C::PPL; ++i) {
+                    const u32x2_t av = {lds_u32(lds, lut_addr((i & 1) ? O01 : E01, off_v4, i >> 1)),
+                                        lds_u32(lds, lut_addr((i & 1) ? O23 : E23, off_v4, i >> 1))};
+                    into(I0 + i, __builtin_bit_cast(half4_t, av));
+                  }
+                } else if constexpr (b == 3) {
+                  // octet of token e = bits 24 e .. 24 e + 23 of the 3 words;
+                  // keys of the pair table: code(t0) | code(t1) << 3
+                  const uint32_t sh = (uint32_t)(3 * C::PPL * sub);
+                  const uint32_t x0 = w[0] >> sh;
+                  const uint32_t x1 = __builtin_amdgcn_alignbit(w[1], w[0], 24) >> sh;
+                  const uint32_t x2 = __builtin_amdgcn_alignbit(w[2], w[1], 16) >> sh;
+                  const uint32_t x3 = (w[2] >> 8) >> sh;
+  #pragma unroll
+                  for (int i = 0; i < C::PPL; ++i) {
+                    const uint32_t k01 = ((x0 >> (3 * i)) & 7u) | (((x1 >> (3 * i)) & 7u) << 3);
+                    const uint32_t k23 = ((x2 >> (3 * i)) & 7u) | (((x3 >> (3 * i)) & 7u) << 3);
+                    const u32x2_t av = {lds_u32(lds, (k01 << 6) | off3), lds_u32(lds, (k23 << 6) | off3)};
+                    into(I0 + i, __builtin_bit_cast(half4_t, av));
+                  }
+                } else {
+                  // octet of token e = half-word e of the 2 words (8 crumbs);
+                  // crumbs sub PPL + i of the 4 tokens transposed so that byte i
+                  // holds position i of tokens 0-3: the crumb table returns the
+                  // operand's 4 values in token order
+                  const uint32_t sh = (uint32_t)(2 * C::PPL * sub);
+                  const uint32_t y = ((w[0] >> sh) & 0xFFu) | (((w[0] >> 16 >> sh) & 0xFFu) << 8) |
+                                     (((w[1] >> sh) & 0xFFu) << 16) | (((w[1] >> 16 >> sh) & 0xFFu) << 24);
+                  uint32_t t = (y ^ (y >> 6)) & 0x00CC00CCu;
+                  uint32_t x = y ^ t ^ (t << 6);
+                  t = (x ^ (x >> 12)) & 0x0000F0F0u;
+                  x = x ^ t ^ (t << 12);
+  #pragma unroll
+                  for (int i = 0; i < C::PPL; ++i) {
+                    const uint2 l4 = lds_u64(lds, lut_addr(x, off_v2, i));
+                    into(I0 + i, __builtin_bit_cast(half4_t, u32x2_t{l4.x, l4.y}));
+                  }
+                }
+              };
+              group(std::integral_constant<int, C::VB0>{}, cur.v, std::integral_constant<int, 0>{});
+              group(std::integral_constant<int, C::VB1>{}, cur.v + C::VB0, std::integral_constant<int, C::PPL>{});
+            } else if constexpr (VK == V4) {
+              // Lookup keys pair the nibbles of two tokens for one dim, so the
+              // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
+              // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
+              const uint32_t w0 = vword(cur, 0), w1 = vword(cur, 1), w2 = vword(cur, 2), w3 = vword(cur, 3);
+              const uint32_t x1s = w1 << 4, x3s = w3 << 4;
+              const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
+              const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+              const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
+              const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
+              constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
+  #pragma unroll
+              for (int k = 0; k < NB; ++k) {
+  #pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                  const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
+                                      lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
+                  into(2 * k + hh, __builtin_bit_cast(half4_t, av));
+                }
+              }
+            } else {
+              constexpr int NBY = D / 64;  // bytes per token in this lane (4 dims each)
+  #pragma unroll
+              for (int k = 0; k < NBY; ++k) {
+                uint2 lk[4];
+  #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
+                  if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
+                  else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
+                }
+  #pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                  const uint32_t w0 = (t >> 1) ? lk[0].y : lk[0].x;
+                  const uint32_t w1 = (t >> 1) ? lk[1].y : lk[1].x;
+                  const uint32_t w2 = (t >> 1) ? lk[2].y : lk[2].x;
+                  const uint32_t w3 = (t >> 1) ? lk[3].y : lk[3].x;
+                  const u32x2_t av = {__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
+                  into(4 * k + t, __builtin_bit_cast(half4_t, av));
+                }
+              }
+            }
+          };
+          // B operand: p * n_V in fp16 (p carrying 2^e_run), each rounded once
+          // (two V groups: one operand per group's norms)
+          half4_t pb[C::NVG];
+  #pragma unroll
+          for (int g = 0; g < C::NVG; ++g) {
+            u32x2_t pw = {mul_h2(pr[0], pr[1], cur.vn[g].x), mul_h2(pr[2], pr[3], cur.vn[g].y)};
+            if (part) {
+              // a masked token's weight is 0, but its norm bytes may hold any
+              // bits (a NaN times 0 is NaN): its operand is set to +0
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (!live(e)) pw[e >> 1] &= ~(0xFFFFu << (16 * (e & 1)));
+            }
+            pb[g] = __builtin_bit_cast(half4_t, pw);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          pv([&](int i, half4_t av) {
+            o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb[C::MIXED_V && i >= C::PPL ? 1 : 0], o_acc[i], 0, 0, 0);
+          });
+        };
+
+        // one block (j): issue tile j+2, look up the entry of j+3 and take the
+        // index of j+4, compute tile j
+        auto step = [&](const Tile<D, KK, VK>& cur, Tile<D, KK, VK>& dst) -> bool {
+          if (idx_c >= n) return false;
+          bool ok2;
+          entry(ph2v, idx_2, ok2);
+          load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
+          const int idx_3 = __builtin_amdgcn_readfirstlane(g3);
+          const int ph3v = bt_at(idx_3);
+          g3 = grab();
+          compute(cur, b0 + idx_c, ok_c);
+          idx_c = idx_1; ok_c = ok_1;
+          idx_1 = idx_2; ok_1 = ok2;
+          idx_2 = idx_3; ph2v = ph3v;
+          return true;
+        };
+        for (;;) {
+          if (!step(A, C3)) break;
+          if (!step(B, A)) break;
+          if (!step(C3, B)) break;
+        }
+
+        // -------- wave states to LDS (rotated domain): wave w stores its
+        // unnormalised O rows (q head g at slot row 8 w + g) and its running
+        // max / sum per q head
+        __syncthreads();  // every wave is done with the q operands (the slots overlay them)
+        TQ_MARK(4 + 4 * n_done);
+        const int le = fresh_lane();
+        l_run += lane_xor<16>(l_run, le);
+        l_run += lane_xor<32>(l_run, le);
+        if (!lo_part) {
+          if constexpr (C::MIXED_V) {
+            // accumulator (i, e) is position 8 (rho % OCT) + (rho / OCT) PPL +
+            // i % PPL of V group i / PPL, rho = 4 a + e: stored at its channel
+            float* srow = slots + (8 * wave + gq) * C::DS;
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int rho = 4 * a + e;
+  #pragma unroll
+              for (int i = 0; i < C::R; ++i) {
+                const int pos = (i / C::PPL) * (D / 2) + 8 * (rho % C::OCT) + (rho / C::OCT) * C::PPL + i % C::PPL;
+                const int ch = (int)((s_vch[pos >> 2] >> (8 * (pos & 3))) & 0xFFu);
+                srow[ch] = o_acc[i][e];
+              }
+            }
+          } else {
+            float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
+  #pragma unroll
+            for (int e = 0; e < 4; ++e)
+  #pragma unroll
+              for (int h = 0; h < C::R / 4; ++h)
+                *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
+                    float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
+          }
+          if (a == 0) {   // the exp2-domain offset of the weights (-inf: no token), and their sum
+            s_ml[16 * wave + gq] = m_run == -INFINITY ? -INFINITY : -nm;
+            s_ml[16 * wave + 8 + gq] = l_run;
+          }
+        }
+        __syncthreads();
+
+        // -------- combine the parts of each (virtual head, column) pair,
+        // normalise, inverse rotation, write.  The pairs (CV columns per
+        // virtual head) are taken 64 at a time; wave w takes pairs 4 w .. 4 w +
+        // 3 of each round, 16 lanes each.  Lane m of a pair first holds dims m
+        // + 16 k (k < D / 16) and runs the transform stages over k in its
+        // registers, passes the row through LDS, then holds dims (D / 16) m + k,
+        // runs the stages over k again and the remaining ones across the lanes
+        // of the pair.
+        const int CV = CG == 1 ? p.G : 8;
+        const int npair = VH * CV;
+        for (int pbase = 4 * wave; pbase < npair; pbase += 4 * kWaves) {
+          constexpr int ND = D / 16;
+          const int m = le & 15;
+          const int pr_raw = pbase + (le >> 4);
+          const int pr = pr_raw < npair ? pr_raw : npair - 1;
+          const int h2 = CG == 1 ? (int)(((float)pr + 0.5f) * p.inv_G) : pr >> 3;   // virtual head: pr / CV (pr < 128)
+          const int g = pr - h2 * CV;
+          const int hk = h2 / CG;                   // its kv head of the group
+          const int col = 8 * (h2 - hk * CG) + g;   // its column of the kv head
+          const bool live = pr_raw < npair && col < p.G;
+          float M = -INFINITY;   // wave states: weights 2^(w s - X_w), sums l_w
+          for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * wave_of_part(h2, q, VH) + g]);
+          float y[ND];
+  #pragma unroll
+          for (int k = 0; k < ND; ++k) y[k] = 0.f;
+          float L = 0.f;
+          for (int q = 0; q < NPW; ++q) {
+            const int wq = wave_of_part(h2, q, VH);
+            const float mw = s_ml[16 * wq + g];
+            const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+            L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
+            const float* srow = slots + (8 * wq + g) * C::DS + m;
+  #pragma unroll
+            for (int k = 0; k < ND; ++k) y[k] = __builtin_fmaf(f, srow[16 * k], y[k]);
+          }
+  #pragma unroll
+          for (int h = 1; h < ND; h <<= 1) {
+  #pragma unroll
+            for (int e = 0; e < ND; ++e)
               if ((e & h) == 0) {
                 const float a0 = y[e], b0v = y[e + h];
                 y[e] = a0 + b0v;
                 y[e + h] = a0 - b0v;
               }
           }
-          float amax = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int c = PER * k + PH * l8;
-            if constexpr (PH == 2) *reinterpret_cast<float2*>(qrow + c) = float2{y[2 * k], y[2 * k + 1]};
-            else qrow[c] = y[k];
+          // the row of part 0 is read only by this pair's lanes, each lane
+          // rewrites the dims it read; the fence below orders those writes
+          // before the reads of the other lanes' dims
+          float* row = slots + (8 * wave_of_part(h2, 0, VH) + g) * C::DS;
+  #pragma unroll
+          for (int k = 0; k < ND; ++k) row[m + 16 * k] = y[k];
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // other lanes' values below
+  #pragma unroll
+          for (int k = 0; k < ND; k += 4) {
+            const float4 f = *reinterpret_cast<const float4*>(row + ND * m + k);
+            y[k] = f.x; y[k + 1] = f.y; y[k + 2] = f.z; y[k + 3] = f.w;
           }
-#pragma unroll
-          for (int e = 0; e < 8 * PH; ++e) amax = fmaxf(amax, fabsf(y[e]));
-          amax = fmaxf(amax, lane_xor<1>(amax, ln));
-          amax = fmaxf(amax, lane_xor<2>(amax, ln));
-          amax = fmaxf(amax, lane_xor<4>(amax, ln));
-          int ex = 0;
-          if (amax > 0.f) frexpf(amax, &ex);
-          if (l8 == 0) s_qexp[8 * vh + g8] = 15 - ex;   // amax * 2^(15-ex) in [2^14, 2^15)
-        }
-      }
-      if constexpr (C::QJ) {
-        // QJL: the projected rows u_g = S_g q_g of every virtual head (q_g:
-        // the rotated row scaled by 2^(15-ex), group g's channels in listed
-        // order) on the matrix cores, in 16-output tiles spread over all the
-        // workgroup's waves: A = S (fp16 high and low parts of the fp32 values,
-        // one MFMA each), B = the rows (high part in columns 0-7, low part in
-        // 8-15), so each output sums all four cross products in fp32.  The u
-        // rows go to the area of virtual head 8 + vh (at most 8 of them).
-        __syncthreads();   // the rotated rows of every virtual head are staged
-        const int lp = fresh_lane();
-        const int pa = lp >> 4, pc = lp & 15;
-        const int grp = (16 * ot_w) / QM;
-        half8_t ah[QKC], al[QKC];   // A: S_grp[i][32 kc + 8 pa .. + 7], i = output 16 ot_w + pc of the group
-#pragma unroll
-        for (int kc = 0; kc < QKC; ++kc) {
-          const float sv[8] = {spf[2 * kc].x, spf[2 * kc].y, spf[2 * kc].z, spf[2 * kc].w,
-                               spf[2 * kc + 1].x, spf[2 * kc + 1].y, spf[2 * kc + 1].z, spf[2 * kc + 1].w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ah[kc][e] = (_Float16)sv[e];
-            al[kc][e] = (_Float16)(sv[e] - (float)ah[kc][e]);
-          }
-        }
-        for (int vq = wave / QOT; vq < VH; vq += kWaves / QOT) {
-          const float* rows = reinterpret_cast<const float*>(qv_all + vq * NQK * 64);
-          float* const urows = reinterpret_cast<float*>(qv_all + (8 + vq) * NQK * 64);
-          const float rpow = ldexpf(1.0f, s_qexp[8 * vq + (pc & 7)]);   // the column's row scale
-          float4_t acc = {0.f, 0.f, 0.f, 0.f};
-          // listed channels of positions grp M + 32 kc + 8 pa .. + 7 (two-group
-          // K: 8 bytes of the channel list, read at once for every kc)
-          uint2 chw[QKC];
-          if constexpr (C::MIXED) {
-#pragma unroll
-            for (int kc = 0; kc < QKC; ++kc)
-              chw[kc] = *reinterpret_cast<const uint2*>(s_par + 32 + ((grp * QM + 32 * kc + 8 * pa) >> 2));
-          }
-#pragma unroll
-          for (int kc = 0; kc < QKC; ++kc) {
-            // B: values j = 32 kc + 8 pa + e of row pc & 7 (group order)
-            half8_t bq;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              int chn = grp * QM + 32 * kc + 8 * pa + e;
-              if constexpr (C::MIXED) chn = (int)((((e >> 2) ? chw[kc].y : chw[kc].x) >> (8 * (e & 3))) & 0xFFu);
-              const float v = rows[(pc & 7) * D + chn] * rpow;
-              const _Float16 hi = (_Float16)v;
-              bq[e] = (pc & 8) ? (_Float16)(v - (float)hi) : hi;
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[kc], bq, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[kc], bq, acc, 0, 0, 0);
-          }
-          // output 16 ot_w + 4 pa + e of row pc (columns pc and pc + 8 summed)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float u = acc[e] + row_ror8(acc[e]);
-            if (pc < 8) urows[pc * D + 16 * ot_w + 4 * pa + e] = u;
-          }
-        }
-        __syncthreads();   // every u row is written
-      }
-      if (part == 0) {
-        float* const stage = reinterpret_cast<float*>(qv_all + vh * NQK * 64);
-        // (lane roles recomputed from the fresh lane index: values kept
-        // across the block loop may sit in scratch, whose reloads here would
-        // wait for the tile loads in flight)
-        const int la = ln >> 4, lq = ln & 7;
-        const bool lo_q = (ln & 8) != 0;
-        const float q_pow = ldexpf(1.0f, s_qexp[8 * vh + lq]);
-        const float* qrow = stage + lq * D;
-        // operand t of this lane: the 8 values it multiplies, scaled by
-        // 2^(15-ex) and split into the fp16 high part (lanes j < 8) or the
-        // fp16 rounding of the remainder (lanes j >= 8); all operands are
-        // built in registers before any is written over the rows
-        half8_t qvr[NQK];
-        // two-group K: operand element (t, e) of lane (a, j) is channel
-        // k_ch[pos] of the column, pos = (t / per_g) m + a (m / 4) + 8 (t %
-        // per_g) + e; the 8 list bytes of each t are read at once, before
-        // any row value
-        uint2 chl[NQK];
-        if constexpr (C::MIXED) {
-          constexpr int m = D / 2;
-          constexpr int per_g = NQK / 2;
-#pragma unroll
-          for (int t = 0; t < NQK; ++t)
-            chl[t] = *reinterpret_cast<const uint2*>(s_par + 32 + (((t / per_g) * m + la * (m / 4) + 8 * (t % per_g)) >> 2));
-        }
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) {
-          float vq[8];
-          if constexpr (C::MIXED) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int chn = (int)((((e >> 2) ? chl[t].y : chl[t].x) >> (8 * (e & 3))) & 0xFFu);
-              vq[e] = qrow[chn];
-            }
-          } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const float4 f = *reinterpret_cast<const float4*>(qrow + la * (D / 4) + 8 * t + 4 * h);
-              vq[4 * h] = f.x; vq[4 * h + 1] = f.y; vq[4 * h + 2] = f.z; vq[4 * h + 3] = f.w;
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = vq[e] * q_pow;
-            const _Float16 hi = (_Float16)v;
-            const _Float16 lo = (_Float16)(v - (float)hi);
-            qvr[t][e] = lo_q ? lo : hi;
-          }
-        }
-        // every row read above is done before the operand writes below reuse
-        // the bytes
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-        for (int t = 0; t < NQK; ++t) qv_all[(vh * NQK + t) * 64 + ln] = qvr[t];
-        if constexpr (C::QJ) {
-          // sketch operands: lane (a, j) multiplies outputs (D / 4) a + 8 t + e
-          // of its column's u row (sign byte NQK a + t of a K row), scaled
-          // by 2^(15-eu) (largest |u| of the row in [2^14, 2^15)) and split
-          // into high and low fp16 parts like q
-          const float* urow = reinterpret_cast<const float*>(qv_all + (8 + vh) * NQK * 64) + lq * D;
-          float uv[NQK][8];
-          float amax = 0.f;
-#pragma unroll
-          for (int t = 0; t < NQK; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const float4 f = *reinterpret_cast<const float4*>(urow + la * (D / 4) + 8 * t + 4 * h);
-              uv[t][4 * h] = f.x; uv[t][4 * h + 1] = f.y; uv[t][4 * h + 2] = f.z; uv[t][4 * h + 3] = f.w;
-              amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
-            }
-          amax = fmaxf(amax, lane_xor<16>(amax, ln));
-          amax = fmaxf(amax, lane_xor<32>(amax, ln));
-          int eu = 0;
-          if (amax > 0.f) frexpf(amax, &eu);
-          const float u_pow = ldexpf(1.0f, 15 - eu);
-          // the sketch's weight relative to the q.K sum: sqrt(pi / 2) / m
-          // against 1 / sqrt(m) (both over sqrt(d)), and the two scalings
-          if (ln < 8) s_rq[8 * vh + ln] = ldexpf(sqrtf(1.5707963267948966f / (float)(D / C::NGK)), eu - 15);
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the u rows are read
-#pragma unroll
-          for (int t = 0; t < NQK; ++t) {
-            half8_t sv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float v = uv[t][e] * u_pow;
-              const _Float16 hi = (_Float16)v;
-              sv[e] = lo_q ? (_Float16)(v - (float)hi) : hi;
-            }
-            qv_all[((8 + vh) * NQK + t) * 64 + ln] = sv;
-          }
-        }
-      }
-      if constexpr (C::QJ) first_tiles();
-      __syncthreads();  // operands, counters and block-table entries ready
-      TQ_MARK(3 + 4 * n_done);
-      int ph2v = bt_at(idx_2);
-      int g3 = grab();
-      const float w_col = ldexpf(p.score_mul, -s_qexp[8 * vh + gq]);
-      const half8_t* qb = qv_all + vh * NQK * 64 + lane;   // qb[64 * t]: operand of MFMA t
-      const half8_t* qs = qv_all + (8 + vh) * NQK * 64 + lane;   // QJL: sketch operand t at qs[64 * t]
-      const float r_col = C::QJ ? s_rq[8 * vh + gq] : 0.f;
-
-      // -------- stream this wave's blocks of the piece
-      // online softmax state per column: running max m_run (raw score
-      // units), sum l_run and accumulator o_acc of the weights
-      // 2^(w_col (s - m_run) + e_run); e_run (the same in every lane) is the
-      // power of two that keeps p * n_V * 2^e_run in fp16's normal range:
-      // 15 - ex, 2^(ex-1) <= the largest V norm so far < 2^ex (39 before any)
-      float m_run = -INFINITY, l_run = 0.f;
-      int e_run = 39;
-      uint32_t v_hi = v_bound_m1(39);
-      float nm = 39.f;   // exp2 offset: e_run - w_col m_run (e_run while m_run is -inf)
-      float4_t o_acc[C::R];
-#pragma unroll
-      for (int u = 0; u < C::R; ++u) o_acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-      // token r's V bytes of this lane, from byte 0 (r compile-time)
-      auto vword = [&](const Tile<D, KK, VK>& t, int r) -> uint32_t {
-        if constexpr (C::VLANE == 4) return t.v[r];
-        else if constexpr (C::VLANE == 2) return (r & 1) ? (t.v[r >> 1] >> 16) : t.v[r >> 1];
-        else return t.v[0] >> (8 * r);
-      };
-      auto compute = [&](const Tile<D, KK, VK>& cur, int b, bool ok) {
-        float4_t acc0 = {0.f, 0.f, 0.f, 0.f};
-        float4_t acc1 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (C::KB == K4) {
-#pragma unroll
-          for (int t = 0; t < NQK; ++t) {
-            u32x4_t av;
-#pragma unroll
-            for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[t], off4_k, by));
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
-          }
-        } else if constexpr (C::KB == K2) {
-#pragma unroll
-          for (int t = 0; t < NQK; ++t) {
-            const uint2 x0 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1)));
-            const uint2 x1 = lds_u64(lds, lut_addr(cur.k[t >> 1], off2_k, 2 * (t & 1) + 1));
-            const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * t], acc0, 0, 0, 0);
-          }
-        } else if constexpr (C::KB == KM43) {   // 4-bit group 0 by the nibble table, 3-bit group 1 by the pair table
-          constexpr int per_g = NQK / 2;
-#pragma unroll
-          for (int u = 0; u < per_g; ++u) {
-            u32x4_t av;
-#pragma unroll
-            for (int by = 0; by < 4; ++by) av[by] = lds_u32(lds, lut_addr(cur.k[u], off4_k, by));
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
-          }
-          constexpr int LB = 3 * D / 64;
-          const int lo_off = tokK * C::KROW + D / 4 + LB * a;
-          const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((lo_off & 3) * 8);
-#pragma unroll
-          for (int u = 0; u < per_g; ++u) {
-            u32x4_t av;
-#pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-              const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
-              av[pr] = lds_u32(lds, (key << 6) | off3);
-            }
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
-          }
-        } else {   // 3 + 2 bits: 3-bit group 0 by the pair table, 2-bit group 1 by the crumb table
-          constexpr int per_g = NQK / 2;
-          constexpr int LB = 3 * D / 64;
-          const int g0_off = tokK * C::KROW + LB * a;
-          const uint64_t win = ((uint64_t)cur.k_lo[1] << 32 | cur.k_lo[0]) >> ((g0_off & 3) * 8);
-#pragma unroll
-          for (int u = 0; u < per_g; ++u) {
-            u32x4_t av;
-#pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
-              const uint32_t key = (uint32_t)(win >> (6 * (4 * u + pr))) & 63u;
-              av[pr] = lds_u32(lds, (key << 6) | off3);
-            }
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * u], acc0, 0, 0, 0);
-          }
-          const int g1_off = tokK * C::KROW + 3 * D / 16 + (D / 32) * a;
-          const uint32_t kw = cur.k[0] >> ((g1_off & 3) * 8);
-#pragma unroll
-          for (int u = 0; u < per_g; ++u) {
-            const uint2 x0 = lds_u64(lds, lut_addr(kw, off2_k, 2 * u));
-            const uint2 x1 = lds_u64(lds, lut_addr(kw, off2_k, 2 * u + 1));
-            const u32x4_t av = {x0.x, x0.y, x1.x, x1.y};
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qb[64 * (per_g + u)], acc1, 0, 0, 0);
-          }
-        }
-
-        // stage boundary: keeps the scheduler from hoisting the next stage's
-        // table reads above these MFMAs (bounds the live registers)
-        __builtin_amdgcn_sched_barrier(0);
-        const int tok0 = 16 * b;
-        const bool part = !(ok && tok0 + 16 <= ctx_all);   // partial or skipped block (wave-uniform)
-        // tokens a + 4e of this lane that count (all, unless part)
-        auto live = [&](int e) { return ok && (tok0 + a + 4 * e) < ctx_col; };
-        // raw scores of this lane's 4 tokens for q head gq: sr = (q . c) * n_K;
-        // the exp2-domain score is w_col * sr (w_col > 0), folded into one fma
-        float sc[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float full0 = acc0[e] + row_ror8(acc0[e]);
-          const uint32_t kw = (e >> 1) ? cur.kn[0].y : cur.kn[0].x;
-          float v = (e & 1) ? mul_h<1>(full0, kw) : mul_h<0>(full0, kw);
-          if constexpr (C::MIXED) {
-            const float full1 = acc1[e] + row_ror8(acc1[e]);
-            const uint32_t kw1 = (e >> 1) ? cur.kn[1].y : cur.kn[1].x;
-            v = (e & 1) ? fma_h<1>(full1, kw1, v) : fma_h<0>(full1, kw1, v);
-          }
-          sc[e] = v;
-        }
-        if constexpr (C::QJ) {
-          // QJL: the sketch sum of this lane's K row against the projected
-          // query (after the q.K sums are consumed, so that its accumulator
-          // reuses their registers), one MFMA per 32 outputs with A =
-          // +-(residual norm) in fp16 (exact): sign bit e2 of a byte to bit
-          // 15, bit e2 + 1 to bit 31 of the operand dword
-          float4_t accq = {0.f, 0.f, 0.f, 0.f};
-          const int lq = fresh_lane();
-          const uint32_t sb_all = cur.sg >> (8 * ((NQK * (lq >> 4)) & 3));
-          const uint32_t gam = (cur.gm >> (16 * (lq & 1))) & 0xFFFFu;
-          const uint32_t g2 = gam | (gam << 16);
-#pragma unroll
-          for (int t = 0; t < NQK; ++t) {
-            const uint32_t sb = (sb_all >> (8 * t)) & 0xFFu;
-            const uint32_t spread = sb | (sb << 15);
-            u32x4_t av;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) av[e2] = ((spread << (15 - 2 * e2)) & 0x80008000u) | g2;
-            accq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), qs[64 * t], accq, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[e] = __builtin_fmaf(accq[e] + row_ror8(accq[e]), r_col, sc[e]);
-        }
-        if (part) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[e] = live(e) ? sc[e] : -INFINITY;
-        }
-        const float bm = max_rows(max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3])));
-        const float m_new = max_nn(m_run, bm);
-        // a V norm of this lane's tokens too large for the current e_run?
-        // (masked tokens' norm bytes may hold anything: left out)
-        u16x2_t mxv = __builtin_elementwise_max(as_u16x2(cur.vn[0].x), as_u16x2(cur.vn[0].y));
-        if constexpr (C::MIXED_V)
-          mxv = __builtin_elementwise_max(mxv, __builtin_elementwise_max(as_u16x2(cur.vn[1].x), as_u16x2(cur.vn[1].y)));
-        if (part) {
-          mxv = u16x2_t{0, 0};
-#pragma unroll
-          for (int g = 0; g < C::NVG; ++g) {
-            uint32_t vx = cur.vn[g].x, vy = cur.vn[g].y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (!live(e)) {
-                if (e >> 1) vy &= ~(0xFFFFu << (16 * (e & 1)));
-                else vx &= ~(0xFFFFu << (16 * (e & 1)));
+  #pragma unroll
+          for (int h = 1; h < ND; h <<= 1) {
+  #pragma unroll
+            for (int e = 0; e < ND; ++e)
+              if ((e & h) == 0) {
+                const float a0 = y[e], b0v = y[e + h];
+                y[e] = a0 + b0v;
+                y[e + h] = a0 - b0v;
               }
-            mxv = __builtin_elementwise_max(mxv, __builtin_elementwise_max(as_u16x2(vx), as_u16x2(vy)));
           }
-        }
-        const bool over = __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(mxv, u16x2_t{(uint16_t)v_hi, (uint16_t)v_hi})) != 0u;
-        if (__builtin_amdgcn_ballot_w64((m_new > m_run) | over)) {
-          asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch
-          int e_new = e_run;
-          if (__builtin_amdgcn_ballot_w64(over)) {
-            // 15 - ex for the largest V norm of the tile (all 16 tokens),
-            // capped at the largest finite fp16
-            const uint32_t mh = mxv[0] > mxv[1] ? mxv[0] : mxv[1];
-            const float nmax = fminf(max_rows(f16_exact<0>(mh)), 65504.f);
-            const int ex = uni((int)((__float_as_uint(nmax) >> 23) & 0xFF) - 126);
-            e_new = 15 - ex < e_run ? 15 - ex : e_run;
-            v_hi = v_bound_m1(e_new);
+          wht_lanes<1>(y, le);   // dim bit 3 (D = 128) or bits 2, 3 (D = 64)
+          if constexpr (ND == 4) wht_lanes<2>(y, le);
+          const bool empty = !(L > 0.f);
+          const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
+          const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
+          const float lse = empty ? -INFINITY : (M + log2f(L)) * kLn2;
+          const int qi = (int)(((float)col + 0.5f) * p.inv_Gr);   // column col = (query qi, q head col - qi Gr)
+          const int64_t rowq = ((int64_t)s * p.NQ + qi) * p.Hq + (grp * HG + hk) * p.Gr + (col - qi * p.Gr);
+          const int d0 = ND * m;
+          const uint32_t sgn = s_par[24 + (d0 >> 5)] >> (d0 & 31);
+  #pragma unroll
+          for (int k = 0; k < ND; ++k) {
+            const float sv = y[k] * scale;
+            y[k] = ((sgn >> k) & 1u) ? -sv : sv;
           }
-          const float sh = (float)(e_new - e_run);   // <= 0
-          const float alpha = __builtin_amdgcn_exp2f((m_new > m_run) ? __builtin_fmaf(m_run - m_new, w_col, sh) : sh);
-          l_run *= alpha;
-#pragma unroll
-          for (int u = 0; u < C::R; ++u) o_acc[u] *= alpha;
-          m_run = m_new;
-          e_run = e_new;
-          nm = (m_run == -INFINITY) ? (float)e_run : __builtin_fmaf(-m_run, w_col, (float)e_run);
-        }
-        float pr[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], w_col, nm));   // -inf -> 0
-        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-
-        // P.V on the matrix cores: A = V (dims x tokens) per MFMA i, through
-        // `into(i, A)` (i compile-time)
-        auto pv = [&](auto&& into) {
-          if constexpr (C::MIXED_V) {
-            // two groups: MFMAs 0 .. PPL-1 take group 0, PPL .. 2 PPL-1 group
-            // 1; MFMA (g, i) row r is position 8 (r % OCT) + (r / OCT) PPL + i
-            // of group g, so this lane's codes of token e sit at index
-            // (lane & 15) / OCT * PPL + i of the token's octet in its run
-            const int sub = (fresh_lane() & 15) / C::OCT;
-            auto group = [&](auto bk, const uint32_t* w, auto base) {
-              constexpr int b = decltype(bk)::value;
-              constexpr int I0 = decltype(base)::value;
-              if constexpr (b == 4) {
-                // octet of token e = word e (8 nibbles); nibbles sub PPL + i,
-                // paired across tokens as in the one-group 4-bit path
-                const uint32_t sh = (uint32_t)(4 * C::PPL * sub);
-                const uint32_t w0 = w[0] >> sh, w1 = w[1] >> sh, w2 = w[2] >> sh, w3 = w[3] >> sh;
-                const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
-                const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
-                const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | ((w3 << 4) & 0xF0F0F0F0u);
-                const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
-#pragma unroll
-                for (int i = 0; i < C::PPL; ++i) {
-                  const u32x2_t av = {lds_u32(lds, lut_addr((i & 1) ? O01 : E01, off_v4, i >> 1)),
-                                      lds_u32(lds, lut_addr((i & 1) ? O23 : E23, off_v4, i >> 1))};
-                  into(I0 + i, __builtin_bit_cast(half4_t, av));
-                }
-              } else if constexpr (b == 3) {
-                // octet of token e = bits 24 e .. 24 e + 23 of the 3 words;
-                // keys of the pair table: code(t0) | code(t1) << 3
-                const uint32_t sh = (uint32_t)(3 * C::PPL * sub);
-                const uint32_t x0 = w[0] >> sh;
-                const uint32_t x1 = __builtin_amdgcn_alignbit(w[1], w[0], 24) >> sh;
-                const uint32_t x2 = __builtin_amdgcn_alignbit(w[2], w[1], 16) >> sh;
-                const uint32_t x3 = (w[2] >> 8) >> sh;
-#pragma unroll
-                for (int i = 0; i < C::PPL; ++i) {
-                  const uint32_t k01 = ((x0 >> (3 * i)) & 7u) | (((x1 >> (3 * i)) & 7u) << 3);
-                  const uint32_t k23 = ((x2 >> (3 * i)) & 7u) | (((x3 >> (3 * i)) & 7u) << 3);
-                  const u32x2_t av = {lds_u32(lds, (k01 << 6) | off3), lds_u32(lds, (k23 << 6) | off3)};
-                  into(I0 + i, __builtin_bit_cast(half4_t, av));
-                }
+          if (live) {
+            if (whole) {
+              const int64_t off = rowq * D + d0;
+              if (p.out_f32) {
+  #pragma unroll
+                for (int k = 0; k < ND; k += 4)
+                  *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off + k) = float4{y[k], y[k + 1], y[k + 2], y[k + 3]};
               } else {
-                // octet of token e = half-word e of the 2 words (8 crumbs);
-                // crumbs sub PPL + i of the 4 tokens transposed so that byte i
-                // holds position i of tokens 0-3: the crumb table returns the
-                // operand's 4 values in token order
-                const uint32_t sh = (uint32_t)(2 * C::PPL * sub);
-                const uint32_t y = ((w[0] >> sh) & 0xFFu) | (((w[0] >> 16 >> sh) & 0xFFu) << 8) |
-                                   (((w[1] >> sh) & 0xFFu) << 16) | (((w[1] >> 16 >> sh) & 0xFFu) << 24);
-                uint32_t t = (y ^ (y >> 6)) & 0x00CC00CCu;
-                uint32_t x = y ^ t ^ (t << 6);
-                t = (x ^ (x >> 12)) & 0x0000F0F0u;
-                x = x ^ t ^ (t << 12);
-#pragma unroll
-                for (int i = 0; i < C::PPL; ++i) {
-                  const uint2 l4 = lds_u64(lds, lut_addr(x, off_v2, i));
-                  into(I0 + i, __builtin_bit_cast(half4_t, u32x2_t{l4.x, l4.y}));
-                }
+                uint32_t w[ND / 2];
+  #pragma unroll
+                for (int k = 0; k < ND / 2; ++k)
+                  w[k] = (uint32_t)f32_to_bf16_rne(y[2 * k]) | ((uint32_t)f32_to_bf16_rne(y[2 * k + 1]) << 16);
+                uint16_t* o16 = static_cast<uint16_t*>(p.out) + off;
+                if constexpr (ND == 8) *reinterpret_cast<uint4*>(o16) = uint4{w[0], w[1], w[2], w[3]};
+                else *reinterpret_cast<uint2*>(o16) = uint2{w[0], w[1]};
               }
-            };
-            group(std::integral_constant<int, C::VB0>{}, cur.v, std::integral_constant<int, 0>{});
-            group(std::integral_constant<int, C::VB1>{}, cur.v + C::VB0, std::integral_constant<int, C::PPL>{});
-          } else if constexpr (VK == V4) {
-            // Lookup keys pair the nibbles of two tokens for one dim, so the
-            // nibble table returns the MFMA operand dword (V[t0][d], V[t1][d])
-            // directly: byte k of E holds dim 2k, byte k of Od dim 2k+1.
-            const uint32_t w0 = vword(cur, 0), w1 = vword(cur, 1), w2 = vword(cur, 2), w3 = vword(cur, 3);
-            const uint32_t x1s = w1 << 4, x3s = w3 << 4;
-            const uint32_t E01 = (w0 & 0x0F0F0F0Fu) | (x1s & 0xF0F0F0F0u);
-            const uint32_t O01 = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
-            const uint32_t E23 = (w2 & 0x0F0F0F0Fu) | (x3s & 0xF0F0F0F0u);
-            const uint32_t O23 = ((w2 >> 4) & 0x0F0F0F0Fu) | (w3 & 0xF0F0F0F0u);
-            constexpr int NB = D / 32;  // bytes per token in this lane (2 dims each)
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {
-#pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                const u32x2_t av = {lds_u32(lds, lut_addr(hh ? O01 : E01, off_v4, k)),
-                                    lds_u32(lds, lut_addr(hh ? O23 : E23, off_v4, k))};
-                into(2 * k + hh, __builtin_bit_cast(half4_t, av));
-              }
-            }
-          } else {
-            constexpr int NBY = D / 64;  // bytes per token in this lane (4 dims each)
-#pragma unroll
-            for (int k = 0; k < NBY; ++k) {
-              uint2 lk[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                // byte k of token r: word r / 2, byte 2 (r % 2) + k (2-byte runs) or byte r (1-byte runs)
-                if constexpr (C::VLANE == 2) lk[r] = lds_u64(lds, lut_addr(cur.v[r >> 1], off_v2, 2 * (r & 1) + k));
-                else lk[r] = lds_u64(lds, lut_addr(cur.v[0], off_v2, r + k));
-              }
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-                const uint32_t w0 = (t >> 1) ? lk[0].y : lk[0].x;
-                const uint32_t w1 = (t >> 1) ? lk[1].y : lk[1].x;
-                const uint32_t w2 = (t >> 1) ? lk[2].y : lk[2].x;
-                const uint32_t w3 = (t >> 1) ? lk[3].y : lk[3].x;
-                const u32x2_t av = {__builtin_amdgcn_perm(w1, w0, sel), __builtin_amdgcn_perm(w3, w2, sel)};
-                into(4 * k + t, __builtin_bit_cast(half4_t, av));
-              }
-            }
-          }
-        };
-        // B operand: p * n_V in fp16 (p carrying 2^e_run), each rounded once
-        // (two V groups: one operand per group's norms)
-        half4_t pb[C::NVG];
-#pragma unroll
-        for (int g = 0; g < C::NVG; ++g) {
-          u32x2_t pw = {mul_h2(pr[0], pr[1], cur.vn[g].x), mul_h2(pr[2], pr[3], cur.vn[g].y)};
-          if (part) {
-            // a masked token's weight is 0, but its norm bytes may hold any
-            // bits (a NaN times 0 is NaN): its operand is set to +0
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (!live(e)) pw[e >> 1] &= ~(0xFFFFu << (16 * (e & 1)));
-          }
-          pb[g] = __builtin_bit_cast(half4_t, pw);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        pv([&](int i, half4_t av) {
-          o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb[C::MIXED_V && i >= C::PPL ? 1 : 0], o_acc[i], 0, 0, 0);
-        });
-      };
-
-      // one block (j): issue tile j+2, look up the entry of j+3 and take the
-      // index of j+4, compute tile j
-      auto step = [&](const Tile<D, KK, VK>& cur, Tile<D, KK, VK>& dst) -> bool {
-        if (idx_c >= n) return false;
-        bool ok2;
-        entry(ph2v, idx_2, ok2);
-        load_tile<D, KK, VK>(dst, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
-        const int idx_3 = __builtin_amdgcn_readfirstlane(g3);
-        const int ph3v = bt_at(idx_3);
-        g3 = grab();
-        compute(cur, b0 + idx_c, ok_c);
-        idx_c = idx_1; ok_c = ok_1;
-        idx_1 = idx_2; ok_1 = ok2;
-        idx_2 = idx_3; ph2v = ph3v;
-        return true;
-      };
-      for (;;) {
-        if (!step(A, C3)) break;
-        if (!step(B, A)) break;
-        if (!step(C3, B)) break;
-      }
-
-      // -------- wave states to LDS (rotated domain): wave w stores its
-      // unnormalised O rows (q head g at slot row 8 w + g) and its running
-      // max / sum per q head
-      __syncthreads();  // every wave is done with the q operands (the slots overlay them)
-      TQ_MARK(4 + 4 * n_done);
-      const int le = fresh_lane();
-      l_run += lane_xor<16>(l_run, le);
-      l_run += lane_xor<32>(l_run, le);
-      if (!lo_part) {
-        if constexpr (C::MIXED_V) {
-          // accumulator (i, e) is position 8 (rho % OCT) + (rho / OCT) PPL +
-          // i % PPL of V group i / PPL, rho = 4 a + e: stored at its channel
-          float* srow = slots + (8 * wave + gq) * C::DS;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int rho = 4 * a + e;
-#pragma unroll
-            for (int i = 0; i < C::R; ++i) {
-              const int pos = (i / C::PPL) * (D / 2) + 8 * (rho % C::OCT) + (rho / C::OCT) * C::PPL + i % C::PPL;
-              const int ch = (int)((s_vch[pos >> 2] >> (8 * (pos & 3))) & 0xFFu);
-              srow[ch] = o_acc[i][e];
-            }
-          }
-        } else {
-          float* srow = slots + (8 * wave + gq) * C::DS + R4 * a;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int h = 0; h < C::R / 4; ++h)
-              *reinterpret_cast<float4*>(srow + C::R * e + 4 * h) =
-                  float4{o_acc[4 * h][e], o_acc[4 * h + 1][e], o_acc[4 * h + 2][e], o_acc[4 * h + 3][e]};
-        }
-        if (a == 0) {   // the exp2-domain offset of the weights (-inf: no token), and their sum
-          s_ml[16 * wave + gq] = m_run == -INFINITY ? -INFINITY : -nm;
-          s_ml[16 * wave + 8 + gq] = l_run;
-        }
-      }
-      __syncthreads();
-
-      // -------- combine the parts of each (virtual head, column) pair,
-      // normalise, inverse rotation, write.  The pairs (CV columns per
-      // virtual head) are taken 64 at a time; wave w takes pairs 4 w .. 4 w +
-      // 3 of each round, 16 lanes each.  Lane m of a pair first holds dims m
-      // + 16 k (k < D / 16) and runs the transform stages over k in its
-      // registers, passes the row through LDS, then holds dims (D / 16) m + k,
-      // runs the stages over k again and the remaining ones across the lanes
-      // of the pair.
-      const int CV = CG == 1 ? p.G : 8;
-      const int npair = VH * CV;
-      for (int pbase = 4 * wave; pbase < npair; pbase += 4 * kWaves) {
-        constexpr int ND = D / 16;
-        const int m = le & 15;
-        const int pr_raw = pbase + (le >> 4);
-        const int pr = pr_raw < npair ? pr_raw : npair - 1;
-        const int h2 = CG == 1 ? (int)(((float)pr + 0.5f) * p.inv_G) : pr >> 3;   // virtual head: pr / CV (pr < 128)
-        const int g = pr - h2 * CV;
-        const int hk = h2 / CG;                   // its kv head of the group
-        const int col = 8 * (h2 - hk * CG) + g;   // its column of the kv head
-        const bool live = pr_raw < npair && col < p.G;
-        float M = -INFINITY;   // wave states: weights 2^(w s - X_w), sums l_w
-        for (int q = 0; q < NPW; ++q) M = fmaxf(M, s_ml[16 * wave_of_part(h2, q, VH) + g]);
-        float y[ND];
-#pragma unroll
-        for (int k = 0; k < ND; ++k) y[k] = 0.f;
-        float L = 0.f;
-        for (int q = 0; q < NPW; ++q) {
-          const int wq = wave_of_part(h2, q, VH);
-          const float mw = s_ml[16 * wq + g];
-          const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-          L = __builtin_fmaf(f, s_ml[16 * wq + 8 + g], L);
-          const float* srow = slots + (8 * wq + g) * C::DS + m;
-#pragma unroll
-          for (int k = 0; k < ND; ++k) y[k] = __builtin_fmaf(f, srow[16 * k], y[k]);
-        }
-#pragma unroll
-        for (int h = 1; h < ND; h <<= 1) {
-#pragma unroll
-          for (int e = 0; e < ND; ++e)
-            if ((e & h) == 0) {
-              const float a0 = y[e], b0v = y[e + h];
-              y[e] = a0 + b0v;
-              y[e + h] = a0 - b0v;
-            }
-        }
-        // the row of part 0 is read only by this pair's lanes, each lane
-        // rewrites the dims it read; the fence below orders those writes
-        // before the reads of the other lanes' dims
-        float* row = slots + (8 * wave_of_part(h2, 0, VH) + g) * C::DS;
-#pragma unroll
-        for (int k = 0; k < ND; ++k) row[m + 16 * k] = y[k];
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // other lanes' values below
-#pragma unroll
-        for (int k = 0; k < ND; k += 4) {
-          const float4 f = *reinterpret_cast<const float4*>(row + ND * m + k);
-          y[k] = f.x; y[k + 1] = f.y; y[k + 2] = f.z; y[k + 3] = f.w;
-        }
-#pragma unroll
-        for (int h = 1; h < ND; h <<= 1) {
-#pragma unroll
-          for (int e = 0; e < ND; ++e)
-            if ((e & h) == 0) {
-              const float a0 = y[e], b0v = y[e + h];
-              y[e] = a0 + b0v;
-              y[e + h] = a0 - b0v;
-            }
-        }
-        wht_lanes<1>(y, le);   // dim bit 3 (D = 128) or bits 2, 3 (D = 64)
-        if constexpr (ND == 4) wht_lanes<2>(y, le);
-        const bool empty = !(L > 0.f);
-        const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
-        const float scale = empty ? 0.f : inv_sqrt_d * p.v_mul / L;
-        const float lse = empty ? -INFINITY : (M + log2f(L)) * kLn2;
-        const int qi = (int)(((float)col + 0.5f) * p.inv_Gr);   // column col = (query qi, q head col - qi Gr)
-        const int64_t rowq = ((int64_t)s * p.NQ + qi) * p.Hq + (grp * HG + hk) * p.Gr + (col - qi * p.Gr);
-        const int d0 = ND * m;
-        const uint32_t sgn = s_par[24 + (d0 >> 5)] >> (d0 & 31);
-#pragma unroll
-        for (int k = 0; k < ND; ++k) {
-          const float sv = y[k] * scale;
-          y[k] = ((sgn >> k) & 1u) ? -sv : sv;
-        }
-        if (live) {
-          if (whole) {
-            const int64_t off = rowq * D + d0;
-            if (p.out_f32) {
-#pragma unroll
-              for (int k = 0; k < ND; k += 4)
-                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off + k) = float4{y[k], y[k + 1], y[k + 2], y[k + 3]};
+              if (m == 0 && p.lse) p.lse[rowq] = lse;
+              if (m == 0 && p.P > 1) p.part_lse[rowq * p.PS] = __uint_as_float(kDoneBits);
             } else {
-              uint32_t w[ND / 2];
-#pragma unroll
-              for (int k = 0; k < ND / 2; ++k)
-                w[k] = (uint32_t)f32_to_bf16_rne(y[2 * k]) | ((uint32_t)f32_to_bf16_rne(y[2 * k + 1]) << 16);
-              uint16_t* o16 = static_cast<uint16_t*>(p.out) + off;
-              if constexpr (ND == 8) *reinterpret_cast<uint4*>(o16) = uint4{w[0], w[1], w[2], w[3]};
-              else *reinterpret_cast<uint2*>(o16) = uint2{w[0], w[1]};
+              const int64_t row0 = rowq * p.PS;
+              const int64_t prow = row0 + piece;
+  #pragma unroll
+              for (int k = 0; k < ND; k += 4)
+                *reinterpret_cast<float4*>(p.part_o + prow * D + d0 + k) = float4{y[k], y[k + 1], y[k + 2], y[k + 3]};
+              if (m == 0) p.part_lse[prow] = lse;
+              if (piece == n_pieces - 1)   // the last piece closes the slots no piece uses
+                for (int i = n_pieces + m; i < p.P; i += 16) p.part_lse[row0 + i] = -INFINITY;
             }
-            if (m == 0 && p.lse) p.lse[rowq] = lse;
-            if (m == 0 && p.P > 1) p.part_lse[rowq * p.PS] = __uint_as_float(kDoneBits);
-          } else {
-            const int64_t row0 = rowq * p.PS;
-            const int64_t prow = row0 + piece;
-#pragma unroll
-            for (int k = 0; k < ND; k += 4)
-              *reinterpret_cast<float4*>(p.part_o + prow * D + d0 + k) = float4{y[k], y[k + 1], y[k + 2], y[k + 3]};
-            if (m == 0) p.part_lse[prow] = lse;
-            if (piece == n_pieces - 1)   // the last piece closes the slots no piece uses
-              for (int i = n_pieces + m; i < p.P; i += 16) p.part_lse[row0 + i] = -INFINITY;
           }
         }
+        TQ_MARK(5 + 4 * n_done);
+        ++n_done;
       }
-      TQ_MARK(5 + 4 * n_done);
-      ++n_done;
-    }
 
-    // -------- next segment
-    pos = vb0 + nb_s;
-    if (pos >= r1) break;
-    off = 0;
-    if (++grp == p.NG) {
-      grp = 0;
-      do {
-        ++s;
-        nb_s = (seq_len(p, s_cl, s) + 15) >> 4;
-      } while (nb_s == 0);
+      // -------- next segment
+      pos = vb0 + nb_s;
+      if (pos >= r1) break;
+      off = 0;
+      if (++grp == p.NG) {
+        grp = 0;
+        do {
+          ++s;
+          nb_s = (seq_len(p, s_cl, s) + 15) >> 4;
+        } while (nb_s == 0);
+      }
     }
   }
   window_items();
