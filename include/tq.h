@@ -225,6 +225,19 @@ tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype, int64_t n
                       const tq_format* vfmt, int32_t* dev_err, tq_stream_t stream);
 
 /*
+ * Device self-test of the write path's arithmetic (diagnostics; the bit
+ * exact encoding above rests on it): for i < n, out_sqrt[i] = sqrt(a[i]),
+ * out_div[i] = a[i] / b[i], out_mul[i] = a[i] * b[i] (each IEEE binary64,
+ * correctly rounded) and out_f16[i] = the binary16 bits of a[i] rounded to
+ * nearest, ties to even, directly from binary64 -- computed by a kernel
+ * built like the write kernel (no fused multiply-add).  A caller compares
+ * them with any IEEE host.  All pointers device; n in [0, 2^31); VALUE on a
+ * bad argument.
+ */
+tq_status tq_selftest_fp64(const double* a, const double* b, int64_t n, double* out_sqrt, double* out_div,
+                           double* out_mul, uint16_t* out_f16, tq_stream_t stream);
+
+/*
  * Workspace of tq_decode_paged: num_seqs * num_q_heads * num_splits *
  * (head_dim + 1) * 4 bytes when num_splits > 1, else 0.  It depends on the
  * runtime shape only, never on context length ([D "Serving Route Design"]:

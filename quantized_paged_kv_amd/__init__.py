@@ -70,6 +70,7 @@ def _load(path: str = LIB_PATH):
         "tq_tile_bytes": ([fmtp, i32, P, P], i32),
         "tq_write_kv": ([P, P, i32, i64, i32, P, P, P, i64, i32, fmtp, fmtp, P, P], i32),
         "tq_decode_workspace_bytes": ([i32, i32, i32, i32, P], i32),
+        "tq_selftest_fp64": ([P, P, i64, P, P, P, P, P], i32),
         "tq_decode_paged": ([P, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, f32, i32, P, u64,
                              P, i32, P, P, P], i32),
         "tq_decode_paged_multi": ([P, i32, i32, i32, i32, i32, P, P, i64, i32, P, i32, P, fmtp, fmtp, f32, i32,
@@ -280,6 +281,18 @@ def write_kv(k, v, slot_mapping, k_pages, v_pages, kfmt: Format, vfmt: Format, d
         raise_device_error(dev_err, "tq_write_kv")
 
 
+def selftest_fp64(a, b, stream=None):
+    """The write path's fp64 operations on the device: for float64 GPU
+    tensors a, b of one shape returns (sqrt(a), a / b, a * b, binary16 bits
+    of a as int16), computed by a kernel built like the write kernel."""
+    import torch
+    _need(a.is_cuda and b.is_cuda and a.dtype == torch.float64 and b.dtype == torch.float64 and a.shape == b.shape
+          and a.is_contiguous() and b.is_contiguous(), "a and b must be contiguous float64 GPU tensors of one shape")
+    outs = [torch.empty_like(a) for _ in range(3)] + [torch.empty(a.shape, dtype=torch.int16, device=a.device)]
+    _check(_lib.tq_selftest_fp64(_ptr(a), _ptr(b), a.numel(), *[_ptr(t) for t in outs], _stream(stream)))
+    return tuple(outs)
+
+
 def workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
     b = ctypes.c_uint64()
     _check(_lib.tq_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_splits, ctypes.byref(b)))
@@ -474,5 +487,5 @@ def set_phase_trace(buf) -> bool:
 
 __all__ = ["Format", "UnsupportedFormatError", "DeviceError", "lloyd_max_codebook", "alloc_pages",
            "new_error_word", "raise_device_error", "write_kv", "workspace_bytes", "decode_paged", "decode_paged_noalloc",
-           "split_merge", "decode_dense", "decode_paged_window", "set_phase_trace",
+           "split_merge", "decode_dense", "decode_paged_window", "set_phase_trace", "selftest_fp64",
            "LIB_PATH", "BLOCK_SIZE"]

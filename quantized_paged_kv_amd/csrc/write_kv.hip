@@ -440,10 +440,35 @@ int resident_per_cu() {
   return n;
 }
 
+// The write path's fp64 operations on given inputs, as the write kernel
+// compiles them (same file, same flags: no contraction): element i of each
+// output is sqrt(a_i), a_i / b_i, a_i * b_i and the binary16 bits of a_i.
+__global__ __launch_bounds__(256) void selftest_fp64_kernel(const double* a, const double* b, int64_t n,
+                                                            double* out_sqrt, double* out_div, double* out_mul,
+                                                            uint16_t* out_f16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const double x = a[i], y = b[i];
+  out_sqrt[i] = __builtin_sqrt(x);
+  out_div[i] = x / y;
+  out_mul[i] = x * y;
+  out_f16[i] = f64_to_f16_rne(x);
+}
+
 }  // namespace
 }  // namespace tq
 
 using namespace tq;
+
+extern "C" tq_status tq_selftest_fp64(const double* a, const double* b, int64_t n, double* out_sqrt, double* out_div,
+                                      double* out_mul, uint16_t* out_f16, tq_stream_t stream) {
+  if (n < 0 || n >= (1ll << 31)) return set_error(TQ_ERR_VALUE, "n must be in [0, 2^31)");
+  if (n == 0) return TQ_OK;
+  if (!a || !b || !out_sqrt || !out_div || !out_mul || !out_f16) return set_error(TQ_ERR_VALUE, "NULL pointer");
+  hipLaunchKernelGGL(selftest_fp64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), a, b, n, out_sqrt, out_div, out_mul, out_f16);
+  return launch_status("tq_selftest_fp64 launch");
+}
 
 extern "C" tq_status tq_write_kv(const void* k, const void* v, tq_dtype in_dtype, int64_t num_tokens,
                                  int32_t num_kv_heads, const int64_t* slot_mapping, uint8_t* k_pages,

@@ -183,3 +183,34 @@ def test_write_workload_full_size():
     kp, vp = _gpu_write(xk, xv, w.slot_mapping, w.num_blocks, w.kfmt, w.vfmt, "bf16")
     _assert_pool_equal(kp, _oracle_pool(xk, w.slot_mapping, w.num_blocks, w.kfmt, "k"), "K")
     _assert_pool_equal(vp, _oracle_pool(xv, w.slot_mapping, w.num_blocks, w.vfmt, "v"), "V")
+
+
+def test_two_streams_write_disjoint_slots_concurrently():
+    """Two write batches with disjoint slots on two streams, with no order
+    between them: every other token of the same blocks, so both batches write
+    rows of the same tiles at the same time.  Rows are whole bytes and each
+    norm its own 2-byte slot, so concurrent writers touch no common byte: the
+    pools equal the oracle's whole pools."""
+    import torch
+    import quantized_paged_kv_amd as tq
+    w = wl.write_workload(seed=91, num_seqs=4, new_tokens=512, num_kv_heads=8, head_dim=128, kbits=[4, 3],
+                          vbits=[2])
+    xk, xv = wl.write_values(w, "k"), wl.write_values(w, "v")
+    kf, vf = product_format(w.kfmt), product_format(w.vfmt)
+    kp = torch.full((w.num_blocks, 8, kf.tile_bytes()[1]), 0xA5, dtype=torch.uint8, device="cuda")
+    vp = torch.full((w.num_blocks, 8, vf.tile_bytes()[1]), 0xA5, dtype=torch.uint8, device="cuda")
+    halves = []
+    for part in (0, 1):
+        idx = np.arange(part, len(w.slot_mapping), 2)
+        halves.append((to_device(xk[idx], "bf16"), to_device(xv[idx], "bf16"),
+                       torch.from_numpy(w.slot_mapping[idx].astype(np.int64)).cuda(), tq.new_error_word()))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    print("case two streams, interleaved slots", flush=True)
+    for (k, v, sl, err), st in zip(halves, streams):
+        tq.write_kv(k, v, sl, kp, vp, kf, vf, dev_err=err, stream=st)
+    torch.cuda.synchronize()
+    for _, _, _, err in halves:
+        tq.raise_device_error(err, "concurrent write")
+    _assert_pool_equal(kp.cpu().numpy(), _oracle_pool(xk, w.slot_mapping, w.num_blocks, w.kfmt, "k"), "K")
+    _assert_pool_equal(vp.cpu().numpy(), _oracle_pool(xv, w.slot_mapping, w.num_blocks, w.vfmt, "v"), "V")
