@@ -11,7 +11,8 @@ from tests.test_gpu_selftest import exact_f16_bits, f16_edge_cases
 def test_numpy_binary16_rounding_is_exact_on_edge_cases():
     x = f16_edge_cases()
     sel = np.random.default_rng(3).choice(len(x), 3000, replace=False)
-    got = x[sel].astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):   # values past 65520 round to infinity, as they should
+        got = x[sel].astype(np.float16).view(np.uint16)
     ref = np.array([exact_f16_bits(v) for v in x[sel]], dtype=np.uint16)
     assert np.array_equal(got, ref)
 
