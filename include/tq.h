@@ -71,7 +71,15 @@ typedef enum tq_status {
   TQ_ERR_DEVICE = 5
 } tq_status;
 
-typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+/* The two bounding enumerators give the type the range of int32, so that
+ * any int32 a caller passes as a dtype is a value of the type (and is
+ * rejected by the calls' checks unless it is TQ_F32 or TQ_BF16). */
+typedef enum tq_dtype {
+  TQ_F32 = 0,
+  TQ_BF16 = 1,
+  TQ_DTYPE_RANGE_LOW_ = -2147483647 - 1,
+  TQ_DTYPE_RANGE_HIGH_ = 2147483647
+} tq_dtype;
 
 #define TQ_MAX_HEAD_DIM 128
 #define TQ_BLOCK_SIZE 16
