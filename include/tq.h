@@ -20,7 +20,8 @@
  * persistent bytes, the attention path only consumes them):
  *   - The caller allocates every buffer (pages, q, out, lse, workspace,
  *     slot_mapping, block tables, context lengths, error words).  The library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing; its only state between calls is the device array of
+ *     tq_decode_paged_noalloc (part of its code object, one per GPU).
  *   - Pointers named "device" must be device memory; "host" pointers are
  *     read during the call only.
  *   - Every GPU call is asynchronous on `stream` (a hipStream_t; NULL is the
