@@ -504,6 +504,15 @@ __device__ __forceinline__ int wave_of_part(int h, int q, int VH) {
   return h + VH * q;
 }
 
+// Workgroup barrier that orders LDS accesses only: the waves' global loads
+// (the first page tiles) stay in flight across it, where __syncthreads would
+// wait for every outstanding load.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Workgroup LDS.  The tables come first so that every table address
 // (< 64 KB) fits the immediate offset of the LDS read.
 template <int D, int KK, int VK>
@@ -917,15 +926,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         Tile<D, KK, VK> A, B, C3;
         bool ok_c, ok_1;
         // the first two tiles go out now, so that their latency overlaps the
-        // q rotation; with the QJL stage they go out after the projection,
-        // whose loads would otherwise wait for them (loads complete in order)
+        // q rotation (and the QJL projection): the barriers up to the block
+        // loop order LDS accesses only, so the tile loads stay in flight
         auto first_tiles = [&]() {
           entry(v0, idx_c, ok_c);
           load_tile<D, KK, VK>(A, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
           entry(v1, idx_1, ok_1);
           load_tile<D, KK, VK>(B, kt, vt, kb, vb, k_off, klo_off, n_off, v_off, v_off1, sg_off, gm_off);
         };
-        if constexpr (!C::QJ) first_tiles();
+        first_tiles();
   #pragma unroll
         for (int i = 0; i < NBT; ++i) s_bt[tid + kThreads * i] = btv[i];
 
@@ -1025,7 +1034,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           // one MFMA each), B = the rows (high part in columns 0-7, low part in
           // 8-15), so each output sums all four cross products in fp32.  The u
           // rows go to the area of virtual head 8 + vh (at most 8 of them).
-          __syncthreads();   // the rotated rows of every virtual head are staged
+          lds_barrier();   // the rotated rows of every virtual head are staged
           const int lp = fresh_lane();
           const int pa = lp >> 4, pc = lp & 15;
           const int grp = (16 * ot_w) / QM;
@@ -1170,8 +1179,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             }
           }
         }
-        if constexpr (C::QJ) first_tiles();
-        __syncthreads();  // operands, counters and block-table entries ready
+        lds_barrier();  // operands, counters and block-table entries ready
         TQ_MARK(3 + 4 * n_done);
         int ph2v = bt_at(idx_2);
         int g3 = grab();
