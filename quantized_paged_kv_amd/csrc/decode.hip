@@ -1495,9 +1495,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             pb[g] = __builtin_bit_cast(half4_t, pw);
           }
           __builtin_amdgcn_sched_barrier(0);
-          pv([&](int i, half4_t av) {
-            o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb[C::MIXED_V && i >= C::PPL ? 1 : 0], o_acc[i], 0, 0, 0);
-          });
+          if constexpr (C::KB == KM32) {
+            // every V operand of the tile is looked up before the first P.V
+            // MFMA (one LDS round trip per tile instead of one per MFMA);
+            // measured faster with the 3+2-bit K recipe only (with the other
+            // K kinds the same order is no faster or slower)
+            half4_t va[C::R];
+            pv([&](int i, half4_t av) { va[i] = av; });
+            __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+            for (int i = 0; i < C::R; ++i)
+              o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[i], pb[C::MIXED_V && i >= C::PPL ? 1 : 0], o_acc[i], 0, 0, 0);
+          } else {
+            pv([&](int i, half4_t av) {
+              o_acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb[C::MIXED_V && i >= C::PPL ? 1 : 0], o_acc[i], 0, 0, 0);
+            });
+          }
         };
 
         // one block (j): issue tile j+2, look up the entry of j+3 and take the
