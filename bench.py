@@ -577,7 +577,7 @@ def main():
         "us_per_layer_step": round(ms_step * 1e3, 2),
         "us_per_layer_step_graph": round(ms_graph * 1e3, 2),
         "step_launch": "calls issued one by one (value, us_per_layer_step); us_per_layer_step_graph replays the "
-                       "same step captured as a HIP graph, slower here than the three eager launches",
+                       "same step captured as a HIP graph (within a few us of the eager launches, either way)",
         "decode_us": stats_us(dec_ms),
         "decode_us_layers_cycled": stats_us(dec_warm),
         "decode_GBs_median": round(b.decode_bytes / (dec_ms[len(dec_ms) // 2] * 1e-3) / 1e9, 1),
