@@ -347,8 +347,14 @@ __global__ __launch_bounds__(kThreads, 5) void write_kv_kernel(WriteParams p) {
     const uint32_t fld = field[0];
     const int b0 = bits * L;   // first row byte of this lane
     const int c = f.chunk;
+    // (run, place) of a byte of the lane-major plane; the chunk of the
+    // served one-group formats is a power of two (shifts, not a division)
+    const bool c_pow2 = (c & (c - 1)) == 0;
+    const int c_sh = __builtin_ctz((unsigned)c | 0x100u);
     auto at = [&](int byte) -> uint8_t* {
       if (c == 0) return tile + offs * f.row_bytes + byte;
+      if (c_pow2)
+        return tile + (((16 * (offs & 3) + (byte >> c_sh)) * 4 + (offs >> 2)) << c_sh) + (byte & (c - 1));
       return tile + ((16 * (offs & 3) + byte / c) * 4 + (offs >> 2)) * c + byte % c;
     };
     if (!valid) {
